@@ -1,0 +1,195 @@
+"""Seeded synthetic inputs shared by the tests, the smoke check and the bench.
+
+This module draws numbers and nothing else: it holds none of the path's
+arithmetic (no quantiser, no GEMM, no routing-to-blocks logic).  Quantised
+weights are drawn directly as codes plus scales of the magnitude the source
+workloads describe, so neither the HIP library nor the oracle depends on it
+for anything but its random draws.
+
+Recipes (shapes and distributions follow the source pages' tests and the
+DeepSeek- / GPT-OSS-shaped workloads the path is measured on):
+
+* per-tensor W8A16 ("SGLang PR 32618 review", ``test_gemm.py`` listing):
+  ``A = bf16(randn/10)``, ``W = e4m3(randn)``, scale 0.01, fp32 ``randn`` bias.
+* block FP8 weights: codes ``e4m3(clamp(100 * randn, +-448))`` -- so a 128x128
+  block spans the e4m3 range the way a block-quantised tensor does -- and
+  fp32 block scales ``0.05 / 100 * U(0.8, 1.2)``, so decoded weights look like
+  ``0.05 * randn``.
+* MXFP4 weights: uniformly random e2m1 nibbles (two per byte) and e8m0 block
+  scales uniform in [118, 122] (2^-9 .. 2^-5).
+* activations ``bf16(randn)``; MXFP4 ``w1`` bias fp32 ``randn``.
+* routing: deterministic per-expert counts over consecutive tokens (weight
+  1.0); softmax-then-top-k of ``randn`` logits (weights not renormalised);
+  Zipf(s) popularity over a seeded permutation of the experts, ``topk``
+  distinct experts per token, weights = softmax of ``randn`` logits.
+
+Generation runs on any torch device; big expert stacks are drawn one expert at
+a time (seed + expert id) so host memory stays bounded.
+"""
+
+from __future__ import annotations
+
+from typing import Dict, Optional, Sequence
+
+import torch
+
+FP8_CODE_STD = 100.0
+WEIGHT_STD = 0.05
+
+
+def _gen(seed: int, device) -> torch.Generator:
+    g = torch.Generator(device=torch.device(device))
+    g.manual_seed(int(seed))
+    return g
+
+
+def fp8_codes(shape, g: torch.Generator, device, std: float = FP8_CODE_STD) -> torch.Tensor:
+    """uint8 e4m3 codes of ``clamp(std * randn, +-448)`` (torch's own cast)."""
+    v = torch.randn(*shape, generator=g, device=device) * std
+    return v.clamp_(-448.0, 448.0).to(torch.float8_e4m3fn).view(torch.uint8)
+
+
+def fp8_block_scales(shape, g: torch.Generator, device) -> torch.Tensor:
+    u = torch.rand(*shape, generator=g, device=device)
+    return ((0.8 + 0.4 * u) * (WEIGHT_STD / FP8_CODE_STD)).float()
+
+
+def bf16_randn(shape, g, device, std: float = 1.0) -> torch.Tensor:
+    return (torch.randn(*shape, generator=g, device=device) * std).to(torch.bfloat16)
+
+
+# --------------------------------------------------------------------------- dense
+
+def dense_w8a16(M: int, N: int, K: int, seed: int, device="cpu", has_bias=True,
+                scale: float = 0.01) -> Dict[str, torch.Tensor]:
+    g = _gen(seed, device)
+    a = (torch.randn(M, K, generator=g, device=device) / 10).to(torch.bfloat16)
+    w = torch.randn(N, K, generator=g, device=device).to(torch.float8_e4m3fn).view(torch.uint8)
+    bias = torch.randn(N, generator=g, device=device) if has_bias else None
+    return {"a": a, "w": w, "scale": torch.tensor([scale], dtype=torch.float32, device=device),
+            "bias": bias}
+
+
+def block_linear(M: int, N: int, K: int, seed: int, device="cpu", block_n: int = 128,
+                 bias_dtype: Optional[torch.dtype] = None) -> Dict[str, torch.Tensor]:
+    g = _gen(seed, device)
+    x = bf16_randn((M, K), g, device)
+    w = fp8_codes((N, K), g, device)
+    sw = fp8_block_scales((-(-N // block_n), K // 128), g, device)
+    bias = None
+    if bias_dtype is not None:
+        bias = torch.randn(N, generator=g, device=device).to(bias_dtype)
+    return {"x": x, "w": w, "sw": sw, "bias": bias, "block_n": block_n}
+
+
+# --------------------------------------------------------------------------- routing
+
+def route_counts(counts: Sequence[int], device="cpu"):
+    """topk=1: expert e gets ``counts[e]`` consecutive tokens, weight 1.0."""
+    ids = torch.cat([torch.full((c,), e, dtype=torch.int32) for e, c in enumerate(counts)])
+    w = torch.ones(ids.numel(), 1, dtype=torch.float32)
+    return ids.view(-1, 1).to(device), w.to(device)
+
+
+def route_softmax_topk(M: int, E: int, topk: int, seed: int, device="cpu"):
+    g = _gen(seed, "cpu")
+    logits = torch.randn(M, E, generator=g)
+    probs = torch.softmax(logits.float(), dim=-1)
+    w, ids = torch.topk(probs, topk, dim=-1)
+    return ids.to(torch.int32).to(device), w.float().to(device)
+
+
+def route_zipf(M: int, E: int, topk: int, s: float, seed: int, device="cpu"):
+    g = _gen(seed, "cpu")
+    perm = torch.randperm(E, generator=g)
+    pop = torch.empty(E, dtype=torch.float64)
+    pop[perm] = torch.arange(1, E + 1, dtype=torch.float64) ** (-s)
+    ids = torch.multinomial(pop.expand(M, E), topk, replacement=False, generator=g)
+    w = torch.softmax(torch.randn(M, topk, generator=g), dim=-1)
+    return ids.to(torch.int32).to(device), w.float().to(device)
+
+
+# --------------------------------------------------------------------------- experts
+
+def moe_fp8_weights(E: int, H: int, I: int, seed: int, device="cpu"):
+    """w1 [E, 2I, H], w2 [E, H, I] e4m3 codes with 128x128 fp32 block scales."""
+    w1 = torch.empty(E, 2 * I, H, dtype=torch.uint8, device=device)
+    w2 = torch.empty(E, H, I, dtype=torch.uint8, device=device)
+    s1 = torch.empty(E, -(-2 * I // 128), H // 128, dtype=torch.float32, device=device)
+    s2 = torch.empty(E, -(-H // 128), I // 128, dtype=torch.float32, device=device)
+    for e in range(E):
+        g = _gen(seed + 7919 * (e + 1), device)
+        w1[e] = fp8_codes((2 * I, H), g, device)
+        w2[e] = fp8_codes((H, I), g, device)
+        s1[e] = fp8_block_scales(s1.shape[1:], g, device)
+        s2[e] = fp8_block_scales(s2.shape[1:], g, device)
+    return {"w1": w1, "w1_scale": s1, "w2": w2, "w2_scale": s2}
+
+
+def moe_mxfp4_weights(E: int, H: int, I: int, seed: int, device="cpu", with_bias=True):
+    """w1 [E, 2I, H/2], w2 [E, H, I/2] packed e2m1; e8m0 scales per 32 columns."""
+    w1 = torch.empty(E, 2 * I, H // 2, dtype=torch.uint8, device=device)
+    w2 = torch.empty(E, H, I // 2, dtype=torch.uint8, device=device)
+    s1 = torch.empty(E, 2 * I, H // 32, dtype=torch.uint8, device=device)
+    s2 = torch.empty(E, H, I // 32, dtype=torch.uint8, device=device)
+    b1 = torch.empty(E, 2 * I, dtype=torch.float32, device=device) if with_bias else None
+    for e in range(E):
+        g = _gen(seed + 7919 * (e + 1), device)
+        w1[e] = torch.randint(0, 256, (2 * I, H // 2), generator=g, device=device, dtype=torch.int32).to(torch.uint8)
+        w2[e] = torch.randint(0, 256, (H, I // 2), generator=g, device=device, dtype=torch.int32).to(torch.uint8)
+        s1[e] = torch.randint(118, 123, (2 * I, H // 32), generator=g, device=device, dtype=torch.int32).to(torch.uint8)
+        s2[e] = torch.randint(118, 123, (H, I // 32), generator=g, device=device, dtype=torch.int32).to(torch.uint8)
+        if b1 is not None:
+            b1[e] = torch.randn(2 * I, generator=g, device=device)
+    return {"w1": w1, "w1_scale": s1, "w2": w2, "w2_scale": s2, "w1_bias": b1}
+
+
+# --------------------------------------------------------------------------- workloads
+
+WORKLOADS = {
+    "per_tensor_w8a16_97x576x224": dict(kind="fp8_scaled_mm", M=97, K=576, N=224),
+    "block_w8a8_linear_2048x2048x7168": dict(kind="block_fp8_linear", M=2048, K=2048, N=7168),
+    "moe_block_fp8_w8a16_e8_h2048_i1024": dict(
+        kind="fused_moe_fp8", E=8, topk=1, H=2048, I=1024,
+        counts=(4, 5, 33, 0, 0, 12, 1, 73), act_quant=False),
+    "moe_mxfp4_gptoss_decode_m32": dict(
+        kind="fused_moe_mxfp4", M=32, E=128, topk=4, H=2880, I=2880),
+    "moe_block_fp8_w8a8_deepseek_prefill_m4096": dict(
+        kind="fused_moe_fp8", M=4096, E=256, topk=8, H=7168, I=2048, zipf=1.1, act_quant=True),
+}
+
+
+def moe_inputs(name_or_spec, seed: int, device="cpu", M: Optional[int] = None) -> Dict:
+    """All inputs of one routed-MoE workload (``M`` overrides the token count)."""
+    spec = dict(WORKLOADS[name_or_spec]) if isinstance(name_or_spec, str) else dict(name_or_spec)
+    E, topk, H, I = spec["E"], spec["topk"], spec["H"], spec["I"]
+    if "counts" in spec:
+        ids, w = route_counts(spec["counts"], device)
+        M = ids.shape[0]
+    else:
+        M = spec["M"] if M is None else M
+        if "zipf" in spec:
+            ids, w = route_zipf(M, E, topk, spec["zipf"], seed + 1, device)
+        else:
+            ids, w = route_softmax_topk(M, E, topk, seed + 1, device)
+    g = _gen(seed, device)
+    x = bf16_randn((M, H), g, device)
+    if spec["kind"] == "fused_moe_mxfp4":
+        wts = moe_mxfp4_weights(E, H, I, seed + 2, device)
+    else:
+        wts = moe_fp8_weights(E, H, I, seed + 2, device)
+        wts["w1_bias"] = None
+    out = {"x": x, "topk_ids": ids, "topk_weights": w, "E": E, "topk": topk, "H": H, "I": I,
+           "act_quant": bool(spec.get("act_quant", False)), "kind": spec["kind"]}
+    out.update(wts)
+    return out
+
+
+def moe_flops(M: int, topk: int, H: int, I: int) -> float:
+    R = M * topk
+    return 2.0 * R * (2 * I * H + H * I)
+
+
+def ceil_div(a: int, b: int) -> int:
+    return -(-a // b)
+
