@@ -1,0 +1,263 @@
+"""Benchmark of the scaled low-precision GEMM / routed fused-MoE hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-secondary]
+
+Headline workload: block-wise FP8 W8A8 linear, bf16 A [2048, 2048] quantised per
+token per 128 columns, e4m3 W [7168, 2048] with 128x128 block scales, bf16 out.
+One step = the 1x128 quantisation kernel + the block-scaled FP8 GEMM, on a
+rotating set of input copies (> 512 MB in total, so the 256 MB last-level
+cache cannot hold the operands between steps).  Inputs are resident in HBM
+before the timed region starts.
+
+Printed: ONE JSON line with the throughput of the step (TFLOP/s), the roofline
+of the dominant kernel (the GEMM, against the FP8 dense MFMA peak, timed with
+HIP events on the stream it runs on), the CPU oracle's throughput on the same
+workload, and secondary measurements of the two routed-MoE workloads
+(GPT-OSS-shaped MXFP4 decode and DeepSeek-shaped W8A8 prefill).
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "fused-MoE & block-FP8 GEMM TFLOP/s + weight GB/s, % of MI355X roofline"
+HBM_PEAK_GBS = 8000.0
+FP8_PEAK_TFLOPS = 5000.0
+BF16_PEAK_TFLOPS = 2500.0
+
+# HBM traffic of the dominant kernel from rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE (per launch, bytes),
+# scaled by the copy-kernel calibration; None until measured for the current kernel.
+GEMM_TRAFFIC_BYTES = None
+
+
+def _args():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-secondary", action="store_true")
+    p.add_argument("--only", choices=["linear", "decode", "prefill"], default=None,
+                   help="time one workload only (profiling runs)")
+    return p.parse_args()
+
+
+def _lib():
+    from mxfp4_block_scaled_expert_amd import _lib as L
+    return L, L.load()
+
+
+def _check(st, what):
+    if st != 0:
+        raise RuntimeError(f"{what} failed with status {st}")
+
+
+# ----------------------------------------------------------------------------- headline
+
+def bench_linear(steps: int, warmup: int):
+    from mxfp4_block_scaled_expert_amd import synth
+    L, lib = _lib()
+    dev = torch.device("cuda", 0)
+    M, K, N = 2048, 2048, 7168
+    per_set = M * K * 2 + N * K + (N // 128) * (K // 128) * 4
+    n_rot = max(2, -(-(600 << 20) // per_set))
+    sets = [synth.block_linear(M, N, K, seed=1002 + i, device=dev) for i in range(n_rot)]
+    q = torch.empty(M, K, dtype=torch.uint8, device=dev)
+    s = torch.empty(M, K // 128, dtype=torch.float32, device=dev)
+    out = torch.empty(M, N, dtype=torch.bfloat16, device=dev)
+    stream = torch.cuda.current_stream()
+    sh = stream.cuda_stream
+
+    def step(i, ev=None):
+        d = sets[i % n_rot]
+        if ev:
+            ev[0].record(stream)
+        _check(lib.mxq_per_token_group_quant_fp8(d["x"].data_ptr(), M, K, K, 128, q.data_ptr(), s.data_ptr(), sh),
+               "quant")
+        if ev:
+            ev[1].record(stream)
+        _check(lib.mxq_block_fp8_linear(q.data_ptr(), L.MXQ_DTYPE_E4M3, s.data_ptr(), M, K, K, d["w"].data_ptr(), N,
+                                        d["sw"].data_ptr(), K // 128, 1, 128, 128, None, 0, out.data_ptr(), N, None,
+                                        0, sh), "block_fp8_linear")
+        if ev:
+            ev[2].record(stream)
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(i, evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    total_ms = evs[0][0].elapsed_time(evs[-1][2])
+    quant_ms = [e[0].elapsed_time(e[1]) for e in evs]
+    gemm_ms = [e[1].elapsed_time(e[2]) for e in evs]
+    flops = 2.0 * M * N * K
+    gemm_avg = float(np.mean(gemm_ms))
+    gemm_bytes = M * K + M * (K // 128) * 4 + N * K + (N // 128) * (K // 128) * 4 + M * N * 2
+    return {
+        "M": M, "K": K, "N": N, "flops": flops, "rotating_sets": n_rot,
+        "ms_per_step": total_ms / steps, "wall_ms_per_step": wall * 1e3 / steps,
+        "quant_us_median": float(np.median(quant_ms)) * 1e3,
+        "gemm_us_avg": gemm_avg * 1e3, "gemm_us_median": float(np.median(gemm_ms)) * 1e3,
+        "gemm_us_p10": float(np.percentile(gemm_ms, 10)) * 1e3, "gemm_us_p90": float(np.percentile(gemm_ms, 90)) * 1e3,
+        "gemm_tflops": flops / (gemm_avg * 1e-3) / 1e12,
+        "gemm_alg_bytes": gemm_bytes,
+    }
+
+
+# ----------------------------------------------------------------------------- MoE workloads
+
+def _touched_bytes(inp) -> int:
+    ids = inp["topk_ids"].cpu().numpy()
+    used = np.unique(ids)
+    per = 0
+    for k in ("w1", "w2", "w1_scale", "w2_scale", "w1_bias"):
+        t = inp.get(k)
+        if t is not None:
+            per += t[0].numel() * t.element_size()
+    M, H = inp["x"].shape
+    return int(used.size * per + 2 * M * H * 2 + ids.size * 8)
+
+
+def bench_moe(name: str, steps: int, warmup: int, seed: int):
+    from mxfp4_block_scaled_expert_amd import ops, synth
+    dev = torch.device("cuda", 0)
+    inp = synth.moe_inputs(name, seed=seed, device=dev)
+    M, H = inp["x"].shape
+    I, E, topk = inp["I"], inp["E"], inp["topk"]
+    mx = inp["kind"] == "fused_moe_mxfp4"
+    from mxfp4_block_scaled_expert_amd import _lib as L
+    ws = ops.fused_moe_workspace(M, H, I, E, topk, L.MXQ_WEIGHTS_MXFP4 if mx else L.MXQ_WEIGHTS_FP8_BLOCK,
+                                 inp["act_quant"], dev)
+    out = torch.empty(M, H, dtype=torch.bfloat16, device=dev)
+
+    def run():
+        if mx:
+            ops.fused_moe_mxfp4(inp["x"], inp["topk_ids"], inp["topk_weights"], inp["w1"], inp["w1_scale"],
+                                inp["w2"], inp["w2_scale"], inp["w1_bias"], workspace=ws, out=out)
+        else:
+            ops.fused_moe_fp8(inp["x"], inp["topk_ids"], inp["topk_weights"], inp["w1"], inp["w1_scale"],
+                              inp["w2"], inp["w2_scale"], None, act_quant=inp["act_quant"], workspace=ws, out=out)
+
+    for _ in range(warmup):
+        run()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+    for i in range(steps):
+        evs[i][0].record(stream)
+        run()
+        evs[i][1].record(stream)
+    torch.cuda.synchronize()
+    ms = np.array([e[0].elapsed_time(e[1]) for e in evs])
+    flops = 2.0 * M * topk * (2 * I * H + H * I)
+    byts = _touched_bytes(inp)
+    med = float(np.median(ms))
+    return {
+        "workload": name, "us_median": med * 1e3, "us_p10": float(np.percentile(ms, 10)) * 1e3,
+        "us_p90": float(np.percentile(ms, 90)) * 1e3, "tflops": flops / (med * 1e-3) / 1e12,
+        "touched_bytes": byts, "weight_gbs": byts / (med * 1e-3) / 1e9,
+        "hbm_frac": byts / (med * 1e-3) / 1e9 / HBM_PEAK_GBS,
+        "fp8_mfma_frac": flops / (med * 1e-3) / 1e12 / FP8_PEAK_TFLOPS,
+        "distinct_experts": int(np.unique(inp["topk_ids"].cpu().numpy()).size),
+    }
+
+
+# ----------------------------------------------------------------------------- CPU oracle
+
+def cpu_baseline(budget_s: float = 12.0):
+    from mxfp4_block_scaled_expert_amd import synth
+    from oracle import dense as OD
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max(i.get("num_threads", 1) for i in threadpool_info()) if threadpool_info() else os.cpu_count()
+    except Exception:
+        cores = os.cpu_count()
+    M, K, N = 2048, 2048, 7168
+    d = synth.block_linear(M, N, K, seed=1002, device="cpu")
+    xb = d["x"].view(torch.int16).numpy().view(np.uint16)
+    w = d["w"].numpy()
+    sw = d["sw"].numpy()
+    runs = 0
+    t0 = time.perf_counter()
+    while True:
+        OD.block_fp8_linear_bf16(xb, w, sw, 128)
+        runs += 1
+        if time.perf_counter() - t0 > budget_s or runs >= 10:
+            break
+    dt = (time.perf_counter() - t0) / runs
+    return {"value": 2.0 * M * N * K / dt / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"whole 2048x2048x7168 workload (quantise + linear), {runs} run(s), {dt:.2f} s each"}
+
+
+def main():
+    a = _args()
+    if a.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
+                          "requested_gpus": a.gpus}), flush=True)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print(json.dumps({"error": "no GPU visible"}), flush=True)
+        sys.exit(1)
+    torch.cuda.set_device(0)
+    from mxfp4_block_scaled_expert_amd import ops
+    ops.init(0)
+
+    if a.only == "decode":
+        print(json.dumps(bench_moe("moe_mxfp4_gptoss_decode_m32", a.steps, a.warmup, 1004)), flush=True)
+        return
+    if a.only == "prefill":
+        print(json.dumps(bench_moe("moe_block_fp8_w8a8_deepseek_prefill_m4096", a.steps, a.warmup, 1005)),
+              flush=True)
+        return
+
+    lin = bench_linear(a.steps, a.warmup)
+    if a.only == "linear":
+        print(json.dumps(lin), flush=True)
+        return
+    value = lin["flops"] / (lin["ms_per_step"] * 1e-3) / 1e12
+    roof = {
+        "kernel": "gemm_w8a8_kernel (block-FP8 W8A8, 128x128 tiles)",
+        "bound": "mfma", "achieved": lin["gemm_tflops"], "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s",
+        "frac": lin["gemm_tflops"] / FP8_PEAK_TFLOPS, "traffic": GEMM_TRAFFIC_BYTES,
+        "alg_bytes_per_launch": lin["gemm_alg_bytes"], "avg_launch_us": lin["gemm_us_avg"],
+    }
+    secondary = {}
+    if not a.no_secondary:
+        secondary["gptoss_mxfp4_decode_m32"] = bench_moe("moe_mxfp4_gptoss_decode_m32", max(10, a.steps // 2),
+                                                        a.warmup, 1004)
+        torch.cuda.empty_cache()
+        secondary["deepseek_w8a8_prefill_m4096"] = bench_moe("moe_block_fp8_w8a8_deepseek_prefill_m4096",
+                                                            max(3, a.steps // 10), 2, 1005)
+        torch.cuda.empty_cache()
+    cpu = None if a.no_cpu_baseline else cpu_baseline()
+    line = {
+        "metric": METRIC, "value": value, "unit": "TFLOP/s", "n_gpus": 1, "steps": a.steps, "warmup": a.warmup,
+        "ms_per_step": lin["ms_per_step"], "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "e4m3 x e4m3 -> fp32 accumulate (bf16 in/out)", "data": "synthetic",
+        "config": {"workload": "block_w8a8_linear_2048x2048x7168 (1x128 act quant + 128x128 weight blocks)",
+                   "M": lin["M"], "K": lin["K"], "N": lin["N"], "rotating_input_sets": lin["rotating_sets"]},
+        "roofline": roof, "cpu_baseline": cpu,
+        "detail": {k: lin[k] for k in ("quant_us_median", "gemm_us_median", "gemm_us_p10", "gemm_us_p90",
+                                       "wall_ms_per_step")},
+        "secondary": secondary,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,208 @@
+/*
+ * mxq -- scaled low-precision GEMM and routed fused-MoE experts for AMD MI355X (gfx950).
+ *
+ * C ABI of libmxq.so.  Conventions for every entry point:
+ *
+ *  - Tensor arguments are DEVICE pointers owned by the caller; the library
+ *    never keeps them past the call and never allocates device memory.  Calls
+ *    that need scratch take a caller-owned workspace (void* + size in bytes);
+ *    the matching *_workspace_size() query returns the bytes needed.
+ *  - Every call is asynchronous: it validates its arguments on the host,
+ *    enqueues kernels on `stream` (a hipStream_t; NULL = the null stream) and
+ *    returns.  Nothing synchronises with the host; launch grids are sized to
+ *    upper bounds and surplus workgroups exit at once.
+ *  - Scalars that live on the device (the per-tensor weight scale) are read by
+ *    the kernels, so no host round trip is needed.
+ *  - bf16 tensors are passed as 16-bit patterns, e4m3 as bytes (OCP FP8 E4M3FN,
+ *    gfx950's native FP8: max 448, no infinities), e2m1 as packed nibbles (OCP
+ *    MX FP4, element 2j in the low nibble of byte j), e8m0 as bytes (OCP MX
+ *    scale, value 2^(e-127); 0xFF is not a valid scale).
+ *  - Every pointer argument must be 16-byte aligned, and every row stride must
+ *    keep rows 16-byte aligned, unless noted.
+ *  - Return value: MXQ_OK or an error code (mxq_status_string() names it).  On
+ *    an error nothing has been enqueued.
+ *
+ * Source pages cited below:
+ *  [A] "vLLM PR 50949 review" -- routed FP8 / MXFP4 fused-MoE on CPU, with the
+ *      BRGEMM-or-TinyGEMM choice taken per expert block from its real row
+ *      count and column width (summary, implementation items 1-4, the
+ *      moe_fp8.cpp and gemm.h listings).
+ *  [B] "SGLang PR 32618 review" -- per-tensor FP8 W8A16 GEMM
+ *      fp8_per_tensor_scaled_mm_cpu (implementation items 1-2, the fp8.py and
+ *      test_gemm.py listings).
+ *  [C] "SGLang PR 35605 review" -- block-wise FP8 W8A8 linear through
+ *      scaled_mm (implementation items 1 and 3, the fp8_utils.py and
+ *      test_xpu_fp8_linear.py listings).
+ */
+#ifndef MXQ_H
+#define MXQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t mxq_status;
+
+#define MXQ_OK 0
+#define MXQ_ERR_NULL 1      /* a required pointer is NULL */
+#define MXQ_ERR_SHAPE 2     /* sizes, strides or alignment not supported */
+#define MXQ_ERR_BLOCK 3     /* block_size not in {[1,128], [128,128]} (page [C], fp8_utils.py listing) */
+#define MXQ_ERR_DTYPE 4     /* unsupported dtype tag */
+#define MXQ_ERR_WORKSPACE 5 /* workspace missing or too small */
+#define MXQ_ERR_ARCH 6      /* the current device is not gfx950 */
+#define MXQ_ERR_LAUNCH 7    /* a kernel launch failed (hipGetLastError) */
+#define MXQ_ERR_ARG 8       /* any other invalid argument */
+
+/* dtype tags */
+#define MXQ_DTYPE_BF16 0
+#define MXQ_DTYPE_F32 1
+#define MXQ_DTYPE_E4M3 2
+
+/* Text for a status code (static storage, never NULL). */
+const char* mxq_status_string(mxq_status status);
+
+/* ABI version of this header (bumped on any signature change). */
+int32_t mxq_abi_version(void);
+
+/* Checks that `device` is a gfx950 GPU and makes it current.  Every other
+ * entry point checks the current device on first use per device and returns
+ * MXQ_ERR_ARCH on anything else (the GPU counterpart of the AMX-only assert of
+ * page [B], fp8.py listing). */
+mxq_status mxq_init(int32_t device);
+
+/* ------------------------------------------------------------------ quantise
+ * Per-token group quantisation to e4m3 (page [C], implementation item 1 and the
+ * fp8_utils.py listing: activations get one fp32 scale per token per 128
+ * columns, scale tensor [M, K/128]).  For each row and each group of 128
+ * columns:  s = max(max|x|, 1e-10) / 448;  q = e4m3_rne(clamp(x / s, +-448))
+ * with IEEE fp32 divisions; codes and scales are exact (bit-for-bit) results.
+ *   x   bf16 [M, K], row stride ldx elements (ldx >= K, multiple of 8)
+ *   q   e4m3 [M, K], contiguous (row stride K bytes)
+ *   s   fp32 [M, K/128], contiguous
+ *   group must be 128; K must be a multiple of 128 (else MXQ_ERR_BLOCK / MXQ_ERR_SHAPE).
+ *   M == 0 or K == 0 is a no-op. */
+mxq_status mxq_per_token_group_quant_fp8(const void* x, int64_t M, int64_t K, int64_t ldx, int32_t group,
+                                         void* q, float* s, void* stream);
+
+/* ------------------------------------------------------------------ per-tensor W8A16
+ * out = bf16((A @ dec(W)^T) * scale + bias)   (page [B], implementation items 1-2
+ * and the test_gemm.py listing; the per-tensor scale is the block scale with every
+ * block equal, applied here once after the K loop).
+ *   A      bf16 [M, K], row stride lda elements (lda >= K, multiple of 8)
+ *   W      e4m3 [N, K], contiguous
+ *   scale  fp32 device scalar (a 0-d or 1-element tensor)
+ *   bias   NULL, or [N] of bias_dtype (MXQ_DTYPE_F32 or MXQ_DTYPE_BF16), added in fp32
+ *   out    bf16 [M, N], row stride ldo elements (ldo >= N)
+ *   K must be a multiple of 32.  fp32 accumulation on the bf16 matrix cores. */
+mxq_status mxq_fp8_scaled_mm(const void* A, int64_t M, int64_t K, int64_t lda, const void* W, int64_t N,
+                             const float* scale, const void* bias, int32_t bias_dtype, void* out, int64_t ldo,
+                             void* stream);
+
+/* ------------------------------------------------------------------ block-FP8 W8A8 linear
+ * out[m, n] = bf16( sum_kb sa[m, kb] * sw[n / block_n, kb] * sum_{k in kb} dec(qa[m, k]) dec(W[n, k]) + bias[n] )
+ * (page [C], implementation items 1 and 3 and the fp8_utils.py listing).
+ *   A         a_dtype MXQ_DTYPE_BF16: bf16 [M, K] (row stride lda elements), quantised
+ *             inside the call exactly as mxq_per_token_group_quant_fp8 does;
+ *             a_dtype MXQ_DTYPE_E4M3: pre-quantised e4m3 [M, K] (row stride lda bytes)
+ *             with a_scale fp32 [M, K/128] contiguous.  a_scale is ignored for bf16 input.
+ *   W         e4m3 [N, K], contiguous
+ *   w_scale   fp32 grid of logical shape [ceil(N / block_n), K / 128], element (i, j) at
+ *             w_scale[i * ws_stride0 + j * ws_stride1] -- row-major and the transposed
+ *             storage of page [C]'s load-time relayout both work, bit-identically.
+ *   block_n, block_k   the weight block: (128, 128) or (1, 128); anything else -> MXQ_ERR_BLOCK
+ *   bias      NULL or [N] of bias_dtype (fp32 or bf16)
+ *   out       bf16 [M, N], row stride ldo elements
+ *   workspace bf16 input needs mxq_block_fp8_linear_workspace_size(M, K, a_dtype) bytes
+ *             (the quantised activations); e4m3 input needs none (may be NULL).
+ *   K must be a multiple of 128.  FP8 matrix cores (16x16x128 per K block), fp32 accumulation. */
+size_t mxq_block_fp8_linear_workspace_size(int64_t M, int64_t K, int32_t a_dtype);
+mxq_status mxq_block_fp8_linear(const void* A, int32_t a_dtype, const float* a_scale, int64_t M, int64_t K,
+                                int64_t lda, const void* W, int64_t N, const float* w_scale, int64_t ws_stride0,
+                                int64_t ws_stride1, int32_t block_n, int32_t block_k, const void* bias,
+                                int32_t bias_dtype, void* out, int64_t ldo, void* workspace, size_t workspace_bytes,
+                                void* stream);
+
+/* ------------------------------------------------------------------ expert sort / align
+ * Groups the R = M * topk routed rows (flat id r = t * topk + k) by expert for the
+ * block walk of page [A] (moe_fp8.cpp listing: expert_ids[mb], offsets[mb] with
+ * m_size = offsets[mb+1] - offsets[mb], input token sorted_ids[mb * BLOCK_M + m] / topk).
+ * Layout: experts ascending; inside an expert, flat ids ascending (stable); each
+ * expert's rows cut into blocks of block_m (only its last block may be partial);
+ * unused slots hold R; blocks past *num_blocks have expert -1 and offset R.
+ *   topk_ids    int32 [M, topk]; ids outside [0, E) are ignored (those rows are dropped)
+ *   sorted_ids  int32 [max_blocks * block_m]
+ *   expert_ids  int32 [max_blocks]
+ *   offsets     int32 [max_blocks + 1]
+ *   num_blocks  int32 device scalar
+ *   with max_blocks = mxq_moe_max_blocks(M, topk, E, block_m) = ceil(R / block_m) + min(E, R).
+ *   1 <= E <= 512, 1 <= block_m <= 1024.  Runs as one workgroup; no host sync. */
+int64_t mxq_moe_max_blocks(int64_t M, int32_t topk, int32_t E, int32_t block_m);
+mxq_status mxq_moe_align(const int32_t* topk_ids, int64_t M, int32_t topk, int32_t E, int32_t block_m,
+                         int32_t* sorted_ids, int32_t* expert_ids, int32_t* offsets, int32_t* num_blocks,
+                         void* stream);
+
+/* ------------------------------------------------------------------ fused MoE experts
+ * out[t] = bf16( sum_k topk_weights[t, k] * y[t*topk + k] ),
+ *   y[r]  = ic1[r] @ w2[e]^T                                     (fp32)
+ *   ic1   = bf16( silu(ic0[:, :I]) * ic0[:, I:] ),  silu(g) = g / (1 + exp(-g))
+ *   ic0   = bf16( x[t] @ w1[e]^T + w1_bias[e] ),   e = topk_ids[t, k]
+ * (page [A], implementation item 2 and the moe_fp8.cpp listing: stage 1 hidden @ w1
+ * into a 2N-wide gate/up intermediate with an optional w1 bias, activation, stage 2
+ * activation @ w2; the top-k combine weights each expert output by its routing
+ * weight).  Rows [0, I) of w1 are the gate, rows [I, 2I) the up projection.
+ * Each expert block picks its kernel from its own row count (page [A],
+ * implementation items 1-2): a wavefront-reduction GEMV for tiny blocks, MFMA
+ * tiles of 16/32/64/128 rows otherwise (see mxq_moe_set_dispatch).
+ *
+ * mxq_fused_moe_fp8: block-FP8 weights.
+ *   x            bf16 [M, H], contiguous
+ *   topk_ids     int32 [M, topk];  topk_weights fp32 [M, topk]
+ *   w1           e4m3 [E, 2I, H];  w1_scale fp32 [E, ceil(2I/128), H/128]
+ *   w2           e4m3 [E, H, I];   w2_scale fp32 [E, ceil(H/128), I/128]
+ *   w1_bias      NULL or fp32 [E, 2I]
+ *   act_quant    0: W8A16 (bf16 activations into both stages);
+ *                1: W8A8 (x and ic1 quantised per token per 128 columns, as
+ *                   mxq_per_token_group_quant_fp8)
+ *   out          bf16 [M, H], contiguous
+ *   H and I must be multiples of 128.
+ * mxq_fused_moe_mxfp4: MXFP4 weights, bf16 activations (W4A16).
+ *   w1           packed e2m1 [E, 2I, H/2];  w1_scale e8m0 [E, 2I, H/32]
+ *   w2           packed e2m1 [E, H, I/2];   w2_scale e8m0 [E, H, I/32]
+ *   w1_bias      NULL or fp32 [E, 2I]
+ *   H and I must be multiples of 32.
+ * Both: workspace of mxq_fused_moe_workspace_size(...) bytes (routing tables,
+ * intermediates); experts that receive no rows are never read; 1 <= E <= 512. */
+#define MXQ_WEIGHTS_FP8_BLOCK 0
+#define MXQ_WEIGHTS_MXFP4 1
+size_t mxq_fused_moe_workspace_size(int64_t M, int64_t H, int64_t I, int32_t E, int32_t topk, int32_t weights,
+                                    int32_t act_quant);
+mxq_status mxq_fused_moe_fp8(const void* x, int64_t M, int64_t H, int64_t I, int32_t E, int32_t topk,
+                             const int32_t* topk_ids, const float* topk_weights, const void* w1,
+                             const float* w1_scale, const void* w2, const float* w2_scale, const float* w1_bias,
+                             int32_t act_quant, void* out, void* workspace, size_t workspace_bytes, void* stream);
+mxq_status mxq_fused_moe_mxfp4(const void* x, int64_t M, int64_t H, int64_t I, int32_t E, int32_t topk,
+                               const int32_t* topk_ids, const float* topk_weights, const void* w1,
+                               const void* w1_scale, const void* w2, const void* w2_scale, const float* w1_bias,
+                               void* out, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Per-block dispatch control for the fused MoE (process-wide, not thread-safe).
+ *   mode MXQ_DISPATCH_PER_BLOCK (default): each block's class from its own row count;
+ *   mode MXQ_DISPATCH_FORCED: every block runs class `forced_class` (0 = GEMV,
+ *        1 = 16-row, 2 = 32-row, 3 = 64-row, 4 = 128-row MFMA tiles) -- for tests;
+ *   mode MXQ_DISPATCH_LAYER_AVERAGE: one class for the whole layer, chosen from
+ *        max(1, M * topk / E) rows (the per-layer rule page [A] replaces; for
+ *        ablation measurements).
+ *   gemv_max_rows: largest block that takes the GEMV class in per-block mode (default 4, max 4). */
+#define MXQ_DISPATCH_PER_BLOCK 0
+#define MXQ_DISPATCH_FORCED 1
+#define MXQ_DISPATCH_LAYER_AVERAGE 2
+mxq_status mxq_moe_set_dispatch(int32_t mode, int32_t forced_class, int32_t gemv_max_rows);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MXQ_H */

@@ -1,0 +1,25 @@
+"""mxq: scaled low-precision GEMM and routed fused-MoE experts for AMD MI355X (gfx950).
+
+The compute lives in ``libmxq.so`` (hand-written HIP kernels behind the C ABI
+of ``include/mxq.h``); ``ops`` is a thin torch binding that only marshals
+arguments.  Build the library with ``python -m mxfp4_block_scaled_expert_amd.build``.
+"""
+
+from .ops import (  # noqa: F401
+    init,
+    per_token_group_quant_fp8,
+    fp8_scaled_mm,
+    block_fp8_linear,
+    moe_max_blocks,
+    moe_align,
+    fused_moe_fp8,
+    fused_moe_mxfp4,
+    fused_moe_workspace,
+    moe_set_dispatch,
+)
+from ._lib import (  # noqa: F401
+    LIB_PATH,
+    MXQ_DISPATCH_PER_BLOCK,
+    MXQ_DISPATCH_FORCED,
+    MXQ_DISPATCH_LAYER_AVERAGE,
+)

@@ -1,0 +1,94 @@
+"""ctypes loader for libmxq.so (the C ABI declared in include/mxq.h).
+
+There is no fallback: if the library has not been built, every call raises.
+"""
+
+from __future__ import annotations
+
+import ctypes as C
+import os
+import threading
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libmxq.so")
+
+MXQ_OK = 0
+MXQ_ERR_NULL = 1
+MXQ_ERR_SHAPE = 2
+MXQ_ERR_BLOCK = 3
+MXQ_ERR_DTYPE = 4
+MXQ_ERR_WORKSPACE = 5
+MXQ_ERR_ARCH = 6
+MXQ_ERR_LAUNCH = 7
+MXQ_ERR_ARG = 8
+
+MXQ_DTYPE_BF16 = 0
+MXQ_DTYPE_F32 = 1
+MXQ_DTYPE_E4M3 = 2
+
+MXQ_WEIGHTS_FP8_BLOCK = 0
+MXQ_WEIGHTS_MXFP4 = 1
+
+MXQ_DISPATCH_PER_BLOCK = 0
+MXQ_DISPATCH_FORCED = 1
+MXQ_DISPATCH_LAYER_AVERAGE = 2
+
+_p = C.c_void_p
+_i32 = C.c_int32
+_i64 = C.c_int64
+_sz = C.c_size_t
+
+# name -> (restype, argtypes), mirroring include/mxq.h
+SIGNATURES = {
+    "mxq_status_string": (C.c_char_p, [_i32]),
+    "mxq_abi_version": (_i32, []),
+    "mxq_init": (_i32, [_i32]),
+    "mxq_per_token_group_quant_fp8": (_i32, [_p, _i64, _i64, _i64, _i32, _p, _p, _p]),
+    "mxq_fp8_scaled_mm": (_i32, [_p, _i64, _i64, _i64, _p, _i64, _p, _p, _i32, _p, _i64, _p]),
+    "mxq_block_fp8_linear_workspace_size": (_sz, [_i64, _i64, _i32]),
+    "mxq_block_fp8_linear": (_i32, [_p, _i32, _p, _i64, _i64, _i64, _p, _i64, _p, _i64, _i64, _i32, _i32,
+                                     _p, _i32, _p, _i64, _p, _sz, _p]),
+    "mxq_moe_max_blocks": (_i64, [_i64, _i32, _i32, _i32]),
+    "mxq_moe_align": (_i32, [_p, _i64, _i32, _i32, _i32, _p, _p, _p, _p, _p]),
+    "mxq_fused_moe_workspace_size": (_sz, [_i64, _i64, _i64, _i32, _i32, _i32, _i32]),
+    "mxq_fused_moe_fp8": (_i32, [_p, _i64, _i64, _i64, _i32, _i32, _p, _p, _p, _p, _p, _p, _p, _i32, _p, _p,
+                                  _sz, _p]),
+    "mxq_fused_moe_mxfp4": (_i32, [_p, _i64, _i64, _i64, _i32, _i32, _p, _p, _p, _p, _p, _p, _p, _p, _p,
+                                    _sz, _p]),
+    "mxq_moe_set_dispatch": (_i32, [_i32, _i32, _i32]),
+}
+
+_lock = threading.Lock()
+_lib = None
+
+
+class MxqError(RuntimeError):
+    def __init__(self, fn: str, status: int, text: str):
+        super().__init__(f"{fn}: {text} (status {status})")
+        self.status = status
+
+
+def load() -> C.CDLL:
+    global _lib
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(LIB_PATH):
+                raise RuntimeError(
+                    f"{LIB_PATH} is not built; run `python -m mxfp4_block_scaled_expert_amd.build` "
+                    "(there is no non-HIP fallback)")
+            lib = C.CDLL(LIB_PATH)
+            for name, (res, args) in SIGNATURES.items():
+                f = getattr(lib, name)
+                f.restype = res
+                f.argtypes = args
+            _lib = lib
+    return _lib
+
+
+def check(fn: str, status: int) -> None:
+    if status == MXQ_OK:
+        return
+    text = load().mxq_status_string(status).decode()
+    if status in (MXQ_ERR_SHAPE, MXQ_ERR_BLOCK, MXQ_ERR_DTYPE):
+        raise ValueError(f"{fn}: {text} (status {status})")
+    raise MxqError(fn, status, text)

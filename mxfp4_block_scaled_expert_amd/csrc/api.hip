@@ -1,0 +1,425 @@
+// C ABI of libmxq (declared and documented in include/mxq.h): host-side
+// argument validation, workspace carving, per-class grid bounds, and the kernel
+// sequences of each entry point.
+#include <string.h>
+
+#include <atomic>
+#include <mutex>
+
+#include "../../include/mxq.h"
+#include "kernels.hpp"
+
+using namespace mxq;
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_arch_ok[kMaxDevices];  // 0 unknown, 1 gfx950, -1 other
+
+mxq_status check_arch() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return MXQ_ERR_ARCH;
+  int st = g_arch_ok[dev].load(std::memory_order_relaxed);
+  if (st == 0) {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return MXQ_ERR_ARCH;
+    st = (strncmp(prop.gcnArchName, "gfx950", 6) == 0) ? 1 : -1;
+    g_arch_ok[dev].store(st, std::memory_order_relaxed);
+  }
+  return st == 1 ? MXQ_OK : MXQ_ERR_ARCH;
+}
+
+mxq_status launch_status() { return hipGetLastError() == hipSuccess ? MXQ_OK : MXQ_ERR_LAUNCH; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+#define MXQ_TRY(expr)                \
+  do {                               \
+    const mxq_status _s = (expr);    \
+    if (_s != MXQ_OK) return _s;     \
+  } while (0)
+
+// MoE dispatch state (process-wide)
+std::mutex g_dispatch_mu;
+int g_dispatch_mode = MXQ_DISPATCH_PER_BLOCK;
+int g_forced_class = 0;
+int g_gemv_max_rows = 4;
+
+constexpr int kMoeBlockM = 128;
+constexpr int kNumClasses = 5;  // GEMV, 16-, 32-, 64-, 128-row MFMA tiles
+constexpr int kClassTile[kNumClasses] = {-1, 3, 2, 1, 0};  // launcher tile index per class
+constexpr int kClassRows[kNumClasses] = {4, 16, 32, 64, 128};
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+struct MoeWorkspace {
+  int32_t *sorted_ids, *expert_ids, *offsets, *num_blocks, *class_lists, *class_counts;
+  uint8_t* qx;
+  float* sx;
+  uint16_t* ic0;
+  uint16_t* ic1;
+  uint8_t* ic1_q;
+  float* ic1_s;
+  float* y;
+  size_t bytes;
+};
+
+MoeWorkspace carve_moe(void* base, int64_t M, int64_t H, int64_t I, int32_t E, int32_t topk, bool act_quant) {
+  const int64_t R = M * topk;
+  const int64_t mbk = mxq_moe_max_blocks(M, topk, E, kMoeBlockM);
+  MoeWorkspace w{};
+  size_t off = 0;
+  auto take = [&](size_t bytes) -> uint8_t* {
+    uint8_t* p = base ? static_cast<uint8_t*>(base) + off : nullptr;
+    off += align256(bytes);
+    return p;
+  };
+  w.sorted_ids = reinterpret_cast<int32_t*>(take(sizeof(int32_t) * mbk * kMoeBlockM));
+  w.expert_ids = reinterpret_cast<int32_t*>(take(sizeof(int32_t) * mbk));
+  w.offsets = reinterpret_cast<int32_t*>(take(sizeof(int32_t) * (mbk + 1)));
+  w.num_blocks = reinterpret_cast<int32_t*>(take(sizeof(int32_t)));
+  w.class_lists = reinterpret_cast<int32_t*>(take(sizeof(int32_t) * mbk * kNumClasses));
+  w.class_counts = reinterpret_cast<int32_t*>(take(sizeof(int32_t) * kNumClasses));
+  if (act_quant) {
+    w.qx = take(size_t(M) * H);
+    w.sx = reinterpret_cast<float*>(take(sizeof(float) * M * (H / 128)));
+  }
+  w.ic0 = reinterpret_cast<uint16_t*>(take(sizeof(uint16_t) * R * 2 * I));
+  if (act_quant) {
+    w.ic1_q = take(size_t(R) * I);
+    w.ic1_s = reinterpret_cast<float*>(take(sizeof(float) * R * (I / 128)));
+  } else {
+    w.ic1 = reinterpret_cast<uint16_t*>(take(sizeof(uint16_t) * R * I));
+  }
+  w.y = reinterpret_cast<float*>(take(sizeof(float) * R * H));
+  w.bytes = off;
+  return w;
+}
+
+// Largest number of blocks that can fall in class c (no host sync: from sizes only).
+int64_t class_bound(int c, int64_t R, int32_t E, int64_t max_blocks, const ClassPolicy& pol) {
+  if (pol.forced >= 0) return c == pol.forced ? max_blocks : 0;
+  const int lo = c == 0 ? 0 : pol.bound[c - 1];
+  const int hi = c == pol.n_classes - 1 ? kMoeBlockM : pol.bound[c];
+  if (hi <= lo) return 0;
+  int64_t ub = std::min<int64_t>(max_blocks, R / (lo + 1));
+  if (hi < kMoeBlockM) ub = std::min<int64_t>(ub, E);  // only an expert's last block is partial
+  return std::max<int64_t>(ub, 0);
+}
+
+ClassPolicy make_policy(int64_t R, int32_t E) {
+  std::lock_guard<std::mutex> lk(g_dispatch_mu);
+  ClassPolicy pol{};
+  pol.n_classes = kNumClasses;
+  pol.forced = -1;
+  pol.bound[0] = g_gemv_max_rows;
+  for (int c = 1; c < kNumClasses; ++c) pol.bound[c] = kClassRows[c];
+  if (g_dispatch_mode == MXQ_DISPATCH_FORCED) {
+    pol.forced = g_forced_class;
+  } else if (g_dispatch_mode == MXQ_DISPATCH_LAYER_AVERAGE) {
+    const int64_t avg = std::max<int64_t>(1, R / std::max<int32_t>(E, 1));
+    int c = kNumClasses - 1;
+    for (int i = 0; i < kNumClasses - 1; ++i)
+      if (avg <= pol.bound[i]) { c = i; break; }
+    pol.forced = c;
+  }
+  return pol;
+}
+
+mxq_status run_moe(const void* x, int64_t M, int64_t H, int64_t I, int32_t E, int32_t topk, const int32_t* ids,
+                   const float* wts, const void* w1, const void* w1s, const void* w2, const void* w2s,
+                   const float* b1, int wfmt, bool act_quant, void* out, void* ws, size_t ws_bytes,
+                   hipStream_t st) {
+  const int64_t R = M * topk;
+  if (R == 0) return MXQ_OK;
+  const int64_t mbk = mxq_moe_max_blocks(M, topk, E, kMoeBlockM);
+  MoeWorkspace w = carve_moe(ws, M, H, I, E, topk, act_quant);
+  if (!ws || ws_bytes < w.bytes) return MXQ_ERR_WORKSPACE;
+  const ClassPolicy pol = make_policy(R, E);
+
+  launch_moe_align(ids, M, topk, E, kMoeBlockM, w.sorted_ids, w.expert_ids, w.offsets, w.num_blocks, mbk, pol,
+                   w.class_lists, mbk, w.class_counts, st);
+  if (act_quant) launch_quant_1x128(static_cast<const uint16_t*>(x), M, H, H, w.qx, H, w.sx, st);
+
+  const bool mx = wfmt == W_E2M1_MX;
+  BlockRouting rt{w.sorted_ids, w.expert_ids, w.offsets, nullptr, nullptr, kMoeBlockM, topk};
+
+  // stage 1: ic0 = x @ w1^T (+ b1), compact rows
+  GemmArgs g1{};
+  g1.A = act_quant ? static_cast<const void*>(w.qx) : x;
+  g1.lda = H;
+  g1.sa = w.sx;
+  g1.lds = H / 128;
+  g1.W = static_cast<const uint8_t*>(w1);
+  g1.ldw = mx ? H / 2 : H;
+  g1.w_estride = g1.ldw * 2 * I;
+  g1.ws = w1s;
+  if (mx) {
+    g1.ws_s0 = H / 32;
+    g1.ws_estride = 2 * I * (H / 32);
+  } else {
+    g1.ws_s0 = H / 128;
+    g1.ws_s1 = 1;
+    g1.ws_estride = cdiv(2 * I, 128) * (H / 128);
+  }
+  g1.block_n = 128;
+  g1.bias = b1;
+  g1.bias_bf16 = 0;
+  g1.bias_estride = 2 * I;
+  g1.out = w.ic0;
+  g1.ldo = 2 * I;
+  g1.M = R;
+  g1.N = 2 * I;
+  g1.K = H;
+  g1.rt = rt;
+
+  // stage 2: y = ic1 @ w2^T, rows scattered back to flat ids
+  GemmArgs g2{};
+  g2.A = act_quant ? static_cast<const void*>(w.ic1_q) : static_cast<const void*>(w.ic1);
+  g2.lda = I;
+  g2.sa = w.ic1_s;
+  g2.lds = I / 128;
+  g2.W = static_cast<const uint8_t*>(w2);
+  g2.ldw = mx ? I / 2 : I;
+  g2.w_estride = g2.ldw * H;
+  g2.ws = w2s;
+  if (mx) {
+    g2.ws_s0 = I / 32;
+    g2.ws_estride = H * (I / 32);
+  } else {
+    g2.ws_s0 = I / 128;
+    g2.ws_s1 = 1;
+    g2.ws_estride = cdiv(H, 128) * (I / 128);
+  }
+  g2.block_n = 128;
+  g2.out = w.y;
+  g2.ldo = H;
+  g2.M = R;
+  g2.N = H;
+  g2.K = I;
+  g2.rt = rt;
+
+  const int wfmt_w16 = mx ? W_E2M1_MX : W_E4M3_BLOCK;
+  for (int stage = 0; stage < 2; ++stage) {
+    if (stage == 1) launch_silu_mul(w.ic0, R, I, w.ic1, w.ic1_q, w.ic1_s, st);
+    GemmArgs& g = stage == 0 ? g1 : g2;
+    const int mode = stage == 0 ? ROWS_GATHER_TOK : ROWS_COMPACT_IN;
+    const bool out_f32 = stage == 1;
+    for (int c = 0; c < kNumClasses; ++c) {
+      const int64_t ub = class_bound(c, R, E, mbk, pol);
+      if (ub <= 0) continue;
+      g.rt.work_list = w.class_lists + int64_t(c) * mbk;
+      g.rt.work_count = w.class_counts + c;
+      if (c == 0)
+        launch_gemv(g, wfmt_w16, act_quant, mode, out_f32, ub, st);
+      else if (act_quant)
+        launch_gemm_w8a8(g, mode, kClassTile[c], out_f32, ub, st);
+      else
+        launch_gemm_w16(g, wfmt_w16, mode, kClassTile[c], out_f32, ub, st);
+    }
+  }
+  launch_combine(w.y, wts, ids, E, M, topk, H, static_cast<uint16_t*>(out), st);
+  return launch_status();
+}
+
+int dense_tile_for(int64_t M) { return M <= 16 ? 3 : M <= 32 ? 2 : M <= 64 ? 1 : 0; }
+int64_t tile_rows(int tile) { return tile == 0 ? 128 : tile == 1 ? 64 : tile == 2 ? 32 : 16; }
+
+}  // namespace
+
+extern "C" {
+
+const char* mxq_status_string(mxq_status s) {
+  switch (s) {
+    case MXQ_OK: return "ok";
+    case MXQ_ERR_NULL: return "a required pointer is NULL";
+    case MXQ_ERR_SHAPE: return "unsupported sizes, strides or alignment";
+    case MXQ_ERR_BLOCK: return "block size must be [1,128] or [128,128] (group 128)";
+    case MXQ_ERR_DTYPE: return "unsupported dtype";
+    case MXQ_ERR_WORKSPACE: return "workspace missing or too small";
+    case MXQ_ERR_ARCH: return "the current device is not gfx950 (MI355X)";
+    case MXQ_ERR_LAUNCH: return "kernel launch failed";
+    case MXQ_ERR_ARG: return "invalid argument";
+    default: return "unknown status";
+  }
+}
+
+int32_t mxq_abi_version(void) { return 1; }
+
+mxq_status mxq_init(int32_t device) {
+  if (hipSetDevice(device) != hipSuccess) return MXQ_ERR_ARCH;
+  return check_arch();
+}
+
+mxq_status mxq_per_token_group_quant_fp8(const void* x, int64_t M, int64_t K, int64_t ldx, int32_t group, void* q,
+                                         float* s, void* stream) {
+  if (group != 128) return MXQ_ERR_BLOCK;
+  if (M < 0 || K < 0 || K % 128 != 0 || ldx < K || ldx % 8 != 0) return MXQ_ERR_SHAPE;
+  if (M == 0 || K == 0) return MXQ_OK;
+  if (!x || !q || !s) return MXQ_ERR_NULL;
+  if (!aligned16(x) || (reinterpret_cast<uintptr_t>(q) & 7u)) return MXQ_ERR_SHAPE;
+  MXQ_TRY(check_arch());
+  launch_quant_1x128(static_cast<const uint16_t*>(x), M, K, ldx, static_cast<uint8_t*>(q), K, s,
+                     static_cast<hipStream_t>(stream));
+  return launch_status();
+}
+
+mxq_status mxq_fp8_scaled_mm(const void* A, int64_t M, int64_t K, int64_t lda, const void* W, int64_t N,
+                             const float* scale, const void* bias, int32_t bias_dtype, void* out, int64_t ldo,
+                             void* stream) {
+  if (M < 0 || N < 0 || K < 0 || K % 32 != 0 || lda < K || lda % 8 != 0 || ldo < N) return MXQ_ERR_SHAPE;
+  if (bias && bias_dtype != MXQ_DTYPE_F32 && bias_dtype != MXQ_DTYPE_BF16) return MXQ_ERR_DTYPE;
+  if (M == 0 || N == 0) return MXQ_OK;
+  if (!A || !W || !scale || !out) return MXQ_ERR_NULL;
+  if (!aligned16(A) || !aligned16(W)) return MXQ_ERR_SHAPE;
+  MXQ_TRY(check_arch());
+  GemmArgs g{};
+  g.A = A;
+  g.lda = lda;
+  g.W = static_cast<const uint8_t*>(W);
+  g.ldw = K;
+  g.ws = scale;
+  g.bias = bias;
+  g.bias_bf16 = bias_dtype == MXQ_DTYPE_BF16;
+  g.out = out;
+  g.ldo = ldo;
+  g.M = M;
+  g.N = N;
+  g.K = K;
+  const int tile = dense_tile_for(M);
+  launch_gemm_w16(g, W_E4M3_TENSOR, ROWS_DENSE, tile, false, cdiv(M, tile_rows(tile)),
+                  static_cast<hipStream_t>(stream));
+  return launch_status();
+}
+
+size_t mxq_block_fp8_linear_workspace_size(int64_t M, int64_t K, int32_t a_dtype) {
+  if (a_dtype != MXQ_DTYPE_BF16 || M <= 0 || K <= 0) return 0;
+  return align256(size_t(M) * K) + align256(sizeof(float) * M * (K / 128));
+}
+
+mxq_status mxq_block_fp8_linear(const void* A, int32_t a_dtype, const float* a_scale, int64_t M, int64_t K,
+                                int64_t lda, const void* W, int64_t N, const float* w_scale, int64_t ws_stride0,
+                                int64_t ws_stride1, int32_t block_n, int32_t block_k, const void* bias,
+                                int32_t bias_dtype, void* out, int64_t ldo, void* workspace, size_t workspace_bytes,
+                                void* stream) {
+  if (block_k != 128 || (block_n != 1 && block_n != 128)) return MXQ_ERR_BLOCK;
+  if (a_dtype != MXQ_DTYPE_BF16 && a_dtype != MXQ_DTYPE_E4M3) return MXQ_ERR_DTYPE;
+  if (bias && bias_dtype != MXQ_DTYPE_F32 && bias_dtype != MXQ_DTYPE_BF16) return MXQ_ERR_DTYPE;
+  if (M < 0 || N < 0 || K < 0 || K % 128 != 0 || lda < K || ldo < N) return MXQ_ERR_SHAPE;
+  if (a_dtype == MXQ_DTYPE_BF16 ? (lda % 8 != 0) : (lda % 16 != 0)) return MXQ_ERR_SHAPE;
+  if (M == 0 || N == 0) return MXQ_OK;
+  if (!A || !W || !w_scale || !out) return MXQ_ERR_NULL;
+  if (a_dtype == MXQ_DTYPE_E4M3 && !a_scale) return MXQ_ERR_NULL;
+  if (!aligned16(A) || !aligned16(W)) return MXQ_ERR_SHAPE;
+  if (K == 0) return MXQ_ERR_SHAPE;
+  MXQ_TRY(check_arch());
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const uint8_t* qa = static_cast<const uint8_t*>(A);
+  const float* sa = a_scale;
+  int64_t lqa = lda;
+  if (a_dtype == MXQ_DTYPE_BF16) {
+    const size_t need = mxq_block_fp8_linear_workspace_size(M, K, a_dtype);
+    if (!workspace || workspace_bytes < need) return MXQ_ERR_WORKSPACE;
+    uint8_t* q = static_cast<uint8_t*>(workspace);
+    float* s = reinterpret_cast<float*>(q + align256(size_t(M) * K));
+    launch_quant_1x128(static_cast<const uint16_t*>(A), M, K, lda, q, K, s, st);
+    qa = q;
+    sa = s;
+    lqa = K;
+  }
+  GemmArgs g{};
+  g.A = qa;
+  g.lda = lqa;
+  g.sa = sa;
+  g.lds = K / 128;
+  g.W = static_cast<const uint8_t*>(W);
+  g.ldw = K;
+  g.ws = w_scale;
+  g.ws_s0 = ws_stride0;
+  g.ws_s1 = ws_stride1;
+  g.block_n = block_n;
+  g.bias = bias;
+  g.bias_bf16 = bias_dtype == MXQ_DTYPE_BF16;
+  g.out = out;
+  g.ldo = ldo;
+  g.M = M;
+  g.N = N;
+  g.K = K;
+  const int tile = dense_tile_for(M);
+  launch_gemm_w8a8(g, ROWS_DENSE, tile, false, cdiv(M, tile_rows(tile)), st);
+  return launch_status();
+}
+
+int64_t mxq_moe_max_blocks(int64_t M, int32_t topk, int32_t E, int32_t block_m) {
+  if (M < 0 || topk <= 0 || E <= 0 || block_m <= 0) return 0;
+  const int64_t R = M * topk;
+  return cdiv(R, block_m) + std::min<int64_t>(E, R);
+}
+
+mxq_status mxq_moe_align(const int32_t* topk_ids, int64_t M, int32_t topk, int32_t E, int32_t block_m,
+                         int32_t* sorted_ids, int32_t* expert_ids, int32_t* offsets, int32_t* num_blocks,
+                         void* stream) {
+  if (M < 0 || topk <= 0 || E <= 0 || E > 512 || block_m <= 0 || block_m > 1024) return MXQ_ERR_SHAPE;
+  if (!offsets || !num_blocks || (M > 0 && (!topk_ids || !sorted_ids || !expert_ids))) return MXQ_ERR_NULL;
+  MXQ_TRY(check_arch());
+  ClassPolicy pol{};
+  pol.n_classes = 0;
+  pol.forced = -1;
+  launch_moe_align(topk_ids, M, topk, E, block_m, sorted_ids, expert_ids, offsets, num_blocks,
+                   mxq_moe_max_blocks(M, topk, E, block_m), pol, nullptr, 0, nullptr,
+                   static_cast<hipStream_t>(stream));
+  return launch_status();
+}
+
+size_t mxq_fused_moe_workspace_size(int64_t M, int64_t H, int64_t I, int32_t E, int32_t topk, int32_t weights,
+                                    int32_t act_quant) {
+  if (M <= 0 || H <= 0 || I <= 0 || E <= 0 || topk <= 0) return 0;
+  (void)weights;
+  return carve_moe(nullptr, M, H, I, E, topk, act_quant != 0).bytes;
+}
+
+static mxq_status moe_common_checks(const void* x, int64_t M, int64_t H, int64_t I, int32_t E, int32_t topk,
+                                    const int32_t* ids, const float* wts, const void* w1, const void* w1s,
+                                    const void* w2, const void* w2s, void* out) {
+  if (M < 0 || H <= 0 || I <= 0 || E <= 0 || E > 512 || topk <= 0 || topk > E) return MXQ_ERR_SHAPE;
+  if (M == 0) return MXQ_OK;
+  if (!x || !ids || !wts || !w1 || !w1s || !w2 || !w2s || !out) return MXQ_ERR_NULL;
+  if (!aligned16(x) || !aligned16(w1) || !aligned16(w2) || !aligned16(out)) return MXQ_ERR_SHAPE;
+  return check_arch();
+}
+
+mxq_status mxq_fused_moe_fp8(const void* x, int64_t M, int64_t H, int64_t I, int32_t E, int32_t topk,
+                             const int32_t* topk_ids, const float* topk_weights, const void* w1,
+                             const float* w1_scale, const void* w2, const float* w2_scale, const float* w1_bias,
+                             int32_t act_quant, void* out, void* workspace, size_t workspace_bytes, void* stream) {
+  if (H % 128 != 0 || I % 128 != 0) return MXQ_ERR_SHAPE;
+  if (act_quant != 0 && act_quant != 1) return MXQ_ERR_ARG;
+  MXQ_TRY(moe_common_checks(x, M, H, I, E, topk, topk_ids, topk_weights, w1, w1_scale, w2, w2_scale, out));
+  if (M == 0) return MXQ_OK;
+  return run_moe(x, M, H, I, E, topk, topk_ids, topk_weights, w1, w1_scale, w2, w2_scale, w1_bias, W_E4M3_BLOCK,
+                 act_quant != 0, out, workspace, workspace_bytes, static_cast<hipStream_t>(stream));
+}
+
+mxq_status mxq_fused_moe_mxfp4(const void* x, int64_t M, int64_t H, int64_t I, int32_t E, int32_t topk,
+                               const int32_t* topk_ids, const float* topk_weights, const void* w1,
+                               const void* w1_scale, const void* w2, const void* w2_scale, const float* w1_bias,
+                               void* out, void* workspace, size_t workspace_bytes, void* stream) {
+  if (H % 32 != 0 || I % 32 != 0) return MXQ_ERR_SHAPE;
+  MXQ_TRY(moe_common_checks(x, M, H, I, E, topk, topk_ids, topk_weights, w1, w1_scale, w2, w2_scale, out));
+  if (M == 0) return MXQ_OK;
+  return run_moe(x, M, H, I, E, topk, topk_ids, topk_weights, w1, w1_scale, w2, w2_scale, w1_bias, W_E2M1_MX, false,
+                 out, workspace, workspace_bytes, static_cast<hipStream_t>(stream));
+}
+
+mxq_status mxq_moe_set_dispatch(int32_t mode, int32_t forced_class, int32_t gemv_max_rows) {
+  if (mode < MXQ_DISPATCH_PER_BLOCK || mode > MXQ_DISPATCH_LAYER_AVERAGE) return MXQ_ERR_ARG;
+  if (forced_class < 0 || forced_class >= kNumClasses) return MXQ_ERR_ARG;
+  if (gemv_max_rows < 0 || gemv_max_rows > 4) return MXQ_ERR_ARG;
+  std::lock_guard<std::mutex> lk(g_dispatch_mu);
+  g_dispatch_mode = mode;
+  g_forced_class = forced_class;
+  g_gemv_max_rows = gemv_max_rows;
+  return MXQ_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,264 @@
+// bf16-activation GEMMs with FP8 or MXFP4 weights on the gfx950 bf16 matrix cores.
+//
+// * W8A16 per-tensor ("SGLang PR 32618 review", implementation items 1-2):
+//   out = bf16((A @ dec(W)^T) * s + bias).  The scale is applied once after the
+//   K loop, which equals applying it per K block (every block scale is the
+//   same constant).
+// * W8A16 block-scaled experts ("vLLM PR 50949 review", moe_fp8.cpp listing):
+//   each 128-wide K block's partial sum is multiplied by its weight-block scale
+//   before it is added to the accumulator.
+// * W4A16 MXFP4 experts (same listing, MXFP4 weights): the e8m0 scale of each
+//   32-element group is a power of two, so it is folded into the exact
+//   e2m1 -> bf16 decode and no promotion step is needed.
+//
+// Weights are decoded to bf16 in registers right after their LDS fragment read
+// (e4m3 and scaled e2m1 values are exact in bf16); V_MFMA_F32_16X16X32_BF16
+// accumulates in fp32.  A is staged through LDS; K may end on any multiple of
+// 32 (the tail of the last 128-wide step is zero-filled on both operands).
+#include "tile_rows.hpp"
+
+namespace mxq {
+
+template <int WFMT>
+struct W16Layout {
+  // bytes of one weight row per 128-wide K step, and the padded LDS row
+  static constexpr int row_bytes = (WFMT == W_E2M1_MX) ? 64 : 128;
+  static constexpr int lds_row = row_bytes + 16;
+  static constexpr int chunks = row_bytes / 16;  // 16-byte chunks per row
+};
+
+template <int BM, int BN, int WAVES_M, int MODE, int WFMT, bool OUT_F32, bool HAS_BIAS>
+__global__ __launch_bounds__(256) void gemm_w16_kernel(GemmArgs a, int64_t grid_blocks) {
+  constexpr int WAVES_N = 4 / WAVES_M;
+  constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
+  constexpr int TM = WM / 16, TN = WN / 16;
+  static_assert(TM >= 1 && TN >= 1, "wave tile smaller than one MFMA tile");
+  using L = W16Layout<WFMT>;
+  constexpr int A_LROW = 256 + 16;  // 128 bf16 + pad
+  constexpr int A_IT = (BM * 16 + 255) / 256;
+  constexpr int B_IT = (BN * L::chunks + 255) / 256;
+  constexpr bool MX = WFMT == W_E2M1_MX;
+
+  __shared__ __align__(16) uint8_t sA[BM * A_LROW];
+  __shared__ __align__(16) uint8_t sB[BN * L::lds_row];
+  __shared__ uint32_t sBs[MX ? BN : 1];
+  __shared__ int64_t sArow[BM];
+  __shared__ int64_t sOrow[BM];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave / WAVES_N, wn = wave % WAVES_N;
+  const int64_t tile = blockIdx.x % grid_blocks;
+  const int64_t nt = blockIdx.x / grid_blocks;
+  const int64_t n0 = nt * BN;
+  if (n0 >= a.N) return;
+
+  TileInfo t;
+  if (!tile_info<BM, MODE>(a, tile, t)) return;
+  const int64_t expert = t.expert;
+  for (int m_base = 0; m_base < t.m_total; m_base += BM) {
+  const int m_size = min(BM, t.m_total - m_base);
+  __syncthreads();
+  fill_rows<BM, MODE>(a, t, m_base, sArow, sOrow);
+  __syncthreads();
+
+  const uint16_t* A = reinterpret_cast<const uint16_t*>(a.A);
+  const uint8_t* Wb = a.W + expert * a.w_estride;
+  const int KS = int(cdiv(a.K, 128));
+
+  const uint16_t* pa[A_IT];
+  int ka[A_IT];
+  const uint8_t* pb[B_IT];
+  int kbo[B_IT];
+#pragma unroll
+  for (int i = 0; i < A_IT; ++i) {
+    const int c = min(tid + 256 * i, BM * 16 - 1);
+    ka[i] = (c & 15) * 8;
+    pa[i] = A + sArow[c >> 4] * a.lda + ka[i];
+  }
+#pragma unroll
+  for (int i = 0; i < B_IT; ++i) {
+    const int c = min(tid + 256 * i, BN * L::chunks - 1);
+    const int64_t n = min<int64_t>(n0 + c / L::chunks, a.N - 1);
+    kbo[i] = (c % L::chunks) * (MX ? 32 : 16);  // first K element of the chunk
+    pb[i] = Wb + n * a.ldw + (c % L::chunks) * 16;
+  }
+  const uint8_t* pbs = nullptr;
+  if (MX) {
+    const int64_t n = min<int64_t>(n0 + min(tid, BN - 1), a.N - 1);
+    pbs = reinterpret_cast<const uint8_t*>(a.ws) + expert * a.ws_estride + n * a.ws_s0;
+  }
+
+  uint4 ra[A_IT], rb[B_IT];
+  uint32_t rbs = 0;
+  auto gload = [&](int ks) __attribute__((always_inline)) {
+    const int64_t kbase = int64_t(ks) * 128;
+#pragma unroll
+    for (int i = 0; i < A_IT; ++i)
+      ra[i] = (kbase + ka[i] < a.K) ? *reinterpret_cast<const uint4*>(pa[i] + kbase) : make_uint4(0, 0, 0, 0);
+#pragma unroll
+    for (int i = 0; i < B_IT; ++i)
+      rb[i] = (kbase + kbo[i] < a.K) ? *reinterpret_cast<const uint4*>(pb[i] + kbase * L::row_bytes / 128)
+                                     : make_uint4(0, 0, 0, 0);
+    if (MX && tid < BN) {
+      const int g0 = ks * 4;  // first 32-group of this step
+      uint32_t v = 0;
+      const int ngrp = int(a.K >> 5);
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+        if (g0 + g < ngrp) v |= uint32_t(pbs[g0 + g]) << (8 * g);
+      rbs = v;
+    }
+  };
+  auto lstore = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < A_IT; ++i) {
+      const int c = tid + 256 * i;
+      if (A_IT * 256 == BM * 16 || c < BM * 16)
+        *reinterpret_cast<uint4*>(sA + (c >> 4) * A_LROW + (c & 15) * 16) = ra[i];
+    }
+#pragma unroll
+    for (int i = 0; i < B_IT; ++i) {
+      const int c = tid + 256 * i;
+      if (B_IT * 256 == BN * L::chunks || c < BN * L::chunks)
+        *reinterpret_cast<uint4*>(sB + (c / L::chunks) * L::lds_row + (c % L::chunks) * 16) = rb[i];
+    }
+    if (MX && tid < BN) sBs[tid] = rbs;
+  };
+
+  f32x4 acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const int frow = lane & 15;
+  const int fq = lane >> 4;  // which 8-element K slice of a 32-wide MFMA step
+  const float* swb = reinterpret_cast<const float*>(a.ws) + expert * a.ws_estride;
+  const int64_t nb_scale = n0 / 128;
+
+  gload(0);
+  for (int ks = 0; ks < KS; ++ks) {
+    __syncthreads();
+    lstore();
+    __syncthreads();
+    if (ks + 1 < KS) gload(ks + 1);
+
+    const int nsub = int(min<int64_t>(4, (a.K - int64_t(ks) * 128) >> 5));
+    f32x4 part[TM][TN];
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j) part[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      if (s >= nsub) break;
+      i32x4 af[TM], bfr[TN];
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+        af[i] = *reinterpret_cast<const i32x4*>(sA + (wm * WM + 16 * i + frow) * A_LROW + (s * 32 + fq * 8) * 2);
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        const int brow = wn * WN + 16 * j + frow;
+        if (MX) {
+          const uint32_t v = *reinterpret_cast<const uint32_t*>(sB + brow * L::lds_row + s * 16 + fq * 4);
+          const float sc = e8m0_to_f32((sBs[brow] >> (8 * s)) & 0xffu);
+          uint32_t o[4];
+          e2m1x8_to_bf16(v, sc, o);
+          bfr[j] = i32x4{int(o[0]), int(o[1]), int(o[2]), int(o[3])};
+        } else {
+          const uint2 v = *reinterpret_cast<const uint2*>(sB + brow * L::lds_row + s * 32 + fq * 8);
+          uint32_t o0, o1, o2, o3;
+          e4m3x4_to_bf16(v.x, o0, o1);
+          e4m3x4_to_bf16(v.y, o2, o3);
+          bfr[j] = i32x4{int(o0), int(o1), int(o2), int(o3)};
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+          if (WFMT == W_E4M3_BLOCK)
+            part[i][j] = mfma_16x16x32_bf16(af[i], bfr[j], part[i][j]);
+          else
+            acc[i][j] = mfma_16x16x32_bf16(af[i], bfr[j], acc[i][j]);
+        }
+    }
+    if (WFMT == W_E4M3_BLOCK) {
+      const float sw = swb[nb_scale * a.ws_s0 + ks * a.ws_s1];
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) acc[i][j][r] = fmaf(part[i][j][r], sw, acc[i][j][r]);
+    }
+  }
+
+  const float tscale = (WFMT == W_E4M3_TENSOR) ? reinterpret_cast<const float*>(a.ws)[0] : 1.f;
+#pragma unroll
+  for (int j = 0; j < TN; ++j) {
+    const int64_t col = n0 + wn * WN + 16 * j + frow;
+    if (col >= a.N) continue;
+    const float b = HAS_BIAS ? load_bias(a, expert, col) : 0.f;
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int rl = wm * WM + 16 * i + 4 * (lane >> 4) + r;
+        if (rl >= m_size) continue;
+        float v = acc[i][j][r];
+        if (WFMT == W_E4M3_TENSOR) v = v * tscale;
+        v = v + b;
+        const int64_t orow = sOrow[rl];
+        if (OUT_F32)
+          reinterpret_cast<float*>(a.out)[orow * a.ldo + col] = v;
+        else
+          reinterpret_cast<uint16_t*>(a.out)[orow * a.ldo + col] = f2bf(v);
+      }
+  }
+  }  // m sub-tiles
+}
+
+template <int BM, int BN, int WAVES_M, int MODE, int WFMT>
+static void launch_w16_t(const GemmArgs& a, bool out_f32, int64_t grid_blocks, hipStream_t st) {
+  const int64_t n_tiles = cdiv(a.N, BN);
+  const dim3 grid(unsigned(grid_blocks * n_tiles)), block(256);
+  const bool bias = a.bias != nullptr;
+#define MXQ_W16_GO(OF, HB) \
+  hipLaunchKernelGGL((gemm_w16_kernel<BM, BN, WAVES_M, MODE, WFMT, OF, HB>), grid, block, 0, st, a, grid_blocks)
+  if (out_f32) { if (bias) MXQ_W16_GO(true, true); else MXQ_W16_GO(true, false); }
+  else { if (bias) MXQ_W16_GO(false, true); else MXQ_W16_GO(false, false); }
+#undef MXQ_W16_GO
+}
+
+template <int MODE, int WFMT>
+static void launch_w16_mode(const GemmArgs& a, int tile, bool out_f32, int64_t gb, hipStream_t st) {
+  switch (tile) {
+    case 0: launch_w16_t<128, 128, 2, MODE, WFMT>(a, out_f32, gb, st); break;
+    case 1: launch_w16_t<64, 128, 2, MODE, WFMT>(a, out_f32, gb, st); break;
+    case 2: launch_w16_t<32, 128, 1, MODE, WFMT>(a, out_f32, gb, st); break;
+    default: launch_w16_t<16, 128, 1, MODE, WFMT>(a, out_f32, gb, st); break;
+  }
+}
+
+template <int MODE>
+static void launch_w16_fmt(const GemmArgs& a, int wfmt, int tile, bool out_f32, int64_t gb, hipStream_t st) {
+  switch (wfmt) {
+    case W_E4M3_BLOCK: launch_w16_mode<MODE, W_E4M3_BLOCK>(a, tile, out_f32, gb, st); break;
+    case W_E4M3_TENSOR: launch_w16_mode<MODE, W_E4M3_TENSOR>(a, tile, out_f32, gb, st); break;
+    default: launch_w16_mode<MODE, W_E2M1_MX>(a, tile, out_f32, gb, st); break;
+  }
+}
+
+void launch_gemm_w16(const GemmArgs& a, int wfmt, int row_mode, int tile, bool out_f32, int64_t grid_blocks,
+                     hipStream_t stream) {
+  if (grid_blocks <= 0 || a.N <= 0) return;
+  switch (row_mode) {
+    case ROWS_DENSE: launch_w16_fmt<ROWS_DENSE>(a, wfmt, tile, out_f32, grid_blocks, stream); break;
+    case ROWS_GATHER_TOK: launch_w16_fmt<ROWS_GATHER_TOK>(a, wfmt, tile, out_f32, grid_blocks, stream); break;
+    default: launch_w16_fmt<ROWS_COMPACT_IN>(a, wfmt, tile, out_f32, grid_blocks, stream); break;
+  }
+}
+
+}  // namespace mxq

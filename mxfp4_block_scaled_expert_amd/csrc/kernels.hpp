@@ -1,0 +1,99 @@
+// Internal interface between the C-ABI layer (api.hip) and the kernel files.
+#pragma once
+
+#include "common.hpp"
+
+namespace mxq {
+
+// Which rows a GEMM tile reads and writes.
+enum RowMode : int {
+  ROWS_DENSE = 0,      // tile rows m0 .. m0+BM of a plain [M, K] operand
+  ROWS_GATHER_TOK = 1, // routed block: A row = sorted_ids[..] / topk, out row = offsets[mb] + i
+  ROWS_COMPACT_IN = 2, // routed block: A row = offsets[mb] + i, out row = sorted_ids[..]
+};
+
+// Weight formats.
+enum WFmt : int {
+  W_E4M3_BLOCK = 0,   // e4m3 + fp32 scale per (block_n x 128) block
+  W_E4M3_TENSOR = 1,  // e4m3 + one fp32 scale (device scalar)
+  W_E2M1_MX = 2,      // packed e2m1 + e8m0 scale per row per 32 columns
+};
+
+// Routed-block description shared by every MoE stage kernel.
+struct BlockRouting {
+  const int32_t* sorted_ids;  // [max_blocks * block_m]
+  const int32_t* expert_ids;  // [max_blocks]
+  const int32_t* offsets;     // [max_blocks + 1]
+  const int32_t* work_list;   // block ids of this tile class
+  const int32_t* work_count;  // device scalar: number of valid entries
+  int32_t block_m;
+  int32_t topk;
+};
+
+struct GemmArgs {
+  // activations
+  const void* A;        // bf16 or e4m3 rows
+  int64_t lda;          // elements (bf16) or bytes (e4m3)
+  const float* sa;      // e4m3 activations: [rows, K/128] fp32
+  int64_t lds;          // row stride of sa (elements)
+  // weights (per expert: base + e * w_estride)
+  const uint8_t* W;
+  int64_t ldw;          // bytes per weight row
+  int64_t w_estride;    // bytes per expert
+  const void* ws;       // fp32 block grid | fp32 scalar | e8m0 [N, K/32] bytes
+  int64_t ws_s0, ws_s1; // grid strides (elements); for e8m0: row stride (bytes)
+  int64_t ws_estride;   // per expert (elements or bytes)
+  int32_t block_n;      // 1 or 128 for W_E4M3_BLOCK
+  // bias (optional)
+  const void* bias;
+  int32_t bias_bf16;    // 1: bf16 bias, 0: fp32 bias
+  int64_t bias_estride; // elements per expert
+  // output
+  void* out;
+  int64_t ldo;          // elements
+  int64_t M, N, K;
+  BlockRouting rt;
+};
+
+// ---------------------------------------------------------------- launchers
+
+void launch_quant_1x128(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, uint8_t* q, int64_t ldq,
+                        float* s, hipStream_t stream);
+
+// W8A8: e4m3 activations with 1x128 scales x e4m3 block-scaled weights (MFMA 16x16x128).
+// tile: 0 = 128x128, 1 = 64x128, 2 = 32x128, 3 = 16x128.  `grid_blocks` is the number of
+// row tiles (dense) or the work-list capacity (routed); out_f32 selects an fp32 output.
+void launch_gemm_w8a8(const GemmArgs& a, int row_mode, int tile, bool out_f32, int64_t grid_blocks,
+                      hipStream_t stream);
+
+// W8A16 / W4A16: bf16 activations x decoded e4m3 / e2m1 weights (MFMA 16x16x32 bf16).
+void launch_gemm_w16(const GemmArgs& a, int wfmt, int row_mode, int tile, bool out_f32, int64_t grid_blocks,
+                     hipStream_t stream);
+
+// Wavefront-reduction GEMV for routed blocks of at most 4 rows.
+// a_e4m3: activations are e4m3 + 1x128 scales (W8A8), else bf16.
+void launch_gemv(const GemmArgs& a, int wfmt, bool a_e4m3, int row_mode, bool out_f32, int64_t grid_blocks,
+                 hipStream_t stream);
+
+// Expert sort / block alignment.  Optionally also fills per-class work lists
+// (class_lists[c * list_stride + i], class_counts[c]) using the per-block selector.
+struct ClassPolicy {
+  int32_t n_classes;      // 0: no class lists
+  int32_t bound[8];       // class c takes blocks with bound[c-1] < m_size <= bound[c]
+  int32_t forced;         // >= 0: every non-empty block goes to this class
+};
+void launch_moe_align(const int32_t* topk_ids, int64_t M, int32_t topk, int32_t E, int32_t block_m,
+                      int32_t* sorted_ids, int32_t* expert_ids, int32_t* offsets, int32_t* num_blocks,
+                      int64_t max_blocks, const ClassPolicy& pol, int32_t* class_lists, int64_t list_stride,
+                      int32_t* class_counts, hipStream_t stream);
+
+// ic1 = bf16(silu(gate) * up) over compact rows; optionally re-quantised 1x128 to e4m3.
+void launch_silu_mul(const uint16_t* ic0, int64_t rows, int64_t inter, uint16_t* ic1_bf16, uint8_t* ic1_q,
+                     float* ic1_s, hipStream_t stream);
+
+// out[t] = bf16(sum_k w[t,k] * y[t*topk+k]).
+// Rows whose expert id lies outside [0, E) are skipped.
+void launch_combine(const float* y, const float* topk_weights, const int32_t* topk_ids, int32_t E, int64_t M,
+                    int32_t topk, int64_t H, uint16_t* out, hipStream_t stream);
+
+}  // namespace mxq

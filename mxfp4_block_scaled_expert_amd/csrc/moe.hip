@@ -1,0 +1,273 @@
+// Routed-MoE support kernels: expert sort / block alignment with the per-block
+// tile-class selector, SiLU-and-mul (with the W8A8 1x128 re-quantisation) and
+// the top-k weighted combine.
+//
+// Alignment ("vLLM PR 50949 review", moe_fp8.cpp listing, and implementation
+// items 2-3): the fused expert kernels walk blocks of at most BLOCK_M rows of
+// one expert; expert_ids[mb], offsets[mb] (compact row prefix; the block holds
+// offsets[mb+1] - offsets[mb] rows and an empty block is skipped) and
+// sorted_ids[mb * BLOCK_M + m] (flat routed id t * topk + k) describe them.
+// The layout produced here: experts in ascending id, rows of one expert in
+// ascending flat id (a stable counting sort), pad value R in unused slots,
+// trailing blocks with expert -1 and offset R.  The whole sort runs in one
+// 1024-thread workgroup with no host synchronisation; ranks inside a wave come
+// from ballots over the bits of the expert id, so the order is deterministic.
+//
+// The per-block selector (implementation items 1-2: the decision is taken per
+// expert block from its real row count, not once per layer from an average)
+// assigns every non-empty block to the smallest tile class whose row bound
+// holds it and appends the block id to that class's work list.
+#include "kernels.hpp"
+#include "quant_common.hpp"
+
+namespace mxq {
+
+constexpr int kAlignThreads = 1024;
+constexpr int kAlignWaves = kAlignThreads / 64;
+
+__device__ __forceinline__ int pick_class(const ClassPolicy& pol, int m_size) {
+  if (pol.forced >= 0) return pol.forced;
+  for (int c = 0; c < pol.n_classes - 1; ++c)
+    if (m_size <= pol.bound[c]) return c;
+  return pol.n_classes - 1;
+}
+
+__global__ __launch_bounds__(kAlignThreads) void moe_align_kernel(
+    const int32_t* __restrict__ ids, int64_t R, int32_t E, int32_t block_m, int32_t* __restrict__ sorted_ids,
+    int32_t* __restrict__ expert_ids, int32_t* __restrict__ offsets, int32_t* __restrict__ num_blocks,
+    int64_t max_blocks, ClassPolicy pol, int32_t* __restrict__ class_lists, int64_t list_stride,
+    int32_t* __restrict__ class_counts) {
+  extern __shared__ int32_t smem[];
+  int32_t* cnt = smem;                     // [E]
+  int32_t* blk_start = cnt + E;            // [E + 1]
+  int32_t* row_start = blk_start + E + 1;  // [E + 1]
+  int32_t* running = row_start + E + 1;    // [E]
+  int32_t* wave_cnt = running + E;         // [kAlignWaves][E]
+  __shared__ int32_t cls_cnt[8];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  for (int e = tid; e < E; e += kAlignThreads) {
+    cnt[e] = 0;
+    running[e] = 0;
+  }
+  if (tid < 8) cls_cnt[tid] = 0;
+  __syncthreads();
+
+  // 1. histogram (expert ids outside [0, E) are ignored)
+  for (int64_t r = tid; r < R; r += kAlignThreads) {
+    const int e = ids[r];
+    if (e >= 0 && e < E) atomicAdd(&cnt[e], 1);
+  }
+  __syncthreads();
+
+  // 2. exclusive scans of blocks and rows per expert (each thread owns a run of experts)
+  {
+    const int per = int(cdiv(E, kAlignThreads));
+    const int e0 = min(E, tid * per), e1 = min(E, e0 + per);
+    int nb = 0, nr = 0;
+    for (int e = e0; e < e1; ++e) {
+      nb += (cnt[e] + block_m - 1) / block_m;
+      nr += cnt[e];
+    }
+    // wave-level inclusive scan of (nb, nr)
+    int sb = nb, sr = nr;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int tb = __shfl_up(sb, o, 64), tr = __shfl_up(sr, o, 64);
+      if (lane >= o) {
+        sb += tb;
+        sr += tr;
+      }
+    }
+    __shared__ int32_t wsum_b[kAlignWaves], wsum_r[kAlignWaves];
+    if (lane == 63) {
+      wsum_b[wave] = sb;
+      wsum_r[wave] = sr;
+    }
+    __syncthreads();
+    int pb = 0, pr = 0;
+    for (int w = 0; w < wave; ++w) {
+      pb += wsum_b[w];
+      pr += wsum_r[w];
+    }
+    int b = pb + sb - nb, rr = pr + sr - nr;  // exclusive prefix at e0
+    for (int e = e0; e < e1; ++e) {
+      blk_start[e] = b;
+      row_start[e] = rr;
+      b += (cnt[e] + block_m - 1) / block_m;
+      rr += cnt[e];
+    }
+    if (tid == kAlignThreads - 1) {
+      blk_start[E] = pb + sb;
+      row_start[E] = pr + sr;
+    }
+  }
+  __syncthreads();
+  const int nblocks = blk_start[E];
+  const int rows_total = row_start[E];
+  if (tid == 0) *num_blocks = nblocks;
+
+  // 3. block table, class lists, and pad slots
+  for (int e = tid; e < E; e += kAlignThreads) {
+    const int c_e = cnt[e];
+    for (int b = 0; b * block_m < c_e; ++b) {
+      const int mb = blk_start[e] + b;
+      const int m_size = min(block_m, c_e - b * block_m);
+      expert_ids[mb] = e;
+      offsets[mb] = row_start[e] + b * block_m;
+      for (int i = m_size; i < block_m; ++i) sorted_ids[int64_t(mb) * block_m + i] = int32_t(R);
+      if (pol.n_classes > 0) {
+        const int c = pick_class(pol, m_size);
+        const int pos = atomicAdd(&cls_cnt[c], 1);
+        class_lists[int64_t(c) * list_stride + pos] = mb;
+      }
+    }
+  }
+  for (int64_t mb = nblocks + tid; mb < max_blocks; mb += kAlignThreads) {
+    expert_ids[mb] = -1;
+    offsets[mb] = rows_total;
+    for (int i = 0; i < block_m; ++i) sorted_ids[mb * block_m + i] = int32_t(R);
+  }
+  if (tid == 0) offsets[max_blocks] = rows_total;
+  __syncthreads();
+  if (pol.n_classes > 0 && tid < pol.n_classes) class_counts[tid] = cls_cnt[tid];
+
+  // 4. stable scatter, 1024 rows at a time
+  int nbits = 1;
+  while ((1 << nbits) < E) ++nbits;
+  for (int64_t base = 0; base < R; base += kAlignThreads) {
+    for (int i = tid; i < kAlignWaves * E; i += kAlignThreads) wave_cnt[i] = 0;
+    __syncthreads();
+    const int64_t r = base + tid;
+    int e = (r < R) ? ids[r] : -1;
+    const bool valid = e >= 0 && e < E;
+    uint64_t mask = __ballot(valid);
+    for (int bit = 0; bit < nbits; ++bit) {
+      const bool set = valid && ((e >> bit) & 1);
+      const uint64_t bm = __ballot(set);
+      mask &= set ? bm : ~bm;
+    }
+    const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    const int rank = __popcll(mask & lt);
+    if (valid && rank == 0) wave_cnt[wave * E + e] = __popcll(mask);
+    __syncthreads();
+    if (valid) {
+      int pos = running[e] + rank;
+      for (int w = 0; w < wave; ++w) pos += wave_cnt[w * E + e];
+      const int b = pos / block_m, slot = pos - b * block_m;
+      sorted_ids[int64_t(blk_start[e] + b) * block_m + slot] = int32_t(r);
+    }
+    __syncthreads();
+    for (int ee = tid; ee < E; ee += kAlignThreads) {
+      int add = 0;
+      for (int w = 0; w < kAlignWaves; ++w) add += wave_cnt[w * E + ee];
+      running[ee] += add;
+    }
+    __syncthreads();
+  }
+}
+
+void launch_moe_align(const int32_t* topk_ids, int64_t M, int32_t topk, int32_t E, int32_t block_m,
+                      int32_t* sorted_ids, int32_t* expert_ids, int32_t* offsets, int32_t* num_blocks,
+                      int64_t max_blocks, const ClassPolicy& pol, int32_t* class_lists, int64_t list_stride,
+                      int32_t* class_counts, hipStream_t stream) {
+  // cnt[E] + blk_start[E+1] + row_start[E+1] + running[E] + wave_cnt[waves][E]
+  const size_t smem = sizeof(int32_t) * (size_t(E) * 4 + 2 + size_t(kAlignWaves) * E);
+  hipLaunchKernelGGL(moe_align_kernel, dim3(1), dim3(kAlignThreads), smem, stream, topk_ids, M * topk, E, block_m,
+                     sorted_ids, expert_ids, offsets, num_blocks, max_blocks, pol, class_lists, list_stride,
+                     class_counts);
+}
+
+// ---------------------------------------------------------------- SiLU-and-mul
+
+// ic0 [rows, 2I] bf16 (gate = columns [0, I), up = [I, 2I)).  16 lanes cover
+// 128 output columns (8 each).  bf16 output: ic1 [rows, I]; W8A8: the bf16
+// products are re-quantised per 128 columns into q [rows, I] + s [rows, I/128].
+template <bool QUANT>
+__global__ __launch_bounds__(256) void silu_mul_kernel(const uint16_t* __restrict__ ic0, int64_t rows, int64_t inter,
+                                                       uint16_t* __restrict__ ic1, uint8_t* __restrict__ q,
+                                                       float* __restrict__ s) {
+  const int64_t per_row = inter / 8;
+  const int64_t idx = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+  const bool valid = idx < rows * per_row;
+  const int64_t ii = valid ? idx : 0;
+  const int64_t row = ii / per_row;
+  const int64_t col = (ii - row * per_row) * 8;
+  uint4 g = make_uint4(0, 0, 0, 0), u = make_uint4(0, 0, 0, 0);
+  if (valid) {
+    g = *reinterpret_cast<const uint4*>(ic0 + row * 2 * inter + col);
+    u = *reinterpret_cast<const uint4*>(ic0 + row * 2 * inter + inter + col);
+  }
+  const uint32_t gw[4] = {g.x, g.y, g.z, g.w}, uw[4] = {u.x, u.y, u.z, u.w};
+  uint32_t hw[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float g0 = bf16lo(gw[i]), g1 = bf16hi(gw[i]);
+    const float h0 = g0 / (1.0f + __expf(-g0)) * bf16lo(uw[i]);
+    const float h1 = g1 / (1.0f + __expf(-g1)) * bf16hi(uw[i]);
+    hw[i] = pack_bf16x2(h0, h1);
+  }
+  const uint4 h = make_uint4(hw[0], hw[1], hw[2], hw[3]);
+  if (!QUANT) {
+    if (valid) *reinterpret_cast<uint4*>(ic1 + row * inter + col) = h;
+  } else {
+    const float amax = group16_max(amax8_bf16(h));
+    if (valid) {
+      uint2 qv;
+      const float sc = quant8_e4m3(h, amax, qv);
+      *reinterpret_cast<uint2*>(q + row * inter + col) = qv;
+      if ((threadIdx.x & 15) == 0) s[row * (inter >> 7) + (col >> 7)] = sc;
+    }
+  }
+}
+
+void launch_silu_mul(const uint16_t* ic0, int64_t rows, int64_t inter, uint16_t* ic1_bf16, uint8_t* ic1_q,
+                     float* ic1_s, hipStream_t stream) {
+  const int64_t threads = rows * (inter / 8);
+  if (threads == 0) return;
+  const unsigned grid = unsigned(cdiv(threads, 256));
+  if (ic1_q)
+    hipLaunchKernelGGL(silu_mul_kernel<true>, dim3(grid), dim3(256), 0, stream, ic0, rows, inter, ic1_bf16, ic1_q,
+                       ic1_s);
+  else
+    hipLaunchKernelGGL(silu_mul_kernel<false>, dim3(grid), dim3(256), 0, stream, ic0, rows, inter, ic1_bf16, ic1_q,
+                       ic1_s);
+}
+
+// ---------------------------------------------------------------- combine
+
+__global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ y, const float* __restrict__ w,
+                                                      const int32_t* __restrict__ ids, int32_t E, int64_t M,
+                                                      int32_t topk, int64_t H, uint16_t* __restrict__ out) {
+  const int64_t per_row = H / 4;
+  const int64_t idx = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (idx >= M * per_row) return;
+  const int64_t t = idx / per_row;
+  const int64_t col = (idx - t * per_row) * 4;
+  float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
+  for (int k = 0; k < topk; ++k) {
+    const int64_t r = t * topk + k;
+    const int e = ids[r];
+    if (e < 0 || e >= E) continue;
+    const float wk = w[r];
+    const float4 v = *reinterpret_cast<const float4*>(y + r * H + col);
+    a0 = fmaf(wk, v.x, a0);
+    a1 = fmaf(wk, v.y, a1);
+    a2 = fmaf(wk, v.z, a2);
+    a3 = fmaf(wk, v.w, a3);
+  }
+  uint2 o;
+  o.x = pack_bf16x2(a0, a1);
+  o.y = pack_bf16x2(a2, a3);
+  *reinterpret_cast<uint2*>(out + t * H + col) = o;
+}
+
+void launch_combine(const float* y, const float* topk_weights, const int32_t* topk_ids, int32_t E, int64_t M,
+                    int32_t topk, int64_t H, uint16_t* out, hipStream_t stream) {
+  const int64_t threads = M * (H / 4);
+  if (threads == 0) return;
+  hipLaunchKernelGGL(combine_kernel, dim3(unsigned(cdiv(threads, 256))), dim3(256), 0, stream, y, topk_weights,
+                     topk_ids, E, M, topk, H, out);
+}
+
+}  // namespace mxq

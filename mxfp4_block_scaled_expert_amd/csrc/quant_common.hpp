@@ -1,0 +1,35 @@
+// 1x128 group quantisation step shared by the standalone quantiser and the
+// fused SiLU-and-mul re-quantisation of the W8A8 MoE: 16 lanes hold one
+// 128-value group, 8 bf16 values per lane.
+#pragma once
+
+#include "common.hpp"
+
+namespace mxq {
+
+__device__ __forceinline__ float amax8_bf16(const uint4 raw) {
+  float m = 0.f;
+  m = fmaxf(m, fabsf(bf16lo(raw.x))); m = fmaxf(m, fabsf(bf16hi(raw.x)));
+  m = fmaxf(m, fabsf(bf16lo(raw.y))); m = fmaxf(m, fabsf(bf16hi(raw.y)));
+  m = fmaxf(m, fabsf(bf16lo(raw.z))); m = fmaxf(m, fabsf(bf16hi(raw.z)));
+  m = fmaxf(m, fabsf(bf16lo(raw.w))); m = fmaxf(m, fabsf(bf16hi(raw.w)));
+  return m;
+}
+
+// s = max(amax, 1e-10) / 448 and q = e4m3(clamp(x / s, +-448)) for this lane's
+// 8 values.  Both divisions are IEEE fp32 divisions.  Returns s.
+__device__ __forceinline__ float quant8_e4m3(const uint4 raw, float group_amax, uint2& q) {
+  const float s = fmaxf(group_amax, 1e-10f) / 448.0f;
+  float v[8];
+  v[0] = bf16lo(raw.x); v[1] = bf16hi(raw.x);
+  v[2] = bf16lo(raw.y); v[3] = bf16hi(raw.y);
+  v[4] = bf16lo(raw.z); v[5] = bf16hi(raw.z);
+  v[6] = bf16lo(raw.w); v[7] = bf16hi(raw.w);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) v[i] = fminf(fmaxf(v[i] / s, -448.0f), 448.0f);
+  q.x = cvt_pk_e4m3(v[0], v[1]) | (cvt_pk_e4m3(v[2], v[3]) << 16);
+  q.y = cvt_pk_e4m3(v[4], v[5]) | (cvt_pk_e4m3(v[6], v[7]) << 16);
+  return s;
+}
+
+}  // namespace mxq

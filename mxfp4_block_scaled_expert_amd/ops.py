@@ -1,0 +1,280 @@
+"""Thin torch binding of libmxq: argument marshalling only.
+
+Each function validates dtypes and shapes, flattens leading dimensions, takes
+``data_ptr()``s and the current HIP stream, allocates outputs and workspaces
+with torch's caching allocator, and calls the C entry point of the same name
+(``mxq_<name>``).  Every step of the computation runs in the HIP kernels.
+
+Semantics carried over from the source pages:
+
+* N-D inputs are flattened to 2-D and the result is viewed back ("SGLang PR
+  32618 review", fp8.py listing; "SGLang PR 35605 review", fp8_utils.py
+  listing).
+* An input whose last dimension is not unit-stride is copied; other strides
+  are passed through (fp8_utils.py listing).
+* ``block_size`` must be ``[1, 128]`` or ``[128, 128]``, anything else raises
+  ``ValueError`` (fp8_utils.py listing).
+* The per-tensor scale may be a 0-d or a 1-element tensor ("SGLang PR 32618
+  review", test_gemm.py listing).
+"""
+
+from __future__ import annotations
+
+from typing import Optional, Sequence, Tuple
+
+import torch
+
+from . import _lib as L
+
+_E4M3 = torch.float8_e4m3fn
+
+
+def _stream() -> int:
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _as_u8(t: torch.Tensor, name: str) -> torch.Tensor:
+    if t.dtype == _E4M3:
+        return t.view(torch.uint8)
+    if t.dtype == torch.uint8:
+        return t
+    raise ValueError(f"{name} must be float8_e4m3fn or uint8 codes, got {t.dtype}")
+
+
+def _require_cuda(*ts):
+    for t in ts:
+        if t is not None and not t.is_cuda:
+            raise ValueError("all tensors must be on the GPU")
+
+
+def _unit_last(t: torch.Tensor) -> torch.Tensor:
+    if t.stride(-1) != 1 or (t.data_ptr() % 16) != 0 or (t.dim() >= 2 and (t.stride(-2) * t.element_size()) % 16 != 0):
+        t = t.contiguous()
+    return t
+
+
+def _2d(t: torch.Tensor) -> torch.Tensor:
+    t2 = t.reshape(-1, t.shape[-1])
+    return _unit_last(t2)
+
+
+def _bias_dtype(b: Optional[torch.Tensor]) -> int:
+    if b is None:
+        return L.MXQ_DTYPE_F32
+    if b.dtype == torch.float32:
+        return L.MXQ_DTYPE_F32
+    if b.dtype == torch.bfloat16:
+        return L.MXQ_DTYPE_BF16
+    raise ValueError(f"bias must be fp32 or bf16, got {b.dtype}")
+
+
+def init(device: int = 0) -> None:
+    L.check("mxq_init", L.load().mxq_init(device))
+
+
+def per_token_group_quant_fp8(x: torch.Tensor, group: int = 128) -> Tuple[torch.Tensor, torch.Tensor]:
+    """bf16 [..., K] -> (e4m3 codes [..., K] as float8_e4m3fn, fp32 scales [..., K/group])."""
+    if x.dtype != torch.bfloat16:
+        raise ValueError("x must be bf16")
+    _require_cuda(x)
+    shape = x.shape
+    x2 = x.reshape(-1, shape[-1])
+    if x2.stride(-1) != 1 or x2.data_ptr() % 16 or x2.stride(0) % 8:
+        x2 = x2.contiguous()
+    M, K = x2.shape
+    q = torch.empty((M, K), dtype=torch.uint8, device=x.device)
+    s = torch.empty((M, K // group if group else 0), dtype=torch.float32, device=x.device)
+    st = L.load().mxq_per_token_group_quant_fp8(x2.data_ptr(), M, K, x2.stride(0), group, q.data_ptr(),
+                                                s.data_ptr(), _stream())
+    L.check("mxq_per_token_group_quant_fp8", st)
+    return q.view(_E4M3).view(*shape), s.view(*shape[:-1], s.shape[-1])
+
+
+def fp8_scaled_mm(x: torch.Tensor, weight: torch.Tensor, scale: torch.Tensor,
+                  bias: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Per-tensor W8A16: bf16 [..., K] @ e4m3 [N, K]^T * scale (+ bias) -> bf16 [..., N]."""
+    if x.dtype != torch.bfloat16:
+        raise ValueError("x must be bf16")
+    w = _as_u8(weight, "weight").contiguous()
+    if scale.numel() != 1 or scale.dtype != torch.float32:
+        raise ValueError("scale must be a single fp32 value (0-d or [1])")
+    _require_cuda(x, w, scale, bias)
+    x2 = _2d(x)
+    M, K = x2.shape
+    N = w.shape[0]
+    if w.shape[1] != K:
+        raise ValueError(f"weight K {w.shape[1]} != input K {K}")
+    if bias is not None and bias.numel() != N:
+        raise ValueError("bias must have N elements")
+    out = torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
+    sc = scale.reshape(1).contiguous()
+    b = None if bias is None else bias.contiguous()
+    st = L.load().mxq_fp8_scaled_mm(x2.data_ptr(), M, K, x2.stride(0), w.data_ptr(), N, sc.data_ptr(), _ptr(b),
+                                    _bias_dtype(b), out.data_ptr(), N, _stream())
+    L.check("mxq_fp8_scaled_mm", st)
+    return out.view(*x.shape[:-1], N)
+
+
+def block_fp8_linear(x: torch.Tensor, weight: torch.Tensor, block_size: Sequence[int], weight_scale: torch.Tensor,
+                     input_scale: Optional[torch.Tensor] = None,
+                     bias: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Block-wise FP8 W8A8 linear -> bf16 [..., N].
+
+    ``x`` is bf16 (quantised per token per 128 columns inside the call) or e4m3
+    codes with ``input_scale`` [..., K/128].  ``weight_scale`` has logical shape
+    [ceil(N / block_n), K / 128] and may have any strides (the transposed
+    storage of a load-time relayout included).
+    """
+    if not isinstance(block_size, (list, tuple)) or len(block_size) != 2:
+        raise ValueError(f"block_size must have two entries, got {block_size}")
+    block_n, block_k = int(block_size[0]), int(block_size[1])
+    if block_k != 128 or block_n not in (1, 128):
+        raise ValueError(f"block_size must be [1, 128] or [128, 128], got {list(block_size)}")
+    w = _as_u8(weight, "weight")
+    if w.stride(-1) != 1:
+        w = w.contiguous()
+    w = w.contiguous()
+    _require_cuda(x, w, weight_scale, input_scale, bias)
+    if weight_scale.dtype != torch.float32 or weight_scale.dim() != 2:
+        raise ValueError("weight_scale must be a 2-D fp32 tensor")
+    N, K = w.shape
+    if input_scale is None:
+        if x.dtype != torch.bfloat16:
+            raise ValueError("x must be bf16 when input_scale is None")
+        a = _2d(x)
+        a_dtype = L.MXQ_DTYPE_BF16
+        a_scale = None
+    else:
+        a = _2d(_as_u8(x, "x"))
+        a_dtype = L.MXQ_DTYPE_E4M3
+        a_scale = input_scale.reshape(-1, input_scale.shape[-1]).contiguous()
+        if a_scale.dtype != torch.float32:
+            raise ValueError("input_scale must be fp32")
+    M = a.shape[0]
+    if a.shape[1] != K:
+        raise ValueError(f"weight K {K} != input K {a.shape[1]}")
+    if tuple(weight_scale.shape) != (-(-N // block_n), K // 128):
+        raise ValueError(f"weight_scale shape {tuple(weight_scale.shape)} != {(-(-N // block_n), K // 128)}")
+    if a_scale is not None and tuple(a_scale.shape) != (M, K // 128):
+        raise ValueError("input_scale must be [..., K/128]")
+    b = None if bias is None else bias.contiguous()
+    if b is not None and b.numel() != N:
+        raise ValueError("bias must have N elements")
+    out = torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
+    lib = L.load()
+    ws_bytes = lib.mxq_block_fp8_linear_workspace_size(M, K, a_dtype)
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=x.device)
+    st = lib.mxq_block_fp8_linear(a.data_ptr(), a_dtype, _ptr(a_scale), M, K, a.stride(0), w.data_ptr(), N,
+                                  weight_scale.data_ptr(), weight_scale.stride(0), weight_scale.stride(1), block_n,
+                                  block_k, _ptr(b), _bias_dtype(b), out.data_ptr(), N, ws.data_ptr(), ws_bytes,
+                                  _stream())
+    L.check("mxq_block_fp8_linear", st)
+    return out.view(*x.shape[:-1], N)
+
+
+def moe_max_blocks(M: int, topk: int, E: int, block_m: int) -> int:
+    return int(L.load().mxq_moe_max_blocks(M, topk, E, block_m))
+
+
+def moe_align(topk_ids: torch.Tensor, E: int, block_m: int):
+    """int32 [M, topk] -> (sorted_ids, expert_ids, offsets, num_blocks) device tensors."""
+    if topk_ids.dtype != torch.int32 or topk_ids.dim() != 2:
+        raise ValueError("topk_ids must be int32 [M, topk]")
+    _require_cuda(topk_ids)
+    ids = topk_ids.contiguous()
+    M, topk = ids.shape
+    nb = moe_max_blocks(M, topk, E, block_m)
+    dev = ids.device
+    sorted_ids = torch.empty(max(nb * block_m, 1), dtype=torch.int32, device=dev)
+    expert_ids = torch.empty(max(nb, 1), dtype=torch.int32, device=dev)
+    offsets = torch.empty(nb + 1, dtype=torch.int32, device=dev)
+    num_blocks = torch.empty(1, dtype=torch.int32, device=dev)
+    st = L.load().mxq_moe_align(ids.data_ptr(), M, topk, E, block_m, sorted_ids.data_ptr(), expert_ids.data_ptr(),
+                                offsets.data_ptr(), num_blocks.data_ptr(), _stream())
+    L.check("mxq_moe_align", st)
+    return sorted_ids[:nb * block_m], expert_ids[:nb], offsets, num_blocks
+
+
+def _moe_common(x, topk_ids, topk_weights):
+    if x.dtype != torch.bfloat16 or x.dim() != 2:
+        raise ValueError("x must be bf16 [M, H]")
+    if topk_ids.dtype != torch.int32 or topk_weights.dtype != torch.float32:
+        raise ValueError("topk_ids must be int32 and topk_weights fp32")
+    if topk_ids.shape != topk_weights.shape or topk_ids.shape[0] != x.shape[0]:
+        raise ValueError("topk_ids / topk_weights must be [M, topk]")
+    return x.contiguous(), topk_ids.contiguous(), topk_weights.contiguous()
+
+
+def fused_moe_workspace(M: int, H: int, I: int, E: int, topk: int, weights: int, act_quant: bool,
+                        device) -> torch.Tensor:
+    n = L.load().mxq_fused_moe_workspace_size(M, H, I, E, topk, weights, int(act_quant))
+    return torch.empty(max(n, 1), dtype=torch.uint8, device=device)
+
+
+def fused_moe_fp8(x, topk_ids, topk_weights, w1, w1_scale, w2, w2_scale, w1_bias=None, act_quant=False,
+                  workspace: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Routed MoE with block-FP8 experts (W8A16, or W8A8 with ``act_quant``) -> bf16 [M, H]."""
+    x, ids, wts = _moe_common(x, topk_ids, topk_weights)
+    w1 = _as_u8(w1, "w1").contiguous()
+    w2 = _as_u8(w2, "w2").contiguous()
+    _require_cuda(x, ids, wts, w1, w2, w1_scale, w2_scale, w1_bias)
+    M, H = x.shape
+    E, two_i, h1 = w1.shape
+    I = two_i // 2
+    topk = ids.shape[1]
+    if h1 != H or tuple(w2.shape) != (E, H, I):
+        raise ValueError("w1 must be [E, 2I, H] and w2 [E, H, I]")
+    if tuple(w1_scale.shape) != (E, -(-2 * I // 128), H // 128) or tuple(w2_scale.shape) != (E, -(-H // 128), I // 128):
+        raise ValueError("block scales must be [E, ceil(2I/128), H/128] and [E, ceil(H/128), I/128]")
+    s1 = w1_scale.float().contiguous()
+    s2 = w2_scale.float().contiguous()
+    b1 = None if w1_bias is None else w1_bias.float().contiguous()
+    if out is None:
+        out = torch.empty((M, H), dtype=torch.bfloat16, device=x.device)
+    if workspace is None:
+        workspace = fused_moe_workspace(M, H, I, E, topk, L.MXQ_WEIGHTS_FP8_BLOCK, act_quant, x.device)
+    st = L.load().mxq_fused_moe_fp8(x.data_ptr(), M, H, I, E, topk, ids.data_ptr(), wts.data_ptr(), w1.data_ptr(),
+                                    s1.data_ptr(), w2.data_ptr(), s2.data_ptr(), _ptr(b1), int(bool(act_quant)),
+                                    out.data_ptr(), workspace.data_ptr(), workspace.numel(), _stream())
+    L.check("mxq_fused_moe_fp8", st)
+    return out
+
+
+def fused_moe_mxfp4(x, topk_ids, topk_weights, w1, w1_scale, w2, w2_scale, w1_bias=None,
+                    workspace: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Routed MoE with MXFP4 experts (packed e2m1 + e8m0 per 32), bf16 activations -> bf16 [M, H]."""
+    x, ids, wts = _moe_common(x, topk_ids, topk_weights)
+    w1 = w1.contiguous()
+    w2 = w2.contiguous()
+    s1 = w1_scale.contiguous()
+    s2 = w2_scale.contiguous()
+    for t, n in ((w1, "w1"), (w2, "w2"), (s1, "w1_scale"), (s2, "w2_scale")):
+        if t.dtype != torch.uint8:
+            raise ValueError(f"{n} must be uint8")
+    _require_cuda(x, ids, wts, w1, w2, s1, s2, w1_bias)
+    M, H = x.shape
+    E, two_i, hh = w1.shape
+    I = two_i // 2
+    topk = ids.shape[1]
+    if hh * 2 != H or tuple(w2.shape) != (E, H, I // 2):
+        raise ValueError("w1 must be [E, 2I, H/2] and w2 [E, H, I/2]")
+    if tuple(s1.shape) != (E, 2 * I, H // 32) or tuple(s2.shape) != (E, H, I // 32):
+        raise ValueError("scales must be [E, 2I, H/32] and [E, H, I/32]")
+    b1 = None if w1_bias is None else w1_bias.float().contiguous()
+    if out is None:
+        out = torch.empty((M, H), dtype=torch.bfloat16, device=x.device)
+    if workspace is None:
+        workspace = fused_moe_workspace(M, H, I, E, topk, L.MXQ_WEIGHTS_MXFP4, False, x.device)
+    st = L.load().mxq_fused_moe_mxfp4(x.data_ptr(), M, H, I, E, topk, ids.data_ptr(), wts.data_ptr(),
+                                      w1.data_ptr(), s1.data_ptr(), w2.data_ptr(), s2.data_ptr(), _ptr(b1),
+                                      out.data_ptr(), workspace.data_ptr(), workspace.numel(), _stream())
+    L.check("mxq_fused_moe_mxfp4", st)
+    return out
+
+
+def moe_set_dispatch(mode: int = L.MXQ_DISPATCH_PER_BLOCK, forced_class: int = 0, gemv_max_rows: int = 4) -> None:
+    L.check("mxq_moe_set_dispatch", L.load().mxq_moe_set_dispatch(mode, forced_class, gemv_max_rows))

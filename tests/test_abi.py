@@ -1,0 +1,105 @@
+"""CPU checks of the C ABI: the library loads, exports every entry point the
+header declares, and answers the host-only queries and argument checks
+(no kernel is launched here)."""
+
+import ctypes as C
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mxq.h")
+
+
+def _lib():
+    from mxfp4_block_scaled_expert_amd import _lib as L
+    if not os.path.exists(L.LIB_PATH):
+        pytest.skip("libmxq.so not built")
+    return L, L.load()
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(mxq_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_header_declares_the_entry_points():
+    names = _declared()
+    for n in ("mxq_per_token_group_quant_fp8", "mxq_fp8_scaled_mm", "mxq_block_fp8_linear", "mxq_moe_align",
+              "mxq_fused_moe_fp8", "mxq_fused_moe_mxfp4"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    L, lib = _lib()
+    raw = C.CDLL(L.LIB_PATH)
+    for n in _declared():
+        assert hasattr(raw, n), f"{n} declared in mxq.h but not exported"
+        assert n in L.SIGNATURES, f"{n} has no ctypes signature in the binding"
+
+
+def test_status_strings_and_version():
+    L, lib = _lib()
+    assert lib.mxq_abi_version() == 1
+    for code in range(0, 9):
+        assert lib.mxq_status_string(code)
+    assert b"unknown" in lib.mxq_status_string(99)
+
+
+def test_max_blocks_matches_formula():
+    _, lib = _lib()
+    from oracle.align import max_blocks
+    for M, topk, E, bm in [(4096, 8, 256, 128), (32, 4, 128, 128), (128, 1, 8, 16), (0, 2, 4, 8), (3, 2, 100, 4)]:
+        assert lib.mxq_moe_max_blocks(M, topk, E, bm) == max_blocks(M, topk, E, bm)
+
+
+def test_workspace_queries():
+    L, lib = _lib()
+    assert lib.mxq_block_fp8_linear_workspace_size(2048, 2048, L.MXQ_DTYPE_E4M3) == 0
+    n = lib.mxq_block_fp8_linear_workspace_size(2048, 2048, L.MXQ_DTYPE_BF16)
+    assert n >= 2048 * 2048 + 2048 * 16 * 4
+    a = lib.mxq_fused_moe_workspace_size(4096, 7168, 2048, 256, 8, L.MXQ_WEIGHTS_FP8_BLOCK, 1)
+    b = lib.mxq_fused_moe_workspace_size(4096, 7168, 2048, 256, 8, L.MXQ_WEIGHTS_FP8_BLOCK, 0)
+    R = 4096 * 8
+    assert a >= R * 2 * 2048 * 2 + R * 7168 * 4  # ic0 + y at least
+    assert a != b
+    assert lib.mxq_fused_moe_workspace_size(0, 7168, 2048, 256, 8, 0, 1) == 0
+
+
+def test_argument_errors_before_any_launch():
+    L, lib = _lib()
+    null = None
+    # block size validation ("SGLang PR 35605 review", fp8_utils.py listing)
+    for bn, bk in [(1, 32), (64, 64), (128, 64), (2, 128)]:
+        st = lib.mxq_block_fp8_linear(null, L.MXQ_DTYPE_BF16, null, 4, 256, 256, null, 256, null, 2, 1, bn, bk,
+                                      null, 0, null, 256, null, 0, null)
+        assert st == L.MXQ_ERR_BLOCK
+    assert lib.mxq_per_token_group_quant_fp8(null, 4, 256, 256, 64, null, null, null) == L.MXQ_ERR_BLOCK
+    assert lib.mxq_per_token_group_quant_fp8(null, 4, 200, 200, 128, null, null, null) == L.MXQ_ERR_SHAPE
+    assert lib.mxq_per_token_group_quant_fp8(null, 4, 256, 256, 128, null, null, null) == L.MXQ_ERR_NULL
+    assert lib.mxq_per_token_group_quant_fp8(null, 0, 256, 256, 128, null, null, null) == L.MXQ_OK
+    assert lib.mxq_fp8_scaled_mm(null, 4, 100, 100, null, 8, null, null, 0, null, 8, null) == L.MXQ_ERR_SHAPE
+    assert lib.mxq_fp8_scaled_mm(null, 4, 128, 128, null, 8, null, null, 7, null, 8, null) == L.MXQ_ERR_NULL
+    assert lib.mxq_fused_moe_fp8(null, 4, 100, 128, 8, 2, null, null, null, null, null, null, null, 0, null, null, 0,
+                                 null) == L.MXQ_ERR_SHAPE
+    assert lib.mxq_fused_moe_mxfp4(null, 4, 100, 128, 8, 2, null, null, null, null, null, null, null, null, null, 0,
+                                   null) == L.MXQ_ERR_SHAPE
+    assert lib.mxq_fused_moe_fp8(null, 4, 256, 128, 8, 2, null, null, null, null, null, null, null, 0, null, null, 0,
+                                 null) == L.MXQ_ERR_NULL
+    assert lib.mxq_moe_align(null, 4, 2, 2000, 16, null, null, null, null, null) == L.MXQ_ERR_SHAPE
+    assert lib.mxq_moe_set_dispatch(7, 0, 4) == L.MXQ_ERR_ARG
+    assert lib.mxq_moe_set_dispatch(0, 0, 9) == L.MXQ_ERR_ARG
+    assert lib.mxq_moe_set_dispatch(0, 0, 4) == L.MXQ_OK
+
+
+def test_binding_rejects_bad_block_size_without_gpu():
+    import torch
+    from mxfp4_block_scaled_expert_amd import ops
+    x = torch.zeros(2, 256, dtype=torch.bfloat16)
+    w = torch.zeros(256, 256, dtype=torch.uint8)
+    s = torch.ones(2, 2)
+    for bs in ([1, 32], [64, 64], [128], (128, 128, 1)):
+        with pytest.raises(ValueError):
+            ops.block_fp8_linear(x, w, bs, s)

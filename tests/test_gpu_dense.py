@@ -1,0 +1,151 @@
+"""GPU parity of the dense linears against the oracle.
+
+* fp8_scaled_mm: the test grid of "SGLang PR 32618 review" (test_gemm.py
+  listing: M in {1, 11, 97}, N in {128, 224}, K in {512, 576}, 0-d or [1]
+  scale, with and without bias).
+* block_fp8_linear: the cases of "SGLang PR 35605 review" (implementation
+  item 4 and the test_xpu_fp8_linear.py listing: M = 1/8/16/17, 2-D and 3-D,
+  non-contiguous input, pre-quantised input, both weight recipes, a non-square
+  scale grid, and the transposed scale storage giving identical bits), plus the
+  2048 x 2048 x 7168 workload on sampled rows.
+"""
+
+import json
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from mxfp4_block_scaled_expert_amd import ops, synth
+from oracle import dense as OD
+from oracle.quant import per_token_group_quant_fp8 as oracle_quant
+from tests._util import assert_bf16_close, bf16_bits, f32, u8, gpu
+
+pytestmark = pytest.mark.gpu
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "page_recipes.json")
+RECIPES = json.load(open(GOLDEN))
+G = RECIPES["per_tensor_w8a16_grid"]
+
+
+@pytest.mark.parametrize("M", G["M"])
+@pytest.mark.parametrize("N", G["N"])
+@pytest.mark.parametrize("K", G["K"])
+@pytest.mark.parametrize("scale_as_vector", G["scale_as_vector"])
+@pytest.mark.parametrize("has_bias", G["has_bias"])
+def test_fp8_scaled_mm_page_grid(M, N, K, scale_as_vector, has_bias):
+    d = synth.dense_w8a16(M, N, K, seed=M * 1000 + N + K, device=gpu(), has_bias=has_bias, scale=G["scale"])
+    scale = d["scale"] if scale_as_vector else d["scale"].reshape(())
+    out = ops.fp8_scaled_mm(d["a"], d["w"], scale, d["bias"])
+    torch.cuda.synchronize()
+    want = OD.fp8_scaled_mm(bf16_bits(d["a"]), u8(d["w"]), float(f32(d["scale"])[0]),
+                            None if d["bias"] is None else f32(d["bias"]))
+    assert_bf16_close(bf16_bits(out), want, what=f"fp8_scaled_mm {M}x{N}x{K}")
+
+
+def test_fp8_scaled_mm_workload_and_bf16_bias_and_3d():
+    d = synth.dense_w8a16(97, 224, 576, seed=1, device=gpu())
+    x3 = d["a"].view(1, 97, 576)
+    out = ops.fp8_scaled_mm(x3, d["w"], d["scale"], d["bias"].to(torch.bfloat16))
+    assert out.shape == (1, 97, 224)
+    torch.cuda.synchronize()
+    bias_b = f32(d["bias"].to(torch.bfloat16))
+    want = OD.fp8_scaled_mm(bf16_bits(d["a"]), u8(d["w"]), 0.01, bias_b)
+    assert_bf16_close(bf16_bits(out.view(97, 224)), want, what="fp8_scaled_mm bf16 bias")
+
+
+def _block_case(M, N, K, block_n, seed, bias_dtype=None, scale_recipe="synth"):
+    d = synth.block_linear(M, N, K, seed=seed, device=gpu(), block_n=block_n, bias_dtype=bias_dtype)
+    if scale_recipe == "page":  # rand(N/bn, K/128) + 0.1 as in the page's accuracy test
+        g = torch.Generator(device="cuda").manual_seed(seed + 1)
+        d["sw"] = torch.rand(d["sw"].shape, generator=g, device=gpu()) + 0.1
+        d["w"] = torch.randn(N, K, generator=g, device=gpu()).to(torch.bfloat16).to(torch.float8_e4m3fn).view(torch.uint8)
+    return d
+
+
+def _oracle_block(d, x2=None):
+    x = d["x"] if x2 is None else x2
+    bias = None if d["bias"] is None else f32(d["bias"].float())
+    return OD.block_fp8_linear_bf16(bf16_bits(x.reshape(-1, x.shape[-1])), u8(d["w"]), f32(d["sw"]), d["block_n"],
+                                    bias)
+
+
+@pytest.mark.parametrize("M", [1, 8, 16, 17])
+@pytest.mark.parametrize("block_n", [128, 1])
+def test_block_linear_page_recipe(M, block_n):
+    d = _block_case(M, 256, 256, block_n, seed=M + block_n, bias_dtype=torch.bfloat16, scale_recipe="page")
+    out = ops.block_fp8_linear(d["x"], d["w"], [block_n, 128], d["sw"], bias=d["bias"])
+    torch.cuda.synchronize()
+    assert_bf16_close(bf16_bits(out), _oracle_block(d), what=f"block linear M={M} bn={block_n}")
+    # the load-time relayout of the scale grid (stored transposed) gives the same bits
+    sw_t = torch.empty_strided(d["sw"].shape, (1, d["sw"].shape[0]), dtype=torch.float32, device=gpu())
+    sw_t.copy_(d["sw"])
+    out_t = ops.block_fp8_linear(d["x"], d["w"], [block_n, 128], sw_t, bias=d["bias"])
+    torch.cuda.synchronize()
+    assert torch.equal(out_t, out)
+
+
+@pytest.mark.parametrize("M,N,K", [(200, 384, 512), (130, 200, 256), (64, 1152, 1024), (257, 640, 384)])
+def test_block_linear_ragged_tiles(M, N, K):
+    d = _block_case(M, N, K, 128, seed=M + N + K, bias_dtype=torch.float32)
+    out = ops.block_fp8_linear(d["x"], d["w"], [128, 128], d["sw"], bias=d["bias"])
+    torch.cuda.synchronize()
+    assert_bf16_close(bf16_bits(out), _oracle_block(d), what=f"block linear {M}x{N}x{K}")
+
+
+def test_block_linear_prequantised_3d_and_noncontiguous():
+    d = _block_case(34, 256, 384, 128, seed=77)
+    q, s = ops.per_token_group_quant_fp8(d["x"])
+    out_q = ops.block_fp8_linear(q, d["w"], [128, 128], d["sw"], input_scale=s)
+    out_b = ops.block_fp8_linear(d["x"], d["w"], [128, 128], d["sw"])
+    torch.cuda.synchronize()
+    assert torch.equal(out_q, out_b)
+    x3 = d["x"].view(2, 17, 384)
+    out3 = ops.block_fp8_linear(x3, d["w"], [128, 128], d["sw"])
+    assert out3.shape == (2, 17, 256)
+    assert torch.equal(out3.view(34, 256), out_b)
+    # non-contiguous 3-D view (last dim strided)
+    big = torch.zeros(2, 17, 384, 2, dtype=torch.bfloat16, device=gpu())
+    big[..., 0] = x3
+    xs = big[..., 0]
+    assert xs.stride(-1) != 1
+    outs = ops.block_fp8_linear(xs, d["w"], [128, 128], d["sw"])
+    torch.cuda.synchronize()
+    assert torch.equal(outs.view(34, 256), out_b)
+    assert_bf16_close(bf16_bits(out_b), _oracle_block(d), what="prequantised")
+
+
+def test_block_linear_non_square_scale_grid():
+    d = _block_case(9, 384, 1024, 128, seed=5)  # grid [3, 8]
+    out = ops.block_fp8_linear(d["x"], d["w"], (128, 128), d["sw"])
+    torch.cuda.synchronize()
+    assert_bf16_close(bf16_bits(out), _oracle_block(d), what="non-square grid")
+
+
+def test_block_linear_rejects_bad_block_sizes():
+    d = _block_case(4, 256, 256, 128, seed=3)
+    for bs in RECIPES["block_fp8_shapes"]["rejected_block_sizes"]:
+        with pytest.raises(ValueError):
+            ops.block_fp8_linear(d["x"], d["w"], bs, d["sw"])
+
+
+def test_block_linear_workload_sampled_rows():
+    M, K, N = 2048, 2048, 7168
+    d = _block_case(M, N, K, 128, seed=1002)
+    out = ops.block_fp8_linear(d["x"], d["w"], [128, 128], d["sw"])
+    torch.cuda.synchronize()
+    rows = np.array([0, 1, 127, 128, 129, 1000, 1023, 1024, 2046, 2047])
+    want = OD.block_fp8_linear_bf16(bf16_bits(d["x"][rows]), u8(d["w"]), f32(d["sw"]), 128)
+    assert_bf16_close(bf16_bits(out[rows]), want, what="2048x2048x7168 sampled rows")
+    # the quantised activations of the workload are bit-exact too
+    q, s = ops.per_token_group_quant_fp8(d["x"])
+    torch.cuda.synchronize()
+    q_ref, s_ref = oracle_quant(bf16_bits(d["x"][rows]))
+    assert np.array_equal(u8(q)[rows], q_ref) and np.array_equal(f32(s)[rows], s_ref)
+
+
+def test_block_linear_zero_rows():
+    d = _block_case(1, 256, 256, 128, seed=4)
+    out = ops.block_fp8_linear(d["x"][:0], d["w"], [128, 128], d["sw"])
+    assert out.shape == (0, 256)
