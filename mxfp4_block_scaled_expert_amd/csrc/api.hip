@@ -345,8 +345,13 @@ mxq_status mxq_block_fp8_linear(const void* A, int32_t a_dtype, const float* a_s
   g.M = M;
   g.N = N;
   g.K = K;
-  const int tile = dense_tile_for(M);
-  launch_gemm_w8a8(g, ROWS_DENSE, tile, false, cdiv(M, tile_rows(tile)), st);
+  if (block_n == 128 && M > 128 && K <= 16384 && int64_t(M) * lqa < (int64_t(1) << 32) &&
+      N * K < (int64_t(1) << 32)) {
+    launch_gemm_w8a8_big(g, ROWS_DENSE, false, cdiv(M, 256), st);
+  } else {
+    const int tile = dense_tile_for(M);
+    launch_gemm_w8a8(g, ROWS_DENSE, tile, false, cdiv(M, tile_rows(tile)), st);
+  }
   return launch_status();
 }
 
