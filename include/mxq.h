@@ -190,16 +190,22 @@ mxq_status mxq_fused_moe_mxfp4(const void* x, int64_t M, int64_t H, int64_t I, i
 
 /* Per-block dispatch control for the fused MoE (process-wide, not thread-safe).
  *   mode MXQ_DISPATCH_PER_BLOCK (default): each block's class from its own row count;
- *   mode MXQ_DISPATCH_FORCED: every block runs class `forced_class` (0 = GEMV,
+ *   mode MXQ_DISPATCH_FORCED: every block runs class `forced_class` (0 = tiny-block kernel,
  *        1 = 16-row, 2 = 32-row, 3 = 64-row, 4 = 128-row MFMA tiles) -- for tests;
  *   mode MXQ_DISPATCH_LAYER_AVERAGE: one class for the whole layer, chosen from
  *        max(1, M * topk / E) rows (the per-layer rule page [A] replaces; for
  *        ablation measurements).
- *   gemv_max_rows: largest block that takes the GEMV class in per-block mode (default 4, max 4). */
+ *   gemv_max_rows: largest block that takes the tiny-block class in per-block mode
+ *        (default 4, max 4).
+ *   tiny_kernel: the tiny-block kernel -- MXQ_TINY_MFMA (default: weights streamed into
+ *        registers, K reduced by 16x16x32 bf16 MFMAs) or MXQ_TINY_GEMV (vector-ALU dot
+ *        products with a wavefront reduction). */
 #define MXQ_DISPATCH_PER_BLOCK 0
 #define MXQ_DISPATCH_FORCED 1
 #define MXQ_DISPATCH_LAYER_AVERAGE 2
-mxq_status mxq_moe_set_dispatch(int32_t mode, int32_t forced_class, int32_t gemv_max_rows);
+#define MXQ_TINY_MFMA 0
+#define MXQ_TINY_GEMV 1
+mxq_status mxq_moe_set_dispatch(int32_t mode, int32_t forced_class, int32_t gemv_max_rows, int32_t tiny_kernel);
 
 #ifdef __cplusplus
 }

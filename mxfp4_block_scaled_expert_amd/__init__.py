@@ -22,4 +22,6 @@ from ._lib import (  # noqa: F401
     MXQ_DISPATCH_PER_BLOCK,
     MXQ_DISPATCH_FORCED,
     MXQ_DISPATCH_LAYER_AVERAGE,
+    MXQ_TINY_MFMA,
+    MXQ_TINY_GEMV,
 )

@@ -33,6 +33,9 @@ MXQ_DISPATCH_PER_BLOCK = 0
 MXQ_DISPATCH_FORCED = 1
 MXQ_DISPATCH_LAYER_AVERAGE = 2
 
+MXQ_TINY_MFMA = 0
+MXQ_TINY_GEMV = 1
+
 _p = C.c_void_p
 _i32 = C.c_int32
 _i64 = C.c_int64
@@ -55,7 +58,7 @@ SIGNATURES = {
                                   _sz, _p]),
     "mxq_fused_moe_mxfp4": (_i32, [_p, _i64, _i64, _i64, _i32, _i32, _p, _p, _p, _p, _p, _p, _p, _p, _p,
                                     _sz, _p]),
-    "mxq_moe_set_dispatch": (_i32, [_i32, _i32, _i32]),
+    "mxq_moe_set_dispatch": (_i32, [_i32, _i32, _i32, _i32]),
 }
 
 _lock = threading.Lock()

@@ -44,6 +44,8 @@ std::mutex g_dispatch_mu;
 int g_dispatch_mode = MXQ_DISPATCH_PER_BLOCK;
 int g_forced_class = 0;
 int g_gemv_max_rows = 4;
+int g_tiny_kernel = MXQ_TINY_MFMA;
+constexpr size_t kSkinnyMaxLds = 64 * 1024;
 
 constexpr int kMoeBlockM = 128;
 constexpr int kNumClasses = 5;  // GEMV, 16-, 32-, 64-, 128-row MFMA tiles
@@ -136,6 +138,11 @@ mxq_status run_moe(const void* x, int64_t M, int64_t H, int64_t I, int32_t E, in
   MoeWorkspace w = carve_moe(ws, M, H, I, E, topk, act_quant);
   if (!ws || ws_bytes < w.bytes) return MXQ_ERR_WORKSPACE;
   const ClassPolicy pol = make_policy(R, E);
+  int tiny;
+  {
+    std::lock_guard<std::mutex> lk(g_dispatch_mu);
+    tiny = g_tiny_kernel;
+  }
 
   launch_moe_align(ids, M, topk, E, kMoeBlockM, w.sorted_ids, w.expert_ids, w.offsets, w.num_blocks, mbk, pol,
                    w.class_lists, mbk, w.class_counts, st);
@@ -210,7 +217,10 @@ mxq_status run_moe(const void* x, int64_t M, int64_t H, int64_t I, int32_t E, in
       if (ub <= 0) continue;
       g.rt.work_list = w.class_lists + int64_t(c) * mbk;
       g.rt.work_count = w.class_counts + c;
-      if (c == 0)
+      // the tiny-block MFMA kernel keeps four activation rows of the whole K in LDS
+      if (c == 0 && tiny == MXQ_TINY_MFMA && skinny_lds_bytes(act_quant, g.K) <= kSkinnyMaxLds)
+        launch_skinny(g, wfmt_w16, act_quant, mode, out_f32, ub, st);
+      else if (c == 0)
         launch_gemv(g, wfmt_w16, act_quant, mode, out_f32, ub, st);
       else if (act_quant)
         launch_gemm_w8a8(g, mode, kClassTile[c], out_f32, ub, st);
@@ -244,7 +254,7 @@ const char* mxq_status_string(mxq_status s) {
   }
 }
 
-int32_t mxq_abi_version(void) { return 1; }
+int32_t mxq_abi_version(void) { return 2; }
 
 mxq_status mxq_init(int32_t device) {
   if (hipSetDevice(device) != hipSuccess) return MXQ_ERR_ARCH;
@@ -416,14 +426,16 @@ mxq_status mxq_fused_moe_mxfp4(const void* x, int64_t M, int64_t H, int64_t I, i
                  out, workspace, workspace_bytes, static_cast<hipStream_t>(stream));
 }
 
-mxq_status mxq_moe_set_dispatch(int32_t mode, int32_t forced_class, int32_t gemv_max_rows) {
+mxq_status mxq_moe_set_dispatch(int32_t mode, int32_t forced_class, int32_t gemv_max_rows, int32_t tiny_kernel) {
   if (mode < MXQ_DISPATCH_PER_BLOCK || mode > MXQ_DISPATCH_LAYER_AVERAGE) return MXQ_ERR_ARG;
+  if (tiny_kernel != MXQ_TINY_MFMA && tiny_kernel != MXQ_TINY_GEMV) return MXQ_ERR_ARG;
   if (forced_class < 0 || forced_class >= kNumClasses) return MXQ_ERR_ARG;
   if (gemv_max_rows < 0 || gemv_max_rows > 4) return MXQ_ERR_ARG;
   std::lock_guard<std::mutex> lk(g_dispatch_mu);
   g_dispatch_mode = mode;
   g_forced_class = forced_class;
   g_gemv_max_rows = gemv_max_rows;
+  g_tiny_kernel = tiny_kernel;
   return MXQ_OK;
 }
 

@@ -78,6 +78,13 @@ void launch_gemm_w16(const GemmArgs& a, int wfmt, int row_mode, int tile, bool o
 void launch_gemv(const GemmArgs& a, int wfmt, bool a_e4m3, int row_mode, bool out_f32, int64_t grid_blocks,
                  hipStream_t stream);
 
+// Weight-streaming MFMA kernel for routed blocks of at most 4 rows (more rows are processed
+// 4 at a time); routed row modes only.
+void launch_skinny(const GemmArgs& a, int wfmt, bool a_e4m3, int row_mode, bool out_f32, int64_t grid_blocks,
+                   hipStream_t stream);
+// Dynamic LDS the weight-streaming kernel takes for reduction length K.
+size_t skinny_lds_bytes(bool a_e4m3, int64_t K);
+
 // Expert sort / block alignment.  Optionally also fills per-class work lists
 // (class_lists[c * list_stride + i], class_counts[c]) using the per-block selector.
 struct ClassPolicy {

@@ -276,5 +276,6 @@ def fused_moe_mxfp4(x, topk_ids, topk_weights, w1, w1_scale, w2, w2_scale, w1_bi
     return out
 
 
-def moe_set_dispatch(mode: int = L.MXQ_DISPATCH_PER_BLOCK, forced_class: int = 0, gemv_max_rows: int = 4) -> None:
-    L.check("mxq_moe_set_dispatch", L.load().mxq_moe_set_dispatch(mode, forced_class, gemv_max_rows))
+def moe_set_dispatch(mode: int = L.MXQ_DISPATCH_PER_BLOCK, forced_class: int = 0, gemv_max_rows: int = 4,
+                     tiny_kernel: int = L.MXQ_TINY_MFMA) -> None:
+    L.check("mxq_moe_set_dispatch", L.load().mxq_moe_set_dispatch(mode, forced_class, gemv_max_rows, tiny_kernel))

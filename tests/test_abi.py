@@ -42,7 +42,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_status_strings_and_version():
     L, lib = _lib()
-    assert lib.mxq_abi_version() == 1
+    assert lib.mxq_abi_version() == 2
     for code in range(0, 9):
         assert lib.mxq_status_string(code)
     assert b"unknown" in lib.mxq_status_string(99)
@@ -89,9 +89,10 @@ def test_argument_errors_before_any_launch():
     assert lib.mxq_fused_moe_fp8(null, 4, 256, 128, 8, 2, null, null, null, null, null, null, null, 0, null, null, 0,
                                  null) == L.MXQ_ERR_NULL
     assert lib.mxq_moe_align(null, 4, 2, 2000, 16, null, null, null, null, null) == L.MXQ_ERR_SHAPE
-    assert lib.mxq_moe_set_dispatch(7, 0, 4) == L.MXQ_ERR_ARG
-    assert lib.mxq_moe_set_dispatch(0, 0, 9) == L.MXQ_ERR_ARG
-    assert lib.mxq_moe_set_dispatch(0, 0, 4) == L.MXQ_OK
+    assert lib.mxq_moe_set_dispatch(7, 0, 4, 0) == L.MXQ_ERR_ARG
+    assert lib.mxq_moe_set_dispatch(0, 0, 9, 0) == L.MXQ_ERR_ARG
+    assert lib.mxq_moe_set_dispatch(0, 0, 4, 5) == L.MXQ_ERR_ARG
+    assert lib.mxq_moe_set_dispatch(0, 0, 4, 0) == L.MXQ_OK
 
 
 def test_binding_rejects_bad_block_size_without_gpu():

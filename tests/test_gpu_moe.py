@@ -124,6 +124,27 @@ def test_small_expert_blocks_every_class(forced):
     assert_bf16_close(bf16_bits(out), want, what=f"forced class {forced}")
 
 
+@pytest.mark.parametrize("tiny", [mx.MXQ_TINY_MFMA, mx.MXQ_TINY_GEMV])
+@pytest.mark.parametrize("kind", ["w8a16", "w8a8", "mxfp4"])
+def test_tiny_block_kernels(kind, tiny):
+    """Both tiny-block kernels, every block forced through them, each weight format."""
+    if kind == "w8a16":
+        inp = synth.moe_inputs(SMALL_BLOCKS, seed=1003, device=gpu())
+        check = assert_bf16_close
+    elif kind == "w8a8":
+        inp = synth.moe_inputs(_small_spec("fused_moe_fp8", 300, 16, 4, 512, 256, zipf=1.1, act_quant=True),
+                               seed=21, device=gpu())
+        check = assert_bf16_close_requant
+    else:
+        inp = synth.moe_inputs(_small_spec("fused_moe_mxfp4", 40, 8, 4, 2880, 2880), seed=22, device=gpu())
+        check = assert_bf16_close
+    want = _run_oracle(inp)
+    ops.moe_set_dispatch(mx.MXQ_DISPATCH_FORCED, 0, 4, tiny)
+    out = _run_gpu(inp)
+    torch.cuda.synchronize()
+    check(bf16_bits(out), want, what=f"{kind} tiny={tiny}")
+
+
 def test_layer_average_rule_matches_too():
     inp = synth.moe_inputs(SMALL_BLOCKS, seed=1003, device=gpu())
     ops.moe_set_dispatch(mx.MXQ_DISPATCH_LAYER_AVERAGE, 0, 4)
