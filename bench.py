@@ -133,10 +133,20 @@ def _touched_bytes(inp) -> int:
     return int(used.size * per + 2 * M * H * 2 + ids.size * 8)
 
 
-def bench_moe(name: str, steps: int, warmup: int, seed: int):
+def bench_moe(name: str, steps: int, warmup: int, seed: int, layout: str = "tiled"):
+    """Times one fused-MoE call.  ``layout="tiled"``: the weights are relaid out once with the
+    load-time prepack before timing (as a model would at weight-loading time)."""
     from mxfp4_block_scaled_expert_amd import ops, synth
     dev = torch.device("cuda", 0)
     inp = synth.moe_inputs(name, seed=seed, device=dev)
+    byts = _touched_bytes(inp)
+    if layout == "tiled":
+        for k in ("w1", "w2"):
+            inp[k] = ops.moe_prepack(inp[k])
+        if inp["kind"] == "fused_moe_mxfp4":
+            for k in ("w1_scale", "w2_scale"):
+                inp[k] = ops.moe_prepack_scales(inp[k])
+        torch.cuda.synchronize()
     M, H = inp["x"].shape
     I, E, topk = inp["I"], inp["E"], inp["topk"]
     mx = inp["kind"] == "fused_moe_mxfp4"
@@ -148,10 +158,12 @@ def bench_moe(name: str, steps: int, warmup: int, seed: int):
     def run():
         if mx:
             ops.fused_moe_mxfp4(inp["x"], inp["topk_ids"], inp["topk_weights"], inp["w1"], inp["w1_scale"],
-                                inp["w2"], inp["w2_scale"], inp["w1_bias"], workspace=ws, out=out)
+                                inp["w2"], inp["w2_scale"], inp["w1_bias"], workspace=ws, out=out,
+                                weight_layout=layout)
         else:
             ops.fused_moe_fp8(inp["x"], inp["topk_ids"], inp["topk_weights"], inp["w1"], inp["w1_scale"],
-                              inp["w2"], inp["w2_scale"], None, act_quant=inp["act_quant"], workspace=ws, out=out)
+                              inp["w2"], inp["w2_scale"], None, act_quant=inp["act_quant"], workspace=ws, out=out,
+                              weight_layout=layout)
 
     for _ in range(warmup):
         run()
@@ -165,10 +177,9 @@ def bench_moe(name: str, steps: int, warmup: int, seed: int):
     torch.cuda.synchronize()
     ms = np.array([e[0].elapsed_time(e[1]) for e in evs])
     flops = 2.0 * M * topk * (2 * I * H + H * I)
-    byts = _touched_bytes(inp)
     med = float(np.median(ms))
     return {
-        "workload": name, "us_median": med * 1e3, "us_p10": float(np.percentile(ms, 10)) * 1e3,
+        "workload": name, "weight_layout": layout, "us_median": med * 1e3, "us_p10": float(np.percentile(ms, 10)) * 1e3,
         "us_p90": float(np.percentile(ms, 90)) * 1e3, "tflops": flops / (med * 1e-3) / 1e12,
         "touched_bytes": byts, "weight_gbs": byts / (med * 1e-3) / 1e9,
         "hbm_frac": byts / (med * 1e-3) / 1e9 / HBM_PEAK_GBS,

@@ -154,7 +154,7 @@ mxq_status mxq_moe_align(const int32_t* topk_ids, int64_t M, int32_t topk, int32
  * activation @ w2; the top-k combine weights each expert output by its routing
  * weight).  Rows [0, I) of w1 are the gate, rows [I, 2I) the up projection.
  * Each expert block picks its kernel from its own row count (page [A],
- * implementation items 1-2): a wavefront-reduction GEMV for tiny blocks, MFMA
+ * implementation items 1-2): a weight-streaming kernel for tiny blocks, MFMA
  * tiles of 16/32/64/128 rows otherwise (see mxq_moe_set_dispatch).
  *
  * mxq_fused_moe_fp8: block-FP8 weights.
@@ -166,27 +166,59 @@ mxq_status mxq_moe_align(const int32_t* topk_ids, int64_t M, int32_t topk, int32
  *   act_quant    0: W8A16 (bf16 activations into both stages);
  *                1: W8A8 (x and ic1 quantised per token per 128 columns, as
  *                   mxq_per_token_group_quant_fp8)
+ *   weight_layout MXQ_LAYOUT_PLAIN: w1 / w2 as above;  MXQ_LAYOUT_TILED: w1 / w2 are
+ *                the outputs of mxq_moe_prepack (the block scales keep their layout)
  *   out          bf16 [M, H], contiguous
  *   H and I must be multiples of 128.
  * mxq_fused_moe_mxfp4: MXFP4 weights, bf16 activations (W4A16).
  *   w1           packed e2m1 [E, 2I, H/2];  w1_scale e8m0 [E, 2I, H/32]
  *   w2           packed e2m1 [E, H, I/2];   w2_scale e8m0 [E, H, I/32]
  *   w1_bias      NULL or fp32 [E, 2I]
+ *   weight_layout MXQ_LAYOUT_TILED: w1 / w2 from mxq_moe_prepack and w1_scale / w2_scale
+ *                from mxq_moe_prepack_scales
  *   H and I must be multiples of 32.
  * Both: workspace of mxq_fused_moe_workspace_size(...) bytes (routing tables,
- * intermediates); experts that receive no rows are never read; 1 <= E <= 512. */
+ * intermediates); experts that receive no rows are never read; 1 <= E <= 512.
+ * The two layouts give bit-identical outputs. */
 #define MXQ_WEIGHTS_FP8_BLOCK 0
 #define MXQ_WEIGHTS_MXFP4 1
+#define MXQ_LAYOUT_PLAIN 0
+#define MXQ_LAYOUT_TILED 1
 size_t mxq_fused_moe_workspace_size(int64_t M, int64_t H, int64_t I, int32_t E, int32_t topk, int32_t weights,
                                     int32_t act_quant);
 mxq_status mxq_fused_moe_fp8(const void* x, int64_t M, int64_t H, int64_t I, int32_t E, int32_t topk,
                              const int32_t* topk_ids, const float* topk_weights, const void* w1,
                              const float* w1_scale, const void* w2, const float* w2_scale, const float* w1_bias,
-                             int32_t act_quant, void* out, void* workspace, size_t workspace_bytes, void* stream);
+                             int32_t act_quant, int32_t weight_layout, void* out, void* workspace,
+                             size_t workspace_bytes, void* stream);
 mxq_status mxq_fused_moe_mxfp4(const void* x, int64_t M, int64_t H, int64_t I, int32_t E, int32_t topk,
                                const int32_t* topk_ids, const float* topk_weights, const void* w1,
                                const void* w1_scale, const void* w2, const void* w2_scale, const float* w1_bias,
-                               void* out, void* workspace, size_t workspace_bytes, void* stream);
+                               int32_t weight_layout, void* out, void* workspace, size_t workspace_bytes,
+                               void* stream);
+
+/* ------------------------------------------------------------------ load-time weight relayout
+ * Converts routed-expert weights into the tiled layout the MoE kernels stream (page [B]:
+ * the per-tensor GEMM takes prepacked or unpacked weights and its tests run both;
+ * page [C]: layout work moved from the forward pass to weight loading).  Run once
+ * when the weights are loaded; the caller owns both buffers.
+ * mxq_moe_prepack: w [E, N, row_bytes] (e4m3 rows: row_bytes = K; packed e2m1: K/2)
+ *   -> out of mxq_moe_prepack_size(E, N, row_bytes) bytes.  Rows are cut into
+ *   16-row groups and 128-byte steps (the last step zero-padded); tile (e, g, s) is
+ *   the 2048 bytes at ((e * N/16 + g) * S + s) * 2048, S = ceil(row_bytes / 128), and
+ *   its byte 1024 h + 16 L holds bytes [32 (L / 16) + 16 h, +16) of row 16 g + L % 16
+ *   (h in {0, 1}, L in [0, 64)).
+ * mxq_moe_prepack_scales: e8m0 s [E, N, groups] -> out of
+ *   mxq_moe_prepack_scales_size(E, N, groups) bytes; tile (e, g, s) is the 128 bytes at
+ *   ((e * N/16 + g) * S + s) * 128, S = ceil(groups / 8), whose bytes 2 L and 2 L + 1
+ *   hold groups 8 s + 2 (L / 16) and 8 s + 2 (L / 16) + 1 of row 16 g + L % 16 (0 past
+ *   the row end).
+ * N must be a multiple of 16 and row_bytes of 16 (else MXQ_ERR_SHAPE; the size queries
+ * return 0); w and out 16-byte aligned. */
+size_t mxq_moe_prepack_size(int64_t E, int64_t N, int64_t row_bytes);
+size_t mxq_moe_prepack_scales_size(int64_t E, int64_t N, int64_t groups);
+mxq_status mxq_moe_prepack(const void* w, int64_t E, int64_t N, int64_t row_bytes, void* out, void* stream);
+mxq_status mxq_moe_prepack_scales(const void* s, int64_t E, int64_t N, int64_t groups, void* out, void* stream);
 
 /* Per-block dispatch control for the fused MoE (process-wide, not thread-safe).
  *   mode MXQ_DISPATCH_PER_BLOCK (default): each block's class from its own row count;
@@ -195,17 +227,18 @@ mxq_status mxq_fused_moe_mxfp4(const void* x, int64_t M, int64_t H, int64_t I, i
  *   mode MXQ_DISPATCH_LAYER_AVERAGE: one class for the whole layer, chosen from
  *        max(1, M * topk / E) rows (the per-layer rule page [A] replaces; for
  *        ablation measurements).
- *   gemv_max_rows: largest block that takes the tiny-block class in per-block mode
- *        (default 4, max 4).
+ *   tiny_max_rows: largest block that takes the tiny-block class in per-block mode
+ *        (default 16, max 16).
  *   tiny_kernel: the tiny-block kernel -- MXQ_TINY_MFMA (default: weights streamed into
- *        registers, K reduced by 16x16x32 bf16 MFMAs) or MXQ_TINY_GEMV (vector-ALU dot
- *        products with a wavefront reduction). */
+ *        registers, K reduced by MFMAs, up to 8 rows per pass) or MXQ_TINY_GEMV
+ *        (vector-ALU dot products with a wavefront reduction, 4 rows per pass; plain
+ *        weight layout only -- with tiled weights the MFMA kernel runs). */
 #define MXQ_DISPATCH_PER_BLOCK 0
 #define MXQ_DISPATCH_FORCED 1
 #define MXQ_DISPATCH_LAYER_AVERAGE 2
 #define MXQ_TINY_MFMA 0
 #define MXQ_TINY_GEMV 1
-mxq_status mxq_moe_set_dispatch(int32_t mode, int32_t forced_class, int32_t gemv_max_rows, int32_t tiny_kernel);
+mxq_status mxq_moe_set_dispatch(int32_t mode, int32_t forced_class, int32_t tiny_max_rows, int32_t tiny_kernel);
 
 #ifdef __cplusplus
 }

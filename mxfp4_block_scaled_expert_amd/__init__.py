@@ -15,6 +15,8 @@ from .ops import (  # noqa: F401
     fused_moe_fp8,
     fused_moe_mxfp4,
     fused_moe_workspace,
+    moe_prepack,
+    moe_prepack_scales,
     moe_set_dispatch,
 )
 from ._lib import (  # noqa: F401
@@ -24,4 +26,6 @@ from ._lib import (  # noqa: F401
     MXQ_DISPATCH_LAYER_AVERAGE,
     MXQ_TINY_MFMA,
     MXQ_TINY_GEMV,
+    MXQ_LAYOUT_PLAIN,
+    MXQ_LAYOUT_TILED,
 )

@@ -36,6 +36,9 @@ MXQ_DISPATCH_LAYER_AVERAGE = 2
 MXQ_TINY_MFMA = 0
 MXQ_TINY_GEMV = 1
 
+MXQ_LAYOUT_PLAIN = 0
+MXQ_LAYOUT_TILED = 1
+
 _p = C.c_void_p
 _i32 = C.c_int32
 _i64 = C.c_int64
@@ -54,10 +57,14 @@ SIGNATURES = {
     "mxq_moe_max_blocks": (_i64, [_i64, _i32, _i32, _i32]),
     "mxq_moe_align": (_i32, [_p, _i64, _i32, _i32, _i32, _p, _p, _p, _p, _p]),
     "mxq_fused_moe_workspace_size": (_sz, [_i64, _i64, _i64, _i32, _i32, _i32, _i32]),
-    "mxq_fused_moe_fp8": (_i32, [_p, _i64, _i64, _i64, _i32, _i32, _p, _p, _p, _p, _p, _p, _p, _i32, _p, _p,
-                                  _sz, _p]),
-    "mxq_fused_moe_mxfp4": (_i32, [_p, _i64, _i64, _i64, _i32, _i32, _p, _p, _p, _p, _p, _p, _p, _p, _p,
+    "mxq_fused_moe_fp8": (_i32, [_p, _i64, _i64, _i64, _i32, _i32, _p, _p, _p, _p, _p, _p, _p, _i32, _i32, _p,
+                                  _p, _sz, _p]),
+    "mxq_fused_moe_mxfp4": (_i32, [_p, _i64, _i64, _i64, _i32, _i32, _p, _p, _p, _p, _p, _p, _p, _i32, _p, _p,
                                     _sz, _p]),
+    "mxq_moe_prepack_size": (_sz, [_i64, _i64, _i64]),
+    "mxq_moe_prepack_scales_size": (_sz, [_i64, _i64, _i64]),
+    "mxq_moe_prepack": (_i32, [_p, _i64, _i64, _i64, _p, _p]),
+    "mxq_moe_prepack_scales": (_i32, [_p, _i64, _i64, _i64, _p, _p]),
     "mxq_moe_set_dispatch": (_i32, [_i32, _i32, _i32, _i32]),
 }
 

@@ -43,14 +43,14 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 std::mutex g_dispatch_mu;
 int g_dispatch_mode = MXQ_DISPATCH_PER_BLOCK;
 int g_forced_class = 0;
-int g_gemv_max_rows = 4;
+int g_tiny_max_rows = 16;
 int g_tiny_kernel = MXQ_TINY_MFMA;
 constexpr size_t kSkinnyMaxLds = 64 * 1024;
 
 constexpr int kMoeBlockM = 128;
-constexpr int kNumClasses = 5;  // GEMV, 16-, 32-, 64-, 128-row MFMA tiles
+constexpr int kNumClasses = 5;  // tiny-block kernel, 16-, 32-, 64-, 128-row MFMA tiles
 constexpr int kClassTile[kNumClasses] = {-1, 3, 2, 1, 0};  // launcher tile index per class
-constexpr int kClassRows[kNumClasses] = {4, 16, 32, 64, 128};
+constexpr int kClassRows[kNumClasses] = {16, 16, 32, 64, 128};  // [0] is set at run time
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
@@ -101,43 +101,56 @@ MoeWorkspace carve_moe(void* base, int64_t M, int64_t H, int64_t I, int32_t E, i
 // Largest number of blocks that can fall in class c (no host sync: from sizes only).
 int64_t class_bound(int c, int64_t R, int32_t E, int64_t max_blocks, const ClassPolicy& pol) {
   if (pol.forced >= 0) return c == pol.forced ? max_blocks : 0;
+  if (c >= pol.n_live) return 0;
   const int lo = c == 0 ? 0 : pol.bound[c - 1];
-  const int hi = c == pol.n_classes - 1 ? kMoeBlockM : pol.bound[c];
+  const bool top = c == pol.n_live - 1;  // also takes every block past the launched bounds
+  const int hi = top ? kMoeBlockM : pol.bound[c];
   if (hi <= lo) return 0;
   int64_t ub = std::min<int64_t>(max_blocks, R / (lo + 1));
   if (hi < kMoeBlockM) ub = std::min<int64_t>(ub, E);  // only an expert's last block is partial
   return std::max<int64_t>(ub, 0);
 }
 
-ClassPolicy make_policy(int64_t R, int32_t E) {
+// M caps the rows of one expert when every token names distinct experts, so the
+// classes whose lower bound reaches M are not launched (a block beyond that, from
+// repeated ids, still lands in the largest launched class).
+ClassPolicy make_policy(int64_t M, int64_t R, int32_t E) {
   std::lock_guard<std::mutex> lk(g_dispatch_mu);
   ClassPolicy pol{};
   pol.n_classes = kNumClasses;
   pol.forced = -1;
-  pol.bound[0] = g_gemv_max_rows;
+  pol.bound[0] = g_tiny_max_rows;
   for (int c = 1; c < kNumClasses; ++c) pol.bound[c] = kClassRows[c];
+  pol.n_live = kNumClasses;
+  for (int c = 1; c < kNumClasses; ++c)
+    if (pol.bound[c - 1] >= M) {
+      pol.n_live = c;
+      break;
+    }
   if (g_dispatch_mode == MXQ_DISPATCH_FORCED) {
     pol.forced = g_forced_class;
+    pol.n_live = kNumClasses;
   } else if (g_dispatch_mode == MXQ_DISPATCH_LAYER_AVERAGE) {
     const int64_t avg = std::max<int64_t>(1, R / std::max<int32_t>(E, 1));
     int c = kNumClasses - 1;
     for (int i = 0; i < kNumClasses - 1; ++i)
       if (avg <= pol.bound[i]) { c = i; break; }
     pol.forced = c;
+    pol.n_live = kNumClasses;
   }
   return pol;
 }
 
 mxq_status run_moe(const void* x, int64_t M, int64_t H, int64_t I, int32_t E, int32_t topk, const int32_t* ids,
                    const float* wts, const void* w1, const void* w1s, const void* w2, const void* w2s,
-                   const float* b1, int wfmt, bool act_quant, void* out, void* ws, size_t ws_bytes,
+                   const float* b1, int wfmt, bool act_quant, bool tiled, void* out, void* ws, size_t ws_bytes,
                    hipStream_t st) {
   const int64_t R = M * topk;
   if (R == 0) return MXQ_OK;
   const int64_t mbk = mxq_moe_max_blocks(M, topk, E, kMoeBlockM);
   MoeWorkspace w = carve_moe(ws, M, H, I, E, topk, act_quant);
   if (!ws || ws_bytes < w.bytes) return MXQ_ERR_WORKSPACE;
-  const ClassPolicy pol = make_policy(R, E);
+  const ClassPolicy pol = make_policy(M, R, E);
   int tiny;
   {
     std::lock_guard<std::mutex> lk(g_dispatch_mu);
@@ -145,7 +158,7 @@ mxq_status run_moe(const void* x, int64_t M, int64_t H, int64_t I, int32_t E, in
   }
 
   launch_moe_align(ids, M, topk, E, kMoeBlockM, w.sorted_ids, w.expert_ids, w.offsets, w.num_blocks, mbk, pol,
-                   w.class_lists, mbk, w.class_counts, st);
+                   w.class_lists, mbk, w.class_counts, false, st);
   if (act_quant) launch_quant_1x128(static_cast<const uint16_t*>(x), M, H, H, w.qx, H, w.sx, st);
 
   const bool mx = wfmt == W_E2M1_MX;
@@ -159,11 +172,12 @@ mxq_status run_moe(const void* x, int64_t M, int64_t H, int64_t I, int32_t E, in
   g1.lds = H / 128;
   g1.W = static_cast<const uint8_t*>(w1);
   g1.ldw = mx ? H / 2 : H;
-  g1.w_estride = g1.ldw * 2 * I;
+  g1.w_tiled = tiled;
+  g1.w_estride = tiled ? 2 * I * tiled_steps(g1.ldw) * 128 : g1.ldw * 2 * I;
   g1.ws = w1s;
   if (mx) {
     g1.ws_s0 = H / 32;
-    g1.ws_estride = 2 * I * (H / 32);
+    g1.ws_estride = tiled ? 2 * I * tiled_scale_steps(H / 32) * 8 : 2 * I * (H / 32);
   } else {
     g1.ws_s0 = H / 128;
     g1.ws_s1 = 1;
@@ -188,11 +202,12 @@ mxq_status run_moe(const void* x, int64_t M, int64_t H, int64_t I, int32_t E, in
   g2.lds = I / 128;
   g2.W = static_cast<const uint8_t*>(w2);
   g2.ldw = mx ? I / 2 : I;
-  g2.w_estride = g2.ldw * H;
+  g2.w_tiled = tiled;
+  g2.w_estride = tiled ? H * tiled_steps(g2.ldw) * 128 : g2.ldw * H;
   g2.ws = w2s;
   if (mx) {
     g2.ws_s0 = I / 32;
-    g2.ws_estride = H * (I / 32);
+    g2.ws_estride = tiled ? H * tiled_scale_steps(I / 32) * 8 : H * (I / 32);
   } else {
     g2.ws_s0 = I / 128;
     g2.ws_s1 = 1;
@@ -217,15 +232,20 @@ mxq_status run_moe(const void* x, int64_t M, int64_t H, int64_t I, int32_t E, in
       if (ub <= 0) continue;
       g.rt.work_list = w.class_lists + int64_t(c) * mbk;
       g.rt.work_count = w.class_counts + c;
-      // the tiny-block MFMA kernel keeps four activation rows of the whole K in LDS
-      if (c == 0 && tiny == MXQ_TINY_MFMA && skinny_lds_bytes(act_quant, g.K) <= kSkinnyMaxLds)
-        launch_skinny(g, wfmt_w16, act_quant, mode, out_f32, ub, st);
-      else if (c == 0)
+      // Tiny blocks: the weight-streaming MFMA kernel keeps a pass of activation rows over the
+      // whole K in LDS; past its LDS cap they take the 16-row MFMA tile.  The vector-ALU GEMV
+      // alternative reads the plain weight layout only.
+      const bool skinny_fits = skinny_lds_bytes(wfmt_w16, act_quant, g.K) <= kSkinnyMaxLds;
+      const bool use_gemv = tiny == MXQ_TINY_GEMV && !tiled;
+      const int tile = c == 0 ? kClassTile[1] : kClassTile[c];
+      if (c == 0 && use_gemv)
         launch_gemv(g, wfmt_w16, act_quant, mode, out_f32, ub, st);
+      else if (c == 0 && skinny_fits)
+        launch_skinny(g, wfmt_w16, act_quant, mode, out_f32, ub, st);
       else if (act_quant)
-        launch_gemm_w8a8(g, mode, kClassTile[c], out_f32, ub, st);
+        launch_gemm_w8a8(g, mode, tile, out_f32, ub, st);
       else
-        launch_gemm_w16(g, wfmt_w16, mode, kClassTile[c], out_f32, ub, st);
+        launch_gemm_w16(g, wfmt_w16, mode, tile, out_f32, ub, st);
     }
   }
   launch_combine(w.y, wts, ids, E, M, topk, H, static_cast<uint16_t*>(out), st);
@@ -254,7 +274,7 @@ const char* mxq_status_string(mxq_status s) {
   }
 }
 
-int32_t mxq_abi_version(void) { return 2; }
+int32_t mxq_abi_version(void) { return 3; }
 
 mxq_status mxq_init(int32_t device) {
   if (hipSetDevice(device) != hipSuccess) return MXQ_ERR_ARCH;
@@ -381,7 +401,7 @@ mxq_status mxq_moe_align(const int32_t* topk_ids, int64_t M, int32_t topk, int32
   pol.n_classes = 0;
   pol.forced = -1;
   launch_moe_align(topk_ids, M, topk, E, block_m, sorted_ids, expert_ids, offsets, num_blocks,
-                   mxq_moe_max_blocks(M, topk, E, block_m), pol, nullptr, 0, nullptr,
+                   mxq_moe_max_blocks(M, topk, E, block_m), pol, nullptr, 0, nullptr, true,
                    static_cast<hipStream_t>(stream));
   return launch_status();
 }
@@ -406,35 +426,71 @@ static mxq_status moe_common_checks(const void* x, int64_t M, int64_t H, int64_t
 mxq_status mxq_fused_moe_fp8(const void* x, int64_t M, int64_t H, int64_t I, int32_t E, int32_t topk,
                              const int32_t* topk_ids, const float* topk_weights, const void* w1,
                              const float* w1_scale, const void* w2, const float* w2_scale, const float* w1_bias,
-                             int32_t act_quant, void* out, void* workspace, size_t workspace_bytes, void* stream) {
+                             int32_t act_quant, int32_t weight_layout, void* out, void* workspace,
+                             size_t workspace_bytes, void* stream) {
   if (H % 128 != 0 || I % 128 != 0) return MXQ_ERR_SHAPE;
   if (act_quant != 0 && act_quant != 1) return MXQ_ERR_ARG;
+  if (weight_layout != MXQ_LAYOUT_PLAIN && weight_layout != MXQ_LAYOUT_TILED) return MXQ_ERR_ARG;
   MXQ_TRY(moe_common_checks(x, M, H, I, E, topk, topk_ids, topk_weights, w1, w1_scale, w2, w2_scale, out));
   if (M == 0) return MXQ_OK;
   return run_moe(x, M, H, I, E, topk, topk_ids, topk_weights, w1, w1_scale, w2, w2_scale, w1_bias, W_E4M3_BLOCK,
-                 act_quant != 0, out, workspace, workspace_bytes, static_cast<hipStream_t>(stream));
+                 act_quant != 0, weight_layout == MXQ_LAYOUT_TILED, out, workspace, workspace_bytes,
+                 static_cast<hipStream_t>(stream));
 }
 
 mxq_status mxq_fused_moe_mxfp4(const void* x, int64_t M, int64_t H, int64_t I, int32_t E, int32_t topk,
                                const int32_t* topk_ids, const float* topk_weights, const void* w1,
                                const void* w1_scale, const void* w2, const void* w2_scale, const float* w1_bias,
-                               void* out, void* workspace, size_t workspace_bytes, void* stream) {
+                               int32_t weight_layout, void* out, void* workspace, size_t workspace_bytes,
+                               void* stream) {
   if (H % 32 != 0 || I % 32 != 0) return MXQ_ERR_SHAPE;
+  if (weight_layout != MXQ_LAYOUT_PLAIN && weight_layout != MXQ_LAYOUT_TILED) return MXQ_ERR_ARG;
   MXQ_TRY(moe_common_checks(x, M, H, I, E, topk, topk_ids, topk_weights, w1, w1_scale, w2, w2_scale, out));
   if (M == 0) return MXQ_OK;
   return run_moe(x, M, H, I, E, topk, topk_ids, topk_weights, w1, w1_scale, w2, w2_scale, w1_bias, W_E2M1_MX, false,
-                 out, workspace, workspace_bytes, static_cast<hipStream_t>(stream));
+                 weight_layout == MXQ_LAYOUT_TILED, out, workspace, workspace_bytes,
+                 static_cast<hipStream_t>(stream));
 }
 
-mxq_status mxq_moe_set_dispatch(int32_t mode, int32_t forced_class, int32_t gemv_max_rows, int32_t tiny_kernel) {
+size_t mxq_moe_prepack_size(int64_t E, int64_t N, int64_t row_bytes) {
+  if (E <= 0 || N <= 0 || row_bytes <= 0 || N % 16 != 0 || row_bytes % 16 != 0) return 0;
+  return size_t(E) * size_t(N) * size_t(tiled_steps(row_bytes)) * 128;
+}
+
+size_t mxq_moe_prepack_scales_size(int64_t E, int64_t N, int64_t groups) {
+  if (E <= 0 || N <= 0 || groups <= 0 || N % 16 != 0) return 0;
+  return size_t(E) * size_t(N) * size_t(tiled_scale_steps(groups)) * 8;
+}
+
+mxq_status mxq_moe_prepack(const void* w, int64_t E, int64_t N, int64_t row_bytes, void* out, void* stream) {
+  if (E <= 0 || N <= 0 || row_bytes <= 0 || N % 16 != 0 || row_bytes % 16 != 0) return MXQ_ERR_SHAPE;
+  if (!w || !out) return MXQ_ERR_NULL;
+  if (!aligned16(w) || !aligned16(out)) return MXQ_ERR_SHAPE;
+  MXQ_TRY(check_arch());
+  launch_prepack_w(static_cast<const uint8_t*>(w), E, N, row_bytes, static_cast<uint8_t*>(out),
+                   static_cast<hipStream_t>(stream));
+  return launch_status();
+}
+
+mxq_status mxq_moe_prepack_scales(const void* s, int64_t E, int64_t N, int64_t groups, void* out, void* stream) {
+  if (E <= 0 || N <= 0 || groups <= 0 || N % 16 != 0) return MXQ_ERR_SHAPE;
+  if (!s || !out) return MXQ_ERR_NULL;
+  if (reinterpret_cast<uintptr_t>(out) & 1u) return MXQ_ERR_SHAPE;
+  MXQ_TRY(check_arch());
+  launch_prepack_s(static_cast<const uint8_t*>(s), E, N, groups, static_cast<uint8_t*>(out),
+                   static_cast<hipStream_t>(stream));
+  return launch_status();
+}
+
+mxq_status mxq_moe_set_dispatch(int32_t mode, int32_t forced_class, int32_t tiny_max_rows, int32_t tiny_kernel) {
   if (mode < MXQ_DISPATCH_PER_BLOCK || mode > MXQ_DISPATCH_LAYER_AVERAGE) return MXQ_ERR_ARG;
   if (tiny_kernel != MXQ_TINY_MFMA && tiny_kernel != MXQ_TINY_GEMV) return MXQ_ERR_ARG;
   if (forced_class < 0 || forced_class >= kNumClasses) return MXQ_ERR_ARG;
-  if (gemv_max_rows < 0 || gemv_max_rows > 4) return MXQ_ERR_ARG;
+  if (tiny_max_rows < 0 || tiny_max_rows > 16) return MXQ_ERR_ARG;
   std::lock_guard<std::mutex> lk(g_dispatch_mu);
   g_dispatch_mode = mode;
   g_forced_class = forced_class;
-  g_gemv_max_rows = gemv_max_rows;
+  g_tiny_max_rows = tiny_max_rows;
   g_tiny_kernel = tiny_kernel;
   return MXQ_OK;
 }

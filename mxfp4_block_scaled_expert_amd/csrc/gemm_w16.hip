@@ -15,6 +15,9 @@
 // (e4m3 and scaled e2m1 values are exact in bf16); V_MFMA_F32_16X16X32_BF16
 // accumulates in fp32.  A is staged through LDS; K may end on any multiple of
 // 32 (the tail of the last 128-wide step is zero-filled on both operands).
+// Routed weights and MX scales may come in the tiled layout of prepack.hip
+// (TILED): each weight chunk is then read from one contiguous 2 KB tile, and
+// the K tail is already zero in memory.
 #include "tile_rows.hpp"
 
 namespace mxq {
@@ -27,7 +30,7 @@ struct W16Layout {
   static constexpr int chunks = row_bytes / 16;  // 16-byte chunks per row
 };
 
-template <int BM, int BN, int WAVES_M, int MODE, int WFMT, bool OUT_F32, bool HAS_BIAS>
+template <int BM, int BN, int WAVES_M, int MODE, int WFMT, bool OUT_F32, bool HAS_BIAS, bool TILED>
 __global__ __launch_bounds__(256) void gemm_w16_kernel(GemmArgs a, int64_t grid_blocks) {
   constexpr int WAVES_N = 4 / WAVES_M;
   constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
@@ -69,6 +72,9 @@ __global__ __launch_bounds__(256) void gemm_w16_kernel(GemmArgs a, int64_t grid_
   int ka[A_IT];
   const uint8_t* pb[B_IT];
   int kbo[B_IT];
+  int sbo[B_IT];  // LDS byte offset of the chunk
+  // tiled layout: 128-byte row steps per 16-row tile; an MXFP4 K step uses half a row step
+  const int64_t tsteps = (a.K * (MX ? 1 : 2) / 2 + 127) / 128;
 #pragma unroll
   for (int i = 0; i < A_IT; ++i) {
     const int c = min(tid + 256 * i, BM * 16 - 1);
@@ -78,14 +84,34 @@ __global__ __launch_bounds__(256) void gemm_w16_kernel(GemmArgs a, int64_t grid_
 #pragma unroll
   for (int i = 0; i < B_IT; ++i) {
     const int c = min(tid + 256 * i, BN * L::chunks - 1);
-    const int64_t n = min<int64_t>(n0 + c / L::chunks, a.N - 1);
-    kbo[i] = (c % L::chunks) * (MX ? 32 : 16);  // first K element of the chunk
-    pb[i] = Wb + n * a.ldw + (c % L::chunks) * 16;
+    if (TILED) {
+      // FP8: chunk c = bytes 16 (c % 128) of tile c / 128.  MXFP4: the K step is one half
+      // (512 bytes per 1 KB half-tile) of a tile step, chunk c = 16 (c % 32) of half c / 32 % 2.
+      constexpr int CPT = MX ? 64 : 128;  // chunks per tile per K step
+      const int t = c / CPT, p = c % CPT;
+      const int64_t grp16 = min<int64_t>(n0 / 16 + t, a.N / 16 - 1);
+      const int h = MX ? (p >> 5) : (p >> 6);
+      const int L16 = p & 15, qq = MX ? ((p >> 4) & 1) : ((p >> 4) & 3);
+      pb[i] = Wb + grp16 * tsteps * 2048 + h * 1024 + (qq * 16 + L16) * 16;
+      sbo[i] = (16 * t + L16) * L::lds_row + qq * 32 + h * 16;
+      kbo[i] = 0;  // the K tail is zero-padded in memory
+    } else {
+      const int64_t n = min<int64_t>(n0 + c / L::chunks, a.N - 1);
+      kbo[i] = (c % L::chunks) * (MX ? 32 : 16);  // first K element of the chunk
+      pb[i] = Wb + n * a.ldw + (c % L::chunks) * 16;
+      sbo[i] = (c / L::chunks) * L::lds_row + (c % L::chunks) * 16;
+    }
   }
   const uint8_t* pbs = nullptr;
   if (MX) {
-    const int64_t n = min<int64_t>(n0 + min(tid, BN - 1), a.N - 1);
-    pbs = reinterpret_cast<const uint8_t*>(a.ws) + expert * a.ws_estride + n * a.ws_s0;
+    if (TILED) {
+      const int r = min(tid, BN - 1);
+      const int64_t grp16 = min<int64_t>(n0 / 16 + r / 16, a.N / 16 - 1);
+      pbs = reinterpret_cast<const uint8_t*>(a.ws) + expert * a.ws_estride + grp16 * tsteps * 128 + (r & 15) * 2;
+    } else {
+      const int64_t n = min<int64_t>(n0 + min(tid, BN - 1), a.N - 1);
+      pbs = reinterpret_cast<const uint8_t*>(a.ws) + expert * a.ws_estride + n * a.ws_s0;
+    }
   }
 
   uint4 ra[A_IT], rb[B_IT];
@@ -95,11 +121,18 @@ __global__ __launch_bounds__(256) void gemm_w16_kernel(GemmArgs a, int64_t grid_
 #pragma unroll
     for (int i = 0; i < A_IT; ++i)
       ra[i] = (kbase + ka[i] < a.K) ? *reinterpret_cast<const uint4*>(pa[i] + kbase) : make_uint4(0, 0, 0, 0);
+    // byte offset of this K step inside a chunk's row (plain) or tile sequence (tiled)
+    const int64_t bstep = TILED ? (MX ? int64_t(ks >> 1) * 2048 + (ks & 1) * 512 : int64_t(ks) * 2048)
+                                : kbase * L::row_bytes / 128;
 #pragma unroll
     for (int i = 0; i < B_IT; ++i)
-      rb[i] = (kbase + kbo[i] < a.K) ? *reinterpret_cast<const uint4*>(pb[i] + kbase * L::row_bytes / 128)
-                                     : make_uint4(0, 0, 0, 0);
-    if (MX && tid < BN) {
+      rb[i] = (kbase + kbo[i] < a.K) ? *reinterpret_cast<const uint4*>(pb[i] + bstep) : make_uint4(0, 0, 0, 0);
+    if (MX && TILED && tid < BN) {
+      // groups 4 ks .. 4 ks + 3: two byte pairs of the row's scale tile
+      const uint8_t* sp = pbs + int64_t(ks >> 1) * 128 + (ks & 1) * 64;
+      rbs = uint32_t(*reinterpret_cast<const uint16_t*>(sp)) |
+            (uint32_t(*reinterpret_cast<const uint16_t*>(sp + 32)) << 16);
+    } else if (MX && tid < BN) {
       const int g0 = ks * 4;  // first 32-group of this step
       uint32_t v = 0;
       const int ngrp = int(a.K >> 5);
@@ -119,8 +152,7 @@ __global__ __launch_bounds__(256) void gemm_w16_kernel(GemmArgs a, int64_t grid_
 #pragma unroll
     for (int i = 0; i < B_IT; ++i) {
       const int c = tid + 256 * i;
-      if (B_IT * 256 == BN * L::chunks || c < BN * L::chunks)
-        *reinterpret_cast<uint4*>(sB + (c / L::chunks) * L::lds_row + (c % L::chunks) * 16) = rb[i];
+      if (B_IT * 256 == BN * L::chunks || c < BN * L::chunks) *reinterpret_cast<uint4*>(sB + sbo[i]) = rb[i];
     }
     if (MX && tid < BN) sBs[tid] = rbs;
   };
@@ -220,16 +252,27 @@ __global__ __launch_bounds__(256) void gemm_w16_kernel(GemmArgs a, int64_t grid_
   }  // m sub-tiles
 }
 
-template <int BM, int BN, int WAVES_M, int MODE, int WFMT>
-static void launch_w16_t(const GemmArgs& a, bool out_f32, int64_t grid_blocks, hipStream_t st) {
+template <int BM, int BN, int WAVES_M, int MODE, int WFMT, bool TL>
+static void launch_w16_tl(const GemmArgs& a, bool out_f32, int64_t grid_blocks, hipStream_t st) {
   const int64_t n_tiles = cdiv(a.N, BN);
   const dim3 grid(unsigned(grid_blocks * n_tiles)), block(256);
   const bool bias = a.bias != nullptr;
 #define MXQ_W16_GO(OF, HB) \
-  hipLaunchKernelGGL((gemm_w16_kernel<BM, BN, WAVES_M, MODE, WFMT, OF, HB>), grid, block, 0, st, a, grid_blocks)
+  hipLaunchKernelGGL((gemm_w16_kernel<BM, BN, WAVES_M, MODE, WFMT, OF, HB, TL>), grid, block, 0, st, a, grid_blocks)
   if (out_f32) { if (bias) MXQ_W16_GO(true, true); else MXQ_W16_GO(true, false); }
   else { if (bias) MXQ_W16_GO(false, true); else MXQ_W16_GO(false, false); }
 #undef MXQ_W16_GO
+}
+
+template <int BM, int BN, int WAVES_M, int MODE, int WFMT>
+static void launch_w16_t(const GemmArgs& a, bool out_f32, int64_t grid_blocks, hipStream_t st) {
+  if constexpr (MODE != ROWS_DENSE && WFMT != W_E4M3_TENSOR) {
+    if (a.w_tiled) {
+      launch_w16_tl<BM, BN, WAVES_M, MODE, WFMT, true>(a, out_f32, grid_blocks, st);
+      return;
+    }
+  }
+  launch_w16_tl<BM, BN, WAVES_M, MODE, WFMT, false>(a, out_f32, grid_blocks, st);
 }
 
 template <int MODE, int WFMT>

@@ -13,6 +13,8 @@
 // vector ALU (one FMA per accumulator element per K block).
 //
 // Tiles: BM x BN per 256-thread workgroup (4 waves, WAVES_M x WAVES_N), K step 128.
+// Routed weights may come in the tiled layout of prepack.hip (TILED): then each
+// 16-row x 128-byte piece of the weight tile is one contiguous 2 KB tile.
 // Operand tiles are staged through LDS with a 16-byte row pad (no bank
 // conflicts on the 32-byte fragment reads); the next K block's tiles are
 // fetched into registers while the current one is multiplied.
@@ -22,7 +24,7 @@ namespace mxq {
 
 constexpr int kLdsRow = 144;  // 128 data bytes + 16 pad
 
-template <int BM, int BN, int WAVES_M, int MODE, bool SW_COL, bool OUT_F32, bool HAS_BIAS>
+template <int BM, int BN, int WAVES_M, int MODE, bool SW_COL, bool OUT_F32, bool HAS_BIAS, bool TILED>
 __global__ __launch_bounds__(256) void gemm_w8a8_kernel(GemmArgs a, int64_t grid_blocks) {
   constexpr int WAVES_N = 4 / WAVES_M;
   constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
@@ -62,6 +64,8 @@ __global__ __launch_bounds__(256) void gemm_w8a8_kernel(GemmArgs a, int64_t grid
   // per-thread global chunk coordinates (16-byte chunks, 8 per 128-byte row)
   const uint8_t* pa[A_IT];
   const uint8_t* pb[B_IT];
+  int sbo[B_IT];  // LDS byte offset of the chunk
+  constexpr int B_KSTRIDE = TILED ? 2048 : 128;  // bytes between consecutive K blocks of one chunk
 #pragma unroll
   for (int i = 0; i < A_IT; ++i) {
     const int c = min(tid + 256 * i, BM * 8 - 1);
@@ -70,8 +74,17 @@ __global__ __launch_bounds__(256) void gemm_w8a8_kernel(GemmArgs a, int64_t grid
 #pragma unroll
   for (int i = 0; i < B_IT; ++i) {
     const int c = min(tid + 256 * i, BN * 8 - 1);
-    const int64_t n = min<int64_t>(n0 + (c >> 3), a.N - 1);
-    pb[i] = Wb + n * a.ldw + (c & 7) * 16;
+    if (TILED) {
+      // chunk c = 16 contiguous bytes of tile c / 128 (consecutive threads read one 2 KB tile)
+      const int t = c >> 7, p = c & 127, L = p & 63;
+      const int64_t grp16 = min<int64_t>(n0 / 16 + t, a.N / 16 - 1);
+      pb[i] = Wb + grp16 * KB * 2048 + p * 16;
+      sbo[i] = (16 * t + (L & 15)) * kLdsRow + (L >> 4) * 32 + (p >> 6) * 16;
+    } else {
+      const int64_t n = min<int64_t>(n0 + (c >> 3), a.N - 1);
+      pb[i] = Wb + n * a.ldw + (c & 7) * 16;
+      sbo[i] = (c >> 3) * kLdsRow + (c & 7) * 16;
+    }
   }
   const float* psa = a.sa + sArow[min(tid, BM - 1)] * a.lds;
 
@@ -82,7 +95,7 @@ __global__ __launch_bounds__(256) void gemm_w8a8_kernel(GemmArgs a, int64_t grid
     _Pragma("unroll") for (int i = 0; i < A_IT; ++i) ra[i] =                                   \
         *reinterpret_cast<const i32x4*>(pa[i] + (KB) * 128);                                   \
     _Pragma("unroll") for (int i = 0; i < B_IT; ++i) rb[i] =                                   \
-        *reinterpret_cast<const i32x4*>(pb[i] + (KB) * 128);                                   \
+        *reinterpret_cast<const i32x4*>(pb[i] + (KB) * B_KSTRIDE);                             \
     rsa = psa[KB];                                                                             \
   } while (0)
 
@@ -109,8 +122,7 @@ __global__ __launch_bounds__(256) void gemm_w8a8_kernel(GemmArgs a, int64_t grid
 #pragma unroll
     for (int i = 0; i < B_IT; ++i) {
       const int c = tid + 256 * i;
-      if (B_IT * 256 == BN * 8 || c < BN * 8)
-        *reinterpret_cast<i32x4*>(sB + (c >> 3) * kLdsRow + (c & 7) * 16) = rb[i];
+      if (B_IT * 256 == BN * 8 || c < BN * 8) *reinterpret_cast<i32x4*>(sB + sbo[i]) = rb[i];
     }
     if (tid < BM) sSa[tid] = rsa;
     __syncthreads();
@@ -184,13 +196,13 @@ __global__ __launch_bounds__(256) void gemm_w8a8_kernel(GemmArgs a, int64_t grid
 #undef MXQ_W8A8_GLOAD
 }
 
-template <int BM, int BN, int WAVES_M, int MODE>
-static void launch_w8a8_t(const GemmArgs& a, bool sw_col, bool out_f32, int64_t grid_blocks, hipStream_t st) {
+template <int BM, int BN, int WAVES_M, int MODE, bool TL>
+static void launch_w8a8_tl(const GemmArgs& a, bool sw_col, bool out_f32, int64_t grid_blocks, hipStream_t st) {
   const int64_t n_tiles = cdiv(a.N, BN);
   const dim3 grid(unsigned(grid_blocks * n_tiles)), block(256);
   const bool bias = a.bias != nullptr;
 #define MXQ_W8A8_GO(SWC, OF, HB) \
-  hipLaunchKernelGGL((gemm_w8a8_kernel<BM, BN, WAVES_M, MODE, SWC, OF, HB>), grid, block, 0, st, a, grid_blocks)
+  hipLaunchKernelGGL((gemm_w8a8_kernel<BM, BN, WAVES_M, MODE, SWC, OF, HB, TL>), grid, block, 0, st, a, grid_blocks)
   if (sw_col) {
     if (out_f32) { if (bias) MXQ_W8A8_GO(true, true, true); else MXQ_W8A8_GO(true, true, false); }
     else { if (bias) MXQ_W8A8_GO(true, false, true); else MXQ_W8A8_GO(true, false, false); }
@@ -199,6 +211,17 @@ static void launch_w8a8_t(const GemmArgs& a, bool sw_col, bool out_f32, int64_t 
     else { if (bias) MXQ_W8A8_GO(false, false, true); else MXQ_W8A8_GO(false, false, false); }
   }
 #undef MXQ_W8A8_GO
+}
+
+template <int BM, int BN, int WAVES_M, int MODE>
+static void launch_w8a8_t(const GemmArgs& a, bool sw_col, bool out_f32, int64_t grid_blocks, hipStream_t st) {
+  if constexpr (MODE != ROWS_DENSE) {
+    if (a.w_tiled) {
+      launch_w8a8_tl<BM, BN, WAVES_M, MODE, true>(a, sw_col, out_f32, grid_blocks, st);
+      return;
+    }
+  }
+  launch_w8a8_tl<BM, BN, WAVES_M, MODE, false>(a, sw_col, out_f32, grid_blocks, st);
 }
 
 template <int MODE>

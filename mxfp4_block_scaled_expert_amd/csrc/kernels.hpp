@@ -40,6 +40,7 @@ struct GemmArgs {
   const uint8_t* W;
   int64_t ldw;          // bytes per weight row
   int64_t w_estride;    // bytes per expert
+  int32_t w_tiled;      // routed weights (and MX scales) in the tiled layout of prepack.hip
   const void* ws;       // fp32 block grid | fp32 scalar | e8m0 [N, K/32] bytes
   int64_t ws_s0, ws_s1; // grid strides (elements); for e8m0: row stride (bytes)
   int64_t ws_estride;   // per expert (elements or bytes)
@@ -83,7 +84,13 @@ void launch_gemv(const GemmArgs& a, int wfmt, bool a_e4m3, int row_mode, bool ou
 void launch_skinny(const GemmArgs& a, int wfmt, bool a_e4m3, int row_mode, bool out_f32, int64_t grid_blocks,
                    hipStream_t stream);
 // Dynamic LDS the weight-streaming kernel takes for reduction length K.
-size_t skinny_lds_bytes(bool a_e4m3, int64_t K);
+size_t skinny_lds_bytes(int wfmt, bool a_e4m3, int64_t K);
+
+// Load-time relayout into the tiled layout (see prepack.hip).
+int64_t tiled_steps(int64_t row_bytes);
+int64_t tiled_scale_steps(int64_t groups);
+void launch_prepack_w(const uint8_t* w, int64_t E, int64_t N, int64_t row_bytes, uint8_t* out, hipStream_t stream);
+void launch_prepack_s(const uint8_t* s, int64_t E, int64_t N, int64_t groups, uint8_t* out, hipStream_t stream);
 
 // Expert sort / block alignment.  Optionally also fills per-class work lists
 // (class_lists[c * list_stride + i], class_counts[c]) using the per-block selector.
@@ -91,11 +98,12 @@ struct ClassPolicy {
   int32_t n_classes;      // 0: no class lists
   int32_t bound[8];       // class c takes blocks with bound[c-1] < m_size <= bound[c]
   int32_t forced;         // >= 0: every non-empty block goes to this class
+  int32_t n_live;         // classes >= n_live are not launched; their blocks go to class n_live - 1
 };
 void launch_moe_align(const int32_t* topk_ids, int64_t M, int32_t topk, int32_t E, int32_t block_m,
                       int32_t* sorted_ids, int32_t* expert_ids, int32_t* offsets, int32_t* num_blocks,
                       int64_t max_blocks, const ClassPolicy& pol, int32_t* class_lists, int64_t list_stride,
-                      int32_t* class_counts, hipStream_t stream);
+                      int32_t* class_counts, bool write_pads, hipStream_t stream);
 
 // ic1 = bf16(silu(gate) * up) over compact rows; optionally re-quantised 1x128 to e4m3.
 void launch_silu_mul(const uint16_t* ic0, int64_t rows, int64_t inter, uint16_t* ic1_bf16, uint8_t* ic1_q,

@@ -16,7 +16,10 @@
 // The per-block selector (implementation items 1-2: the decision is taken per
 // expert block from its real row count, not once per layer from an average)
 // assigns every non-empty block to the smallest tile class whose row bound
-// holds it and appends the block id to that class's work list.
+// holds it and appends the block id to that class's work list.  Classes the
+// host did not launch (their lower bound reaches the token count, which caps an
+// expert's rows when a token's experts are distinct) receive nothing: a block
+// past every launched bound goes to the largest launched class.
 #include "kernels.hpp"
 #include "quant_common.hpp"
 
@@ -27,16 +30,16 @@ constexpr int kAlignWaves = kAlignThreads / 64;
 
 __device__ __forceinline__ int pick_class(const ClassPolicy& pol, int m_size) {
   if (pol.forced >= 0) return pol.forced;
-  for (int c = 0; c < pol.n_classes - 1; ++c)
+  for (int c = 0; c < pol.n_live - 1; ++c)
     if (m_size <= pol.bound[c]) return c;
-  return pol.n_classes - 1;
+  return pol.n_live - 1;  // the tile kernels loop over row sub-tiles, so any block fits
 }
 
 __global__ __launch_bounds__(kAlignThreads) void moe_align_kernel(
     const int32_t* __restrict__ ids, int64_t R, int32_t E, int32_t block_m, int32_t* __restrict__ sorted_ids,
     int32_t* __restrict__ expert_ids, int32_t* __restrict__ offsets, int32_t* __restrict__ num_blocks,
     int64_t max_blocks, ClassPolicy pol, int32_t* __restrict__ class_lists, int64_t list_stride,
-    int32_t* __restrict__ class_counts) {
+    int32_t* __restrict__ class_counts, int write_pads) {
   extern __shared__ int32_t smem[];
   int32_t* cnt = smem;                     // [E]
   int32_t* blk_start = cnt + E;            // [E + 1]
@@ -107,7 +110,7 @@ __global__ __launch_bounds__(kAlignThreads) void moe_align_kernel(
   const int rows_total = row_start[E];
   if (tid == 0) *num_blocks = nblocks;
 
-  // 3. block table, class lists, and pad slots
+  // 3. block table and class lists
   for (int e = tid; e < E; e += kAlignThreads) {
     const int c_e = cnt[e];
     for (int b = 0; b * block_m < c_e; ++b) {
@@ -115,7 +118,6 @@ __global__ __launch_bounds__(kAlignThreads) void moe_align_kernel(
       const int m_size = min(block_m, c_e - b * block_m);
       expert_ids[mb] = e;
       offsets[mb] = row_start[e] + b * block_m;
-      for (int i = m_size; i < block_m; ++i) sorted_ids[int64_t(mb) * block_m + i] = int32_t(R);
       if (pol.n_classes > 0) {
         const int c = pick_class(pol, m_size);
         const int pos = atomicAdd(&cls_cnt[c], 1);
@@ -126,9 +128,26 @@ __global__ __launch_bounds__(kAlignThreads) void moe_align_kernel(
   for (int64_t mb = nblocks + tid; mb < max_blocks; mb += kAlignThreads) {
     expert_ids[mb] = -1;
     offsets[mb] = rows_total;
-    for (int i = 0; i < block_m; ++i) sorted_ids[mb * block_m + i] = int32_t(R);
   }
   if (tid == 0) offsets[max_blocks] = rows_total;
+  // pad slots (slots past a block's rows, and every slot of a trailing block) hold R; the
+  // fused path never reads them and skips this
+  if (write_pads) {
+    for (int64_t idx = tid; idx < max_blocks * block_m; idx += kAlignThreads) {
+      const int64_t mb = idx / block_m;
+      const int i = int(idx - mb * block_m);
+      bool pad = mb >= nblocks;
+      if (!pad) {
+        int lo = 0, hi = E;  // the expert e with blk_start[e] <= mb < blk_start[e + 1]
+        while (hi - lo > 1) {
+          const int mid = (lo + hi) >> 1;
+          if (blk_start[mid] <= mb) lo = mid; else hi = mid;
+        }
+        pad = i >= cnt[lo] - int(mb - blk_start[lo]) * block_m;
+      }
+      if (pad) sorted_ids[idx] = int32_t(R);
+    }
+  }
   __syncthreads();
   if (pol.n_classes > 0 && tid < pol.n_classes) class_counts[tid] = cls_cnt[tid];
 
@@ -170,12 +189,12 @@ __global__ __launch_bounds__(kAlignThreads) void moe_align_kernel(
 void launch_moe_align(const int32_t* topk_ids, int64_t M, int32_t topk, int32_t E, int32_t block_m,
                       int32_t* sorted_ids, int32_t* expert_ids, int32_t* offsets, int32_t* num_blocks,
                       int64_t max_blocks, const ClassPolicy& pol, int32_t* class_lists, int64_t list_stride,
-                      int32_t* class_counts, hipStream_t stream) {
+                      int32_t* class_counts, bool write_pads, hipStream_t stream) {
   // cnt[E] + blk_start[E+1] + row_start[E+1] + running[E] + wave_cnt[waves][E]
   const size_t smem = sizeof(int32_t) * (size_t(E) * 4 + 2 + size_t(kAlignWaves) * E);
   hipLaunchKernelGGL(moe_align_kernel, dim3(1), dim3(kAlignThreads), smem, stream, topk_ids, M * topk, E, block_m,
                      sorted_ids, expert_ids, offsets, num_blocks, max_blocks, pol, class_lists, list_stride,
-                     class_counts);
+                     class_counts, write_pads ? 1 : 0);
 }
 
 // ---------------------------------------------------------------- SiLU-and-mul

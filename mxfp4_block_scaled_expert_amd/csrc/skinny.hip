@@ -1,218 +1,349 @@
-// Weight-streaming kernel for tiny routed expert blocks (at most 4 rows) on gfx950.
+// Weight-streaming kernel for tiny routed expert blocks on gfx950.
 //
 // "vLLM PR 50949 review" (implementation items 1-2, gemm.h listing): an expert
 // block with few rows wants a fixed-row micro-kernel, not a large tile.  Such a
 // block is bound by reading its expert's weights once, so this kernel is built
 // around streaming them at HBM speed:
 //
-//  * each wave owns 16 weight rows and walks K in steps of 128 bytes per row;
-//    lane (row r = lane % 16, q = lane / 16) loads the 32 contiguous bytes
-//    [32q, 32q + 32) of row r's step straight into registers (whole 128-byte
-//    lines per four lanes), through a 4-deep register ring, so ~6 KB per wave
-//    are in flight and the weights never touch LDS;
-//  * each 32-element K slice is one V_MFMA_F32_16X16X32_BF16.  The MFMA sums
-//    over whatever K elements a lane supplies as long as both operands use the
-//    same assignment, so slice s of lane group q takes the lane's own bytes
-//    (elements 32q + 8s .. +8 of an e4m3 step, 64q + 8s .. +8 of an e2m1 step)
-//    and the activation operand reads the same elements from LDS;
-//  * weights are decoded to bf16 in registers (e4m3 exactly; e2m1 with its
-//    e8m0 scale folded in), activation rows 4..15 of the MFMA are zero, and the
-//    vector ALU only decodes: the K reduction happens in the matrix core;
-//  * e4m3 block weights are promoted per 128-wide K block with their fp32
-//    scale (times the per-token activation scale for W8A8); MXFP4 needs none.
+//  * a workgroup owns 64 * G weight rows of one expert block; wave w owns the
+//    16-row groups w, w + 4, ..., and walks K in steps of 128 bytes per row,
+//    K-outer: each step loads the step's bytes of all G groups, so one
+//    activation fragment read from LDS feeds G MFMAs;
+//  * lane (r = lane % 16, q = lane / 16) loads bytes [32q, 32q + 32) of row r's
+//    step straight into registers through a D-deep ring (no LDS for weights);
+//    loads are issued unconditionally (past-the-end steps read a valid dummy
+//    address) so the compiler's wait before a step counts only newer loads;
+//  * the first D - 1 steps are requested before the activation rows are staged,
+//    so the staging latency overlaps the weight stream;
+//  * e2m1 (MXFP4) and e4m3 weights with bf16 activations are decoded to bf16 and
+//    reduced by V_MFMA_F32_16X16X32_BF16 (e8m0 scale folded into the decode;
+//    e4m3 block scales applied per 128-wide K block); with e4m3 activations
+//    (W8A8) both operands go to V_MFMA_F32_16X16X128_F8F6F4 undecoded and the
+//    two block scales are applied per K block;
+//  * MFMA rows past the block's row count read activation row 0 and are never
+//    stored, so the loop needs no lane masking; activation rows are zero-padded
+//    in LDS to a whole number of steps, which covers a ragged K tail;
+//  * AR activation rows (4 or 8) are staged per pass; a taller block takes
+//    several passes over the same weights;
+//  * with weights in the tiled layout (prepack.hip) a step of one 16-row group
+//    is 2 KB of contiguous memory, so each 64-lane load reads 1 KB in one piece;
+//    the plain layout reads 16 rows x 64 bytes per load instead.
 #include "tile_rows.hpp"
 
 namespace mxq {
 
 namespace {
-constexpr int kSkRows = 16;   // weight rows per wave
 constexpr int kSkWaves = 4;
-constexpr int kSkTileN = kSkRows * kSkWaves;
-constexpr int kSkDepth = 4;   // register ring depth (steps)
-constexpr int kSkActRows = 4;
+constexpr int kSkMaxRows = 8;
+
+// groups per wave (G) and ring depth in steps (D) per weight / activation format
+// groups per wave (G), ring depth in steps (D) and the waves per SIMD the register
+// budget targets (W), per weight / activation format; chosen by measurement on the
+// decode workload (no register spills at these budgets)
+template <int WFMT, bool AE>
+struct SkinnyShape {
+  static constexpr int G = 2;
+  static constexpr int D = 3;
+  static constexpr int W = WFMT == W_E2M1_MX ? 3 : 4;
+};
 }  // namespace
 
-template <int WFMT, bool A_E4M3, int MODE, bool OUT_F32, bool HAS_BIAS>
-__global__ __launch_bounds__(256) void skinny_kernel(GemmArgs a, int64_t grid_blocks) {
+// LDS layout (bytes): activation rows [AR][row_stride] | weight scales [K/128][nb] | act scales [K/128][AR]
+struct SkinnyLds {
+  int row_stride, kpad, kb, nb;
+  uint32_t sw_off, sa_off, total;
+};
+
+__host__ __device__ inline SkinnyLds skinny_lds_layout(bool mx, bool a_e4m3, int64_t K, int G, int AR) {
+  SkinnyLds L;
+  const int kstep = mx ? 256 : 128;
+  const int ae = a_e4m3 ? 1 : 2;
+  L.kpad = int((K + kstep - 1) / kstep) * kstep;
+  L.row_stride = L.kpad * ae + 16;  // +16 B: rows read together fall in different LDS banks
+  L.kb = int(K >> 7);
+  L.nb = G >= 2 ? G / 2 : 1;
+  L.sw_off = uint32_t(AR * L.row_stride);
+  const uint32_t sw_bytes = mx ? 0u : uint32_t(L.kb * L.nb * 4);
+  L.sa_off = (L.sw_off + sw_bytes + 15u) & ~15u;
+  L.total = L.sa_off + (a_e4m3 ? uint32_t(L.kb * AR * 4) : 0u);
+  return L;
+}
+
+template <int WFMT, bool A_E4M3, int MODE, bool OUT_F32, bool HAS_BIAS, bool TILED, int AR, int G, int D>
+__global__ __launch_bounds__(256, (SkinnyShape<WFMT, A_E4M3>::W)) void skinny_kernel(GemmArgs a,
+                                                                                     int64_t grid_blocks) {
   constexpr bool MX = WFMT == W_E2M1_MX;
   constexpr int KSTEP = MX ? 256 : 128;  // K elements per 128-byte row step
-  constexpr int SUBS = KSTEP / 32;       // MFMA K slices per step
-  constexpr int EPL = KSTEP / 4;         // K elements per lane per step
   constexpr int AE = A_E4M3 ? 1 : 2;     // activation bytes per element
+  static_assert(!(MX && A_E4M3), "MXFP4 weights take bf16 activations");
+  static_assert(AR == 4 || AR == 8, "four or eight activation rows per pass");
 
   extern __shared__ __align__(16) uint8_t smem[];
-  float* s_sa = reinterpret_cast<float*>(smem);                 // W8A8: [4][K/128]
-  uint8_t* act = smem + (A_E4M3 ? kSkActRows * ((a.K >> 7) + 4) * 4 : 0);  // [4][K] activations
-  __shared__ int64_t s_arow[kSkActRows];
-  __shared__ int64_t s_orow[kSkActRows];
+  __shared__ int64_t s_arow[AR];
+  __shared__ int64_t s_orow[AR];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l16 = lane & 15, q = lane >> 4;
-  const int64_t tile = blockIdx.x % grid_blocks;
-  const int64_t nt = blockIdx.x / grid_blocks;
-  const int64_t n0 = nt * kSkTileN;
-  if (n0 >= a.N) return;
+  const int64_t N = a.N, K = a.K;
+  const int64_t ntiles = (N + 64 * G - 1) / (64 * G);
+  // n-tile fastest: concurrently running workgroups stream adjacent rows of one expert
+  const int64_t tile = blockIdx.x / ntiles;
+  const int64_t nt = blockIdx.x - tile * ntiles;
+  if (tile >= grid_blocks) return;
   TileInfo t;
   if (!tile_info<1, MODE>(a, tile, t)) return;
-  const int64_t expert = t.expert;
-  const int64_t K = a.K;
-  const int nsteps = int(cdiv(K, KSTEP));
-  const int KB = int(K >> 7);
-  const int64_t nw = n0 + wave * kSkRows;
-  const int64_t nrow = min<int64_t>(nw + l16, a.N - 1);
-  const uint8_t* wrow = a.W + expert * a.w_estride + nrow * a.ldw;
-  const int64_t row_bytes = MX ? K / 2 : K;
-  const uint8_t* srow = MX ? reinterpret_cast<const uint8_t*>(a.ws) + expert * a.ws_estride + nrow * a.ws_s0 : nullptr;
-  const float* swf = reinterpret_cast<const float*>(a.ws) + expert * a.ws_estride +
-                     (min<int64_t>(nw, a.N - 1) >> 7) * a.ws_s0;
 
-  for (int m_base = 0; m_base < t.m_total; m_base += kSkActRows) {
-    const int m_size = min(kSkActRows, t.m_total - m_base);
-    __syncthreads();
-    if (tid < kSkActRows) {
+  const SkinnyLds L = skinny_lds_layout(MX, A_E4M3, K, G, AR);
+  const int nsteps = L.kpad / KSTEP;
+  const int64_t n0 = nt * 64 * G;
+  const int64_t row_bytes = MX ? K / 2 : K;
+  const bool ragged = !TILED && MX && (row_bytes & 127) != 0;
+
+  // per-group offsets inside the expert (32-bit: an expert's weights stay below 4 GB)
+  const uint8_t* wexp = a.W + t.expert * a.w_estride;
+  uint32_t woff[G];  // plain: row * ldw + 32 q;  tiled: first tile of the group + 16 lane
+  uint32_t soff[G];  // MXFP4 scales.  plain: row * (K / 32);  tiled: first tile + 2 lane
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    if (TILED) {
+      const int64_t grp16 = min<int64_t>(n0 / 16 + g * kSkWaves + wave, N / 16 - 1);
+      woff[g] = uint32_t(grp16 * nsteps * 2048 + lane * 16);
+      soff[g] = MX ? uint32_t(grp16 * nsteps * 128 + lane * 2) : 0u;
+    } else {
+      const int64_t row = min<int64_t>(n0 + (g * kSkWaves + wave) * 16 + l16, N - 1);
+      woff[g] = uint32_t(row * a.ldw + q * 32);
+      soff[g] = MX ? uint32_t(row * a.ws_s0) : 0u;
+    }
+  }
+  const uint8_t* sexp = MX ? reinterpret_cast<const uint8_t*>(a.ws) + t.expert * a.ws_estride : nullptr;
+  const int64_t ngroups = K / 32;  // MXFP4 scale groups per row
+
+  i32x4 wb[D][G][2];
+  uint32_t sb[D][G][2];  // raw e8m0 bytes, combined only where used
+
+  // all weight / scale addresses are a wave-uniform base plus a 32-bit lane offset
+  auto load = [&](int st, int slot) __attribute__((always_inline)) {
+    const uint32_t sc = uint32_t(min(st, nsteps - 1));
+    if (TILED) {
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        wb[slot][g][0] = *reinterpret_cast<const i32x4*>(wexp + woff[g] + sc * 2048u);
+        wb[slot][g][1] = *reinterpret_cast<const i32x4*>(wexp + woff[g] + sc * 2048u + 1024u);
+        if (MX) {
+          const uint32_t v = *reinterpret_cast<const uint16_t*>(sexp + soff[g] + sc * 128u);
+          sb[slot][g][0] = v & 0xffu;
+          sb[slot][g][1] = v >> 8;
+        }
+      }
+      return;
+    }
+    const uint32_t in_row = sc * 128u + uint32_t(q) * 32u;
+    const bool past0 = ragged && int64_t(in_row) + 16 > row_bytes;
+    const bool past1 = ragged && int64_t(in_row) + 32 > row_bytes;
+    const uint32_t g0 = min(sc * 8u + 2u * uint32_t(q), uint32_t(ngroups - 1));
+    const uint32_t g1 = min(sc * 8u + 2u * uint32_t(q) + 1u, uint32_t(ngroups - 1));
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      // 16-byte halves past the row end (ragged K) re-read the row's first bytes:
+      // finite codes whose activations are the zero padding
+      const uint32_t rowo = woff[g] - uint32_t(q) * 32u;
+      const uint32_t o0 = past0 ? rowo : woff[g] + sc * 128u;
+      const uint32_t o1 = past1 ? rowo : woff[g] + sc * 128u + 16u;
+      wb[slot][g][0] = *reinterpret_cast<const i32x4*>(wexp + o0);
+      wb[slot][g][1] = *reinterpret_cast<const i32x4*>(wexp + o1);
+      if (MX) {
+        sb[slot][g][0] = sexp[soff[g] + g0];
+        sb[slot][g][1] = sexp[soff[g] + g1];
+      }
+    }
+  };
+
+  for (int m_base = 0; m_base < t.m_total; m_base += AR) {
+    const int m_size = min(AR, t.m_total - m_base);
+    __syncthreads();  // the previous pass is done with LDS
+
+    // request the first steps of the weight stream before staging the activations
+#pragma unroll
+    for (int u = 0; u < D - 1; ++u) load(u, u);
+
+    if (tid < AR) {
       int64_t ar, orw;
       row_of<MODE>(a, t, m_base + min(tid, m_size - 1), ar, orw);
       s_arow[tid] = ar;
       s_orow[tid] = orw;
     }
     __syncthreads();
-    // ---- stage the activation rows (and their per-token scales for W8A8) in LDS
     {
-      const int64_t chunks = K * AE / 16;
-      for (int64_t c = tid; c < kSkActRows * chunks; c += blockDim.x) {
-        const int m = int(c / chunks);
-        const int64_t cc = c - m * chunks;
-        const uint8_t* g = reinterpret_cast<const uint8_t*>(a.A) + s_arow[m] * a.lda * AE + cc * 16;
-        *reinterpret_cast<i32x4*>(act + m * K * AE + cc * 16) = *reinterpret_cast<const i32x4*>(g);
+      // activation rows (rows >= m_size are never read), zero-padded to whole steps
+      const int chunks = L.kpad * AE / 16;
+      const int kchunks = int(K * AE / 16);
+      for (int c = tid; c < m_size * chunks; c += 256) {
+        const int m = c / chunks, cc = c - m * chunks;
+        i32x4 v = {0, 0, 0, 0};
+        if (cc < kchunks)
+          v = *reinterpret_cast<const i32x4*>(reinterpret_cast<const uint8_t*>(a.A) + s_arow[m] * a.lda * AE +
+                                               int64_t(cc) * 16);
+        *reinterpret_cast<i32x4*>(smem + m * L.row_stride + cc * 16) = v;
       }
-      if (A_E4M3)
-        for (int c = tid; c < kSkActRows * KB; c += blockDim.x) {
-          const int m = c / KB, kb = c - m * KB;
-          s_sa[m * KB + kb] = a.sa[s_arow[m] * a.lds + kb];
+      if (!MX) {
+        // weight block scales of the workgroup's n-blocks, [kb][nb]
+        float* s_sw = reinterpret_cast<float*>(smem + L.sw_off);
+        const float* swe = reinterpret_cast<const float*>(a.ws) + t.expert * a.ws_estride;
+        const int64_t nb_total = (N + 127) / 128;
+        for (int c = tid; c < L.kb * L.nb; c += 256) {
+          const int kb = c / L.nb, nb = c - kb * L.nb;
+          const int64_t gnb = min<int64_t>((n0 >> 7) + nb, nb_total - 1);
+          s_sw[c] = swe[gnb * a.ws_s0 + kb * a.ws_s1];
         }
+      }
+      if (A_E4M3) {
+        // per-token activation scales, [kb][AR]; rows past m_size repeat valid rows
+        float* s_sa = reinterpret_cast<float*>(smem + L.sa_off);
+        for (int c = tid; c < L.kb * AR; c += 256) {
+          const int kb = c / AR, m = c - kb * AR;
+          s_sa[c] = a.sa[s_arow[m] * a.lds + kb];
+        }
+      }
     }
     __syncthreads();
 
-    // ---- stream the wave's 16 weight rows through a register ring
-    i32x4 wb[kSkDepth][2];
-    uint32_t sb[kSkDepth][2];  // raw e8m0 bytes, combined only where used
-    float swr[kSkDepth];
-    auto load = [&](int st, int slot) __attribute__((always_inline)) {
-      // 16-byte halves wholly past the row end (K tail) fetch the row's first line instead
-      const int64_t off = int64_t(st) * 128 + q * 32;
-      wb[slot][0] = *reinterpret_cast<const i32x4*>(wrow + (off + 16 <= row_bytes ? off : 0));
-      wb[slot][1] = *reinterpret_cast<const i32x4*>(wrow + (off + 32 <= row_bytes ? off + 16 : 0));
-      if (MX) {
-        // this lane's two 32-element groups; indices past the row are clamped (never
-        // branched around: a load under a branch would make the compiler drain the ring)
-        const int64_t grp = int64_t(st) * 8 + 2 * q;
-        const int64_t ng = row_bytes / 16;
-        sb[slot][0] = srow[min(grp, ng - 1)];
-        sb[slot][1] = srow[min(grp + 1, ng - 1)];
-      } else {
-        swr[slot] = swf[min(st, KB - 1) * a.ws_s1];
-      }
-    };
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    const bool arow_ok = l16 < m_size;
-    const uint8_t* arow_lds = act + (arow_ok ? l16 : 0) * K * AE;
+    f32x4 acc[G];
+#pragma unroll
+    for (int g = 0; g < G; ++g) acc[g] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const uint8_t* arow = smem + (l16 < m_size ? l16 : 0) * L.row_stride;
+    const float* s_sw = reinterpret_cast<const float*>(smem + L.sw_off);
+    const float* s_sa = reinterpret_cast<const float*>(smem + L.sa_off);
+    const int sa_q = min(q, AR / 4 - 1);  // lanes past the staged rows hold unused outputs
+
     auto compute = [&](int st, int slot) __attribute__((always_inline)) {
-      f32x4 part = {0.f, 0.f, 0.f, 0.f};
+      if constexpr (MX) {
 #pragma unroll
-      for (int s = 0; s < SUBS; ++s) {
-        const int64_t k0 = int64_t(st) * KSTEP + q * EPL + 8 * s;
-        // a lane's 8 elements lie wholly inside or wholly past K (K % 32 == 0)
-        const bool kin = k0 + 8 <= K;
-        i32x4 af = {0, 0, 0, 0};
-        if (arow_ok && kin) {
-          if (A_E4M3) {
-            const uint2 v = *reinterpret_cast<const uint2*>(arow_lds + k0);
+        for (int s = 0; s < 8; ++s) {
+          const i32x4 af = *reinterpret_cast<const i32x4*>(arow + (st * KSTEP + q * 64 + 8 * s) * 2);
+#pragma unroll
+          for (int g = 0; g < G; ++g) {
+            uint32_t o[4];
+            e2m1x8_to_bf16(uint32_t(wb[slot][g][s >> 2][s & 3]), e8m0_to_f32(sb[slot][g][s >> 2]), o);
+            acc[g] = mfma_16x16x32_bf16(af, i32x4{int(o[0]), int(o[1]), int(o[2]), int(o[3])}, acc[g]);
+          }
+        }
+      } else if constexpr (A_E4M3) {
+        const i32x4 a0 = *reinterpret_cast<const i32x4*>(arow + st * KSTEP + q * 32);
+        const i32x4 a1 = *reinterpret_cast<const i32x4*>(arow + st * KSTEP + q * 32 + 16);
+        const i32x8 af = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
+        const f32x4 sa = *reinterpret_cast<const f32x4*>(s_sa + st * AR + 4 * sa_q);
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+          const i32x4 w0 = wb[slot][g][0];
+          const i32x4 w1 = wb[slot][g][1];
+          const i32x8 bf = {w0[0], w0[1], w0[2], w0[3], w1[0], w1[1], w1[2], w1[3]};
+          const f32x4 part = mfma_16x16x128_e4m3(af, bf, f32x4{0.f, 0.f, 0.f, 0.f});
+          const float sw = s_sw[st * L.nb + ((g * kSkWaves + wave) >> 3)];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) acc[g][r] = fmaf(part[r], sw * sa[r], acc[g][r]);
+        }
+      } else {
+        f32x4 part[G];
+#pragma unroll
+        for (int g = 0; g < G; ++g) part[g] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          const i32x4 af = *reinterpret_cast<const i32x4*>(arow + (st * KSTEP + q * 32 + 8 * s) * 2);
+#pragma unroll
+          for (int g = 0; g < G; ++g) {
             uint32_t o0, o1, o2, o3;
-            e4m3x4_to_bf16(v.x, o0, o1);
-            e4m3x4_to_bf16(v.y, o2, o3);
-            af = i32x4{int(o0), int(o1), int(o2), int(o3)};
-          } else {
-            af = *reinterpret_cast<const i32x4*>(arow_lds + k0 * 2);
+            e4m3x4_to_bf16(uint32_t(wb[slot][g][s >> 1][(2 * s) & 3]), o0, o1);
+            e4m3x4_to_bf16(uint32_t(wb[slot][g][s >> 1][(2 * s + 1) & 3]), o2, o3);
+            part[g] = mfma_16x16x32_bf16(af, i32x4{int(o0), int(o1), int(o2), int(o3)}, part[g]);
           }
         }
-        i32x4 bfr;
-        if (MX) {
-          const float sc = e8m0_to_f32(sb[slot][s >> 2]);
-          uint32_t o[4];
-          e2m1x8_to_bf16(uint32_t(wb[slot][s >> 2][s & 3]), sc, o);
-          bfr = i32x4{int(o[0]), int(o[1]), int(o[2]), int(o[3])};
-        } else {
-          uint32_t o0, o1, o2, o3;
-          e4m3x4_to_bf16(uint32_t(wb[slot][s >> 1][(2 * s) & 3]), o0, o1);
-          e4m3x4_to_bf16(uint32_t(wb[slot][s >> 1][(2 * s + 1) & 3]), o2, o3);
-          bfr = i32x4{int(o0), int(o1), int(o2), int(o3)};
-        }
-        if (MX)
-          acc = mfma_16x16x32_bf16(af, bfr, acc);
-        else
-          part = mfma_16x16x32_bf16(af, bfr, part);
-      }
-      if (!MX) {
-        const float sw = swr[slot];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          float c = sw;
-          if (A_E4M3) {
-            const int m = 4 * q + r;
-            c *= (m < m_size) ? s_sa[(m < kSkActRows ? m : 0) * KB + st] : 0.f;
-          }
-          acc[r] = fmaf(part[r], c, acc[r]);
+        for (int g = 0; g < G; ++g) {
+          const float sw = s_sw[st * L.nb + ((g * kSkWaves + wave) >> 3)];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) acc[g][r] = fmaf(part[g][r], sw, acc[g][r]);
         }
       }
     };
 
-    // Loads are issued unconditionally (steps past the end read valid dummy addresses) and
-    // the loop has no early exit, so the wait before each step's compute counts only the
-    // newer steps' loads and the ring stays full.
+    for (int st0 = 0; st0 < nsteps; st0 += D) {
 #pragma unroll
-    for (int u = 0; u < kSkDepth - 1; ++u) load(u, u);
-    for (int st0 = 0; st0 < nsteps; st0 += kSkDepth) {
-#pragma unroll
-      for (int u = 0; u < kSkDepth; ++u) {
-        load(st0 + u + kSkDepth - 1, (u + kSkDepth - 1) % kSkDepth);
+      for (int u = 0; u < D; ++u) {
+        load(st0 + u + D - 1, (u + D - 1) % D);
         if (st0 + u < nsteps) compute(st0 + u, u);
       }
     }
 
-    // ---- epilogue: lane holds D[m = 4q + r][n = l16]
-    const int64_t col = nw + l16;
-    if (col < a.N) {
-      const float b = HAS_BIAS ? load_bias(a, expert, col) : 0.f;
+    // epilogue: lane (l16, q) holds D[4q + r][l16] of each group
+    if (4 * q < m_size) {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int m = 4 * q + r;
-        if (m >= m_size) continue;
-        const int64_t o = s_orow[m] * a.ldo + col;
-        const float v = acc[r] + b;
-        if (OUT_F32)
-          reinterpret_cast<float*>(a.out)[o] = v;
-        else
-          reinterpret_cast<uint16_t*>(a.out)[o] = f2bf(v);
+      for (int g = 0; g < G; ++g) {
+        const int64_t col = n0 + (g * kSkWaves + wave) * 16 + l16;
+        if (col >= N) continue;
+        const float b = HAS_BIAS ? load_bias(a, t.expert, col) : 0.f;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int m = 4 * q + r;
+          if (m >= m_size) continue;
+          const int64_t o = s_orow[m] * a.ldo + col;
+          const float v = acc[g][r] + b;
+          if (OUT_F32)
+            reinterpret_cast<float*>(a.out)[o] = v;
+          else
+            reinterpret_cast<uint16_t*>(a.out)[o] = f2bf(v);
+        }
       }
     }
   }
 }
 
-size_t skinny_lds_bytes(bool a_e4m3, int64_t K) {
-  return size_t(kSkActRows) * size_t(K) * (a_e4m3 ? 1 : 2) +
-         (a_e4m3 ? size_t(kSkActRows) * size_t((K >> 7) + 4) * 4 : 0);
+template <int WFMT, bool AE>
+static size_t skinny_lds_t(int64_t K, int AR) {
+  return skinny_lds_layout(WFMT == W_E2M1_MX, AE, K, SkinnyShape<WFMT, AE>::G, AR).total;
+}
+
+// Activation rows per pass: eight while the LDS stays within kSkLdsCap (so that several
+// workgroups still share a compute unit), else four.
+#ifndef MXQ_SK_AR8_CAP
+#define MXQ_SK_AR8_CAP (32 * 1024)
+#endif
+constexpr size_t kSkLdsCap = MXQ_SK_AR8_CAP;
+template <int WFMT, bool AE>
+static int skinny_rows_t(int64_t K) {
+  return skinny_lds_t<WFMT, AE>(K, 8) <= kSkLdsCap ? 8 : 4;
+}
+
+size_t skinny_lds_bytes(int wfmt, bool a_e4m3, int64_t K) {
+  if (wfmt == W_E2M1_MX) return skinny_lds_t<W_E2M1_MX, false>(K, skinny_rows_t<W_E2M1_MX, false>(K));
+  if (a_e4m3) return skinny_lds_t<W_E4M3_BLOCK, true>(K, skinny_rows_t<W_E4M3_BLOCK, true>(K));
+  return skinny_lds_t<W_E4M3_BLOCK, false>(K, skinny_rows_t<W_E4M3_BLOCK, false>(K));
+}
+
+template <int WFMT, bool AE, int MODE, bool TL, int AR>
+static void launch_skinny_ar(const GemmArgs& a, bool out_f32, int64_t gb, hipStream_t st) {
+  constexpr int G = SkinnyShape<WFMT, AE>::G;
+  constexpr int D = SkinnyShape<WFMT, AE>::D;
+  const int64_t n_tiles = cdiv(a.N, int64_t(64 * G));
+  const dim3 grid(static_cast<unsigned>(gb * n_tiles)), block(256);
+  const size_t lds = skinny_lds_t<WFMT, AE>(a.K, AR);
+  const bool bias = a.bias != nullptr;
+#define MXQ_SK_GO(OF, HB) \
+  hipLaunchKernelGGL((skinny_kernel<WFMT, AE, MODE, OF, HB, TL, AR, G, D>), grid, block, lds, st, a, gb)
+  if (out_f32) { if (bias) MXQ_SK_GO(true, true); else MXQ_SK_GO(true, false); }
+  else { if (bias) MXQ_SK_GO(false, true); else MXQ_SK_GO(false, false); }
+#undef MXQ_SK_GO
 }
 
 template <int WFMT, bool AE, int MODE>
 static void launch_skinny_t(const GemmArgs& a, bool out_f32, int64_t gb, hipStream_t st) {
-  const int64_t n_tiles = cdiv(a.N, kSkTileN);
-  const dim3 grid(static_cast<unsigned>(gb * n_tiles)), block(256);
-  const size_t lds = skinny_lds_bytes(AE, a.K);
-  const bool bias = a.bias != nullptr;
-#define MXQ_SK_GO(OF, HB) hipLaunchKernelGGL((skinny_kernel<WFMT, AE, MODE, OF, HB>), grid, block, lds, st, a, gb)
-  if (out_f32) { if (bias) MXQ_SK_GO(true, true); else MXQ_SK_GO(true, false); }
-  else { if (bias) MXQ_SK_GO(false, true); else MXQ_SK_GO(false, false); }
-#undef MXQ_SK_GO
+  const bool eight = skinny_rows_t<WFMT, AE>(a.K) == 8;
+  if (a.w_tiled) {
+    if (eight) launch_skinny_ar<WFMT, AE, MODE, true, 8>(a, out_f32, gb, st);
+    else launch_skinny_ar<WFMT, AE, MODE, true, 4>(a, out_f32, gb, st);
+  } else {
+    if (eight) launch_skinny_ar<WFMT, AE, MODE, false, 8>(a, out_f32, gb, st);
+    else launch_skinny_ar<WFMT, AE, MODE, false, 4>(a, out_f32, gb, st);
+  }
 }
 
 template <int MODE>

@@ -215,9 +215,62 @@ def fused_moe_workspace(M: int, H: int, I: int, E: int, topk: int, weights: int,
     return torch.empty(max(n, 1), dtype=torch.uint8, device=device)
 
 
+_LAYOUTS = {"plain": L.MXQ_LAYOUT_PLAIN, "tiled": L.MXQ_LAYOUT_TILED}
+
+
+def _layout(weight_layout: str) -> int:
+    if weight_layout not in _LAYOUTS:
+        raise ValueError(f"weight_layout must be 'plain' or 'tiled', got {weight_layout!r}")
+    return _LAYOUTS[weight_layout]
+
+
+def _tiled_row(row_bytes: int) -> int:
+    return -(-row_bytes // 128) * 128
+
+
+def moe_prepack(w: torch.Tensor) -> torch.Tensor:
+    """Routed-expert weights [E, N, row_bytes] (e4m3 or packed e2m1 codes) -> the tiled layout
+    of ``mxq_moe_prepack``, returned as uint8 [E, N, ceil(row_bytes / 128) * 128]."""
+    w = _as_u8(w, "w").contiguous()
+    if w.dim() != 3:
+        raise ValueError("w must be [E, N, row_bytes]")
+    _require_cuda(w)
+    E, N, rb = w.shape
+    lib = L.load()
+    n = lib.mxq_moe_prepack_size(E, N, rb)
+    if n == 0:
+        raise ValueError(f"N ({N}) and row_bytes ({rb}) must be positive multiples of 16")
+    out = torch.empty((E, N, _tiled_row(rb)), dtype=torch.uint8, device=w.device)
+    assert out.numel() == n
+    L.check("mxq_moe_prepack", lib.mxq_moe_prepack(w.data_ptr(), E, N, rb, out.data_ptr(), _stream()))
+    return out
+
+
+def moe_prepack_scales(s: torch.Tensor) -> torch.Tensor:
+    """e8m0 MX scales [E, N, groups] -> the tiled layout of ``mxq_moe_prepack_scales``, returned as
+    uint8 [E, N, ceil(groups / 8) * 8]."""
+    if s.dtype != torch.uint8 or s.dim() != 3:
+        raise ValueError("scales must be uint8 [E, N, groups]")
+    _require_cuda(s)
+    s = s.contiguous()
+    E, N, G = s.shape
+    lib = L.load()
+    n = lib.mxq_moe_prepack_scales_size(E, N, G)
+    if n == 0:
+        raise ValueError(f"N ({N}) must be a positive multiple of 16")
+    out = torch.empty((E, N, -(-G // 8) * 8), dtype=torch.uint8, device=s.device)
+    assert out.numel() == n
+    L.check("mxq_moe_prepack_scales", lib.mxq_moe_prepack_scales(s.data_ptr(), E, N, G, out.data_ptr(), _stream()))
+    return out
+
+
 def fused_moe_fp8(x, topk_ids, topk_weights, w1, w1_scale, w2, w2_scale, w1_bias=None, act_quant=False,
-                  workspace: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """Routed MoE with block-FP8 experts (W8A16, or W8A8 with ``act_quant``) -> bf16 [M, H]."""
+                  workspace: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
+                  weight_layout: str = "plain") -> torch.Tensor:
+    """Routed MoE with block-FP8 experts (W8A16, or W8A8 with ``act_quant``) -> bf16 [M, H].
+
+    ``weight_layout="tiled"``: ``w1`` / ``w2`` come from :func:`moe_prepack`."""
+    layout = _layout(weight_layout)
     x, ids, wts = _moe_common(x, topk_ids, topk_weights)
     w1 = _as_u8(w1, "w1").contiguous()
     w2 = _as_u8(w2, "w2").contiguous()
@@ -226,8 +279,9 @@ def fused_moe_fp8(x, topk_ids, topk_weights, w1, w1_scale, w2, w2_scale, w1_bias
     E, two_i, h1 = w1.shape
     I = two_i // 2
     topk = ids.shape[1]
-    if h1 != H or tuple(w2.shape) != (E, H, I):
-        raise ValueError("w1 must be [E, 2I, H] and w2 [E, H, I]")
+    rb1, rb2 = (H, I) if layout == L.MXQ_LAYOUT_PLAIN else (_tiled_row(H), _tiled_row(I))
+    if h1 != rb1 or tuple(w2.shape) != (E, H, rb2):
+        raise ValueError(f"w1 must be [E, 2I, {rb1}] and w2 [E, H, {rb2}] for the {weight_layout} layout")
     if tuple(w1_scale.shape) != (E, -(-2 * I // 128), H // 128) or tuple(w2_scale.shape) != (E, -(-H // 128), I // 128):
         raise ValueError("block scales must be [E, ceil(2I/128), H/128] and [E, ceil(H/128), I/128]")
     s1 = w1_scale.float().contiguous()
@@ -239,14 +293,18 @@ def fused_moe_fp8(x, topk_ids, topk_weights, w1, w1_scale, w2, w2_scale, w1_bias
         workspace = fused_moe_workspace(M, H, I, E, topk, L.MXQ_WEIGHTS_FP8_BLOCK, act_quant, x.device)
     st = L.load().mxq_fused_moe_fp8(x.data_ptr(), M, H, I, E, topk, ids.data_ptr(), wts.data_ptr(), w1.data_ptr(),
                                     s1.data_ptr(), w2.data_ptr(), s2.data_ptr(), _ptr(b1), int(bool(act_quant)),
-                                    out.data_ptr(), workspace.data_ptr(), workspace.numel(), _stream())
+                                    layout, out.data_ptr(), workspace.data_ptr(), workspace.numel(), _stream())
     L.check("mxq_fused_moe_fp8", st)
     return out
 
 
 def fused_moe_mxfp4(x, topk_ids, topk_weights, w1, w1_scale, w2, w2_scale, w1_bias=None,
-                    workspace: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """Routed MoE with MXFP4 experts (packed e2m1 + e8m0 per 32), bf16 activations -> bf16 [M, H]."""
+                    workspace: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
+                    weight_layout: str = "plain") -> torch.Tensor:
+    """Routed MoE with MXFP4 experts (packed e2m1 + e8m0 per 32), bf16 activations -> bf16 [M, H].
+
+    ``weight_layout="tiled"``: weights from :func:`moe_prepack`, scales from :func:`moe_prepack_scales`."""
+    layout = _layout(weight_layout)
     x, ids, wts = _moe_common(x, topk_ids, topk_weights)
     w1 = w1.contiguous()
     w2 = w2.contiguous()
@@ -260,10 +318,15 @@ def fused_moe_mxfp4(x, topk_ids, topk_weights, w1, w1_scale, w2, w2_scale, w1_bi
     E, two_i, hh = w1.shape
     I = two_i // 2
     topk = ids.shape[1]
-    if hh * 2 != H or tuple(w2.shape) != (E, H, I // 2):
-        raise ValueError("w1 must be [E, 2I, H/2] and w2 [E, H, I/2]")
-    if tuple(s1.shape) != (E, 2 * I, H // 32) or tuple(s2.shape) != (E, H, I // 32):
-        raise ValueError("scales must be [E, 2I, H/32] and [E, H, I/32]")
+    if layout == L.MXQ_LAYOUT_PLAIN:
+        rb1, rb2, g1, g2 = H // 2, I // 2, H // 32, I // 32
+    else:
+        rb1, rb2 = _tiled_row(H // 2), _tiled_row(I // 2)
+        g1, g2 = -(-(H // 32) // 8) * 8, -(-(I // 32) // 8) * 8
+    if hh != rb1 or tuple(w2.shape) != (E, H, rb2):
+        raise ValueError(f"w1 must be [E, 2I, {rb1}] and w2 [E, H, {rb2}] for the {weight_layout} layout")
+    if tuple(s1.shape) != (E, 2 * I, g1) or tuple(s2.shape) != (E, H, g2):
+        raise ValueError(f"scales must be [E, 2I, {g1}] and [E, H, {g2}] for the {weight_layout} layout")
     b1 = None if w1_bias is None else w1_bias.float().contiguous()
     if out is None:
         out = torch.empty((M, H), dtype=torch.bfloat16, device=x.device)
@@ -271,11 +334,11 @@ def fused_moe_mxfp4(x, topk_ids, topk_weights, w1, w1_scale, w2, w2_scale, w1_bi
         workspace = fused_moe_workspace(M, H, I, E, topk, L.MXQ_WEIGHTS_MXFP4, False, x.device)
     st = L.load().mxq_fused_moe_mxfp4(x.data_ptr(), M, H, I, E, topk, ids.data_ptr(), wts.data_ptr(),
                                       w1.data_ptr(), s1.data_ptr(), w2.data_ptr(), s2.data_ptr(), _ptr(b1),
-                                      out.data_ptr(), workspace.data_ptr(), workspace.numel(), _stream())
+                                      layout, out.data_ptr(), workspace.data_ptr(), workspace.numel(), _stream())
     L.check("mxq_fused_moe_mxfp4", st)
     return out
 
 
-def moe_set_dispatch(mode: int = L.MXQ_DISPATCH_PER_BLOCK, forced_class: int = 0, gemv_max_rows: int = 4,
+def moe_set_dispatch(mode: int = L.MXQ_DISPATCH_PER_BLOCK, forced_class: int = 0, tiny_max_rows: int = 16,
                      tiny_kernel: int = L.MXQ_TINY_MFMA) -> None:
-    L.check("mxq_moe_set_dispatch", L.load().mxq_moe_set_dispatch(mode, forced_class, gemv_max_rows, tiny_kernel))
+    L.check("mxq_moe_set_dispatch", L.load().mxq_moe_set_dispatch(mode, forced_class, tiny_max_rows, tiny_kernel))

@@ -28,7 +28,7 @@ def _declared():
 def test_header_declares_the_entry_points():
     names = _declared()
     for n in ("mxq_per_token_group_quant_fp8", "mxq_fp8_scaled_mm", "mxq_block_fp8_linear", "mxq_moe_align",
-              "mxq_fused_moe_fp8", "mxq_fused_moe_mxfp4"):
+              "mxq_fused_moe_fp8", "mxq_fused_moe_mxfp4", "mxq_moe_prepack", "mxq_moe_prepack_scales"):
         assert n in names
 
 
@@ -42,7 +42,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_status_strings_and_version():
     L, lib = _lib()
-    assert lib.mxq_abi_version() == 2
+    assert lib.mxq_abi_version() == 3
     for code in range(0, 9):
         assert lib.mxq_status_string(code)
     assert b"unknown" in lib.mxq_status_string(99)
@@ -82,17 +82,39 @@ def test_argument_errors_before_any_launch():
     assert lib.mxq_per_token_group_quant_fp8(null, 0, 256, 256, 128, null, null, null) == L.MXQ_OK
     assert lib.mxq_fp8_scaled_mm(null, 4, 100, 100, null, 8, null, null, 0, null, 8, null) == L.MXQ_ERR_SHAPE
     assert lib.mxq_fp8_scaled_mm(null, 4, 128, 128, null, 8, null, null, 7, null, 8, null) == L.MXQ_ERR_NULL
-    assert lib.mxq_fused_moe_fp8(null, 4, 100, 128, 8, 2, null, null, null, null, null, null, null, 0, null, null, 0,
-                                 null) == L.MXQ_ERR_SHAPE
-    assert lib.mxq_fused_moe_mxfp4(null, 4, 100, 128, 8, 2, null, null, null, null, null, null, null, null, null, 0,
+    assert lib.mxq_fused_moe_fp8(null, 4, 100, 128, 8, 2, null, null, null, null, null, null, null, 0, 0, null, null,
+                                 0, null) == L.MXQ_ERR_SHAPE
+    assert lib.mxq_fused_moe_mxfp4(null, 4, 100, 128, 8, 2, null, null, null, null, null, null, null, 0, null, null, 0,
                                    null) == L.MXQ_ERR_SHAPE
-    assert lib.mxq_fused_moe_fp8(null, 4, 256, 128, 8, 2, null, null, null, null, null, null, null, 0, null, null, 0,
-                                 null) == L.MXQ_ERR_NULL
+    assert lib.mxq_fused_moe_fp8(null, 4, 256, 128, 8, 2, null, null, null, null, null, null, null, 0, 0, null, null,
+                                 0, null) == L.MXQ_ERR_NULL
+    assert lib.mxq_fused_moe_fp8(null, 4, 256, 128, 8, 2, null, null, null, null, null, null, null, 0, 2, null, null,
+                                 0, null) == L.MXQ_ERR_ARG
+    assert lib.mxq_fused_moe_mxfp4(null, 4, 256, 128, 8, 2, null, null, null, null, null, null, null, 5, null, null,
+                                   0, null) == L.MXQ_ERR_ARG
+    # load-time relayout: N and row bytes multiples of 16
+    assert lib.mxq_moe_prepack(null, 2, 24, 128, null, null) == L.MXQ_ERR_SHAPE
+    assert lib.mxq_moe_prepack(null, 2, 32, 136, null, null) == L.MXQ_ERR_SHAPE
+    assert lib.mxq_moe_prepack(null, 2, 32, 128, null, null) == L.MXQ_ERR_NULL
+    assert lib.mxq_moe_prepack_scales(null, 2, 24, 90, null, null) == L.MXQ_ERR_SHAPE
+    assert lib.mxq_moe_prepack_scales(null, 2, 32, 90, null, null) == L.MXQ_ERR_NULL
     assert lib.mxq_moe_align(null, 4, 2, 2000, 16, null, null, null, null, null) == L.MXQ_ERR_SHAPE
     assert lib.mxq_moe_set_dispatch(7, 0, 4, 0) == L.MXQ_ERR_ARG
-    assert lib.mxq_moe_set_dispatch(0, 0, 9, 0) == L.MXQ_ERR_ARG
+    assert lib.mxq_moe_set_dispatch(0, 0, 17, 0) == L.MXQ_ERR_ARG
     assert lib.mxq_moe_set_dispatch(0, 0, 4, 5) == L.MXQ_ERR_ARG
-    assert lib.mxq_moe_set_dispatch(0, 0, 4, 0) == L.MXQ_OK
+    assert lib.mxq_moe_set_dispatch(0, 0, 8, 0) == L.MXQ_OK
+
+
+def test_prepack_size_queries():
+    _, lib = _lib()
+    # weights: E * N * ceil(row_bytes / 128) * 128
+    assert lib.mxq_moe_prepack_size(128, 5760, 1440) == 128 * 5760 * 1536
+    assert lib.mxq_moe_prepack_size(256, 4096, 7168) == 256 * 4096 * 7168
+    assert lib.mxq_moe_prepack_size(2, 24, 128) == 0
+    # MX scales: E * N * ceil(groups / 8) * 8
+    assert lib.mxq_moe_prepack_scales_size(128, 5760, 90) == 128 * 5760 * 96
+    assert lib.mxq_moe_prepack_scales_size(1, 16, 8) == 16 * 8
+    assert lib.mxq_moe_prepack_scales_size(1, 8, 8) == 0
 
 
 def test_binding_rejects_bad_block_size_without_gpu():

@@ -25,9 +25,9 @@ pytestmark = pytest.mark.gpu
 
 @pytest.fixture(autouse=True)
 def _default_dispatch():
-    ops.moe_set_dispatch(mx.MXQ_DISPATCH_PER_BLOCK, 0, 4)
+    ops.moe_set_dispatch()
     yield
-    ops.moe_set_dispatch(mx.MXQ_DISPATCH_PER_BLOCK, 0, 4)
+    ops.moe_set_dispatch()
 
 
 # ------------------------------------------------------------------ align
