@@ -46,6 +46,10 @@ int g_forced_class = 0;
 int g_tiny_max_rows = 16;
 int g_tiny_kernel = MXQ_TINY_MFMA;
 constexpr size_t kSkinnyMaxLds = 64 * 1024;
+#ifndef MXQ_DENSE_BIG_BM
+#define MXQ_DENSE_BIG_BM 256
+#endif
+constexpr int kDenseBigBM = MXQ_DENSE_BIG_BM;  // tile rows of the large dense W8A8 GEMM
 
 constexpr int kMoeBlockM = 128;
 constexpr int kNumClasses = 5;  // tiny-block kernel, 16-, 32-, 64-, 128-row MFMA tiles
@@ -242,6 +246,9 @@ mxq_status run_moe(const void* x, int64_t M, int64_t H, int64_t I, int32_t E, in
         launch_gemv(g, wfmt_w16, act_quant, mode, out_f32, ub, st);
       else if (c == 0 && skinny_fits)
         launch_skinny(g, wfmt_w16, act_quant, mode, out_f32, ub, st);
+      else if (act_quant && c == kNumClasses - 1 && g.K <= 16384)
+        // blocks of 65..128 rows: the 128 x 256 three-stage direct-to-LDS tile
+        launch_gemm_w8a8_big(g, mode, 128, out_f32, ub, st);
       else if (act_quant)
         launch_gemm_w8a8(g, mode, tile, out_f32, ub, st);
       else
@@ -377,7 +384,7 @@ mxq_status mxq_block_fp8_linear(const void* A, int32_t a_dtype, const float* a_s
   g.K = K;
   if (block_n == 128 && M > 128 && K <= 16384 && int64_t(M) * lqa < (int64_t(1) << 32) &&
       N * K < (int64_t(1) << 32)) {
-    launch_gemm_w8a8_big(g, ROWS_DENSE, false, cdiv(M, 256), st);
+    launch_gemm_w8a8_big(g, ROWS_DENSE, kDenseBigBM, false, cdiv(M, kDenseBigBM), st);
   } else {
     const int tile = dense_tile_for(M);
     launch_gemm_w8a8(g, ROWS_DENSE, tile, false, cdiv(M, tile_rows(tile)), st);

@@ -25,7 +25,7 @@ namespace mxq {
 constexpr int kLdsRow = 144;  // 128 data bytes + 16 pad
 
 template <int BM, int BN, int WAVES_M, int MODE, bool SW_COL, bool OUT_F32, bool HAS_BIAS, bool TILED>
-__global__ __launch_bounds__(256) void gemm_w8a8_kernel(GemmArgs a, int64_t grid_blocks) {
+__global__ __launch_bounds__(256, 2) void gemm_w8a8_kernel(GemmArgs a, int64_t grid_blocks) {
   constexpr int WAVES_N = 4 / WAVES_M;
   constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
   constexpr int TM = WM / 16, TN = WN / 16;
@@ -126,6 +126,18 @@ __global__ __launch_bounds__(256) void gemm_w8a8_kernel(GemmArgs a, int64_t grid
     }
     if (tid < BM) sSa[tid] = rsa;
     __syncthreads();
+    // this block's weight scales are loaded before the next block's operands: loads retire
+    // in order, so waiting for the scales does not wait for the prefetch
+    float sw_tile = 1.f;
+    float swc[TN];
+    if (!SW_COL) sw_tile = swb[nb_scale * a.ws_s0 + kb * a.ws_s1];
+    if (SW_COL) {
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        const int64_t n = min<int64_t>(n0 + wn * WN + 16 * j + frow, a.N - 1);
+        swc[j] = swb[n * a.ws_s0 + kb * a.ws_s1];
+      }
+    }
     if (kb + 1 < KB) MXQ_W8A8_GLOAD(kb + 1);
 
     i32x8 af[TM], bfr[TN];
@@ -144,32 +156,31 @@ __global__ __launch_bounds__(256) void gemm_w8a8_kernel(GemmArgs a, int64_t grid
       bfr[j] = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
     }
     float cs[TM][4];
-    float sw_tile = 1.f;
-    if (!SW_COL) sw_tile = swb[nb_scale * a.ws_s0 + kb * a.ws_s1];
 #pragma unroll
     for (int i = 0; i < TM; ++i)
 #pragma unroll
       for (int r = 0; r < 4; ++r) cs[i][r] = sSa[wm * WM + 16 * i + 4 * (lane >> 4) + r] * sw_tile;
-    float swc[TN];
-    if (SW_COL) {
-#pragma unroll
-      for (int j = 0; j < TN; ++j) {
-        const int64_t n = min<int64_t>(n0 + wn * WN + 16 * j + frow, a.N - 1);
-        swc[j] = swb[n * a.ws_s0 + kb * a.ws_s1];
-      }
-    }
     const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+    // Products t = TN * i + j run as a software pipeline: step t issues the MFMA of product
+    // t + 2 and promotes product t, whose MFMA went out two MFMAs earlier, from a ring of
+    // three partial-sum registers; the fence after each step keeps that order.
+    constexpr int NT = TM * TN, DIST = NT < 2 ? NT : 2, NB = DIST + 1;
+    f32x4 pb[NB];
 #pragma unroll
-    for (int i = 0; i < TM; ++i)
+    for (int t = 0; t < DIST; ++t) pb[t] = mfma_16x16x128_e4m3(af[t / TN], bfr[t % TN], zero);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int j = 0; j < TN; ++j) {
-        const f32x4 p = mfma_16x16x128_e4m3(af[i], bfr[j], zero);
+    for (int t = 0; t < NT; ++t) {
+      const int tm = t + DIST;
+      if (tm < NT) pb[tm % NB] = mfma_16x16x128_e4m3(af[tm / TN], bfr[tm % TN], zero);
+      const int i = t / TN, j = t % TN;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float c = SW_COL ? cs[i][r] * swc[j] : cs[i][r];
-          acc[i][j][r] = fmaf(p[r], c, acc[i][j][r]);
-        }
+      for (int r = 0; r < 4; ++r) {
+        const float c = SW_COL ? cs[i][r] * swc[j] : cs[i][r];
+        acc[i][j][r] = fmaf(pb[t % NB][r], c, acc[i][j][r]);
       }
+      __builtin_amdgcn_sched_barrier(0);
+    }
   }
 
   // epilogue: lane holds rows 4*(lane/16)+r of each 16x16 tile, column lane%16

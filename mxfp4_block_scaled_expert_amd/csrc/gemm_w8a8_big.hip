@@ -1,39 +1,53 @@
-// Large-tile block-scaled W8A8 GEMM for gfx950: 256 x 256 output tile per
+// Large-tile block-scaled W8A8 GEMM for gfx950: BM x 256 output tile per
 // 512-thread workgroup (8 waves, 2 per SIMD), K step 128 = one weight-scale
-// block = one V_MFMA_F32_16X16X128_F8F6F4 per 16 x 16 sub-tile.
+// block = one V_MFMA_F32_16X16X128_F8F6F4 per 16 x 16 sub-tile.  BM = 256 (two
+// LDS stages) or 128 (three stages: one more K block in flight).
 //
 // Arithmetic ("SGLang PR 35605 review", implementation item 1 and the
 // fp8_utils.py listing): out[m, n] = sum_kb sa[m, kb] * sw[n/128, kb] *
 // sum_{k in kb} qa[m, k] * w[n, k] (+ bias), fp32 accumulation, bf16 (or fp32)
 // output.  Each K block's partial product is formed on the matrix core from
-// zero and promoted into the fp32 accumulator with one FMA by sa * sw.
+// zero and promoted into the fp32 accumulator with one FMA by sa * sw.  The
+// routed-expert stages ("vLLM PR 50949 review", moe_fp8.cpp listing) run the
+// same tile over an expert block's rows.
 //
 // gfx950 specifics:
 //  * operands go global -> LDS with GLOBAL_LOAD_LDS_DWORDX4 (no VGPR staging):
-//    one instruction moves 64 x 16 bytes = 8 rows of a 128-byte K slice; the
-//    16-byte chunk c of row r is stored at chunk position c ^ swz(r), which
-//    keeps the 32-byte fragment reads free of bank conflicts;
-//  * two LDS stages (2 x 64 KB of the 160 KB) and one barrier per K block: the
-//    loads of block kb+1 are in flight while block kb is multiplied;
+//    one instruction moves 64 x 16 bytes.  Plain-layout rows: 8 rows of a
+//    128-byte K slice, 16-byte chunk c of row r stored at chunk c ^ swz(r) so the
+//    32-byte fragment reads are free of bank conflicts.  Tiled weights (the
+//    load-time layout of prepack.hip): half of one 2 KB tile, stored as is, which
+//    is already the fragment order (lane L reads 16 bytes at 16 L and 1024 + 16 L);
 //  * the MFMA A operand is the weight tile and the B operand the activation
 //    tile, so each lane ends up owning four consecutive output columns of one
 //    row: one activation scale per lane per sub-tile and 8-byte (bf16) or
 //    16-byte (fp32) stores;
-//  * waves are laid out 2 (rows) x 4 (columns); a wave owns 128 x 64 outputs,
-//    so its 64 weight rows sit inside one 128-wide scale block (one scalar
-//    weight scale per wave per K block);
+//  * waves are laid out 2 (rows) x 4 (columns); a wave owns BM/2 x 64 outputs,
+//    so its 64 weight rows sit inside one 128-wide scale block (one weight scale
+//    per wave per K block, staged in LDS for all K blocks up front);
+//  * the products of a K block run as a software pipeline (the MFMA of product
+//    t + 2 is issued before product t is promoted);
 //  * dense tiles are rastered so that the tiles resident on one XCD (the
 //    dispatcher deals workgroups round-robin over the 8 XCDs) share operands in
-//    that XCD's L2.
+//    that XCD's L2, and every K block's operands are touched in L2 one block
+//    before their DMA.
 #include "tile_rows.hpp"
 
 namespace mxq {
 
 namespace {
 
-constexpr int kBM = 256, kBN = 256, kKS = 128;
+constexpr int kBN = 256, kKS = 128;
 constexpr int kThreads = 512;
 constexpr int kMaxKB = 128;  // K <= 16384 on this kernel
+
+template <int BM>
+struct BigCfg {
+  static constexpr int STAGES = BM == 256 ? 2 : 3;
+  static constexpr int TI = BM / 32;     // 16-row sub-tiles per wave (a wave covers BM / 2 rows)
+  static constexpr int A_DMA = BM / 64;  // 1 KB activation DMAs per wave per K block
+  static constexpr int STAGE_BYTES = (BM + kBN) * kKS;
+};
 
 __device__ __forceinline__ int swz(int row) { return (row & 7) ^ ((row >> 3) & 1); }
 
@@ -44,10 +58,10 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 }
 
 // GLOBAL_LOAD_LDS (each lane's `size` bytes land at M0 + lane * size).  Issued
-// as inline asm so the compiler does not treat the loads of the next K block
-// as a hazard for the LDS reads of the current one (it cannot tell the two
-// stages apart and would wait for the DMA before every fragment read); the
-// kernel waits on vmcnt itself before each barrier.
+// as inline asm so the compiler does not treat the loads of a later K block
+// as a hazard for the LDS reads of the current one (it cannot tell the stages
+// apart and would wait for the DMA before every fragment read); the kernel
+// waits on vmcnt itself before each barrier.
 __device__ __forceinline__ void lds_dma16(const void* g, uint32_t lds) {
   asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(lds)
                : "memory", "m0");
@@ -57,7 +71,7 @@ __device__ __forceinline__ void lds_dma4(const void* g, uint32_t lds) {
                : "memory", "m0");
 }
 
-// 32-byte fragment of row `row` (K chunks 2q, 2q+1) from a swizzled tile.
+// 32-byte fragment of row `row` (K chunks 2q, 2q+1) from a swizzled row-major tile.
 __device__ __forceinline__ i32x8 read_frag(const uint8_t* tile, int row, int q) {
   const int s = swz(row);
   const uint8_t* base = tile + row * kKS;
@@ -66,20 +80,32 @@ __device__ __forceinline__ i32x8 read_frag(const uint8_t* tile, int row, int q) 
   return i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
 }
 
+// Fragment of 16-row group g of a tile stored in the tiled (lane) order.
+__device__ __forceinline__ i32x8 read_frag_tiled(const uint8_t* tile, int g, int lane) {
+  const uint8_t* base = tile + g * 2048 + lane * 16;
+  const i32x4 lo = *reinterpret_cast<const i32x4*>(base);
+  const i32x4 hi = *reinterpret_cast<const i32x4*>(base + 1024);
+  return i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt immediate");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
 }  // namespace
 
-template <int MODE, bool OUT_F32, bool HAS_BIAS>
+template <int BM, int MODE, bool OUT_F32, bool HAS_BIAS, bool TILED>
 __global__ __launch_bounds__(kThreads) void gemm_w8a8_big_kernel(GemmArgs a, int64_t grid_blocks, int64_t n_tiles) {
-  __shared__ __align__(1024) uint8_t sA0[kBM * kKS];
-  __shared__ __align__(1024) uint8_t sA1[kBM * kKS];
-  __shared__ __align__(1024) uint8_t sB0[kBN * kKS];
-  __shared__ __align__(1024) uint8_t sB1[kBN * kKS];
-  __shared__ __align__(16) float sS0[kBM];
-  __shared__ __align__(16) float sS1[kBM];
-  __shared__ int64_t sArow[kBM];
-  __shared__ int64_t sOrow[kBM];
-  __shared__ float sSW[2][kMaxKB];
-  __shared__ __align__(256) float sPF[kThreads];  // landing area of the L2 prefetch (never read)  // weight scales of the tile's two 128-wide column blocks, all K blocks
+  using C = BigCfg<BM>;
+  constexpr int S = C::STAGES, TI = C::TI, NT = 4 * TI;
+  __shared__ __align__(1024) uint8_t sOps[S * C::STAGE_BYTES];  // stage s: A [BM][128] then W [256][128]
+  __shared__ __align__(16) float sS[S][BM];
+  __shared__ int64_t sArow[BM];
+  __shared__ int64_t sOrow[BM];
+  __shared__ float sSW[2][kMaxKB];  // weight scales of the tile's two 128-wide column blocks, all K blocks
+  __shared__ __align__(256) float sPF[kThreads];  // landing area of the L2 touches and filler DMAs (never read)
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 2, wn = wave & 3;
@@ -101,153 +127,199 @@ __global__ __launch_bounds__(kThreads) void gemm_w8a8_big_kernel(GemmArgs a, int
     tile = band * gm + in_band % band_rows;
     nt = in_band / band_rows;
   } else {
-    tile = blockIdx.x % grid_blocks;
-    nt = blockIdx.x / grid_blocks;
+    // routed: column tile fastest, so concurrently running workgroups share one block's rows
+    tile = blockIdx.x / n_tiles;
+    nt = blockIdx.x - tile * n_tiles;
+    if (tile >= grid_blocks) return;
   }
   const int64_t n0 = nt * kBN;
   if (n0 >= a.N) return;
 
   TileInfo t;
-  if (!tile_info<kBM, MODE>(a, tile, t)) return;
+  if (!tile_info<BM, MODE>(a, tile, t)) return;
   const int64_t expert = t.expert;
   const uint8_t* A = reinterpret_cast<const uint8_t*>(a.A);
   const uint8_t* Wb = a.W + expert * a.w_estride;
   const float* swb = reinterpret_cast<const float*>(a.ws) + expert * a.ws_estride;
   const int KB = int(a.K >> 7);
-  // The weight scales the tile needs are staged in LDS once: every K block then reads
-  // its scale with a DS load, so no vector-memory load (and no vmcnt wait) sits in
-  // the K loop besides the operand DMA.
-  for (int i = tid; i < 2 * KB; i += kThreads) {
-    const int blk = i / KB, kb = i - blk * KB;
-    const int64_t nb = min<int64_t>((n0 >> 7) + blk, cdiv(a.N, 128) - 1);
-    sSW[blk][kb] = swb[nb * a.ws_s0 + kb * a.ws_s1];
-  }
+  // staged once, after the first operand DMA is in flight so the two latencies overlap
+  auto stage_weight_scales = [&]() __attribute__((always_inline)) {
+    for (int i = tid; i < 2 * KB; i += kThreads) {
+      const int blk = i / KB, kb = i - blk * KB;
+      const int64_t nb = min<int64_t>((n0 >> 7) + blk, cdiv(a.N, 128) - 1);
+      sSW[blk][kb] = swb[nb * a.ws_s0 + kb * a.ws_s1];
+    }
+  };
   const int sw_blk = wn >> 1;  // waves 0-1 cover the first 128 columns, 2-3 the second
   const bool vec_store = (a.ldo & 3) == 0;   // 16-byte fp32 stores
   const bool vec8_store = (a.ldo & 7) == 0;  // 16-byte bf16 stores
 
-  for (int m_base = 0; m_base < t.m_total; m_base += kBM) {
-    const int m_size = min(kBM, t.m_total - m_base);
+  for (int m_base = 0; m_base < t.m_total; m_base += BM) {
+    const int m_size = min(BM, t.m_total - m_base);
     __syncthreads();
-    fill_rows<kBM, MODE>(a, t, m_base, sArow, sOrow);
+    fill_rows<BM, MODE>(a, t, m_base, sArow, sOrow);
     __syncthreads();
 
-    // ---- per-lane DMA sources: 4 x 1 KB blocks of A and of W per wave per K block
-    // (32-bit byte offsets: the host only routes operands below 4 GiB here)
-    uint32_t oa[4], ob[4];
+    // ---- per-lane DMA sources (32-bit byte offsets: the host routes operands below 4 GiB here)
+    uint32_t oa[C::A_DMA], ob[4];
 #pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      const int row = (wave * 4 + b) * 8 + (lane >> 3);
+    for (int b = 0; b < C::A_DMA; ++b) {
+      const int row = (wave * C::A_DMA + b) * 8 + (lane >> 3);
       const int chunk = (lane & 7) ^ swz(row);
       oa[b] = uint32_t(sArow[row] * a.lda + chunk * 16);
-      const int64_t n = min<int64_t>(n0 + row, a.N - 1);
-      ob[b] = uint32_t(n * a.ldw + chunk * 16);
     }
-    const float* gs = a.sa + sArow[(wave & 3) * 64 + lane] * a.lds;
-
-    auto issue = [&](int kb, uint8_t* dA, uint8_t* dB, float* dS) __attribute__((always_inline)) {
-      const uint8_t* Ak = A + kb * kKS;
-      const uint8_t* Wk = Wb + kb * kKS;
-      const uint32_t la = __builtin_amdgcn_readfirstlane(lds_addr(dA) + wave * 4096);
-      const uint32_t lb = __builtin_amdgcn_readfirstlane(lds_addr(dB) + wave * 4096);
 #pragma unroll
-      for (int b = 0; b < 4; ++b) {
-        lds_dma16(Ak + oa[b], la + b * 1024);
-        lds_dma16(Wk + ob[b], lb + b * 1024);
+    for (int b = 0; b < 4; ++b) {
+      if (TILED) {
+        // DMA b of this wave = half (b & 1) of the tile of 16-row group 2 wave + b / 2
+        const int64_t g16 = min<int64_t>(n0 / 16 + wave * 2 + (b >> 1), a.N / 16 - 1);
+        ob[b] = uint32_t(g16 * KB * 2048 + (b & 1) * 1024 + lane * 16);
+      } else {
+        const int row = (wave * 4 + b) * 8 + (lane >> 3);
+        const int chunk = (lane & 7) ^ swz(row);
+        const int64_t n = min<int64_t>(n0 + row, a.N - 1);
+        ob[b] = uint32_t(n * a.ldw + chunk * 16);
       }
-      if (wave < 4) lds_dma4(gs + kb, __builtin_amdgcn_readfirstlane(lds_addr(dS) + wave * 256));
-    };
-    // Warm L2 with the K block after the one being DMA'd: one dword of every 128-byte
-    // operand line (threads 0-255 the activation rows, 256-511 the weight rows).  With
-    // only two LDS stages this is what lets the next DMA find its lines in L2.
-    const uint8_t* pf_base = (tid < 256) ? A + sArow[tid] * a.lda
-                                         : Wb + min<int64_t>(n0 + (tid - 256), a.N - 1) * a.ldw;
-    const uint32_t pf_lds = __builtin_amdgcn_readfirstlane(lds_addr(sPF) + wave * 256);
-    auto prefetch = [&](int kb) __attribute__((always_inline)) {
-      lds_dma4(pf_base + kb * kKS, pf_lds);
-    };
+    }
+    // activation scales: waves < BM/64 fetch 64 rows each; the others fetch a filler dword
+    // into sPF so that every wave issues the same number of loads per K block
+    const bool sa_wave = wave < BM / 64;
+    const float* gs = a.sa + sArow[(wave % (BM / 64)) * 64 + lane] * a.lds;
 
-    f32x4 acc[8][4];
+    auto stageA = [&](int s) -> uint8_t* { return sOps + s * C::STAGE_BYTES; };
+    auto stageB = [&](int s) -> uint8_t* { return sOps + s * C::STAGE_BYTES + BM * kKS; };
+
+    // one K block: (A_DMA + 4) operand DMAs and one scale DMA per wave
+    auto issue = [&](int kb, int s) __attribute__((always_inline)) {
+      const uint8_t* Ak = A + kb * kKS;
+      const uint8_t* Wk = Wb + kb * (TILED ? 2048 : kKS);
+      const uint32_t la = __builtin_amdgcn_readfirstlane(lds_addr(stageA(s)) + wave * C::A_DMA * 1024);
+      const uint32_t lb = __builtin_amdgcn_readfirstlane(lds_addr(stageB(s)) + wave * 4096);
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
+      for (int b = 0; b < C::A_DMA; ++b) lds_dma16(Ak + oa[b], la + b * 1024);
+#pragma unroll
+      for (int b = 0; b < 4; ++b) lds_dma16(Wk + ob[b], lb + b * 1024);
+      const uint32_t ls = sa_wave ? lds_addr(&sS[s][0]) + wave * 256 : lds_addr(sPF) + wave * 256;
+      lds_dma4(gs + kb, __builtin_amdgcn_readfirstlane(ls));
+    };
+    constexpr int kIssueOps = C::A_DMA + 5;
+    // Warm L2 with a later K block: one dword of every 128-byte operand line (threads
+    // 0..BM-1 the activation rows, 256..511 the weight rows; tiled weights: one line each).
+    const uint8_t* pf_base;
+    int pf_stride;
+    if (tid >= 256) {
+      const int r = tid - 256;
+      if (TILED) {
+        const int64_t g16 = min<int64_t>(n0 / 16 + r / 16, a.N / 16 - 1);
+        pf_base = Wb + g16 * KB * 2048 + (r & 15) * 128;
+        pf_stride = 2048;
+      } else {
+        pf_base = Wb + min<int64_t>(n0 + r, a.N - 1) * a.ldw;
+        pf_stride = kKS;
+      }
+    } else {
+      pf_base = A + sArow[tid % BM] * a.lda;
+      pf_stride = kKS;
+    }
+    const uint32_t pf_lds = __builtin_amdgcn_readfirstlane(lds_addr(sPF) + wave * 256);
+    auto prefetch = [&](int kb) __attribute__((always_inline)) { lds_dma4(pf_base + kb * pf_stride, pf_lds); };
+
+    f32x4 acc[TI][4];
+#pragma unroll
+    for (int i = 0; i < TI; ++i)
 #pragma unroll
       for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    // One K block: hold the wave's 4 weight fragments and stream the 8 activation
-    // fragments.  Software-pipelined: the MFMAs of sub-tile row i+1 are interleaved with
-    // the promotion FMAs of row i (whose partials finished during row i+1's issue), so a
-    // single wave keeps its matrix core busy instead of waiting on its own results.
-    auto compute = [&](int kb, const uint8_t* cA, const uint8_t* cB, const float* cS) __attribute__((always_inline)) {
+    // One K block: hold the wave's 4 weight fragments and stream the TI activation
+    // fragments.  The products t = 4 i + j run as a software pipeline: step t issues the
+    // MFMA of product t + 2 and promotes product t (acc += partial * sa * sw), whose MFMA
+    // went out two MFMAs earlier, from a ring of three partial-sum registers.  A scheduling
+    // fence after each step keeps that order (left alone, the scheduler moves each
+    // promotion right behind the MFMA that produces it and stalls on the result).
+    auto compute = [&](int kb, int s) __attribute__((always_inline)) {
+      const uint8_t* cA = stageA(s);
+      const uint8_t* cB = stageB(s);
+      const float* cS = sS[s];
+      constexpr int DIST = 2, NB = DIST + 1;
       i32x8 wf[4];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) wf[j] = read_frag(cB, wn * 64 + 16 * j + l16, q);
+      for (int j = 0; j < 4; ++j)
+        wf[j] = TILED ? read_frag_tiled(cB, wn * 4 + j, lane) : read_frag(cB, wn * 64 + 16 * j + l16, q);
       const float sw = sSW[sw_blk][kb];
       const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
-      i32x8 af_n = read_frag(cA, wm * 128 + 16 + l16, q);
-      float sa_n = cS[wm * 128 + 16 + l16];
-      f32x4 pc[4];
-      {
-        const i32x8 af0 = read_frag(cA, wm * 128 + l16, q);
+      const int mrow = wm * (BM / 2);
+      i32x8 afr[2];  // activation fragments of rows i (slot i & 1)
+      float cr[2];   // combined scales of rows i
 #pragma unroll
-        for (int j = 0; j < 4; ++j) pc[j] = mfma_16x16x128_e4m3(wf[j], af0, zero);
+      for (int r = 0; r < 2; ++r) {
+        afr[r] = read_frag(cA, mrow + 16 * r + l16, q);
+        cr[r] = cS[mrow + 16 * r + l16] * sw;
       }
-      float c_cur = cS[wm * 128 + l16] * sw;
+      f32x4 pb[NB];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        // for each j: promote row i's partial j, then reuse its registers for row i+1
-        const i32x8 af = af_n;
-        const float c_next = sa_n * sw;
-        if (i < 6) {
-          af_n = read_frag(cA, wm * 128 + 16 * (i + 2) + l16, q);
-          sa_n = cS[wm * 128 + 16 * (i + 2) + l16];
+      for (int u = 0; u < DIST; ++u) pb[u] = mfma_16x16x128_e4m3(wf[u & 3], afr[(u >> 2) & 1], zero);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int u = 0; u < NT; ++u) {
+        const int um = u + DIST;
+        if (um < NT) {
+          const int im = um >> 2, jm = um & 3;
+          pb[um % NB] = mfma_16x16x128_e4m3(wf[jm], afr[im & 1], zero);
+          // the last MFMA of row im is out: its fragment slot takes row im + 2
+          if (jm == 3 && im + 2 < TI) afr[im & 1] = read_frag(cA, mrow + 16 * (im + 2) + l16, q);
         }
+        const int i = u >> 2, j = u & 3;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-#pragma unroll
-          for (int r = 0; r < 4; ++r) acc[i][j][r] = fmaf(pc[j][r], c_cur, acc[i][j][r]);
-          if (i < 7) pc[j] = mfma_16x16x128_e4m3(wf[j], af, zero);
-        }
-        if (i < 7) {
-#pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-          }
-        }
-        // pin row i's promotion here (otherwise it sinks below every later MFMA)
-        asm volatile("" : "+v"(acc[i][0]), "+v"(acc[i][1]), "+v"(acc[i][2]), "+v"(acc[i][3]));
-        c_cur = c_next;
+        for (int r = 0; r < 4; ++r) acc[i][j][r] = fmaf(pb[u % NB][r], cr[i & 1], acc[i][j][r]);
+        if (j == 3 && i + 2 < TI) cr[i & 1] = cS[mrow + 16 * (i + 2) + l16] * sw;
+        __builtin_amdgcn_sched_barrier(0);
       }
     };
 
-    // vmcnt bookkeeping: every iteration issues the operand DMA of block kb+1 and then one
-    // prefetch of block kb+2; waiting for vmcnt <= 1 at the top of the next iteration
-    // retires the DMA (loads retire in issue order) while the prefetch stays in flight.
-    issue(0, sA0, sB0, sS0);
-    prefetch(KB > 1 ? 1 : 0);
-    for (int kb = 0; kb < KB; kb += 2) {
-      asm volatile("s_waitcnt vmcnt(1)" ::: "memory");
-      __syncthreads();
-      if (kb + 1 < KB) issue(kb + 1, sA1, sB1, sS1);
-      prefetch(min(kb + 2, KB - 1));
-      compute(kb, sA0, sB0, sS0);
-      if (kb + 1 < KB) {
-        asm volatile("s_waitcnt vmcnt(1)" ::: "memory");
+    // ---- K loop.  Loads retire in issue order.  Each iteration waits for its own stage,
+    // publishes it with a barrier (which also retires every wave's reads of the stage the
+    // next DMA overwrites), issues the DMA S - 1 blocks ahead plus one L2 touch, computes.
+    if (S == 2) {
+      // ops after DMA(kb) at the top of iteration kb: the touch issued with it
+      issue(0, 0);
+      prefetch(min(1, KB - 1));
+      if (m_base == 0) stage_weight_scales();
+      for (int kb = 0; kb < KB; ++kb) {
+        wait_vmcnt<1>();
         __syncthreads();
-        if (kb + 2 < KB) issue(kb + 2, sA0, sB0, sS0);
+        if (kb + 1 < KB) issue(kb + 1, (kb + 1) & 1);
+        prefetch(min(kb + 2, KB - 1));
+        compute(kb, kb & 1);
+      }
+    } else {
+      // ops after DMA(kb): touch(kb+1), [DMA(kb+1)], touch(kb+2)
+      issue(0, 0);
+      prefetch(min(1, KB - 1));
+      if (KB > 1) issue(1, 1);
+      prefetch(min(2, KB - 1));
+      if (m_base == 0) stage_weight_scales();
+      int s = 0;
+      for (int kb = 0; kb < KB; ++kb) {
+        if (kb + 1 < KB)
+          wait_vmcnt<kIssueOps + 2>();
+        else
+          wait_vmcnt<2>();
+        __syncthreads();
+        if (kb + 2 < KB) issue(kb + 2, s == 0 ? 2 : s - 1);
         prefetch(min(kb + 3, KB - 1));
-        compute(kb + 1, sA1, sB1, sS1);
+        compute(kb, s);
+        s = s == S - 1 ? 0 : s + 1;
       }
     }
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    wait_vmcnt<0>();
 
-    // ---- epilogue: lane owns rows m = wm*128 + 16i + l16, columns n = wn*64 + 16j + 4q .. +3
+    // ---- epilogue: lane owns rows m = wm*BM/2 + 16i + l16, columns n = wn*64 + 16j + 4q .. +3
     if (!OUT_F32) {
-      // bf16: stage each wave's 128 x 64 block through LDS (the operand buffers are free
-      // now) and write whole 128-byte row segments; 16-byte chunk c of row r sits at
-      // chunk position c ^ (r & 7).
+      // bf16: stage each wave's BM/2 x 64 block through LDS (the operand stages are free
+      // now) and write whole 128-byte row segments; 16-byte chunk c of row r sits at chunk
+      // position c ^ (r & 7).
       __syncthreads();
-      uint8_t* region = (wave < 2 ? sA0 : wave < 4 ? sA1 : wave < 6 ? sB0 : sB1) + (wave & 1) * 16384;
+      uint8_t* region = sOps + wave * (BM / 2) * 128;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int64_t n = n0 + wn * 64 + 16 * j + 4 * q;
@@ -257,7 +329,7 @@ __global__ __launch_bounds__(kThreads) void gemm_w8a8_big_kernel(GemmArgs a, int
           for (int r = 0; r < 4; ++r) b[r] = (n + r < a.N) ? load_bias(a, expert, n + r) : 0.f;
         }
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
+        for (int i = 0; i < TI; ++i) {
           const int row = 16 * i + l16;
           const int pc = (2 * j + (q >> 1)) ^ (row & 7);
           uint2 pk;
@@ -268,25 +340,27 @@ __global__ __launch_bounds__(kThreads) void gemm_w8a8_big_kernel(GemmArgs a, int
       }
       __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's LDS writes are done
       __builtin_amdgcn_wave_barrier();
-      // all 16 chunk reads first (the accumulators are dead, registers are free), then
-      // all 16 stores, so each wave keeps 16 KB of writes in flight
-      i32x4 v[16];
+      // all chunk reads first (the accumulators are dead, registers are free), then all
+      // stores, so each wave keeps its whole block of writes in flight
+      constexpr int CH = BM / 16;  // 16-byte chunks per lane
+      i32x4 v[CH];
 #pragma unroll
-      for (int it = 0; it < 16; ++it) {
+      for (int it = 0; it < CH; ++it) {
         const int id = it * 64 + lane;
         v[it] = *reinterpret_cast<const i32x4*>(region + (id >> 3) * 128 + (id & 7) * 16);
       }
 #pragma unroll
-      for (int it = 0; it < 16; ++it) {
+      for (int it = 0; it < CH; ++it) {
         const int id = it * 64 + lane;
         const int row = id >> 3, pc = id & 7;
         const int c = pc ^ (row & 7);
-        const int ml = wm * 128 + row;
+        const int ml = wm * (BM / 2) + row;
         if (ml >= m_size) continue;
         const int64_t n = n0 + wn * 64 + c * 8;
         uint16_t* o = reinterpret_cast<uint16_t*>(a.out) + sOrow[ml] * a.ldo + n;
         if (vec8_store && n + 8 <= a.N) {
-          *reinterpret_cast<i32x4*>(o) = v[it];
+          // streaming store: the output is not re-read by this kernel
+          __builtin_nontemporal_store(v[it], reinterpret_cast<i32x4*>(o));
         } else {
           const uint16_t* e = reinterpret_cast<const uint16_t*>(&v[it]);
           for (int r = 0; r < 8 && n + r < a.N; ++r) o[r] = e[r];
@@ -302,8 +376,8 @@ __global__ __launch_bounds__(kThreads) void gemm_w8a8_big_kernel(GemmArgs a, int
           for (int r = 0; r < 4; ++r) b[r] = (n + r < a.N) ? load_bias(a, expert, n + r) : 0.f;
         }
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const int ml = wm * 128 + 16 * i + l16;
+        for (int i = 0; i < TI; ++i) {
+          const int ml = wm * (BM / 2) + 16 * i + l16;
           if (ml >= m_size) continue;
           const int64_t o = sOrow[ml] * a.ldo + n;
           const float v[4] = {acc[i][j][0] + b[0], acc[i][j][1] + b[1], acc[i][j][2] + b[2], acc[i][j][3] + b[3]};
@@ -320,32 +394,47 @@ __global__ __launch_bounds__(kThreads) void gemm_w8a8_big_kernel(GemmArgs a, int
   }
 }
 
-void launch_gemm_w8a8_big(const GemmArgs& a, int row_mode, bool out_f32, int64_t grid_blocks, hipStream_t st) {
-  if (grid_blocks <= 0 || a.N <= 0) return;
+template <int BM, int MODE, bool TL>
+static void launch_big_t(const GemmArgs& a, bool out_f32, int64_t grid_blocks, hipStream_t st) {
   const int64_t n_tiles = cdiv(a.N, kBN);
   int64_t nwg = grid_blocks * n_tiles;
-  if (row_mode == ROWS_DENSE) nwg = cdiv(nwg, 8) * 8;
+  if (MODE == ROWS_DENSE) nwg = cdiv(nwg, 8) * 8;
   const dim3 grid(static_cast<unsigned>(nwg)), block(kThreads);
   const bool bias = a.bias != nullptr;
-#define MXQ_BIG_GO(MODE, OF, HB) \
-  hipLaunchKernelGGL((gemm_w8a8_big_kernel<MODE, OF, HB>), grid, block, 0, st, a, grid_blocks, n_tiles)
-#define MXQ_BIG_MODE(MODE)                                   \
-  do {                                                       \
-    if (out_f32) {                                           \
-      if (bias) MXQ_BIG_GO(MODE, true, true);                \
-      else MXQ_BIG_GO(MODE, true, false);                    \
-    } else {                                                 \
-      if (bias) MXQ_BIG_GO(MODE, false, true);               \
-      else MXQ_BIG_GO(MODE, false, false);                   \
-    }                                                        \
-  } while (0)
-  switch (row_mode) {
-    case ROWS_DENSE: MXQ_BIG_MODE(ROWS_DENSE); break;
-    case ROWS_GATHER_TOK: MXQ_BIG_MODE(ROWS_GATHER_TOK); break;
-    default: MXQ_BIG_MODE(ROWS_COMPACT_IN); break;
-  }
-#undef MXQ_BIG_MODE
+#define MXQ_BIG_GO(OF, HB) \
+  hipLaunchKernelGGL((gemm_w8a8_big_kernel<BM, MODE, OF, HB, TL>), grid, block, 0, st, a, grid_blocks, n_tiles)
+  if (out_f32) { if (bias) MXQ_BIG_GO(true, true); else MXQ_BIG_GO(true, false); }
+  else { if (bias) MXQ_BIG_GO(false, true); else MXQ_BIG_GO(false, false); }
 #undef MXQ_BIG_GO
+}
+
+template <int BM>
+static void launch_big_bm(const GemmArgs& a, int row_mode, bool out_f32, int64_t gb, hipStream_t st) {
+  if constexpr (BM == 256) {
+    // routed blocks hold at most 128 rows: the 256-row tile serves dense GEMMs only
+    launch_big_t<BM, ROWS_DENSE, false>(a, out_f32, gb, st);
+    return;
+  }
+  switch (row_mode) {
+    case ROWS_DENSE: launch_big_t<BM, ROWS_DENSE, false>(a, out_f32, gb, st); break;
+    case ROWS_GATHER_TOK:
+      if (a.w_tiled) launch_big_t<BM, ROWS_GATHER_TOK, true>(a, out_f32, gb, st);
+      else launch_big_t<BM, ROWS_GATHER_TOK, false>(a, out_f32, gb, st);
+      break;
+    default:
+      if (a.w_tiled) launch_big_t<BM, ROWS_COMPACT_IN, true>(a, out_f32, gb, st);
+      else launch_big_t<BM, ROWS_COMPACT_IN, false>(a, out_f32, gb, st);
+      break;
+  }
+}
+
+void launch_gemm_w8a8_big(const GemmArgs& a, int row_mode, int bm, bool out_f32, int64_t grid_blocks,
+                          hipStream_t st) {
+  if (grid_blocks <= 0 || a.N <= 0) return;
+  if (bm == 256 && row_mode == ROWS_DENSE)
+    launch_big_bm<256>(a, row_mode, out_f32, grid_blocks, st);
+  else
+    launch_big_bm<128>(a, row_mode, out_f32, grid_blocks, st);
 }
 
 }  // namespace mxq

@@ -67,8 +67,10 @@ void launch_quant_1x128(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, ui
 void launch_gemm_w8a8(const GemmArgs& a, int row_mode, int tile, bool out_f32, int64_t grid_blocks,
                       hipStream_t stream);
 
-// W8A8 with 256 x 256 tiles (8 waves, direct-to-LDS loads); 128x128 weight blocks only.
-void launch_gemm_w8a8_big(const GemmArgs& a, int row_mode, bool out_f32, int64_t grid_blocks, hipStream_t stream);
+// W8A8 with bm x 256 tiles, bm = 256 or 128 (8 waves, direct-to-LDS loads); 128x128 weight
+// blocks only; K <= 16384; operand offsets below 4 GiB.  Routed modes read plain or tiled weights.
+void launch_gemm_w8a8_big(const GemmArgs& a, int row_mode, int bm, bool out_f32, int64_t grid_blocks,
+                          hipStream_t stream);
 
 // W8A16 / W4A16: bf16 activations x decoded e4m3 / e2m1 weights (MFMA 16x16x32 bf16).
 void launch_gemm_w16(const GemmArgs& a, int wfmt, int row_mode, int tile, bool out_f32, int64_t grid_blocks,

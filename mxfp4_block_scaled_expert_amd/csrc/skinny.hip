@@ -40,6 +40,9 @@ constexpr int kSkMaxRows = 8;
 // groups per wave (G), ring depth in steps (D) and the waves per SIMD the register
 // budget targets (W), per weight / activation format; chosen by measurement on the
 // decode workload (no register spills at these budgets)
+#ifndef MXQ_SK_GSEL
+#define MXQ_SK_GSEL 4096
+#endif
 template <int WFMT, bool AE>
 struct SkinnyShape {
   static constexpr int G = 2;
@@ -297,9 +300,13 @@ __global__ __launch_bounds__(256, (SkinnyShape<WFMT, A_E4M3>::W)) void skinny_ke
   }
 }
 
+// two 16-row groups per wave for wide outputs, one for narrow ones (more, smaller
+// workgroups: less idle tail in the last round of a grid that is a few rounds deep)
+static int skinny_groups(int64_t N) { return N >= MXQ_SK_GSEL ? 2 : 1; }
+
 template <int WFMT, bool AE>
-static size_t skinny_lds_t(int64_t K, int AR) {
-  return skinny_lds_layout(WFMT == W_E2M1_MX, AE, K, SkinnyShape<WFMT, AE>::G, AR).total;
+static size_t skinny_lds_t(int64_t K, int AR, int G) {
+  return skinny_lds_layout(WFMT == W_E2M1_MX, AE, K, G, AR).total;
 }
 
 // Activation rows per pass: eight while the LDS stays within kSkLdsCap (so that several
@@ -309,23 +316,22 @@ static size_t skinny_lds_t(int64_t K, int AR) {
 #endif
 constexpr size_t kSkLdsCap = MXQ_SK_AR8_CAP;
 template <int WFMT, bool AE>
-static int skinny_rows_t(int64_t K) {
-  return skinny_lds_t<WFMT, AE>(K, 8) <= kSkLdsCap ? 8 : 4;
+static int skinny_rows_t(int64_t K, int G) {
+  return skinny_lds_t<WFMT, AE>(K, 8, G) <= kSkLdsCap ? 8 : 4;
 }
 
 size_t skinny_lds_bytes(int wfmt, bool a_e4m3, int64_t K) {
-  if (wfmt == W_E2M1_MX) return skinny_lds_t<W_E2M1_MX, false>(K, skinny_rows_t<W_E2M1_MX, false>(K));
-  if (a_e4m3) return skinny_lds_t<W_E4M3_BLOCK, true>(K, skinny_rows_t<W_E4M3_BLOCK, true>(K));
-  return skinny_lds_t<W_E4M3_BLOCK, false>(K, skinny_rows_t<W_E4M3_BLOCK, false>(K));
+  // the larger of the two group counts (the weight-scale table grows with G)
+  if (wfmt == W_E2M1_MX) return skinny_lds_t<W_E2M1_MX, false>(K, skinny_rows_t<W_E2M1_MX, false>(K, 2), 2);
+  if (a_e4m3) return skinny_lds_t<W_E4M3_BLOCK, true>(K, skinny_rows_t<W_E4M3_BLOCK, true>(K, 2), 2);
+  return skinny_lds_t<W_E4M3_BLOCK, false>(K, skinny_rows_t<W_E4M3_BLOCK, false>(K, 2), 2);
 }
 
-template <int WFMT, bool AE, int MODE, bool TL, int AR>
+template <int WFMT, bool AE, int MODE, bool TL, int AR, int G, int D>
 static void launch_skinny_ar(const GemmArgs& a, bool out_f32, int64_t gb, hipStream_t st) {
-  constexpr int G = SkinnyShape<WFMT, AE>::G;
-  constexpr int D = SkinnyShape<WFMT, AE>::D;
   const int64_t n_tiles = cdiv(a.N, int64_t(64 * G));
   const dim3 grid(static_cast<unsigned>(gb * n_tiles)), block(256);
-  const size_t lds = skinny_lds_t<WFMT, AE>(a.K, AR);
+  const size_t lds = skinny_lds_t<WFMT, AE>(a.K, AR, G);
   const bool bias = a.bias != nullptr;
 #define MXQ_SK_GO(OF, HB) \
   hipLaunchKernelGGL((skinny_kernel<WFMT, AE, MODE, OF, HB, TL, AR, G, D>), grid, block, lds, st, a, gb)
@@ -334,16 +340,24 @@ static void launch_skinny_ar(const GemmArgs& a, bool out_f32, int64_t gb, hipStr
 #undef MXQ_SK_GO
 }
 
+template <int WFMT, bool AE, int MODE, int G, int D>
+static void launch_skinny_g(const GemmArgs& a, bool out_f32, int64_t gb, hipStream_t st) {
+  const bool eight = skinny_rows_t<WFMT, AE>(a.K, G) == 8;
+  if (a.w_tiled) {
+    if (eight) launch_skinny_ar<WFMT, AE, MODE, true, 8, G, D>(a, out_f32, gb, st);
+    else launch_skinny_ar<WFMT, AE, MODE, true, 4, G, D>(a, out_f32, gb, st);
+  } else {
+    if (eight) launch_skinny_ar<WFMT, AE, MODE, false, 8, G, D>(a, out_f32, gb, st);
+    else launch_skinny_ar<WFMT, AE, MODE, false, 4, G, D>(a, out_f32, gb, st);
+  }
+}
+
 template <int WFMT, bool AE, int MODE>
 static void launch_skinny_t(const GemmArgs& a, bool out_f32, int64_t gb, hipStream_t st) {
-  const bool eight = skinny_rows_t<WFMT, AE>(a.K) == 8;
-  if (a.w_tiled) {
-    if (eight) launch_skinny_ar<WFMT, AE, MODE, true, 8>(a, out_f32, gb, st);
-    else launch_skinny_ar<WFMT, AE, MODE, true, 4>(a, out_f32, gb, st);
-  } else {
-    if (eight) launch_skinny_ar<WFMT, AE, MODE, false, 8>(a, out_f32, gb, st);
-    else launch_skinny_ar<WFMT, AE, MODE, false, 4>(a, out_f32, gb, st);
-  }
+  if (skinny_groups(a.N) == 2)
+    launch_skinny_g<WFMT, AE, MODE, 2, 3>(a, out_f32, gb, st);
+  else
+    launch_skinny_g<WFMT, AE, MODE, 1, 4>(a, out_f32, gb, st);
 }
 
 template <int MODE>
