@@ -36,9 +36,12 @@ HBM_PEAK_GBS = 8000.0
 FP8_PEAK_TFLOPS = 5000.0
 BF16_PEAK_TFLOPS = 2500.0
 
-# HBM traffic of the dominant kernel from rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE (per launch, bytes),
-# scaled by the copy-kernel calibration; None until measured for the current kernel.
-GEMM_TRAFFIC_BYTES = None
+# HBM traffic of the dominant kernel per launch (bytes): rocprofv3 --pmc FETCH_SIZE and WRITE_SIZE
+# on this workload, each divided by what the same counter reads for a 256 MiB device copy (FETCH_SIZE
+# 0.500, WRITE_SIZE 1.000 of the true bytes); figures and commands in
+# profiles/gemm_w8a8_big_block_linear_2048x2048x7168.md and profiles/copy_calibration_256MiB.md.
+# Set back to None whenever gemm_w8a8_big_kernel changes until the counters are taken again.
+GEMM_TRAFFIC_BYTES = 76461860
 
 
 def _args():
@@ -48,8 +51,8 @@ def _args():
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-secondary", action="store_true")
-    p.add_argument("--only", choices=["linear", "decode", "prefill"], default=None,
-                   help="time one workload only (profiling runs)")
+    p.add_argument("--only", choices=["linear", "decode", "prefill", "copy"], default=None,
+                   help="time one workload only (profiling runs); copy = counter calibration")
     return p.parse_args()
 
 
@@ -65,7 +68,15 @@ def _check(st, what):
 
 # ----------------------------------------------------------------------------- headline
 
+def _events():
+    return torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+
 def bench_linear(steps: int, warmup: int):
+    """Headline step (quantise + GEMM) and the GEMM's own average launch time.
+
+    Both are timed over back-to-back launches between one pair of HIP events on the
+    stream the kernels run on, so per-launch event overhead does not inflate them."""
     from mxfp4_block_scaled_expert_amd import synth
     L, lib = _lib()
     dev = torch.device("cuda", 0)
@@ -78,43 +89,62 @@ def bench_linear(steps: int, warmup: int):
     out = torch.empty(M, N, dtype=torch.bfloat16, device=dev)
     stream = torch.cuda.current_stream()
     sh = stream.cuda_stream
+    # pre-quantised activations of every set, for the GEMM-only timing
+    qs = [torch.empty_like(q) for _ in range(n_rot)]
+    ss = [torch.empty_like(s) for _ in range(n_rot)]
 
-    def step(i, ev=None):
-        d = sets[i % n_rot]
-        if ev:
-            ev[0].record(stream)
-        _check(lib.mxq_per_token_group_quant_fp8(d["x"].data_ptr(), M, K, K, 128, q.data_ptr(), s.data_ptr(), sh),
+    def quant(d, qq, sc):
+        _check(lib.mxq_per_token_group_quant_fp8(d["x"].data_ptr(), M, K, K, 128, qq.data_ptr(), sc.data_ptr(), sh),
                "quant")
-        if ev:
-            ev[1].record(stream)
-        _check(lib.mxq_block_fp8_linear(q.data_ptr(), L.MXQ_DTYPE_E4M3, s.data_ptr(), M, K, K, d["w"].data_ptr(), N,
+
+    def gemm(d, qq, sc):
+        _check(lib.mxq_block_fp8_linear(qq.data_ptr(), L.MXQ_DTYPE_E4M3, sc.data_ptr(), M, K, K, d["w"].data_ptr(), N,
                                         d["sw"].data_ptr(), K // 128, 1, 128, 128, None, 0, out.data_ptr(), N, None,
                                         0, sh), "block_fp8_linear")
-        if ev:
-            ev[2].record(stream)
 
+    for i in range(n_rot):
+        quant(sets[i], qs[i], ss[i])
     for i in range(warmup):
-        step(i)
+        quant(sets[i % n_rot], q, s)
+        gemm(sets[i % n_rot], q, s)
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+
+    # headline: K steps of the whole path
+    e0, e1 = _events()
     t0 = time.perf_counter()
+    e0.record(stream)
     for i in range(steps):
-        step(i, evs[i])
+        d = sets[i % n_rot]
+        quant(d, q, s)
+        gemm(d, q, s)
+    e1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    total_ms = evs[0][0].elapsed_time(evs[-1][2])
-    quant_ms = [e[0].elapsed_time(e[1]) for e in evs]
-    gemm_ms = [e[1].elapsed_time(e[2]) for e in evs]
+    step_ms = e0.elapsed_time(e1) / steps
+
+    # the dominant kernel alone, same rotation
+    g0, g1 = _events()
+    g0.record(stream)
+    for i in range(steps):
+        gemm(sets[i % n_rot], qs[i % n_rot], ss[i % n_rot])
+    g1.record(stream)
+    # the quantiser alone
+    q0, q1 = _events()
+    q0.record(stream)
+    for i in range(steps):
+        quant(sets[i % n_rot], q, s)
+    q1.record(stream)
+    torch.cuda.synchronize()
+    gemm_ms = g0.elapsed_time(g1) / steps
+    quant_ms = q0.elapsed_time(q1) / steps
+
     flops = 2.0 * M * N * K
-    gemm_avg = float(np.mean(gemm_ms))
     gemm_bytes = M * K + M * (K // 128) * 4 + N * K + (N // 128) * (K // 128) * 4 + M * N * 2
     return {
         "M": M, "K": K, "N": N, "flops": flops, "rotating_sets": n_rot,
-        "ms_per_step": total_ms / steps, "wall_ms_per_step": wall * 1e3 / steps,
-        "quant_us_median": float(np.median(quant_ms)) * 1e3,
-        "gemm_us_avg": gemm_avg * 1e3, "gemm_us_median": float(np.median(gemm_ms)) * 1e3,
-        "gemm_us_p10": float(np.percentile(gemm_ms, 10)) * 1e3, "gemm_us_p90": float(np.percentile(gemm_ms, 90)) * 1e3,
-        "gemm_tflops": flops / (gemm_avg * 1e-3) / 1e12,
+        "ms_per_step": step_ms, "wall_ms_per_step": wall * 1e3 / steps,
+        "quant_us_avg": quant_ms * 1e3, "gemm_us_avg": gemm_ms * 1e3,
+        "gemm_tflops": flops / (gemm_ms * 1e-3) / 1e12,
         "gemm_alg_bytes": gemm_bytes,
     }
 
@@ -169,18 +199,18 @@ def bench_moe(name: str, steps: int, warmup: int, seed: int, layout: str = "tile
         run()
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
-    for i in range(steps):
-        evs[i][0].record(stream)
+    # back-to-back calls between one pair of events (the weights of the decode and prefill
+    # workloads exceed the 256 MB last-level cache, so every call streams them from HBM)
+    e0, e1 = _events()
+    e0.record(stream)
+    for _ in range(steps):
         run()
-        evs[i][1].record(stream)
+    e1.record(stream)
     torch.cuda.synchronize()
-    ms = np.array([e[0].elapsed_time(e[1]) for e in evs])
+    med = e0.elapsed_time(e1) / steps
     flops = 2.0 * M * topk * (2 * I * H + H * I)
-    med = float(np.median(ms))
     return {
-        "workload": name, "weight_layout": layout, "us_median": med * 1e3, "us_p10": float(np.percentile(ms, 10)) * 1e3,
-        "us_p90": float(np.percentile(ms, 90)) * 1e3, "tflops": flops / (med * 1e-3) / 1e12,
+        "workload": name, "weight_layout": layout, "us_avg": med * 1e3, "tflops": flops / (med * 1e-3) / 1e12,
         "touched_bytes": byts, "weight_gbs": byts / (med * 1e-3) / 1e9,
         "hbm_frac": byts / (med * 1e-3) / 1e9 / HBM_PEAK_GBS,
         "fp8_mfma_frac": flops / (med * 1e-3) / 1e12 / FP8_PEAK_TFLOPS,
@@ -215,6 +245,18 @@ def cpu_baseline(budget_s: float = 12.0):
             "sample": f"whole 2048x2048x7168 workload (quantise + linear), {runs} run(s), {dt:.2f} s each"}
 
 
+def calibrate_copy(steps: int = 10, mib: int = 256):
+    """A plain device copy of known size, for scaling the FETCH_SIZE / WRITE_SIZE counters
+    (run under rocprofv3 --pmc; every launch reads and writes exactly `mib` MiB)."""
+    n = mib << 20
+    src = torch.randint(0, 255, (n,), dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(steps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    return {"calibration": "copy", "bytes_read_per_launch": n, "bytes_written_per_launch": n, "launches": steps}
+
+
 def main():
     a = _args()
     if a.gpus != 1:
@@ -228,6 +270,9 @@ def main():
     from mxfp4_block_scaled_expert_amd import ops
     ops.init(0)
 
+    if a.only == "copy":
+        print(json.dumps(calibrate_copy()), flush=True)
+        return
     if a.only == "decode":
         print(json.dumps(bench_moe("moe_mxfp4_gptoss_decode_m32", a.steps, a.warmup, 1004)), flush=True)
         return
@@ -242,10 +287,11 @@ def main():
         return
     value = lin["flops"] / (lin["ms_per_step"] * 1e-3) / 1e12
     roof = {
-        "kernel": "gemm_w8a8_kernel (block-FP8 W8A8, 128x128 tiles)",
+        "kernel": "gemm_w8a8_big_kernel (block-FP8 W8A8, 256x256 tiles, direct-to-LDS operands)",
         "bound": "mfma", "achieved": lin["gemm_tflops"], "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s",
         "frac": lin["gemm_tflops"] / FP8_PEAK_TFLOPS, "traffic": GEMM_TRAFFIC_BYTES,
-        "alg_bytes_per_launch": lin["gemm_alg_bytes"], "avg_launch_us": lin["gemm_us_avg"],
+        "alg_flops_per_launch": lin["flops"], "alg_bytes_per_launch": lin["gemm_alg_bytes"],
+        "avg_launch_us": lin["gemm_us_avg"],
     }
     secondary = {}
     if not a.no_secondary:
@@ -259,12 +305,11 @@ def main():
     line = {
         "metric": METRIC, "value": value, "unit": "TFLOP/s", "n_gpus": 1, "steps": a.steps, "warmup": a.warmup,
         "ms_per_step": lin["ms_per_step"], "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "e4m3 x e4m3 -> fp32 accumulate (bf16 in/out)", "data": "synthetic",
+        "dtype": "e4m3", "data": "synthetic",
         "config": {"workload": "block_w8a8_linear_2048x2048x7168 (1x128 act quant + 128x128 weight blocks)",
                    "M": lin["M"], "K": lin["K"], "N": lin["N"], "rotating_input_sets": lin["rotating_sets"]},
         "roofline": roof, "cpu_baseline": cpu,
-        "detail": {k: lin[k] for k in ("quant_us_median", "gemm_us_median", "gemm_us_p10", "gemm_us_p90",
-                                       "wall_ms_per_step")},
+        "detail": {k: lin[k] for k in ("quant_us_avg", "gemm_us_avg", "wall_ms_per_step")},
         "secondary": secondary,
     }
     print(json.dumps(line), flush=True)
