@@ -46,10 +46,10 @@ int g_forced_class = 0;
 int g_tiny_max_rows = 16;
 int g_tiny_kernel = MXQ_TINY_MFMA;
 constexpr size_t kSkinnyMaxLds = 64 * 1024;
-#ifndef MXQ_DENSE_BIG_BM
-#define MXQ_DENSE_BIG_BM 256
+#ifndef MXQ_DENSE_BIG_SHAPE
+#define MXQ_DENSE_BIG_SHAPE 0
 #endif
-constexpr int kDenseBigBM = MXQ_DENSE_BIG_BM;  // tile rows of the large dense W8A8 GEMM
+constexpr int kDenseBigShape = MXQ_DENSE_BIG_SHAPE;  // tile shape of the large dense W8A8 GEMM
 
 constexpr int kMoeBlockM = 128;
 constexpr int kNumClasses = 5;  // tiny-block kernel, 16-, 32-, 64-, 128-row MFMA tiles
@@ -125,6 +125,10 @@ ClassPolicy make_policy(int64_t M, int64_t R, int32_t E) {
   pol.forced = -1;
   pol.bound[0] = g_tiny_max_rows;
   for (int c = 1; c < kNumClasses; ++c) pol.bound[c] = kClassRows[c];
+  // When M is at most twice the tiny-block bound the tiny class takes every block (an expert
+  // holds at most M rows): blocks of bound..M rows take a few passes of the weight-streaming
+  // kernel instead of a mostly empty launch of the next tile class.
+  if (g_tiny_max_rows > 0 && M <= 2 * int64_t(g_tiny_max_rows)) pol.bound[0] = std::max<int>(pol.bound[0], int(M));
   pol.n_live = kNumClasses;
   for (int c = 1; c < kNumClasses; ++c)
     if (pol.bound[c - 1] >= M) {
@@ -226,8 +230,17 @@ mxq_status run_moe(const void* x, int64_t M, int64_t H, int64_t I, int32_t E, in
   g2.rt = rt;
 
   const int wfmt_w16 = mx ? W_E2M1_MX : W_E4M3_BLOCK;
+  // With bf16 activations and only the tiny-block class launched, stage 2 computes the
+  // SiLU-and-mul while staging its rows (no ic1 round trip, one launch fewer).
+  const bool fuse_silu = !act_quant && pol.forced < 0 && pol.n_live == 1 && tiny == MXQ_TINY_MFMA &&
+                         skinny_lds_bytes(wfmt_w16, false, I) <= kSkinnyMaxLds;
+  if (fuse_silu) {
+    g2.A = w.ic0;
+    g2.lda = 2 * I;
+    g2.a_silu = 1;
+  }
   for (int stage = 0; stage < 2; ++stage) {
-    if (stage == 1) launch_silu_mul(w.ic0, R, I, w.ic1, w.ic1_q, w.ic1_s, st);
+    if (stage == 1 && !fuse_silu) launch_silu_mul(w.ic0, R, I, w.ic1, w.ic1_q, w.ic1_s, st);
     GemmArgs& g = stage == 0 ? g1 : g2;
     const int mode = stage == 0 ? ROWS_GATHER_TOK : ROWS_COMPACT_IN;
     const bool out_f32 = stage == 1;
@@ -248,7 +261,7 @@ mxq_status run_moe(const void* x, int64_t M, int64_t H, int64_t I, int32_t E, in
         launch_skinny(g, wfmt_w16, act_quant, mode, out_f32, ub, st);
       else if (act_quant && c == kNumClasses - 1 && g.K <= 16384)
         // blocks of 65..128 rows: the 128 x 256 three-stage direct-to-LDS tile
-        launch_gemm_w8a8_big(g, mode, 128, out_f32, ub, st);
+        launch_gemm_w8a8_big(g, mode, 1, out_f32, ub, st);
       else if (act_quant)
         launch_gemm_w8a8(g, mode, tile, out_f32, ub, st);
       else
@@ -384,7 +397,7 @@ mxq_status mxq_block_fp8_linear(const void* A, int32_t a_dtype, const float* a_s
   g.K = K;
   if (block_n == 128 && M > 128 && K <= 16384 && int64_t(M) * lqa < (int64_t(1) << 32) &&
       N * K < (int64_t(1) << 32)) {
-    launch_gemm_w8a8_big(g, ROWS_DENSE, kDenseBigBM, false, cdiv(M, kDenseBigBM), st);
+    launch_gemm_w8a8_big(g, ROWS_DENSE, kDenseBigShape, false, cdiv(M, int64_t(big_tile_rows(kDenseBigShape))), st);
   } else {
     const int tile = dense_tile_for(M);
     launch_gemm_w8a8(g, ROWS_DENSE, tile, false, cdiv(M, tile_rows(tile)), st);

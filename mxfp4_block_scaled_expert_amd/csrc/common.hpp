@@ -25,16 +25,13 @@ __device__ __forceinline__ float bf16lo(uint32_t v) { return __uint_as_float(v <
 __device__ __forceinline__ float bf16hi(uint32_t v) { return __uint_as_float(v & 0xffff0000u); }
 __device__ __forceinline__ float bf16f(uint16_t v) { return __uint_as_float(uint32_t(v) << 16); }
 
-// fp32 -> bf16 bits, round to nearest even (finite inputs; NaN stays NaN).
-__device__ __forceinline__ uint16_t f2bf(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return uint16_t((u >> 16) | 0x40);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return uint16_t(u >> 16);
-}
+// fp32 -> bf16 bits, round to nearest even (NaN stays NaN): gfx950's V_CVT_PK_BF16_F32,
+// one instruction per pair.
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return uint32_t(f2bf(lo)) | (uint32_t(f2bf(hi)) << 16);
+  const bf16x2 b = __builtin_convertvector(f32x2{lo, hi}, bf16x2);
+  return __builtin_bit_cast(uint32_t, b);
 }
+__device__ __forceinline__ uint16_t f2bf(float f) { return uint16_t(pack_bf16x2(f, 0.f)); }
 
 // ---------------------------------------------------------------- fp8 / fp4
 

@@ -37,16 +37,23 @@ namespace mxq {
 
 namespace {
 
-constexpr int kBN = 256, kKS = 128;
-constexpr int kThreads = 512;
+constexpr int kKS = 128;
 constexpr int kMaxKB = 128;  // K <= 16384 on this kernel
 
-template <int BM>
+// BM x BN tile, NW waves laid out WM (rows) x WN (columns) with 64 columns per wave, NS stages.
+template <int BM, int BN, int NW, int NS>
 struct BigCfg {
-  static constexpr int STAGES = BM == 256 ? 2 : 3;
-  static constexpr int TI = BM / 32;     // 16-row sub-tiles per wave (a wave covers BM / 2 rows)
-  static constexpr int A_DMA = BM / 64;  // 1 KB activation DMAs per wave per K block
-  static constexpr int STAGE_BYTES = (BM + kBN) * kKS;
+  static constexpr int THREADS = NW * 64;
+  static constexpr int WN = BN / 64, WM = NW / WN;
+  static constexpr int WROWS = BM / WM;  // rows per wave
+  static constexpr int TI = WROWS / 16;  // 16-row sub-tiles per wave
+  static constexpr int STAGE_BYTES = (BM + BN) * kKS;
+  static constexpr int STAGES = NS;  // LDS stages (2 or 3)
+  static constexpr int A_DMA = BM / 8 / NW;  // 1 KB activation DMAs per wave per K block
+  static constexpr int B_DMA = BN / 8 / NW;  // 1 KB weight DMAs per wave per K block
+  static constexpr int SA_WAVES = BM / 64;   // waves fetching 64 activation scales each
+  static_assert(WM * WN == NW && TI >= 2 && A_DMA >= 1 && B_DMA >= 1 && SA_WAVES <= NW, "tile shape");
+  static_assert(BN % 128 == 0 || BN == 64, "a wave's 64 columns sit inside one 128-wide weight-scale block");
 };
 
 __device__ __forceinline__ int swz(int row) { return (row & 7) ^ ((row >> 3) & 1); }
@@ -96,19 +103,20 @@ __device__ __forceinline__ void wait_vmcnt() {
 
 }  // namespace
 
-template <int BM, int MODE, bool OUT_F32, bool HAS_BIAS, bool TILED>
-__global__ __launch_bounds__(kThreads) void gemm_w8a8_big_kernel(GemmArgs a, int64_t grid_blocks, int64_t n_tiles) {
-  using C = BigCfg<BM>;
-  constexpr int S = C::STAGES, TI = C::TI, NT = 4 * TI;
-  __shared__ __align__(1024) uint8_t sOps[S * C::STAGE_BYTES];  // stage s: A [BM][128] then W [256][128]
+template <int BM, int BN, int NW, int NS, int MODE, bool OUT_F32, bool HAS_BIAS, bool TILED>
+__global__ __launch_bounds__((BigCfg<BM, BN, NW, NS>::THREADS)) void gemm_w8a8_big_kernel(GemmArgs a, int64_t grid_blocks,
+                                                                                 int64_t n_tiles) {
+  using C = BigCfg<BM, BN, NW, NS>;
+  constexpr int S = C::STAGES, TI = C::TI, NT = 4 * TI, WROWS = C::WROWS;
+  __shared__ __align__(1024) uint8_t sOps[S * C::STAGE_BYTES];  // stage s: A [BM][128] then W [BN][128]
   __shared__ __align__(16) float sS[S][BM];
   __shared__ int64_t sArow[BM];
   __shared__ int64_t sOrow[BM];
-  __shared__ float sSW[2][kMaxKB];  // weight scales of the tile's two 128-wide column blocks, all K blocks
-  __shared__ __align__(256) float sPF[kThreads];  // landing area of the L2 touches and filler DMAs (never read)
+  __shared__ float sSW[2][kMaxKB];  // weight scales of the tile's (up to two) 128-wide column blocks
+  __shared__ __align__(256) float sFill[NW * 64];  // landing area of the filler scale DMAs (never read)
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 2, wn = wave & 3;
+  const int wm = wave / C::WN, wn = wave % C::WN;
   const int l16 = lane & 15, q = lane >> 4;
 
   // ---- which tile
@@ -132,7 +140,7 @@ __global__ __launch_bounds__(kThreads) void gemm_w8a8_big_kernel(GemmArgs a, int
     nt = blockIdx.x - tile * n_tiles;
     if (tile >= grid_blocks) return;
   }
-  const int64_t n0 = nt * kBN;
+  const int64_t n0 = nt * BN;
   if (n0 >= a.N) return;
 
   TileInfo t;
@@ -142,15 +150,16 @@ __global__ __launch_bounds__(kThreads) void gemm_w8a8_big_kernel(GemmArgs a, int
   const uint8_t* Wb = a.W + expert * a.w_estride;
   const float* swb = reinterpret_cast<const float*>(a.ws) + expert * a.ws_estride;
   const int KB = int(a.K >> 7);
+  constexpr int NSB = BN > 128 ? 2 : 1;  // 128-wide weight-scale blocks the tile spans
   // staged once, after the first operand DMA is in flight so the two latencies overlap
   auto stage_weight_scales = [&]() __attribute__((always_inline)) {
-    for (int i = tid; i < 2 * KB; i += kThreads) {
+    for (int i = tid; i < NSB * KB; i += C::THREADS) {
       const int blk = i / KB, kb = i - blk * KB;
       const int64_t nb = min<int64_t>((n0 >> 7) + blk, cdiv(a.N, 128) - 1);
       sSW[blk][kb] = swb[nb * a.ws_s0 + kb * a.ws_s1];
     }
   };
-  const int sw_blk = wn >> 1;  // waves 0-1 cover the first 128 columns, 2-3 the second
+  const int sw_blk = (wn * 64) >> 7;  // the 128-wide scale block of this wave's columns
   const bool vec_store = (a.ldo & 3) == 0;   // 16-byte fp32 stores
   const bool vec8_store = (a.ldo & 7) == 0;  // 16-byte bf16 stores
 
@@ -161,7 +170,7 @@ __global__ __launch_bounds__(kThreads) void gemm_w8a8_big_kernel(GemmArgs a, int
     __syncthreads();
 
     // ---- per-lane DMA sources (32-bit byte offsets: the host routes operands below 4 GiB here)
-    uint32_t oa[C::A_DMA], ob[4];
+    uint32_t oa[C::A_DMA], ob[C::B_DMA];
 #pragma unroll
     for (int b = 0; b < C::A_DMA; ++b) {
       const int row = (wave * C::A_DMA + b) * 8 + (lane >> 3);
@@ -169,60 +178,41 @@ __global__ __launch_bounds__(kThreads) void gemm_w8a8_big_kernel(GemmArgs a, int
       oa[b] = uint32_t(sArow[row] * a.lda + chunk * 16);
     }
 #pragma unroll
-    for (int b = 0; b < 4; ++b) {
+    for (int b = 0; b < C::B_DMA; ++b) {
+      const int d = wave * C::B_DMA + b;  // the tile's d-th 1 KB weight piece
       if (TILED) {
-        // DMA b of this wave = half (b & 1) of the tile of 16-row group 2 wave + b / 2
-        const int64_t g16 = min<int64_t>(n0 / 16 + wave * 2 + (b >> 1), a.N / 16 - 1);
-        ob[b] = uint32_t(g16 * KB * 2048 + (b & 1) * 1024 + lane * 16);
+        // piece d = half (d & 1) of the tile of 16-row group d / 2
+        const int64_t g16 = min<int64_t>(n0 / 16 + (d >> 1), a.N / 16 - 1);
+        ob[b] = uint32_t(g16 * KB * 2048 + (d & 1) * 1024 + lane * 16);
       } else {
-        const int row = (wave * 4 + b) * 8 + (lane >> 3);
+        const int row = d * 8 + (lane >> 3);
         const int chunk = (lane & 7) ^ swz(row);
         const int64_t n = min<int64_t>(n0 + row, a.N - 1);
         ob[b] = uint32_t(n * a.ldw + chunk * 16);
       }
     }
     // activation scales: waves < BM/64 fetch 64 rows each; the others fetch a filler dword
-    // into sPF so that every wave issues the same number of loads per K block
-    const bool sa_wave = wave < BM / 64;
-    const float* gs = a.sa + sArow[(wave % (BM / 64)) * 64 + lane] * a.lds;
+    // into sFill so that every wave issues the same number of loads per K block
+    const bool sa_wave = wave < C::SA_WAVES;
+    const float* gs = a.sa + sArow[(wave % C::SA_WAVES) * 64 + lane] * a.lds;
 
     auto stageA = [&](int s) -> uint8_t* { return sOps + s * C::STAGE_BYTES; };
     auto stageB = [&](int s) -> uint8_t* { return sOps + s * C::STAGE_BYTES + BM * kKS; };
 
-    // one K block: (A_DMA + 4) operand DMAs and one scale DMA per wave
+    // one K block: A_DMA + B_DMA operand DMAs and one scale DMA per wave
     auto issue = [&](int kb, int s) __attribute__((always_inline)) {
       const uint8_t* Ak = A + kb * kKS;
       const uint8_t* Wk = Wb + kb * (TILED ? 2048 : kKS);
       const uint32_t la = __builtin_amdgcn_readfirstlane(lds_addr(stageA(s)) + wave * C::A_DMA * 1024);
-      const uint32_t lb = __builtin_amdgcn_readfirstlane(lds_addr(stageB(s)) + wave * 4096);
+      const uint32_t lb = __builtin_amdgcn_readfirstlane(lds_addr(stageB(s)) + wave * C::B_DMA * 1024);
 #pragma unroll
       for (int b = 0; b < C::A_DMA; ++b) lds_dma16(Ak + oa[b], la + b * 1024);
 #pragma unroll
-      for (int b = 0; b < 4; ++b) lds_dma16(Wk + ob[b], lb + b * 1024);
-      const uint32_t ls = sa_wave ? lds_addr(&sS[s][0]) + wave * 256 : lds_addr(sPF) + wave * 256;
+      for (int b = 0; b < C::B_DMA; ++b) lds_dma16(Wk + ob[b], lb + b * 1024);
+      const uint32_t ls = sa_wave ? lds_addr(&sS[s][0]) + wave * 256 : lds_addr(sFill) + wave * 256;
       lds_dma4(gs + kb, __builtin_amdgcn_readfirstlane(ls));
     };
-    constexpr int kIssueOps = C::A_DMA + 5;
-    // Warm L2 with a later K block: one dword of every 128-byte operand line (threads
-    // 0..BM-1 the activation rows, 256..511 the weight rows; tiled weights: one line each).
-    const uint8_t* pf_base;
-    int pf_stride;
-    if (tid >= 256) {
-      const int r = tid - 256;
-      if (TILED) {
-        const int64_t g16 = min<int64_t>(n0 / 16 + r / 16, a.N / 16 - 1);
-        pf_base = Wb + g16 * KB * 2048 + (r & 15) * 128;
-        pf_stride = 2048;
-      } else {
-        pf_base = Wb + min<int64_t>(n0 + r, a.N - 1) * a.ldw;
-        pf_stride = kKS;
-      }
-    } else {
-      pf_base = A + sArow[tid % BM] * a.lda;
-      pf_stride = kKS;
-    }
-    const uint32_t pf_lds = __builtin_amdgcn_readfirstlane(lds_addr(sPF) + wave * 256);
-    auto prefetch = [&](int kb) __attribute__((always_inline)) { lds_dma4(pf_base + kb * pf_stride, pf_lds); };
+    constexpr int kIssueOps = C::A_DMA + C::B_DMA + 1;
 
     f32x4 acc[TI][4];
 #pragma unroll
@@ -247,7 +237,7 @@ __global__ __launch_bounds__(kThreads) void gemm_w8a8_big_kernel(GemmArgs a, int
         wf[j] = TILED ? read_frag_tiled(cB, wn * 4 + j, lane) : read_frag(cB, wn * 64 + 16 * j + l16, q);
       const float sw = sSW[sw_blk][kb];
       const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
-      const int mrow = wm * (BM / 2);
+      const int mrow = wm * WROWS;
       i32x8 afr[2];  // activation fragments of rows i (slot i & 1)
       float cr[2];   // combined scales of rows i
 #pragma unroll
@@ -278,48 +268,42 @@ __global__ __launch_bounds__(kThreads) void gemm_w8a8_big_kernel(GemmArgs a, int
 
     // ---- K loop.  Loads retire in issue order.  Each iteration waits for its own stage,
     // publishes it with a barrier (which also retires every wave's reads of the stage the
-    // next DMA overwrites), issues the DMA S - 1 blocks ahead plus one L2 touch, computes.
+    // next DMA overwrites), issues the DMA S - 1 blocks ahead, and computes.
     if (S == 2) {
-      // ops after DMA(kb) at the top of iteration kb: the touch issued with it
       issue(0, 0);
-      prefetch(min(1, KB - 1));
       if (m_base == 0) stage_weight_scales();
       for (int kb = 0; kb < KB; ++kb) {
-        wait_vmcnt<1>();
+        wait_vmcnt<0>();
         __syncthreads();
         if (kb + 1 < KB) issue(kb + 1, (kb + 1) & 1);
-        prefetch(min(kb + 2, KB - 1));
         compute(kb, kb & 1);
       }
     } else {
-      // ops after DMA(kb): touch(kb+1), [DMA(kb+1)], touch(kb+2)
+      // ops issued after DMA(kb) at the top of iteration kb: DMA(kb+1) when it exists
       issue(0, 0);
-      prefetch(min(1, KB - 1));
       if (KB > 1) issue(1, 1);
-      prefetch(min(2, KB - 1));
       if (m_base == 0) stage_weight_scales();
       int s = 0;
       for (int kb = 0; kb < KB; ++kb) {
         if (kb + 1 < KB)
-          wait_vmcnt<kIssueOps + 2>();
+          wait_vmcnt<kIssueOps>();
         else
-          wait_vmcnt<2>();
+          wait_vmcnt<0>();
         __syncthreads();
         if (kb + 2 < KB) issue(kb + 2, s == 0 ? 2 : s - 1);
-        prefetch(min(kb + 3, KB - 1));
         compute(kb, s);
         s = s == S - 1 ? 0 : s + 1;
       }
     }
     wait_vmcnt<0>();
 
-    // ---- epilogue: lane owns rows m = wm*BM/2 + 16i + l16, columns n = wn*64 + 16j + 4q .. +3
+    // ---- epilogue: lane owns rows m = wm*WROWS + 16i + l16, columns n = wn*64 + 16j + 4q .. +3
     if (!OUT_F32) {
-      // bf16: stage each wave's BM/2 x 64 block through LDS (the operand stages are free
+      // bf16: stage each wave's WROWS x 64 block through LDS (the operand stages are free
       // now) and write whole 128-byte row segments; 16-byte chunk c of row r sits at chunk
       // position c ^ (r & 7).
       __syncthreads();
-      uint8_t* region = sOps + wave * (BM / 2) * 128;
+      uint8_t* region = sOps + wave * WROWS * 128;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int64_t n = n0 + wn * 64 + 16 * j + 4 * q;
@@ -342,7 +326,7 @@ __global__ __launch_bounds__(kThreads) void gemm_w8a8_big_kernel(GemmArgs a, int
       __builtin_amdgcn_wave_barrier();
       // all chunk reads first (the accumulators are dead, registers are free), then all
       // stores, so each wave keeps its whole block of writes in flight
-      constexpr int CH = BM / 16;  // 16-byte chunks per lane
+      constexpr int CH = WROWS / 8;  // 16-byte chunks per lane
       i32x4 v[CH];
 #pragma unroll
       for (int it = 0; it < CH; ++it) {
@@ -354,7 +338,7 @@ __global__ __launch_bounds__(kThreads) void gemm_w8a8_big_kernel(GemmArgs a, int
         const int id = it * 64 + lane;
         const int row = id >> 3, pc = id & 7;
         const int c = pc ^ (row & 7);
-        const int ml = wm * (BM / 2) + row;
+        const int ml = wm * WROWS + row;
         if (ml >= m_size) continue;
         const int64_t n = n0 + wn * 64 + c * 8;
         uint16_t* o = reinterpret_cast<uint16_t*>(a.out) + sOrow[ml] * a.ldo + n;
@@ -377,7 +361,7 @@ __global__ __launch_bounds__(kThreads) void gemm_w8a8_big_kernel(GemmArgs a, int
         }
 #pragma unroll
         for (int i = 0; i < TI; ++i) {
-          const int ml = wm * (BM / 2) + 16 * i + l16;
+          const int ml = wm * WROWS + 16 * i + l16;
           if (ml >= m_size) continue;
           const int64_t o = sOrow[ml] * a.ldo + n;
           const float v[4] = {acc[i][j][0] + b[0], acc[i][j][1] + b[1], acc[i][j][2] + b[2], acc[i][j][3] + b[3]};
@@ -394,47 +378,46 @@ __global__ __launch_bounds__(kThreads) void gemm_w8a8_big_kernel(GemmArgs a, int
   }
 }
 
-template <int BM, int MODE, bool TL>
+template <int BM, int BN, int NW, int NS, int MODE, bool TL>
 static void launch_big_t(const GemmArgs& a, bool out_f32, int64_t grid_blocks, hipStream_t st) {
-  const int64_t n_tiles = cdiv(a.N, kBN);
+  const int64_t n_tiles = cdiv(a.N, int64_t(BN));
   int64_t nwg = grid_blocks * n_tiles;
   if (MODE == ROWS_DENSE) nwg = cdiv(nwg, 8) * 8;
-  const dim3 grid(static_cast<unsigned>(nwg)), block(kThreads);
+  const dim3 grid(static_cast<unsigned>(nwg)), block(BigCfg<BM, BN, NW, NS>::THREADS);
   const bool bias = a.bias != nullptr;
-#define MXQ_BIG_GO(OF, HB) \
-  hipLaunchKernelGGL((gemm_w8a8_big_kernel<BM, MODE, OF, HB, TL>), grid, block, 0, st, a, grid_blocks, n_tiles)
+#define MXQ_BIG_GO(OF, HB)                                                                                     \
+  hipLaunchKernelGGL((gemm_w8a8_big_kernel<BM, BN, NW, NS, MODE, OF, HB, TL>), grid, block, 0, st, a, grid_blocks, \
+                     n_tiles)
   if (out_f32) { if (bias) MXQ_BIG_GO(true, true); else MXQ_BIG_GO(true, false); }
   else { if (bias) MXQ_BIG_GO(false, true); else MXQ_BIG_GO(false, false); }
 #undef MXQ_BIG_GO
 }
 
-template <int BM>
-static void launch_big_bm(const GemmArgs& a, int row_mode, bool out_f32, int64_t gb, hipStream_t st) {
-  if constexpr (BM == 256) {
-    // routed blocks hold at most 128 rows: the 256-row tile serves dense GEMMs only
-    launch_big_t<BM, ROWS_DENSE, false>(a, out_f32, gb, st);
-    return;
-  }
-  switch (row_mode) {
-    case ROWS_DENSE: launch_big_t<BM, ROWS_DENSE, false>(a, out_f32, gb, st); break;
-    case ROWS_GATHER_TOK:
-      if (a.w_tiled) launch_big_t<BM, ROWS_GATHER_TOK, true>(a, out_f32, gb, st);
-      else launch_big_t<BM, ROWS_GATHER_TOK, false>(a, out_f32, gb, st);
-      break;
-    default:
-      if (a.w_tiled) launch_big_t<BM, ROWS_COMPACT_IN, true>(a, out_f32, gb, st);
-      else launch_big_t<BM, ROWS_COMPACT_IN, false>(a, out_f32, gb, st);
-      break;
-  }
-}
+int big_tile_rows(int shape) { return shape == 0 ? 256 : 128; }
 
-void launch_gemm_w8a8_big(const GemmArgs& a, int row_mode, int bm, bool out_f32, int64_t grid_blocks,
+// Shapes: 0 = 256 x 256 (8 waves, 2 stages), 1 = 128 x 256 (8 waves, 3 stages),
+// 2 = 128 x 128 (4 waves, 2 stages: two workgroups per CU), 3 = 128 x 128 (4 waves, 3 stages).
+void launch_gemm_w8a8_big(const GemmArgs& a, int row_mode, int shape, bool out_f32, int64_t grid_blocks,
                           hipStream_t st) {
   if (grid_blocks <= 0 || a.N <= 0) return;
-  if (bm == 256 && row_mode == ROWS_DENSE)
-    launch_big_bm<256>(a, row_mode, out_f32, grid_blocks, st);
-  else
-    launch_big_bm<128>(a, row_mode, out_f32, grid_blocks, st);
+  if (row_mode == ROWS_DENSE) {
+    switch (shape) {
+      case 0: launch_big_t<256, 256, 8, 2, ROWS_DENSE, false>(a, out_f32, grid_blocks, st); break;
+      case 2: launch_big_t<128, 128, 4, 2, ROWS_DENSE, false>(a, out_f32, grid_blocks, st); break;
+      case 3: launch_big_t<128, 128, 4, 3, ROWS_DENSE, false>(a, out_f32, grid_blocks, st); break;
+      default: launch_big_t<128, 256, 8, 3, ROWS_DENSE, false>(a, out_f32, grid_blocks, st); break;
+    }
+    return;
+  }
+  // routed blocks hold at most 128 rows: the 128 x 256 three-stage tile
+  const bool tl = a.w_tiled != 0;
+  if (row_mode == ROWS_GATHER_TOK) {
+    if (tl) launch_big_t<128, 256, 8, 3, ROWS_GATHER_TOK, true>(a, out_f32, grid_blocks, st);
+    else launch_big_t<128, 256, 8, 3, ROWS_GATHER_TOK, false>(a, out_f32, grid_blocks, st);
+  } else {
+    if (tl) launch_big_t<128, 256, 8, 3, ROWS_COMPACT_IN, true>(a, out_f32, grid_blocks, st);
+    else launch_big_t<128, 256, 8, 3, ROWS_COMPACT_IN, false>(a, out_f32, grid_blocks, st);
+  }
 }
 
 }  // namespace mxq

@@ -34,6 +34,8 @@ struct GemmArgs {
   // activations
   const void* A;        // bf16 or e4m3 rows
   int64_t lda;          // elements (bf16) or bytes (e4m3)
+  int32_t a_silu;       // tiny-block kernel: A rows are [gate | up] pairs of width K; the kernel
+                        // stages bf16(silu(gate) * up) (the SiLU-and-mul fused into stage 2)
   const float* sa;      // e4m3 activations: [rows, K/128] fp32
   int64_t lds;          // row stride of sa (elements)
   // weights (per expert: base + e * w_estride)
@@ -67,10 +69,12 @@ void launch_quant_1x128(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, ui
 void launch_gemm_w8a8(const GemmArgs& a, int row_mode, int tile, bool out_f32, int64_t grid_blocks,
                       hipStream_t stream);
 
-// W8A8 with bm x 256 tiles, bm = 256 or 128 (8 waves, direct-to-LDS loads); 128x128 weight
-// blocks only; K <= 16384; operand offsets below 4 GiB.  Routed modes read plain or tiled weights.
-void launch_gemm_w8a8_big(const GemmArgs& a, int row_mode, int bm, bool out_f32, int64_t grid_blocks,
+// W8A8 with large direct-to-LDS tiles; 128x128 weight blocks only; K <= 16384; operand offsets
+// below 4 GiB.  Dense shape: 0 = 256x256, 1 = 128x256, 2 = 128x128 tiles; routed modes use
+// 128x256 and read plain or tiled weights.  `grid_blocks` = row tiles (dense) or work-list capacity.
+void launch_gemm_w8a8_big(const GemmArgs& a, int row_mode, int shape, bool out_f32, int64_t grid_blocks,
                           hipStream_t stream);
+int big_tile_rows(int shape);
 
 // W8A16 / W4A16: bf16 activations x decoded e4m3 / e2m1 weights (MFMA 16x16x32 bf16).
 void launch_gemm_w16(const GemmArgs& a, int wfmt, int row_mode, int tile, bool out_f32, int64_t grid_blocks,

@@ -217,16 +217,7 @@ __global__ __launch_bounds__(256) void silu_mul_kernel(const uint16_t* __restric
     g = *reinterpret_cast<const uint4*>(ic0 + row * 2 * inter + col);
     u = *reinterpret_cast<const uint4*>(ic0 + row * 2 * inter + inter + col);
   }
-  const uint32_t gw[4] = {g.x, g.y, g.z, g.w}, uw[4] = {u.x, u.y, u.z, u.w};
-  uint32_t hw[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const float g0 = bf16lo(gw[i]), g1 = bf16hi(gw[i]);
-    const float h0 = g0 / (1.0f + __expf(-g0)) * bf16lo(uw[i]);
-    const float h1 = g1 / (1.0f + __expf(-g1)) * bf16hi(uw[i]);
-    hw[i] = pack_bf16x2(h0, h1);
-  }
-  const uint4 h = make_uint4(hw[0], hw[1], hw[2], hw[3]);
+  const uint4 h = silu_mul8(g, u);
   if (!QUANT) {
     if (valid) *reinterpret_cast<uint4*>(ic1 + row * inter + col) = h;
   } else {

@@ -28,6 +28,7 @@
 //  * with weights in the tiled layout (prepack.hip) a step of one 16-row group
 //    is 2 KB of contiguous memory, so each 64-lane load reads 1 KB in one piece;
 //    the plain layout reads 16 rows x 64 bytes per load instead.
+#include "quant_common.hpp"
 #include "tile_rows.hpp"
 
 namespace mxq {
@@ -183,9 +184,18 @@ __global__ __launch_bounds__(256, (SkinnyShape<WFMT, A_E4M3>::W)) void skinny_ke
       for (int c = tid; c < m_size * chunks; c += 256) {
         const int m = c / chunks, cc = c - m * chunks;
         i32x4 v = {0, 0, 0, 0};
-        if (cc < kchunks)
-          v = *reinterpret_cast<const i32x4*>(reinterpret_cast<const uint8_t*>(a.A) + s_arow[m] * a.lda * AE +
-                                               int64_t(cc) * 16);
+        if (cc < kchunks) {
+          const uint8_t* src = reinterpret_cast<const uint8_t*>(a.A) + s_arow[m] * a.lda * AE + int64_t(cc) * 16;
+          if (!A_E4M3 && a.a_silu) {
+            // gate chunk and the matching up chunk K elements further along the row
+            const uint4 g = *reinterpret_cast<const uint4*>(src);
+            const uint4 u = *reinterpret_cast<const uint4*>(src + K * 2);
+            const uint4 h = silu_mul8(g, u);
+            v = i32x4{int(h.x), int(h.y), int(h.z), int(h.w)};
+          } else {
+            v = *reinterpret_cast<const i32x4*>(src);
+          }
+        }
         *reinterpret_cast<i32x4*>(smem + m * L.row_stride + cc * 16) = v;
       }
       if (!MX) {

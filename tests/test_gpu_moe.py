@@ -228,3 +228,21 @@ def test_zero_tokens():
     out = ops.fused_moe_fp8(inp["x"][:0], inp["topk_ids"][:0], inp["topk_weights"][:0], inp["w1"], inp["w1_scale"],
                             inp["w2"], inp["w2_scale"])
     assert out.shape == (0, 256)
+
+
+@pytest.mark.parametrize("kind", ["w8a16", "mxfp4"])
+def test_small_batch_fused_silu_matches_unfused_and_oracle(kind):
+    """M <= 32: every block takes the tiny-block kernel and stage 2 computes the SiLU-and-mul while
+    staging its rows.  Forcing the tiny class keeps the same kernels with the standalone
+    SiLU-and-mul pass, so the two must agree bit for bit; both must match the oracle."""
+    if kind == "w8a16":
+        spec = _small_spec("fused_moe_fp8", 24, 8, 2, 512, 256)
+    else:
+        spec = _small_spec("fused_moe_mxfp4", 16, 8, 4, 2880, 2880)
+    inp = synth.moe_inputs(spec, seed=41, device=gpu())
+    fused = _run_gpu(inp)
+    ops.moe_set_dispatch(mx.MXQ_DISPATCH_FORCED, 0)
+    plain = _run_gpu(inp)
+    torch.cuda.synchronize()
+    assert torch.equal(fused.view(torch.int16), plain.view(torch.int16))
+    assert_bf16_close(bf16_bits(fused), _run_oracle(inp), what=f"{kind} fused SiLU")
