@@ -33,6 +33,26 @@
 
 namespace mxq {
 
+#ifndef MXQ_SK_NTSCALE
+#define MXQ_SK_NTSCALE 1
+#endif
+#if MXQ_SK_NTSCALE
+#define MXQ_SK_NTS(p) __builtin_nontemporal_load(p)
+#else
+#define MXQ_SK_NTS(p) (*(p))
+#endif
+#ifndef MXQ_SK_MXW
+#define MXQ_SK_MXW 3
+#endif
+#ifndef MXQ_SK_FENCE
+#define MXQ_SK_FENCE 0
+#endif
+#if MXQ_SK_FENCE
+#define SK_SLICE_FENCE() __builtin_amdgcn_sched_barrier(0)
+#else
+#define SK_SLICE_FENCE() ((void)0)
+#endif
+
 namespace {
 constexpr int kSkWaves = 4;
 constexpr int kSkMaxRows = 8;
@@ -48,7 +68,7 @@ template <int WFMT, bool AE>
 struct SkinnyShape {
   static constexpr int G = 2;
   static constexpr int D = 3;
-  static constexpr int W = WFMT == W_E2M1_MX ? 3 : 4;
+  static constexpr int W = WFMT == W_E2M1_MX ? MXQ_SK_MXW : 4;
 };
 }  // namespace
 
@@ -123,20 +143,33 @@ __global__ __launch_bounds__(256, (SkinnyShape<WFMT, A_E4M3>::W)) void skinny_ke
   const int64_t ngroups = K / 32;  // MXFP4 scale groups per row
 
   i32x4 wb[D][G][2];
-  uint32_t sb[D][G][2];  // raw e8m0 bytes, combined only where used
+  // e8m0 scales of the lane's two 32-element groups: tiled, the two bytes as loaded (split where
+  // used); plain, one byte each
+  uint32_t sb[D][G][TILED ? 1 : 2];
+  // tiled MXFP4 rows whose length is not a whole number of steps: in the last step, a lane
+  // whose 16-byte chunk is padding reads its row's first chunk of that step instead (a line
+  // lanes 0-15 fetch anyway), so the padding never travels from HBM; its activations are the
+  // LDS zero padding, and e2m1 codes are finite, so the products are exact zeros
+  uint32_t last_h0 = 0u, last_h1 = 1024u;
+  if (TILED && MX) {
+    const uint32_t rb_last = uint32_t(row_bytes - int64_t(nsteps - 1) * 128);
+    if (32u * uint32_t(q) + 16u > rb_last) last_h0 = 0u - 256u * uint32_t(q);
+    if (32u * uint32_t(q) + 32u > rb_last) last_h1 = 0u - 256u * uint32_t(q);
+  }
 
   // all weight / scale addresses are a wave-uniform base plus a 32-bit lane offset
   auto load = [&](int st, int slot) __attribute__((always_inline)) {
     const uint32_t sc = uint32_t(min(st, nsteps - 1));
     if (TILED) {
+      const bool last = MX && int(sc) == nsteps - 1;
+      const uint32_t h0 = last ? last_h0 : 0u, h1 = last ? last_h1 : 1024u;
 #pragma unroll
       for (int g = 0; g < G; ++g) {
-        wb[slot][g][0] = *reinterpret_cast<const i32x4*>(wexp + woff[g] + sc * 2048u);
-        wb[slot][g][1] = *reinterpret_cast<const i32x4*>(wexp + woff[g] + sc * 2048u + 1024u);
+        wb[slot][g][0] = __builtin_nontemporal_load(reinterpret_cast<const i32x4*>(wexp + (woff[g] + sc * 2048u + h0)));
+        wb[slot][g][1] = __builtin_nontemporal_load(reinterpret_cast<const i32x4*>(wexp + (woff[g] + sc * 2048u + h1)));
         if (MX) {
-          const uint32_t v = *reinterpret_cast<const uint16_t*>(sexp + soff[g] + sc * 128u);
-          sb[slot][g][0] = v & 0xffu;
-          sb[slot][g][1] = v >> 8;
+          const uint32_t v = MXQ_SK_NTS(reinterpret_cast<const uint16_t*>(sexp + soff[g] + sc * 128u));
+          sb[slot][g][0] = v;
         }
       }
       return;
@@ -153,11 +186,11 @@ __global__ __launch_bounds__(256, (SkinnyShape<WFMT, A_E4M3>::W)) void skinny_ke
       const uint32_t rowo = woff[g] - uint32_t(q) * 32u;
       const uint32_t o0 = past0 ? rowo : woff[g] + sc * 128u;
       const uint32_t o1 = past1 ? rowo : woff[g] + sc * 128u + 16u;
-      wb[slot][g][0] = *reinterpret_cast<const i32x4*>(wexp + o0);
-      wb[slot][g][1] = *reinterpret_cast<const i32x4*>(wexp + o1);
+      wb[slot][g][0] = __builtin_nontemporal_load(reinterpret_cast<const i32x4*>(wexp + o0));
+      wb[slot][g][1] = __builtin_nontemporal_load(reinterpret_cast<const i32x4*>(wexp + o1));
       if (MX) {
         sb[slot][g][0] = sexp[soff[g] + g0];
-        sb[slot][g][1] = sexp[soff[g] + g1];
+        sb[slot][g][TILED ? 0 : 1] = sexp[soff[g] + g1];
       }
     }
   };
@@ -236,9 +269,13 @@ __global__ __launch_bounds__(256, (SkinnyShape<WFMT, A_E4M3>::W)) void skinny_ke
 #pragma unroll
           for (int g = 0; g < G; ++g) {
             uint32_t o[4];
-            e2m1x8_to_bf16(uint32_t(wb[slot][g][s >> 2][s & 3]), e8m0_to_f32(sb[slot][g][s >> 2]), o);
+            const uint32_t e = TILED ? (sb[slot][g][0] >> (8 * (s >> 2))) & 0xffu : sb[slot][g][(s >> 2) & (TILED ? 0 : 1)];
+            e2m1x8_to_bf16(uint32_t(wb[slot][g][s >> 2][s & 3]), e8m0_to_f32(e), o);
             acc[g] = mfma_16x16x32_bf16(af, i32x4{int(o[0]), int(o[1]), int(o[2]), int(o[3])}, acc[g]);
           }
+          // keep each K slice's fragment read and decode next to its MFMAs (hoisting all of
+          // them costs registers the weight ring needs)
+          SK_SLICE_FENCE();
         }
       } else if constexpr (A_E4M3) {
         const i32x4 a0 = *reinterpret_cast<const i32x4*>(arow + st * KSTEP + q * 32);
