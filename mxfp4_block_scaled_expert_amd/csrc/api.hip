@@ -84,7 +84,7 @@ MoeWorkspace carve_moe(void* base, int64_t M, int64_t H, int64_t I, int32_t E, i
   w.expert_ids = reinterpret_cast<int32_t*>(take(sizeof(int32_t) * mbk));
   w.offsets = reinterpret_cast<int32_t*>(take(sizeof(int32_t) * (mbk + 1)));
   w.num_blocks = reinterpret_cast<int32_t*>(take(sizeof(int32_t)));
-  w.class_lists = reinterpret_cast<int32_t*>(take(sizeof(int32_t) * mbk * kNumClasses));
+  w.class_lists = reinterpret_cast<int32_t*>(take(sizeof(int32_t) * 4 * mbk * kNumClasses));
   w.class_counts = reinterpret_cast<int32_t*>(take(sizeof(int32_t) * kNumClasses));
   if (act_quant) {
     w.qx = take(size_t(M) * H);
@@ -247,7 +247,7 @@ mxq_status run_moe(const void* x, int64_t M, int64_t H, int64_t I, int32_t E, in
     for (int c = 0; c < kNumClasses; ++c) {
       const int64_t ub = class_bound(c, R, E, mbk, pol);
       if (ub <= 0) continue;
-      g.rt.work_list = w.class_lists + int64_t(c) * mbk;
+      g.rt.work_desc = w.class_lists + int64_t(c) * mbk * 4;
       g.rt.work_count = w.class_counts + c;
       // Tiny blocks: the weight-streaming MFMA kernel keeps a pass of activation rows over the
       // whole K in LDS; past its LDS cap they take the 16-row MFMA tile.  The vector-ALU GEMV

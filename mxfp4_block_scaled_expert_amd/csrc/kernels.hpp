@@ -24,7 +24,8 @@ struct BlockRouting {
   const int32_t* sorted_ids;  // [max_blocks * block_m]
   const int32_t* expert_ids;  // [max_blocks]
   const int32_t* offsets;     // [max_blocks + 1]
-  const int32_t* work_list;   // block ids of this tile class
+  const int32_t* work_desc;   // this tile class's blocks, 4 ints each: block id, expert, first
+                              // compact row, row count (entries past work_count are stale)
   const int32_t* work_count;  // device scalar: number of valid entries
   int32_t block_m;
   int32_t topk;
@@ -98,8 +99,10 @@ int64_t tiled_scale_steps(int64_t groups);
 void launch_prepack_w(const uint8_t* w, int64_t E, int64_t N, int64_t row_bytes, uint8_t* out, hipStream_t stream);
 void launch_prepack_s(const uint8_t* s, int64_t E, int64_t N, int64_t groups, uint8_t* out, hipStream_t stream);
 
-// Expert sort / block alignment.  Optionally also fills per-class work lists
-// (class_lists[c * list_stride + i], class_counts[c]) using the per-block selector.
+// Expert sort / block alignment.  Optionally also fills per-class work lists using the
+// per-block selector: class c's i-th block descriptor is the int4 at
+// class_lists + (c * list_stride + i) * 4 (block id, expert, first compact row, row
+// count), and class_counts[c] holds the number of entries.
 struct ClassPolicy {
   int32_t n_classes;      // 0: no class lists
   int32_t bound[8];       // class c takes blocks with bound[c-1] < m_size <= bound[c]

@@ -16,10 +16,12 @@
 // The per-block selector (implementation items 1-2: the decision is taken per
 // expert block from its real row count, not once per layer from an average)
 // assigns every non-empty block to the smallest tile class whose row bound
-// holds it and appends the block id to that class's work list.  Classes the
-// host did not launch (their lower bound reaches the token count, which caps an
-// expert's rows when a token's experts are distinct) receive nothing: a block
-// past every launched bound goes to the largest launched class.
+// holds it and appends the block's descriptor (block id, expert, first compact
+// row, row count) to that class's work list, so that a tile kernel learns all of
+// it in one read.  Classes the host did not launch (their lower bound reaches the
+// token count, which caps an expert's rows when a token's experts are distinct)
+// receive nothing: a block past every launched bound goes to the largest
+// launched class.
 #include "kernels.hpp"
 #include "quant_common.hpp"
 
@@ -121,7 +123,8 @@ __global__ __launch_bounds__(kAlignThreads) void moe_align_kernel(
       if (pol.n_classes > 0) {
         const int c = pick_class(pol, m_size);
         const int pos = atomicAdd(&cls_cnt[c], 1);
-        class_lists[int64_t(c) * list_stride + pos] = mb;
+        *reinterpret_cast<int4*>(class_lists + (int64_t(c) * list_stride + pos) * 4) =
+            make_int4(mb, e, row_start[e] + b * block_m, m_size);
       }
     }
   }

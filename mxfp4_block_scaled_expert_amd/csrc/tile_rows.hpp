@@ -31,12 +31,18 @@ __device__ __forceinline__ bool tile_info(const GemmArgs& a, int64_t tile, TileI
     t.m_total = int(min<int64_t>(BM, a.M - t.m0));
     return true;
   }
-  if (tile >= int64_t(*a.rt.work_count)) return false;
-  t.mb = a.rt.work_list[tile];
-  t.expert = a.rt.expert_ids[t.mb];
-  t.off = a.rt.offsets[t.mb];
-  t.m_total = a.rt.offsets[t.mb + 1] - t.off;
-  return t.m_total > 0 && t.expert >= 0;
+  // the count and the descriptor are read together (one memory round trip); a launch holds
+  // at most the list's capacity of tiles, so the descriptor read stays in bounds
+  const int4 d = *reinterpret_cast<const int4*>(a.rt.work_desc + tile * 4);
+  const int32_t count = *a.rt.work_count;
+  // one combined test over every field (no short-circuit), so that no part of either read
+  // is deferred behind the other
+  const bool live = (tile < int64_t(count)) & (d.x >= 0) & (d.y >= 0) & (d.w > 0);
+  t.mb = d.x;
+  t.expert = d.y;
+  t.off = d.z;
+  t.m_total = d.w;
+  return live;
 }
 
 // Input row / output row of local row i (0 <= i < m_total).
