@@ -29,8 +29,8 @@
 //    t + 2 is issued before product t is promoted);
 //  * dense tiles are rastered so that the tiles resident on one XCD (the
 //    dispatcher deals workgroups round-robin over the 8 XCDs) share operands in
-//    that XCD's L2, and every K block's operands are touched in L2 one block
-//    before their DMA.
+//    that XCD's L2; routed tiles run block-fastest, so the blocks of one expert
+//    share its weight tiles.
 #include "tile_rows.hpp"
 
 namespace mxq {
@@ -233,10 +233,11 @@ __global__ __launch_bounds__((BigCfg<BM, BN, NW, NS>::THREADS)) void gemm_w8a8_b
 
     // One K block: hold the wave's 4 weight fragments and stream the TI activation
     // fragments.  The products t = 4 i + j run as a software pipeline: step t issues the
-    // MFMA of product t + 2 and promotes product t (acc += partial * sa * sw), whose MFMA
-    // went out two MFMAs earlier, from a ring of three partial-sum registers.  A scheduling
-    // fence after each step keeps that order (left alone, the scheduler moves each
-    // promotion right behind the MFMA that produces it and stalls on the result).
+    // MFMA of product t + 2 and then promotes product t (acc += partial * sa * sw), whose
+    // MFMA went out two MFMAs earlier, from a ring of three partial-sum registers.
+    // Scheduling fences around the promotion keep that order (left alone, the scheduler
+    // moves each promotion right behind the MFMA that produces it and stalls on the
+    // result).
     auto compute = [&](int kb, int s) __attribute__((always_inline)) {
       const uint8_t* cA = stageA(s);
       const uint8_t* cB = stageB(s);
@@ -269,6 +270,7 @@ __global__ __launch_bounds__((BigCfg<BM, BN, NW, NS>::THREADS)) void gemm_w8a8_b
           // the last MFMA of row im is out: its fragment slot takes row im + 2
           if (jm == 3 && im + 2 < TI) afr[im & 1] = read_frag(cA, mrow + 16 * (im + 2) + l16, q);
         }
+        __builtin_amdgcn_sched_barrier(0);
         const int i = u >> 2, j = u & 3;
 #pragma unroll
         for (int r = 0; r < 4; ++r) acc[i][j][r] = fmaf(pb[u % NB][r], cr[i & 1], acc[i][j][r]);
