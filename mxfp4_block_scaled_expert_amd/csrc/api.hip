@@ -118,7 +118,11 @@ int64_t class_bound(int c, int64_t R, int32_t E, int64_t max_blocks, const Class
 // M caps the rows of one expert when every token names distinct experts, so the
 // classes whose lower bound reaches M are not launched (a block beyond that, from
 // repeated ids, still lands in the largest launched class).
-ClassPolicy make_policy(int64_t M, int64_t R, int32_t E) {
+//
+// `pass_rows` (> 0) is how many rows the weight-streaming tiny-block kernel stages per pass
+// for these sizes; a taller block streams its expert's weights once per pass, so at larger
+// token counts the tiny class stops there and the next tile class takes such blocks.
+ClassPolicy make_policy(int64_t M, int64_t R, int32_t E, int pass_rows) {
   std::lock_guard<std::mutex> lk(g_dispatch_mu);
   ClassPolicy pol{};
   pol.n_classes = kNumClasses;
@@ -128,7 +132,10 @@ ClassPolicy make_policy(int64_t M, int64_t R, int32_t E) {
   // When M is at most twice the tiny-block bound the tiny class takes every block (an expert
   // holds at most M rows): blocks of bound..M rows take a few passes of the weight-streaming
   // kernel instead of a mostly empty launch of the next tile class.
-  if (g_tiny_max_rows > 0 && M <= 2 * int64_t(g_tiny_max_rows)) pol.bound[0] = std::max<int>(pol.bound[0], int(M));
+  if (g_tiny_max_rows > 0 && M <= 2 * int64_t(g_tiny_max_rows))
+    pol.bound[0] = std::max<int>(pol.bound[0], int(M));
+  else if (pass_rows > 0 && g_tiny_kernel == MXQ_TINY_MFMA)
+    pol.bound[0] = std::min<int>(pol.bound[0], pass_rows);
   pol.n_live = kNumClasses;
   for (int c = 1; c < kNumClasses; ++c)
     if (pol.bound[c - 1] >= M) {
@@ -158,7 +165,10 @@ mxq_status run_moe(const void* x, int64_t M, int64_t H, int64_t I, int32_t E, in
   const int64_t mbk = mxq_moe_max_blocks(M, topk, E, kMoeBlockM);
   MoeWorkspace w = carve_moe(ws, M, H, I, E, topk, act_quant);
   if (!ws || ws_bytes < w.bytes) return MXQ_ERR_WORKSPACE;
-  const ClassPolicy pol = make_policy(M, R, E);
+  const int wfmt_tiny = wfmt == W_E2M1_MX ? W_E2M1_MX : W_E4M3_BLOCK;
+  const ClassPolicy pol = make_policy(M, R, E,
+                                      std::min(skinny_pass_rows(wfmt_tiny, act_quant, H),
+                                               skinny_pass_rows(wfmt_tiny, act_quant, I)));
   int tiny;
   {
     std::lock_guard<std::mutex> lk(g_dispatch_mu);
