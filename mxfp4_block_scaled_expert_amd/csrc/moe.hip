@@ -10,7 +10,7 @@
 // The layout produced here: experts in ascending id, rows of one expert in
 // ascending flat id (a stable counting sort), pad value R in unused slots,
 // trailing blocks with expert -1 and offset R.  The whole sort runs in one
-// 1024-thread workgroup with no host synchronisation; ranks inside a wave come
+// workgroup (256 or 1024 threads) with no host synchronisation; ranks inside a wave come
 // from ballots over the bits of the expert id, so the order is deterministic.
 //
 // The per-block selector (implementation items 1-2: the decision is taken per
@@ -27,8 +27,6 @@
 
 namespace mxq {
 
-constexpr int kAlignThreads = 1024;
-constexpr int kAlignWaves = kAlignThreads / 64;
 
 __device__ __forceinline__ int pick_class(const ClassPolicy& pol, int m_size) {
   if (pol.forced >= 0) return pol.forced;
@@ -37,17 +35,22 @@ __device__ __forceinline__ int pick_class(const ClassPolicy& pol, int m_size) {
   return pol.n_live - 1;  // the tile kernels loop over row sub-tiles, so any block fits
 }
 
-__global__ __launch_bounds__(kAlignThreads) void moe_align_kernel(
+// One workgroup of T threads (1024 for large routings; 256 when the routing is small, where
+// the kernel is a chain of barriers and fewer waves make each one cheaper).
+template <int T>
+__global__ __launch_bounds__(T) void moe_align_kernel(
     const int32_t* __restrict__ ids, int64_t R, int32_t E, int32_t block_m, int32_t* __restrict__ sorted_ids,
     int32_t* __restrict__ expert_ids, int32_t* __restrict__ offsets, int32_t* __restrict__ num_blocks,
     int64_t max_blocks, ClassPolicy pol, int32_t* __restrict__ class_lists, int64_t list_stride,
     int32_t* __restrict__ class_counts, int write_pads) {
+  constexpr int kAlignThreads = T;
+  constexpr int kAlignWaves = T / 64;
   extern __shared__ int32_t smem[];
   int32_t* cnt = smem;                     // [E]
   int32_t* blk_start = cnt + E;            // [E + 1]
   int32_t* row_start = blk_start + E + 1;  // [E + 1]
   int32_t* running = row_start + E + 1;    // [E]
-  int32_t* wave_cnt = running + E;         // [kAlignWaves][E]
+  int32_t* wave_cnt = running + E;         // [T / 64][E]
   __shared__ int32_t cls_cnt[8];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -58,8 +61,11 @@ __global__ __launch_bounds__(kAlignThreads) void moe_align_kernel(
   if (tid < 8) cls_cnt[tid] = 0;
   __syncthreads();
 
-  // 1. histogram (expert ids outside [0, E) are ignored)
-  for (int64_t r = tid; r < R; r += kAlignThreads) {
+  // 1. histogram (expert ids outside [0, E) are ignored); the first T ids stay in registers
+  // for the scatter
+  const int e_first = tid < R ? ids[tid] : -1;
+  if (e_first >= 0 && e_first < E) atomicAdd(&cnt[e_first], 1);
+  for (int64_t r = tid + kAlignThreads; r < R; r += kAlignThreads) {
     const int e = ids[r];
     if (e >= 0 && e < E) atomicAdd(&cnt[e], 1);
   }
@@ -161,7 +167,7 @@ __global__ __launch_bounds__(kAlignThreads) void moe_align_kernel(
     for (int i = tid; i < kAlignWaves * E; i += kAlignThreads) wave_cnt[i] = 0;
     __syncthreads();
     const int64_t r = base + tid;
-    int e = (r < R) ? ids[r] : -1;
+    int e = base == 0 ? e_first : (r < R) ? ids[r] : -1;
     const bool valid = e >= 0 && e < E;
     uint64_t mask = __ballot(valid);
     for (int bit = 0; bit < nbits; ++bit) {
@@ -194,10 +200,18 @@ void launch_moe_align(const int32_t* topk_ids, int64_t M, int32_t topk, int32_t 
                       int64_t max_blocks, const ClassPolicy& pol, int32_t* class_lists, int64_t list_stride,
                       int32_t* class_counts, bool write_pads, hipStream_t stream) {
   // cnt[E] + blk_start[E+1] + row_start[E+1] + running[E] + wave_cnt[waves][E]
-  const size_t smem = sizeof(int32_t) * (size_t(E) * 4 + 2 + size_t(kAlignWaves) * E);
-  hipLaunchKernelGGL(moe_align_kernel, dim3(1), dim3(kAlignThreads), smem, stream, topk_ids, M * topk, E, block_m,
-                     sorted_ids, expert_ids, offsets, num_blocks, max_blocks, pol, class_lists, list_stride,
-                     class_counts, write_pads ? 1 : 0);
+  const int64_t R = M * topk;
+  const bool small = R <= 2048;
+  const int waves = small ? 4 : 16;
+  const size_t smem = sizeof(int32_t) * (size_t(E) * 4 + 2 + size_t(waves) * E);
+  if (small)
+    hipLaunchKernelGGL(moe_align_kernel<256>, dim3(1), dim3(256), smem, stream, topk_ids, R, E, block_m,
+                       sorted_ids, expert_ids, offsets, num_blocks, max_blocks, pol, class_lists, list_stride,
+                       class_counts, write_pads ? 1 : 0);
+  else
+    hipLaunchKernelGGL(moe_align_kernel<1024>, dim3(1), dim3(1024), smem, stream, topk_ids, R, E, block_m,
+                       sorted_ids, expert_ids, offsets, num_blocks, max_blocks, pol, class_lists, list_stride,
+                       class_counts, write_pads ? 1 : 0);
 }
 
 // ---------------------------------------------------------------- SiLU-and-mul
@@ -252,22 +266,39 @@ void launch_silu_mul(const uint16_t* ic0, int64_t rows, int64_t inter, uint16_t*
 __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ y, const float* __restrict__ w,
                                                       const int32_t* __restrict__ ids, int32_t E, int64_t M,
                                                       int32_t topk, int64_t H, uint16_t* __restrict__ out) {
+  constexpr int kBatch = 8;  // routed rows whose loads go out together
   const int64_t per_row = H / 4;
   const int64_t idx = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
   if (idx >= M * per_row) return;
   const int64_t t = idx / per_row;
   const int64_t col = (idx - t * per_row) * 4;
   float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
-  for (int k = 0; k < topk; ++k) {
-    const int64_t r = t * topk + k;
-    const int e = ids[r];
-    if (e < 0 || e >= E) continue;
-    const float wk = w[r];
-    const float4 v = *reinterpret_cast<const float4*>(y + r * H + col);
-    a0 = fmaf(wk, v.x, a0);
-    a1 = fmaf(wk, v.y, a1);
-    a2 = fmaf(wk, v.z, a2);
-    a3 = fmaf(wk, v.w, a3);
+  for (int k0 = 0; k0 < topk; k0 += kBatch) {
+    // routing ids and weights of the batch first, then every y read, then the sums (k ascending):
+    // two memory round trips per batch instead of two per routed row
+    float wk[kBatch];
+    int64_t rk[kBatch];
+    bool ok[kBatch];
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) {
+      const int k = min(k0 + j, topk - 1);
+      const int64_t r = t * topk + k;
+      const int e = ids[r];
+      ok[j] = k0 + j < topk && e >= 0 && e < E;
+      wk[j] = w[r];
+      rk[j] = r;
+    }
+    float4 v[kBatch];
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) v[j] = *reinterpret_cast<const float4*>(y + rk[j] * H + col);
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) {
+      if (!ok[j]) continue;  // past top-k, or an id outside [0, E) (its y row is never written)
+      a0 = fmaf(wk[j], v[j].x, a0);
+      a1 = fmaf(wk[j], v[j].y, a1);
+      a2 = fmaf(wk[j], v[j].z, a2);
+      a3 = fmaf(wk[j], v[j].w, a3);
+    }
   }
   uint2 o;
   o.x = pack_bf16x2(a0, a1);
