@@ -51,8 +51,9 @@ def _args():
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-secondary", action="store_true")
-    p.add_argument("--only", choices=["linear", "decode", "prefill", "copy"], default=None,
-                   help="time one workload only (profiling runs); copy = counter calibration")
+    p.add_argument("--only", choices=["linear", "decode", "prefill", "copy", "ablation"], default=None,
+                   help="time one workload only (profiling runs); copy = counter calibration; "
+                        "ablation = per-block vs per-layer tile-class dispatch")
     return p.parse_args()
 
 
@@ -163,12 +164,13 @@ def _touched_bytes(inp) -> int:
     return int(used.size * per + 2 * M * H * 2 + ids.size * 8)
 
 
-def bench_moe(name: str, steps: int, warmup: int, seed: int, layout: str = "tiled"):
-    """Times one fused-MoE call.  ``layout="tiled"``: the weights are relaid out once with the
-    load-time prepack before timing (as a model would at weight-loading time)."""
+def _moe_setup(name_or_spec, seed: int, layout: str = "tiled", M=None):
+    """Inputs (weights prepacked once for ``layout="tiled"``, as a model would at weight-loading
+    time), workspace and a closure running one fused-MoE call."""
     from mxfp4_block_scaled_expert_amd import ops, synth
+    from mxfp4_block_scaled_expert_amd import _lib as L
     dev = torch.device("cuda", 0)
-    inp = synth.moe_inputs(name, seed=seed, device=dev)
+    inp = synth.moe_inputs(name_or_spec, seed=seed, device=dev, M=M)
     byts = _touched_bytes(inp)
     if layout == "tiled":
         for k in ("w1", "w2"):
@@ -177,13 +179,12 @@ def bench_moe(name: str, steps: int, warmup: int, seed: int, layout: str = "tile
             for k in ("w1_scale", "w2_scale"):
                 inp[k] = ops.moe_prepack_scales(inp[k])
         torch.cuda.synchronize()
-    M, H = inp["x"].shape
+    Mt, H = inp["x"].shape
     I, E, topk = inp["I"], inp["E"], inp["topk"]
     mx = inp["kind"] == "fused_moe_mxfp4"
-    from mxfp4_block_scaled_expert_amd import _lib as L
-    ws = ops.fused_moe_workspace(M, H, I, E, topk, L.MXQ_WEIGHTS_MXFP4 if mx else L.MXQ_WEIGHTS_FP8_BLOCK,
+    ws = ops.fused_moe_workspace(Mt, H, I, E, topk, L.MXQ_WEIGHTS_MXFP4 if mx else L.MXQ_WEIGHTS_FP8_BLOCK,
                                  inp["act_quant"], dev)
-    out = torch.empty(M, H, dtype=torch.bfloat16, device=dev)
+    out = torch.empty(Mt, H, dtype=torch.bfloat16, device=dev)
 
     def run():
         if mx:
@@ -195,27 +196,75 @@ def bench_moe(name: str, steps: int, warmup: int, seed: int, layout: str = "tile
                               inp["w2"], inp["w2_scale"], None, act_quant=inp["act_quant"], workspace=ws, out=out,
                               weight_layout=layout)
 
+    flops = 2.0 * Mt * topk * (2 * I * H + H * I)
+    return {"inp": inp, "run": run, "bytes": byts, "flops": flops, "M": Mt}
+
+
+def _time_calls(run, steps: int, warmup: int) -> float:
+    """Average µs of `steps` back-to-back calls between one pair of events (the weights of the
+    decode and prefill workloads exceed the 256 MB last-level cache, so every call streams them
+    from HBM)."""
     for _ in range(warmup):
         run()
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
-    # back-to-back calls between one pair of events (the weights of the decode and prefill
-    # workloads exceed the 256 MB last-level cache, so every call streams them from HBM)
     e0, e1 = _events()
     e0.record(stream)
     for _ in range(steps):
         run()
     e1.record(stream)
     torch.cuda.synchronize()
-    med = e0.elapsed_time(e1) / steps
-    flops = 2.0 * M * topk * (2 * I * H + H * I)
+    return e0.elapsed_time(e1) / steps * 1e3
+
+
+def bench_moe(name: str, steps: int, warmup: int, seed: int, layout: str = "tiled"):
+    """Times one fused-MoE workload."""
+    w = _moe_setup(name, seed, layout)
+    us = _time_calls(w["run"], steps, warmup)
+    byts, flops = w["bytes"], w["flops"]
     return {
-        "workload": name, "weight_layout": layout, "us_avg": med * 1e3, "tflops": flops / (med * 1e-3) / 1e12,
-        "touched_bytes": byts, "weight_gbs": byts / (med * 1e-3) / 1e9,
-        "hbm_frac": byts / (med * 1e-3) / 1e9 / HBM_PEAK_GBS,
-        "fp8_mfma_frac": flops / (med * 1e-3) / 1e12 / FP8_PEAK_TFLOPS,
-        "distinct_experts": int(np.unique(inp["topk_ids"].cpu().numpy()).size),
+        "workload": name, "weight_layout": layout, "us_avg": us, "tflops": flops / (us * 1e-6) / 1e12,
+        "touched_bytes": byts, "weight_gbs": byts / (us * 1e-6) / 1e9,
+        "hbm_frac": byts / (us * 1e-6) / 1e9 / HBM_PEAK_GBS,
+        "fp8_mfma_frac": flops / (us * 1e-6) / 1e12 / FP8_PEAK_TFLOPS,
+        "distinct_experts": int(np.unique(w["inp"]["topk_ids"].cpu().numpy()).size),
     }
+
+
+def bench_dispatch_ablation(steps: int, warmup: int):
+    """The pages' central comparison at kernel level: each expert block choosing its tile class
+    from its own row count (the default) against one class for the whole layer chosen from the
+    average rows per expert, over decode batch sizes and routing skews.  One JSON line per case;
+    `speedup` = layer-average time / per-block time."""
+    from mxfp4_block_scaled_expert_amd import ops, synth
+    from mxfp4_block_scaled_expert_amd import _lib as L
+    ds = dict(kind="fused_moe_fp8", E=256, topk=8, H=7168, I=2048, act_quant=True)
+    cases = [
+        ("c3 counts (4,5,33,0,0,12,1,73), W8A16", "moe_block_fp8_w8a16_e8_h2048_i1024", None, 1003),
+        ("GPT-OSS MXFP4 decode M=32", "moe_mxfp4_gptoss_decode_m32", 32, 1004),
+        ("GPT-OSS MXFP4 decode M=64", "moe_mxfp4_gptoss_decode_m32", 64, 1004),
+        ("DeepSeek W8A8 M=512 uniform", dict(ds, zipf=0.0), 512, 1005),
+        ("DeepSeek W8A8 M=512 Zipf 1.1", dict(ds, zipf=1.1), 512, 1005),
+        ("DeepSeek W8A8 M=4096 uniform", dict(ds, zipf=0.0), 4096, 1005),
+        ("DeepSeek W8A8 M=4096 Zipf 1.1", dict(ds, zipf=1.1), 4096, 1005),
+    ]
+    rows = []
+    for label, spec, M, seed in cases:
+        w = _moe_setup(spec, seed, "tiled", M=M)
+        big = w["M"] >= 512
+        n, wu = (max(3, steps // 10), 2) if big else (steps, warmup)
+        res = {}
+        for mode, key in ((L.MXQ_DISPATCH_PER_BLOCK, "per_block_us"), (L.MXQ_DISPATCH_LAYER_AVERAGE, "layer_avg_us")):
+            ops.moe_set_dispatch(mode, 0, 16)
+            res[key] = _time_calls(w["run"], n, wu)
+        ops.moe_set_dispatch()
+        row = {"case": label, "M": w["M"], **res, "speedup": res["layer_avg_us"] / res["per_block_us"],
+               "per_block_weight_gbs": w["bytes"] / (res["per_block_us"] * 1e-6) / 1e9}
+        print(json.dumps(row), flush=True)
+        rows.append(row)
+        del w
+        torch.cuda.empty_cache()
+    return rows
 
 
 # ----------------------------------------------------------------------------- CPU oracle
@@ -272,6 +321,9 @@ def main():
 
     if a.only == "copy":
         print(json.dumps(calibrate_copy()), flush=True)
+        return
+    if a.only == "ablation":
+        bench_dispatch_ablation(a.steps, a.warmup)
         return
     if a.only == "decode":
         print(json.dumps(bench_moe("moe_mxfp4_gptoss_decode_m32", a.steps, a.warmup, 1004)), flush=True)

@@ -228,9 +228,11 @@ mxq_status mxq_moe_prepack_scales(const void* s, int64_t E, int64_t N, int64_t g
  *        max(1, M * topk / E) rows (the per-layer rule page [A] replaces; for
  *        ablation measurements).
  *   tiny_max_rows: largest block that takes the tiny-block class in per-block mode
- *        (default 16, max 16).  With the MFMA tiny kernel the bound is also capped at
- *        the rows that kernel stages per pass, unless M <= 2 * tiny_max_rows (then the
- *        tiny class takes every block, taller ones in several passes).
+ *        (default 16, max 16).  When M <= 2 * tiny_max_rows the tiny class takes every
+ *        block (taller ones in several passes).  Otherwise, for W8A8 with K <= 16384 on
+ *        both stages, the tiny bound is cut to the rows the MFMA tiny kernel stages per
+ *        pass and the 16-, 32- and 64-row classes fold into the 128-row class (its
+ *        128 x 256 tile streams the weights better even for short blocks).
  *   tiny_kernel: the tiny-block kernel -- MXQ_TINY_MFMA (default: weights streamed into
  *        registers, K reduced by MFMAs, up to 8 rows per pass) or MXQ_TINY_GEMV
  *        (vector-ALU dot products with a wavefront reduction, 4 rows per pass; plain

@@ -119,10 +119,15 @@ int64_t class_bound(int c, int64_t R, int32_t E, int64_t max_blocks, const Class
 // classes whose lower bound reaches M are not launched (a block beyond that, from
 // repeated ids, still lands in the largest launched class).
 //
-// `pass_rows` (> 0) is how many rows the weight-streaming tiny-block kernel stages per pass
-// for these sizes; a taller block streams its expert's weights once per pass, so at larger
-// token counts the tiny class stops there and the next tile class takes such blocks.
-ClassPolicy make_policy(int64_t M, int64_t R, int32_t E, int pass_rows) {
+// `big_tile`: the stage GEMMs have the 128 x 256 direct-to-LDS W8A8 tile (W8A8, K <= 16384).
+// Measured on the prefill shapes (E = 256, 4096 tokens), that tile streams an expert's weights
+// better than the 16-64-row tiles even for short blocks, and each extra class launch leaves the
+// GPU partly idle while its few blocks run; so at larger token counts the classes between the
+// tiny one and the 128-row one are folded into the 128-row one, and the tiny class is cut to
+// the rows its kernel stages in one pass (`pass_rows`: a taller block would stream its
+// expert's weights once per pass).  With bf16 activations the next classes have no such tile,
+// and taking a few passes in the tiny kernel measured faster.
+ClassPolicy make_policy(int64_t M, int64_t R, int32_t E, int pass_rows, bool big_tile) {
   std::lock_guard<std::mutex> lk(g_dispatch_mu);
   ClassPolicy pol{};
   pol.n_classes = kNumClasses;
@@ -132,10 +137,12 @@ ClassPolicy make_policy(int64_t M, int64_t R, int32_t E, int pass_rows) {
   // When M is at most twice the tiny-block bound the tiny class takes every block (an expert
   // holds at most M rows): blocks of bound..M rows take a few passes of the weight-streaming
   // kernel instead of a mostly empty launch of the next tile class.
-  if (g_tiny_max_rows > 0 && M <= 2 * int64_t(g_tiny_max_rows))
+  if (g_tiny_max_rows > 0 && M <= 2 * int64_t(g_tiny_max_rows)) {
     pol.bound[0] = std::max<int>(pol.bound[0], int(M));
-  else if (pass_rows > 0 && g_tiny_kernel == MXQ_TINY_MFMA)
-    pol.bound[0] = std::min<int>(pol.bound[0], pass_rows);
+  } else if (big_tile) {
+    if (pass_rows > 0 && g_tiny_kernel == MXQ_TINY_MFMA) pol.bound[0] = std::min<int>(pol.bound[0], pass_rows);
+    for (int c = 1; c < kNumClasses - 1; ++c) pol.bound[c] = pol.bound[0];
+  }
   pol.n_live = kNumClasses;
   for (int c = 1; c < kNumClasses; ++c)
     if (pol.bound[c - 1] >= M) {
@@ -146,10 +153,11 @@ ClassPolicy make_policy(int64_t M, int64_t R, int32_t E, int pass_rows) {
     pol.forced = g_forced_class;
     pol.n_live = kNumClasses;
   } else if (g_dispatch_mode == MXQ_DISPATCH_LAYER_AVERAGE) {
+    // the per-layer rule maps the average onto the plain class bounds (no folding)
     const int64_t avg = std::max<int64_t>(1, R / std::max<int32_t>(E, 1));
     int c = kNumClasses - 1;
     for (int i = 0; i < kNumClasses - 1; ++i)
-      if (avg <= pol.bound[i]) { c = i; break; }
+      if (avg <= (i == 0 ? g_tiny_max_rows : kClassRows[i])) { c = i; break; }
     pol.forced = c;
     pol.n_live = kNumClasses;
   }
@@ -168,7 +176,8 @@ mxq_status run_moe(const void* x, int64_t M, int64_t H, int64_t I, int32_t E, in
   const int wfmt_tiny = wfmt == W_E2M1_MX ? W_E2M1_MX : W_E4M3_BLOCK;
   const ClassPolicy pol = make_policy(M, R, E,
                                       std::min(skinny_pass_rows(wfmt_tiny, act_quant, H),
-                                               skinny_pass_rows(wfmt_tiny, act_quant, I)));
+                                               skinny_pass_rows(wfmt_tiny, act_quant, I)),
+                                      act_quant && H <= 16384 && I <= 16384);
   int tiny;
   {
     std::lock_guard<std::mutex> lk(g_dispatch_mu);
