@@ -31,6 +31,8 @@
 //    dispatcher deals workgroups round-robin over the 8 XCDs) share operands in
 //    that XCD's L2; routed tiles run block-fastest, so the blocks of one expert
 //    share its weight tiles.
+#include <type_traits>
+
 #include "tile_rows.hpp"
 
 namespace mxq {
@@ -238,7 +240,12 @@ __global__ __launch_bounds__((BigCfg<BM, BN, NW, NS>::THREADS)) void gemm_w8a8_b
     // Scheduling fences around the promotion keep that order (left alone, the scheduler
     // moves each promotion right behind the MFMA that produces it and stalls on the
     // result).
-    auto compute = [&](int kb, int s) __attribute__((always_inline)) {
+    // `tie` (a compile-time count <= TI): the wave's leading 16-row sub-tiles that hold rows of
+    // the block; the others are neither multiplied nor promoted (a short routed block in a
+    // 128-row tile costs only its own rows' MFMAs).
+    auto compute = [&](int kb, int s, auto tie) __attribute__((always_inline)) {
+      constexpr int TIE = decltype(tie)::value;
+      constexpr int NTE = 4 * TIE;
       const uint8_t* cA = stageA(s);
       const uint8_t* cB = stageB(s);
       const float* cS = sS[s];
@@ -254,6 +261,7 @@ __global__ __launch_bounds__((BigCfg<BM, BN, NW, NS>::THREADS)) void gemm_w8a8_b
       float cr[2];   // combined scales of rows i
 #pragma unroll
       for (int r = 0; r < 2; ++r) {
+        if (r >= TIE) break;
         afr[r] = read_frag(cA, mrow + 16 * r + l16, q);
         cr[r] = cS[mrow + 16 * r + l16] * sw;
       }
@@ -262,20 +270,39 @@ __global__ __launch_bounds__((BigCfg<BM, BN, NW, NS>::THREADS)) void gemm_w8a8_b
       for (int u = 0; u < DIST; ++u) pb[u] = mfma_16x16x128_e4m3(wf[u & 3], afr[(u >> 2) & 1], zero);
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int u = 0; u < NT; ++u) {
+      for (int u = 0; u < NTE; ++u) {
         const int um = u + DIST;
-        if (um < NT) {
+        if (um < NTE) {
           const int im = um >> 2, jm = um & 3;
           pb[um % NB] = mfma_16x16x128_e4m3(wf[jm], afr[im & 1], zero);
           // the last MFMA of row im is out: its fragment slot takes row im + 2
-          if (jm == 3 && im + 2 < TI) afr[im & 1] = read_frag(cA, mrow + 16 * (im + 2) + l16, q);
+          if (jm == 3 && im + 2 < TIE) afr[im & 1] = read_frag(cA, mrow + 16 * (im + 2) + l16, q);
         }
         __builtin_amdgcn_sched_barrier(0);
         const int i = u >> 2, j = u & 3;
 #pragma unroll
         for (int r = 0; r < 4; ++r) acc[i][j][r] = fmaf(pb[u % NB][r], cr[i & 1], acc[i][j][r]);
-        if (j == 3 && i + 2 < TI) cr[i & 1] = cS[mrow + 16 * (i + 2) + l16] * sw;
+        if (j == 3 && i + 2 < TIE) cr[i & 1] = cS[mrow + 16 * (i + 2) + l16] * sw;
         __builtin_amdgcn_sched_barrier(0);
+      }
+    };
+    // sub-tiles of this wave holding rows of the pass (routed blocks may be short; dense tiles
+    // are full except possibly the last, which keeps the full product)
+    const int n_ti = MODE == ROWS_DENSE ? TI : max(0, min(TI, (m_size - wm * WROWS + 15) / 16));
+    auto compute_rows = [&](int kb, int s) __attribute__((always_inline)) {
+      if (n_ti == TI) {
+        compute(kb, s, std::integral_constant<int, TI>{});
+        return;
+      }
+      switch (n_ti) {
+        case 1: compute(kb, s, std::integral_constant<int, 1>{}); break;
+        case 2: if constexpr (TI > 2) compute(kb, s, std::integral_constant<int, (TI > 2 ? 2 : TI)>{}); break;
+        case 3: if constexpr (TI > 3) compute(kb, s, std::integral_constant<int, (TI > 3 ? 3 : TI)>{}); break;
+        case 4: if constexpr (TI > 4) compute(kb, s, std::integral_constant<int, (TI > 4 ? 4 : TI)>{}); break;
+        case 5: if constexpr (TI > 5) compute(kb, s, std::integral_constant<int, (TI > 5 ? 5 : TI)>{}); break;
+        case 6: if constexpr (TI > 6) compute(kb, s, std::integral_constant<int, (TI > 6 ? 6 : TI)>{}); break;
+        case 7: if constexpr (TI > 7) compute(kb, s, std::integral_constant<int, (TI > 7 ? 7 : TI)>{}); break;
+        default: break;  // no rows of the pass in this wave's sub-tiles
       }
     };
 
@@ -289,7 +316,7 @@ __global__ __launch_bounds__((BigCfg<BM, BN, NW, NS>::THREADS)) void gemm_w8a8_b
         wait_vmcnt<0>();
         __syncthreads();
         if (kb + 1 < KB) issue(kb + 1, (kb + 1) & 1);
-        compute(kb, kb & 1);
+        compute_rows(kb, kb & 1);
       }
     } else {
       // ops issued after DMA(kb) at the top of iteration kb: DMA(kb+1) when it exists
@@ -304,7 +331,7 @@ __global__ __launch_bounds__((BigCfg<BM, BN, NW, NS>::THREADS)) void gemm_w8a8_b
           wait_vmcnt<0>();
         __syncthreads();
         if (kb + 2 < KB) issue(kb + 2, s == 0 ? 2 : s - 1);
-        compute(kb, s);
+        compute_rows(kb, s);
         s = s == S - 1 ? 0 : s + 1;
       }
     }
