@@ -42,7 +42,7 @@ __global__ __launch_bounds__(T) void moe_align_kernel(
     const int32_t* __restrict__ ids, int64_t R, int32_t E, int32_t block_m, int32_t* __restrict__ sorted_ids,
     int32_t* __restrict__ expert_ids, int32_t* __restrict__ offsets, int32_t* __restrict__ num_blocks,
     int64_t max_blocks, ClassPolicy pol, int32_t* __restrict__ class_lists, int64_t list_stride,
-    int32_t* __restrict__ class_counts, int write_pads) {
+    int32_t* __restrict__ class_counts, int write_pads, int cache_ids) {
   constexpr int kAlignThreads = T;
   constexpr int kAlignWaves = T / 64;
   extern __shared__ int32_t smem[];
@@ -51,6 +51,7 @@ __global__ __launch_bounds__(T) void moe_align_kernel(
   int32_t* row_start = blk_start + E + 1;  // [E + 1]
   int32_t* running = row_start + E + 1;    // [E]
   int32_t* wave_cnt = running + E;         // [T / 64][E]
+  int32_t* s_ids = wave_cnt + (T / 64) * E; // [R] when cache_ids: the ids, read once from memory
   __shared__ int32_t cls_cnt[8];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -61,13 +62,23 @@ __global__ __launch_bounds__(T) void moe_align_kernel(
   if (tid < 8) cls_cnt[tid] = 0;
   __syncthreads();
 
-  // 1. histogram (expert ids outside [0, E) are ignored); the first T ids stay in registers
-  // for the scatter
+  // 1. histogram (expert ids outside [0, E) are ignored).  The first T ids stay in registers
+  // for the scatter, the rest are read 8 per thread at a time (one memory round trip per
+  // batch) and, when they fit, kept in LDS for the scatter.
   const int e_first = tid < R ? ids[tid] : -1;
   if (e_first >= 0 && e_first < E) atomicAdd(&cnt[e_first], 1);
-  for (int64_t r = tid + kAlignThreads; r < R; r += kAlignThreads) {
-    const int e = ids[r];
-    if (e >= 0 && e < E) atomicAdd(&cnt[e], 1);
+  constexpr int kIdBatch = 8;
+  for (int64_t r0 = int64_t(tid) + kAlignThreads; r0 < R; r0 += int64_t(kAlignThreads) * kIdBatch) {
+    int eb[kIdBatch];
+#pragma unroll
+    for (int j = 0; j < kIdBatch; ++j) eb[j] = ids[min<int64_t>(r0 + int64_t(j) * kAlignThreads, R - 1)];
+#pragma unroll
+    for (int j = 0; j < kIdBatch; ++j) {
+      const int64_t r = r0 + int64_t(j) * kAlignThreads;
+      if (r >= R) break;
+      if (eb[j] >= 0 && eb[j] < E) atomicAdd(&cnt[eb[j]], 1);
+      if (cache_ids) s_ids[r] = eb[j];
+    }
   }
   __syncthreads();
 
@@ -167,7 +178,7 @@ __global__ __launch_bounds__(T) void moe_align_kernel(
     for (int i = tid; i < kAlignWaves * E; i += kAlignThreads) wave_cnt[i] = 0;
     __syncthreads();
     const int64_t r = base + tid;
-    int e = base == 0 ? e_first : (r < R) ? ids[r] : -1;
+    int e = base == 0 ? e_first : (r >= R) ? -1 : cache_ids ? s_ids[r] : ids[r];
     const bool valid = e >= 0 && e < E;
     uint64_t mask = __ballot(valid);
     for (int bit = 0; bit < nbits; ++bit) {
@@ -203,15 +214,18 @@ void launch_moe_align(const int32_t* topk_ids, int64_t M, int32_t topk, int32_t 
   const int64_t R = M * topk;
   const bool small = R <= 2048;
   const int waves = small ? 4 : 16;
-  const size_t smem = sizeof(int32_t) * (size_t(E) * 4 + 2 + size_t(waves) * E);
+  size_t smem = sizeof(int32_t) * (size_t(E) * 4 + 2 + size_t(waves) * E);
+  // keep the ids in LDS for the scatter when they fit beside the tables (gfx950: 160 KB)
+  const bool cache = !small && smem + sizeof(int32_t) * size_t(R) <= size_t(152) * 1024;
+  if (cache) smem += sizeof(int32_t) * size_t(R);
   if (small)
     hipLaunchKernelGGL(moe_align_kernel<256>, dim3(1), dim3(256), smem, stream, topk_ids, R, E, block_m,
                        sorted_ids, expert_ids, offsets, num_blocks, max_blocks, pol, class_lists, list_stride,
-                       class_counts, write_pads ? 1 : 0);
+                       class_counts, write_pads ? 1 : 0, 0);
   else
     hipLaunchKernelGGL(moe_align_kernel<1024>, dim3(1), dim3(1024), smem, stream, topk_ids, R, E, block_m,
                        sorted_ids, expert_ids, offsets, num_blocks, max_blocks, pol, class_lists, list_stride,
-                       class_counts, write_pads ? 1 : 0);
+                       class_counts, write_pads ? 1 : 0, cache ? 1 : 0);
 }
 
 // ---------------------------------------------------------------- SiLU-and-mul
