@@ -10,8 +10,11 @@
 // The layout produced here: experts in ascending id, rows of one expert in
 // ascending flat id (a stable counting sort), pad value R in unused slots,
 // trailing blocks with expert -1 and offset R.  The whole sort runs in one
-// workgroup (256 or 1024 threads) with no host synchronisation; ranks inside a wave come
-// from ballots over the bits of the expert id, so the order is deterministic.
+// workgroup (256 or 1024 threads) with no host synchronisation.  Wave w owns a contiguous
+// chunk of the routed rows and walks it 64 rows at a time, twice: first counting its rows per
+// expert, then (after a prefix over the waves) placing them; ranks inside a 64-row step come
+// from ballots over the bits of the expert id.  No barrier is needed inside a walk and the
+// order is deterministic.
 //
 // The per-block selector (implementation items 1-2: the decision is taken per
 // expert block from its real row count, not once per layer from an average)
@@ -49,36 +52,60 @@ __global__ __launch_bounds__(T) void moe_align_kernel(
   int32_t* cnt = smem;                     // [E]
   int32_t* blk_start = cnt + E;            // [E + 1]
   int32_t* row_start = blk_start + E + 1;  // [E + 1]
-  int32_t* running = row_start + E + 1;    // [E]
-  int32_t* wave_cnt = running + E;         // [T / 64][E]
+  int32_t* wave_cnt = row_start + E + 1;   // [T / 64][E]: a wave's rows per expert, then its base
   int32_t* s_ids = wave_cnt + (T / 64) * E; // [R] when cache_ids: the ids, read once from memory
   __shared__ int32_t cls_cnt[8];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  for (int e = tid; e < E; e += kAlignThreads) {
-    cnt[e] = 0;
-    running[e] = 0;
-  }
+  int32_t* my_cnt = wave_cnt + wave * E;
+  for (int e = lane; e < E; e += 64) my_cnt[e] = 0;
   if (tid < 8) cls_cnt[tid] = 0;
-  __syncthreads();
 
-  // 1. histogram (expert ids outside [0, E) are ignored).  The first T ids stay in registers
-  // for the scatter, the rest are read 8 per thread at a time (one memory round trip per
-  // batch) and, when they fit, kept in LDS for the scatter.
-  const int e_first = tid < R ? ids[tid] : -1;
-  if (e_first >= 0 && e_first < E) atomicAdd(&cnt[e_first], 1);
+  // rows of wave w: [w * chunk, min(R, (w + 1) * chunk)), chunk a multiple of 64
+  const int64_t chunk = ((R + kAlignWaves - 1) / kAlignWaves + 63) / 64 * 64;
+  const int64_t r_lo = min<int64_t>(R, int64_t(wave) * chunk), r_hi = min<int64_t>(R, r_lo + chunk);
+  int nbits = 1;
+  while ((1 << nbits) < E) ++nbits;
+  const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  // lanes holding the same valid expert id as this lane (ballots over the id's bits)
+  auto same_expert = [&](int e, bool valid) __attribute__((always_inline)) {
+    uint64_t mask = __ballot(valid);
+    for (int bit = 0; bit < nbits; ++bit) {
+      const bool set = valid && ((e >> bit) & 1);
+      const uint64_t bm = __ballot(set);
+      mask &= set ? bm : ~bm;
+    }
+    return mask;
+  };
+
+  // 1. per-wave histogram of the chunk (expert ids outside [0, E) are ignored); the ids are read
+  // 8 steps at a time and, when they fit, kept in LDS for the second walk
   constexpr int kIdBatch = 8;
-  for (int64_t r0 = int64_t(tid) + kAlignThreads; r0 < R; r0 += int64_t(kAlignThreads) * kIdBatch) {
+  for (int64_t r0 = r_lo; r0 < r_hi; r0 += 64 * kIdBatch) {
     int eb[kIdBatch];
 #pragma unroll
-    for (int j = 0; j < kIdBatch; ++j) eb[j] = ids[min<int64_t>(r0 + int64_t(j) * kAlignThreads, R - 1)];
+    for (int j = 0; j < kIdBatch; ++j) eb[j] = ids[min<int64_t>(r0 + 64 * j + lane, R - 1)];
 #pragma unroll
     for (int j = 0; j < kIdBatch; ++j) {
-      const int64_t r = r0 + int64_t(j) * kAlignThreads;
-      if (r >= R) break;
-      if (eb[j] >= 0 && eb[j] < E) atomicAdd(&cnt[eb[j]], 1);
-      if (cache_ids) s_ids[r] = eb[j];
+      const int64_t r = r0 + 64 * j + lane;
+      if (r0 + 64 * j >= r_hi) break;  // wave-uniform
+      const int e = r < r_hi ? eb[j] : -1;
+      if (cache_ids && r < r_hi) s_ids[r] = e;
+      const bool valid = e >= 0 && e < E;
+      const uint64_t mask = same_expert(e, valid);
+      if (valid && __popcll(mask & lt) == 0) my_cnt[e] += __popcll(mask);
     }
+  }
+  __syncthreads();
+  // per expert: total rows, and each wave's first position among them
+  for (int e = tid; e < E; e += kAlignThreads) {
+    int acc = 0;
+    for (int w = 0; w < kAlignWaves; ++w) {
+      const int c = wave_cnt[w * E + e];
+      wave_cnt[w * E + e] = acc;
+      acc += c;
+    }
+    cnt[e] = acc;
   }
   __syncthreads();
 
@@ -171,38 +198,21 @@ __global__ __launch_bounds__(T) void moe_align_kernel(
   __syncthreads();
   if (pol.n_classes > 0 && tid < pol.n_classes) class_counts[tid] = cls_cnt[tid];
 
-  // 4. stable scatter, 1024 rows at a time
-  int nbits = 1;
-  while ((1 << nbits) < E) ++nbits;
-  for (int64_t base = 0; base < R; base += kAlignThreads) {
-    for (int i = tid; i < kAlignWaves * E; i += kAlignThreads) wave_cnt[i] = 0;
-    __syncthreads();
-    const int64_t r = base + tid;
-    int e = base == 0 ? e_first : (r >= R) ? -1 : cache_ids ? s_ids[r] : ids[r];
+  // 4. stable scatter: each wave walks its chunk again; a row's position within its expert is
+  // the wave's base for that expert plus its rank among the wave's earlier rows of the expert
+  for (int64_t r0 = r_lo; r0 < r_hi; r0 += 64) {
+    const int64_t r = r0 + lane;
+    const int e = r < r_hi ? (cache_ids ? s_ids[r] : ids[r]) : -1;
     const bool valid = e >= 0 && e < E;
-    uint64_t mask = __ballot(valid);
-    for (int bit = 0; bit < nbits; ++bit) {
-      const bool set = valid && ((e >> bit) & 1);
-      const uint64_t bm = __ballot(set);
-      mask &= set ? bm : ~bm;
-    }
-    const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    const uint64_t mask = same_expert(e, valid);
     const int rank = __popcll(mask & lt);
-    if (valid && rank == 0) wave_cnt[wave * E + e] = __popcll(mask);
-    __syncthreads();
+    int pos = 0;
+    if (valid) pos = my_cnt[e] + rank;
+    if (valid && rank == 0) my_cnt[e] += __popcll(mask);
     if (valid) {
-      int pos = running[e] + rank;
-      for (int w = 0; w < wave; ++w) pos += wave_cnt[w * E + e];
       const int b = pos / block_m, slot = pos - b * block_m;
       sorted_ids[int64_t(blk_start[e] + b) * block_m + slot] = int32_t(r);
     }
-    __syncthreads();
-    for (int ee = tid; ee < E; ee += kAlignThreads) {
-      int add = 0;
-      for (int w = 0; w < kAlignWaves; ++w) add += wave_cnt[w * E + ee];
-      running[ee] += add;
-    }
-    __syncthreads();
   }
 }
 
@@ -210,18 +220,18 @@ void launch_moe_align(const int32_t* topk_ids, int64_t M, int32_t topk, int32_t 
                       int32_t* sorted_ids, int32_t* expert_ids, int32_t* offsets, int32_t* num_blocks,
                       int64_t max_blocks, const ClassPolicy& pol, int32_t* class_lists, int64_t list_stride,
                       int32_t* class_counts, bool write_pads, hipStream_t stream) {
-  // cnt[E] + blk_start[E+1] + row_start[E+1] + running[E] + wave_cnt[waves][E]
+  // cnt[E] + blk_start[E+1] + row_start[E+1] + wave_cnt[waves][E] (+ ids[R])
   const int64_t R = M * topk;
-  const bool small = R <= 2048;
+  const bool small = R <= 2048;  // one 64-row step per wave or a few
   const int waves = small ? 4 : 16;
-  size_t smem = sizeof(int32_t) * (size_t(E) * 4 + 2 + size_t(waves) * E);
+  size_t smem = sizeof(int32_t) * (size_t(E) * 3 + 2 + size_t(waves) * E);
   // keep the ids in LDS for the scatter when they fit beside the tables (gfx950: 160 KB)
-  const bool cache = !small && smem + sizeof(int32_t) * size_t(R) <= size_t(152) * 1024;
+  const bool cache = smem + sizeof(int32_t) * size_t(R) <= size_t(152) * 1024;
   if (cache) smem += sizeof(int32_t) * size_t(R);
   if (small)
     hipLaunchKernelGGL(moe_align_kernel<256>, dim3(1), dim3(256), smem, stream, topk_ids, R, E, block_m,
                        sorted_ids, expert_ids, offsets, num_blocks, max_blocks, pol, class_lists, list_stride,
-                       class_counts, write_pads ? 1 : 0, 0);
+                       class_counts, write_pads ? 1 : 0, cache ? 1 : 0);
   else
     hipLaunchKernelGGL(moe_align_kernel<1024>, dim3(1), dim3(1024), smem, stream, topk_ids, R, E, block_m,
                        sorted_ids, expert_ids, offsets, num_blocks, max_blocks, pol, class_lists, list_stride,
