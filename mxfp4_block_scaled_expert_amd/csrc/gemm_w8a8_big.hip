@@ -37,10 +37,6 @@
 
 namespace mxq {
 
-#ifndef MXQ_BIG_ROUTED_BLOCK_MAJOR
-#define MXQ_BIG_ROUTED_BLOCK_MAJOR 0
-#endif
-
 namespace {
 
 constexpr int kKS = 128;
@@ -141,17 +137,11 @@ __global__ __launch_bounds__((BigCfg<BM, BN, NW, NS>::THREADS)) void gemm_w8a8_b
     tile = band * gm + in_band % band_rows;
     nt = in_band / band_rows;
   } else {
-#if MXQ_BIG_ROUTED_BLOCK_MAJOR
-    tile = blockIdx.x / n_tiles;
-    nt = blockIdx.x - tile * n_tiles;
-    if (tile >= grid_blocks) return;
-#else
     // routed: block fastest, so the blocks running together read the same weight columns, and
     // the blocks of one heavily routed expert share each weight tile through the caches
     // instead of each streaming the whole expert
     nt = blockIdx.x / grid_blocks;
     tile = blockIdx.x - nt * grid_blocks;
-#endif
   }
   const int64_t n0 = nt * BN;
   if (n0 >= a.N) return;

@@ -33,41 +33,22 @@
 
 namespace mxq {
 
-#ifndef MXQ_SK_NTSCALE
-#define MXQ_SK_NTSCALE 1
-#endif
-#if MXQ_SK_NTSCALE
-#define MXQ_SK_NTS(p) __builtin_nontemporal_load(p)
-#else
-#define MXQ_SK_NTS(p) (*(p))
-#endif
-#ifndef MXQ_SK_MXW
-#define MXQ_SK_MXW 3
-#endif
-#ifndef MXQ_SK_FENCE
-#define MXQ_SK_FENCE 0
-#endif
-#if MXQ_SK_FENCE
-#define SK_SLICE_FENCE() __builtin_amdgcn_sched_barrier(0)
-#else
-#define SK_SLICE_FENCE() ((void)0)
-#endif
-
 namespace {
 constexpr int kSkWaves = 4;
 constexpr int kSkMaxRows = 8;
 
-// groups per wave (G) and ring depth in steps (D) per weight / activation format
-// groups per wave (G), ring depth in steps (D) and the waves per SIMD the register
-// budget targets (W), per weight / activation format; chosen by measurement on the
-// decode workload (no register spills at these budgets)
+// Waves per SIMD the register budget targets, per weight format: MXFP4 (decode work per step
+// is larger) 3, e4m3 4; chosen by measurement on the decode workloads, no register spills at
+// these budgets.  Groups per wave and ring depth: G = 2, D = 3 for outputs of at least
+// MXQ_SK_GSEL rows, else G = 1, D = 4 (see skinny_groups).
+#ifndef MXQ_SK_MXW
+#define MXQ_SK_MXW 3
+#endif
 #ifndef MXQ_SK_GSEL
 #define MXQ_SK_GSEL 4096
 #endif
 template <int WFMT, bool AE>
 struct SkinnyShape {
-  static constexpr int G = 2;
-  static constexpr int D = 3;
   static constexpr int W = WFMT == W_E2M1_MX ? MXQ_SK_MXW : 4;
 };
 }  // namespace
@@ -168,7 +149,7 @@ __global__ __launch_bounds__(256, (SkinnyShape<WFMT, A_E4M3>::W)) void skinny_ke
         wb[slot][g][0] = __builtin_nontemporal_load(reinterpret_cast<const i32x4*>(wexp + (woff[g] + sc * 2048u + h0)));
         wb[slot][g][1] = __builtin_nontemporal_load(reinterpret_cast<const i32x4*>(wexp + (woff[g] + sc * 2048u + h1)));
         if (MX) {
-          const uint32_t v = MXQ_SK_NTS(reinterpret_cast<const uint16_t*>(sexp + soff[g] + sc * 128u));
+          const uint32_t v = __builtin_nontemporal_load(reinterpret_cast<const uint16_t*>(sexp + soff[g] + sc * 128u));
           sb[slot][g][0] = v;
         }
       }
@@ -273,9 +254,6 @@ __global__ __launch_bounds__(256, (SkinnyShape<WFMT, A_E4M3>::W)) void skinny_ke
             e2m1x8_to_bf16(uint32_t(wb[slot][g][s >> 2][s & 3]), e8m0_to_f32(e), o);
             acc[g] = mfma_16x16x32_bf16(af, i32x4{int(o[0]), int(o[1]), int(o[2]), int(o[3])}, acc[g]);
           }
-          // keep each K slice's fragment read and decode next to its MFMAs (hoisting all of
-          // them costs registers the weight ring needs)
-          SK_SLICE_FENCE();
         }
       } else if constexpr (A_E4M3) {
         const i32x4 a0 = *reinterpret_cast<const i32x4*>(arow + st * KSTEP + q * 32);
