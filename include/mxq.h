@@ -229,7 +229,12 @@ mxq_status mxq_moe_prepack_scales(const void* s, int64_t E, int64_t N, int64_t g
  *        ablation measurements).
  *   tiny_max_rows: largest block that takes the tiny-block class in per-block mode
  *        (default 16, max 16).  When M <= 2 * tiny_max_rows the tiny class takes every
- *        block (taller ones in several passes).  Otherwise, for W8A8 with K <= 16384 on
+ *        block (taller ones in several passes); with bf16 activations, the MFMA tiny
+ *        kernel, at most 4096 routed rows, E <= 512 and both stages' operands fitting the
+ *        kernel's LDS budget, this case runs as two persistent expert-streaming kernels
+ *        that group the routed rows by expert themselves (no sort and no block tables;
+ *        the SiLU-and-mul ends stage 1) -- same arithmetic, bit-identical outputs.
+ *        Otherwise, for W8A8 with K <= 16384 on
  *        both stages, the tiny bound is cut to the rows the MFMA tiny kernel stages per
  *        pass and the 16-, 32- and 64-row classes fold into the 128-row class (its
  *        128 x 256 tile streams the weights better even for short blocks).

@@ -46,6 +46,11 @@ int g_forced_class = 0;
 int g_tiny_max_rows = 16;
 int g_tiny_kernel = MXQ_TINY_MFMA;
 constexpr size_t kSkinnyMaxLds = 64 * 1024;
+// Expert-streaming path: routing tables and two activation buffers per workgroup in LDS, at
+// most kStreamMaxLds so that two or more workgroups share a compute unit.
+constexpr int64_t kStreamMaxRows = 4096;
+constexpr int32_t kStreamMaxExperts = 512;
+constexpr size_t kStreamMaxLds = 80 * 1024;
 #ifndef MXQ_DENSE_BIG_SHAPE
 #define MXQ_DENSE_BIG_SHAPE 0
 #endif
@@ -183,12 +188,61 @@ mxq_status run_moe(const void* x, int64_t M, int64_t H, int64_t I, int32_t E, in
     std::lock_guard<std::mutex> lk(g_dispatch_mu);
     tiny = g_tiny_kernel;
   }
+  const bool mx = wfmt == W_E2M1_MX;
+  const int wfmt_w16 = mx ? W_E2M1_MX : W_E4M3_BLOCK;
+
+  // Every block of the routing is tiny and the activations stay bf16: the expert-streaming
+  // kernels group the routed rows by expert themselves (no sort, no block tables), stage 1 ends
+  // in the SiLU-and-mul, and rows are indexed by flat routed id up to the combine.
+  if (!act_quant && pol.forced < 0 && pol.n_live == 1 && tiny == MXQ_TINY_MFMA && R <= kStreamMaxRows &&
+      E <= kStreamMaxExperts && I % 16 == 0 &&
+      expert_stream_lds_bytes(wfmt_w16, 1, 2 * I, H, E, R) <= kStreamMaxLds &&
+      expert_stream_lds_bytes(wfmt_w16, 2, H, I, E, R) <= kStreamMaxLds) {
+    const EsRoute er{ids, int32_t(R), E, topk};
+    GemmArgs s1{};
+    s1.A = x;
+    s1.lda = H;
+    s1.W = static_cast<const uint8_t*>(w1);
+    s1.ldw = mx ? H / 2 : H;
+    s1.w_tiled = tiled;
+    s1.w_estride = tiled ? 2 * I * tiled_steps(s1.ldw) * 128 : s1.ldw * 2 * I;
+    s1.ws = w1s;
+    s1.ws_s0 = mx ? H / 32 : H / 128;
+    s1.ws_s1 = 1;
+    s1.ws_estride = mx ? (tiled ? 2 * I * tiled_scale_steps(H / 32) * 8 : 2 * I * (H / 32)) : cdiv(2 * I, 128) * (H / 128);
+    s1.bias = b1;
+    s1.bias_estride = 2 * I;
+    s1.out = w.ic1;
+    s1.ldo = I;
+    s1.M = R;
+    s1.N = 2 * I;
+    s1.K = H;
+    GemmArgs s2{};
+    s2.A = w.ic1;
+    s2.lda = I;
+    s2.W = static_cast<const uint8_t*>(w2);
+    s2.ldw = mx ? I / 2 : I;
+    s2.w_tiled = tiled;
+    s2.w_estride = tiled ? H * tiled_steps(s2.ldw) * 128 : s2.ldw * H;
+    s2.ws = w2s;
+    s2.ws_s0 = mx ? I / 32 : I / 128;
+    s2.ws_s1 = 1;
+    s2.ws_estride = mx ? (tiled ? H * tiled_scale_steps(I / 32) * 8 : H * (I / 32)) : cdiv(H, 128) * (I / 128);
+    s2.out = w.y;
+    s2.ldo = H;
+    s2.M = R;
+    s2.N = H;
+    s2.K = I;
+    launch_expert_stream(s1, wfmt_w16, 1, er, st);
+    launch_expert_stream(s2, wfmt_w16, 2, er, st);
+    launch_combine(w.y, wts, ids, E, M, topk, H, static_cast<uint16_t*>(out), st);
+    return launch_status();
+  }
 
   launch_moe_align(ids, M, topk, E, kMoeBlockM, w.sorted_ids, w.expert_ids, w.offsets, w.num_blocks, mbk, pol,
                    w.class_lists, mbk, w.class_counts, false, st);
   if (act_quant) launch_quant_1x128(static_cast<const uint16_t*>(x), M, H, H, w.qx, H, w.sx, st);
 
-  const bool mx = wfmt == W_E2M1_MX;
   BlockRouting rt{w.sorted_ids, w.expert_ids, w.offsets, nullptr, nullptr, kMoeBlockM, topk};
 
   // stage 1: ic0 = x @ w1^T (+ b1), compact rows
@@ -248,7 +302,6 @@ mxq_status run_moe(const void* x, int64_t M, int64_t H, int64_t I, int32_t E, in
   g2.K = I;
   g2.rt = rt;
 
-  const int wfmt_w16 = mx ? W_E2M1_MX : W_E4M3_BLOCK;
   // With bf16 activations and only the tiny-block class launched, stage 2 computes the
   // SiLU-and-mul while staging its rows (no ic1 round trip, one launch fewer).
   const bool fuse_silu = !act_quant && pol.forced < 0 && pol.n_live == 1 && tiny == MXQ_TINY_MFMA &&

@@ -30,9 +30,10 @@
 //  * dense tiles are rastered so that the tiles resident on one XCD (the
 //    dispatcher deals workgroups round-robin over the 8 XCDs) share operands in
 //    that XCD's L2; routed tiles run block-fastest, so the blocks of one expert
-//    share its weight tiles.
+//    (adjacent in the work list) share its weight tiles.
 #include <type_traits>
 
+#include "lds_dma.hpp"
 #include "tile_rows.hpp"
 
 namespace mxq {
@@ -60,26 +61,6 @@ struct BigCfg {
 
 __device__ __forceinline__ int swz(int row) { return (row & 7) ^ ((row >> 3) & 1); }
 
-typedef __attribute__((address_space(3))) void* lds_ptr_t;
-
-__device__ __forceinline__ uint32_t lds_addr(const void* p) {
-  return uint32_t(reinterpret_cast<uintptr_t>((lds_ptr_t)(const_cast<void*>(p))));
-}
-
-// GLOBAL_LOAD_LDS (each lane's `size` bytes land at M0 + lane * size).  Issued
-// as inline asm so the compiler does not treat the loads of a later K block
-// as a hazard for the LDS reads of the current one (it cannot tell the stages
-// apart and would wait for the DMA before every fragment read); the kernel
-// waits on vmcnt itself before each barrier.
-__device__ __forceinline__ void lds_dma16(const void* g, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(lds)
-               : "memory", "m0");
-}
-__device__ __forceinline__ void lds_dma4(const void* g, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off" ::"v"(g), "s"(lds)
-               : "memory", "m0");
-}
-
 // 32-byte fragment of row `row` (K chunks 2q, 2q+1) from a swizzled row-major tile.
 __device__ __forceinline__ i32x8 read_frag(const uint8_t* tile, int row, int q) {
   const int s = swz(row);
@@ -97,11 +78,6 @@ __device__ __forceinline__ i32x8 read_frag_tiled(const uint8_t* tile, int g, int
   return i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
 }
 
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt immediate");
-  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
-}
 
 }  // namespace
 
@@ -138,8 +114,9 @@ __global__ __launch_bounds__((BigCfg<BM, BN, NW, NS>::THREADS)) void gemm_w8a8_b
     nt = in_band / band_rows;
   } else {
     // routed: block fastest, so the blocks running together read the same weight columns, and
-    // the blocks of one heavily routed expert share each weight tile through the caches
-    // instead of each streaming the whole expert
+    // the blocks of one heavily routed expert (adjacent in the work list) share each weight
+    // tile through the caches instead of each streaming the whole expert.  (Rastering bands of
+    // entries per XCD, as for dense tiles, measured slower on the skewed prefill routing.)
     nt = blockIdx.x / grid_blocks;
     tile = blockIdx.x - nt * grid_blocks;
   }
@@ -412,7 +389,7 @@ template <int BM, int BN, int NW, int NS, int MODE, bool TL>
 static void launch_big_t(const GemmArgs& a, bool out_f32, int64_t grid_blocks, hipStream_t st) {
   const int64_t n_tiles = cdiv(a.N, int64_t(BN));
   int64_t nwg = grid_blocks * n_tiles;
-  if (MODE == ROWS_DENSE) nwg = cdiv(nwg, 8) * 8;
+  if (MODE == ROWS_DENSE) nwg = cdiv(nwg, 8) * 8;  // whole rounds over the 8 XCDs
   const dim3 grid(static_cast<unsigned>(nwg)), block(BigCfg<BM, BN, NW, NS>::THREADS);
   const bool bias = a.bias != nullptr;
 #define MXQ_BIG_GO(OF, HB)                                                                                     \

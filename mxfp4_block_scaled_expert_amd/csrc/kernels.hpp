@@ -95,6 +95,20 @@ size_t skinny_lds_bytes(int wfmt, bool a_e4m3, int64_t K);
 // activation rows the tiny-block kernel stages per pass (a taller block re-reads its weights)
 int skinny_pass_rows(int wfmt, bool a_e4m3, int64_t K);
 
+// Persistent expert-streaming kernel for routings made only of tiny expert blocks (bf16
+// activations, e2m1 or e4m3 weights): each workgroup groups the routed rows by expert itself
+// (no sorted block tables) and rows are indexed by flat routed id.  Stage 1 reads x rows
+// (flat id / topk), takes N = 2 I weight rows (gate then up, I % 16 == 0) and writes
+// h = bf16(silu(gate + b) * (up + b)) as [R, I] bf16 (b: fp32 bias, optional); stage 2 reads h
+// rows and writes [R, N] fp32.
+struct EsRoute {
+  const int32_t* ids;  // [R] expert of each flat routed row; ids outside [0, E) are dropped
+  int32_t R, E, topk;
+};
+void launch_expert_stream(const GemmArgs& a, int wfmt, int stage, const EsRoute& rt, hipStream_t stream);
+// Dynamic LDS of one workgroup of that kernel (N: weight rows of the stage, K: reduction length).
+size_t expert_stream_lds_bytes(int wfmt, int stage, int64_t N, int64_t K, int64_t E, int64_t R);
+
 // Load-time relayout into the tiled layout (see prepack.hip).
 int64_t tiled_steps(int64_t row_bytes);
 int64_t tiled_scale_steps(int64_t groups);

@@ -110,9 +110,9 @@ __global__ __launch_bounds__(T) void moe_align_kernel(
   __syncthreads();
 
   // 2. exclusive scans of blocks and rows per expert (each thread owns a run of experts)
+  const int per = int(cdiv(E, kAlignThreads));
+  const int e0 = min(E, tid * per), e1 = min(E, e0 + per);
   {
-    const int per = int(cdiv(E, kAlignThreads));
-    const int e0 = min(E, tid * per), e1 = min(E, e0 + per);
     int nb = 0, nr = 0;
     for (int e = e0; e < e1; ++e) {
       nb += (cnt[e] + block_m - 1) / block_m;
@@ -156,8 +156,45 @@ __global__ __launch_bounds__(T) void moe_align_kernel(
   const int rows_total = row_start[E];
   if (tid == 0) *num_blocks = nblocks;
 
-  // 3. block table and class lists
-  for (int e = tid; e < E; e += kAlignThreads) {
+  // 3. block table and class lists.  A class list holds its blocks in expert order (a scan of
+  // each thread's per-class block counts gives its run's first position in every list), so the
+  // blocks of one expert sit side by side for the tile kernels.
+  int pos[8];
+  if (pol.n_classes > 0) {
+    int my[8];
+#pragma unroll
+    for (int c = 0; c < 8; ++c) my[c] = 0;
+    for (int e = e0; e < e1; ++e)
+      for (int b = 0; b * block_m < cnt[e]; ++b) {
+        const int c = pick_class(pol, min(block_m, cnt[e] - b * block_m));
+#pragma unroll
+        for (int k = 0; k < 8; ++k) my[k] += (k == c) ? 1 : 0;
+      }
+    __shared__ int32_t wsum_c[kAlignWaves][8];
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      int sc = my[c];
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const int t = __shfl_up(sc, o, 64);
+        if (lane >= o) sc += t;
+      }
+      pos[c] = sc - my[c];  // exclusive, within the wave
+      if (lane == 63) wsum_c[wave][c] = sc;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      int base = 0, total = 0;
+      for (int w = 0; w < kAlignWaves; ++w) {
+        base += w < wave ? wsum_c[w][c] : 0;
+        total += wsum_c[w][c];
+      }
+      pos[c] += base;
+      if (tid == 0) cls_cnt[c] = total;
+    }
+  }
+  for (int e = e0; e < e1; ++e) {
     const int c_e = cnt[e];
     for (int b = 0; b * block_m < c_e; ++b) {
       const int mb = blk_start[e] + b;
@@ -166,8 +203,11 @@ __global__ __launch_bounds__(T) void moe_align_kernel(
       offsets[mb] = row_start[e] + b * block_m;
       if (pol.n_classes > 0) {
         const int c = pick_class(pol, m_size);
-        const int pos = atomicAdd(&cls_cnt[c], 1);
-        *reinterpret_cast<int4*>(class_lists + (int64_t(c) * list_stride + pos) * 4) =
+        int p = 0;
+#pragma unroll
+        for (int k = 0; k < 8; ++k)
+          if (k == c) p = pos[k]++;
+        *reinterpret_cast<int4*>(class_lists + (int64_t(c) * list_stride + p) * 4) =
             make_int4(mb, e, row_start[e] + b * block_m, m_size);
       }
     }

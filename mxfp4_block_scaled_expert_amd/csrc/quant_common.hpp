@@ -32,20 +32,21 @@ __device__ __forceinline__ float quant8_e4m3(const uint4 raw, float group_amax, 
   return s;
 }
 
-// SiLU-and-mul of 8 gate / up bf16 pairs ("vLLM PR 50949 review", implementation item 2:
-// the activation between the two stages): bf16(silu(g) * u), silu(g) = g / (1 + e^-g), in
-// fp32.  Shared by the standalone SiLU-and-mul kernel and the stage-2 activation staging of the
-// tiny-block kernel, so both produce the same bits.
+// SiLU-and-mul ("vLLM PR 50949 review", implementation item 2: the activation between the two
+// stages): silu(g) * u with silu(g) = g / (1 + e^-g), in fp32, of a gate / up pair that has
+// already been rounded to bf16; the caller rounds the result to bf16.  The standalone
+// SiLU-and-mul kernel, the stage-2 activation staging of the tiny-block kernel and the stage-1
+// epilogue of the expert-streaming kernel all evaluate this one expression, so they produce
+// the same bits.
+__device__ __forceinline__ float silu_mul_f32(float g, float u) { return g / (1.0f + __expf(-g)) * u; }
+
+// Eight gate / up bf16 pairs -> eight bf16.
 __device__ __forceinline__ uint4 silu_mul8(const uint4 g, const uint4 u) {
   const uint32_t gw[4] = {g.x, g.y, g.z, g.w}, uw[4] = {u.x, u.y, u.z, u.w};
   uint32_t hw[4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const float g0 = bf16lo(gw[i]), g1 = bf16hi(gw[i]);
-    const float h0 = g0 / (1.0f + __expf(-g0)) * bf16lo(uw[i]);
-    const float h1 = g1 / (1.0f + __expf(-g1)) * bf16hi(uw[i]);
-    hw[i] = pack_bf16x2(h0, h1);
-  }
+  for (int i = 0; i < 4; ++i)
+    hw[i] = pack_bf16x2(silu_mul_f32(bf16lo(gw[i]), bf16lo(uw[i])), silu_mul_f32(bf16hi(gw[i]), bf16hi(uw[i])));
   return make_uint4(hw[0], hw[1], hw[2], hw[3]);
 }
 
