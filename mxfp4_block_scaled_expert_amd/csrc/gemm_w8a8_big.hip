@@ -27,10 +27,11 @@
 //    per wave per K block, staged in LDS for all K blocks up front);
 //  * the products of a K block run as a software pipeline (the MFMA of product
 //    t + 2 is issued before product t is promoted);
-//  * dense tiles are rastered so that the tiles resident on one XCD (the
-//    dispatcher deals workgroups round-robin over the 8 XCDs) share operands in
-//    that XCD's L2; routed tiles run block-fastest, so the blocks of one expert
-//    (adjacent in the work list) share its weight tiles.
+//  * tiles are rastered so that the tiles resident on one XCD (the dispatcher
+//    deals workgroups round-robin over the 8 XCDs) share operands in that XCD's
+//    L2: bands of 4 row tiles (dense) or of 3 work-list entries (routed, where an
+//    expert's blocks are adjacent; bands dealt round-robin over the XCDs) run all
+//    their column tiles together.
 #include <type_traits>
 
 #include "lds_dma.hpp"
@@ -58,6 +59,11 @@ struct BigCfg {
   static_assert(WM * WN == NW && TI >= 2 && A_DMA >= 1 && B_DMA >= 1 && SA_WAVES <= NW, "tile shape");
   static_assert(BN % 128 == 0 || BN == 64, "a wave's 64 columns sit inside one 128-wide weight-scale block");
 };
+
+// Work-list entries per band of the routed raster (1, 2, 3, 4 and 8 measured on the DeepSeek
+// prefill shapes, 512 and 4096 tokens, uniform and Zipf routing: 3 fastest at 4096 tokens by
+// ~10 % over block-fastest order without XCD bands, within a few % of the best elsewhere).
+constexpr int64_t kRoutedBand = 3;
 
 __device__ __forceinline__ int swz(int row) { return (row & 7) ^ ((row >> 3) & 1); }
 
@@ -113,12 +119,23 @@ __global__ __launch_bounds__((BigCfg<BM, BN, NW, NS>::THREADS)) void gemm_w8a8_b
     tile = band * gm + in_band % band_rows;
     nt = in_band / band_rows;
   } else {
-    // routed: block fastest, so the blocks running together read the same weight columns, and
-    // the blocks of one heavily routed expert (adjacent in the work list) share each weight
-    // tile through the caches instead of each streaming the whole expert.  (Rastering bands of
-    // entries per XCD, as for dense tiles, measured slower on the skewed prefill routing.)
-    nt = blockIdx.x / grid_blocks;
-    tile = blockIdx.x - nt * grid_blocks;
+    // routed: bands of kRoutedBand consecutive work-list entries run all their column tiles
+    // on one XCD (entries fastest), so a band's activation rows are shared across its column
+    // tiles and each weight tile across the band's blocks of one expert (an expert's blocks are
+    // adjacent in the list) in that XCD's L2; the bands are dealt round-robin over the XCDs, so
+    // every XCD gets a mix of long and short blocks.  The live entry count is read first; the
+    // grid covers the list's capacity.
+    const int64_t count = *a.rt.work_count;
+    const int64_t n_bands = cdiv(count, kRoutedBand);
+    const int64_t band_tiles = kRoutedBand * n_tiles;
+    const int64_t x = blockIdx.x % 8, slot = blockIdx.x / 8;
+    const int64_t band = (slot / band_tiles) * 8 + x;
+    const int64_t in_band = slot % band_tiles;
+    if (band >= n_bands) return;
+    const int64_t band_rows = min<int64_t>(kRoutedBand, count - band * kRoutedBand);
+    if (in_band >= band_rows * n_tiles) return;
+    tile = band * kRoutedBand + in_band % band_rows;
+    nt = in_band / band_rows;
   }
   const int64_t n0 = nt * BN;
   if (n0 >= a.N) return;
@@ -388,8 +405,9 @@ __global__ __launch_bounds__((BigCfg<BM, BN, NW, NS>::THREADS)) void gemm_w8a8_b
 template <int BM, int BN, int NW, int NS, int MODE, bool TL>
 static void launch_big_t(const GemmArgs& a, bool out_f32, int64_t grid_blocks, hipStream_t st) {
   const int64_t n_tiles = cdiv(a.N, int64_t(BN));
-  int64_t nwg = grid_blocks * n_tiles;
-  if (MODE == ROWS_DENSE) nwg = cdiv(nwg, 8) * 8;  // whole rounds over the 8 XCDs
+  // whole rounds over the 8 XCDs; routed: every XCD's share of bands at full width
+  const int64_t nwg = MODE == ROWS_DENSE ? cdiv(grid_blocks * n_tiles, 8) * 8
+                                         : 8 * cdiv(cdiv(grid_blocks, kRoutedBand), 8) * kRoutedBand * n_tiles;
   const dim3 grid(static_cast<unsigned>(nwg)), block(BigCfg<BM, BN, NW, NS>::THREADS);
   const bool bias = a.bias != nullptr;
 #define MXQ_BIG_GO(OF, HB)                                                                                     \
