@@ -316,6 +316,9 @@ mxq_status run_moe(const void* x, int64_t M, int64_t H, int64_t I, int32_t E, in
     GemmArgs& g = stage == 0 ? g1 : g2;
     const int mode = stage == 0 ? ROWS_GATHER_TOK : ROWS_COMPACT_IN;
     const bool out_f32 = stage == 1;
+    // bf16 activations: the 16/32/64/128-row tile classes go out together in one grouped launch
+    GemmArgs grp[4] = {g, g, g, g};
+    int64_t grp_ub[4] = {0, 0, 0, 0};
     for (int c = 0; c < kNumClasses; ++c) {
       const int64_t ub = class_bound(c, R, E, mbk, pol);
       if (ub <= 0) continue;
@@ -336,9 +339,14 @@ mxq_status run_moe(const void* x, int64_t M, int64_t H, int64_t I, int32_t E, in
         launch_gemm_w8a8_big(g, mode, 1, out_f32, ub, st);
       else if (act_quant)
         launch_gemm_w8a8(g, mode, tile, out_f32, ub, st);
-      else
+      else if (c == 0)
         launch_gemm_w16(g, wfmt_w16, mode, tile, out_f32, ub, st);
+      else {
+        grp[3 - tile] = g;  // tile 3 (16 rows) .. tile 0 (128 rows)
+        grp_ub[3 - tile] = ub;
+      }
     }
+    if (!act_quant) launch_gemm_w16_grouped(grp, grp_ub, wfmt_w16, mode, out_f32, st);
   }
   launch_combine(w.y, wts, ids, E, M, topk, H, static_cast<uint16_t*>(out), st);
   return launch_status();

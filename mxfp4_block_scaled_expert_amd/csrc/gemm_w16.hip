@@ -18,6 +18,8 @@
 // Routed weights and MX scales may come in the tiled layout of prepack.hip
 // (TILED): each weight chunk is then read from one contiguous 2 KB tile, and
 // the K tail is already zero in memory.
+#include <algorithm>
+
 #include "tile_rows.hpp"
 
 namespace mxq {
@@ -30,8 +32,15 @@ struct W16Layout {
   static constexpr int chunks = row_bytes / 16;  // 16-byte chunks per row
 };
 
+// LDS of one tile: A [BM][A_LROW] | W [BN][lds_row] | MX scales [BN]
+template <int BM, int BN, int WFMT>
+__host__ __device__ constexpr size_t w16_lds_bytes() {
+  return size_t(BM) * (256 + 16) + size_t(BN) * W16Layout<WFMT>::lds_row + (WFMT == W_E2M1_MX ? 4 * BN : 16);
+}
+
+// One BM x BN output tile; `bid` is the tile's index in its launch, `lds` its share of LDS.
 template <int BM, int BN, int WAVES_M, int MODE, int WFMT, bool OUT_F32, bool HAS_BIAS, bool TILED>
-__global__ __launch_bounds__(256) void gemm_w16_kernel(GemmArgs a, int64_t grid_blocks) {
+__device__ __forceinline__ void w16_tile(const GemmArgs& a, int64_t grid_blocks, int64_t bid, uint8_t* lds) {
   constexpr int WAVES_N = 4 / WAVES_M;
   constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
   constexpr int TM = WM / 16, TN = WN / 16;
@@ -42,16 +51,16 @@ __global__ __launch_bounds__(256) void gemm_w16_kernel(GemmArgs a, int64_t grid_
   constexpr int B_IT = (BN * L::chunks + 255) / 256;
   constexpr bool MX = WFMT == W_E2M1_MX;
 
-  __shared__ __align__(16) uint8_t sA[BM * A_LROW];
-  __shared__ __align__(16) uint8_t sB[BN * L::lds_row];
-  __shared__ uint32_t sBs[MX ? BN : 1];
+  uint8_t* sA = lds;
+  uint8_t* sB = lds + BM * A_LROW;
+  uint32_t* sBs = reinterpret_cast<uint32_t*>(sB + BN * L::lds_row);
   __shared__ int64_t sArow[BM];
   __shared__ int64_t sOrow[BM];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / WAVES_N, wn = wave % WAVES_N;
-  const int64_t tile = blockIdx.x % grid_blocks;
-  const int64_t nt = blockIdx.x / grid_blocks;
+  const int64_t tile = bid % grid_blocks;
+  const int64_t nt = bid / grid_blocks;
   const int64_t n0 = nt * BN;
   if (n0 >= a.N) return;
 
@@ -252,13 +261,43 @@ __global__ __launch_bounds__(256) void gemm_w16_kernel(GemmArgs a, int64_t grid_
   }  // m sub-tiles
 }
 
+template <int BM, int BN, int WAVES_M, int MODE, int WFMT, bool OUT_F32, bool HAS_BIAS, bool TILED>
+__global__ __launch_bounds__(256) void gemm_w16_kernel(GemmArgs a, int64_t grid_blocks) {
+  extern __shared__ __align__(16) uint8_t w16_lds[];
+  w16_tile<BM, BN, WAVES_M, MODE, WFMT, OUT_F32, HAS_BIAS, TILED>(a, grid_blocks, blockIdx.x, w16_lds);
+}
+
+// Routed tile classes 16 / 32 / 64 / 128 rows in one launch: workgroups [off[c], off[c + 1])
+// run tiles of class c over its own work list, so the classes of a stage run side by side
+// instead of one launch after another (small batches leave most of the GPU idle in each).
+struct W16Group {
+  GemmArgs a[4];    // per class: the stage's arguments with that class's work list
+  int64_t gb[4];    // per class: work-list capacity
+  int64_t off[5];   // first workgroup of each class; off[4] = grid size
+};
+
+template <int MODE, int WFMT, bool OUT_F32, bool HAS_BIAS, bool TILED>
+__global__ __launch_bounds__(256) void gemm_w16_grouped_kernel(W16Group g) {
+  extern __shared__ __align__(16) uint8_t w16_lds[];
+  const int64_t b = blockIdx.x;
+  if (b < g.off[1])
+    w16_tile<16, 128, 1, MODE, WFMT, OUT_F32, HAS_BIAS, TILED>(g.a[0], g.gb[0], b - g.off[0], w16_lds);
+  else if (b < g.off[2])
+    w16_tile<32, 128, 1, MODE, WFMT, OUT_F32, HAS_BIAS, TILED>(g.a[1], g.gb[1], b - g.off[1], w16_lds);
+  else if (b < g.off[3])
+    w16_tile<64, 128, 2, MODE, WFMT, OUT_F32, HAS_BIAS, TILED>(g.a[2], g.gb[2], b - g.off[2], w16_lds);
+  else
+    w16_tile<128, 128, 2, MODE, WFMT, OUT_F32, HAS_BIAS, TILED>(g.a[3], g.gb[3], b - g.off[3], w16_lds);
+}
+
 template <int BM, int BN, int WAVES_M, int MODE, int WFMT, bool TL>
 static void launch_w16_tl(const GemmArgs& a, bool out_f32, int64_t grid_blocks, hipStream_t st) {
   const int64_t n_tiles = cdiv(a.N, BN);
   const dim3 grid(unsigned(grid_blocks * n_tiles)), block(256);
   const bool bias = a.bias != nullptr;
+  const size_t lds = w16_lds_bytes<BM, BN, WFMT>();
 #define MXQ_W16_GO(OF, HB) \
-  hipLaunchKernelGGL((gemm_w16_kernel<BM, BN, WAVES_M, MODE, WFMT, OF, HB, TL>), grid, block, 0, st, a, grid_blocks)
+  hipLaunchKernelGGL((gemm_w16_kernel<BM, BN, WAVES_M, MODE, WFMT, OF, HB, TL>), grid, block, lds, st, a, grid_blocks)
   if (out_f32) { if (bias) MXQ_W16_GO(true, true); else MXQ_W16_GO(true, false); }
   else { if (bias) MXQ_W16_GO(false, true); else MXQ_W16_GO(false, false); }
 #undef MXQ_W16_GO
@@ -291,6 +330,51 @@ static void launch_w16_fmt(const GemmArgs& a, int wfmt, int tile, bool out_f32, 
     case W_E4M3_BLOCK: launch_w16_mode<MODE, W_E4M3_BLOCK>(a, tile, out_f32, gb, st); break;
     case W_E4M3_TENSOR: launch_w16_mode<MODE, W_E4M3_TENSOR>(a, tile, out_f32, gb, st); break;
     default: launch_w16_mode<MODE, W_E2M1_MX>(a, tile, out_f32, gb, st); break;
+  }
+}
+
+template <int MODE, int WFMT, bool TL>
+static void launch_w16_grouped_t(const W16Group& g, bool out_f32, size_t lds, hipStream_t st) {
+  const dim3 grid(unsigned(g.off[4])), block(256);
+  const bool bias = g.a[0].bias != nullptr;
+#define MXQ_W16G_GO(OF, HB) \
+  hipLaunchKernelGGL((gemm_w16_grouped_kernel<MODE, WFMT, OF, HB, TL>), grid, block, lds, st, g)
+  if (out_f32) { if (bias) MXQ_W16G_GO(true, true); else MXQ_W16G_GO(true, false); }
+  else { if (bias) MXQ_W16G_GO(false, true); else MXQ_W16G_GO(false, false); }
+#undef MXQ_W16G_GO
+}
+
+template <int MODE, int WFMT>
+static void launch_w16_grouped_m(const W16Group& g, bool out_f32, hipStream_t st) {
+  // LDS of the largest class that holds workgroups
+  size_t lds = 0;
+  const size_t per[4] = {w16_lds_bytes<16, 128, WFMT>(), w16_lds_bytes<32, 128, WFMT>(),
+                         w16_lds_bytes<64, 128, WFMT>(), w16_lds_bytes<128, 128, WFMT>()};
+  for (int c = 0; c < 4; ++c)
+    if (g.off[c + 1] > g.off[c]) lds = std::max(lds, per[c]);
+  if (g.a[0].w_tiled)
+    launch_w16_grouped_t<MODE, WFMT, true>(g, out_f32, lds, st);
+  else
+    launch_w16_grouped_t<MODE, WFMT, false>(g, out_f32, lds, st);
+}
+
+void launch_gemm_w16_grouped(const GemmArgs cls[4], const int64_t grid_blocks[4], int wfmt, int row_mode,
+                             bool out_f32, hipStream_t stream) {
+  W16Group g{};
+  g.off[0] = 0;
+  for (int c = 0; c < 4; ++c) {
+    g.a[c] = cls[c];
+    g.gb[c] = std::max<int64_t>(grid_blocks[c], 0);
+    g.off[c + 1] = g.off[c] + g.gb[c] * cdiv(cls[c].N, 128);
+  }
+  if (g.off[4] <= 0) return;
+  const bool mx = wfmt == W_E2M1_MX;
+  if (row_mode == ROWS_GATHER_TOK) {
+    if (mx) launch_w16_grouped_m<ROWS_GATHER_TOK, W_E2M1_MX>(g, out_f32, stream);
+    else launch_w16_grouped_m<ROWS_GATHER_TOK, W_E4M3_BLOCK>(g, out_f32, stream);
+  } else {
+    if (mx) launch_w16_grouped_m<ROWS_COMPACT_IN, W_E2M1_MX>(g, out_f32, stream);
+    else launch_w16_grouped_m<ROWS_COMPACT_IN, W_E4M3_BLOCK>(g, out_f32, stream);
   }
 }
 

@@ -81,6 +81,11 @@ int big_tile_rows(int shape);
 void launch_gemm_w16(const GemmArgs& a, int wfmt, int row_mode, int tile, bool out_f32, int64_t grid_blocks,
                      hipStream_t stream);
 
+// Routed W8A16 / W4A16 tile classes of 16, 32, 64 and 128 rows (cls[c]: the stage's arguments
+// with class c + 1's work list; grid_blocks[c]: its capacity, 0 for none) in one launch.
+void launch_gemm_w16_grouped(const GemmArgs cls[4], const int64_t grid_blocks[4], int wfmt, int row_mode,
+                             bool out_f32, hipStream_t stream);
+
 // Wavefront-reduction GEMV for routed blocks of at most 4 rows.
 // a_e4m3: activations are e4m3 + 1x128 scales (W8A8), else bf16.
 void launch_gemv(const GemmArgs& a, int wfmt, bool a_e4m3, int row_mode, bool out_f32, int64_t grid_blocks,
