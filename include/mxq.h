@@ -235,9 +235,9 @@ mxq_status mxq_moe_prepack_scales(const void* s, int64_t E, int64_t N, int64_t g
  *        that group the routed rows by expert themselves (no sort and no block tables;
  *        the SiLU-and-mul ends stage 1) -- same arithmetic, bit-identical outputs.
  *        Otherwise, for W8A8 with K <= 16384 on
- *        both stages, the tiny bound is cut to the rows the MFMA tiny kernel stages per
- *        pass and the 16-, 32- and 64-row classes fold into the 128-row class (its
- *        128 x 256 tile streams the weights better even for short blocks).
+ *        both stages, every smaller class (the tiny one too, with the MFMA tiny kernel)
+ *        folds into the 128-row class: its 128 x 256 tile streams the weights better even
+ *        for short blocks, and no launch runs a handful of blocks.
  *   tiny_kernel: the tiny-block kernel -- MXQ_TINY_MFMA (default: weights streamed into
  *        registers, K reduced by MFMAs, up to 8 rows per pass) or MXQ_TINY_GEMV
  *        (vector-ALU dot products with a wavefront reduction, 4 rows per pass; plain

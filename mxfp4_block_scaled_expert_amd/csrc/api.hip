@@ -125,14 +125,14 @@ int64_t class_bound(int c, int64_t R, int32_t E, int64_t max_blocks, const Class
 // repeated ids, still lands in the largest launched class).
 //
 // `big_tile`: the stage GEMMs have the 128 x 256 direct-to-LDS W8A8 tile (W8A8, K <= 16384).
-// Measured on the prefill shapes (E = 256, 4096 tokens), that tile streams an expert's weights
-// better than the 16-64-row tiles even for short blocks, and each extra class launch leaves the
-// GPU partly idle while its few blocks run; so at larger token counts the classes between the
-// tiny one and the 128-row one are folded into the 128-row one, and the tiny class is cut to
-// the rows its kernel stages in one pass (`pass_rows`: a taller block would stream its
-// expert's weights once per pass).  With bf16 activations the next classes have no such tile,
-// and taking a few passes in the tiny kernel measured faster.
-ClassPolicy make_policy(int64_t M, int64_t R, int32_t E, int pass_rows, bool big_tile) {
+// Measured on the prefill shapes (E = 256, 512 and 4096 tokens), that tile streams an expert's
+// weights better than the 16-64-row tiles even for short blocks, and each extra class launch
+// leaves the GPU partly idle while its few blocks run; so at larger token counts every class
+// below the 128-row one is folded into it -- with the MFMA tiny kernel selected, the tiny class
+// too (the blocks of at most a few rows then cost no separate launch: measured equal at 512
+// tokens and 4-5 % faster at 4096 with uniform routing).  With bf16 activations the next
+// classes have no such tile, and taking a few passes in the tiny kernel measured faster.
+ClassPolicy make_policy(int64_t M, int64_t R, int32_t E, bool big_tile) {
   std::lock_guard<std::mutex> lk(g_dispatch_mu);
   ClassPolicy pol{};
   pol.n_classes = kNumClasses;
@@ -145,7 +145,7 @@ ClassPolicy make_policy(int64_t M, int64_t R, int32_t E, int pass_rows, bool big
   if (g_tiny_max_rows > 0 && M <= 2 * int64_t(g_tiny_max_rows)) {
     pol.bound[0] = std::max<int>(pol.bound[0], int(M));
   } else if (big_tile) {
-    if (pass_rows > 0 && g_tiny_kernel == MXQ_TINY_MFMA) pol.bound[0] = std::min<int>(pol.bound[0], pass_rows);
+    if (g_tiny_kernel == MXQ_TINY_MFMA) pol.bound[0] = 0;
     for (int c = 1; c < kNumClasses - 1; ++c) pol.bound[c] = pol.bound[0];
   }
   pol.n_live = kNumClasses;
@@ -178,11 +178,7 @@ mxq_status run_moe(const void* x, int64_t M, int64_t H, int64_t I, int32_t E, in
   const int64_t mbk = mxq_moe_max_blocks(M, topk, E, kMoeBlockM);
   MoeWorkspace w = carve_moe(ws, M, H, I, E, topk, act_quant);
   if (!ws || ws_bytes < w.bytes) return MXQ_ERR_WORKSPACE;
-  const int wfmt_tiny = wfmt == W_E2M1_MX ? W_E2M1_MX : W_E4M3_BLOCK;
-  const ClassPolicy pol = make_policy(M, R, E,
-                                      std::min(skinny_pass_rows(wfmt_tiny, act_quant, H),
-                                               skinny_pass_rows(wfmt_tiny, act_quant, I)),
-                                      act_quant && H <= 16384 && I <= 16384);
+  const ClassPolicy pol = make_policy(M, R, E, act_quant && H <= 16384 && I <= 16384);
   int tiny;
   {
     std::lock_guard<std::mutex> lk(g_dispatch_mu);

@@ -97,8 +97,6 @@ void launch_skinny(const GemmArgs& a, int wfmt, bool a_e4m3, int row_mode, bool 
                    hipStream_t stream);
 // Dynamic LDS the weight-streaming kernel takes for reduction length K.
 size_t skinny_lds_bytes(int wfmt, bool a_e4m3, int64_t K);
-// activation rows the tiny-block kernel stages per pass (a taller block re-reads its weights)
-int skinny_pass_rows(int wfmt, bool a_e4m3, int64_t K);
 
 // Persistent expert-streaming kernel for routings made only of tiny expert blocks (bf16
 // activations, e2m1 or e4m3 weights): each workgroup groups the routed rows by expert itself

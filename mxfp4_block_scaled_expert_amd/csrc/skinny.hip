@@ -345,12 +345,6 @@ static int skinny_rows_t(int64_t K, int G) {
   return skinny_lds_t<WFMT, AE>(K, 8, G) <= kSkLdsCap ? 8 : 4;
 }
 
-int skinny_pass_rows(int wfmt, bool a_e4m3, int64_t K) {
-  if (wfmt == W_E2M1_MX) return skinny_rows_t<W_E2M1_MX, false>(K, 2);
-  if (a_e4m3) return skinny_rows_t<W_E4M3_BLOCK, true>(K, 2);
-  return skinny_rows_t<W_E4M3_BLOCK, false>(K, 2);
-}
-
 size_t skinny_lds_bytes(int wfmt, bool a_e4m3, int64_t K) {
   // the larger of the two group counts (the weight-scale table grows with G)
   if (wfmt == W_E2M1_MX) return skinny_lds_t<W_E2M1_MX, false>(K, skinny_rows_t<W_E2M1_MX, false>(K, 2), 2);
