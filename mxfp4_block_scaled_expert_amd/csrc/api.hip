@@ -471,7 +471,7 @@ mxq_status mxq_block_fp8_linear(const void* A, int32_t a_dtype, const float* a_s
   g.M = M;
   g.N = N;
   g.K = K;
-  if (block_n == 128 && M > 128 && K <= 16384 && int64_t(M) * lqa < (int64_t(1) << 32) &&
+  if ((block_n == 128 || block_n == 1) && M > 128 && K <= 16384 && int64_t(M) * lqa < (int64_t(1) << 32) &&
       N * K < (int64_t(1) << 32)) {
     launch_gemm_w8a8_big(g, ROWS_DENSE, kDenseBigShape, false, cdiv(M, int64_t(big_tile_rows(kDenseBigShape))), st);
   } else {

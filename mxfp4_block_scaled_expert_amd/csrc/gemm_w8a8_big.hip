@@ -87,9 +87,13 @@ __device__ __forceinline__ i32x8 read_frag_tiled(const uint8_t* tile, int g, int
 
 }  // namespace
 
-template <int BM, int BN, int NW, int NS, int MODE, bool OUT_F32, bool HAS_BIAS, bool TILED>
+// SWCOL (dense, block_n = 1: one weight scale per output column and 128-wide K block): each K
+// block's column scales travel with its operands into LDS, and each product is promoted with
+// sa[row] * sw[col] -- the promotion of the smaller tiles, element for element.
+template <int BM, int BN, int NW, int NS, int MODE, bool OUT_F32, bool HAS_BIAS, bool TILED, bool SWCOL = false>
 __global__ __launch_bounds__((BigCfg<BM, BN, NW, NS>::THREADS)) void gemm_w8a8_big_kernel(GemmArgs a, int64_t grid_blocks,
                                                                                  int64_t n_tiles) {
+  static_assert(!SWCOL || MODE == ROWS_DENSE, "per-column weight scales: dense GEMM only");
   using C = BigCfg<BM, BN, NW, NS>;
   constexpr int S = C::STAGES, TI = C::TI, NT = 4 * TI, WROWS = C::WROWS;
   __shared__ __align__(1024) uint8_t sOps[S * C::STAGE_BYTES];  // stage s: A [BM][128] then W [BN][128]
@@ -98,6 +102,7 @@ __global__ __launch_bounds__((BigCfg<BM, BN, NW, NS>::THREADS)) void gemm_w8a8_b
   __shared__ int64_t sOrow[BM];
   __shared__ float sSW[2][kMaxKB];  // weight scales of the tile's (up to two) 128-wide column blocks
   __shared__ __align__(256) float sFill[NW * 64];  // landing area of the filler scale DMAs (never read)
+  __shared__ __align__(16) float sSWc[SWCOL ? S : 1][SWCOL ? BN : 4];  // per-column weight scales
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / C::WN, wn = wave % C::WN;
@@ -208,8 +213,15 @@ __global__ __launch_bounds__((BigCfg<BM, BN, NW, NS>::THREADS)) void gemm_w8a8_b
       for (int b = 0; b < C::B_DMA; ++b) lds_dma16(Wk + ob[b], lb + b * 1024);
       const uint32_t ls = sa_wave ? lds_addr(&sS[s][0]) + wave * 256 : lds_addr(sFill) + wave * 256;
       lds_dma4(gs + kb, __builtin_amdgcn_readfirstlane(ls));
+      if constexpr (SWCOL) {
+        // waves < BN / 64 fetch 64 column scales each; the others a filler dword
+        const bool sw_wave = wave < BN / 64;
+        const int64_t col = min<int64_t>(n0 + (wave % (BN / 64)) * 64 + lane, a.N - 1);
+        const uint32_t lw = sw_wave ? lds_addr(&sSWc[s][0]) + wave * 256 : lds_addr(sFill) + wave * 256;
+        lds_dma4(swb + col * a.ws_s0 + kb * a.ws_s1, __builtin_amdgcn_readfirstlane(lw));
+      }
     };
-    constexpr int kIssueOps = C::A_DMA + C::B_DMA + 1;
+    constexpr int kIssueOps = C::A_DMA + C::B_DMA + 1 + (SWCOL ? 1 : 0);
 
     f32x4 acc[TI][4];
 #pragma unroll
@@ -238,7 +250,12 @@ __global__ __launch_bounds__((BigCfg<BM, BN, NW, NS>::THREADS)) void gemm_w8a8_b
 #pragma unroll
       for (int j = 0; j < 4; ++j)
         wf[j] = TILED ? read_frag_tiled(cB, wn * 4 + j, lane) : read_frag(cB, wn * 64 + 16 * j + l16, q);
-      const float sw = sSW[sw_blk][kb];
+      const float sw = SWCOL ? 1.f : sSW[sw_blk][kb];
+      f32x4 csw[4];  // SWCOL: the scales of this lane's 4 columns in each of the wave's 4 blocks
+      if constexpr (SWCOL) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) csw[j] = *reinterpret_cast<const f32x4*>(&sSWc[s][wn * 64 + 16 * j + 4 * q]);
+      }
       const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
       const int mrow = wm * WROWS;
       i32x8 afr[2];  // activation fragments of rows i (slot i & 1)
@@ -265,7 +282,8 @@ __global__ __launch_bounds__((BigCfg<BM, BN, NW, NS>::THREADS)) void gemm_w8a8_b
         __builtin_amdgcn_sched_barrier(0);
         const int i = u >> 2, j = u & 3;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) acc[i][j][r] = fmaf(pb[u % NB][r], cr[i & 1], acc[i][j][r]);
+        for (int r = 0; r < 4; ++r)
+          acc[i][j][r] = fmaf(pb[u % NB][r], SWCOL ? cr[i & 1] * csw[j][r] : cr[i & 1], acc[i][j][r]);
         if (j == 3 && i + 2 < TIE) cr[i & 1] = cS[mrow + 16 * (i + 2) + l16] * sw;
         __builtin_amdgcn_sched_barrier(0);
       }
@@ -295,7 +313,7 @@ __global__ __launch_bounds__((BigCfg<BM, BN, NW, NS>::THREADS)) void gemm_w8a8_b
     // next DMA overwrites), issues the DMA S - 1 blocks ahead, and computes.
     if (S == 2) {
       issue(0, 0);
-      if (m_base == 0) stage_weight_scales();
+      if (!SWCOL && m_base == 0) stage_weight_scales();
       for (int kb = 0; kb < KB; ++kb) {
         wait_vmcnt<0>();
         __syncthreads();
@@ -306,7 +324,7 @@ __global__ __launch_bounds__((BigCfg<BM, BN, NW, NS>::THREADS)) void gemm_w8a8_b
       // ops issued after DMA(kb) at the top of iteration kb: DMA(kb+1) when it exists
       issue(0, 0);
       if (KB > 1) issue(1, 1);
-      if (m_base == 0) stage_weight_scales();
+      if (!SWCOL && m_base == 0) stage_weight_scales();
       int s = 0;
       for (int kb = 0; kb < KB; ++kb) {
         if (kb + 1 < KB)
@@ -402,7 +420,7 @@ __global__ __launch_bounds__((BigCfg<BM, BN, NW, NS>::THREADS)) void gemm_w8a8_b
   }
 }
 
-template <int BM, int BN, int NW, int NS, int MODE, bool TL>
+template <int BM, int BN, int NW, int NS, int MODE, bool TL, bool SWC = false>
 static void launch_big_t(const GemmArgs& a, bool out_f32, int64_t grid_blocks, hipStream_t st) {
   const int64_t n_tiles = cdiv(a.N, int64_t(BN));
   // whole rounds over the 8 XCDs; routed: every XCD's share of bands at full width
@@ -411,7 +429,7 @@ static void launch_big_t(const GemmArgs& a, bool out_f32, int64_t grid_blocks, h
   const dim3 grid(static_cast<unsigned>(nwg)), block(BigCfg<BM, BN, NW, NS>::THREADS);
   const bool bias = a.bias != nullptr;
 #define MXQ_BIG_GO(OF, HB)                                                                                     \
-  hipLaunchKernelGGL((gemm_w8a8_big_kernel<BM, BN, NW, NS, MODE, OF, HB, TL>), grid, block, 0, st, a, grid_blocks, \
+  hipLaunchKernelGGL((gemm_w8a8_big_kernel<BM, BN, NW, NS, MODE, OF, HB, TL, SWC>), grid, block, 0, st, a, grid_blocks, \
                      n_tiles)
   if (out_f32) { if (bias) MXQ_BIG_GO(true, true); else MXQ_BIG_GO(true, false); }
   else { if (bias) MXQ_BIG_GO(false, true); else MXQ_BIG_GO(false, false); }
@@ -426,6 +444,16 @@ void launch_gemm_w8a8_big(const GemmArgs& a, int row_mode, int shape, bool out_f
                           hipStream_t st) {
   if (grid_blocks <= 0 || a.N <= 0) return;
   if (row_mode == ROWS_DENSE) {
+    // block_n == 1: per-column weight scales
+    if (a.block_n == 1) {
+      switch (shape) {
+        case 0: launch_big_t<256, 256, 8, 2, ROWS_DENSE, false, true>(a, out_f32, grid_blocks, st); break;
+        case 2: launch_big_t<128, 128, 4, 2, ROWS_DENSE, false, true>(a, out_f32, grid_blocks, st); break;
+        case 3: launch_big_t<128, 128, 4, 3, ROWS_DENSE, false, true>(a, out_f32, grid_blocks, st); break;
+        default: launch_big_t<128, 256, 8, 3, ROWS_DENSE, false, true>(a, out_f32, grid_blocks, st); break;
+      }
+      return;
+    }
     switch (shape) {
       case 0: launch_big_t<256, 256, 8, 2, ROWS_DENSE, false>(a, out_f32, grid_blocks, st); break;
       case 2: launch_big_t<128, 128, 4, 2, ROWS_DENSE, false>(a, out_f32, grid_blocks, st); break;

@@ -70,7 +70,7 @@ void launch_quant_1x128(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, ui
 void launch_gemm_w8a8(const GemmArgs& a, int row_mode, int tile, bool out_f32, int64_t grid_blocks,
                       hipStream_t stream);
 
-// W8A8 with large direct-to-LDS tiles; 128x128 weight blocks only; K <= 16384; operand offsets
+// W8A8 with large direct-to-LDS tiles; 128x128 weight blocks (1x128 too for the dense GEMM); K <= 16384; operand offsets
 // below 4 GiB.  Dense shape: 0 = 256x256, 1 = 128x256, 2 = 128x128 tiles; routed modes use
 // 128x256 and read plain or tiled weights.  `grid_blocks` = row tiles (dense) or work-list capacity.
 void launch_gemm_w8a8_big(const GemmArgs& a, int row_mode, int shape, bool out_f32, int64_t grid_blocks,

@@ -86,12 +86,20 @@ def test_block_linear_page_recipe(M, block_n):
     assert torch.equal(out_t, out)
 
 
+@pytest.mark.parametrize("block_n", [128, 1])
 @pytest.mark.parametrize("M,N,K", [(200, 384, 512), (130, 200, 256), (64, 1152, 1024), (257, 640, 384)])
-def test_block_linear_ragged_tiles(M, N, K):
-    d = _block_case(M, N, K, 128, seed=M + N + K, bias_dtype=torch.float32)
-    out = ops.block_fp8_linear(d["x"], d["w"], [128, 128], d["sw"], bias=d["bias"])
+def test_block_linear_ragged_tiles(M, N, K, block_n):
+    """M > 128 takes the large direct-to-LDS tile, for 128x128 and (per-column scales) 1x128
+    weight blocks alike; the scale grid stored transposed gives the same bits."""
+    d = _block_case(M, N, K, block_n, seed=M + N + K + block_n, bias_dtype=torch.float32)
+    out = ops.block_fp8_linear(d["x"], d["w"], [block_n, 128], d["sw"], bias=d["bias"])
     torch.cuda.synchronize()
-    assert_bf16_close(bf16_bits(out), _oracle_block(d), what=f"block linear {M}x{N}x{K}")
+    assert_bf16_close(bf16_bits(out), _oracle_block(d), what=f"block linear {M}x{N}x{K} bn={block_n}")
+    sw_t = torch.empty_strided(d["sw"].shape, (1, d["sw"].shape[0]), dtype=torch.float32, device=gpu())
+    sw_t.copy_(d["sw"])
+    out_t = ops.block_fp8_linear(d["x"], d["w"], [block_n, 128], sw_t, bias=d["bias"])
+    torch.cuda.synchronize()
+    assert torch.equal(out_t, out)
 
 
 def test_block_linear_prequantised_3d_and_noncontiguous():
@@ -130,14 +138,17 @@ def test_block_linear_rejects_bad_block_sizes():
             ops.block_fp8_linear(d["x"], d["w"], bs, d["sw"])
 
 
-def test_block_linear_workload_sampled_rows():
+@pytest.mark.parametrize("block_n", [128, 1])
+def test_block_linear_workload_sampled_rows(block_n):
     M, K, N = 2048, 2048, 7168
-    d = _block_case(M, N, K, 128, seed=1002)
-    out = ops.block_fp8_linear(d["x"], d["w"], [128, 128], d["sw"])
+    d = _block_case(M, N, K, block_n, seed=1002)
+    out = ops.block_fp8_linear(d["x"], d["w"], [block_n, 128], d["sw"])
     torch.cuda.synchronize()
     rows = np.array([0, 1, 127, 128, 129, 1000, 1023, 1024, 2046, 2047])
-    want = OD.block_fp8_linear_bf16(bf16_bits(d["x"][rows]), u8(d["w"]), f32(d["sw"]), 128)
-    assert_bf16_close(bf16_bits(out[rows]), want, what="2048x2048x7168 sampled rows")
+    want = OD.block_fp8_linear_bf16(bf16_bits(d["x"][rows]), u8(d["w"]), f32(d["sw"]), block_n)
+    assert_bf16_close(bf16_bits(out[rows]), want, what=f"2048x2048x7168 sampled rows bn={block_n}")
+    if block_n != 128:
+        return
     # the quantised activations of the workload are bit-exact too
     q, s = ops.per_token_group_quant_fp8(d["x"])
     torch.cuda.synchronize()
