@@ -196,7 +196,7 @@ __global__ __launch_bounds__((BigCfg<BM, BN, NW, NS>::THREADS)) void gemm_w8a8_b
     // activation scales: waves < BM/64 fetch 64 rows each; the others fetch a filler dword
     // into sFill so that every wave issues the same number of loads per K block
     const bool sa_wave = wave < C::SA_WAVES;
-    const float* gs = a.sa + sArow[(wave % C::SA_WAVES) * 64 + lane] * a.lds;
+    const uint32_t os = uint32_t(sArow[(wave % C::SA_WAVES) * 64 + lane] * a.lds * 4);
 
     auto stageA = [&](int s) -> uint8_t* { return sOps + s * C::STAGE_BYTES; };
     auto stageB = [&](int s) -> uint8_t* { return sOps + s * C::STAGE_BYTES + BM * kKS; };
@@ -208,11 +208,11 @@ __global__ __launch_bounds__((BigCfg<BM, BN, NW, NS>::THREADS)) void gemm_w8a8_b
       const uint32_t la = __builtin_amdgcn_readfirstlane(lds_addr(stageA(s)) + wave * C::A_DMA * 1024);
       const uint32_t lb = __builtin_amdgcn_readfirstlane(lds_addr(stageB(s)) + wave * C::B_DMA * 1024);
 #pragma unroll
-      for (int b = 0; b < C::A_DMA; ++b) lds_dma16(Ak + oa[b], la + b * 1024);
+      for (int b = 0; b < C::A_DMA; ++b) lds_dma16(Ak, oa[b], la + b * 1024);
 #pragma unroll
-      for (int b = 0; b < C::B_DMA; ++b) lds_dma16(Wk + ob[b], lb + b * 1024);
+      for (int b = 0; b < C::B_DMA; ++b) lds_dma16(Wk, ob[b], lb + b * 1024);
       const uint32_t ls = sa_wave ? lds_addr(&sS[s][0]) + wave * 256 : lds_addr(sFill) + wave * 256;
-      lds_dma4(gs + kb, __builtin_amdgcn_readfirstlane(ls));
+      lds_dma4(a.sa + kb, os, __builtin_amdgcn_readfirstlane(ls));
       if constexpr (SWCOL) {
         // waves < BN / 64 fetch 64 column scales each; the others a filler dword
         const bool sw_wave = wave < BN / 64;
@@ -246,6 +246,12 @@ __global__ __launch_bounds__((BigCfg<BM, BN, NW, NS>::THREADS)) void gemm_w8a8_b
       const uint8_t* cB = stageB(s);
       const float* cS = sS[s];
       constexpr int DIST = 2, NB = DIST + 1;
+      const int mrow = wm * WROWS;
+      // the activation scales of all the wave's rows are read first, so that no wait for one
+      // of them also waits for the fragment reads issued after it
+      float cr[TI];  // combined scales of rows i
+#pragma unroll
+      for (int r = 0; r < TIE; ++r) cr[r] = cS[mrow + 16 * r + l16];
       i32x8 wf[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j)
@@ -257,15 +263,14 @@ __global__ __launch_bounds__((BigCfg<BM, BN, NW, NS>::THREADS)) void gemm_w8a8_b
         for (int j = 0; j < 4; ++j) csw[j] = *reinterpret_cast<const f32x4*>(&sSWc[s][wn * 64 + 16 * j + 4 * q]);
       }
       const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
-      const int mrow = wm * WROWS;
       i32x8 afr[2];  // activation fragments of rows i (slot i & 1)
-      float cr[2];   // combined scales of rows i
 #pragma unroll
       for (int r = 0; r < 2; ++r) {
         if (r >= TIE) break;
         afr[r] = read_frag(cA, mrow + 16 * r + l16, q);
-        cr[r] = cS[mrow + 16 * r + l16] * sw;
       }
+#pragma unroll
+      for (int r = 0; r < TIE; ++r) cr[r] *= sw;
       f32x4 pb[NB];
 #pragma unroll
       for (int u = 0; u < DIST; ++u) pb[u] = mfma_16x16x128_e4m3(wf[u & 3], afr[(u >> 2) & 1], zero);
@@ -283,8 +288,7 @@ __global__ __launch_bounds__((BigCfg<BM, BN, NW, NS>::THREADS)) void gemm_w8a8_b
         const int i = u >> 2, j = u & 3;
 #pragma unroll
         for (int r = 0; r < 4; ++r)
-          acc[i][j][r] = fmaf(pb[u % NB][r], SWCOL ? cr[i & 1] * csw[j][r] : cr[i & 1], acc[i][j][r]);
-        if (j == 3 && i + 2 < TIE) cr[i & 1] = cS[mrow + 16 * (i + 2) + l16] * sw;
+          acc[i][j][r] = fmaf(pb[u % NB][r], SWCOL ? cr[i] * csw[j][r] : cr[i], acc[i][j][r]);
         __builtin_amdgcn_sched_barrier(0);
       }
     };

@@ -28,6 +28,19 @@ __device__ __forceinline__ void lds_dma4(const void* g, uint32_t lds) {
                : "memory", "m0");
 }
 
+// The same copies addressed as a wave-uniform base (kept in SGPRs) plus a 32-bit per-lane byte
+// offset, so a loop that walks a matrix only moves the base.
+__device__ __forceinline__ void lds_dma16(const void* base, uint32_t off, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(base),
+               "s"(__builtin_amdgcn_readfirstlane(lds))
+               : "memory", "m0");
+}
+__device__ __forceinline__ void lds_dma4(const void* base, uint32_t off, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1" ::"v"(off), "s"(base),
+               "s"(__builtin_amdgcn_readfirstlane(lds))
+               : "memory", "m0");
+}
+
 // Wait until at most N vector memory operations of this wave are outstanding.
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
