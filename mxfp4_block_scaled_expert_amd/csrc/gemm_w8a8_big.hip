@@ -48,15 +48,24 @@ constexpr int kMaxKB = 128;  // K <= 16384 on this kernel
 template <int BM, int BN, int NW, int NS>
 struct BigCfg {
   static constexpr int THREADS = NW * 64;
+  static constexpr int NW_ = NW;
   static constexpr int WN = BN / 64, WM = NW / WN;
   static constexpr int WROWS = BM / WM;  // rows per wave
   static constexpr int TI = WROWS / 16;  // 16-row sub-tiles per wave
   static constexpr int STAGE_BYTES = (BM + BN) * kKS;
   static constexpr int STAGES = NS;  // LDS stages (2 or 3)
-  static constexpr int A_DMA = BM / 8 / NW;  // 1 KB activation DMAs per wave per K block
-  static constexpr int B_DMA = BN / 8 / NW;  // 1 KB weight DMAs per wave per K block
   static constexpr int SA_WAVES = BM / 64;   // waves fetching 64 activation scales each
-  static_assert(WM * WN == NW && TI >= 2 && A_DMA >= 1 && B_DMA >= 1 && SA_WAVES <= NW, "tile shape");
+  // Copying waves.  Three stages: every wave copies its share of the next blocks.  Two
+  // stages (one block of look-ahead): only the upper half of the waves copies (twice the
+  // pieces each).  Issuing copies holds a wave until the copy engine has queued them (the
+  // engine moves ~64 B per clock per CU, ~1000 clocks per 256x256 block); this way the lower
+  // wave of each SIMD starts its products right after the barrier instead of waiting there too.
+  static constexpr bool HALF = NS == 2;
+  static constexpr int COPY_WAVES = HALF ? NW / 2 : NW;
+  static constexpr int A_PIECES = BM / 8 / COPY_WAVES;  // 1 KB activation DMAs per copying wave
+  static constexpr int B_PIECES = BN / 8 / COPY_WAVES;  // 1 KB weight DMAs per copying wave
+  static_assert(WM * WN == NW && TI >= 2 && A_PIECES >= 1 && B_PIECES >= 1 && SA_WAVES <= COPY_WAVES, "tile shape");
+  static_assert(BN / 64 <= COPY_WAVES, "per-column scale fetch");
   static_assert(BN % 128 == 0 || BN == 64, "a wave's 64 columns sit inside one 128-wide weight-scale block");
 };
 
@@ -172,56 +181,64 @@ __global__ __launch_bounds__((BigCfg<BM, BN, NW, NS>::THREADS)) void gemm_w8a8_b
     __syncthreads();
 
     // ---- per-lane DMA sources (32-bit byte offsets: the host routes operands below 4 GiB here)
-    uint32_t oa[C::A_DMA], ob[C::B_DMA];
+    // cw: this wave's index among the copying waves (a wave that copies nothing computes
+    // valid but unused offsets)
+    const bool copier = !C::HALF || wave >= C::NW_ / 2;
+    const int cw = C::HALF ? max(wave - C::NW_ / 2, 0) : wave;
+    uint32_t oa[C::A_PIECES], ob[C::B_PIECES];
 #pragma unroll
-    for (int b = 0; b < C::A_DMA; ++b) {
-      const int row = (wave * C::A_DMA + b) * 8 + (lane >> 3);
+    for (int b = 0; b < C::A_PIECES; ++b) {
+      const int row = (cw * C::A_PIECES + b) * 8 + (lane >> 3);
       const int chunk = (lane & 7) ^ swz(row);
       oa[b] = uint32_t(sArow[row] * a.lda + chunk * 16);
     }
-#pragma unroll
-    for (int b = 0; b < C::B_DMA; ++b) {
-      const int d = wave * C::B_DMA + b;  // the tile's d-th 1 KB weight piece
+    // weight piece b of this wave's share: the tile's d-th 1 KB piece
+    auto w_offset = [&](int b) __attribute__((always_inline)) -> uint32_t {
+      const int d = cw * C::B_PIECES + b;
       if (TILED) {
         // piece d = half (d & 1) of the tile of 16-row group d / 2
         const int64_t g16 = min<int64_t>(n0 / 16 + (d >> 1), a.N / 16 - 1);
-        ob[b] = uint32_t(g16 * KB * 2048 + (d & 1) * 1024 + lane * 16);
-      } else {
-        const int row = d * 8 + (lane >> 3);
-        const int chunk = (lane & 7) ^ swz(row);
-        const int64_t n = min<int64_t>(n0 + row, a.N - 1);
-        ob[b] = uint32_t(n * a.ldw + chunk * 16);
+        return uint32_t(g16 * KB * 2048 + (d & 1) * 1024 + lane * 16);
       }
-    }
-    // activation scales: waves < BM/64 fetch 64 rows each; the others fetch a filler dword
-    // into sFill so that every wave issues the same number of loads per K block
-    const bool sa_wave = wave < C::SA_WAVES;
-    const uint32_t os = uint32_t(sArow[(wave % C::SA_WAVES) * 64 + lane] * a.lds * 4);
+      const int row = d * 8 + (lane >> 3);
+      const int chunk = (lane & 7) ^ swz(row);
+      const int64_t n = min<int64_t>(n0 + row, a.N - 1);
+      return uint32_t(n * a.ldw + chunk * 16);
+    };
+#pragma unroll
+    for (int b = 0; b < C::B_PIECES; ++b) ob[b] = w_offset(b);
+    // activation scales: copying waves cw < BM/64 fetch 64 rows each; the other ones fetch a
+    // filler dword into sFill so that every copying wave issues the same number of loads per
+    // K block
+    const bool sa_wave = cw < C::SA_WAVES;
+    const uint32_t os = uint32_t(sArow[(cw % C::SA_WAVES) * 64 + lane] * a.lds * 4);
 
     auto stageA = [&](int s) -> uint8_t* { return sOps + s * C::STAGE_BYTES; };
     auto stageB = [&](int s) -> uint8_t* { return sOps + s * C::STAGE_BYTES + BM * kKS; };
 
-    // one K block: A_DMA + B_DMA operand DMAs and one scale DMA per wave
+    // one K block: A_PIECES + B_PIECES operand DMAs and one scale DMA per copying wave (one
+    // more with per-column weight scales)
     auto issue = [&](int kb, int s) __attribute__((always_inline)) {
+      if (!copier) return;
       const uint8_t* Ak = A + kb * kKS;
       const uint8_t* Wk = Wb + kb * (TILED ? 2048 : kKS);
-      const uint32_t la = __builtin_amdgcn_readfirstlane(lds_addr(stageA(s)) + wave * C::A_DMA * 1024);
-      const uint32_t lb = __builtin_amdgcn_readfirstlane(lds_addr(stageB(s)) + wave * C::B_DMA * 1024);
+      const uint32_t la = __builtin_amdgcn_readfirstlane(lds_addr(stageA(s)) + cw * C::A_PIECES * 1024);
+      const uint32_t lb = __builtin_amdgcn_readfirstlane(lds_addr(stageB(s)) + cw * C::B_PIECES * 1024);
 #pragma unroll
-      for (int b = 0; b < C::A_DMA; ++b) lds_dma16(Ak, oa[b], la + b * 1024);
+      for (int b = 0; b < C::A_PIECES; ++b) lds_dma16(Ak, oa[b], la + b * 1024);
 #pragma unroll
-      for (int b = 0; b < C::B_DMA; ++b) lds_dma16(Wk, ob[b], lb + b * 1024);
-      const uint32_t ls = sa_wave ? lds_addr(&sS[s][0]) + wave * 256 : lds_addr(sFill) + wave * 256;
+      for (int b = 0; b < C::B_PIECES; ++b) lds_dma16(Wk, ob[b], lb + b * 1024);
+      const uint32_t ls = sa_wave ? lds_addr(&sS[s][0]) + cw * 256 : lds_addr(sFill) + wave * 256;
       lds_dma4(a.sa + kb, os, __builtin_amdgcn_readfirstlane(ls));
       if constexpr (SWCOL) {
-        // waves < BN / 64 fetch 64 column scales each; the others a filler dword
-        const bool sw_wave = wave < BN / 64;
-        const int64_t col = min<int64_t>(n0 + (wave % (BN / 64)) * 64 + lane, a.N - 1);
-        const uint32_t lw = sw_wave ? lds_addr(&sSWc[s][0]) + wave * 256 : lds_addr(sFill) + wave * 256;
+        // copying waves cw < BN / 64 fetch 64 column scales each; the others a filler dword
+        const bool sw_wave = cw < BN / 64;
+        const int64_t col = min<int64_t>(n0 + (cw % (BN / 64)) * 64 + lane, a.N - 1);
+        const uint32_t lw = sw_wave ? lds_addr(&sSWc[s][0]) + cw * 256 : lds_addr(sFill) + wave * 256;
         lds_dma4(swb + col * a.ws_s0 + kb * a.ws_s1, __builtin_amdgcn_readfirstlane(lw));
       }
     };
-    constexpr int kIssueOps = C::A_DMA + C::B_DMA + 1 + (SWCOL ? 1 : 0);
+    constexpr int kIssueOps = C::A_PIECES + C::B_PIECES + 1 + (SWCOL ? 1 : 0);  // per copying wave
 
     f32x4 acc[TI][4];
 #pragma unroll
