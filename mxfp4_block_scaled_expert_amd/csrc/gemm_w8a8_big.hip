@@ -55,13 +55,11 @@ struct BigCfg {
   static constexpr int STAGE_BYTES = (BM + BN) * kKS;
   static constexpr int STAGES = NS;  // LDS stages (2 or 3)
   static constexpr int SA_WAVES = BM / 64;   // waves fetching 64 activation scales each
-  // Copying waves.  Three stages: every wave copies its share of the next blocks.  Two
-  // stages (one block of look-ahead): only the upper half of the waves copies (twice the
-  // pieces each).  Issuing copies holds a wave until the copy engine has queued them (the
-  // engine moves ~64 B per clock per CU, ~1000 clocks per 256x256 block); this way the lower
-  // wave of each SIMD starts its products right after the barrier instead of waiting there too.
-  static constexpr bool HALF = NS == 2;
-  static constexpr int COPY_WAVES = HALF ? NW / 2 : NW;
+  // Copying waves: only the upper half of the waves copies (twice the pieces each).  Issuing
+  // copies holds a wave until the copy engine has queued them (it moves ~64 B per clock per
+  // CU, ~1000 clocks per 256x256 block); this way the lower wave of each SIMD starts its
+  // products right after the barrier instead of waiting there too.
+  static constexpr int COPY_WAVES = NW / 2;
   static constexpr int A_PIECES = BM / 8 / COPY_WAVES;  // 1 KB activation DMAs per copying wave
   static constexpr int B_PIECES = BN / 8 / COPY_WAVES;  // 1 KB weight DMAs per copying wave
   static_assert(WM * WN == NW && TI >= 2 && A_PIECES >= 1 && B_PIECES >= 1 && SA_WAVES <= COPY_WAVES, "tile shape");
@@ -183,8 +181,8 @@ __global__ __launch_bounds__((BigCfg<BM, BN, NW, NS>::THREADS)) void gemm_w8a8_b
     // ---- per-lane DMA sources (32-bit byte offsets: the host routes operands below 4 GiB here)
     // cw: this wave's index among the copying waves (a wave that copies nothing computes
     // valid but unused offsets)
-    const bool copier = !C::HALF || wave >= C::NW_ / 2;
-    const int cw = C::HALF ? max(wave - C::NW_ / 2, 0) : wave;
+    const bool copier = wave >= C::NW_ / 2;
+    const int cw = max(wave - C::NW_ / 2, 0);
     uint32_t oa[C::A_PIECES], ob[C::B_PIECES];
 #pragma unroll
     for (int b = 0; b < C::A_PIECES; ++b) {
@@ -342,7 +340,8 @@ __global__ __launch_bounds__((BigCfg<BM, BN, NW, NS>::THREADS)) void gemm_w8a8_b
         compute_rows(kb, kb & 1);
       }
     } else {
-      // ops issued after DMA(kb) at the top of iteration kb: DMA(kb+1) when it exists
+      // ops a copying wave has issued after DMA(kb) at the top of iteration kb: DMA(kb+1) when
+      // it exists (the other waves have none outstanding)
       issue(0, 0);
       if (KB > 1) issue(1, 1);
       if (!SWCOL && m_base == 0) stage_weight_scales();
