@@ -64,7 +64,7 @@ typedef int32_t mxq_status;
 /* Text for a status code (static storage, never NULL). */
 const char* mxq_status_string(mxq_status status);
 
-/* ABI version of this header (bumped on any signature change). */
+/* ABI version of this header (bumped on any signature change or added entry point). */
 int32_t mxq_abi_version(void);
 
 /* Checks that `device` is a gfx950 GPU and makes it current.  Every other
@@ -100,6 +100,27 @@ mxq_status mxq_per_token_group_quant_fp8(const void* x, int64_t M, int64_t K, in
 mxq_status mxq_fp8_scaled_mm(const void* A, int64_t M, int64_t K, int64_t lda, const void* W, int64_t N,
                              const float* scale, const void* bias, int32_t bias_dtype, void* out, int64_t ldo,
                              void* stream);
+
+/* ------------------------------------------------------------------ batched per-tensor W8A16
+ * For z = 0 .. batch-1:  out[z] = bf16((A[z] @ dec(W[z])^T) * scale[z] + bias[z])  -- the batched
+ * FP8 scaled GEMM that page [B] names as the existing use of its kernel (DeepSeek MLA's
+ * per-head products, "Feature and motivation"); every entry is exactly the product
+ * mxq_fp8_scaled_mm computes (same kernel, same arithmetic, bit-identical outputs).
+ *   A      bf16, entry z = [M, K] at A + z * a_bstride elements, row stride lda elements
+ *          (lda >= K, lda and a_bstride multiples of 8; 0 shares one A)
+ *   W      e4m3, entry z = contiguous [N, K] at W + z * w_bstride bytes (w_bstride a
+ *          multiple of 16; 0 shares one W)
+ *   scale  fp32 device array, entry z at scale[z * scale_bstride] (0: one shared scale)
+ *   bias   NULL, or bias_dtype (MXQ_DTYPE_F32 / MXQ_DTYPE_BF16), entry z = [N] at
+ *          bias + z * bias_bstride elements (0: one shared bias)
+ *   out    bf16, entry z = [M, N] at out + z * o_bstride elements, row stride ldo (>= N);
+ *          entries may not overlap (o_bstride >= (M - 1) * ldo + N), else MXQ_ERR_SHAPE
+ *   K must be a multiple of 32; 0 <= batch <= 65535 (batch, M or N == 0: no-op).  All
+ *   buffers are the caller's device memory; the call enqueues on `stream` and returns. */
+mxq_status mxq_fp8_scaled_bmm(const void* A, int64_t batch, int64_t M, int64_t K, int64_t lda, int64_t a_bstride,
+                              const void* W, int64_t N, int64_t w_bstride, const float* scale,
+                              int64_t scale_bstride, const void* bias, int32_t bias_dtype, int64_t bias_bstride,
+                              void* out, int64_t ldo, int64_t o_bstride, void* stream);
 
 /* ------------------------------------------------------------------ block-FP8 W8A8 linear
  * out[m, n] = bf16( sum_kb sa[m, kb] * sw[n / block_n, kb] * sum_{k in kb} dec(qa[m, k]) dec(W[n, k]) + bias[n] )

@@ -9,6 +9,7 @@ from .ops import (  # noqa: F401
     init,
     per_token_group_quant_fp8,
     fp8_scaled_mm,
+    fp8_scaled_bmm,
     block_fp8_linear,
     moe_max_blocks,
     moe_align,

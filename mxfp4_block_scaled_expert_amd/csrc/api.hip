@@ -370,7 +370,7 @@ const char* mxq_status_string(mxq_status s) {
   }
 }
 
-int32_t mxq_abi_version(void) { return 3; }
+int32_t mxq_abi_version(void) { return 4; }
 
 mxq_status mxq_init(int32_t device) {
   if (hipSetDevice(device) != hipSuccess) return MXQ_ERR_ARCH;
@@ -415,6 +415,44 @@ mxq_status mxq_fp8_scaled_mm(const void* A, int64_t M, int64_t K, int64_t lda, c
   const int tile = dense_tile_for(M);
   launch_gemm_w16(g, W_E4M3_TENSOR, ROWS_DENSE, tile, false, cdiv(M, tile_rows(tile)),
                   static_cast<hipStream_t>(stream));
+  return launch_status();
+}
+
+mxq_status mxq_fp8_scaled_bmm(const void* A, int64_t batch, int64_t M, int64_t K, int64_t lda, int64_t a_bstride,
+                              const void* W, int64_t N, int64_t w_bstride, const float* scale,
+                              int64_t scale_bstride, const void* bias, int32_t bias_dtype, int64_t bias_bstride,
+                              void* out, int64_t ldo, int64_t o_bstride, void* stream) {
+  if (batch < 0 || batch > 65535 || M < 0 || N < 0 || K < 0 || K % 32 != 0 || lda < K || lda % 8 != 0 ||
+      ldo < N)
+    return MXQ_ERR_SHAPE;
+  if (bias && bias_dtype != MXQ_DTYPE_F32 && bias_dtype != MXQ_DTYPE_BF16) return MXQ_ERR_DTYPE;
+  if (batch == 0 || M == 0 || N == 0) return MXQ_OK;
+  // inputs may be shared between entries (stride 0 included); outputs may not overlap
+  if (a_bstride < 0 || a_bstride % 8 != 0 || w_bstride < 0 || w_bstride % 16 != 0 || scale_bstride < 0 ||
+      bias_bstride < 0 || o_bstride < 0 || (batch > 1 && o_bstride < (M - 1) * ldo + N))
+    return MXQ_ERR_SHAPE;
+  if (!A || !W || !scale || !out) return MXQ_ERR_NULL;
+  if (!aligned16(A) || !aligned16(W)) return MXQ_ERR_SHAPE;
+  MXQ_TRY(check_arch());
+  GemmArgs g{};
+  g.A = A;
+  g.lda = lda;
+  g.a_bstride = a_bstride;
+  g.W = static_cast<const uint8_t*>(W);
+  g.ldw = K;
+  g.w_estride = w_bstride;
+  g.ws = scale;
+  g.ws_estride = scale_bstride;
+  g.bias = bias;
+  g.bias_bf16 = bias_dtype == MXQ_DTYPE_BF16;
+  g.bias_estride = bias_bstride;
+  g.out = out;
+  g.ldo = ldo;
+  g.o_bstride = o_bstride;
+  g.M = M;
+  g.N = N;
+  g.K = K;
+  launch_gemm_w16_batched(g, dense_tile_for(M), batch, static_cast<hipStream_t>(stream));
   return launch_status();
 }
 

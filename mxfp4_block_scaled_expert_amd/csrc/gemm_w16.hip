@@ -264,6 +264,16 @@ __device__ __forceinline__ void w16_tile(const GemmArgs& a, int64_t grid_blocks,
 template <int BM, int BN, int WAVES_M, int MODE, int WFMT, bool OUT_F32, bool HAS_BIAS, bool TILED>
 __global__ __launch_bounds__(256) void gemm_w16_kernel(GemmArgs a, int64_t grid_blocks) {
   extern __shared__ __align__(16) uint8_t w16_lds[];
+  if constexpr (MODE == ROWS_DENSE && WFMT == W_E4M3_TENSOR) {
+    // batch entry z = blockIdx.y of a batched product (z = 0 otherwise)
+    const int64_t z = blockIdx.y;
+    a.A = static_cast<const uint16_t*>(a.A) + z * a.a_bstride;
+    a.W += z * a.w_estride;
+    a.ws = static_cast<const float*>(a.ws) + z * a.ws_estride;
+    if (HAS_BIAS)
+      a.bias = static_cast<const uint8_t*>(a.bias) + z * a.bias_estride * (a.bias_bf16 ? 2 : 4);
+    a.out = static_cast<uint8_t*>(a.out) + z * a.o_bstride * (OUT_F32 ? 4 : 2);
+  }
   w16_tile<BM, BN, WAVES_M, MODE, WFMT, OUT_F32, HAS_BIAS, TILED>(a, grid_blocks, blockIdx.x, w16_lds);
 }
 
@@ -291,9 +301,9 @@ __global__ __launch_bounds__(256) void gemm_w16_grouped_kernel(W16Group g) {
 }
 
 template <int BM, int BN, int WAVES_M, int MODE, int WFMT, bool TL>
-static void launch_w16_tl(const GemmArgs& a, bool out_f32, int64_t grid_blocks, hipStream_t st) {
+static void launch_w16_tl(const GemmArgs& a, bool out_f32, int64_t grid_blocks, hipStream_t st, unsigned batch = 1) {
   const int64_t n_tiles = cdiv(a.N, BN);
-  const dim3 grid(unsigned(grid_blocks * n_tiles)), block(256);
+  const dim3 grid(unsigned(grid_blocks * n_tiles), batch), block(256);
   const bool bias = a.bias != nullptr;
   const size_t lds = w16_lds_bytes<BM, BN, WFMT>();
 #define MXQ_W16_GO(OF, HB) \
@@ -304,23 +314,24 @@ static void launch_w16_tl(const GemmArgs& a, bool out_f32, int64_t grid_blocks, 
 }
 
 template <int BM, int BN, int WAVES_M, int MODE, int WFMT>
-static void launch_w16_t(const GemmArgs& a, bool out_f32, int64_t grid_blocks, hipStream_t st) {
+static void launch_w16_t(const GemmArgs& a, bool out_f32, int64_t grid_blocks, hipStream_t st, unsigned batch = 1) {
   if constexpr (MODE != ROWS_DENSE && WFMT != W_E4M3_TENSOR) {
     if (a.w_tiled) {
       launch_w16_tl<BM, BN, WAVES_M, MODE, WFMT, true>(a, out_f32, grid_blocks, st);
       return;
     }
   }
-  launch_w16_tl<BM, BN, WAVES_M, MODE, WFMT, false>(a, out_f32, grid_blocks, st);
+  launch_w16_tl<BM, BN, WAVES_M, MODE, WFMT, false>(a, out_f32, grid_blocks, st, batch);
 }
 
 template <int MODE, int WFMT>
-static void launch_w16_mode(const GemmArgs& a, int tile, bool out_f32, int64_t gb, hipStream_t st) {
+static void launch_w16_mode(const GemmArgs& a, int tile, bool out_f32, int64_t gb, hipStream_t st,
+                            unsigned batch = 1) {
   switch (tile) {
-    case 0: launch_w16_t<128, 128, 2, MODE, WFMT>(a, out_f32, gb, st); break;
-    case 1: launch_w16_t<64, 128, 2, MODE, WFMT>(a, out_f32, gb, st); break;
-    case 2: launch_w16_t<32, 128, 1, MODE, WFMT>(a, out_f32, gb, st); break;
-    default: launch_w16_t<16, 128, 1, MODE, WFMT>(a, out_f32, gb, st); break;
+    case 0: launch_w16_t<128, 128, 2, MODE, WFMT>(a, out_f32, gb, st, batch); break;
+    case 1: launch_w16_t<64, 128, 2, MODE, WFMT>(a, out_f32, gb, st, batch); break;
+    case 2: launch_w16_t<32, 128, 1, MODE, WFMT>(a, out_f32, gb, st, batch); break;
+    default: launch_w16_t<16, 128, 1, MODE, WFMT>(a, out_f32, gb, st, batch); break;
   }
 }
 
@@ -356,6 +367,12 @@ static void launch_w16_grouped_m(const W16Group& g, bool out_f32, hipStream_t st
     launch_w16_grouped_t<MODE, WFMT, true>(g, out_f32, lds, st);
   else
     launch_w16_grouped_t<MODE, WFMT, false>(g, out_f32, lds, st);
+}
+
+void launch_gemm_w16_batched(const GemmArgs& a, int tile, int64_t batch, hipStream_t stream) {
+  const int64_t gb = cdiv(a.M, int64_t(tile == 0 ? 128 : tile == 1 ? 64 : tile == 2 ? 32 : 16));
+  if (batch <= 0 || gb <= 0 || a.N <= 0) return;
+  launch_w16_mode<ROWS_DENSE, W_E4M3_TENSOR>(a, tile, false, gb, stream, unsigned(batch));
 }
 
 void launch_gemm_w16_grouped(const GemmArgs cls[4], const int64_t grid_blocks[4], int wfmt, int row_mode,

@@ -57,6 +57,10 @@ struct GemmArgs {
   int64_t ldo;          // elements
   int64_t M, N, K;
   BlockRouting rt;
+  // batched dense products (launch_gemm_w16_batched): entry z reads A + z * a_bstride
+  // (elements), W + z * w_estride, ws + z * ws_estride, bias + z * bias_estride and writes
+  // out + z * o_bstride (elements)
+  int64_t a_bstride, o_bstride;
 };
 
 // ---------------------------------------------------------------- launchers
@@ -83,6 +87,10 @@ void launch_gemm_w16(const GemmArgs& a, int wfmt, int row_mode, int tile, bool o
 
 // Routed W8A16 / W4A16 tile classes of 16, 32, 64 and 128 rows (cls[c]: the stage's arguments
 // with class c + 1's work list; grid_blocks[c]: its capacity, 0 for none) in one launch.
+// Batched dense W8A16 products with per-tensor e4m3 weights: `batch` independent entries
+// (grid.y), each exactly the product launch_gemm_w16 computes for W_E4M3_TENSOR / ROWS_DENSE.
+void launch_gemm_w16_batched(const GemmArgs& a, int tile, int64_t batch, hipStream_t stream);
+
 void launch_gemm_w16_grouped(const GemmArgs cls[4], const int64_t grid_blocks[4], int wfmt, int row_mode,
                              bool out_f32, hipStream_t stream);
 

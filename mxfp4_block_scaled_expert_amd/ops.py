@@ -119,6 +119,44 @@ def fp8_scaled_mm(x: torch.Tensor, weight: torch.Tensor, scale: torch.Tensor,
     return out.view(*x.shape[:-1], N)
 
 
+def fp8_scaled_bmm(x: torch.Tensor, weight: torch.Tensor, scale: torch.Tensor,
+                   bias: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Batched per-tensor W8A16: bf16 [B, M, K] @ e4m3 [B, N, K]^T * scale[b] (+ bias[b]) -> bf16 [B, M, N].
+
+    ``scale`` holds one fp32 value (shared) or B values; ``bias`` is None, [N] (shared) or
+    [B, N].  Each entry equals ``fp8_scaled_mm`` on that entry, bit for bit.
+    """
+    if x.dtype != torch.bfloat16 or x.dim() != 3:
+        raise ValueError("x must be bf16 [B, M, K]")
+    w = _as_u8(weight, "weight")
+    if w.dim() != 3:
+        raise ValueError("weight must be [B, N, K]")
+    w = w.contiguous()
+    _require_cuda(x, w, scale, bias)
+    B, M, K = x.shape
+    N = w.shape[1]
+    if w.shape[0] != B or w.shape[2] != K:
+        raise ValueError(f"weight shape {tuple(w.shape)} does not match input {tuple(x.shape)}")
+    if scale.dtype != torch.float32 or scale.numel() not in (1, B):
+        raise ValueError("scale must hold 1 or B fp32 values")
+    if x.stride(-1) != 1 or x.stride(1) % 8 != 0 or x.stride(0) % 8 != 0:
+        x = x.contiguous()
+    sc = scale.reshape(-1).contiguous()
+    b = None
+    b_stride = 0
+    if bias is not None:
+        if bias.shape[-1] != N or bias.numel() not in (N, B * N):
+            raise ValueError("bias must be [N] or [B, N]")
+        b = bias.reshape(-1, N).contiguous()
+        b_stride = N if b.shape[0] == B and B > 1 else 0
+    out = torch.empty((B, M, N), dtype=torch.bfloat16, device=x.device)
+    st = L.load().mxq_fp8_scaled_bmm(x.data_ptr(), B, M, K, x.stride(1), x.stride(0), w.data_ptr(), N, N * K,
+                                     sc.data_ptr(), 1 if sc.numel() == B and B > 1 else 0, _ptr(b), _bias_dtype(b),
+                                     b_stride, out.data_ptr(), N, M * N, _stream())
+    L.check("mxq_fp8_scaled_bmm", st)
+    return out
+
+
 def block_fp8_linear(x: torch.Tensor, weight: torch.Tensor, block_size: Sequence[int], weight_scale: torch.Tensor,
                      input_scale: Optional[torch.Tensor] = None,
                      bias: Optional[torch.Tensor] = None) -> torch.Tensor:

@@ -70,6 +70,18 @@ def dense_w8a16(M: int, N: int, K: int, seed: int, device="cpu", has_bias=True,
             "bias": bias}
 
 
+def batched_w8a16(B: int, M: int, N: int, K: int, seed: int, device="cpu", has_bias=True,
+                  per_entry_scale=True) -> Dict[str, torch.Tensor]:
+    """Batched per-tensor W8A16 operands (per-head products of an MLA-style layer): the
+    per-tensor recipe above for each of B entries; scales rand + 0.005 per entry (or one)."""
+    g = _gen(seed, device)
+    a = (torch.randn(B, M, K, generator=g, device=device) / 10).to(torch.bfloat16)
+    w = torch.randn(B, N, K, generator=g, device=device).to(torch.float8_e4m3fn).view(torch.uint8)
+    scale = torch.rand(B if per_entry_scale else 1, generator=g, device=device) * 0.02 + 0.005
+    bias = torch.randn(B, N, generator=g, device=device) if has_bias else None
+    return {"a": a, "w": w, "scale": scale, "bias": bias}
+
+
 def block_linear(M: int, N: int, K: int, seed: int, device="cpu", block_n: int = 128,
                  bias_dtype: Optional[torch.dtype] = None) -> Dict[str, torch.Tensor]:
     g = _gen(seed, device)

@@ -11,6 +11,11 @@ fp32; the output is rounded fp32 -> bf16 to nearest even.
   bf16 ``A [M, K]``, e4m3 ``W [N, K]``, one fp32 scale, optional fp32 bias.
   The order -- full matmul, then scale, then bias, then bf16 -- is the one the
   listing's reference computes.
+* ``fp8_scaled_bmm`` -- the batched FP8 scaled GEMM that "SGLang PR 32618
+  review" ("Feature and motivation") names as the existing use of the kernel
+  (DeepSeek MLA): entry ``z`` is ``bf16((A[z] @ dec(W[z])^T) * s[z] + bias[z])``,
+  each entry in the same order as ``fp8_scaled_mm``.  The page gives no more
+  than that sentence; one fp32 scale per entry (or one shared) is the reading.
 * ``block_fp8_linear`` -- "SGLang PR 35605 review", implementation item 1 and
   the ``fp8_utils.py`` listing: activations carry one scale per token per 128
   columns (``[M, K/128]``); weights carry one scale per ``block_n`` x 128 block
@@ -62,6 +67,27 @@ def fp8_scaled_mm_f32(a_bf16, w_e4m3, scale, bias=None) -> np.ndarray:
 def fp8_scaled_mm(a_bf16, w_e4m3, scale, bias=None) -> np.ndarray:
     """bf16 [M, K] x e4m3 [N, K]^T * scale (+ bias) -> bf16 [M, N] (uint16 bits)."""
     return f32_to_bf16(fp8_scaled_mm_f32(a_bf16, w_e4m3, scale, bias))
+
+
+def fp8_scaled_bmm_f32(a_bf16, w_e4m3, scales, bias=None) -> np.ndarray:
+    """Batched per-tensor W8A16 before the final bf16 rounding (fp32 [B, M, N]).
+
+    ``a_bf16`` [B, M, K] bf16 bits, ``w_e4m3`` [B, N, K] codes, ``scales`` [B] fp32,
+    ``bias`` None or [B, N] fp32.  Batched float64 matmul, one fp32 rounding per entry
+    sum, then the scale and the bias in fp32.
+    """
+    a = bf16_to_f32(np.asarray(a_bf16)).astype(np.float64)
+    w = E4M3_TABLE[np.asarray(w_e4m3)].astype(np.float64)
+    prod = np.matmul(a, np.swapaxes(w, 1, 2)).astype(np.float32)
+    out = prod * np.asarray(scales, np.float32).reshape(-1, 1, 1)
+    if bias is not None:
+        out = out + np.asarray(bias, np.float32)[:, None, :]
+    return out.astype(np.float32)
+
+
+def fp8_scaled_bmm(a_bf16, w_e4m3, scales, bias=None) -> np.ndarray:
+    """bf16 [B, M, K] x e4m3 [B, N, K]^T * scale[b] (+ bias[b]) -> bf16 [B, M, N] (uint16 bits)."""
+    return f32_to_bf16(fp8_scaled_bmm_f32(a_bf16, w_e4m3, scales, bias))
 
 
 def block_fp8_linear_f32(qa, sa, w, sw, block_n, bias=None) -> np.ndarray:

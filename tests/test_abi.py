@@ -27,7 +27,8 @@ def _declared():
 
 def test_header_declares_the_entry_points():
     names = _declared()
-    for n in ("mxq_per_token_group_quant_fp8", "mxq_fp8_scaled_mm", "mxq_block_fp8_linear", "mxq_moe_align",
+    for n in ("mxq_per_token_group_quant_fp8", "mxq_fp8_scaled_mm", "mxq_fp8_scaled_bmm", "mxq_block_fp8_linear",
+              "mxq_moe_align",
               "mxq_fused_moe_fp8", "mxq_fused_moe_mxfp4", "mxq_moe_prepack", "mxq_moe_prepack_scales"):
         assert n in names
 
@@ -42,7 +43,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_status_strings_and_version():
     L, lib = _lib()
-    assert lib.mxq_abi_version() == 3
+    assert lib.mxq_abi_version() == 4
     for code in range(0, 9):
         assert lib.mxq_status_string(code)
     assert b"unknown" in lib.mxq_status_string(99)
@@ -82,6 +83,18 @@ def test_argument_errors_before_any_launch():
     assert lib.mxq_per_token_group_quant_fp8(null, 0, 256, 256, 128, null, null, null) == L.MXQ_OK
     assert lib.mxq_fp8_scaled_mm(null, 4, 100, 100, null, 8, null, null, 0, null, 8, null) == L.MXQ_ERR_SHAPE
     assert lib.mxq_fp8_scaled_mm(null, 4, 128, 128, null, 8, null, null, 7, null, 8, null) == L.MXQ_ERR_NULL
+    # batched per-tensor: K % 32, lda, batch limit, overlapping outputs, strides, null pointers
+    bmm = lib.mxq_fp8_scaled_bmm
+    assert bmm(null, 2, 4, 100, 100, 400, null, 8, 800, null, 0, null, 0, 0, null, 8, 32, null) == L.MXQ_ERR_SHAPE
+    assert bmm(null, 70000, 4, 128, 128, 512, null, 8, 1024, null, 0, null, 0, 0, null, 8, 32, null) == L.MXQ_ERR_SHAPE
+    assert bmm(null, 2, 4, 128, 128, 512, null, 8, 1024, null, 0, null, 0, 0, null, 8, 31, null) == L.MXQ_ERR_SHAPE
+    assert bmm(null, 2, 4, 128, 128, 500, null, 8, 1024, null, 0, null, 0, 0, null, 8, 32, null) == L.MXQ_ERR_SHAPE
+    assert bmm(null, 2, 4, 128, 128, 512, null, 8, 1000, null, 0, null, 0, 0, null, 8, 32, null) == L.MXQ_ERR_SHAPE
+    fake = C.c_void_p(0x1000)  # never dereferenced: the dtype check comes first
+    assert bmm(null, 2, 4, 128, 128, 512, null, 8, 1024, null, 0, fake, 9, 0, null, 8, 32, null) == L.MXQ_ERR_DTYPE
+    assert bmm(null, 2, 4, 128, 128, 512, null, 8, 1024, null, 0, null, 0, 0, null, 8, 32, null) == L.MXQ_ERR_NULL
+    assert bmm(null, 2, 4, 128, 128, 0, null, 8, 0, null, 0, null, 0, 0, null, 8, 32, null) == L.MXQ_ERR_NULL
+    assert bmm(null, 0, 4, 128, 128, 512, null, 8, 1024, null, 0, null, 0, 0, null, 8, 32, null) == L.MXQ_OK
     assert lib.mxq_fused_moe_fp8(null, 4, 100, 128, 8, 2, null, null, null, null, null, null, null, 0, 0, null, null,
                                  0, null) == L.MXQ_ERR_SHAPE
     assert lib.mxq_fused_moe_mxfp4(null, 4, 100, 128, 8, 2, null, null, null, null, null, null, null, 0, null, null, 0,

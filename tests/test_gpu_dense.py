@@ -55,6 +55,67 @@ def test_fp8_scaled_mm_workload_and_bf16_bias_and_3d():
     assert_bf16_close(bf16_bits(out.view(97, 224)), want, what="fp8_scaled_mm bf16 bias")
 
 
+# ---- batched per-tensor W8A16 (MLA-style per-head products)
+
+def _oracle_bmm(d, bias=None):
+    B = d["a"].shape[0]
+    sc = f32(d["scale"])
+    scales = np.broadcast_to(sc, (B,)) if sc.size == 1 else sc
+    return OD.fp8_scaled_bmm(bf16_bits(d["a"]), u8(d["w"]), scales, None if bias is None else bias)
+
+
+@pytest.mark.parametrize("B,M,N,K", [(4, 97, 224, 576), (16, 1, 128, 512), (3, 130, 200, 512), (2, 33, 128, 96)])
+@pytest.mark.parametrize("per_entry_scale", [True, False])
+def test_fp8_scaled_bmm_matches_per_entry_products_and_oracle(B, M, N, K, per_entry_scale):
+    d = synth.batched_w8a16(B, M, N, K, seed=B * 7 + M + N + K, device=gpu(), per_entry_scale=per_entry_scale)
+    out = ops.fp8_scaled_bmm(d["a"], d["w"], d["scale"], d["bias"])
+    torch.cuda.synchronize()
+    assert out.shape == (B, M, N)
+    for z in range(B):  # every entry is the 2-D product, bit for bit
+        sz = d["scale"][z if per_entry_scale else 0].reshape(1)
+        ref = ops.fp8_scaled_mm(d["a"][z], d["w"][z], sz, d["bias"][z])
+        assert torch.equal(out[z].view(torch.int16), ref.view(torch.int16)), f"entry {z}"
+    assert_bf16_close(bf16_bits(out), _oracle_bmm(d, f32(d["bias"])), what=f"bmm {B}x{M}x{N}x{K}")
+
+
+def test_fp8_scaled_bmm_shared_bias_bf16_and_no_bias():
+    d = synth.batched_w8a16(5, 40, 256, 512, seed=31, device=gpu())
+    shared = d["bias"][0].to(torch.bfloat16)
+    out = ops.fp8_scaled_bmm(d["a"], d["w"], d["scale"], shared)
+    out0 = ops.fp8_scaled_bmm(d["a"], d["w"], d["scale"])
+    torch.cuda.synchronize()
+    bias = np.broadcast_to(f32(shared), (5, 256))
+    assert_bf16_close(bf16_bits(out), _oracle_bmm(d, bias), what="bmm shared bf16 bias")
+    assert_bf16_close(bf16_bits(out0), _oracle_bmm(d), what="bmm no bias")
+
+
+def test_fp8_scaled_bmm_mla_head_shapes_sampled():
+    """DeepSeek MLA-shaped per-head products at full size (128 heads, 64 tokens): the
+    absorbed key projection [T, 128] x [512, 128]^T and the value projection [T, 512] x
+    [128, 512]^T; every head checked against the oracle on its first and last rows."""
+    for (N, K) in [(512, 128), (128, 512)]:
+        d = synth.batched_w8a16(128, 64, N, K, seed=N + K, device=gpu(), has_bias=False)
+        out = ops.fp8_scaled_bmm(d["a"], d["w"], d["scale"])
+        torch.cuda.synchronize()
+        rows = [0, 31, 63]
+        sub = {"a": d["a"][:, rows], "w": d["w"], "scale": d["scale"]}
+        assert_bf16_close(bf16_bits(out[:, rows]), _oracle_bmm(sub), what=f"MLA heads N={N} K={K}")
+
+
+def test_fp8_scaled_bmm_empty_and_strided_input():
+    d = synth.batched_w8a16(3, 20, 128, 256, seed=41, device=gpu())
+    empty = ops.fp8_scaled_bmm(d["a"][:, :0], d["w"], d["scale"], d["bias"])
+    assert empty.shape == (3, 0, 128)
+    # row stride 320 elements and a batch stride with a gap: strided entries, same results
+    big = torch.zeros(3, 24, 320, dtype=torch.bfloat16, device=gpu())
+    big[:, :20, :256] = d["a"]
+    view = big[:, :20, :256]
+    got = ops.fp8_scaled_bmm(view, d["w"], d["scale"], d["bias"])
+    ref = ops.fp8_scaled_bmm(d["a"], d["w"], d["scale"], d["bias"])
+    torch.cuda.synchronize()
+    assert torch.equal(got.view(torch.int16), ref.view(torch.int16))
+
+
 def _block_case(M, N, K, block_n, seed, bias_dtype=None, scale_recipe="synth"):
     d = synth.block_linear(M, N, K, seed=seed, device=gpu(), block_n=block_n, bias_dtype=bias_dtype)
     if scale_recipe == "page":  # rand(N/bn, K/128) + 0.1 as in the page's accuracy test

@@ -130,3 +130,47 @@ def test_row_independence():
     full = D.block_fp8_linear_bf16(x, w, sw, 128)
     part = D.block_fp8_linear_bf16(x[4:6], w, sw, 128)
     assert np.array_equal(full[4:6], part)
+
+
+# ---- batched per-tensor W8A16 (the MLA-style batched FP8 GEMM)
+
+def test_bmm_closed_form_per_entry_scales_and_biases():
+    """A = 1, W = 1.0: entry z is K * 2^-z + bias[z] exactly (small integers, exact in bf16)."""
+    B, M, N, K = 4, 3, 5, 64
+    a = _bf16(np.ones((B, M, K)))
+    w = np.full((B, N, K), 0x38, np.uint8)
+    scales = np.array([2.0 ** -z for z in range(B)], np.float32)
+    bias = np.arange(B * N, dtype=np.float32).reshape(B, N)
+    got = C.bf16_to_f32(D.fp8_scaled_bmm(a, w, scales, bias))
+    want = (K * scales)[:, None, None] + bias[:, None, :]
+    assert np.array_equal(got, np.broadcast_to(want, (B, M, N)).astype(np.float32))
+
+
+def test_bmm_vs_torch_bmm_float64():
+    """The batched definition against torch.bmm of torch-decoded operands (within 2 fp32 ulps
+    before the bf16 rounding): catches a transposed operand or a scale applied to the wrong entry."""
+    rng = np.random.default_rng(7)
+    B, M, N, K = 3, 17, 96, 512
+    a = _bf16(rng.standard_normal((B, M, K)) / 10)
+    w = torch.randn(B, N, K, generator=torch.Generator().manual_seed(7)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    scales = np.array([0.01, 0.5, 3.0], np.float32)
+    bias = rng.standard_normal((B, N)).astype(np.float32)
+    got = D.fp8_scaled_bmm_f32(a, w, scales, bias)
+    at = torch.from_numpy(a.view(np.int16).copy()).view(torch.bfloat16).double()
+    prod = torch.bmm(at, _tdec(w).transpose(1, 2).contiguous()).float()
+    ref = (prod * torch.from_numpy(scales)[:, None, None] + torch.from_numpy(bias)[:, None, :]).numpy()
+    assert np.all(np.abs(got - ref) <= 2 * _ulp32(ref))
+
+
+def test_bmm_entries_are_independent_and_match_the_2d_product():
+    rng = np.random.default_rng(8)
+    B, M, N, K = 3, 4, 32, 64
+    a = _bf16(rng.standard_normal((B, M, K)))
+    w = rng.integers(0, 256, (B, N, K), dtype=np.uint8)
+    w[(w & 0x7F) == 0x7F] = 0x38  # no NaN codes
+    scales = np.array([0.25, 1.5, 0.03125], np.float32)
+    full = D.fp8_scaled_bmm(a, w, scales)
+    perm = np.array([2, 0, 1])
+    assert np.array_equal(D.fp8_scaled_bmm(a[perm], w[perm], scales[perm]), full[perm])
+    for z in range(B):
+        assert np.array_equal(full[z], D.fp8_scaled_mm(a[z], w[z], scales[z]))
