@@ -48,7 +48,6 @@ constexpr int kMaxKB = 128;  // K <= 16384 on this kernel
 template <int BM, int BN, int NW, int NS>
 struct BigCfg {
   static constexpr int THREADS = NW * 64;
-  static constexpr int NW_ = NW;
   static constexpr int WN = BN / 64, WM = NW / WN;
   static constexpr int WROWS = BM / WM;  // rows per wave
   static constexpr int TI = WROWS / 16;  // 16-row sub-tiles per wave
@@ -181,8 +180,8 @@ __global__ __launch_bounds__((BigCfg<BM, BN, NW, NS>::THREADS)) void gemm_w8a8_b
     // ---- per-lane DMA sources (32-bit byte offsets: the host routes operands below 4 GiB here)
     // cw: this wave's index among the copying waves (a wave that copies nothing computes
     // valid but unused offsets)
-    const bool copier = wave >= C::NW_ / 2;
-    const int cw = max(wave - C::NW_ / 2, 0);
+    const bool copier = wave >= NW / 2;
+    const int cw = max(wave - NW / 2, 0);
     uint32_t oa[C::A_PIECES], ob[C::B_PIECES];
 #pragma unroll
     for (int b = 0; b < C::A_PIECES; ++b) {
@@ -190,21 +189,20 @@ __global__ __launch_bounds__((BigCfg<BM, BN, NW, NS>::THREADS)) void gemm_w8a8_b
       const int chunk = (lane & 7) ^ swz(row);
       oa[b] = uint32_t(sArow[row] * a.lda + chunk * 16);
     }
-    // weight piece b of this wave's share: the tile's d-th 1 KB piece
-    auto w_offset = [&](int b) __attribute__((always_inline)) -> uint32_t {
-      const int d = cw * C::B_PIECES + b;
+#pragma unroll
+    for (int b = 0; b < C::B_PIECES; ++b) {
+      const int d = cw * C::B_PIECES + b;  // the tile's d-th 1 KB weight piece
       if (TILED) {
         // piece d = half (d & 1) of the tile of 16-row group d / 2
         const int64_t g16 = min<int64_t>(n0 / 16 + (d >> 1), a.N / 16 - 1);
-        return uint32_t(g16 * KB * 2048 + (d & 1) * 1024 + lane * 16);
+        ob[b] = uint32_t(g16 * KB * 2048 + (d & 1) * 1024 + lane * 16);
+      } else {
+        const int row = d * 8 + (lane >> 3);
+        const int chunk = (lane & 7) ^ swz(row);
+        const int64_t n = min<int64_t>(n0 + row, a.N - 1);
+        ob[b] = uint32_t(n * a.ldw + chunk * 16);
       }
-      const int row = d * 8 + (lane >> 3);
-      const int chunk = (lane & 7) ^ swz(row);
-      const int64_t n = min<int64_t>(n0 + row, a.N - 1);
-      return uint32_t(n * a.ldw + chunk * 16);
-    };
-#pragma unroll
-    for (int b = 0; b < C::B_PIECES; ++b) ob[b] = w_offset(b);
+    }
     // activation scales: copying waves cw < BM/64 fetch 64 rows each; the other ones fetch a
     // filler dword into sFill so that every copying wave issues the same number of loads per
     // K block
