@@ -237,6 +237,43 @@ __device__ __forceinline__ void w16_tile(const GemmArgs& a, int64_t grid_blocks,
   }
 
   const float tscale = (WFMT == W_E4M3_TENSOR) ? reinterpret_cast<const float*>(a.ws)[0] : 1.f;
+  // bf16 output with 16-byte aligned rows: the tile goes through LDS (the operand buffers are
+  // free after the K loop) and leaves as 16-byte row chunks instead of 2-byte column stores
+  constexpr int OROW = BN + 8;  // bf16 elements per staged row (padding against bank conflicts)
+  static_assert(size_t(BM) * OROW * 2 <= w16_lds_bytes<BM, BN, WFMT>(), "staged output fits the tile's LDS");
+  const bool staged = !OUT_F32 && (reinterpret_cast<uintptr_t>(a.out) & 15) == 0 && (a.ldo & 7) == 0;
+  if (staged) {
+    uint16_t* sO = reinterpret_cast<uint16_t*>(lds);
+    __syncthreads();  // every wave is done with the operand buffers
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+      const int cl = wn * WN + 16 * j + frow;
+      const int64_t col = n0 + cl;
+      const float b = HAS_BIAS && col < a.N ? load_bias(a, expert, col) : 0.f;
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          float v = acc[i][j][r];
+          if (WFMT == W_E4M3_TENSOR) v = v * tscale;
+          sO[(wm * WM + 16 * i + 4 * (lane >> 4) + r) * OROW + cl] = f2bf(v + b);
+        }
+    }
+    __syncthreads();
+    const int64_t ncols = min<int64_t>(BN, a.N - n0);
+    for (int c = tid; c < m_size * (BN / 8); c += 256) {
+      const int rl = c / (BN / 8), ch = c % (BN / 8);
+      const int64_t col = n0 + ch * 8;
+      uint16_t* dst = reinterpret_cast<uint16_t*>(a.out) + sOrow[rl] * a.ldo + col;
+      const uint16_t* src = sO + rl * OROW + ch * 8;
+      if (ch * 8 + 8 <= ncols) {
+        *reinterpret_cast<uint4*>(dst) = *reinterpret_cast<const uint4*>(src);
+      } else {
+        for (int e = 0; e < 8 && ch * 8 + e < ncols; ++e) dst[e] = src[e];
+      }
+    }
+    continue;  // next row pass (its first barrier orders these LDS reads before new writes)
+  }
 #pragma unroll
   for (int j = 0; j < TN; ++j) {
     const int64_t col = n0 + wn * WN + 16 * j + frow;
