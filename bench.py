@@ -13,7 +13,8 @@ Printed: ONE JSON line with the throughput of the step (TFLOP/s), the roofline
 of the dominant kernel (the GEMM, against the FP8 dense MFMA peak, timed with
 HIP events on the stream it runs on), the CPU oracle's throughput on the same
 workload, and secondary measurements of the two routed-MoE workloads
-(GPT-OSS-shaped MXFP4 decode and DeepSeek-shaped W8A8 prefill).
+(GPT-OSS-shaped MXFP4 decode and DeepSeek-shaped W8A8 prefill) and of the batched
+per-tensor W8A16 GEMM on MLA-shaped per-head products (128 heads, 64 tokens).
 """
 
 from __future__ import annotations
@@ -231,6 +232,35 @@ def bench_moe(name: str, steps: int, warmup: int, seed: int, layout: str = "tile
     }
 
 
+def bench_mla_bmm(steps: int, warmup: int, tokens: int = 64):
+    """Batched per-tensor W8A16 on MLA-shaped per-head products (128 heads): the key side
+    [T, 128] x [512, 128]^T and the value side [T, 512] x [128, 512]^T, through the C ABI on
+    rotating weight sets."""
+    from mxfp4_block_scaled_expert_amd import synth
+    _, lib = _lib()
+    dev = torch.device("cuda", 0)
+    st = torch.cuda.current_stream()
+    res = {}
+    for name, (N, K) in (("key", (512, 128)), ("value", (128, 512))):
+        B, T = 128, tokens
+        sets = [synth.batched_w8a16(B, T, N, K, seed=2000 + i, device=dev, has_bias=False) for i in range(8)]
+        out = torch.empty(B, T, N, dtype=torch.bfloat16, device=dev)
+        it = [0]
+
+        def run():
+            d = sets[it[0] % len(sets)]
+            it[0] += 1
+            _check(lib.mxq_fp8_scaled_bmm(d["a"].data_ptr(), B, T, K, K, T * K, d["w"].data_ptr(), N, N * K,
+                                          d["scale"].data_ptr(), 1, None, 0, 0, out.data_ptr(), N, T * N,
+                                          st.cuda_stream), "mxq_fp8_scaled_bmm")
+        us = _time_calls(run, steps, warmup)
+        byts = B * N * K + B * T * K * 2 + B * T * N * 2
+        res[name] = {"shape": f"{B}x[{T},{K}]x[{N},{K}]^T", "us_avg": us, "gbs": byts / (us * 1e-6) / 1e9,
+                     "hbm_frac": byts / (us * 1e-6) / 1e9 / HBM_PEAK_GBS}
+        del sets
+    return res
+
+
 def bench_dispatch_ablation(steps: int, warmup: int):
     """The pages' central comparison at kernel level: each expert block choosing its tile class
     from its own row count (the default) against one class for the whole layer chosen from the
@@ -352,6 +382,8 @@ def main():
         torch.cuda.empty_cache()
         secondary["deepseek_w8a8_prefill_m4096"] = bench_moe("moe_block_fp8_w8a8_deepseek_prefill_m4096",
                                                             max(3, a.steps // 10), 2, 1005)
+        torch.cuda.empty_cache()
+        secondary["mla_bmm_128heads_t64"] = bench_mla_bmm(max(10, a.steps // 2), a.warmup)
         torch.cuda.empty_cache()
     cpu = None if a.no_cpu_baseline else cpu_baseline()
     line = {
