@@ -131,22 +131,22 @@ def fp8_scaled_bmm(x: torch.Tensor, weight: torch.Tensor, scale: torch.Tensor,
     w = _as_u8(weight, "weight")
     if w.dim() != 3:
         raise ValueError("weight must be [B, N, K]")
-    w = w.contiguous()
-    _require_cuda(x, w, scale, bias)
     B, M, K = x.shape
     N = w.shape[1]
     if w.shape[0] != B or w.shape[2] != K:
         raise ValueError(f"weight shape {tuple(w.shape)} does not match input {tuple(x.shape)}")
     if scale.dtype != torch.float32 or scale.numel() not in (1, B):
         raise ValueError("scale must hold 1 or B fp32 values")
+    if bias is not None and (bias.shape[-1] != N or bias.numel() not in (N, B * N)):
+        raise ValueError("bias must be [N] or [B, N]")
+    w = w.contiguous()
+    _require_cuda(x, w, scale, bias)
     if x.stride(-1) != 1 or x.stride(1) % 8 != 0 or x.stride(0) % 8 != 0:
         x = x.contiguous()
     sc = scale.reshape(-1).contiguous()
     b = None
     b_stride = 0
     if bias is not None:
-        if bias.shape[-1] != N or bias.numel() not in (N, B * N):
-            raise ValueError("bias must be [N] or [B, N]")
         b = bias.reshape(-1, N).contiguous()
         b_stride = N if b.shape[0] == B and B > 1 else 0
     out = torch.empty((B, M, N), dtype=torch.bfloat16, device=x.device)

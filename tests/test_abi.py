@@ -139,3 +139,20 @@ def test_binding_rejects_bad_block_size_without_gpu():
     for bs in ([1, 32], [64, 64], [128], (128, 128, 1)):
         with pytest.raises(ValueError):
             ops.block_fp8_linear(x, w, bs, s)
+
+
+def test_batched_binding_rejects_mismatched_shapes_without_gpu():
+    import torch
+    from mxfp4_block_scaled_expert_amd import ops
+    x = torch.zeros(2, 4, 256, dtype=torch.bfloat16)
+    w = torch.zeros(2, 128, 256, dtype=torch.uint8)
+    with pytest.raises(ValueError):
+        ops.fp8_scaled_bmm(x, torch.zeros(3, 128, 256, dtype=torch.uint8), torch.ones(1))
+    with pytest.raises(ValueError):
+        ops.fp8_scaled_bmm(x, torch.zeros(2, 128, 128, dtype=torch.uint8), torch.ones(1))
+    with pytest.raises(ValueError):
+        ops.fp8_scaled_bmm(x, w, torch.ones(3))
+    with pytest.raises(ValueError):
+        ops.fp8_scaled_bmm(x, w, torch.ones(1), torch.zeros(3, 128))
+    with pytest.raises(ValueError):
+        ops.fp8_scaled_bmm(x.float(), w, torch.ones(1))

@@ -102,6 +102,33 @@ def test_fp8_scaled_bmm_mla_head_shapes_sampled():
         assert_bf16_close(bf16_bits(out[:, rows]), _oracle_bmm(sub), what=f"MLA heads N={N} K={K}")
 
 
+def test_fp8_scaled_bmm_shared_inputs_through_the_c_abi():
+    """Batch stride 0 on A and on W: every entry reads the same operand (documented sharing)."""
+    from mxfp4_block_scaled_expert_amd import _lib as L
+    lib = L.load()
+    d = synth.batched_w8a16(4, 24, 128, 256, seed=51, device=gpu(), has_bias=False)
+    B, M, N, K = 4, 24, 128, 256
+    out = torch.empty(B, M, N, dtype=torch.bfloat16, device=gpu())
+    st = torch.cuda.current_stream().cuda_stream
+    # shared A (entry 0), per-entry W
+    assert lib.mxq_fp8_scaled_bmm(d["a"].data_ptr(), B, M, K, K, 0, d["w"].data_ptr(), N, N * K, d["scale"].data_ptr(),
+                                  1, None, 0, 0, out.data_ptr(), N, M * N, st) == 0
+    torch.cuda.synchronize()
+    for z in range(B):
+        ref = ops.fp8_scaled_mm(d["a"][0], d["w"][z], d["scale"][z].reshape(1))
+        assert torch.equal(out[z].view(torch.int16), ref.view(torch.int16))
+    # per-entry A, shared W (entry 0) and shared scale
+    assert lib.mxq_fp8_scaled_bmm(d["a"].data_ptr(), B, M, K, K, M * K, d["w"].data_ptr(), N, 0, d["scale"].data_ptr(),
+                                  0, None, 0, 0, out.data_ptr(), N, M * N, st) == 0
+    torch.cuda.synchronize()
+    for z in range(B):
+        ref = ops.fp8_scaled_mm(d["a"][z], d["w"][0], d["scale"][0].reshape(1))
+        assert torch.equal(out[z].view(torch.int16), ref.view(torch.int16))
+    # overlapping outputs are refused before any launch
+    assert lib.mxq_fp8_scaled_bmm(d["a"].data_ptr(), B, M, K, K, M * K, d["w"].data_ptr(), N, N * K,
+                                  d["scale"].data_ptr(), 1, None, 0, 0, out.data_ptr(), N, N, st) == L.MXQ_ERR_SHAPE
+
+
 def test_fp8_scaled_bmm_empty_and_strided_input():
     d = synth.batched_w8a16(3, 20, 128, 256, seed=41, device=gpu())
     empty = ops.fp8_scaled_bmm(d["a"][:, :0], d["w"], d["scale"], d["bias"])
