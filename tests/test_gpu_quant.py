@@ -55,6 +55,22 @@ def test_every_bf16_value_with_unit_scale():
     _check(x)
 
 
+def test_every_bf16_value_with_non_power_of_two_scales():
+    """Group maxima 448, 450, ..., 510 (scales 1 .. 1.138, long mantissas) against every bf16
+    value in [-448, 448]: the quotients land all over the e4m3 grid, some within a few fp32
+    ulps of its rounding midpoints, where the codes must still be those of the division."""
+    pats = torch.arange(65536, dtype=torch.int32).to(torch.int16).view(torch.bfloat16).float()
+    vals = pats[torch.isfinite(pats) & (pats.abs() <= 448)]
+    per = 127
+    n = -(-vals.numel() // per)
+    vals = torch.cat([vals, torch.zeros(n * per - vals.numel())]).view(n, per)
+    rows = []
+    for amax in range(448, 512, 2):
+        rows.append(torch.cat([torch.full((n, 1), float(amax)), vals], dim=1))
+    x = torch.cat(rows).to(torch.bfloat16).to(gpu())
+    _check(x)
+
+
 def test_zero_negative_zero_and_constant_groups():
     x = torch.zeros(4, 512)
     x[0, 5] = -0.0
