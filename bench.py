@@ -42,7 +42,7 @@ BF16_PEAK_TFLOPS = 2500.0
 # 0.500, WRITE_SIZE 1.000 of the true bytes); figures and commands in
 # profiles/gemm_w8a8_big_block_linear_2048x2048x7168.md and profiles/copy_calibration_256MiB.md.
 # Set back to None whenever gemm_w8a8_big_kernel changes until the counters are taken again.
-GEMM_TRAFFIC_BYTES = 76307028
+GEMM_TRAFFIC_BYTES = 76314427
 
 
 def _args():
