@@ -42,14 +42,14 @@ BF16_PEAK_TFLOPS = 2500.0
 # 0.500, WRITE_SIZE 1.000 of the true bytes); figures and commands in
 # profiles/gemm_w8a8_big_block_linear_2048x2048x7168.md and profiles/copy_calibration_256MiB.md.
 # Set back to None whenever gemm_w8a8_big_kernel changes until the counters are taken again.
-GEMM_TRAFFIC_BYTES = 76314427
+GEMM_TRAFFIC_BYTES = 76329103
 
 
 def _args():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=50)
-    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--warmup", type=int, default=1000)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-secondary", action="store_true")
     p.add_argument("--only", choices=["linear", "decode", "prefill", "copy", "ablation"], default=None,
