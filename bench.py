@@ -101,8 +101,8 @@ def bench_linear(steps: int, warmup: int):
 
     def gemm(d, qq, sc):
         _check(lib.mxq_block_fp8_linear(qq.data_ptr(), L.MXQ_DTYPE_E4M3, sc.data_ptr(), M, K, K, d["w"].data_ptr(), N,
-                                        d["sw"].data_ptr(), K // 128, 1, 128, 128, None, 0, out.data_ptr(), N, None,
-                                        0, sh), "block_fp8_linear")
+                                        d["sw"].data_ptr(), K // 128, 1, 128, 128, None, 0, out.data_ptr(),
+                                        L.MXQ_DTYPE_BF16, N, None, 0, sh), "block_fp8_linear")
 
     for i in range(n_rot):
         quant(sets[i], qs[i], ss[i])
@@ -165,7 +165,7 @@ def _touched_bytes(inp) -> int:
     return int(used.size * per + 2 * M * H * 2 + ids.size * 8)
 
 
-def _moe_setup(name_or_spec, seed: int, layout: str = "tiled", M=None):
+def _moe_setup(name_or_spec, seed: int, layout: str = "tiled", M=None, dispatch=None):
     """Inputs (weights prepacked once for ``layout="tiled"``, as a model would at weight-loading
     time), workspace and a closure running one fused-MoE call."""
     from mxfp4_block_scaled_expert_amd import ops, synth
@@ -191,11 +191,11 @@ def _moe_setup(name_or_spec, seed: int, layout: str = "tiled", M=None):
         if mx:
             ops.fused_moe_mxfp4(inp["x"], inp["topk_ids"], inp["topk_weights"], inp["w1"], inp["w1_scale"],
                                 inp["w2"], inp["w2_scale"], inp["w1_bias"], workspace=ws, out=out,
-                                weight_layout=layout)
+                                weight_layout=layout, dispatch=dispatch[0] if dispatch else None)
         else:
             ops.fused_moe_fp8(inp["x"], inp["topk_ids"], inp["topk_weights"], inp["w1"], inp["w1_scale"],
                               inp["w2"], inp["w2_scale"], None, act_quant=inp["act_quant"], workspace=ws, out=out,
-                              weight_layout=layout)
+                              weight_layout=layout, dispatch=dispatch[0] if dispatch else None)
 
     flops = 2.0 * Mt * topk * (2 * I * H + H * I)
     return {"inp": inp, "run": run, "bytes": byts, "flops": flops, "M": Mt}
@@ -280,14 +280,14 @@ def bench_dispatch_ablation(steps: int, warmup: int):
     ]
     rows = []
     for label, spec, M, seed in cases:
-        w = _moe_setup(spec, seed, "tiled", M=M)
+        sel = [None]  # the dispatch the closure passes, switched between the two timings
+        w = _moe_setup(spec, seed, "tiled", M=M, dispatch=sel)
         big = w["M"] >= 512
         n, wu = (max(3, steps // 10), 2) if big else (steps, warmup)
         res = {}
         for mode, key in ((L.MXQ_DISPATCH_PER_BLOCK, "per_block_us"), (L.MXQ_DISPATCH_LAYER_AVERAGE, "layer_avg_us")):
-            ops.moe_set_dispatch(mode, 0, 16)
+            sel[0] = ops.Dispatch(mode, 0, 16)
             res[key] = _time_calls(w["run"], n, wu)
-        ops.moe_set_dispatch()
         row = {"case": label, "M": w["M"], **res, "speedup": res["layer_avg_us"] / res["per_block_us"],
                "per_block_weight_gbs": w["bytes"] / (res["per_block_us"] * 1e-6) / 1e9}
         print(json.dumps(row), flush=True)

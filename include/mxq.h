@@ -135,7 +135,10 @@ mxq_status mxq_fp8_scaled_bmm(const void* A, int64_t batch, int64_t M, int64_t K
  *             storage of page [C]'s load-time relayout both work, bit-identically.
  *   block_n, block_k   the weight block: (128, 128) or (1, 128); anything else -> MXQ_ERR_BLOCK
  *   bias      NULL or [N] of bias_dtype (fp32 or bf16)
- *   out       bf16 [M, N], row stride ldo elements
+ *   out       [M, N] of out_dtype, row stride ldo elements.  out_dtype must be
+ *             MXQ_DTYPE_BF16 (page [C], fp8_utils.py listing: the output takes bf16 for
+ *             pre-quantised input and the input's dtype otherwise, bf16 for every input
+ *             this entry point accepts); anything else -> MXQ_ERR_DTYPE.
  *   workspace bf16 input needs mxq_block_fp8_linear_workspace_size(M, K, a_dtype) bytes
  *             (the quantised activations); e4m3 input needs none (may be NULL).
  *   K must be a multiple of 128.  FP8 matrix cores (16x16x128 per K block), fp32 accumulation. */
@@ -143,8 +146,8 @@ size_t mxq_block_fp8_linear_workspace_size(int64_t M, int64_t K, int32_t a_dtype
 mxq_status mxq_block_fp8_linear(const void* A, int32_t a_dtype, const float* a_scale, int64_t M, int64_t K,
                                 int64_t lda, const void* W, int64_t N, const float* w_scale, int64_t ws_stride0,
                                 int64_t ws_stride1, int32_t block_n, int32_t block_k, const void* bias,
-                                int32_t bias_dtype, void* out, int64_t ldo, void* workspace, size_t workspace_bytes,
-                                void* stream);
+                                int32_t bias_dtype, void* out, int32_t out_dtype, int64_t ldo, void* workspace,
+                                size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------ expert sort / align
  * Groups the R = M * topk routed rows (flat id r = t * topk + k) by expert for the
@@ -176,7 +179,8 @@ mxq_status mxq_moe_align(const int32_t* topk_ids, int64_t M, int32_t topk, int32
  * weight).  Rows [0, I) of w1 are the gate, rows [I, 2I) the up projection.
  * Each expert block picks its kernel from its own row count (page [A],
  * implementation items 1-2): a weight-streaming kernel for tiny blocks, MFMA
- * tiles of 16/32/64/128 rows otherwise (see mxq_moe_set_dispatch).
+ * tiles of 16/32/64/128 rows otherwise (see mxq_moe_dispatch below; `dispatch`
+ * NULL = per-block selection with the default bounds).
  *
  * mxq_fused_moe_fp8: block-FP8 weights.
  *   x            bf16 [M, H], contiguous
@@ -200,23 +204,104 @@ mxq_status mxq_moe_align(const int32_t* topk_ids, int64_t M, int32_t topk, int32
  *   H and I must be multiples of 32.
  * Both: workspace of mxq_fused_moe_workspace_size(...) bytes (routing tables,
  * intermediates); experts that receive no rows are never read; 1 <= E <= 512.
- * The two layouts give bit-identical outputs. */
+ * The two layouts give bit-identical outputs.
+ *
+ * Per-call dispatch (`dispatch`, read during the call only; NULL = the defaults
+ * {MXQ_DISPATCH_PER_BLOCK, 0, 16, MXQ_TINY_MFMA}; invalid fields -> MXQ_ERR_ARG):
+ *   mode MXQ_DISPATCH_PER_BLOCK: each block's class from its own row count;
+ *   mode MXQ_DISPATCH_FORCED: every block runs class `forced_class` (0 = tiny-block kernel,
+ *        1 = 16-row, 2 = 32-row, 3 = 64-row, 4 = 128-row MFMA tiles) -- for tests;
+ *   mode MXQ_DISPATCH_LAYER_AVERAGE: one class for the whole layer, chosen from
+ *        max(1, M * topk / E) rows (the per-layer rule page [A] replaces; for
+ *        ablation measurements).
+ *   tiny_max_rows (0..16): largest block that takes the tiny-block class in per-block
+ *        mode.  When M <= 2 * tiny_max_rows the tiny class takes every block (taller ones
+ *        in several passes); with bf16 activations, the MFMA tiny kernel, at most 4096
+ *        routed rows, E <= 512 and both stages' operands fitting the kernel's LDS budget,
+ *        this case runs as two persistent expert-streaming kernels that group the routed
+ *        rows by expert themselves (no sort and no block tables; the SiLU-and-mul ends
+ *        stage 1) -- same arithmetic, bit-identical outputs.  Otherwise, for W8A8 with
+ *        K <= 16384 on both stages and operands below 4 GiB, every smaller class (the tiny
+ *        one too, with the MFMA tiny kernel) folds into the 128-row class: its 128 x 256
+ *        tile streams the weights better even for short blocks.
+ *   tiny_kernel: MXQ_TINY_MFMA (weights streamed into registers, K reduced by MFMAs, up
+ *        to 8 rows per pass) or MXQ_TINY_GEMV (vector-ALU dot products with a wavefront
+ *        reduction, 4 rows per pass; plain weight layout only -- with tiled weights the
+ *        MFMA kernel runs). */
 #define MXQ_WEIGHTS_FP8_BLOCK 0
 #define MXQ_WEIGHTS_MXFP4 1
 #define MXQ_LAYOUT_PLAIN 0
 #define MXQ_LAYOUT_TILED 1
+#define MXQ_DISPATCH_PER_BLOCK 0
+#define MXQ_DISPATCH_FORCED 1
+#define MXQ_DISPATCH_LAYER_AVERAGE 2
+#define MXQ_TINY_MFMA 0
+#define MXQ_TINY_GEMV 1
+typedef struct mxq_moe_dispatch {
+  int32_t mode;
+  int32_t forced_class;
+  int32_t tiny_max_rows;
+  int32_t tiny_kernel;
+} mxq_moe_dispatch;
 size_t mxq_fused_moe_workspace_size(int64_t M, int64_t H, int64_t I, int32_t E, int32_t topk, int32_t weights,
                                     int32_t act_quant);
 mxq_status mxq_fused_moe_fp8(const void* x, int64_t M, int64_t H, int64_t I, int32_t E, int32_t topk,
                              const int32_t* topk_ids, const float* topk_weights, const void* w1,
                              const float* w1_scale, const void* w2, const float* w2_scale, const float* w1_bias,
-                             int32_t act_quant, int32_t weight_layout, void* out, void* workspace,
-                             size_t workspace_bytes, void* stream);
+                             int32_t act_quant, int32_t weight_layout, const mxq_moe_dispatch* dispatch, void* out,
+                             void* workspace, size_t workspace_bytes, void* stream);
 mxq_status mxq_fused_moe_mxfp4(const void* x, int64_t M, int64_t H, int64_t I, int32_t E, int32_t topk,
                                const int32_t* topk_ids, const float* topk_weights, const void* w1,
                                const void* w1_scale, const void* w2, const void* w2_scale, const float* w1_bias,
-                               int32_t weight_layout, void* out, void* workspace, size_t workspace_bytes,
-                               void* stream);
+                               int32_t weight_layout, const mxq_moe_dispatch* dispatch, void* out, void* workspace,
+                               size_t workspace_bytes, void* stream);
+
+/* Where the fused MoE keeps its intermediates inside the caller's workspace, so that a
+ * caller (a test, a debugger) can read every stage of a call it made.  Fills
+ * offsets[MXQ_MOE_WS_FIELDS] with byte offsets from the workspace base (-1 for a region
+ * this configuration does not use) and returns MXQ_OK, or MXQ_ERR_SHAPE for sizes the
+ * workspace query rejects.  After a call with act_quant = 1 (W8A8) the regions hold:
+ *   SORTED_IDS / EXPERT_IDS / OFFSETS / NUM_BLOCKS  the align tables of mxq_moe_align for
+ *        block_m = offsets[MXQ_MOE_WS_BLOCK_M] (the value, not an offset), without pad
+ *        slots: only slots [offsets[mb], offsets[mb+1]) of block mb are meaningful
+ *        (sorted_ids[mb * block_m + i] is the flat routed id of compact row offsets[mb] + i);
+ *   QX / SX    x quantised as by mxq_per_token_group_quant_fp8 (e4m3 [M, H], fp32 [M, H/128]);
+ *   IC0        bf16 [R, 2I]: stage-1 outputs (+ bias) by compact row;
+ *   IC1_Q / IC1_S  e4m3 [R, I] + fp32 [R, I/128]: mxq_silu_and_mul of IC0, re-quantised;
+ *   Y          fp32 [R, H]: stage-2 outputs by flat routed id t * topk + k.
+ * With bf16 activations (act_quant = 0, and every MXFP4 call) the regions are scratch
+ * whose contents depend on the kernels the dispatch picked (the expert-streaming path
+ * writes neither the tables nor IC0). */
+#define MXQ_MOE_WS_SORTED_IDS 0
+#define MXQ_MOE_WS_EXPERT_IDS 1
+#define MXQ_MOE_WS_OFFSETS 2
+#define MXQ_MOE_WS_NUM_BLOCKS 3
+#define MXQ_MOE_WS_QX 4
+#define MXQ_MOE_WS_SX 5
+#define MXQ_MOE_WS_IC0 6
+#define MXQ_MOE_WS_IC1 7
+#define MXQ_MOE_WS_IC1_Q 8
+#define MXQ_MOE_WS_IC1_S 9
+#define MXQ_MOE_WS_Y 10
+#define MXQ_MOE_WS_BLOCK_M 11
+#define MXQ_MOE_WS_FIELDS 12
+mxq_status mxq_fused_moe_workspace_layout(int64_t M, int64_t H, int64_t I, int32_t E, int32_t topk, int32_t weights,
+                                          int32_t act_quant, int64_t* offsets);
+
+/* ------------------------------------------------------------------ SiLU-and-mul
+ * The activation between the two expert stages (page [A], implementation item 2 and the
+ * moe_fp8.cpp listing: stage 1 writes a 2N-wide gate/up intermediate that the activation
+ * reduces to N columns before stage 2):
+ *   h[r, j] = bf16( silu(g) * u ),  g = ic0[r, j], u = ic0[r, I + j],  silu(g) = g / (1 + exp(-g)),
+ * in fp32 on bf16 inputs.  q == NULL: h is written as bf16 [rows, I] to `out` (contiguous).
+ * q != NULL: h is quantised per row per 128 columns exactly as
+ * mxq_per_token_group_quant_fp8 quantises its input (codes e4m3 [rows, I] to q, scales
+ * fp32 [rows, I/128] to s; `out` is not written and may be NULL) -- the W8A8 path's
+ * re-quantisation of the stage-2 input.
+ *   ic0  bf16 [rows, 2I], row stride ld_in elements (ld_in >= 2I, multiple of 8)
+ *   I must be a multiple of 8 (of 128 when q != NULL).  rows == 0 is a no-op. */
+mxq_status mxq_silu_and_mul(const void* ic0, int64_t rows, int64_t I, int64_t ld_in, void* out, void* q, float* s,
+                            void* stream);
 
 /* ------------------------------------------------------------------ load-time weight relayout
  * Converts routed-expert weights into the tiled layout the MoE kernels stream (page [B]:
@@ -241,34 +326,6 @@ size_t mxq_moe_prepack_scales_size(int64_t E, int64_t N, int64_t groups);
 mxq_status mxq_moe_prepack(const void* w, int64_t E, int64_t N, int64_t row_bytes, void* out, void* stream);
 mxq_status mxq_moe_prepack_scales(const void* s, int64_t E, int64_t N, int64_t groups, void* out, void* stream);
 
-/* Per-block dispatch control for the fused MoE (process-wide, not thread-safe).
- *   mode MXQ_DISPATCH_PER_BLOCK (default): each block's class from its own row count;
- *   mode MXQ_DISPATCH_FORCED: every block runs class `forced_class` (0 = tiny-block kernel,
- *        1 = 16-row, 2 = 32-row, 3 = 64-row, 4 = 128-row MFMA tiles) -- for tests;
- *   mode MXQ_DISPATCH_LAYER_AVERAGE: one class for the whole layer, chosen from
- *        max(1, M * topk / E) rows (the per-layer rule page [A] replaces; for
- *        ablation measurements).
- *   tiny_max_rows: largest block that takes the tiny-block class in per-block mode
- *        (default 16, max 16).  When M <= 2 * tiny_max_rows the tiny class takes every
- *        block (taller ones in several passes); with bf16 activations, the MFMA tiny
- *        kernel, at most 4096 routed rows, E <= 512 and both stages' operands fitting the
- *        kernel's LDS budget, this case runs as two persistent expert-streaming kernels
- *        that group the routed rows by expert themselves (no sort and no block tables;
- *        the SiLU-and-mul ends stage 1) -- same arithmetic, bit-identical outputs.
- *        Otherwise, for W8A8 with K <= 16384 on
- *        both stages, every smaller class (the tiny one too, with the MFMA tiny kernel)
- *        folds into the 128-row class: its 128 x 256 tile streams the weights better even
- *        for short blocks, and no launch runs a handful of blocks.
- *   tiny_kernel: the tiny-block kernel -- MXQ_TINY_MFMA (default: weights streamed into
- *        registers, K reduced by MFMAs, up to 8 rows per pass) or MXQ_TINY_GEMV
- *        (vector-ALU dot products with a wavefront reduction, 4 rows per pass; plain
- *        weight layout only -- with tiled weights the MFMA kernel runs). */
-#define MXQ_DISPATCH_PER_BLOCK 0
-#define MXQ_DISPATCH_FORCED 1
-#define MXQ_DISPATCH_LAYER_AVERAGE 2
-#define MXQ_TINY_MFMA 0
-#define MXQ_TINY_GEMV 1
-mxq_status mxq_moe_set_dispatch(int32_t mode, int32_t forced_class, int32_t tiny_max_rows, int32_t tiny_kernel);
 
 #ifdef __cplusplus
 }

@@ -18,7 +18,9 @@ from .ops import (  # noqa: F401
     fused_moe_workspace,
     moe_prepack,
     moe_prepack_scales,
-    moe_set_dispatch,
+    fused_moe_workspace_layout,
+    silu_and_mul,
+    Dispatch,
 )
 from ._lib import (  # noqa: F401
     LIB_PATH,

@@ -39,6 +39,16 @@ MXQ_TINY_GEMV = 1
 MXQ_LAYOUT_PLAIN = 0
 MXQ_LAYOUT_TILED = 1
 
+# byte offsets reported by mxq_fused_moe_workspace_layout
+MOE_WS_FIELDS = ("sorted_ids", "expert_ids", "offsets", "num_blocks", "qx", "sx", "ic0", "ic1", "ic1_q", "ic1_s",
+                 "y", "block_m")
+
+
+class MoeDispatch(C.Structure):
+    """struct mxq_moe_dispatch (per-call dispatch of the fused MoE)."""
+    _fields_ = [("mode", C.c_int32), ("forced_class", C.c_int32), ("tiny_max_rows", C.c_int32),
+                ("tiny_kernel", C.c_int32)]
+
 _p = C.c_void_p
 _i32 = C.c_int32
 _i64 = C.c_int64
@@ -55,19 +65,20 @@ SIGNATURES = {
                                    _p, _i64, _i64, _p]),
     "mxq_block_fp8_linear_workspace_size": (_sz, [_i64, _i64, _i32]),
     "mxq_block_fp8_linear": (_i32, [_p, _i32, _p, _i64, _i64, _i64, _p, _i64, _p, _i64, _i64, _i32, _i32,
-                                     _p, _i32, _p, _i64, _p, _sz, _p]),
+                                     _p, _i32, _p, _i32, _i64, _p, _sz, _p]),
     "mxq_moe_max_blocks": (_i64, [_i64, _i32, _i32, _i32]),
     "mxq_moe_align": (_i32, [_p, _i64, _i32, _i32, _i32, _p, _p, _p, _p, _p]),
     "mxq_fused_moe_workspace_size": (_sz, [_i64, _i64, _i64, _i32, _i32, _i32, _i32]),
-    "mxq_fused_moe_fp8": (_i32, [_p, _i64, _i64, _i64, _i32, _i32, _p, _p, _p, _p, _p, _p, _p, _i32, _i32, _p,
-                                  _p, _sz, _p]),
-    "mxq_fused_moe_mxfp4": (_i32, [_p, _i64, _i64, _i64, _i32, _i32, _p, _p, _p, _p, _p, _p, _p, _i32, _p, _p,
-                                    _sz, _p]),
+    "mxq_fused_moe_fp8": (_i32, [_p, _i64, _i64, _i64, _i32, _i32, _p, _p, _p, _p, _p, _p, _p, _i32, _i32,
+                                  C.POINTER(MoeDispatch), _p, _p, _sz, _p]),
+    "mxq_fused_moe_mxfp4": (_i32, [_p, _i64, _i64, _i64, _i32, _i32, _p, _p, _p, _p, _p, _p, _p, _i32,
+                                    C.POINTER(MoeDispatch), _p, _p, _sz, _p]),
+    "mxq_fused_moe_workspace_layout": (_i32, [_i64, _i64, _i64, _i32, _i32, _i32, _i32, C.POINTER(_i64)]),
+    "mxq_silu_and_mul": (_i32, [_p, _i64, _i64, _i64, _p, _p, _p, _p]),
     "mxq_moe_prepack_size": (_sz, [_i64, _i64, _i64]),
     "mxq_moe_prepack_scales_size": (_sz, [_i64, _i64, _i64]),
     "mxq_moe_prepack": (_i32, [_p, _i64, _i64, _i64, _p, _p]),
     "mxq_moe_prepack_scales": (_i32, [_p, _i64, _i64, _i64, _p, _p]),
-    "mxq_moe_set_dispatch": (_i32, [_i32, _i32, _i32, _i32]),
 }
 
 _lock = threading.Lock()

@@ -4,7 +4,6 @@
 #include <string.h>
 
 #include <atomic>
-#include <mutex>
 
 #include "../../include/mxq.h"
 #include "kernels.hpp"
@@ -39,12 +38,6 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
     if (_s != MXQ_OK) return _s;     \
   } while (0)
 
-// MoE dispatch state (process-wide)
-std::mutex g_dispatch_mu;
-int g_dispatch_mode = MXQ_DISPATCH_PER_BLOCK;
-int g_forced_class = 0;
-int g_tiny_max_rows = 16;
-int g_tiny_kernel = MXQ_TINY_MFMA;
 constexpr size_t kSkinnyMaxLds = 64 * 1024;
 // Expert-streaming path: routing tables and two activation buffers per workgroup in LDS, at
 // most kStreamMaxLds so that two or more workgroups share a compute unit.
@@ -60,6 +53,25 @@ constexpr int kMoeBlockM = 128;
 constexpr int kNumClasses = 5;  // tiny-block kernel, 16-, 32-, 64-, 128-row MFMA tiles
 constexpr int kClassTile[kNumClasses] = {-1, 3, 2, 1, 0};  // launcher tile index per class
 constexpr int kClassRows[kNumClasses] = {16, 16, 32, 64, 128};  // [0] is set at run time
+
+// The dispatch a call runs with: the caller's mxq_moe_dispatch, or the defaults for NULL.
+mxq_status read_dispatch(const mxq_moe_dispatch* d, mxq_moe_dispatch& out) {
+  out = mxq_moe_dispatch{MXQ_DISPATCH_PER_BLOCK, 0, 16, MXQ_TINY_MFMA};
+  if (!d) return MXQ_OK;
+  if (d->mode < MXQ_DISPATCH_PER_BLOCK || d->mode > MXQ_DISPATCH_LAYER_AVERAGE) return MXQ_ERR_ARG;
+  if (d->tiny_kernel != MXQ_TINY_MFMA && d->tiny_kernel != MXQ_TINY_GEMV) return MXQ_ERR_ARG;
+  if (d->forced_class < 0 || d->forced_class >= kNumClasses) return MXQ_ERR_ARG;
+  if (d->tiny_max_rows < 0 || d->tiny_max_rows > 16) return MXQ_ERR_ARG;
+  out = *d;
+  return MXQ_OK;
+}
+
+// Operands the 128 x 256 direct-to-LDS tile addresses with 32-bit byte offsets: the
+// activation rows of both stages (x / ic1 rows) and one expert's weights.
+bool big_tile_offsets_fit(int64_t M, int64_t R, int64_t H, int64_t I) {
+  constexpr int64_t k4G = int64_t(1) << 32;
+  return M * H < k4G && R * I < k4G && 2 * I * H < k4G;
+}
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
@@ -132,20 +144,19 @@ int64_t class_bound(int c, int64_t R, int32_t E, int64_t max_blocks, const Class
 // too (the blocks of at most a few rows then cost no separate launch: measured equal at 512
 // tokens and 4-5 % faster at 4096 with uniform routing).  With bf16 activations the next
 // classes have no such tile, and taking a few passes in the tiny kernel measured faster.
-ClassPolicy make_policy(int64_t M, int64_t R, int32_t E, bool big_tile) {
-  std::lock_guard<std::mutex> lk(g_dispatch_mu);
+ClassPolicy make_policy(int64_t M, int64_t R, int32_t E, bool big_tile, const mxq_moe_dispatch& dc) {
   ClassPolicy pol{};
   pol.n_classes = kNumClasses;
   pol.forced = -1;
-  pol.bound[0] = g_tiny_max_rows;
+  pol.bound[0] = dc.tiny_max_rows;
   for (int c = 1; c < kNumClasses; ++c) pol.bound[c] = kClassRows[c];
   // When M is at most twice the tiny-block bound the tiny class takes every block (an expert
   // holds at most M rows): blocks of bound..M rows take a few passes of the weight-streaming
   // kernel instead of a mostly empty launch of the next tile class.
-  if (g_tiny_max_rows > 0 && M <= 2 * int64_t(g_tiny_max_rows)) {
+  if (dc.tiny_max_rows > 0 && M <= 2 * int64_t(dc.tiny_max_rows)) {
     pol.bound[0] = std::max<int>(pol.bound[0], int(M));
   } else if (big_tile) {
-    if (g_tiny_kernel == MXQ_TINY_MFMA) pol.bound[0] = 0;
+    if (dc.tiny_kernel == MXQ_TINY_MFMA) pol.bound[0] = 0;
     for (int c = 1; c < kNumClasses - 1; ++c) pol.bound[c] = pol.bound[0];
   }
   pol.n_live = kNumClasses;
@@ -154,15 +165,15 @@ ClassPolicy make_policy(int64_t M, int64_t R, int32_t E, bool big_tile) {
       pol.n_live = c;
       break;
     }
-  if (g_dispatch_mode == MXQ_DISPATCH_FORCED) {
-    pol.forced = g_forced_class;
+  if (dc.mode == MXQ_DISPATCH_FORCED) {
+    pol.forced = dc.forced_class;
     pol.n_live = kNumClasses;
-  } else if (g_dispatch_mode == MXQ_DISPATCH_LAYER_AVERAGE) {
+  } else if (dc.mode == MXQ_DISPATCH_LAYER_AVERAGE) {
     // the per-layer rule maps the average onto the plain class bounds (no folding)
     const int64_t avg = std::max<int64_t>(1, R / std::max<int32_t>(E, 1));
     int c = kNumClasses - 1;
     for (int i = 0; i < kNumClasses - 1; ++i)
-      if (avg <= (i == 0 ? g_tiny_max_rows : kClassRows[i])) { c = i; break; }
+      if (avg <= (i == 0 ? dc.tiny_max_rows : kClassRows[i])) { c = i; break; }
     pol.forced = c;
     pol.n_live = kNumClasses;
   }
@@ -171,19 +182,17 @@ ClassPolicy make_policy(int64_t M, int64_t R, int32_t E, bool big_tile) {
 
 mxq_status run_moe(const void* x, int64_t M, int64_t H, int64_t I, int32_t E, int32_t topk, const int32_t* ids,
                    const float* wts, const void* w1, const void* w1s, const void* w2, const void* w2s,
-                   const float* b1, int wfmt, bool act_quant, bool tiled, void* out, void* ws, size_t ws_bytes,
-                   hipStream_t st) {
+                   const float* b1, int wfmt, bool act_quant, bool tiled, const mxq_moe_dispatch& dc, void* out,
+                   void* ws, size_t ws_bytes, hipStream_t st) {
   const int64_t R = M * topk;
   if (R == 0) return MXQ_OK;
   const int64_t mbk = mxq_moe_max_blocks(M, topk, E, kMoeBlockM);
   MoeWorkspace w = carve_moe(ws, M, H, I, E, topk, act_quant);
   if (!ws || ws_bytes < w.bytes) return MXQ_ERR_WORKSPACE;
-  const ClassPolicy pol = make_policy(M, R, E, act_quant && H <= 16384 && I <= 16384);
-  int tiny;
-  {
-    std::lock_guard<std::mutex> lk(g_dispatch_mu);
-    tiny = g_tiny_kernel;
-  }
+  // the 128 x 256 W8A8 tile: K <= 16384 on both stages and operand offsets below 4 GiB
+  const bool big_tile = act_quant && H <= 16384 && I <= 16384 && big_tile_offsets_fit(M, R, H, I);
+  const ClassPolicy pol = make_policy(M, R, E, big_tile, dc);
+  const int tiny = dc.tiny_kernel;
   const bool mx = wfmt == W_E2M1_MX;
   const int wfmt_w16 = mx ? W_E2M1_MX : W_E4M3_BLOCK;
 
@@ -308,7 +317,7 @@ mxq_status run_moe(const void* x, int64_t M, int64_t H, int64_t I, int32_t E, in
     g2.a_silu = 1;
   }
   for (int stage = 0; stage < 2; ++stage) {
-    if (stage == 1 && !fuse_silu) launch_silu_mul(w.ic0, R, I, w.ic1, w.ic1_q, w.ic1_s, st);
+    if (stage == 1 && !fuse_silu) launch_silu_mul(w.ic0, R, I, 2 * I, w.ic1, w.ic1_q, w.ic1_s, st);
     GemmArgs& g = stage == 0 ? g1 : g2;
     const int mode = stage == 0 ? ROWS_GATHER_TOK : ROWS_COMPACT_IN;
     const bool out_f32 = stage == 1;
@@ -330,7 +339,7 @@ mxq_status run_moe(const void* x, int64_t M, int64_t H, int64_t I, int32_t E, in
         launch_gemv(g, wfmt_w16, act_quant, mode, out_f32, ub, st);
       else if (c == 0 && skinny_fits)
         launch_skinny(g, wfmt_w16, act_quant, mode, out_f32, ub, st);
-      else if (act_quant && c == kNumClasses - 1 && g.K <= 16384)
+      else if (big_tile && c == kNumClasses - 1)
         // blocks of 65..128 rows: the 128 x 256 three-stage direct-to-LDS tile
         launch_gemm_w8a8_big(g, mode, 1, out_f32, ub, st);
       else if (act_quant)
@@ -370,7 +379,7 @@ const char* mxq_status_string(mxq_status s) {
   }
 }
 
-int32_t mxq_abi_version(void) { return 4; }
+int32_t mxq_abi_version(void) { return 5; }
 
 mxq_status mxq_init(int32_t device) {
   if (hipSetDevice(device) != hipSuccess) return MXQ_ERR_ARCH;
@@ -464,10 +473,11 @@ size_t mxq_block_fp8_linear_workspace_size(int64_t M, int64_t K, int32_t a_dtype
 mxq_status mxq_block_fp8_linear(const void* A, int32_t a_dtype, const float* a_scale, int64_t M, int64_t K,
                                 int64_t lda, const void* W, int64_t N, const float* w_scale, int64_t ws_stride0,
                                 int64_t ws_stride1, int32_t block_n, int32_t block_k, const void* bias,
-                                int32_t bias_dtype, void* out, int64_t ldo, void* workspace, size_t workspace_bytes,
-                                void* stream) {
+                                int32_t bias_dtype, void* out, int32_t out_dtype, int64_t ldo, void* workspace,
+                                size_t workspace_bytes, void* stream) {
   if (block_k != 128 || (block_n != 1 && block_n != 128)) return MXQ_ERR_BLOCK;
   if (a_dtype != MXQ_DTYPE_BF16 && a_dtype != MXQ_DTYPE_E4M3) return MXQ_ERR_DTYPE;
+  if (out_dtype != MXQ_DTYPE_BF16) return MXQ_ERR_DTYPE;
   if (bias && bias_dtype != MXQ_DTYPE_F32 && bias_dtype != MXQ_DTYPE_BF16) return MXQ_ERR_DTYPE;
   if (M < 0 || N < 0 || K < 0 || K % 128 != 0 || lda < K || ldo < N) return MXQ_ERR_SHAPE;
   if (a_dtype == MXQ_DTYPE_BF16 ? (lda % 8 != 0) : (lda % 16 != 0)) return MXQ_ERR_SHAPE;
@@ -547,6 +557,44 @@ size_t mxq_fused_moe_workspace_size(int64_t M, int64_t H, int64_t I, int32_t E, 
   return carve_moe(nullptr, M, H, I, E, topk, act_quant != 0).bytes;
 }
 
+mxq_status mxq_fused_moe_workspace_layout(int64_t M, int64_t H, int64_t I, int32_t E, int32_t topk, int32_t weights,
+                                          int32_t act_quant, int64_t* offsets) {
+  if (M <= 0 || H <= 0 || I <= 0 || E <= 0 || topk <= 0) return MXQ_ERR_SHAPE;
+  if (!offsets) return MXQ_ERR_NULL;
+  const bool aq = act_quant != 0 && weights == MXQ_WEIGHTS_FP8_BLOCK;
+  // carve from a fake non-null base so every used region gets its offset
+  uint8_t* const base = reinterpret_cast<uint8_t*>(uintptr_t(1) << 20);
+  const MoeWorkspace w = carve_moe(base, M, H, I, E, topk, aq);
+  auto off = [&](const void* p) -> int64_t { return p ? int64_t(static_cast<const uint8_t*>(p) - base) : -1; };
+  offsets[MXQ_MOE_WS_SORTED_IDS] = off(w.sorted_ids);
+  offsets[MXQ_MOE_WS_EXPERT_IDS] = off(w.expert_ids);
+  offsets[MXQ_MOE_WS_OFFSETS] = off(w.offsets);
+  offsets[MXQ_MOE_WS_NUM_BLOCKS] = off(w.num_blocks);
+  offsets[MXQ_MOE_WS_QX] = off(w.qx);
+  offsets[MXQ_MOE_WS_SX] = off(w.sx);
+  offsets[MXQ_MOE_WS_IC0] = off(w.ic0);
+  offsets[MXQ_MOE_WS_IC1] = off(w.ic1);
+  offsets[MXQ_MOE_WS_IC1_Q] = off(w.ic1_q);
+  offsets[MXQ_MOE_WS_IC1_S] = off(w.ic1_s);
+  offsets[MXQ_MOE_WS_Y] = off(w.y);
+  offsets[MXQ_MOE_WS_BLOCK_M] = kMoeBlockM;
+  return MXQ_OK;
+}
+
+mxq_status mxq_silu_and_mul(const void* ic0, int64_t rows, int64_t I, int64_t ld_in, void* out, void* q, float* s,
+                            void* stream) {
+  if (rows < 0 || I <= 0 || I % 8 != 0 || ld_in < 2 * I || ld_in % 8 != 0) return MXQ_ERR_SHAPE;
+  if (q && I % 128 != 0) return MXQ_ERR_SHAPE;
+  if (rows == 0) return MXQ_OK;
+  if (!ic0 || (q ? !s : !out)) return MXQ_ERR_NULL;
+  if (!aligned16(ic0) || (!q && !aligned16(out)) || (q && (reinterpret_cast<uintptr_t>(q) & 7u)))
+    return MXQ_ERR_SHAPE;
+  MXQ_TRY(check_arch());
+  launch_silu_mul(static_cast<const uint16_t*>(ic0), rows, I, ld_in, static_cast<uint16_t*>(q ? nullptr : out),
+                  static_cast<uint8_t*>(q), s, static_cast<hipStream_t>(stream));
+  return launch_status();
+}
+
 static mxq_status moe_common_checks(const void* x, int64_t M, int64_t H, int64_t I, int32_t E, int32_t topk,
                                     const int32_t* ids, const float* wts, const void* w1, const void* w1s,
                                     const void* w2, const void* w2s, void* out) {
@@ -560,29 +608,33 @@ static mxq_status moe_common_checks(const void* x, int64_t M, int64_t H, int64_t
 mxq_status mxq_fused_moe_fp8(const void* x, int64_t M, int64_t H, int64_t I, int32_t E, int32_t topk,
                              const int32_t* topk_ids, const float* topk_weights, const void* w1,
                              const float* w1_scale, const void* w2, const float* w2_scale, const float* w1_bias,
-                             int32_t act_quant, int32_t weight_layout, void* out, void* workspace,
-                             size_t workspace_bytes, void* stream) {
+                             int32_t act_quant, int32_t weight_layout, const mxq_moe_dispatch* dispatch, void* out,
+                             void* workspace, size_t workspace_bytes, void* stream) {
   if (H % 128 != 0 || I % 128 != 0) return MXQ_ERR_SHAPE;
   if (act_quant != 0 && act_quant != 1) return MXQ_ERR_ARG;
   if (weight_layout != MXQ_LAYOUT_PLAIN && weight_layout != MXQ_LAYOUT_TILED) return MXQ_ERR_ARG;
+  mxq_moe_dispatch dc;
+  MXQ_TRY(read_dispatch(dispatch, dc));
   MXQ_TRY(moe_common_checks(x, M, H, I, E, topk, topk_ids, topk_weights, w1, w1_scale, w2, w2_scale, out));
   if (M == 0) return MXQ_OK;
   return run_moe(x, M, H, I, E, topk, topk_ids, topk_weights, w1, w1_scale, w2, w2_scale, w1_bias, W_E4M3_BLOCK,
-                 act_quant != 0, weight_layout == MXQ_LAYOUT_TILED, out, workspace, workspace_bytes,
+                 act_quant != 0, weight_layout == MXQ_LAYOUT_TILED, dc, out, workspace, workspace_bytes,
                  static_cast<hipStream_t>(stream));
 }
 
 mxq_status mxq_fused_moe_mxfp4(const void* x, int64_t M, int64_t H, int64_t I, int32_t E, int32_t topk,
                                const int32_t* topk_ids, const float* topk_weights, const void* w1,
                                const void* w1_scale, const void* w2, const void* w2_scale, const float* w1_bias,
-                               int32_t weight_layout, void* out, void* workspace, size_t workspace_bytes,
-                               void* stream) {
+                               int32_t weight_layout, const mxq_moe_dispatch* dispatch, void* out, void* workspace,
+                               size_t workspace_bytes, void* stream) {
   if (H % 32 != 0 || I % 32 != 0) return MXQ_ERR_SHAPE;
   if (weight_layout != MXQ_LAYOUT_PLAIN && weight_layout != MXQ_LAYOUT_TILED) return MXQ_ERR_ARG;
+  mxq_moe_dispatch dc;
+  MXQ_TRY(read_dispatch(dispatch, dc));
   MXQ_TRY(moe_common_checks(x, M, H, I, E, topk, topk_ids, topk_weights, w1, w1_scale, w2, w2_scale, out));
   if (M == 0) return MXQ_OK;
   return run_moe(x, M, H, I, E, topk, topk_ids, topk_weights, w1, w1_scale, w2, w2_scale, w1_bias, W_E2M1_MX, false,
-                 weight_layout == MXQ_LAYOUT_TILED, out, workspace, workspace_bytes,
+                 weight_layout == MXQ_LAYOUT_TILED, dc, out, workspace, workspace_bytes,
                  static_cast<hipStream_t>(stream));
 }
 
@@ -614,19 +666,6 @@ mxq_status mxq_moe_prepack_scales(const void* s, int64_t E, int64_t N, int64_t g
   launch_prepack_s(static_cast<const uint8_t*>(s), E, N, groups, static_cast<uint8_t*>(out),
                    static_cast<hipStream_t>(stream));
   return launch_status();
-}
-
-mxq_status mxq_moe_set_dispatch(int32_t mode, int32_t forced_class, int32_t tiny_max_rows, int32_t tiny_kernel) {
-  if (mode < MXQ_DISPATCH_PER_BLOCK || mode > MXQ_DISPATCH_LAYER_AVERAGE) return MXQ_ERR_ARG;
-  if (tiny_kernel != MXQ_TINY_MFMA && tiny_kernel != MXQ_TINY_GEMV) return MXQ_ERR_ARG;
-  if (forced_class < 0 || forced_class >= kNumClasses) return MXQ_ERR_ARG;
-  if (tiny_max_rows < 0 || tiny_max_rows > 16) return MXQ_ERR_ARG;
-  std::lock_guard<std::mutex> lk(g_dispatch_mu);
-  g_dispatch_mode = mode;
-  g_forced_class = forced_class;
-  g_tiny_max_rows = tiny_max_rows;
-  g_tiny_kernel = tiny_kernel;
-  return MXQ_OK;
 }
 
 }  // extern "C"

@@ -54,9 +54,12 @@ __device__ __forceinline__ void e4m3x4_to_bf16(uint32_t v, uint32_t& lo, uint32_
   hi = __builtin_bit_cast(uint32_t, b);
 }
 
-// e8m0 exponent -> fp32 power of two (0 maps to 0.0f: 2^-127 is below what
-// the bf16 products of this path can resolve).
-__device__ __forceinline__ float e8m0_to_f32(uint32_t e) { return __uint_as_float(e << 23); }
+// e8m0 exponent -> fp32 2^(e - 127), the OCP MX scale value: code 0 is 2^-127 (the fp32
+// subnormal 0x00400000, never flushed here), code 0xFF is NaN.
+__device__ __forceinline__ float e8m0_to_f32(uint32_t e) {
+  const uint32_t bits = e == 0 ? 0x00400000u : (e == 0xffu ? 0x7fc00000u : e << 23);
+  return __uint_as_float(bits);
+}
 
 // Eight e2m1 nibbles (one dword, low nibble first) times a power-of-two scale
 // -> eight bf16 (four dwords).  Exact while the scaled values stay in range.

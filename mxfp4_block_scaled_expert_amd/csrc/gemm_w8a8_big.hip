@@ -168,8 +168,10 @@ __global__ __launch_bounds__((BigCfg<BM, BN, NW, NS>::THREADS)) void gemm_w8a8_b
     }
   };
   const int sw_blk = (wn * 64) >> 7;  // the 128-wide scale block of this wave's columns
-  const bool vec_store = (a.ldo & 3) == 0;   // 16-byte fp32 stores
-  const bool vec8_store = (a.ldo & 7) == 0;  // 16-byte bf16 stores
+  // 16-byte stores need 16-byte aligned rows: the row stride and the base address
+  const bool out_al16 = (reinterpret_cast<uintptr_t>(a.out) & 15) == 0;
+  const bool vec_store = out_al16 && (a.ldo & 3) == 0;   // 16-byte fp32 stores
+  const bool vec8_store = out_al16 && (a.ldo & 7) == 0;  // 16-byte bf16 stores
 
   for (int m_base = 0; m_base < t.m_total; m_base += BM) {
     const int m_size = min(BM, t.m_total - m_base);

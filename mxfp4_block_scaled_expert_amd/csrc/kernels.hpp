@@ -142,8 +142,9 @@ void launch_moe_align(const int32_t* topk_ids, int64_t M, int32_t topk, int32_t 
                       int32_t* class_counts, bool write_pads, hipStream_t stream);
 
 // ic1 = bf16(silu(gate) * up) over compact rows; optionally re-quantised 1x128 to e4m3.
-void launch_silu_mul(const uint16_t* ic0, int64_t rows, int64_t inter, uint16_t* ic1_bf16, uint8_t* ic1_q,
-                     float* ic1_s, hipStream_t stream);
+// ic0 rows are `ld_in` elements apart; ic1 / q / s are contiguous.
+void launch_silu_mul(const uint16_t* ic0, int64_t rows, int64_t inter, int64_t ld_in, uint16_t* ic1_bf16,
+                     uint8_t* ic1_q, float* ic1_s, hipStream_t stream);
 
 // out[t] = bf16(sum_k w[t,k] * y[t*topk+k]).
 // Rows whose expert id lies outside [0, E) are skipped.

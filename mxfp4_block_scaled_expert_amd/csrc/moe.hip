@@ -285,8 +285,8 @@ void launch_moe_align(const int32_t* topk_ids, int64_t M, int32_t topk, int32_t 
 // products are re-quantised per 128 columns into q [rows, I] + s [rows, I/128].
 template <bool QUANT>
 __global__ __launch_bounds__(256) void silu_mul_kernel(const uint16_t* __restrict__ ic0, int64_t rows, int64_t inter,
-                                                       uint16_t* __restrict__ ic1, uint8_t* __restrict__ q,
-                                                       float* __restrict__ s) {
+                                                       int64_t ld_in, uint16_t* __restrict__ ic1,
+                                                       uint8_t* __restrict__ q, float* __restrict__ s) {
   const int64_t per_row = inter / 8;
   const int64_t idx = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
   const bool valid = idx < rows * per_row;
@@ -295,8 +295,8 @@ __global__ __launch_bounds__(256) void silu_mul_kernel(const uint16_t* __restric
   const int64_t col = (ii - row * per_row) * 8;
   uint4 g = make_uint4(0, 0, 0, 0), u = make_uint4(0, 0, 0, 0);
   if (valid) {
-    g = *reinterpret_cast<const uint4*>(ic0 + row * 2 * inter + col);
-    u = *reinterpret_cast<const uint4*>(ic0 + row * 2 * inter + inter + col);
+    g = *reinterpret_cast<const uint4*>(ic0 + row * ld_in + col);
+    u = *reinterpret_cast<const uint4*>(ic0 + row * ld_in + inter + col);
   }
   const uint4 h = silu_mul8(g, u);
   if (!QUANT) {
@@ -312,17 +312,17 @@ __global__ __launch_bounds__(256) void silu_mul_kernel(const uint16_t* __restric
   }
 }
 
-void launch_silu_mul(const uint16_t* ic0, int64_t rows, int64_t inter, uint16_t* ic1_bf16, uint8_t* ic1_q,
-                     float* ic1_s, hipStream_t stream) {
+void launch_silu_mul(const uint16_t* ic0, int64_t rows, int64_t inter, int64_t ld_in, uint16_t* ic1_bf16,
+                     uint8_t* ic1_q, float* ic1_s, hipStream_t stream) {
   const int64_t threads = rows * (inter / 8);
   if (threads == 0) return;
   const unsigned grid = unsigned(cdiv(threads, 256));
   if (ic1_q)
-    hipLaunchKernelGGL(silu_mul_kernel<true>, dim3(grid), dim3(256), 0, stream, ic0, rows, inter, ic1_bf16, ic1_q,
-                       ic1_s);
+    hipLaunchKernelGGL(silu_mul_kernel<true>, dim3(grid), dim3(256), 0, stream, ic0, rows, inter, ld_in, ic1_bf16,
+                       ic1_q, ic1_s);
   else
-    hipLaunchKernelGGL(silu_mul_kernel<false>, dim3(grid), dim3(256), 0, stream, ic0, rows, inter, ic1_bf16, ic1_q,
-                       ic1_s);
+    hipLaunchKernelGGL(silu_mul_kernel<false>, dim3(grid), dim3(256), 0, stream, ic0, rows, inter, ld_in, ic1_bf16,
+                       ic1_q, ic1_s);
 }
 
 // ---------------------------------------------------------------- combine

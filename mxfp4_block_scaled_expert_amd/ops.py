@@ -20,11 +20,15 @@ Semantics carried over from the source pages:
 
 from __future__ import annotations
 
-from typing import Optional, Sequence, Tuple
+from typing import Dict, NamedTuple, Optional, Sequence, Tuple
+
+import ctypes
 
 import torch
 
 from . import _lib as L
+
+C_i64 = ctypes.c_int64
 
 _E4M3 = torch.float8_e4m3fn
 
@@ -208,8 +212,8 @@ def block_fp8_linear(x: torch.Tensor, weight: torch.Tensor, block_size: Sequence
     ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=x.device)
     st = lib.mxq_block_fp8_linear(a.data_ptr(), a_dtype, _ptr(a_scale), M, K, a.stride(0), w.data_ptr(), N,
                                   weight_scale.data_ptr(), weight_scale.stride(0), weight_scale.stride(1), block_n,
-                                  block_k, _ptr(b), _bias_dtype(b), out.data_ptr(), N, ws.data_ptr(), ws_bytes,
-                                  _stream())
+                                  block_k, _ptr(b), _bias_dtype(b), out.data_ptr(), L.MXQ_DTYPE_BF16, N,
+                                  ws.data_ptr(), ws_bytes, _stream())
     L.check("mxq_block_fp8_linear", st)
     return out.view(*x.shape[:-1], N)
 
@@ -251,6 +255,54 @@ def fused_moe_workspace(M: int, H: int, I: int, E: int, topk: int, weights: int,
                         device) -> torch.Tensor:
     n = L.load().mxq_fused_moe_workspace_size(M, H, I, E, topk, weights, int(act_quant))
     return torch.empty(max(n, 1), dtype=torch.uint8, device=device)
+
+
+def fused_moe_workspace_layout(M: int, H: int, I: int, E: int, topk: int, weights: int,
+                               act_quant: bool) -> Dict[str, int]:
+    """Byte offsets of the fused MoE's intermediates in its workspace (-1: region unused),
+    plus ``block_m`` (``mxq_fused_moe_workspace_layout``)."""
+    arr = (C_i64 * len(L.MOE_WS_FIELDS))()
+    L.check("mxq_fused_moe_workspace_layout",
+            L.load().mxq_fused_moe_workspace_layout(M, H, I, E, topk, weights, int(act_quant), arr))
+    return {k: int(arr[i]) for i, k in enumerate(L.MOE_WS_FIELDS)}
+
+
+class Dispatch(NamedTuple):
+    """Per-call dispatch of the fused MoE (``struct mxq_moe_dispatch``); None = the defaults."""
+    mode: int = L.MXQ_DISPATCH_PER_BLOCK
+    forced_class: int = 0
+    tiny_max_rows: int = 16
+    tiny_kernel: int = L.MXQ_TINY_MFMA
+
+
+def _dispatch(d: Optional[Dispatch]):
+    if d is None:
+        return None
+    return ctypes.byref(L.MoeDispatch(int(d.mode), int(d.forced_class), int(d.tiny_max_rows), int(d.tiny_kernel)))
+
+
+def silu_and_mul(ic0: torch.Tensor, quant: bool = False):
+    """bf16 [rows, 2I] (gate | up) -> bf16 [rows, I] = silu(gate) * up, or with ``quant`` the
+    e4m3 codes [rows, I] and fp32 scales [rows, I/128] of that product (1x128 groups)."""
+    if ic0.dtype != torch.bfloat16 or ic0.dim() != 2 or ic0.shape[1] % 2:
+        raise ValueError("ic0 must be bf16 [rows, 2I]")
+    _require_cuda(ic0)
+    if ic0.stride(-1) != 1 or ic0.data_ptr() % 16 or ic0.stride(0) % 8:
+        ic0 = ic0.contiguous()
+    rows, two_i = ic0.shape
+    I = two_i // 2
+    lib = L.load()
+    if quant:
+        q = torch.empty((rows, I), dtype=torch.uint8, device=ic0.device)
+        s = torch.empty((rows, I // 128), dtype=torch.float32, device=ic0.device)
+        st = lib.mxq_silu_and_mul(ic0.data_ptr(), rows, I, ic0.stride(0), None, q.data_ptr(), s.data_ptr(),
+                                  _stream())
+        L.check("mxq_silu_and_mul", st)
+        return q.view(_E4M3), s
+    out = torch.empty((rows, I), dtype=torch.bfloat16, device=ic0.device)
+    st = lib.mxq_silu_and_mul(ic0.data_ptr(), rows, I, ic0.stride(0), out.data_ptr(), None, None, _stream())
+    L.check("mxq_silu_and_mul", st)
+    return out
 
 
 _LAYOUTS = {"plain": L.MXQ_LAYOUT_PLAIN, "tiled": L.MXQ_LAYOUT_TILED}
@@ -304,7 +356,7 @@ def moe_prepack_scales(s: torch.Tensor) -> torch.Tensor:
 
 def fused_moe_fp8(x, topk_ids, topk_weights, w1, w1_scale, w2, w2_scale, w1_bias=None, act_quant=False,
                   workspace: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
-                  weight_layout: str = "plain") -> torch.Tensor:
+                  weight_layout: str = "plain", dispatch: Optional[Dispatch] = None) -> torch.Tensor:
     """Routed MoE with block-FP8 experts (W8A16, or W8A8 with ``act_quant``) -> bf16 [M, H].
 
     ``weight_layout="tiled"``: ``w1`` / ``w2`` come from :func:`moe_prepack`."""
@@ -331,14 +383,15 @@ def fused_moe_fp8(x, topk_ids, topk_weights, w1, w1_scale, w2, w2_scale, w1_bias
         workspace = fused_moe_workspace(M, H, I, E, topk, L.MXQ_WEIGHTS_FP8_BLOCK, act_quant, x.device)
     st = L.load().mxq_fused_moe_fp8(x.data_ptr(), M, H, I, E, topk, ids.data_ptr(), wts.data_ptr(), w1.data_ptr(),
                                     s1.data_ptr(), w2.data_ptr(), s2.data_ptr(), _ptr(b1), int(bool(act_quant)),
-                                    layout, out.data_ptr(), workspace.data_ptr(), workspace.numel(), _stream())
+                                    layout, _dispatch(dispatch), out.data_ptr(), workspace.data_ptr(),
+                                    workspace.numel(), _stream())
     L.check("mxq_fused_moe_fp8", st)
     return out
 
 
 def fused_moe_mxfp4(x, topk_ids, topk_weights, w1, w1_scale, w2, w2_scale, w1_bias=None,
                     workspace: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
-                    weight_layout: str = "plain") -> torch.Tensor:
+                    weight_layout: str = "plain", dispatch: Optional[Dispatch] = None) -> torch.Tensor:
     """Routed MoE with MXFP4 experts (packed e2m1 + e8m0 per 32), bf16 activations -> bf16 [M, H].
 
     ``weight_layout="tiled"``: weights from :func:`moe_prepack`, scales from :func:`moe_prepack_scales`."""
@@ -372,11 +425,7 @@ def fused_moe_mxfp4(x, topk_ids, topk_weights, w1, w1_scale, w2, w2_scale, w1_bi
         workspace = fused_moe_workspace(M, H, I, E, topk, L.MXQ_WEIGHTS_MXFP4, False, x.device)
     st = L.load().mxq_fused_moe_mxfp4(x.data_ptr(), M, H, I, E, topk, ids.data_ptr(), wts.data_ptr(),
                                       w1.data_ptr(), s1.data_ptr(), w2.data_ptr(), s2.data_ptr(), _ptr(b1),
-                                      layout, out.data_ptr(), workspace.data_ptr(), workspace.numel(), _stream())
+                                      layout, _dispatch(dispatch), out.data_ptr(), workspace.data_ptr(),
+                                      workspace.numel(), _stream())
     L.check("mxq_fused_moe_mxfp4", st)
     return out
-
-
-def moe_set_dispatch(mode: int = L.MXQ_DISPATCH_PER_BLOCK, forced_class: int = 0, tiny_max_rows: int = 16,
-                     tiny_kernel: int = L.MXQ_TINY_MFMA) -> None:
-    L.check("mxq_moe_set_dispatch", L.load().mxq_moe_set_dispatch(mode, forced_class, tiny_max_rows, tiny_kernel))

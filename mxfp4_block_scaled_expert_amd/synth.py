@@ -1,22 +1,28 @@
 """Seeded synthetic inputs shared by the tests, the smoke check and the bench.
 
-This module draws numbers and nothing else: it holds none of the path's
-arithmetic (no quantiser, no GEMM, no routing-to-blocks logic).  Quantised
-weights are drawn directly as codes plus scales of the magnitude the source
-workloads describe, so neither the HIP library nor the oracle depends on it
-for anything but its random draws.
+This module draws numbers and prepares weights the way a checkpoint would hold
+them; it holds none of the path's arithmetic (no activation quantiser, no
+GEMM, no routing-to-blocks logic) and neither the HIP library nor the oracle
+calls it.  The weight preparation below (block FP8 and MXFP4 weights from
+Gaussian draws) is offline work of a model's weight conversion, not a step of
+the path: the path receives its output, codes plus scales, as inputs.
 
 Recipes (shapes and distributions follow the source pages' tests and the
 DeepSeek- / GPT-OSS-shaped workloads the path is measured on):
 
 * per-tensor W8A16 ("SGLang PR 32618 review", ``test_gemm.py`` listing):
   ``A = bf16(randn/10)``, ``W = e4m3(randn)``, scale 0.01, fp32 ``randn`` bias.
-* block FP8 weights: codes ``e4m3(clamp(100 * randn, +-448))`` -- so a 128x128
-  block spans the e4m3 range the way a block-quantised tensor does -- and
-  fp32 block scales ``0.05 / 100 * U(0.8, 1.2)``, so decoded weights look like
-  ``0.05 * randn``.
-* MXFP4 weights: uniformly random e2m1 nibbles (two per byte) and e8m0 block
-  scales uniform in [118, 122] (2^-9 .. 2^-5).
+* block FP8 weights: ``w = 0.05 * randn`` quantised per 128x128 block (or per
+  row per 128 columns for 1x128 blocks): ``scale_inv = amax / 448``,
+  ``codes = e4m3(clamp(w / scale_inv, +-448))`` with torch's own e4m3 cast
+  (round to nearest even), so every block's largest element lands on +-448.
+* MXFP4 weights: ``w = 0.05 * randn`` quantised per row per 32 columns by the
+  OCP MX rule: shared exponent ``floor(log2(amax)) - 2`` (2 = the largest
+  e2m1 exponent), stored as e8m0 ``exponent + 127``; elements ``w / 2^exp``
+  rounded to the nearest e2m1 value, ties to the even code, saturating at 6.
+* the "page" FP8 recipe (``fp8_codes`` / ``fp8_block_scales``) of "SGLang PR
+  35605 review" (``test_xpu_fp8_linear.py`` listing: codes cast from randn,
+  scales ``rand + 0.1``) for its accuracy cases.
 * activations ``bf16(randn)``; MXFP4 ``w1`` bias fp32 ``randn``.
 * routing: deterministic per-expert counts over consecutive tokens (weight
   1.0); softmax-then-top-k of ``randn`` logits (weights not renormalised);
@@ -58,6 +64,50 @@ def bf16_randn(shape, g, device, std: float = 1.0) -> torch.Tensor:
     return (torch.randn(*shape, generator=g, device=device) * std).to(torch.bfloat16)
 
 
+def fp8_block_quantize(w: torch.Tensor, block_n: int = 128, block_k: int = 128):
+    """fp32 [N, K] -> (uint8 e4m3 codes [N, K], fp32 scale_inv [ceil(N/block_n), K/block_k]).
+
+    Per block: ``scale_inv = amax / 448``; ``codes = e4m3(clamp(w / scale_inv, +-448))``
+    (torch's cast, round to nearest even).  A zero block gets scale 1 and zero codes."""
+    N, K = w.shape
+    nb = -(-N // block_n)
+    wp = torch.zeros(nb * block_n, K, dtype=torch.float32, device=w.device)
+    wp[:N] = w
+    blocks = wp.view(nb, block_n, K // block_k, block_k)
+    amax = blocks.abs().amax(dim=(1, 3))
+    scale = torch.where(amax > 0, amax / 448.0, torch.ones_like(amax)).float()
+    q = (blocks / scale[:, None, :, None]).clamp_(-448.0, 448.0)
+    codes = q.reshape(nb * block_n, K)[:N].to(torch.float8_e4m3fn).view(torch.uint8)
+    return codes.contiguous(), scale.contiguous()
+
+
+# e2m1 magnitudes by code (bits 0-2) and the midpoints between neighbours
+_E2M1_MIDS = (0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0)
+
+
+def mxfp4_quantize(w: torch.Tensor):
+    """fp32 [N, K] (K % 32 == 0) -> (packed e2m1 uint8 [N, K/2], e8m0 uint8 [N, K/32]) by the OCP
+    MX rule: shared exponent floor(log2(amax)) - 2 per 32 elements (an all-zero group takes the
+    smallest exponent, -127), elements rounded to the nearest e2m1 value with ties to the even
+    code and saturated at 6; element 2j in the low nibble of byte j."""
+    N, K = w.shape
+    g = w.reshape(N, K // 32, 32).float()
+    amax = g.abs().amax(dim=2)
+    _, ex = torch.frexp(amax)  # amax = m * 2^ex, m in [0.5, 1): floor(log2 amax) = ex - 1
+    shared = torch.where(amax > 0, ex - 1 - 2, torch.full_like(ex, -127)).clamp_(-127, 127)
+    v = g / torch.ldexp(torch.ones_like(amax), shared)[:, :, None]
+    mag = v.abs()
+    mids = torch.tensor(_E2M1_MIDS, dtype=torch.float32, device=w.device)
+    below = (mag[..., None] > mids).sum(dim=-1)  # code when no tie
+    tie = (mag[..., None] == mids).any(dim=-1)
+    code = below + (tie & (below % 2 == 1)).to(below.dtype)  # a tie goes to the even code
+    code = code | (v < 0).to(code.dtype) * 8
+    code = code.to(torch.uint8).reshape(N, K)
+    packed = (code[:, 0::2] | (code[:, 1::2] << 4)).contiguous()
+    scales = (shared + 127).to(torch.uint8).contiguous()
+    return packed, scales
+
+
 # --------------------------------------------------------------------------- dense
 
 def dense_w8a16(M: int, N: int, K: int, seed: int, device="cpu", has_bias=True,
@@ -84,10 +134,10 @@ def batched_w8a16(B: int, M: int, N: int, K: int, seed: int, device="cpu", has_b
 
 def block_linear(M: int, N: int, K: int, seed: int, device="cpu", block_n: int = 128,
                  bias_dtype: Optional[torch.dtype] = None) -> Dict[str, torch.Tensor]:
+    """bf16 ``randn`` activations and ``0.05 * randn`` weights quantised per block_n x 128."""
     g = _gen(seed, device)
     x = bf16_randn((M, K), g, device)
-    w = fp8_codes((N, K), g, device)
-    sw = fp8_block_scales((-(-N // block_n), K // 128), g, device)
+    w, sw = fp8_block_quantize(torch.randn(N, K, generator=g, device=device) * WEIGHT_STD, block_n)
     bias = None
     if bias_dtype is not None:
         bias = torch.randn(N, generator=g, device=device).to(bias_dtype)
@@ -124,22 +174,21 @@ def route_zipf(M: int, E: int, topk: int, s: float, seed: int, device="cpu"):
 # --------------------------------------------------------------------------- experts
 
 def moe_fp8_weights(E: int, H: int, I: int, seed: int, device="cpu"):
-    """w1 [E, 2I, H], w2 [E, H, I] e4m3 codes with 128x128 fp32 block scales."""
+    """w1 [E, 2I, H], w2 [E, H, I]: ``0.05 * randn`` quantised per 128x128 block."""
     w1 = torch.empty(E, 2 * I, H, dtype=torch.uint8, device=device)
     w2 = torch.empty(E, H, I, dtype=torch.uint8, device=device)
     s1 = torch.empty(E, -(-2 * I // 128), H // 128, dtype=torch.float32, device=device)
     s2 = torch.empty(E, -(-H // 128), I // 128, dtype=torch.float32, device=device)
     for e in range(E):
         g = _gen(seed + 7919 * (e + 1), device)
-        w1[e] = fp8_codes((2 * I, H), g, device)
-        w2[e] = fp8_codes((H, I), g, device)
-        s1[e] = fp8_block_scales(s1.shape[1:], g, device)
-        s2[e] = fp8_block_scales(s2.shape[1:], g, device)
+        w1[e], s1[e] = fp8_block_quantize(torch.randn(2 * I, H, generator=g, device=device) * WEIGHT_STD)
+        w2[e], s2[e] = fp8_block_quantize(torch.randn(H, I, generator=g, device=device) * WEIGHT_STD)
     return {"w1": w1, "w1_scale": s1, "w2": w2, "w2_scale": s2}
 
 
 def moe_mxfp4_weights(E: int, H: int, I: int, seed: int, device="cpu", with_bias=True):
-    """w1 [E, 2I, H/2], w2 [E, H, I/2] packed e2m1; e8m0 scales per 32 columns."""
+    """w1 [E, 2I, H/2], w2 [E, H, I/2] packed e2m1 with e8m0 scales per 32 columns: ``0.05 * randn``
+    quantised by the OCP MX rule."""
     w1 = torch.empty(E, 2 * I, H // 2, dtype=torch.uint8, device=device)
     w2 = torch.empty(E, H, I // 2, dtype=torch.uint8, device=device)
     s1 = torch.empty(E, 2 * I, H // 32, dtype=torch.uint8, device=device)
@@ -147,10 +196,8 @@ def moe_mxfp4_weights(E: int, H: int, I: int, seed: int, device="cpu", with_bias
     b1 = torch.empty(E, 2 * I, dtype=torch.float32, device=device) if with_bias else None
     for e in range(E):
         g = _gen(seed + 7919 * (e + 1), device)
-        w1[e] = torch.randint(0, 256, (2 * I, H // 2), generator=g, device=device, dtype=torch.int32).to(torch.uint8)
-        w2[e] = torch.randint(0, 256, (H, I // 2), generator=g, device=device, dtype=torch.int32).to(torch.uint8)
-        s1[e] = torch.randint(118, 123, (2 * I, H // 32), generator=g, device=device, dtype=torch.int32).to(torch.uint8)
-        s2[e] = torch.randint(118, 123, (H, I // 32), generator=g, device=device, dtype=torch.int32).to(torch.uint8)
+        w1[e], s1[e] = mxfp4_quantize(torch.randn(2 * I, H, generator=g, device=device) * WEIGHT_STD)
+        w2[e], s2[e] = mxfp4_quantize(torch.randn(H, I, generator=g, device=device) * WEIGHT_STD)
         if b1 is not None:
             b1[e] = torch.randn(2 * I, generator=g, device=device)
     return {"w1": w1, "w1_scale": s1, "w2": w2, "w2_scale": s2, "w1_bias": b1}

@@ -24,7 +24,10 @@ Readings of what the pages leave open (the same readings the HIP path uses):
 * No ``w2`` bias.
 
 This is written as its own loop over experts and each expert's rows in
-ascending flat id; it does not call the dense oracle.
+ascending flat id; it does not call the dense oracle.  The stages are also
+exposed one by one (``stage1_rows``, ``silu_mul_bf16``, ``quant_rows``,
+``stage2_rows``, ``combine``) so that each stage of the GPU path can be checked
+on the GPU's own input to that stage; ``_routed_moe`` is their composition.
 """
 
 import numpy as np
@@ -34,7 +37,7 @@ from .codecs import (E4M3_TABLE, bf16_to_f32, f32_to_bf16, e2m1_decode_packed,
 from .quant import group_quant_f32
 
 
-def _dequant_fp8_expert(codes, grid, block_k=128):
+def dequant_fp8_expert(codes, grid, block_k=128):
     """e4m3 [N, K] with [ceil(N/128), K/128] scales -> fp32 [N, K] (128x128 blocks)."""
     N, K = codes.shape
     v = E4M3_TABLE[codes].astype(np.float32)
@@ -42,19 +45,50 @@ def _dequant_fp8_expert(codes, grid, block_k=128):
     return (v * s).astype(np.float32)
 
 
-def _dequant_mxfp4_expert(packed, scales):
+def dequant_mxfp4_expert(packed, scales):
     """packed e2m1 [N, K/2] with e8m0 [N, K/32] -> fp32 [N, K]."""
     v = e2m1_decode_packed(packed)
     s = np.repeat(e8m0_decode(scales), 32, axis=1)
     return (v * s).astype(np.float32)
 
 
-def _silu_mul_bf16(ic0_f32: np.ndarray, inter: int) -> np.ndarray:
+def silu_mul_bf16(ic0_f32: np.ndarray, inter: int) -> np.ndarray:
+    """fp32 [rows, 2I] (the bf16 ic0 values) -> bf16 bits [rows, I] of silu(gate) * up."""
     g = ic0_f32[:, :inter].astype(np.float64)
     u = ic0_f32[:, inter:].astype(np.float64)
     with np.errstate(over="ignore"):
         act = g / (1.0 + np.exp(-g))
     return f32_to_bf16((act * u).astype(np.float32))
+
+
+def stage1_rows(a_f32: np.ndarray, w1_f32: np.ndarray, b1=None) -> np.ndarray:
+    """Stage 1 of routed rows of one expert: bf16 bits of ``a @ w1^T (+ b1)`` ([rows, 2I]);
+    ``a`` the (dequantised) activation rows, ``w1`` the expert's dequantised weights."""
+    g = (a_f32.astype(np.float64) @ w1_f32.astype(np.float64).T).astype(np.float32)
+    if b1 is not None:
+        g = (g + np.asarray(b1, np.float32)).astype(np.float32)
+    return f32_to_bf16(g)
+
+
+def quant_rows(h_bf16: np.ndarray):
+    """W8A8 stage-2 input: bf16 bits [rows, I] -> (e4m3 codes, fp32 [rows, I/128] scales) and
+    the fp32 values the stage multiplies (code value x group scale)."""
+    q, s = group_quant_f32(bf16_to_f32(h_bf16), 128)
+    return q, s, (E4M3_TABLE[q].astype(np.float32) * np.repeat(s, 128, axis=1)).astype(np.float32)
+
+
+def stage2_rows(a2_f32: np.ndarray, w2_f32: np.ndarray) -> np.ndarray:
+    """Stage 2 of routed rows of one expert: fp32 ``a2 @ w2^T`` ([rows, H])."""
+    return (a2_f32.astype(np.float64) @ w2_f32.astype(np.float64).T).astype(np.float32)
+
+
+def combine(y: np.ndarray, topk_weights: np.ndarray) -> np.ndarray:
+    """fp32 y [M * topk, H] (row t * topk + k) and weights [M, topk] -> bf16 bits [M, H] of
+    sum_k w[t, k] * y[t * topk + k] (float64 sum, one rounding to fp32, then bf16)."""
+    w = np.asarray(topk_weights, np.float64)
+    M, topk = w.shape
+    acc = np.einsum("tk,tkh->th", w, np.asarray(y, np.float64).reshape(M, topk, -1))
+    return f32_to_bf16(acc.astype(np.float32))
 
 
 def _routed_moe(x_bf16, topk_ids, topk_weights, n_experts, inter, deq_w1, deq_w2,
@@ -77,23 +111,11 @@ def _routed_moe(x_bf16, topk_ids, topk_weights, n_experts, inter, deq_w1, deq_w2
         rows = np.nonzero(flat == e)[0]
         if rows.size == 0:
             continue  # an empty expert contributes nothing
-        w1 = deq_w1(e).astype(np.float64)
-        w2 = deq_w2(e).astype(np.float64)
-        a = xin[rows // topk].astype(np.float64)
-        g = (a @ w1.T).astype(np.float32)
-        if b1 is not None:
-            g = (g + np.asarray(b1[e], np.float32)).astype(np.float32)
-        ic0 = bf16_to_f32(f32_to_bf16(g))
-        ic1 = _silu_mul_bf16(ic0, inter)
-        if act_quant:
-            q, s = group_quant_f32(bf16_to_f32(ic1), 128)
-            a2 = (E4M3_TABLE[q].astype(np.float32) * np.repeat(s, 128, axis=1)).astype(np.float32)
-        else:
-            a2 = bf16_to_f32(ic1)
-        y[rows] = (a2.astype(np.float64) @ w2.T).astype(np.float32)
-    w = np.asarray(topk_weights, np.float64).reshape(M, topk)
-    acc = np.einsum("tk,tkh->th", w, y.reshape(M, topk, H).astype(np.float64))
-    return f32_to_bf16(acc.astype(np.float32))
+        ic0 = bf16_to_f32(stage1_rows(xin[rows // topk], deq_w1(e), None if b1 is None else b1[e]))
+        ic1 = silu_mul_bf16(ic0, inter)
+        a2 = quant_rows(ic1)[2] if act_quant else bf16_to_f32(ic1)
+        y[rows] = stage2_rows(a2, deq_w2(e))
+    return combine(y, np.asarray(topk_weights).reshape(M, topk))
 
 
 def fused_moe_fp8(x_bf16, topk_ids, topk_weights, w1, w1_scale, w2, w2_scale,
@@ -103,8 +125,8 @@ def fused_moe_fp8(x_bf16, topk_ids, topk_weights, w1, w1_scale, w2, w2_scale,
     E, two_i, _ = w1.shape
     return _routed_moe(
         x_bf16, topk_ids, topk_weights, E, two_i // 2,
-        lambda e: _dequant_fp8_expert(w1[e], w1_scale[e]),
-        lambda e: _dequant_fp8_expert(w2[e], w2_scale[e]),
+        lambda e: dequant_fp8_expert(w1[e], w1_scale[e]),
+        lambda e: dequant_fp8_expert(w2[e], w2_scale[e]),
         w1_bias, act_quant)
 
 
@@ -115,6 +137,6 @@ def fused_moe_mxfp4(x_bf16, topk_ids, topk_weights, w1, w1_scale, w2, w2_scale,
     E, two_i, _ = w1.shape
     return _routed_moe(
         x_bf16, topk_ids, topk_weights, E, two_i // 2,
-        lambda e: _dequant_mxfp4_expert(w1[e], w1_scale[e]),
-        lambda e: _dequant_mxfp4_expert(w2[e], w2_scale[e]),
+        lambda e: dequant_mxfp4_expert(w1[e], w1_scale[e]),
+        lambda e: dequant_mxfp4_expert(w2[e], w2_scale[e]),
         w1_bias, False)

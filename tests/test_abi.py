@@ -43,7 +43,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_status_strings_and_version():
     L, lib = _lib()
-    assert lib.mxq_abi_version() == 4
+    assert lib.mxq_abi_version() == 5
     for code in range(0, 9):
         assert lib.mxq_status_string(code)
     assert b"unknown" in lib.mxq_status_string(99)
@@ -75,8 +75,16 @@ def test_argument_errors_before_any_launch():
     # block size validation ("SGLang PR 35605 review", fp8_utils.py listing)
     for bn, bk in [(1, 32), (64, 64), (128, 64), (2, 128)]:
         st = lib.mxq_block_fp8_linear(null, L.MXQ_DTYPE_BF16, null, 4, 256, 256, null, 256, null, 2, 1, bn, bk,
-                                      null, 0, null, 256, null, 0, null)
+                                      null, 0, null, L.MXQ_DTYPE_BF16, 256, null, 0, null)
         assert st == L.MXQ_ERR_BLOCK
+    # the output dtype is bf16 ("SGLang PR 35605 review", fp8_utils.py listing); others are refused
+    for od in (L.MXQ_DTYPE_F32, L.MXQ_DTYPE_E4M3, 9):
+        st = lib.mxq_block_fp8_linear(null, L.MXQ_DTYPE_BF16, null, 4, 256, 256, null, 256, null, 2, 1, 128, 128,
+                                      null, 0, null, od, 256, null, 0, null)
+        assert st == L.MXQ_ERR_DTYPE
+    st = lib.mxq_block_fp8_linear(null, L.MXQ_DTYPE_BF16, null, 4, 256, 256, null, 256, null, 2, 1, 128, 128,
+                                  null, 0, null, L.MXQ_DTYPE_BF16, 256, null, 0, null)
+    assert st == L.MXQ_ERR_NULL
     assert lib.mxq_per_token_group_quant_fp8(null, 4, 256, 256, 64, null, null, null) == L.MXQ_ERR_BLOCK
     assert lib.mxq_per_token_group_quant_fp8(null, 4, 200, 200, 128, null, null, null) == L.MXQ_ERR_SHAPE
     assert lib.mxq_per_token_group_quant_fp8(null, 4, 256, 256, 128, null, null, null) == L.MXQ_ERR_NULL
@@ -95,16 +103,37 @@ def test_argument_errors_before_any_launch():
     assert bmm(null, 2, 4, 128, 128, 512, null, 8, 1024, null, 0, null, 0, 0, null, 8, 32, null) == L.MXQ_ERR_NULL
     assert bmm(null, 2, 4, 128, 128, 0, null, 8, 0, null, 0, null, 0, 0, null, 8, 32, null) == L.MXQ_ERR_NULL
     assert bmm(null, 0, 4, 128, 128, 512, null, 8, 1024, null, 0, null, 0, 0, null, 8, 32, null) == L.MXQ_OK
-    assert lib.mxq_fused_moe_fp8(null, 4, 100, 128, 8, 2, null, null, null, null, null, null, null, 0, 0, null, null,
-                                 0, null) == L.MXQ_ERR_SHAPE
-    assert lib.mxq_fused_moe_mxfp4(null, 4, 100, 128, 8, 2, null, null, null, null, null, null, null, 0, null, null, 0,
-                                   null) == L.MXQ_ERR_SHAPE
-    assert lib.mxq_fused_moe_fp8(null, 4, 256, 128, 8, 2, null, null, null, null, null, null, null, 0, 0, null, null,
-                                 0, null) == L.MXQ_ERR_NULL
-    assert lib.mxq_fused_moe_fp8(null, 4, 256, 128, 8, 2, null, null, null, null, null, null, null, 0, 2, null, null,
-                                 0, null) == L.MXQ_ERR_ARG
-    assert lib.mxq_fused_moe_mxfp4(null, 4, 256, 128, 8, 2, null, null, null, null, null, null, null, 5, null, null,
-                                   0, null) == L.MXQ_ERR_ARG
+    fp8 = lib.mxq_fused_moe_fp8
+    mx4 = lib.mxq_fused_moe_mxfp4
+    assert fp8(null, 4, 100, 128, 8, 2, null, null, null, null, null, null, null, 0, 0, null, null, null, 0,
+               null) == L.MXQ_ERR_SHAPE
+    assert mx4(null, 4, 100, 128, 8, 2, null, null, null, null, null, null, null, 0, null, null, null, 0,
+               null) == L.MXQ_ERR_SHAPE
+    assert fp8(null, 4, 256, 128, 8, 2, null, null, null, null, null, null, null, 0, 0, null, null, null, 0,
+               null) == L.MXQ_ERR_NULL
+    assert fp8(null, 4, 256, 128, 8, 2, null, null, null, null, null, null, null, 0, 2, null, null, null, 0,
+               null) == L.MXQ_ERR_ARG
+    assert mx4(null, 4, 256, 128, 8, 2, null, null, null, null, null, null, null, 5, null, null, null, 0,
+               null) == L.MXQ_ERR_ARG
+    # per-call dispatch: every field validated before any pointer is looked at
+    for bad in ((7, 0, 4, 0), (0, 0, 17, 0), (0, 0, -1, 0), (0, 0, 4, 5), (1, 5, 16, 0), (1, -1, 16, 0)):
+        d = C.byref(L.MoeDispatch(*bad))
+        assert fp8(null, 4, 256, 128, 8, 2, null, null, null, null, null, null, null, 0, 0, d, null, null, 0,
+                   null) == L.MXQ_ERR_ARG, bad
+        assert mx4(null, 4, 256, 128, 8, 2, null, null, null, null, null, null, null, 0, d, null, null, 0,
+                   null) == L.MXQ_ERR_ARG, bad
+    for good in ((0, 0, 16, 0), (1, 4, 4, 1), (2, 0, 0, 0)):
+        d = C.byref(L.MoeDispatch(*good))
+        assert fp8(null, 4, 256, 128, 8, 2, null, null, null, null, null, null, null, 0, 0, d, null, null, 0,
+                   null) == L.MXQ_ERR_NULL, good
+    # SiLU-and-mul: I % 8 (I % 128 when re-quantising), ld_in >= 2I, required pointers
+    sm = lib.mxq_silu_and_mul
+    assert sm(null, 4, 100, 200, null, null, null, null) == L.MXQ_ERR_SHAPE
+    assert sm(null, 4, 64, 100, null, null, null, null) == L.MXQ_ERR_SHAPE
+    assert sm(null, 4, 64, 128, null, fake, null, null) == L.MXQ_ERR_SHAPE
+    assert sm(null, 4, 64, 128, null, null, null, null) == L.MXQ_ERR_NULL
+    assert sm(null, 4, 128, 256, null, fake, null, null) == L.MXQ_ERR_NULL
+    assert sm(null, 0, 128, 256, null, null, null, null) == L.MXQ_OK
     # load-time relayout: N and row bytes multiples of 16
     assert lib.mxq_moe_prepack(null, 2, 24, 128, null, null) == L.MXQ_ERR_SHAPE
     assert lib.mxq_moe_prepack(null, 2, 32, 136, null, null) == L.MXQ_ERR_SHAPE
@@ -112,10 +141,38 @@ def test_argument_errors_before_any_launch():
     assert lib.mxq_moe_prepack_scales(null, 2, 24, 90, null, null) == L.MXQ_ERR_SHAPE
     assert lib.mxq_moe_prepack_scales(null, 2, 32, 90, null, null) == L.MXQ_ERR_NULL
     assert lib.mxq_moe_align(null, 4, 2, 2000, 16, null, null, null, null, null) == L.MXQ_ERR_SHAPE
-    assert lib.mxq_moe_set_dispatch(7, 0, 4, 0) == L.MXQ_ERR_ARG
-    assert lib.mxq_moe_set_dispatch(0, 0, 17, 0) == L.MXQ_ERR_ARG
-    assert lib.mxq_moe_set_dispatch(0, 0, 4, 5) == L.MXQ_ERR_ARG
-    assert lib.mxq_moe_set_dispatch(0, 0, 8, 0) == L.MXQ_OK
+
+
+
+def test_moe_workspace_layout_query():
+    """Every region lies inside the workspace, regions do not overlap, and each is as large as
+    its tensor; unused regions report -1."""
+    L, lib = _lib()
+    from mxfp4_block_scaled_expert_amd.ops import fused_moe_workspace_layout
+    for (M, H, I, E, topk, wf, aq) in [(4096, 7168, 2048, 256, 8, L.MXQ_WEIGHTS_FP8_BLOCK, 1),
+                                       (128, 2048, 1024, 8, 1, L.MXQ_WEIGHTS_FP8_BLOCK, 0),
+                                       (32, 2880, 2880, 128, 4, L.MXQ_WEIGHTS_MXFP4, 0)]:
+        lay = fused_moe_workspace_layout(M, H, I, E, topk, wf, aq)
+        total = lib.mxq_fused_moe_workspace_size(M, H, I, E, topk, wf, aq)
+        R = M * topk
+        bm = lay["block_m"]
+        mb = lib.mxq_moe_max_blocks(M, topk, E, bm)
+        size = {"sorted_ids": 4 * mb * bm, "expert_ids": 4 * mb, "offsets": 4 * (mb + 1), "num_blocks": 4,
+                "qx": M * H, "sx": 4 * M * (H // 128), "ic0": 2 * R * 2 * I, "ic1": 2 * R * I,
+                "ic1_q": R * I, "ic1_s": 4 * R * (I // 128), "y": 4 * R * H}
+        used = {k: v for k, v in lay.items() if k != "block_m" and v >= 0}
+        if aq:
+            assert lay["ic1"] == -1 and min(lay["qx"], lay["sx"], lay["ic1_q"], lay["ic1_s"]) >= 0
+        else:
+            assert lay["qx"] == lay["sx"] == lay["ic1_q"] == lay["ic1_s"] == -1 and lay["ic1"] >= 0
+        spans = sorted((v, v + size[k], k) for k, v in used.items())
+        for (a0, a1, ka), (b0, b1, kb) in zip(spans, spans[1:]):
+            assert a1 <= b0, (ka, kb)
+        assert spans[-1][1] <= total
+        assert all(v % 256 == 0 for v in used.values())
+    arr = (C.c_int64 * 12)()
+    assert lib.mxq_fused_moe_workspace_layout(0, 7168, 2048, 256, 8, 0, 1, arr) == L.MXQ_ERR_SHAPE
+    assert lib.mxq_fused_moe_workspace_layout(4, 256, 128, 8, 2, 0, 1, None) == L.MXQ_ERR_NULL
 
 
 def test_prepack_size_queries():

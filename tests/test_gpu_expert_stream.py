@@ -23,13 +23,6 @@ from tests.test_gpu_moe import _run_oracle, _small_spec
 pytestmark = pytest.mark.gpu
 
 
-@pytest.fixture(autouse=True)
-def _default_dispatch():
-    ops.moe_set_dispatch()
-    yield
-    ops.moe_set_dispatch()
-
-
 def _tiled(inp):
     t = dict(inp)
     t["w1"] = ops.moe_prepack(inp["w1"])
@@ -40,21 +33,21 @@ def _tiled(inp):
     return t
 
 
-def _run(inp, layout):
+def _run(inp, layout, dispatch=None):
     if inp["kind"] == "fused_moe_mxfp4":
         return ops.fused_moe_mxfp4(inp["x"], inp["topk_ids"], inp["topk_weights"], inp["w1"], inp["w1_scale"],
-                                   inp["w2"], inp["w2_scale"], inp["w1_bias"], weight_layout=layout)
+                                   inp["w2"], inp["w2_scale"], inp["w1_bias"], weight_layout=layout,
+                                   dispatch=dispatch)
     return ops.fused_moe_fp8(inp["x"], inp["topk_ids"], inp["topk_weights"], inp["w1"], inp["w1_scale"],
-                             inp["w2"], inp["w2_scale"], inp.get("w1_bias"), act_quant=False, weight_layout=layout)
+                             inp["w2"], inp["w2_scale"], inp.get("w1_bias"), act_quant=False, weight_layout=layout,
+                             dispatch=dispatch)
 
 
 def _stream_vs_tiny_class(inp, layout, what):
     """Default dispatch (streaming path) and forced tiny class: bit-identical outputs."""
     src = _tiled(inp) if layout == "tiled" else inp
     got = _run(src, layout)
-    ops.moe_set_dispatch(mx.MXQ_DISPATCH_FORCED, 0)
-    ref = _run(src, layout)
-    ops.moe_set_dispatch()
+    ref = _run(src, layout, ops.Dispatch(mx.MXQ_DISPATCH_FORCED, 0))
     torch.cuda.synchronize()
     assert torch.equal(got.view(torch.int16), ref.view(torch.int16)), what
     return got

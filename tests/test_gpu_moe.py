@@ -23,13 +23,6 @@ from tests._util import assert_bf16_close, assert_bf16_close_requant, bf16_bits,
 pytestmark = pytest.mark.gpu
 
 
-@pytest.fixture(autouse=True)
-def _default_dispatch():
-    ops.moe_set_dispatch()
-    yield
-    ops.moe_set_dispatch()
-
-
 # ------------------------------------------------------------------ align
 
 def _check_align(ids: torch.Tensor, E: int, block_m: int):
@@ -74,12 +67,13 @@ def _to_np(inp):
     return out
 
 
-def _run_gpu(inp):
+def _run_gpu(inp, dispatch=None, **kw):
     if inp["kind"] == "fused_moe_mxfp4":
         return ops.fused_moe_mxfp4(inp["x"], inp["topk_ids"], inp["topk_weights"], inp["w1"], inp["w1_scale"],
-                                   inp["w2"], inp["w2_scale"], inp["w1_bias"])
+                                   inp["w2"], inp["w2_scale"], inp["w1_bias"], dispatch=dispatch, **kw)
     return ops.fused_moe_fp8(inp["x"], inp["topk_ids"], inp["topk_weights"], inp["w1"], inp["w1_scale"],
-                             inp["w2"], inp["w2_scale"], inp.get("w1_bias"), act_quant=inp["act_quant"])
+                             inp["w2"], inp["w2_scale"], inp.get("w1_bias"), act_quant=inp["act_quant"],
+                             dispatch=dispatch, **kw)
 
 
 def _run_oracle(inp, tokens=None):
@@ -118,8 +112,7 @@ def test_small_expert_blocks_w8a16_per_block_dispatch():
 def test_small_expert_blocks_every_class(forced):
     inp = synth.moe_inputs(SMALL_BLOCKS, seed=1003, device=gpu())
     want = _run_oracle(inp)
-    ops.moe_set_dispatch(mx.MXQ_DISPATCH_FORCED, forced, 4)
-    out = _run_gpu(inp)
+    out = _run_gpu(inp, ops.Dispatch(mx.MXQ_DISPATCH_FORCED, forced, 4))
     torch.cuda.synchronize()
     assert_bf16_close(bf16_bits(out), want, what=f"forced class {forced}")
 
@@ -139,16 +132,14 @@ def test_tiny_block_kernels(kind, tiny):
         inp = synth.moe_inputs(_small_spec("fused_moe_mxfp4", 40, 8, 4, 2880, 2880), seed=22, device=gpu())
         check = assert_bf16_close
     want = _run_oracle(inp)
-    ops.moe_set_dispatch(mx.MXQ_DISPATCH_FORCED, 0, 4, tiny)
-    out = _run_gpu(inp)
+    out = _run_gpu(inp, ops.Dispatch(mx.MXQ_DISPATCH_FORCED, 0, 4, tiny))
     torch.cuda.synchronize()
     check(bf16_bits(out), want, what=f"{kind} tiny={tiny}")
 
 
 def test_layer_average_rule_matches_too():
     inp = synth.moe_inputs(SMALL_BLOCKS, seed=1003, device=gpu())
-    ops.moe_set_dispatch(mx.MXQ_DISPATCH_LAYER_AVERAGE, 0, 4)
-    out = _run_gpu(inp)
+    out = _run_gpu(inp, ops.Dispatch(mx.MXQ_DISPATCH_LAYER_AVERAGE, 0, 4))
     torch.cuda.synchronize()
     assert_bf16_close(bf16_bits(out), _run_oracle(inp), what="layer-average dispatch")
 
@@ -165,9 +156,7 @@ def test_w8a8_skewed_small(forced):
     spec = _small_spec("fused_moe_fp8", 300, 16, 4, 512, 256, zipf=1.1, act_quant=True)
     inp = synth.moe_inputs(spec, seed=11, device=gpu())
     want = _run_oracle(inp)
-    if forced is not None:
-        ops.moe_set_dispatch(mx.MXQ_DISPATCH_FORCED, forced, 4)
-    out = _run_gpu(inp)
+    out = _run_gpu(inp, None if forced is None else ops.Dispatch(mx.MXQ_DISPATCH_FORCED, forced, 4))
     torch.cuda.synchronize()
     assert_bf16_close_requant(bf16_bits(out), want, what=f"w8a8 forced={forced}")
 
@@ -187,9 +176,7 @@ def test_mxfp4_ragged_k(forced):
     spec = _small_spec("fused_moe_mxfp4", 40, 8, 4, 2880, 2880)
     inp = synth.moe_inputs(spec, seed=13, device=gpu())
     want = _run_oracle(inp)
-    if forced is not None:
-        ops.moe_set_dispatch(mx.MXQ_DISPATCH_FORCED, forced, 4)
-    out = _run_gpu(inp)
+    out = _run_gpu(inp, None if forced is None else ops.Dispatch(mx.MXQ_DISPATCH_FORCED, forced, 4))
     torch.cuda.synchronize()
     assert_bf16_close(bf16_bits(out), want, what=f"mxfp4 forced={forced}")
 
@@ -241,8 +228,7 @@ def test_small_batch_fused_silu_matches_unfused_and_oracle(kind):
         spec = _small_spec("fused_moe_mxfp4", 16, 8, 4, 2880, 2880)
     inp = synth.moe_inputs(spec, seed=41, device=gpu())
     fused = _run_gpu(inp)
-    ops.moe_set_dispatch(mx.MXQ_DISPATCH_FORCED, 0)
-    plain = _run_gpu(inp)
+    plain = _run_gpu(inp, ops.Dispatch(mx.MXQ_DISPATCH_FORCED, 0))
     torch.cuda.synchronize()
     assert torch.equal(fused.view(torch.int16), plain.view(torch.int16))
     assert_bf16_close(bf16_bits(fused), _run_oracle(inp), what=f"{kind} fused SiLU")

@@ -42,13 +42,6 @@ def _tiled_scales_ref(s: np.ndarray) -> np.ndarray:
     return np.ascontiguousarray(t).reshape(E, N, S * 8)
 
 
-@pytest.fixture(autouse=True)
-def _default_dispatch():
-    ops.moe_set_dispatch()
-    yield
-    ops.moe_set_dispatch()
-
-
 @pytest.mark.parametrize("shape", [(3, 48, 1440), (2, 32, 256), (1, 16, 16), (2, 64, 2048)])
 def test_prepack_weight_layout(shape):
     g = torch.Generator().manual_seed(sum(shape))
@@ -77,13 +70,14 @@ def _tiled(inp):
     return t
 
 
-def _run(inp, layout):
+def _run(inp, layout, dispatch=None):
     if inp["kind"] == "fused_moe_mxfp4":
         return ops.fused_moe_mxfp4(inp["x"], inp["topk_ids"], inp["topk_weights"], inp["w1"], inp["w1_scale"],
-                                   inp["w2"], inp["w2_scale"], inp["w1_bias"], weight_layout=layout)
+                                   inp["w2"], inp["w2_scale"], inp["w1_bias"], weight_layout=layout,
+                                   dispatch=dispatch)
     return ops.fused_moe_fp8(inp["x"], inp["topk_ids"], inp["topk_weights"], inp["w1"], inp["w1_scale"],
                              inp["w2"], inp["w2_scale"], inp.get("w1_bias"), act_quant=inp["act_quant"],
-                             weight_layout=layout)
+                             weight_layout=layout, dispatch=dispatch)
 
 
 CASES = {
@@ -99,10 +93,9 @@ CASES = {
 def test_tiled_equals_plain_bit_for_bit(kind, forced):
     inp = CASES[kind]()
     tin = _tiled(inp)
-    if forced is not None:
-        ops.moe_set_dispatch(mx.MXQ_DISPATCH_FORCED, forced)
-    a = _run(inp, "plain")
-    b = _run(tin, "tiled")
+    d = None if forced is None else ops.Dispatch(mx.MXQ_DISPATCH_FORCED, forced)
+    a = _run(inp, "plain", d)
+    b = _run(tin, "tiled", d)
     torch.cuda.synchronize()
     assert torch.equal(a.view(torch.int16), b.view(torch.int16)), f"{kind} forced={forced}"
 
@@ -114,10 +107,8 @@ def test_tiled_tiny_rows_and_gemv_request():
     want = _run_oracle(inp)
     for rows, tiny in ((4, mx.MXQ_TINY_MFMA), (16, mx.MXQ_TINY_MFMA), (8, mx.MXQ_TINY_GEMV)):
         # the plain-layout reference runs the same kernels: the MFMA tiny kernel, same class bound
-        ops.moe_set_dispatch(mx.MXQ_DISPATCH_PER_BLOCK, 0, rows, mx.MXQ_TINY_MFMA)
-        ref = _run(inp, "plain")
-        ops.moe_set_dispatch(mx.MXQ_DISPATCH_PER_BLOCK, 0, rows, tiny)
-        got = _run(tin, "tiled")
+        ref = _run(inp, "plain", ops.Dispatch(mx.MXQ_DISPATCH_PER_BLOCK, 0, rows, mx.MXQ_TINY_MFMA))
+        got = _run(tin, "tiled", ops.Dispatch(mx.MXQ_DISPATCH_PER_BLOCK, 0, rows, tiny))
         torch.cuda.synchronize()
         assert torch.equal(ref.view(torch.int16), got.view(torch.int16)), f"rows={rows} kernel={tiny}"
         assert_bf16_close(bf16_bits(got), want, what=f"tiny rows={rows} kernel={tiny}")
