@@ -55,6 +55,7 @@ typedef int32_t mxq_status;
 #define MXQ_ERR_ARCH 6      /* the current device is not gfx950 */
 #define MXQ_ERR_LAUNCH 7    /* a kernel launch failed (hipGetLastError) */
 #define MXQ_ERR_ARG 8       /* any other invalid argument */
+#define MXQ_ERR_SCRATCH 9   /* input larger than the static scratch of an allocation-free entry point */
 
 /* dtype tags */
 #define MXQ_DTYPE_BF16 0
@@ -148,6 +149,25 @@ mxq_status mxq_block_fp8_linear(const void* A, int32_t a_dtype, const float* a_s
                                 int64_t ws_stride1, int32_t block_n, int32_t block_k, const void* bias,
                                 int32_t bias_dtype, void* out, int32_t out_dtype, int64_t ldo, void* workspace,
                                 size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------ block-FP8 linear, no allocation
+ * For callers that cannot allocate device memory or pass a workspace (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation): mxq_block_fp8_linear with
+ * the same arguments minus the workspace, same kernels and bit-identical results.  A bf16
+ * input's quantised codes and scales go to a static device array of
+ * MXQ_NOALLOC_SCRATCH_BYTES (32 MiB) that the library holds on every GPU it runs on until the
+ * process ends; inputs needing more (M * K + 4 * M * K / 128 bytes, 256-byte aligned parts,
+ * i.e. about M * K <= 32.5 M) return MXQ_ERR_SCRATCH before anything is enqueued.  The call
+ * allocates nothing.  Every call on one GPU shares that GPU's array: calls that may overlap
+ * on one GPU (different streams, no ordering between them) race and must not be issued; calls
+ * on one stream are ordered and safe.  Nothing in the array needs to start at zero (the
+ * quantiser writes all of it that the GEMM reads).  e4m3 input uses no scratch. */
+#define MXQ_NOALLOC_SCRATCH_BYTES (32u << 20)
+mxq_status mxq_block_fp8_linear_noalloc(const void* A, int32_t a_dtype, const float* a_scale, int64_t M, int64_t K,
+                                        int64_t lda, const void* W, int64_t N, const float* w_scale,
+                                        int64_t ws_stride0, int64_t ws_stride1, int32_t block_n, int32_t block_k,
+                                        const void* bias, int32_t bias_dtype, void* out, int32_t out_dtype,
+                                        int64_t ldo, void* stream);
 
 /* ------------------------------------------------------------------ expert sort / align
  * Groups the R = M * topk routed rows (flat id r = t * topk + k) by expert for the

@@ -21,6 +21,8 @@ MXQ_ERR_WORKSPACE = 5
 MXQ_ERR_ARCH = 6
 MXQ_ERR_LAUNCH = 7
 MXQ_ERR_ARG = 8
+MXQ_ERR_SCRATCH = 9
+MXQ_NOALLOC_SCRATCH_BYTES = 32 << 20
 
 MXQ_DTYPE_BF16 = 0
 MXQ_DTYPE_F32 = 1
@@ -66,6 +68,8 @@ SIGNATURES = {
     "mxq_block_fp8_linear_workspace_size": (_sz, [_i64, _i64, _i32]),
     "mxq_block_fp8_linear": (_i32, [_p, _i32, _p, _i64, _i64, _i64, _p, _i64, _p, _i64, _i64, _i32, _i32,
                                      _p, _i32, _p, _i32, _i64, _p, _sz, _p]),
+    "mxq_block_fp8_linear_noalloc": (_i32, [_p, _i32, _p, _i64, _i64, _i64, _p, _i64, _p, _i64, _i64, _i32,
+                                             _i32, _p, _i32, _p, _i32, _i64, _p]),
     "mxq_moe_max_blocks": (_i64, [_i64, _i32, _i32, _i32]),
     "mxq_moe_align": (_i32, [_p, _i64, _i32, _i32, _i32, _p, _p, _p, _p, _p]),
     "mxq_fused_moe_workspace_size": (_sz, [_i64, _i64, _i64, _i32, _i32, _i32, _i32]),

@@ -4,6 +4,7 @@
 #include <string.h>
 
 #include <atomic>
+#include <mutex>
 
 #include "../../include/mxq.h"
 #include "kernels.hpp"
@@ -29,6 +30,28 @@ mxq_status check_arch() {
 }
 
 mxq_status launch_status() { return hipGetLastError() == hipSuccess ? MXQ_OK : MXQ_ERR_LAUNCH; }
+
+// Scratch of mxq_block_fp8_linear_noalloc: the bf16 input's quantised codes and scales.  Every
+// GPU the library runs on holds one copy until the process ends.  In host code `scratch` names
+// a host-side stand-in, never the device memory: the device address of each GPU's copy comes
+// from hipGetSymbolAddress, taken once per device (mxq_init, else the entry point's first call
+// on that device) and kept in g_scratch_ptr.
+static __device__ __align__(256) uint8_t scratch[MXQ_NOALLOC_SCRATCH_BYTES];
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+
+mxq_status scratch_ptr_current_device(void** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return MXQ_ERR_ARCH;
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return MXQ_ERR_LAUNCH;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return MXQ_OK;
+}
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -375,15 +398,20 @@ const char* mxq_status_string(mxq_status s) {
     case MXQ_ERR_ARCH: return "the current device is not gfx950 (MI355X)";
     case MXQ_ERR_LAUNCH: return "kernel launch failed";
     case MXQ_ERR_ARG: return "invalid argument";
+    case MXQ_ERR_SCRATCH:
+      return "the quantised input exceeds the static scratch of the allocation-free entry point "
+             "(MXQ_NOALLOC_SCRATCH_BYTES)";
     default: return "unknown status";
   }
 }
 
-int32_t mxq_abi_version(void) { return 5; }
+int32_t mxq_abi_version(void) { return 6; }
 
 mxq_status mxq_init(int32_t device) {
   if (hipSetDevice(device) != hipSuccess) return MXQ_ERR_ARCH;
-  return check_arch();
+  MXQ_TRY(check_arch());
+  void* p = nullptr;
+  return scratch_ptr_current_device(&p);
 }
 
 mxq_status mxq_per_token_group_quant_fp8(const void* x, int64_t M, int64_t K, int64_t ldx, int32_t group, void* q,
@@ -527,6 +555,27 @@ mxq_status mxq_block_fp8_linear(const void* A, int32_t a_dtype, const float* a_s
     launch_gemm_w8a8(g, ROWS_DENSE, tile, false, cdiv(M, tile_rows(tile)), st);
   }
   return launch_status();
+}
+
+mxq_status mxq_block_fp8_linear_noalloc(const void* A, int32_t a_dtype, const float* a_scale, int64_t M, int64_t K,
+                                        int64_t lda, const void* W, int64_t N, const float* w_scale,
+                                        int64_t ws_stride0, int64_t ws_stride1, int32_t block_n, int32_t block_k,
+                                        const void* bias, int32_t bias_dtype, void* out, int32_t out_dtype,
+                                        int64_t ldo, void* stream) {
+  // the size checks of the allocating entry point first, so that a bad shape reports as such
+  if (block_k != 128 || (block_n != 1 && block_n != 128)) return MXQ_ERR_BLOCK;
+  if (a_dtype != MXQ_DTYPE_BF16 && a_dtype != MXQ_DTYPE_E4M3) return MXQ_ERR_DTYPE;
+  if (M < 0 || N < 0 || K < 0 || K % 128 != 0) return MXQ_ERR_SHAPE;
+  const size_t need = mxq_block_fp8_linear_workspace_size(M, K, a_dtype);
+  if (need > size_t(MXQ_NOALLOC_SCRATCH_BYTES)) return MXQ_ERR_SCRATCH;
+  void* ws = nullptr;
+  if (need > 0 && M > 0 && N > 0) {
+    if (!A || !W || !w_scale || !out) return MXQ_ERR_NULL;
+    MXQ_TRY(check_arch());
+    MXQ_TRY(scratch_ptr_current_device(&ws));
+  }
+  return mxq_block_fp8_linear(A, a_dtype, a_scale, M, K, lda, W, N, w_scale, ws_stride0, ws_stride1, block_n,
+                              block_k, bias, bias_dtype, out, out_dtype, ldo, ws, need, stream);
 }
 
 int64_t mxq_moe_max_blocks(int64_t M, int32_t topk, int32_t E, int32_t block_m) {
