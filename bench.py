@@ -3,23 +3,31 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-secondary]
 
 Headline workload: block-wise FP8 W8A8 linear, bf16 A [2048, 2048] quantised per
-token per 128 columns, e4m3 W [7168, 2048] with 128x128 block scales, bf16 out.
-One step = the 1x128 quantisation kernel + the block-scaled FP8 GEMM, on a
-rotating set of input copies (> 512 MB in total, so the 256 MB last-level
-cache cannot hold the operands between steps).  Inputs are resident in HBM
-before the timed region starts.
+token per 128 columns, e4m3 W [7168, 2048] (0.05 * randn quantised per 128x128
+block), bf16 out.  One step = the 1x128 quantisation kernel + the block-scaled
+FP8 GEMM, on rotating input sets (> 600 MB in total, so the 256 MB last-level
+cache cannot hold the operands between steps), each with its own quantised
+buffers.  Inputs are resident in HBM before the timed region starts.
+
+Timing: W warm-up steps, and more until 0.3 s of untimed load has passed (the
+clocks settle), then exactly K steps in one window with a HIP event at every
+kernel boundary on the kernels' stream: the step, the quantiser and the GEMM
+durations come from the same window (median, p10, p90 reported).
 
 Printed: ONE JSON line with the throughput of the step (TFLOP/s), the roofline
-of the dominant kernel (the GEMM, against the FP8 dense MFMA peak, timed with
-HIP events on the stream it runs on), the CPU oracle's throughput on the same
-workload, and secondary measurements of the two routed-MoE workloads
-(GPT-OSS-shaped MXFP4 decode and DeepSeek-shaped W8A8 prefill) and of the batched
-per-tensor W8A16 GEMM on MLA-shaped per-head products (128 heads, 64 tokens).
+of the dominant kernel (the GEMM, against the FP8 dense MFMA peak; its HBM
+traffic from the counter profile while the kernel sources are unchanged), the
+CPU oracle's throughput on a sample of the same workload, and secondary
+measurements: the per-tensor W8A16 GEMM, the small-block W8A16 MoE, the two
+routed-MoE workloads (GPT-OSS-shaped MXFP4 decode, DeepSeek-shaped W8A8
+prefill) and the batched W8A16 GEMM on MLA-shaped per-head products.
 """
 
 from __future__ import annotations
 
 import argparse
+import ctypes
+import hashlib
 import json
 import os
 import sys
@@ -36,25 +44,32 @@ METRIC = "fused-MoE & block-FP8 GEMM TFLOP/s + weight GB/s, % of MI355X roofline
 HBM_PEAK_GBS = 8000.0
 FP8_PEAK_TFLOPS = 5000.0
 BF16_PEAK_TFLOPS = 2500.0
+# Untimed steps before every timed region last at least this long (the W warm-up steps
+# included): with a few steps only, the clocks have not settled and the GEMM measures ~15 %
+# slower than after a fraction of a second of load.
+SETTLE_S = 0.3
 
-# HBM traffic of the dominant kernel per launch (bytes): rocprofv3 --pmc FETCH_SIZE and WRITE_SIZE
-# on this workload, each divided by what the same counter reads for a 256 MiB device copy (FETCH_SIZE
-# 0.500, WRITE_SIZE 1.000 of the true bytes); figures and commands in
-# profiles/gemm_w8a8_big_block_linear_2048x2048x7168.md and profiles/copy_calibration_256MiB.md.
-# Set back to None whenever gemm_w8a8_big_kernel changes until the counters are taken again.
-GEMM_TRAFFIC_BYTES = 76329103
+# HBM traffic of the headline GEMM comes from rocprofv3 counters (FETCH_SIZE, WRITE_SIZE) taken on
+# this workload and recorded, with a hash of the kernel's sources, in the profile summary below;
+# it is reported only while the sources still hash to that value (else null: the counters no
+# longer describe the kernel).
+GEMM_PROFILE = os.path.join(ROOT, "profiles", "gemm_w8a8_big_block_linear_2048x2048x7168.md")
+GEMM_SOURCES = ("gemm_w8a8_big.hip", "lds_dma.hpp", "tile_rows.hpp", "common.hpp", "kernels.hpp")
 
 
 def _args():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=50)
-    p.add_argument("--warmup", type=int, default=1000)
+    p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-secondary", action="store_true")
-    p.add_argument("--only", choices=["linear", "decode", "prefill", "copy", "ablation"], default=None,
-                   help="time one workload only (profiling runs); copy = counter calibration; "
-                        "ablation = per-block vs per-layer tile-class dispatch")
+    p.add_argument("--settle", type=float, default=None,
+                   help="seconds of untimed load before each timed window (default 0.3; profiling runs use 0)")
+    p.add_argument("--only", choices=["linear", "decode", "prefill", "small", "copy", "ablation"], default=None,
+                   help="time one workload only (profiling runs); small = the per-tensor GEMM and the "
+                        "small-block W8A16 MoE; copy = counter calibration; ablation = per-block vs "
+                        "per-layer tile-class dispatch")
     return p.parse_args()
 
 
@@ -68,87 +83,195 @@ def _check(st, what):
         raise RuntimeError(f"{what} failed with status {st}")
 
 
+def sources_sha16(names=GEMM_SOURCES) -> str:
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "mxfp4_block_scaled_expert_amd", "csrc", n), "rb") as f:
+            h.update(n.encode() + b"\0" + f.read())
+    return h.hexdigest()[:16]
+
+
+def stamped_traffic():
+    """(bytes per launch or None, note) from the profile's `traffic-stamp:` line."""
+    try:
+        with open(GEMM_PROFILE) as f:
+            line = next((l for l in f if l.startswith("traffic-stamp:")), None)
+    except OSError:
+        return None, "no profile"
+    if line is None:
+        return None, "no traffic stamp in the profile"
+    stamp = json.loads(line.split(":", 1)[1])
+    if stamp.get("sources_sha16") != sources_sha16():
+        return None, "kernel sources changed since the counters were taken"
+    return int(stamp["traffic_bytes"]), f"FETCH_SIZE/{stamp['fetch_scale']} + WRITE_SIZE/{stamp['write_scale']}"
+
+
+# ----------------------------------------------------------------------------- timing
+
+class _HipEvents:
+    """Timing events created with hipEventDisableSystemFence, on the HIP runtime torch already
+    loaded: recording one costs no cache write-back or invalidation, so an event between every
+    two kernels barely perturbs them (torch's events do: ~2-3 µs per record here)."""
+    DISABLE_SYSTEM_FENCE = 0x20000000
+
+    def __init__(self):
+        path = next(l.split()[-1] for l in open("/proc/self/maps") if "libamdhip64" in l)
+        self.h = ctypes.CDLL(path)
+        self.h.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+        self.h.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        self.h.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        self.h.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def create(self, n):
+        evs = []
+        for _ in range(n):
+            e = ctypes.c_void_p()
+            _check(self.h.hipEventCreateWithFlags(ctypes.byref(e), self.DISABLE_SYSTEM_FENCE), "hipEventCreate")
+            evs.append(e)
+        return evs
+
+    def record(self, e, stream: int):
+        _check(self.h.hipEventRecord(e, ctypes.c_void_p(stream)), "hipEventRecord")
+
+    def us(self, a, b) -> float:
+        """µs between two recorded events (after a device synchronisation)."""
+        ms = ctypes.c_float()
+        _check(self.h.hipEventElapsedTime(ctypes.byref(ms), a, b), "hipEventElapsedTime")
+        return ms.value * 1e3
+
+    def destroy(self, evs):
+        for e in evs:
+            self.h.hipEventDestroy(e)
+
+
+_HIP = None
+
+
+def _hip():
+    global _HIP
+    if _HIP is None:
+        _HIP = _HipEvents()
+    return _HIP
+
+
+def _stats(us):
+    a = np.asarray(us, np.float64)
+    return {"mean": float(a.mean()), "median": float(np.median(a)), "p10": float(np.percentile(a, 10)),
+            "p90": float(np.percentile(a, 90)), "n": int(a.size)}
+
+
+def _settle(step, warmup: int) -> int:
+    """`warmup` untimed steps, then more until SETTLE_S of wall time has passed."""
+    t0 = time.perf_counter()
+    i = 0
+    while i < warmup or time.perf_counter() - t0 < SETTLE_S:
+        step(i)
+        i += 1
+        if i % 64 == 0:
+            torch.cuda.synchronize()  # bounded queue; wall time tracks the GPU
+    torch.cuda.synchronize()
+    return i
+
+
+def _time_calls(run, steps: int, warmup: int):
+    """Per-call µs of `steps` back-to-back calls (an event between every two calls, all on the
+    calls' stream), after the settle pre-roll.  Returns (stats, total µs of the window)."""
+    _settle(lambda i: run(), warmup)
+    hip = _hip()
+    sh = torch.cuda.current_stream().cuda_stream
+    ev = hip.create(steps + 1)
+    hip.record(ev[0], sh)
+    for i in range(steps):
+        run()
+        hip.record(ev[i + 1], sh)
+    torch.cuda.synchronize()
+    per = [hip.us(ev[i], ev[i + 1]) for i in range(steps)]
+    total = hip.us(ev[0], ev[steps])
+    hip.destroy(ev)
+    return _stats(per), total
+
+
 # ----------------------------------------------------------------------------- headline
 
-def _events():
-    return torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-
-
 def bench_linear(steps: int, warmup: int):
-    """Headline step (quantise + GEMM) and the GEMM's own average launch time.
-
-    Both are timed over back-to-back launches between one pair of HIP events on the
-    stream the kernels run on, so per-launch event overhead does not inflate them."""
+    """Headline step = the 1x128 quantiser + the block-FP8 GEMM on one of several rotating input
+    sets (each with its own quantised buffers; > 600 MB in all, beyond the 256 MB last-level
+    cache).  One timed window of exactly `steps` steps with an event at every kernel boundary,
+    so the step, the quantiser and the GEMM durations all come from the same window."""
     from mxfp4_block_scaled_expert_amd import synth
     L, lib = _lib()
     dev = torch.device("cuda", 0)
     M, K, N = 2048, 2048, 7168
-    per_set = M * K * 2 + N * K + (N // 128) * (K // 128) * 4
+    per_set = M * K * 3 + N * K + (N // 128) * (K // 128) * 4 + M * (K // 128) * 4
     n_rot = max(2, -(-(600 << 20) // per_set))
     sets = [synth.block_linear(M, N, K, seed=1002 + i, device=dev) for i in range(n_rot)]
-    q = torch.empty(M, K, dtype=torch.uint8, device=dev)
-    s = torch.empty(M, K // 128, dtype=torch.float32, device=dev)
+    for d in sets:
+        d["q"] = torch.empty(M, K, dtype=torch.uint8, device=dev)
+        d["s"] = torch.empty(M, K // 128, dtype=torch.float32, device=dev)
     out = torch.empty(M, N, dtype=torch.bfloat16, device=dev)
-    stream = torch.cuda.current_stream()
-    sh = stream.cuda_stream
-    # pre-quantised activations of every set, for the GEMM-only timing
-    qs = [torch.empty_like(q) for _ in range(n_rot)]
-    ss = [torch.empty_like(s) for _ in range(n_rot)]
+    sh = torch.cuda.current_stream().cuda_stream
 
-    def quant(d, qq, sc):
-        _check(lib.mxq_per_token_group_quant_fp8(d["x"].data_ptr(), M, K, K, 128, qq.data_ptr(), sc.data_ptr(), sh),
-               "quant")
+    def quant(d):
+        _check(lib.mxq_per_token_group_quant_fp8(d["x"].data_ptr(), M, K, K, 128, d["q"].data_ptr(),
+                                                 d["s"].data_ptr(), sh), "quant")
 
-    def gemm(d, qq, sc):
-        _check(lib.mxq_block_fp8_linear(qq.data_ptr(), L.MXQ_DTYPE_E4M3, sc.data_ptr(), M, K, K, d["w"].data_ptr(), N,
-                                        d["sw"].data_ptr(), K // 128, 1, 128, 128, None, 0, out.data_ptr(),
-                                        L.MXQ_DTYPE_BF16, N, None, 0, sh), "block_fp8_linear")
+    def gemm(d):
+        _check(lib.mxq_block_fp8_linear(d["q"].data_ptr(), L.MXQ_DTYPE_E4M3, d["s"].data_ptr(), M, K, K,
+                                        d["w"].data_ptr(), N, d["sw"].data_ptr(), K // 128, 1, 128, 128, None, 0,
+                                        out.data_ptr(), L.MXQ_DTYPE_BF16, N, None, 0, sh), "block_fp8_linear")
 
-    for i in range(n_rot):
-        quant(sets[i], qs[i], ss[i])
-    for i in range(warmup):
-        quant(sets[i % n_rot], q, s)
-        gemm(sets[i % n_rot], q, s)
-    torch.cuda.synchronize()
-
-    # headline: K steps of the whole path
-    e0, e1 = _events()
-    t0 = time.perf_counter()
-    e0.record(stream)
-    for i in range(steps):
+    def step(i):
         d = sets[i % n_rot]
-        quant(d, q, s)
-        gemm(d, q, s)
-    e1.record(stream)
+        quant(d)
+        gemm(d)
+
+    settled = _settle(step, warmup)
+    hip = _hip()
+    ev = hip.create(2 * steps + 1)
+    t0 = time.perf_counter()
+    hip.record(ev[0], sh)
+    for i in range(steps):
+        d = sets[(settled + i) % n_rot]
+        quant(d)
+        hip.record(ev[2 * i + 1], sh)
+        gemm(d)
+        hip.record(ev[2 * i + 2], sh)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    step_ms = e0.elapsed_time(e1) / steps
-
-    # the dominant kernel alone, same rotation
-    g0, g1 = _events()
-    g0.record(stream)
-    for i in range(steps):
-        gemm(sets[i % n_rot], qs[i % n_rot], ss[i % n_rot])
-    g1.record(stream)
-    # the quantiser alone
-    q0, q1 = _events()
-    q0.record(stream)
-    for i in range(steps):
-        quant(sets[i % n_rot], q, s)
-    q1.record(stream)
-    torch.cuda.synchronize()
-    gemm_ms = g0.elapsed_time(g1) / steps
-    quant_ms = q0.elapsed_time(q1) / steps
+    step_us = [hip.us(ev[2 * i], ev[2 * i + 2]) for i in range(steps)]
+    quant_us = [hip.us(ev[2 * i], ev[2 * i + 1]) for i in range(steps)]
+    gemm_us = [hip.us(ev[2 * i + 1], ev[2 * i + 2]) for i in range(steps)]
+    window_us = hip.us(ev[0], ev[2 * steps])
+    hip.destroy(ev)
 
     flops = 2.0 * M * N * K
     gemm_bytes = M * K + M * (K // 128) * 4 + N * K + (N // 128) * (K // 128) * 4 + M * N * 2
     return {
-        "M": M, "K": K, "N": N, "flops": flops, "rotating_sets": n_rot,
-        "ms_per_step": step_ms, "wall_ms_per_step": wall * 1e3 / steps,
-        "quant_us_avg": quant_ms * 1e3, "gemm_us_avg": gemm_ms * 1e3,
-        "gemm_tflops": flops / (gemm_ms * 1e-3) / 1e12,
+        "M": M, "K": K, "N": N, "flops": flops, "rotating_sets": n_rot, "settle_steps": settled,
+        "ms_per_step": window_us / steps / 1e3, "wall_ms_per_step": wall * 1e3 / steps,
+        "step_us": _stats(step_us), "quant_us": _stats(quant_us), "gemm_us": _stats(gemm_us),
         "gemm_alg_bytes": gemm_bytes,
     }
+
+
+def bench_per_tensor(steps: int, warmup: int):
+    """The per-tensor W8A16 GEMM of the SGLang CPU page's test, bf16 [97, 576] x e4m3 [224, 576]^T
+    with an fp32 bias: launch-latency bound (0.29 MB, 25 MFLOP), reported in µs."""
+    from mxfp4_block_scaled_expert_amd import synth
+    L, lib = _lib()
+    dev = torch.device("cuda", 0)
+    M, K, N = 97, 576, 224
+    d = synth.dense_w8a16(M, N, K, seed=1001, device=dev)
+    out = torch.empty(M, N, dtype=torch.bfloat16, device=dev)
+    sh = torch.cuda.current_stream().cuda_stream
+
+    def run():
+        _check(lib.mxq_fp8_scaled_mm(d["a"].data_ptr(), M, K, K, d["w"].data_ptr(), N, d["scale"].data_ptr(),
+                                     d["bias"].data_ptr(), L.MXQ_DTYPE_F32, out.data_ptr(), N, sh), "fp8_scaled_mm")
+    st, _ = _time_calls(run, steps, warmup)
+    byts = M * K * 2 + N * K + N * 4 + M * N * 2
+    return {"workload": "per_tensor_w8a16_97x576x224", "us": st, "tflops": 2.0 * M * N * K / (st["median"] * 1e-6) / 1e12,
+            "gbs": byts / (st["median"] * 1e-6) / 1e9}
 
 
 # ----------------------------------------------------------------------------- MoE workloads
@@ -201,30 +324,15 @@ def _moe_setup(name_or_spec, seed: int, layout: str = "tiled", M=None, dispatch=
     return {"inp": inp, "run": run, "bytes": byts, "flops": flops, "M": Mt}
 
 
-def _time_calls(run, steps: int, warmup: int) -> float:
-    """Average µs of `steps` back-to-back calls between one pair of events (the weights of the
-    decode and prefill workloads exceed the 256 MB last-level cache, so every call streams them
-    from HBM)."""
-    for _ in range(warmup):
-        run()
-    torch.cuda.synchronize()
-    stream = torch.cuda.current_stream()
-    e0, e1 = _events()
-    e0.record(stream)
-    for _ in range(steps):
-        run()
-    e1.record(stream)
-    torch.cuda.synchronize()
-    return e0.elapsed_time(e1) / steps * 1e3
-
-
 def bench_moe(name: str, steps: int, warmup: int, seed: int, layout: str = "tiled"):
-    """Times one fused-MoE workload."""
+    """Times one fused-MoE workload: per-call durations (median, p10, p90), throughput from the
+    median."""
     w = _moe_setup(name, seed, layout)
-    us = _time_calls(w["run"], steps, warmup)
+    st, _ = _time_calls(w["run"], steps, warmup)
+    us = st["median"]
     byts, flops = w["bytes"], w["flops"]
     return {
-        "workload": name, "weight_layout": layout, "us_avg": us, "tflops": flops / (us * 1e-6) / 1e12,
+        "workload": name, "weight_layout": layout, "us": st, "tflops": flops / (us * 1e-6) / 1e12,
         "touched_bytes": byts, "weight_gbs": byts / (us * 1e-6) / 1e9,
         "hbm_frac": byts / (us * 1e-6) / 1e9 / HBM_PEAK_GBS,
         "fp8_mfma_frac": flops / (us * 1e-6) / 1e12 / FP8_PEAK_TFLOPS,
@@ -253,9 +361,10 @@ def bench_mla_bmm(steps: int, warmup: int, tokens: int = 64):
             _check(lib.mxq_fp8_scaled_bmm(d["a"].data_ptr(), B, T, K, K, T * K, d["w"].data_ptr(), N, N * K,
                                           d["scale"].data_ptr(), 1, None, 0, 0, out.data_ptr(), N, T * N,
                                           st.cuda_stream), "mxq_fp8_scaled_bmm")
-        us = _time_calls(run, steps, warmup)
+        st_, _ = _time_calls(run, steps, warmup)
+        us = st_["median"]
         byts = B * N * K + B * T * K * 2 + B * T * N * 2
-        res[name] = {"shape": f"{B}x[{T},{K}]x[{N},{K}]^T", "us_avg": us, "gbs": byts / (us * 1e-6) / 1e9,
+        res[name] = {"shape": f"{B}x[{T},{K}]x[{N},{K}]^T", "us": st_, "gbs": byts / (us * 1e-6) / 1e9,
                      "hbm_frac": byts / (us * 1e-6) / 1e9 / HBM_PEAK_GBS}
         del sets
     return res
@@ -287,7 +396,7 @@ def bench_dispatch_ablation(steps: int, warmup: int):
         res = {}
         for mode, key in ((L.MXQ_DISPATCH_PER_BLOCK, "per_block_us"), (L.MXQ_DISPATCH_LAYER_AVERAGE, "layer_avg_us")):
             sel[0] = ops.Dispatch(mode, 0, 16)
-            res[key] = _time_calls(w["run"], n, wu)
+            res[key] = _time_calls(w["run"], n, wu)[0]["median"]
         row = {"case": label, "M": w["M"], **res, "speedup": res["layer_avg_us"] / res["per_block_us"],
                "per_block_weight_gbs": w["bytes"] / (res["per_block_us"] * 1e-6) / 1e9}
         print(json.dumps(row), flush=True)
@@ -338,6 +447,9 @@ def calibrate_copy(steps: int = 10, mib: int = 256):
 
 def main():
     a = _args()
+    global SETTLE_S
+    if a.settle is not None:
+        SETTLE_S = a.settle
     if a.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
                           "requested_gpus": a.gpus}), flush=True)
@@ -362,28 +474,39 @@ def main():
         print(json.dumps(bench_moe("moe_block_fp8_w8a8_deepseek_prefill_m4096", a.steps, a.warmup, 1005)),
               flush=True)
         return
+    if a.only == "small":
+        print(json.dumps(bench_per_tensor(a.steps, a.warmup)), flush=True)
+        print(json.dumps(bench_moe("moe_block_fp8_w8a16_e8_h2048_i1024", a.steps, a.warmup, 1003)), flush=True)
+        return
 
     lin = bench_linear(a.steps, a.warmup)
     if a.only == "linear":
         print(json.dumps(lin), flush=True)
         return
     value = lin["flops"] / (lin["ms_per_step"] * 1e-3) / 1e12
+    g_us = lin["gemm_us"]["mean"]
+    achieved = lin["flops"] / (g_us * 1e-6) / 1e12
+    traffic, traffic_note = stamped_traffic()
     roof = {
         "kernel": "gemm_w8a8_big_kernel (block-FP8 W8A8, 256x256 tiles, direct-to-LDS operands)",
-        "bound": "mfma", "achieved": lin["gemm_tflops"], "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s",
-        "frac": lin["gemm_tflops"] / FP8_PEAK_TFLOPS, "traffic": GEMM_TRAFFIC_BYTES,
+        "bound": "mfma", "achieved": achieved, "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s",
+        "frac": achieved / FP8_PEAK_TFLOPS, "traffic": traffic, "traffic_source": traffic_note,
         "alg_flops_per_launch": lin["flops"], "alg_bytes_per_launch": lin["gemm_alg_bytes"],
-        "avg_launch_us": lin["gemm_us_avg"],
+        "avg_launch_us": g_us, "launch_us": lin["gemm_us"],
     }
     secondary = {}
     if not a.no_secondary:
-        secondary["gptoss_mxfp4_decode_m32"] = bench_moe("moe_mxfp4_gptoss_decode_m32", max(10, a.steps // 2),
+        secondary["per_tensor_w8a16_97x576x224"] = bench_per_tensor(a.steps, a.warmup)
+        secondary["w8a16_small_blocks_e8"] = bench_moe("moe_block_fp8_w8a16_e8_h2048_i1024", a.steps, a.warmup,
+                                                       1003)
+        torch.cuda.empty_cache()
+        secondary["gptoss_mxfp4_decode_m32"] = bench_moe("moe_mxfp4_gptoss_decode_m32", max(10, a.steps),
                                                         a.warmup, 1004)
         torch.cuda.empty_cache()
         secondary["deepseek_w8a8_prefill_m4096"] = bench_moe("moe_block_fp8_w8a8_deepseek_prefill_m4096",
-                                                            max(3, a.steps // 10), 2, 1005)
+                                                            max(5, a.steps // 2), 2, 1005)
         torch.cuda.empty_cache()
-        secondary["mla_bmm_128heads_t64"] = bench_mla_bmm(max(10, a.steps // 2), a.warmup)
+        secondary["mla_bmm_128heads_t64"] = bench_mla_bmm(max(10, a.steps), a.warmup)
         torch.cuda.empty_cache()
     cpu = None if a.no_cpu_baseline else cpu_baseline()
     line = {
@@ -393,7 +516,9 @@ def main():
         "config": {"workload": "block_w8a8_linear_2048x2048x7168 (1x128 act quant + 128x128 weight blocks)",
                    "M": lin["M"], "K": lin["K"], "N": lin["N"], "rotating_input_sets": lin["rotating_sets"]},
         "roofline": roof, "cpu_baseline": cpu,
-        "detail": {k: lin[k] for k in ("quant_us_avg", "gemm_us_avg", "wall_ms_per_step")},
+        "detail": {"step_us": lin["step_us"], "quant_us": lin["quant_us"], "gemm_us": lin["gemm_us"],
+                   "wall_ms_per_step": lin["wall_ms_per_step"], "settle_steps": lin["settle_steps"],
+                   "settle_s": SETTLE_S},
         "secondary": secondary,
     }
     print(json.dumps(line), flush=True)
