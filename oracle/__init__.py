@@ -26,6 +26,8 @@ Modules:
 * ``dense``   -- per-tensor W8A16 GEMM and block-scaled W8A8 / W8A16 linears.
 * ``align``   -- expert sort / block alignment of routed rows.
 * ``moe``     -- routed fused-MoE experts (FP8 block and MXFP4 weights).
+* ``mx``      -- MXFP8 quantisation (e4m3 + e8m0 per 32) and the MX-scaled linear
+  (MXFP8 activations x MXFP8 / MXFP4 weights).
 
 Every function has at least one pin in ``tests/test_oracle_*.py`` that checks
 it against something other than itself (library routines, closed forms,
@@ -33,4 +35,4 @@ brute force, invariants).  The one unpinned piece is the exponential inside
 SiLU (host libm vs device math): only the bf16 tolerance covers it.
 """
 
-from . import codecs, quant, dense, align, moe  # noqa: F401
+from . import codecs, quant, dense, align, moe, mx  # noqa: F401
