@@ -66,7 +66,7 @@ def _args():
     p.add_argument("--no-secondary", action="store_true")
     p.add_argument("--settle", type=float, default=None,
                    help="seconds of untimed load before each timed window (default 0.3; profiling runs use 0)")
-    p.add_argument("--only", choices=["linear", "decode", "prefill", "small", "copy", "ablation"], default=None,
+    p.add_argument("--only", choices=["linear", "decode", "prefill", "small", "mx", "copy", "ablation"], default=None,
                    help="time one workload only (profiling runs); small = the per-tensor GEMM and the "
                         "small-block W8A16 MoE; copy = counter calibration; ablation = per-block vs "
                         "per-layer tile-class dispatch")
@@ -274,6 +274,49 @@ def bench_per_tensor(steps: int, warmup: int):
             "gbs": byts / (st["median"] * 1e-6) / 1e9}
 
 
+def bench_mx(steps: int, warmup: int, w_format: str):
+    """The MX-scaled linear at the headline size, 2048 x 2048 x 7168: MXFP8 activations (e4m3 +
+    e8m0 per 32, quantised before timing) x MXFP4 (``e2m1``) or MXFP8 (``e4m3``) weights, on
+    rotating input sets beyond the last-level cache; and the MXFP8 quantiser of the bf16 input."""
+    from mxfp4_block_scaled_expert_amd import synth
+    L, lib = _lib()
+    dev = torch.device("cuda", 0)
+    M, K, N = 2048, 2048, 7168
+    wbytes = N * K // (2 if w_format == "e2m1" else 1)
+    per_set = M * K * 3 + wbytes + N * K // 32 + M * K // 32
+    n_rot = max(2, -(-(600 << 20) // per_set))
+    sets = []
+    for i in range(n_rot):
+        d = synth.mx_linear(M, N, K, seed=3000 + i, device=dev, w_format=w_format)
+        d["q"] = torch.empty(M, K, dtype=torch.uint8, device=dev)
+        d["s"] = torch.empty(M, K // 32, dtype=torch.uint8, device=dev)
+        sets.append(d)
+    out = torch.empty(M, N, dtype=torch.bfloat16, device=dev)
+    sh = torch.cuda.current_stream().cuda_stream
+    wd = L.MXQ_DTYPE_E2M1 if w_format == "e2m1" else L.MXQ_DTYPE_E4M3
+    it = [0]
+
+    def quant():
+        d = sets[it[0] % n_rot]
+        it[0] += 1
+        _check(lib.mxq_mxfp8_quant(d["x"].data_ptr(), M, K, K, d["q"].data_ptr(), d["s"].data_ptr(), sh), "quant")
+
+    def gemm():
+        d = sets[it[0] % n_rot]
+        it[0] += 1
+        _check(lib.mxq_mx_linear(d["q"].data_ptr(), L.MXQ_DTYPE_E4M3, d["s"].data_ptr(), M, K, K, d["w"].data_ptr(),
+                                 wd, N, d["sw"].data_ptr(), None, 0, out.data_ptr(), N, None, 0, sh), "mx_linear")
+    for _ in range(n_rot):
+        quant()
+    q_st, _ = _time_calls(quant, steps, warmup)
+    g_st, _ = _time_calls(gemm, steps, warmup)
+    flops = 2.0 * M * N * K
+    us = g_st["mean"]
+    return {"workload": f"mx_linear_2048x2048x7168 MXFP8 activations x {'MXFP4' if w_format == 'e2m1' else 'MXFP8'} "
+                        "weights", "gemm_us": g_st, "quant_us": q_st, "tflops": flops / (us * 1e-6) / 1e12,
+            "fp8_mfma_frac": flops / (us * 1e-6) / 1e12 / FP8_PEAK_TFLOPS}
+
+
 # ----------------------------------------------------------------------------- MoE workloads
 
 def _touched_bytes(inp) -> int:
@@ -474,6 +517,10 @@ def main():
         print(json.dumps(bench_moe("moe_block_fp8_w8a8_deepseek_prefill_m4096", a.steps, a.warmup, 1005)),
               flush=True)
         return
+    if a.only == "mx":
+        print(json.dumps(bench_mx(a.steps, a.warmup, "e2m1")), flush=True)
+        print(json.dumps(bench_mx(a.steps, a.warmup, "e4m3")), flush=True)
+        return
     if a.only == "small":
         print(json.dumps(bench_per_tensor(a.steps, a.warmup)), flush=True)
         print(json.dumps(bench_moe("moe_block_fp8_w8a16_e8_h2048_i1024", a.steps, a.warmup, 1003)), flush=True)
@@ -507,6 +554,10 @@ def main():
                                                             max(5, a.steps // 2), 2, 1005)
         torch.cuda.empty_cache()
         secondary["mla_bmm_128heads_t64"] = bench_mla_bmm(max(10, a.steps), a.warmup)
+        torch.cuda.empty_cache()
+        secondary["mx_linear_mxfp4_weights"] = bench_mx(a.steps, a.warmup, "e2m1")
+        torch.cuda.empty_cache()
+        secondary["mx_linear_mxfp8_weights"] = bench_mx(a.steps, a.warmup, "e4m3")
         torch.cuda.empty_cache()
     cpu = None if a.no_cpu_baseline else cpu_baseline()
     line = {

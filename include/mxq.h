@@ -61,6 +61,7 @@ typedef int32_t mxq_status;
 #define MXQ_DTYPE_BF16 0
 #define MXQ_DTYPE_F32 1
 #define MXQ_DTYPE_E4M3 2
+#define MXQ_DTYPE_E2M1 3  /* packed OCP MX FP4, element 2j in the low nibble of byte j */
 
 /* Text for a status code (static storage, never NULL). */
 const char* mxq_status_string(mxq_status status);
@@ -168,6 +169,39 @@ mxq_status mxq_block_fp8_linear_noalloc(const void* A, int32_t a_dtype, const fl
                                         int64_t ws_stride0, int64_t ws_stride1, int32_t block_n, int32_t block_k,
                                         const void* bias, int32_t bias_dtype, void* out, int32_t out_dtype,
                                         int64_t ldo, void* stream);
+
+/* ------------------------------------------------------------------ MX-scaled quantise and linear
+ * The MX block formats the pages name: MXFP4 expert weights (page [A], summary and
+ * implementation item 2: e2m1 elements, one e8m0 scale per 32 elements of a row) and the
+ * [1, 32] activation block recipe (page [C], implementation item 1), here as MXFP8: e4m3
+ * elements with one e8m0 scale per 32 elements of a row.  The multiplications run on gfx950's
+ * MX-scaled matrix instruction (V_MFMA_SCALE_F32_16X16X128_F8F6F4), which applies both
+ * operands' e8m0 scales itself.
+ *
+ * mxq_mxfp8_quant: per row, per 32 columns (the OCP MX conversion rule):
+ *   e = floor(log2(max|x|)) - 8 (8: the exponent of e4m3's largest normal), clamped to
+ *   [-127, 127] (an all-zero block: -127);  s = e + 127 (e8m0);  q = e4m3_rne(clamp(x / 2^e, +-448)).
+ *   Codes and scales are exact (bit-for-bit) results.
+ *   x   bf16 [M, K], row stride ldx elements (ldx >= K, multiple of 8); K % 32 == 0
+ *   q   e4m3 [M, K] contiguous;  s  e8m0 [M, K/32] contiguous.  M == 0 or K == 0: no-op.
+ *
+ * mxq_mx_linear: out[m, n] = bf16( sum_k a[m, k] w[n, k] + bias[n] ),
+ *   a = dec(qa) * 2^(sa - 127), w = dec(qw) * 2^(sw - 127), fp32 accumulation.
+ *   A        a_dtype MXQ_DTYPE_BF16: bf16 [M, K] (row stride lda elements), quantised inside
+ *            the call exactly as mxq_mxfp8_quant does (workspace of
+ *            mxq_mx_linear_workspace_size bytes); a_dtype MXQ_DTYPE_E4M3: codes [M, K] (row
+ *            stride lda bytes, a multiple of 16) with a_scale e8m0 [M, K/32] contiguous.
+ *   W        w_dtype MXQ_DTYPE_E4M3: e4m3 [N, K];  MXQ_DTYPE_E2M1: packed e2m1 [N, K/2];
+ *            contiguous, with w_scale e8m0 [N, K/32] contiguous (4-byte aligned).
+ *   bias     NULL or [N] of bias_dtype (fp32 or bf16), added in fp32
+ *   out      bf16 [M, N], row stride ldo elements
+ *   K must be a multiple of 128; every operand below 4 GiB (else MXQ_ERR_SHAPE). */
+mxq_status mxq_mxfp8_quant(const void* x, int64_t M, int64_t K, int64_t ldx, void* q, void* s, void* stream);
+size_t mxq_mx_linear_workspace_size(int64_t M, int64_t K, int32_t a_dtype);
+mxq_status mxq_mx_linear(const void* A, int32_t a_dtype, const void* a_scale, int64_t M, int64_t K, int64_t lda,
+                         const void* W, int32_t w_dtype, int64_t N, const void* w_scale, const void* bias,
+                         int32_t bias_dtype, void* out, int64_t ldo, void* workspace, size_t workspace_bytes,
+                         void* stream);
 
 /* ------------------------------------------------------------------ expert sort / align
  * Groups the R = M * topk routed rows (flat id r = t * topk + k) by expert for the

@@ -11,6 +11,8 @@ from .ops import (  # noqa: F401
     fp8_scaled_mm,
     fp8_scaled_bmm,
     block_fp8_linear,
+    mxfp8_quant,
+    mx_linear,
     moe_max_blocks,
     moe_align,
     fused_moe_fp8,

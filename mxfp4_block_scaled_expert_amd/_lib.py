@@ -27,6 +27,7 @@ MXQ_NOALLOC_SCRATCH_BYTES = 32 << 20
 MXQ_DTYPE_BF16 = 0
 MXQ_DTYPE_F32 = 1
 MXQ_DTYPE_E4M3 = 2
+MXQ_DTYPE_E2M1 = 3
 
 MXQ_WEIGHTS_FP8_BLOCK = 0
 MXQ_WEIGHTS_MXFP4 = 1
@@ -70,6 +71,9 @@ SIGNATURES = {
                                      _p, _i32, _p, _i32, _i64, _p, _sz, _p]),
     "mxq_block_fp8_linear_noalloc": (_i32, [_p, _i32, _p, _i64, _i64, _i64, _p, _i64, _p, _i64, _i64, _i32,
                                              _i32, _p, _i32, _p, _i32, _i64, _p]),
+    "mxq_mxfp8_quant": (_i32, [_p, _i64, _i64, _i64, _p, _p, _p]),
+    "mxq_mx_linear_workspace_size": (_sz, [_i64, _i64, _i32]),
+    "mxq_mx_linear": (_i32, [_p, _i32, _p, _i64, _i64, _i64, _p, _i32, _i64, _p, _p, _i32, _p, _i64, _p, _sz, _p]),
     "mxq_moe_max_blocks": (_i64, [_i64, _i32, _i32, _i32]),
     "mxq_moe_align": (_i32, [_p, _i64, _i32, _i32, _i32, _p, _p, _p, _p, _p]),
     "mxq_fused_moe_workspace_size": (_sz, [_i64, _i64, _i64, _i32, _i32, _i32, _i32]),

@@ -405,7 +405,7 @@ const char* mxq_status_string(mxq_status s) {
   }
 }
 
-int32_t mxq_abi_version(void) { return 6; }
+int32_t mxq_abi_version(void) { return 7; }
 
 mxq_status mxq_init(int32_t device) {
   if (hipSetDevice(device) != hipSuccess) return MXQ_ERR_ARCH;
@@ -576,6 +576,76 @@ mxq_status mxq_block_fp8_linear_noalloc(const void* A, int32_t a_dtype, const fl
   }
   return mxq_block_fp8_linear(A, a_dtype, a_scale, M, K, lda, W, N, w_scale, ws_stride0, ws_stride1, block_n,
                               block_k, bias, bias_dtype, out, out_dtype, ldo, ws, need, stream);
+}
+
+mxq_status mxq_mxfp8_quant(const void* x, int64_t M, int64_t K, int64_t ldx, void* q, void* s, void* stream) {
+  if (M < 0 || K < 0 || K % 32 != 0 || ldx < K || ldx % 8 != 0) return MXQ_ERR_SHAPE;
+  if (M == 0 || K == 0) return MXQ_OK;
+  if (!x || !q || !s) return MXQ_ERR_NULL;
+  if (!aligned16(x) || (reinterpret_cast<uintptr_t>(q) & 7u)) return MXQ_ERR_SHAPE;
+  MXQ_TRY(check_arch());
+  launch_quant_mx(static_cast<const uint16_t*>(x), M, K, ldx, static_cast<uint8_t*>(q), static_cast<uint8_t*>(s),
+                  static_cast<hipStream_t>(stream));
+  return launch_status();
+}
+
+size_t mxq_mx_linear_workspace_size(int64_t M, int64_t K, int32_t a_dtype) {
+  if (a_dtype != MXQ_DTYPE_BF16 || M <= 0 || K <= 0) return 0;
+  return align256(size_t(M) * K) + align256(size_t(M) * (K / 32));
+}
+
+mxq_status mxq_mx_linear(const void* A, int32_t a_dtype, const void* a_scale, int64_t M, int64_t K, int64_t lda,
+                         const void* W, int32_t w_dtype, int64_t N, const void* w_scale, const void* bias,
+                         int32_t bias_dtype, void* out, int64_t ldo, void* workspace, size_t workspace_bytes,
+                         void* stream) {
+  if (a_dtype != MXQ_DTYPE_BF16 && a_dtype != MXQ_DTYPE_E4M3) return MXQ_ERR_DTYPE;
+  if (w_dtype != MXQ_DTYPE_E4M3 && w_dtype != MXQ_DTYPE_E2M1) return MXQ_ERR_DTYPE;
+  if (bias && bias_dtype != MXQ_DTYPE_F32 && bias_dtype != MXQ_DTYPE_BF16) return MXQ_ERR_DTYPE;
+  if (M < 0 || N < 0 || K < 0 || K % 128 != 0 || lda < K || ldo < N) return MXQ_ERR_SHAPE;
+  if (a_dtype == MXQ_DTYPE_BF16 ? (lda % 8 != 0) : (lda % 16 != 0)) return MXQ_ERR_SHAPE;
+  if (M == 0 || N == 0) return MXQ_OK;
+  if (K == 0) return MXQ_ERR_SHAPE;
+  if (!A || !W || !w_scale || !out) return MXQ_ERR_NULL;
+  if (a_dtype == MXQ_DTYPE_E4M3 && !a_scale) return MXQ_ERR_NULL;
+  const int64_t wrow = w_dtype == MXQ_DTYPE_E2M1 ? K / 2 : K;
+  // operands are addressed with 32-bit byte offsets inside the kernel
+  constexpr int64_t k4G = int64_t(1) << 32;
+  if (M * std::max<int64_t>(lda, K) >= k4G || N * wrow >= k4G || std::max(M, N) * (K / 32) >= k4G)
+    return MXQ_ERR_SHAPE;
+  if (!aligned16(A) || !aligned16(W) || (reinterpret_cast<uintptr_t>(w_scale) & 3u) ||
+      (a_scale && (reinterpret_cast<uintptr_t>(a_scale) & 3u)))
+    return MXQ_ERR_SHAPE;
+  MXQ_TRY(check_arch());
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  MxArgs g{};
+  g.A = A;
+  g.lda = lda;
+  g.sa = a_scale;
+  g.lds_bytes = K / 32;
+  if (a_dtype == MXQ_DTYPE_BF16) {
+    const size_t need = mxq_mx_linear_workspace_size(M, K, a_dtype);
+    if (!workspace || workspace_bytes < need) return MXQ_ERR_WORKSPACE;
+    uint8_t* q = static_cast<uint8_t*>(workspace);
+    uint8_t* s = q + align256(size_t(M) * K);
+    launch_quant_mx(static_cast<const uint16_t*>(A), M, K, lda, q, s, st);
+    g.A = q;
+    g.lda = K;
+    g.sa = s;
+  }
+  g.W = W;
+  g.ldw = wrow;
+  g.sw = w_scale;
+  g.ldws_bytes = K / 32;
+  g.w_fmt = w_dtype == MXQ_DTYPE_E2M1 ? MX_W_E2M1 : MX_W_E4M3;
+  g.bias = bias;
+  g.bias_bf16 = bias_dtype == MXQ_DTYPE_BF16;
+  g.out = out;
+  g.ldo = ldo;
+  g.M = M;
+  g.N = N;
+  g.K = K;
+  launch_gemm_mx(g, st);
+  return launch_status();
 }
 
 int64_t mxq_moe_max_blocks(int64_t M, int32_t topk, int32_t E, int32_t block_m) {

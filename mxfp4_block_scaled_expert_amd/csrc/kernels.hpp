@@ -63,6 +63,29 @@ struct GemmArgs {
   int64_t a_bstride, o_bstride;
 };
 
+// MX-scaled dense GEMM (gemm_mx.hip): MXFP8 activations x MXFP8 / MXFP4 weights.
+enum MxWFmt : int { MX_W_E4M3 = 0, MX_W_E2M1 = 1 };
+struct MxArgs {
+  const void* A;       // e4m3 [M, K], row stride lda bytes
+  int64_t lda;
+  const void* sa;      // e8m0 [M, K/32], row stride lds_bytes
+  int64_t lds_bytes;
+  const void* W;       // e4m3 [N, K] or packed e2m1 [N, K/2], row stride ldw bytes
+  int64_t ldw;
+  const void* sw;      // e8m0 [N, K/32], row stride ldws_bytes
+  int64_t ldws_bytes;
+  int32_t w_fmt;       // MxWFmt
+  const void* bias;    // NULL or [N] fp32 / bf16
+  int32_t bias_bf16;
+  void* out;           // bf16 [M, N], row stride ldo elements
+  int64_t ldo;
+  int64_t M, N, K;     // K % 128 == 0
+};
+void launch_gemm_mx(const MxArgs& a, hipStream_t stream);
+// bf16 [M, K] (row stride ldx) -> e4m3 [M, K] (contiguous) + e8m0 [M, K/32] (contiguous)
+void launch_quant_mx(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, uint8_t* q, uint8_t* s,
+                     hipStream_t stream);
+
 // ---------------------------------------------------------------- launchers
 
 void launch_quant_1x128(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, uint8_t* q, int64_t ldq,

@@ -218,6 +218,75 @@ def block_fp8_linear(x: torch.Tensor, weight: torch.Tensor, block_size: Sequence
     return out.view(*x.shape[:-1], N)
 
 
+def mxfp8_quant(x: torch.Tensor) -> Tuple[torch.Tensor, torch.Tensor]:
+    """bf16 [..., K] -> (e4m3 codes [..., K] as float8_e4m3fn, e8m0 scale codes uint8 [..., K/32])."""
+    if x.dtype != torch.bfloat16:
+        raise ValueError("x must be bf16")
+    _require_cuda(x)
+    shape = x.shape
+    x2 = x.reshape(-1, shape[-1])
+    if x2.stride(-1) != 1 or x2.data_ptr() % 16 or x2.stride(0) % 8:
+        x2 = x2.contiguous()
+    M, K = x2.shape
+    q = torch.empty((M, K), dtype=torch.uint8, device=x.device)
+    s = torch.empty((M, K // 32), dtype=torch.uint8, device=x.device)
+    L.check("mxq_mxfp8_quant", L.load().mxq_mxfp8_quant(x2.data_ptr(), M, K, x2.stride(0), q.data_ptr(),
+                                                         s.data_ptr(), _stream()))
+    return q.view(_E4M3).view(*shape), s.view(*shape[:-1], s.shape[-1])
+
+
+_MX_W = {"e4m3": L.MXQ_DTYPE_E4M3, "e2m1": L.MXQ_DTYPE_E2M1}
+
+
+def mx_linear(x: torch.Tensor, weight: torch.Tensor, weight_scale: torch.Tensor, w_format: str = "e2m1",
+              input_scale: Optional[torch.Tensor] = None, bias: Optional[torch.Tensor] = None,
+              out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """MX-scaled linear -> bf16 [..., N].
+
+    ``x``: bf16 [..., K] (MXFP8-quantised per token per 32 columns inside the call), or e4m3
+    codes with ``input_scale`` e8m0 uint8 [..., K/32].  ``weight``: e4m3 [N, K]
+    (``w_format="e4m3"``, MXFP8) or packed e2m1 uint8 [N, K/2] (``"e2m1"``, MXFP4) with
+    ``weight_scale`` e8m0 uint8 [N, K/32]."""
+    if w_format not in _MX_W:
+        raise ValueError(f"w_format must be 'e4m3' or 'e2m1', got {w_format!r}")
+    w = _as_u8(weight, "weight").contiguous()
+    sw = weight_scale.contiguous()
+    if sw.dtype != torch.uint8:
+        raise ValueError("weight_scale must be uint8 e8m0 codes")
+    _require_cuda(x, w, sw, input_scale, bias)
+    N = w.shape[0]
+    K = w.shape[1] * (2 if w_format == "e2m1" else 1)
+    if input_scale is None:
+        if x.dtype != torch.bfloat16:
+            raise ValueError("x must be bf16 when input_scale is None")
+        a, a_dtype, a_scale = _2d(x), L.MXQ_DTYPE_BF16, None
+    else:
+        a, a_dtype = _2d(_as_u8(x, "x")), L.MXQ_DTYPE_E4M3
+        a_scale = input_scale.reshape(-1, input_scale.shape[-1]).contiguous()
+        if a_scale.dtype != torch.uint8:
+            raise ValueError("input_scale must be uint8 e8m0 codes")
+    M = a.shape[0]
+    if a.shape[1] != K:
+        raise ValueError(f"weight K {K} != input K {a.shape[1]}")
+    if tuple(sw.shape) != (N, K // 32):
+        raise ValueError(f"weight_scale must be [{N}, {K // 32}]")
+    if a_scale is not None and tuple(a_scale.shape) != (M, K // 32):
+        raise ValueError("input_scale must be [..., K/32]")
+    b = None if bias is None else bias.contiguous()
+    if b is not None and b.numel() != N:
+        raise ValueError("bias must have N elements")
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
+    lib = L.load()
+    ws_bytes = lib.mxq_mx_linear_workspace_size(M, K, a_dtype)
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=x.device)
+    st = lib.mxq_mx_linear(a.data_ptr(), a_dtype, _ptr(a_scale), M, K, a.stride(0), w.data_ptr(), _MX_W[w_format], N,
+                           sw.data_ptr(), _ptr(b), _bias_dtype(b), out.data_ptr(), N, ws.data_ptr(), ws_bytes,
+                           _stream())
+    L.check("mxq_mx_linear", st)
+    return out.view(*x.shape[:-1], N)
+
+
 def moe_max_blocks(M: int, topk: int, E: int, block_m: int) -> int:
     return int(L.load().mxq_moe_max_blocks(M, topk, E, block_m))
 

@@ -144,6 +144,24 @@ def block_linear(M: int, N: int, K: int, seed: int, device="cpu", block_n: int =
     return {"x": x, "w": w, "sw": sw, "bias": bias, "block_n": block_n}
 
 
+def mx_linear(M: int, N: int, K: int, seed: int, device="cpu", w_format: str = "e2m1",
+              bias_dtype: Optional[torch.dtype] = None) -> Dict[str, torch.Tensor]:
+    """bf16 ``randn`` activations and MX weights: MXFP4 (``"e2m1"``) from ``0.05 * randn`` by the
+    OCP rule, or MXFP8 (``"e4m3"``) drawn as codes ``e4m3(clamp(100 * randn, +-448))`` with e8m0
+    scale codes uniform in [110, 114] (2^-17 .. 2^-13, decoded weights ~0.05 * randn)."""
+    g = _gen(seed, device)
+    x = bf16_randn((M, K), g, device)
+    if w_format == "e2m1":
+        w, sw = mxfp4_quantize(torch.randn(N, K, generator=g, device=device) * WEIGHT_STD)
+    else:
+        w = fp8_codes((N, K), g, device)
+        sw = torch.randint(110, 115, (N, K // 32), generator=g, device=device, dtype=torch.int32).to(torch.uint8)
+    bias = None
+    if bias_dtype is not None:
+        bias = torch.randn(N, generator=g, device=device).to(bias_dtype)
+    return {"x": x, "w": w, "sw": sw, "bias": bias, "w_format": w_format}
+
+
 # --------------------------------------------------------------------------- routing
 
 def route_counts(counts: Sequence[int], device="cpu"):

@@ -43,7 +43,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_status_strings_and_version():
     L, lib = _lib()
-    assert lib.mxq_abi_version() == 6
+    assert lib.mxq_abi_version() == 7
     for code in range(0, 10):
         assert lib.mxq_status_string(code)
     assert b"unknown" in lib.mxq_status_string(99)
