@@ -66,7 +66,10 @@ def _args():
     p.add_argument("--no-secondary", action="store_true")
     p.add_argument("--settle", type=float, default=None,
                    help="seconds of untimed load before each timed window (default 0.3; profiling runs use 0)")
-    p.add_argument("--only", choices=["linear", "decode", "prefill", "small", "mx", "copy", "ablation"], default=None,
+    p.add_argument("--sweep-shape", default=None, help="class sweep: comma list of shapes (default all)")
+    p.add_argument("--sweep-m", default=None, help="class sweep: comma list of rows per block (default all)")
+    p.add_argument("--only", choices=["linear", "decode", "prefill", "small", "mx", "copy", "ablation", "classes"],
+                   default=None,
                    help="time one workload only (profiling runs); small = the per-tensor GEMM and the "
                         "small-block W8A16 MoE; copy = counter calibration; ablation = per-block vs "
                         "per-layer tile-class dispatch")
@@ -425,6 +428,7 @@ def bench_dispatch_ablation(steps: int, warmup: int):
         ("c3 counts (4,5,33,0,0,12,1,73), W8A16", "moe_block_fp8_w8a16_e8_h2048_i1024", None, 1003),
         ("GPT-OSS MXFP4 decode M=32", "moe_mxfp4_gptoss_decode_m32", 32, 1004),
         ("GPT-OSS MXFP4 decode M=64", "moe_mxfp4_gptoss_decode_m32", 64, 1004),
+        ("DeepSeek W8A8 M=64 Zipf 1.1", dict(ds, zipf=1.1), 64, 1005),
         ("DeepSeek W8A8 M=512 uniform", dict(ds, zipf=0.0), 512, 1005),
         ("DeepSeek W8A8 M=512 Zipf 1.1", dict(ds, zipf=1.1), 512, 1005),
         ("DeepSeek W8A8 M=4096 uniform", dict(ds, zipf=0.0), 4096, 1005),
@@ -438,7 +442,7 @@ def bench_dispatch_ablation(steps: int, warmup: int):
         n, wu = (max(3, steps // 10), 2) if big else (steps, warmup)
         res = {}
         for mode, key in ((L.MXQ_DISPATCH_PER_BLOCK, "per_block_us"), (L.MXQ_DISPATCH_LAYER_AVERAGE, "layer_avg_us")):
-            sel[0] = ops.Dispatch(mode, 0, 16)
+            sel[0] = ops.Dispatch(mode)
             res[key] = _time_calls(w["run"], n, wu)[0]["median"]
         row = {"case": label, "M": w["M"], **res, "speedup": res["layer_avg_us"] / res["per_block_us"],
                "per_block_weight_gbs": w["bytes"] / (res["per_block_us"] * 1e-6) / 1e9}
@@ -446,6 +450,47 @@ def bench_dispatch_ablation(steps: int, warmup: int):
         rows.append(row)
         del w
         torch.cuda.empty_cache()
+    return rows
+
+
+SWEEP_SHAPES = {
+    # (spec with the experts that receive rows, active experts)
+    "gptoss_mxfp4": (dict(kind="fused_moe_mxfp4", H=2880, I=2880), 32),
+    "deepseek_w8a8": (dict(kind="fused_moe_fp8", H=7168, I=2048, act_quant=True), 32),
+    "w8a16_e8": (dict(kind="fused_moe_fp8", H=2048, I=1024, act_quant=False), 8),
+}
+SWEEP_M = (1, 2, 4, 8, 12, 16, 24, 32, 48, 64, 96, 128)
+
+
+def bench_class_sweep(steps: int, warmup: int, shapes=None, ms=None):
+    """Evidence for the per-block tile-class bounds: `E` experts each receive exactly m routed
+    rows (top-1, so every block holds m rows), the fused MoE runs with every class forced in
+    turn (0 = tiny-block kernel, 1..4 = 16/32/64/128-row tiles) and with the per-block default;
+    one JSON line per (shape, m) with the median µs per call and the touched-weight GB/s of
+    each."""
+    from mxfp4_block_scaled_expert_amd import ops, synth
+    from mxfp4_block_scaled_expert_amd import _lib as L
+    rows = []
+    for name in (shapes or SWEEP_SHAPES):
+        base, E = SWEEP_SHAPES[name]
+        for m in (ms or SWEEP_M):
+            spec = dict(base, E=E, topk=1, counts=tuple([m] * E))
+            sel = [None]
+            w = _moe_setup(spec, 1100 + m, "tiled", dispatch=sel)
+            res = {"shape": name, "m": m, "experts": E}
+            for key, d in [("default", None)] + [(f"class{c}", ops.Dispatch(L.MXQ_DISPATCH_FORCED, c, 16))
+                                                 for c in range(5)]:
+                sel[0] = d
+                us = _time_calls(w["run"], steps, warmup)[0]["median"]
+                res[key + "_us"] = us
+                res[key + "_gbs"] = w["bytes"] / (us * 1e-6) / 1e9
+            best = min(range(5), key=lambda c: res[f"class{c}_us"])
+            res["best_class"] = best
+            res["default_over_best"] = res["default_us"] / res[f"class{best}_us"]
+            print(json.dumps(res), flush=True)
+            rows.append(res)
+            del w
+            torch.cuda.empty_cache()
     return rows
 
 
@@ -509,6 +554,10 @@ def main():
         return
     if a.only == "ablation":
         bench_dispatch_ablation(a.steps, a.warmup)
+        return
+    if a.only == "classes":
+        bench_class_sweep(a.steps, a.warmup, a.sweep_shape.split(",") if a.sweep_shape else None,
+                          [int(v) for v in a.sweep_m.split(",")] if a.sweep_m else None)
         return
     if a.only == "decode":
         print(json.dumps(bench_moe("moe_mxfp4_gptoss_decode_m32", a.steps, a.warmup, 1004)), flush=True)

@@ -261,23 +261,26 @@ mxq_status mxq_moe_align(const int32_t* topk_ids, int64_t M, int32_t topk, int32
  * The two layouts give bit-identical outputs.
  *
  * Per-call dispatch (`dispatch`, read during the call only; NULL = the defaults
- * {MXQ_DISPATCH_PER_BLOCK, 0, 16, MXQ_TINY_MFMA}; invalid fields -> MXQ_ERR_ARG):
+ * {MXQ_DISPATCH_PER_BLOCK, 0, MXQ_TINY_ROWS_AUTO, MXQ_TINY_MFMA}; invalid fields -> MXQ_ERR_ARG):
  *   mode MXQ_DISPATCH_PER_BLOCK: each block's class from its own row count;
  *   mode MXQ_DISPATCH_FORCED: every block runs class `forced_class` (0 = tiny-block kernel,
  *        1 = 16-row, 2 = 32-row, 3 = 64-row, 4 = 128-row MFMA tiles) -- for tests;
  *   mode MXQ_DISPATCH_LAYER_AVERAGE: one class for the whole layer, chosen from
  *        max(1, M * topk / E) rows (the per-layer rule page [A] replaces; for
  *        ablation measurements).
- *   tiny_max_rows (0..16): largest block that takes the tiny-block class in per-block
- *        mode.  When M <= 2 * tiny_max_rows the tiny class takes every block (taller ones
- *        in several passes); with bf16 activations, the MFMA tiny kernel, at most 4096
- *        routed rows, E <= 512 and both stages' operands fitting the kernel's LDS budget,
- *        this case runs as two persistent expert-streaming kernels that group the routed
- *        rows by expert themselves (no sort and no block tables; the SiLU-and-mul ends
- *        stage 1) -- same arithmetic, bit-identical outputs.  Otherwise, for W8A8 with
- *        K <= 16384 on both stages and operands below 4 GiB, every smaller class (the tiny
- *        one too, with the MFMA tiny kernel) folds into the 128-row class: its 128 x 256
- *        tile streams the weights better even for short blocks.
+ *   tiny_max_rows (0..16, or MXQ_TINY_ROWS_AUTO): largest block that takes the tiny-block
+ *        class in per-block mode; AUTO = the measured crossover of the weight format: 4 rows
+ *        for W8A8, 8 for W8A16, 12 for MXFP4; 0 = no tiny class.  When M <= 32 or
+ *        M * topk <= 2 E the tiny class takes every block (taller ones in several passes);
+ *        with bf16 activations, the MFMA tiny kernel, at most 4096 routed rows, E <= 512 and
+ *        both stages' operands fitting the kernel's LDS budget, this case runs as two
+ *        persistent expert-streaming kernels that group the routed rows by expert themselves
+ *        (no sort and no block tables; the SiLU-and-mul ends stage 1) -- same arithmetic,
+ *        bit-identical outputs.  Otherwise, for W8A8 with M * topk > 4096, K <= 16384 on both
+ *        stages and operands below 4 GiB, every smaller class (the tiny one too, with the
+ *        MFMA tiny kernel) folds into the 128-row class: its 128 x 256 tile keeps the GPU
+ *        full with one launch per stage.  Column tiles: the 128 x 256 tile takes column
+ *        tiles 256 wide; a last column tile of at most 128 columns takes the 128 x 128 tile.
  *   tiny_kernel: MXQ_TINY_MFMA (weights streamed into registers, K reduced by MFMAs, up
  *        to 8 rows per pass) or MXQ_TINY_GEMV (vector-ALU dot products with a wavefront
  *        reduction, 4 rows per pass; plain weight layout only -- with tiled weights the
@@ -291,6 +294,7 @@ mxq_status mxq_moe_align(const int32_t* topk_ids, int64_t M, int32_t topk, int32
 #define MXQ_DISPATCH_LAYER_AVERAGE 2
 #define MXQ_TINY_MFMA 0
 #define MXQ_TINY_GEMV 1
+#define MXQ_TINY_ROWS_AUTO (-1)
 typedef struct mxq_moe_dispatch {
   int32_t mode;
   int32_t forced_class;

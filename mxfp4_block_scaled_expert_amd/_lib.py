@@ -38,6 +38,7 @@ MXQ_DISPATCH_LAYER_AVERAGE = 2
 
 MXQ_TINY_MFMA = 0
 MXQ_TINY_GEMV = 1
+MXQ_TINY_ROWS_AUTO = -1
 
 MXQ_LAYOUT_PLAIN = 0
 MXQ_LAYOUT_TILED = 1

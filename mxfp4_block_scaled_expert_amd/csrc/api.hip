@@ -79,12 +79,12 @@ constexpr int kClassRows[kNumClasses] = {16, 16, 32, 64, 128};  // [0] is set at
 
 // The dispatch a call runs with: the caller's mxq_moe_dispatch, or the defaults for NULL.
 mxq_status read_dispatch(const mxq_moe_dispatch* d, mxq_moe_dispatch& out) {
-  out = mxq_moe_dispatch{MXQ_DISPATCH_PER_BLOCK, 0, 16, MXQ_TINY_MFMA};
+  out = mxq_moe_dispatch{MXQ_DISPATCH_PER_BLOCK, 0, MXQ_TINY_ROWS_AUTO, MXQ_TINY_MFMA};
   if (!d) return MXQ_OK;
   if (d->mode < MXQ_DISPATCH_PER_BLOCK || d->mode > MXQ_DISPATCH_LAYER_AVERAGE) return MXQ_ERR_ARG;
   if (d->tiny_kernel != MXQ_TINY_MFMA && d->tiny_kernel != MXQ_TINY_GEMV) return MXQ_ERR_ARG;
   if (d->forced_class < 0 || d->forced_class >= kNumClasses) return MXQ_ERR_ARG;
-  if (d->tiny_max_rows < 0 || d->tiny_max_rows > 16) return MXQ_ERR_ARG;
+  if (d->tiny_max_rows < MXQ_TINY_ROWS_AUTO || d->tiny_max_rows > 16) return MXQ_ERR_ARG;
   out = *d;
   return MXQ_OK;
 }
@@ -97,6 +97,29 @@ bool big_tile_offsets_fit(int64_t M, int64_t R, int64_t H, int64_t I) {
 }
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+// The column-width half of the tile choice: the 256-wide direct-to-LDS W8A8 tile takes the
+// column tiles of width 256; a last column tile of n_size <= 128 (where the wide tile would
+// leave at least half of its products unused) takes the 128-wide tile instead.  Returns the
+// columns the wide tile covers.
+constexpr int64_t kWideTileN = 256;
+int64_t wide_tile_columns(int64_t N) {
+  const int64_t tail = N % kWideTileN;
+  return (tail != 0 && tail <= kWideTileN / 2) ? N - tail : N;
+}
+
+// Columns [n0, N) of a GEMM as a problem of their own: weights, weight-scale grid rows, bias
+// and output shifted by n0 columns (n0 a multiple of 256: of every weight-scale block width
+// and of the tiled layout's 16-row groups).
+GemmArgs column_slice(const GemmArgs& g, int64_t n0, bool out_f32) {
+  GemmArgs t = g;
+  t.W = g.W + (g.w_tiled ? (n0 / 16) * tiled_steps(g.ldw) * 2048 : n0 * g.ldw);
+  t.ws = static_cast<const float*>(g.ws) + (n0 / (g.block_n > 0 ? g.block_n : 128)) * g.ws_s0;
+  if (g.bias) t.bias = static_cast<const uint8_t*>(g.bias) + n0 * (g.bias_bf16 ? 2 : 4);
+  t.out = static_cast<uint8_t*>(g.out) + n0 * (out_f32 ? 4 : 2);
+  t.N = g.N - n0;
+  return t;
+}
 
 struct MoeWorkspace {
   int32_t *sorted_ids, *expert_ids, *offsets, *num_blocks, *class_lists, *class_counts;
@@ -155,30 +178,39 @@ int64_t class_bound(int c, int64_t R, int32_t E, int64_t max_blocks, const Class
   return std::max<int64_t>(ub, 0);
 }
 
-// M caps the rows of one expert when every token names distinct experts, so the
-// classes whose lower bound reaches M are not launched (a block beyond that, from
-// repeated ids, still lands in the largest launched class).
-//
-// `big_tile`: the stage GEMMs have the 128 x 256 direct-to-LDS W8A8 tile (W8A8, K <= 16384).
-// Measured on the prefill shapes (E = 256, 512 and 4096 tokens), that tile streams an expert's
-// weights better than the 16-64-row tiles even for short blocks, and each extra class launch
-// leaves the GPU partly idle while its few blocks run; so at larger token counts every class
-// below the 128-row one is folded into it -- with the MFMA tiny kernel selected, the tiny class
-// too (the blocks of at most a few rows then cost no separate launch: measured equal at 512
-// tokens and 4-5 % faster at 4096 with uniform routing).  With bf16 activations the next
-// classes have no such tile, and taking a few passes in the tiny kernel measured faster.
-ClassPolicy make_policy(int64_t M, int64_t R, int32_t E, bool big_tile, const mxq_moe_dispatch& dc) {
+// Per-block tile-class policy (page [A], implementation items 1-2: each block's kernel from its
+// own row count).  The bounds come from the class sweep (`bench.py --only classes`: E experts
+// each holding exactly m rows, every class forced in turn, on the GPT-OSS MXFP4, DeepSeek W8A8
+// and small W8A16 expert shapes):
+//  * the tiny-block kernel is the fastest class up to 4 rows per block with e4m3 activations,
+//    8 with bf16 activations and e4m3 weights, 12 with e2m1 weights (it streams an expert's
+//    weights once per pass of 4-8 rows, the tiles pay a fixed cost per block); then the 16-,
+//    32-, 64- and 128-row tiles each win in their own range;
+//  * the tiny class takes every block when M <= 32 or R <= 2 E: an expert holds at most M rows,
+//    and with at most two routed rows per expert on average (decode batches) an odd taller
+//    block's extra passes run beside the many tiny blocks, while a tile-class launch would run
+//    mostly empty workgroups;
+//  * with the 128 x 256 direct-to-LDS W8A8 tile and R > 4096 routed rows every class folds
+//    into the 128-row one: with many blocks one launch of that tile keeps the GPU full, where
+//    separate class launches each leave it partly idle (DeepSeek prefill, 4096 tokens: 4-5 %
+//    faster than separate classes; equal at 512 tokens, and slower than the 32- and 64-row
+//    tiles with 32 experts of 8-64 rows).
+// M also caps the classes launched: those whose lower bound reaches M get no blocks when every
+// token names distinct experts (a block beyond that, from repeated ids, lands in the largest
+// launched class).
+int tiny_rows_auto(int wfmt, bool act_quant) { return act_quant ? 4 : (wfmt == W_E2M1_MX ? 12 : 8); }
+
+ClassPolicy make_policy(int64_t M, int64_t R, int32_t E, bool big_tile, int wfmt, bool act_quant,
+                        const mxq_moe_dispatch& dc) {
+  const int tiny = dc.tiny_max_rows < 0 ? tiny_rows_auto(wfmt, act_quant) : dc.tiny_max_rows;
   ClassPolicy pol{};
   pol.n_classes = kNumClasses;
   pol.forced = -1;
-  pol.bound[0] = dc.tiny_max_rows;
-  for (int c = 1; c < kNumClasses; ++c) pol.bound[c] = kClassRows[c];
-  // When M is at most twice the tiny-block bound the tiny class takes every block (an expert
-  // holds at most M rows): blocks of bound..M rows take a few passes of the weight-streaming
-  // kernel instead of a mostly empty launch of the next tile class.
-  if (dc.tiny_max_rows > 0 && M <= 2 * int64_t(dc.tiny_max_rows)) {
-    pol.bound[0] = std::max<int>(pol.bound[0], int(M));
-  } else if (big_tile) {
+  pol.bound[0] = tiny;
+  for (int c = 1; c < kNumClasses; ++c) pol.bound[c] = std::max(tiny, kClassRows[c]);
+  if (tiny > 0 && (M <= 32 || R <= 2 * int64_t(E))) {
+    pol.bound[0] = int(std::max<int64_t>(tiny, M));
+  } else if (big_tile && R > 4096) {
     if (dc.tiny_kernel == MXQ_TINY_MFMA) pol.bound[0] = 0;
     for (int c = 1; c < kNumClasses - 1; ++c) pol.bound[c] = pol.bound[0];
   }
@@ -196,7 +228,7 @@ ClassPolicy make_policy(int64_t M, int64_t R, int32_t E, bool big_tile, const mx
     const int64_t avg = std::max<int64_t>(1, R / std::max<int32_t>(E, 1));
     int c = kNumClasses - 1;
     for (int i = 0; i < kNumClasses - 1; ++i)
-      if (avg <= (i == 0 ? dc.tiny_max_rows : kClassRows[i])) { c = i; break; }
+      if (avg <= (i == 0 ? tiny : kClassRows[i])) { c = i; break; }
     pol.forced = c;
     pol.n_live = kNumClasses;
   }
@@ -214,7 +246,7 @@ mxq_status run_moe(const void* x, int64_t M, int64_t H, int64_t I, int32_t E, in
   if (!ws || ws_bytes < w.bytes) return MXQ_ERR_WORKSPACE;
   // the 128 x 256 W8A8 tile: K <= 16384 on both stages and operand offsets below 4 GiB
   const bool big_tile = act_quant && H <= 16384 && I <= 16384 && big_tile_offsets_fit(M, R, H, I);
-  const ClassPolicy pol = make_policy(M, R, E, big_tile, dc);
+  const ClassPolicy pol = make_policy(M, R, E, big_tile, wfmt, act_quant, dc);
   const int tiny = dc.tiny_kernel;
   const bool mx = wfmt == W_E2M1_MX;
   const int wfmt_w16 = mx ? W_E2M1_MX : W_E4M3_BLOCK;
@@ -362,9 +394,17 @@ mxq_status run_moe(const void* x, int64_t M, int64_t H, int64_t I, int32_t E, in
         launch_gemv(g, wfmt_w16, act_quant, mode, out_f32, ub, st);
       else if (c == 0 && skinny_fits)
         launch_skinny(g, wfmt_w16, act_quant, mode, out_f32, ub, st);
-      else if (big_tile && c == kNumClasses - 1)
-        // blocks of 65..128 rows: the 128 x 256 three-stage direct-to-LDS tile
-        launch_gemm_w8a8_big(g, mode, 1, out_f32, ub, st);
+      else if (big_tile && c == kNumClasses - 1) {
+        // blocks of 65..128 rows: the 128 x 256 three-stage direct-to-LDS tile, and for a
+        // narrow last column tile the 128 x 128 tile
+        const int64_t nw = wide_tile_columns(g.N);
+        if (nw > 0) {
+          GemmArgs gw = g;
+          gw.N = nw;
+          launch_gemm_w8a8_big(gw, mode, 1, out_f32, ub, st);
+        }
+        if (nw < g.N) launch_gemm_w8a8(column_slice(g, nw, out_f32), mode, 0, out_f32, ub, st);
+      }
       else if (act_quant)
         launch_gemm_w8a8(g, mode, tile, out_f32, ub, st);
       else if (c == 0)
@@ -549,7 +589,15 @@ mxq_status mxq_block_fp8_linear(const void* A, int32_t a_dtype, const float* a_s
   g.K = K;
   if ((block_n == 128 || block_n == 1) && M > 128 && K <= 16384 && int64_t(M) * lqa < (int64_t(1) << 32) &&
       N * K < (int64_t(1) << 32)) {
-    launch_gemm_w8a8_big(g, ROWS_DENSE, kDenseBigShape, false, cdiv(M, int64_t(big_tile_rows(kDenseBigShape))), st);
+    // the wide tile for the column tiles of width 256, the 128-wide tile for a narrow last one
+    const int64_t nw = wide_tile_columns(N);
+    if (nw > 0) {
+      GemmArgs gw = g;
+      gw.N = nw;
+      launch_gemm_w8a8_big(gw, ROWS_DENSE, kDenseBigShape, false, cdiv(M, int64_t(big_tile_rows(kDenseBigShape))),
+                           st);
+    }
+    if (nw < N) launch_gemm_w8a8(column_slice(g, nw, false), ROWS_DENSE, 0, false, cdiv(M, int64_t(128)), st);
   } else {
     const int tile = dense_tile_for(M);
     launch_gemm_w8a8(g, ROWS_DENSE, tile, false, cdiv(M, tile_rows(tile)), st);

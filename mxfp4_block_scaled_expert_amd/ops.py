@@ -340,7 +340,7 @@ class Dispatch(NamedTuple):
     """Per-call dispatch of the fused MoE (``struct mxq_moe_dispatch``); None = the defaults."""
     mode: int = L.MXQ_DISPATCH_PER_BLOCK
     forced_class: int = 0
-    tiny_max_rows: int = 16
+    tiny_max_rows: int = L.MXQ_TINY_ROWS_AUTO
     tiny_kernel: int = L.MXQ_TINY_MFMA
 
 

@@ -191,10 +191,13 @@ def _spec(M, E, topk, H, I, zipf=1.1):
 
 @pytest.mark.parametrize("forced", [None, 0, 1, 2, 3, 4])
 @pytest.mark.parametrize("layout", ["plain", "tiled"])
-def test_w8a8_moe_stage_by_stage(forced, layout):
-    """A skewed routing whose blocks straddle every class bound, every class forced."""
-    inp = synth.moe_inputs(_spec(300, 16, 4, 512, 256), seed=11, device=gpu())
-    M, H, I, E, topk = 300, 512, 256, 16, 4
+@pytest.mark.parametrize("H", [512, 640])
+def test_w8a8_moe_stage_by_stage(forced, layout, H):
+    """A skewed routing whose blocks straddle every class bound, every class forced.  H = 640:
+    stage 2's last column tile is 128 wide, which the column-width rule sends to the 128-wide
+    tile while the other column tiles of the same blocks take the 256-wide one."""
+    M, I, E, topk = 300, 256, 16, 4
+    inp = synth.moe_inputs(_spec(M, E, topk, H, I), seed=11, device=gpu())
     ws = ops.fused_moe_workspace(M, H, I, E, topk, L.MXQ_WEIGHTS_FP8_BLOCK, True, gpu())
     d = None if forced is None else ops.Dispatch(mx.MXQ_DISPATCH_FORCED, forced, 4)
     out = _run_fp8(inp, ws, layout, d)
