@@ -261,7 +261,8 @@ mxq_status mxq_moe_align(const int32_t* topk_ids, int64_t M, int32_t topk, int32
  * The two layouts give bit-identical outputs.
  *
  * Per-call dispatch (`dispatch`, read during the call only; NULL = the defaults
- * {MXQ_DISPATCH_PER_BLOCK, 0, MXQ_TINY_ROWS_AUTO, MXQ_TINY_MFMA}; invalid fields -> MXQ_ERR_ARG):
+ * {MXQ_DISPATCH_PER_BLOCK, 0, MXQ_TINY_ROWS_AUTO, MXQ_TINY_MFMA, MXQ_K_SPLIT_AUTO};
+ * invalid fields -> MXQ_ERR_ARG):
  *   mode MXQ_DISPATCH_PER_BLOCK: each block's class from its own row count;
  *   mode MXQ_DISPATCH_FORCED: every block runs class `forced_class` (0 = tiny-block kernel,
  *        1 = 16-row, 2 = 32-row, 3 = 64-row, 4 = 128-row MFMA tiles) -- for tests;
@@ -270,7 +271,9 @@ mxq_status mxq_moe_align(const int32_t* topk_ids, int64_t M, int32_t topk, int32
  *        ablation measurements).
  *   tiny_max_rows (0..16, or MXQ_TINY_ROWS_AUTO): largest block that takes the tiny-block
  *        class in per-block mode; AUTO = the measured crossover of the weight format: 4 rows
- *        for W8A8, 8 for W8A16, 12 for MXFP4; 0 = no tiny class.  When M <= 32 or
+ *        for W8A8, 8 for W8A16, 4 for MXFP4; 0 = no tiny class.  With AUTO, bf16 activations,
+ *        K <= 16384 and 16-byte aligned activation rows, a routing of more than AUTO x E rows
+ *        has no tiny class: its tiny blocks take 16-row tiles in the tile launch.  When M <= 32 or
  *        M * topk <= 2 E the tiny class takes every block (taller ones in several passes);
  *        with bf16 activations, the MFMA tiny kernel, at most 4096 routed rows, E <= 512 and
  *        both stages' operands fitting the kernel's LDS budget, this case runs as two
@@ -284,7 +287,17 @@ mxq_status mxq_moe_align(const int32_t* topk_ids, int64_t M, int32_t topk, int32
  *   tiny_kernel: MXQ_TINY_MFMA (weights streamed into registers, K reduced by MFMAs, up
  *        to 8 rows per pass) or MXQ_TINY_GEMV (vector-ALU dot products with a wavefront
  *        reduction, 4 rows per pass; plain weight layout only -- with tiled weights the
- *        MFMA kernel runs). */
+ *        MFMA kernel runs).
+ *   k_split (MXQ_K_SPLIT_AUTO, 1, 2, 4 or 8): with bf16 activations, at most 1024 routed
+ *        rows, the MFMA tiny kernel and outside the expert-streaming case, a stage whose
+ *        blocks give few tiles cuts each tile's K range into chunks (multiples of 256
+ *        columns) that run as workgroups of their own and write fp32 partial sums to the
+ *        workspace; the kernel after the stage sums them in chunk order.  AUTO: with at
+ *        most 256 routed rows, the most chunks that keep min(E, M * topk) blocks of
+ *        128-column tiles within 256 tiles (one per compute unit);
+ *        1: never; 2 / 4 / 8: at most that many.  The workspace bounds the chunks to
+ *        M * topk * chunks <= 2048.  Outputs agree with the unsplit call within rounding
+ *        (the sums over K are grouped differently). */
 #define MXQ_WEIGHTS_FP8_BLOCK 0
 #define MXQ_WEIGHTS_MXFP4 1
 #define MXQ_LAYOUT_PLAIN 0
@@ -295,11 +308,13 @@ mxq_status mxq_moe_align(const int32_t* topk_ids, int64_t M, int32_t topk, int32
 #define MXQ_TINY_MFMA 0
 #define MXQ_TINY_GEMV 1
 #define MXQ_TINY_ROWS_AUTO (-1)
+#define MXQ_K_SPLIT_AUTO 0
 typedef struct mxq_moe_dispatch {
   int32_t mode;
   int32_t forced_class;
   int32_t tiny_max_rows;
   int32_t tiny_kernel;
+  int32_t k_split;
 } mxq_moe_dispatch;
 size_t mxq_fused_moe_workspace_size(int64_t M, int64_t H, int64_t I, int32_t E, int32_t topk, int32_t weights,
                                     int32_t act_quant);
@@ -326,7 +341,8 @@ mxq_status mxq_fused_moe_mxfp4(const void* x, int64_t M, int64_t H, int64_t I, i
  *   QX / SX    x quantised as by mxq_per_token_group_quant_fp8 (e4m3 [M, H], fp32 [M, H/128]);
  *   IC0        bf16 [R, 2I]: stage-1 outputs (+ bias) by compact row;
  *   IC1_Q / IC1_S  e4m3 [R, I] + fp32 [R, I/128]: mxq_silu_and_mul of IC0, re-quantised;
- *   Y          fp32 [R, H]: stage-2 outputs by flat routed id t * topk + k.
+ *   Y          fp32 [R, H]: stage-2 outputs by flat routed id t * topk + k;
+ *   PARTIAL    fp32 K-split partial sums (bf16 activations only; -1 when M * topk > 1024).
  * With bf16 activations (act_quant = 0, and every MXFP4 call) the regions are scratch
  * whose contents depend on the kernels the dispatch picked (the expert-streaming path
  * writes neither the tables nor IC0). */
@@ -342,7 +358,8 @@ mxq_status mxq_fused_moe_mxfp4(const void* x, int64_t M, int64_t H, int64_t I, i
 #define MXQ_MOE_WS_IC1_S 9
 #define MXQ_MOE_WS_Y 10
 #define MXQ_MOE_WS_BLOCK_M 11
-#define MXQ_MOE_WS_FIELDS 12
+#define MXQ_MOE_WS_PARTIAL 12
+#define MXQ_MOE_WS_FIELDS 13
 mxq_status mxq_fused_moe_workspace_layout(int64_t M, int64_t H, int64_t I, int32_t E, int32_t topk, int32_t weights,
                                           int32_t act_quant, int64_t* offsets);
 

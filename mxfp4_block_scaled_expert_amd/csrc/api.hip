@@ -79,12 +79,14 @@ constexpr int kClassRows[kNumClasses] = {16, 16, 32, 64, 128};  // [0] is set at
 
 // The dispatch a call runs with: the caller's mxq_moe_dispatch, or the defaults for NULL.
 mxq_status read_dispatch(const mxq_moe_dispatch* d, mxq_moe_dispatch& out) {
-  out = mxq_moe_dispatch{MXQ_DISPATCH_PER_BLOCK, 0, MXQ_TINY_ROWS_AUTO, MXQ_TINY_MFMA};
+  out = mxq_moe_dispatch{MXQ_DISPATCH_PER_BLOCK, 0, MXQ_TINY_ROWS_AUTO, MXQ_TINY_MFMA, MXQ_K_SPLIT_AUTO};
   if (!d) return MXQ_OK;
   if (d->mode < MXQ_DISPATCH_PER_BLOCK || d->mode > MXQ_DISPATCH_LAYER_AVERAGE) return MXQ_ERR_ARG;
   if (d->tiny_kernel != MXQ_TINY_MFMA && d->tiny_kernel != MXQ_TINY_GEMV) return MXQ_ERR_ARG;
   if (d->forced_class < 0 || d->forced_class >= kNumClasses) return MXQ_ERR_ARG;
   if (d->tiny_max_rows < MXQ_TINY_ROWS_AUTO || d->tiny_max_rows > 16) return MXQ_ERR_ARG;
+  if (d->k_split != MXQ_K_SPLIT_AUTO && d->k_split != 1 && d->k_split != 2 && d->k_split != 4 && d->k_split != 8)
+    return MXQ_ERR_ARG;
   out = *d;
   return MXQ_OK;
 }
@@ -121,8 +123,57 @@ GemmArgs column_slice(const GemmArgs& g, int64_t n0, bool out_f32) {
   return t;
 }
 
+// K split of the routed stages with bf16 activations.  A stage with few expert blocks runs too
+// few workgroups to stream its weights at HBM speed (each holds a bounded number of loads in
+// flight), so each tile's K range is cut into chunks that run as separate workgroups; they
+// write fp32 partial sums to slices of the workspace, summed in slice order by the kernel after
+// the stage (the SiLU-and-mul after stage 1, the combine after stage 2).  Chunks are whole
+// multiples of 256 columns of K.  The workspace holds split_cap(R) slices per stage.
+constexpr int64_t kSplitMaxRows = 1024;    // more routed rows: no split (workspace bound)
+constexpr int64_t kSplitRowSlices = 2048;  // slices x routed rows the workspace holds at most
+constexpr int kSplitMax = 8;
+// Automatic choice, from measurements of the ring-fed tiles (W8A16 E = 8 with the 128-token
+// small-block routing, 256 tokens top-2, MXFP4 40 tokens top-4): a split pays only while the
+// stage's tiles stay at most one per compute unit and the partial sums are small (at most
+// 256 routed rows); beyond that the partial-sum traffic and the extra tile prologues cost more
+// than the shorter K loops save.
+constexpr int64_t kSplitAutoMaxRows = 256;
+constexpr int64_t kSplitTargetTiles = 256;
+
+int split_cap(int64_t R) {
+  if (R > kSplitMaxRows) return 1;
+  int s = 1;
+  while (s < kSplitMax && int64_t(2 * s) * R <= kSplitRowSlices) s *= 2;
+  return s;
+}
+
+struct KSplit {
+  int n;          // chunks (1: no split)
+  int64_t chunk;  // K elements per chunk
+};
+
+// `requested`: MXQ_K_SPLIT_AUTO, or the caller's upper bound (1 = off).  Automatic: with at
+// most kSplitAutoMaxRows routed rows, the most chunks that keep an estimate of the stage's
+// tiles (at most min(E, R) blocks of 128-column tiles) within kSplitTargetTiles.
+KSplit pick_split(int64_t R, int32_t E, int64_t N, int64_t K, int requested) {
+  const int cap = split_cap(R);
+  int s = 1;
+  if (requested > 1) {
+    s = std::min(requested, cap);
+  } else if (requested == MXQ_K_SPLIT_AUTO) {
+    const int64_t tiles = std::min<int64_t>(E, R) * cdiv(N, int64_t(128));
+    if (R <= kSplitAutoMaxRows)
+      while (s < cap && tiles * s * 2 <= kSplitTargetTiles) s *= 2;
+  }
+  if (s <= 1) return {1, 0};
+  const int64_t chunk = cdiv(cdiv(K, int64_t(s)), int64_t(256)) * 256;
+  const int n = int(cdiv(K, chunk));
+  return n > 1 ? KSplit{n, chunk} : KSplit{1, 0};
+}
+
 struct MoeWorkspace {
   int32_t *sorted_ids, *expert_ids, *offsets, *num_blocks, *class_lists, *class_counts;
+  float* partial;  // K-split partial slices (bf16 activations, R <= kSplitMaxRows)
   uint8_t* qx;
   float* sx;
   uint16_t* ic0;
@@ -161,6 +212,8 @@ MoeWorkspace carve_moe(void* base, int64_t M, int64_t H, int64_t I, int32_t E, i
     w.ic1 = reinterpret_cast<uint16_t*>(take(sizeof(uint16_t) * R * I));
   }
   w.y = reinterpret_cast<float*>(take(sizeof(float) * R * H));
+  if (!act_quant && split_cap(R) > 1)
+    w.partial = reinterpret_cast<float*>(take(sizeof(float) * split_cap(R) * R * std::max(2 * I, H)));
   w.bytes = off;
   return w;
 }
@@ -183,9 +236,14 @@ int64_t class_bound(int c, int64_t R, int32_t E, int64_t max_blocks, const Class
 // each holding exactly m rows, every class forced in turn, on the GPT-OSS MXFP4, DeepSeek W8A8
 // and small W8A16 expert shapes):
 //  * the tiny-block kernel is the fastest class up to 4 rows per block with e4m3 activations,
-//    8 with bf16 activations and e4m3 weights, 12 with e2m1 weights (it streams an expert's
+//    8 with bf16 activations and e4m3 weights, 4 with e2m1 weights (it streams an expert's
 //    weights once per pass of 4-8 rows, the tiles pay a fixed cost per block); then the 16-,
 //    32-, 64- and 128-row tiles each win in their own range;
+//  * with bf16 activations on the ring-fed tiles, when the routing averages more rows per
+//    expert than the tiny bound the tile classes are launched anyway: the tiny blocks then
+//    take 16-row tiles in that launch, beside the taller blocks, instead of a launch of their
+//    own after it (W8A16 E = 8 with blocks of 4, 5, 33, 12, 1 and 73 rows: 40 against 54 us;
+//    256 tokens top-2: 54 against 58 us; MXFP4 40 tokens top-4: 73 against 77 us);
 //  * the tiny class takes every block when M <= 32 or R <= 2 E: an expert holds at most M rows,
 //    and with at most two routed rows per expert on average (decode batches) an odd taller
 //    block's extra passes run beside the many tiny blocks, while a tile-class launch would run
@@ -198,9 +256,9 @@ int64_t class_bound(int c, int64_t R, int32_t E, int64_t max_blocks, const Class
 // M also caps the classes launched: those whose lower bound reaches M get no blocks when every
 // token names distinct experts (a block beyond that, from repeated ids, lands in the largest
 // launched class).
-int tiny_rows_auto(int wfmt, bool act_quant) { return act_quant ? 4 : (wfmt == W_E2M1_MX ? 12 : 8); }
+int tiny_rows_auto(int wfmt, bool act_quant) { return act_quant ? 4 : (wfmt == W_E2M1_MX ? 4 : 8); }
 
-ClassPolicy make_policy(int64_t M, int64_t R, int32_t E, bool big_tile, int wfmt, bool act_quant,
+ClassPolicy make_policy(int64_t M, int64_t R, int32_t E, bool big_tile, bool ring, int wfmt, bool act_quant,
                         const mxq_moe_dispatch& dc) {
   const int tiny = dc.tiny_max_rows < 0 ? tiny_rows_auto(wfmt, act_quant) : dc.tiny_max_rows;
   ClassPolicy pol{};
@@ -210,6 +268,12 @@ ClassPolicy make_policy(int64_t M, int64_t R, int32_t E, bool big_tile, int wfmt
   for (int c = 1; c < kNumClasses; ++c) pol.bound[c] = std::max(tiny, kClassRows[c]);
   if (tiny > 0 && (M <= 32 || R <= 2 * int64_t(E))) {
     pol.bound[0] = int(std::max<int64_t>(tiny, M));
+  } else if (ring && dc.tiny_max_rows < 0 && R > int64_t(tiny) * E) {
+    // bf16 activations on the ring-fed tiles: unless the routing averages at most the tiny
+    // bound per expert, the tile classes are launched anyway and the tiny blocks take 16-row
+    // tiles in the same launch (running beside the taller blocks instead of in a launch of
+    // their own)
+    pol.bound[0] = 0;
   } else if (big_tile && R > 4096) {
     if (dc.tiny_kernel == MXQ_TINY_MFMA) pol.bound[0] = 0;
     for (int c = 1; c < kNumClasses - 1; ++c) pol.bound[c] = pol.bound[0];
@@ -246,62 +310,8 @@ mxq_status run_moe(const void* x, int64_t M, int64_t H, int64_t I, int32_t E, in
   if (!ws || ws_bytes < w.bytes) return MXQ_ERR_WORKSPACE;
   // the 128 x 256 W8A8 tile: K <= 16384 on both stages and operand offsets below 4 GiB
   const bool big_tile = act_quant && H <= 16384 && I <= 16384 && big_tile_offsets_fit(M, R, H, I);
-  const ClassPolicy pol = make_policy(M, R, E, big_tile, wfmt, act_quant, dc);
-  const int tiny = dc.tiny_kernel;
   const bool mx = wfmt == W_E2M1_MX;
   const int wfmt_w16 = mx ? W_E2M1_MX : W_E4M3_BLOCK;
-
-  // Every block of the routing is tiny and the activations stay bf16: the expert-streaming
-  // kernels group the routed rows by expert themselves (no sort, no block tables), stage 1 ends
-  // in the SiLU-and-mul, and rows are indexed by flat routed id up to the combine.
-  if (!act_quant && pol.forced < 0 && pol.n_live == 1 && tiny == MXQ_TINY_MFMA && R <= kStreamMaxRows &&
-      E <= kStreamMaxExperts && I % 16 == 0 &&
-      expert_stream_lds_bytes(wfmt_w16, 1, 2 * I, H, E, R) <= kStreamMaxLds &&
-      expert_stream_lds_bytes(wfmt_w16, 2, H, I, E, R) <= kStreamMaxLds) {
-    const EsRoute er{ids, int32_t(R), E, topk};
-    GemmArgs s1{};
-    s1.A = x;
-    s1.lda = H;
-    s1.W = static_cast<const uint8_t*>(w1);
-    s1.ldw = mx ? H / 2 : H;
-    s1.w_tiled = tiled;
-    s1.w_estride = tiled ? 2 * I * tiled_steps(s1.ldw) * 128 : s1.ldw * 2 * I;
-    s1.ws = w1s;
-    s1.ws_s0 = mx ? H / 32 : H / 128;
-    s1.ws_s1 = 1;
-    s1.ws_estride = mx ? (tiled ? 2 * I * tiled_scale_steps(H / 32) * 8 : 2 * I * (H / 32)) : cdiv(2 * I, 128) * (H / 128);
-    s1.bias = b1;
-    s1.bias_estride = 2 * I;
-    s1.out = w.ic1;
-    s1.ldo = I;
-    s1.M = R;
-    s1.N = 2 * I;
-    s1.K = H;
-    GemmArgs s2{};
-    s2.A = w.ic1;
-    s2.lda = I;
-    s2.W = static_cast<const uint8_t*>(w2);
-    s2.ldw = mx ? I / 2 : I;
-    s2.w_tiled = tiled;
-    s2.w_estride = tiled ? H * tiled_steps(s2.ldw) * 128 : s2.ldw * H;
-    s2.ws = w2s;
-    s2.ws_s0 = mx ? I / 32 : I / 128;
-    s2.ws_s1 = 1;
-    s2.ws_estride = mx ? (tiled ? H * tiled_scale_steps(I / 32) * 8 : H * (I / 32)) : cdiv(H, 128) * (I / 128);
-    s2.out = w.y;
-    s2.ldo = H;
-    s2.M = R;
-    s2.N = H;
-    s2.K = I;
-    launch_expert_stream(s1, wfmt_w16, 1, er, st);
-    launch_expert_stream(s2, wfmt_w16, 2, er, st);
-    launch_combine(w.y, wts, ids, E, M, topk, H, static_cast<uint16_t*>(out), st);
-    return launch_status();
-  }
-
-  launch_moe_align(ids, M, topk, E, kMoeBlockM, w.sorted_ids, w.expert_ids, w.offsets, w.num_blocks, mbk, pol,
-                   w.class_lists, mbk, w.class_counts, false, st);
-  if (act_quant) launch_quant_1x128(static_cast<const uint16_t*>(x), M, H, H, w.qx, H, w.sx, st);
 
   BlockRouting rt{w.sorted_ids, w.expert_ids, w.offsets, nullptr, nullptr, kMoeBlockM, topk};
 
@@ -362,9 +372,87 @@ mxq_status run_moe(const void* x, int64_t M, int64_t H, int64_t I, int32_t E, in
   g2.K = I;
   g2.rt = rt;
 
+  // bf16 activations: both stages take the ring-fed tiles (the class policy looks only at the
+  // layout-independent part, so that plain and tiled weights run the same classes)
+  const bool ring_shape = !act_quant && w16_ring_shape_ok(g1, wfmt_w16) && w16_ring_shape_ok(g2, wfmt_w16);
+  const bool ring = ring_shape && w16_ring_supported(g1, wfmt_w16) && w16_ring_supported(g2, wfmt_w16);
+  const ClassPolicy pol = make_policy(M, R, E, big_tile, ring_shape, wfmt, act_quant, dc);
+  const int tiny = dc.tiny_kernel;
+
+  // Every block of the routing is tiny and the activations stay bf16: the expert-streaming
+  // kernels group the routed rows by expert themselves (no sort, no block tables), stage 1 ends
+  // in the SiLU-and-mul, and rows are indexed by flat routed id up to the combine.
+  if (!act_quant && pol.forced < 0 && pol.n_live == 1 && tiny == MXQ_TINY_MFMA && R <= kStreamMaxRows &&
+      E <= kStreamMaxExperts && I % 16 == 0 &&
+      expert_stream_lds_bytes(wfmt_w16, 1, 2 * I, H, E, R) <= kStreamMaxLds &&
+      expert_stream_lds_bytes(wfmt_w16, 2, H, I, E, R) <= kStreamMaxLds) {
+    const EsRoute er{ids, int32_t(R), E, topk};
+    GemmArgs s1{};
+    s1.A = x;
+    s1.lda = H;
+    s1.W = static_cast<const uint8_t*>(w1);
+    s1.ldw = mx ? H / 2 : H;
+    s1.w_tiled = tiled;
+    s1.w_estride = tiled ? 2 * I * tiled_steps(s1.ldw) * 128 : s1.ldw * 2 * I;
+    s1.ws = w1s;
+    s1.ws_s0 = mx ? H / 32 : H / 128;
+    s1.ws_s1 = 1;
+    s1.ws_estride = mx ? (tiled ? 2 * I * tiled_scale_steps(H / 32) * 8 : 2 * I * (H / 32)) : cdiv(2 * I, 128) * (H / 128);
+    s1.bias = b1;
+    s1.bias_estride = 2 * I;
+    s1.out = w.ic1;
+    s1.ldo = I;
+    s1.M = R;
+    s1.N = 2 * I;
+    s1.K = H;
+    GemmArgs s2{};
+    s2.A = w.ic1;
+    s2.lda = I;
+    s2.W = static_cast<const uint8_t*>(w2);
+    s2.ldw = mx ? I / 2 : I;
+    s2.w_tiled = tiled;
+    s2.w_estride = tiled ? H * tiled_steps(s2.ldw) * 128 : s2.ldw * H;
+    s2.ws = w2s;
+    s2.ws_s0 = mx ? I / 32 : I / 128;
+    s2.ws_s1 = 1;
+    s2.ws_estride = mx ? (tiled ? H * tiled_scale_steps(I / 32) * 8 : H * (I / 32)) : cdiv(H, 128) * (I / 128);
+    s2.out = w.y;
+    s2.ldo = H;
+    s2.M = R;
+    s2.N = H;
+    s2.K = I;
+    launch_expert_stream(s1, wfmt_w16, 1, er, st);
+    launch_expert_stream(s2, wfmt_w16, 2, er, st);
+    launch_combine(w.y, 1, 0, wts, ids, E, M, topk, H, static_cast<uint16_t*>(out), st);
+    return launch_status();
+  }
+
+  launch_moe_align(ids, M, topk, E, kMoeBlockM, w.sorted_ids, w.expert_ids, w.offsets, w.num_blocks, mbk, pol,
+                   w.class_lists, mbk, w.class_counts, false, st);
+  if (act_quant) launch_quant_1x128(static_cast<const uint16_t*>(x), M, H, H, w.qx, H, w.sx, st);
+
+
+  // K split (bf16 activations; not with the GEMV tiny kernel): partial slices in the workspace
+  const bool gemv_runs = tiny == MXQ_TINY_GEMV && !tiled;  // the GEMV kernel writes whole sums only
+  const bool can_split = !act_quant && !gemv_runs && w.partial;
+  const KSplit sp1 = can_split ? pick_split(R, E, 2 * I, H, dc.k_split) : KSplit{1, 0};
+  const KSplit sp2 = can_split ? pick_split(R, E, H, I, dc.k_split) : KSplit{1, 0};
+  if (sp1.n > 1) {
+    g1.k_split = sp1.n;
+    g1.k_chunk = sp1.chunk;
+    g1.split_stride = R * 2 * I;
+    g1.out = w.partial;
+  }
+  if (sp2.n > 1) {
+    g2.k_split = sp2.n;
+    g2.k_chunk = sp2.chunk;
+    g2.split_stride = R * H;
+    g2.out = w.partial;
+  }
+
   // With bf16 activations and only the tiny-block class launched, stage 2 computes the
   // SiLU-and-mul while staging its rows (no ic1 round trip, one launch fewer).
-  const bool fuse_silu = !act_quant && pol.forced < 0 && pol.n_live == 1 && tiny == MXQ_TINY_MFMA &&
+  const bool fuse_silu = !act_quant && pol.forced < 0 && pol.n_live == 1 && tiny == MXQ_TINY_MFMA && sp1.n == 1 &&
                          skinny_lds_bytes(wfmt_w16, false, I) <= kSkinnyMaxLds;
   if (fuse_silu) {
     g2.A = w.ic0;
@@ -372,10 +460,13 @@ mxq_status run_moe(const void* x, int64_t M, int64_t H, int64_t I, int32_t E, in
     g2.a_silu = 1;
   }
   for (int stage = 0; stage < 2; ++stage) {
-    if (stage == 1 && !fuse_silu) launch_silu_mul(w.ic0, R, I, 2 * I, w.ic1, w.ic1_q, w.ic1_s, st);
+    if (stage == 1 && sp1.n > 1)
+      launch_split_silu_mul(w.partial, sp1.n, R * 2 * I, R, I, w.ic1, st);
+    else if (stage == 1 && !fuse_silu)
+      launch_silu_mul(w.ic0, R, I, 2 * I, w.ic1, w.ic1_q, w.ic1_s, st);
     GemmArgs& g = stage == 0 ? g1 : g2;
     const int mode = stage == 0 ? ROWS_GATHER_TOK : ROWS_COMPACT_IN;
-    const bool out_f32 = stage == 1;
+    const bool out_f32 = stage == 1 || sp1.n > 1;
     // bf16 activations: the 16/32/64/128-row tile classes go out together in one grouped launch
     GemmArgs grp[4] = {g, g, g, g};
     int64_t grp_ub[4] = {0, 0, 0, 0};
@@ -414,9 +505,17 @@ mxq_status run_moe(const void* x, int64_t M, int64_t H, int64_t I, int32_t E, in
         grp_ub[3 - tile] = ub;
       }
     }
-    if (!act_quant) launch_gemm_w16_grouped(grp, grp_ub, wfmt_w16, mode, out_f32, st);
+    if (!act_quant) {
+      if (ring)
+        launch_gemm_w16_ring(grp, grp_ub, wfmt_w16, mode, out_f32, st);
+      else
+        launch_gemm_w16_grouped(grp, grp_ub, wfmt_w16, mode, out_f32, st);
+    }
   }
-  launch_combine(w.y, wts, ids, E, M, topk, H, static_cast<uint16_t*>(out), st);
+  if (sp2.n > 1)
+    launch_combine(w.partial, sp2.n, R * H, wts, ids, E, M, topk, H, static_cast<uint16_t*>(out), st);
+  else
+    launch_combine(w.y, 1, 0, wts, ids, E, M, topk, H, static_cast<uint16_t*>(out), st);
   return launch_status();
 }
 
@@ -445,7 +544,7 @@ const char* mxq_status_string(mxq_status s) {
   }
 }
 
-int32_t mxq_abi_version(void) { return 7; }
+int32_t mxq_abi_version(void) { return 8; }
 
 mxq_status mxq_init(int32_t device) {
   if (hipSetDevice(device) != hipSuccess) return MXQ_ERR_ARCH;
@@ -745,6 +844,7 @@ mxq_status mxq_fused_moe_workspace_layout(int64_t M, int64_t H, int64_t I, int32
   offsets[MXQ_MOE_WS_IC1_S] = off(w.ic1_s);
   offsets[MXQ_MOE_WS_Y] = off(w.y);
   offsets[MXQ_MOE_WS_BLOCK_M] = kMoeBlockM;
+  offsets[MXQ_MOE_WS_PARTIAL] = off(w.partial);
   return MXQ_OK;
 }
 

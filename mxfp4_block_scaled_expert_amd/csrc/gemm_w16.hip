@@ -32,23 +32,35 @@ struct W16Layout {
   static constexpr int chunks = row_bytes / 16;  // 16-byte chunks per row
 };
 
-// LDS of one tile: A [BM][A_LROW] | W [BN][lds_row] | MX scales [BN]
-template <int BM, int BN, int WFMT>
+// LDS of one tile: A [BM][A_LROW] | W [BN][lds_row] | MX scales [BN]; after the K loop the
+// same memory stages the output tile (bf16 or fp32 rows) for row-contiguous stores.
+template <int BM, int BN, int WFMT, bool OUT_F32>
 __host__ __device__ constexpr size_t w16_lds_bytes() {
-  return size_t(BM) * (256 + 16) + size_t(BN) * W16Layout<WFMT>::lds_row + (WFMT == W_E2M1_MX ? 4 * BN : 16);
+  const size_t ops = size_t(BM) * (256 + 16) + size_t(BN) * W16Layout<WFMT>::lds_row + (WFMT == W_E2M1_MX ? 4 * BN : 16);
+  const size_t out = OUT_F32 ? size_t(BM) * (BN + 4) * 4 : size_t(BM) * (BN + 8) * 2;
+  return ops > out ? ops : out;
 }
 
-// One BM x BN output tile; `bid` is the tile's index in its launch, `lds` its share of LDS.
-template <int BM, int BN, int WAVES_M, int MODE, int WFMT, bool OUT_F32, bool HAS_BIAS, bool TILED>
+// One BM x BN output tile computed by NT threads (NT / 64 waves, WAVES_M of them along M);
+// `bid` is the tile's index in its launch, `lds` its share of LDS.
+//
+// Per 128-wide K step: the weight chunks of the step are requested first (they depend only on
+// the expert and the column tile), the activation rows once the row table is in LDS; operands
+// are staged through registers into LDS one step ahead of the products.  Activation rows past
+// the block's row count are neither loaded nor multiplied: a wave skips the 16-row MFMA tiles
+// that lie wholly past it.
+template <int NT, int BM, int BN, int WAVES_M, int MODE, int WFMT, bool OUT_F32, bool HAS_BIAS, bool TILED>
 __device__ __forceinline__ void w16_tile(const GemmArgs& a, int64_t grid_blocks, int64_t bid, uint8_t* lds) {
-  constexpr int WAVES_N = 4 / WAVES_M;
+  constexpr int WAVES = NT / 64;
+  constexpr int WAVES_N = WAVES / WAVES_M;
   constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
   constexpr int TM = WM / 16, TN = WN / 16;
-  static_assert(TM >= 1 && TN >= 1, "wave tile smaller than one MFMA tile");
+  static_assert(WAVES_M * WAVES_N == WAVES && TM >= 1 && TN >= 1, "wave tile smaller than one MFMA tile");
+  static_assert(BN <= NT, "one thread per weight row for the MX scales");
   using L = W16Layout<WFMT>;
   constexpr int A_LROW = 256 + 16;  // 128 bf16 + pad
-  constexpr int A_IT = (BM * 16 + 255) / 256;
-  constexpr int B_IT = (BN * L::chunks + 255) / 256;
+  constexpr int A_IT = (BM * 16 + NT - 1) / NT;
+  constexpr int B_IT = (BN * L::chunks + NT - 1) / NT;
   constexpr bool MX = WFMT == W_E2M1_MX;
 
   uint8_t* sA = lds;
@@ -59,50 +71,48 @@ __device__ __forceinline__ void w16_tile(const GemmArgs& a, int64_t grid_blocks,
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / WAVES_N, wn = wave % WAVES_N;
-  const int64_t tile = bid % grid_blocks;
-  const int64_t nt = bid / grid_blocks;
+  // K split: chunk `split` of the tile's K range (fastest-varying), then row tile, then column tile
+  const int nsplit = a.k_split > 1 ? a.k_split : 1;
+  const int split = int(bid % nsplit);
+  const int64_t rest = bid / nsplit;
+  const int64_t tile = rest % grid_blocks;
+  const int64_t nt = rest / grid_blocks;
   const int64_t n0 = nt * BN;
   if (n0 >= a.N) return;
 
   TileInfo t;
   if (!tile_info<BM, MODE>(a, tile, t)) return;
   const int64_t expert = t.expert;
-  for (int m_base = 0; m_base < t.m_total; m_base += BM) {
-  const int m_size = min(BM, t.m_total - m_base);
-  __syncthreads();
-  fill_rows<BM, MODE>(a, t, m_base, sArow, sOrow);
-  __syncthreads();
-
   const uint16_t* A = reinterpret_cast<const uint16_t*>(a.A);
   const uint8_t* Wb = a.W + expert * a.w_estride;
   const int KS = int(cdiv(a.K, 128));
+  // this workgroup's 128-wide K steps; an empty range (a chunk past K) stores zeros
+  int ks_b = 0, ks_e = KS;
+  if (nsplit > 1) {
+    const int cs = int(a.k_chunk >> 7);
+    ks_b = min(KS, split * cs);
+    ks_e = min(KS, ks_b + cs);
+  }
 
-  const uint16_t* pa[A_IT];
-  int ka[A_IT];
+  // weight chunk addresses (independent of the rows)
   const uint8_t* pb[B_IT];
   int kbo[B_IT];
   int sbo[B_IT];  // LDS byte offset of the chunk
   // tiled layout: 128-byte row steps per 16-row tile; an MXFP4 K step uses half a row step
   const int64_t tsteps = (a.K * (MX ? 1 : 2) / 2 + 127) / 128;
 #pragma unroll
-  for (int i = 0; i < A_IT; ++i) {
-    const int c = min(tid + 256 * i, BM * 16 - 1);
-    ka[i] = (c & 15) * 8;
-    pa[i] = A + sArow[c >> 4] * a.lda + ka[i];
-  }
-#pragma unroll
   for (int i = 0; i < B_IT; ++i) {
-    const int c = min(tid + 256 * i, BN * L::chunks - 1);
+    const int c = min(tid + NT * i, BN * L::chunks - 1);
     if (TILED) {
       // FP8: chunk c = bytes 16 (c % 128) of tile c / 128.  MXFP4: the K step is one half
       // (512 bytes per 1 KB half-tile) of a tile step, chunk c = 16 (c % 32) of half c / 32 % 2.
       constexpr int CPT = MX ? 64 : 128;  // chunks per tile per K step
-      const int t = c / CPT, p = c % CPT;
-      const int64_t grp16 = min<int64_t>(n0 / 16 + t, a.N / 16 - 1);
+      const int tt = c / CPT, p = c % CPT;
+      const int64_t grp16 = min<int64_t>(n0 / 16 + tt, a.N / 16 - 1);
       const int h = MX ? (p >> 5) : (p >> 6);
       const int L16 = p & 15, qq = MX ? ((p >> 4) & 1) : ((p >> 4) & 3);
       pb[i] = Wb + grp16 * tsteps * 2048 + h * 1024 + (qq * 16 + L16) * 16;
-      sbo[i] = (16 * t + L16) * L::lds_row + qq * 32 + h * 16;
+      sbo[i] = (16 * tt + L16) * L::lds_row + qq * 32 + h * 16;
       kbo[i] = 0;  // the K tail is zero-padded in memory
     } else {
       const int64_t n = min<int64_t>(n0 + c / L::chunks, a.N - 1);
@@ -122,14 +132,14 @@ __device__ __forceinline__ void w16_tile(const GemmArgs& a, int64_t grid_blocks,
       pbs = reinterpret_cast<const uint8_t*>(a.ws) + expert * a.ws_estride + n * a.ws_s0;
     }
   }
+  const float* swb = reinterpret_cast<const float*>(a.ws) + expert * a.ws_estride;
+  const int64_t nb_scale = n0 / 128;
 
   uint4 ra[A_IT], rb[B_IT];
   uint32_t rbs = 0;
-  auto gload = [&](int ks) __attribute__((always_inline)) {
+  float sw_next = 0.f;
+  auto gload_w = [&](int ks) __attribute__((always_inline)) {
     const int64_t kbase = int64_t(ks) * 128;
-#pragma unroll
-    for (int i = 0; i < A_IT; ++i)
-      ra[i] = (kbase + ka[i] < a.K) ? *reinterpret_cast<const uint4*>(pa[i] + kbase) : make_uint4(0, 0, 0, 0);
     // byte offset of this K step inside a chunk's row (plain) or tile sequence (tiled)
     const int64_t bstep = TILED ? (MX ? int64_t(ks >> 1) * 2048 + (ks & 1) * 512 : int64_t(ks) * 2048)
                                 : kbase * L::row_bytes / 128;
@@ -150,18 +160,44 @@ __device__ __forceinline__ void w16_tile(const GemmArgs& a, int64_t grid_blocks,
         if (g0 + g < ngrp) v |= uint32_t(pbs[g0 + g]) << (8 * g);
       rbs = v;
     }
+    // the weight-block scale of the step is read with its operands, one step ahead of its use
+    if (WFMT == W_E4M3_BLOCK) sw_next = swb[nb_scale * a.ws_s0 + ks * a.ws_s1];
+  };
+
+  for (int m_base = 0; m_base < t.m_total; m_base += BM) {
+  const int m_size = min(BM, t.m_total - m_base);
+  __syncthreads();
+  if (ks_b < ks_e) gload_w(ks_b);
+  fill_rows<BM, MODE>(a, t, m_base, sArow, sOrow);
+  __syncthreads();
+
+  const uint16_t* pa[A_IT];
+  int ka[A_IT];
+  bool la[A_IT];  // the chunk's row holds data (rows past m_size are zero-filled)
+#pragma unroll
+  for (int i = 0; i < A_IT; ++i) {
+    const int c = min(tid + NT * i, BM * 16 - 1);
+    ka[i] = (c & 15) * 8;
+    la[i] = (c >> 4) < m_size;
+    pa[i] = A + sArow[c >> 4] * a.lda + ka[i];
+  }
+  auto gload_a = [&](int ks) __attribute__((always_inline)) {
+    const int64_t kbase = int64_t(ks) * 128;
+#pragma unroll
+    for (int i = 0; i < A_IT; ++i)
+      ra[i] = (la[i] && kbase + ka[i] < a.K) ? *reinterpret_cast<const uint4*>(pa[i] + kbase) : make_uint4(0, 0, 0, 0);
   };
   auto lstore = [&]() __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < A_IT; ++i) {
-      const int c = tid + 256 * i;
-      if (A_IT * 256 == BM * 16 || c < BM * 16)
+      const int c = tid + NT * i;
+      if (A_IT * NT == BM * 16 || c < BM * 16)
         *reinterpret_cast<uint4*>(sA + (c >> 4) * A_LROW + (c & 15) * 16) = ra[i];
     }
 #pragma unroll
     for (int i = 0; i < B_IT; ++i) {
-      const int c = tid + 256 * i;
-      if (B_IT * 256 == BN * L::chunks || c < BN * L::chunks) *reinterpret_cast<uint4*>(sB + sbo[i]) = rb[i];
+      const int c = tid + NT * i;
+      if (B_IT * NT == BN * L::chunks || c < BN * L::chunks) *reinterpret_cast<uint4*>(sB + sbo[i]) = rb[i];
     }
     if (MX && tid < BN) sBs[tid] = rbs;
   };
@@ -174,15 +210,19 @@ __device__ __forceinline__ void w16_tile(const GemmArgs& a, int64_t grid_blocks,
 
   const int frow = lane & 15;
   const int fq = lane >> 4;  // which 8-element K slice of a 32-wide MFMA step
-  const float* swb = reinterpret_cast<const float*>(a.ws) + expert * a.ws_estride;
-  const int64_t nb_scale = n0 / 128;
+  // 16-row MFMA tiles of this wave that hold rows of the block
+  const int tm_live = min(TM, max(0, (m_size - wm * WM + 15) >> 4));
 
-  gload(0);
-  for (int ks = 0; ks < KS; ++ks) {
+  if (ks_b < ks_e) gload_a(ks_b);
+  for (int ks = ks_b; ks < ks_e; ++ks) {
+    const float sw = sw_next;
     __syncthreads();
     lstore();
     __syncthreads();
-    if (ks + 1 < KS) gload(ks + 1);
+    if (ks + 1 < ks_e) {
+      gload_w(ks + 1);
+      gload_a(ks + 1);
+    }
 
     const int nsub = int(min<int64_t>(4, (a.K - int64_t(ks) * 128) >> 5));
     f32x4 part[TM][TN];
@@ -197,7 +237,8 @@ __device__ __forceinline__ void w16_tile(const GemmArgs& a, int64_t grid_blocks,
       i32x4 af[TM], bfr[TN];
 #pragma unroll
       for (int i = 0; i < TM; ++i)
-        af[i] = *reinterpret_cast<const i32x4*>(sA + (wm * WM + 16 * i + frow) * A_LROW + (s * 32 + fq * 8) * 2);
+        if (i < tm_live)
+          af[i] = *reinterpret_cast<const i32x4*>(sA + (wm * WM + 16 * i + frow) * A_LROW + (s * 32 + fq * 8) * 2);
 #pragma unroll
       for (int j = 0; j < TN; ++j) {
         const int brow = wn * WN + 16 * j + frow;
@@ -216,7 +257,8 @@ __device__ __forceinline__ void w16_tile(const GemmArgs& a, int64_t grid_blocks,
         }
       }
 #pragma unroll
-      for (int i = 0; i < TM; ++i)
+      for (int i = 0; i < TM; ++i) {
+        if (i >= tm_live) continue;
 #pragma unroll
         for (int j = 0; j < TN; ++j) {
           if (WFMT == W_E4M3_BLOCK)
@@ -224,9 +266,9 @@ __device__ __forceinline__ void w16_tile(const GemmArgs& a, int64_t grid_blocks,
           else
             acc[i][j] = mfma_16x16x32_bf16(af[i], bfr[j], acc[i][j]);
         }
+      }
     }
     if (WFMT == W_E4M3_BLOCK) {
-      const float sw = swb[nb_scale * a.ws_s0 + ks * a.ws_s1];
 #pragma unroll
       for (int i = 0; i < TM; ++i)
 #pragma unroll
@@ -237,39 +279,47 @@ __device__ __forceinline__ void w16_tile(const GemmArgs& a, int64_t grid_blocks,
   }
 
   const float tscale = (WFMT == W_E4M3_TENSOR) ? reinterpret_cast<const float*>(a.ws)[0] : 1.f;
-  // bf16 output with 16-byte aligned rows: the tile goes through LDS (the operand buffers are
-  // free after the K loop) and leaves as 16-byte row chunks instead of 2-byte column stores
-  constexpr int OROW = BN + 8;  // bf16 elements per staged row (padding against bank conflicts)
-  static_assert(size_t(BM) * OROW * 2 <= w16_lds_bytes<BM, BN, WFMT>(), "staged output fits the tile's LDS");
-  const bool staged = !OUT_F32 && (reinterpret_cast<uintptr_t>(a.out) & 15) == 0 && (a.ldo & 7) == 0;
+  // Outputs with 16-byte aligned rows go through LDS (the operand buffers are free after the K
+  // loop) and leave as 16-byte row chunks instead of 2- or 4-byte column stores.  K-split
+  // chunks write their fp32 partial sums to their own slice; the bias rides on chunk 0.
+  constexpr int OE = OUT_F32 ? 4 : 2;          // output element bytes
+  constexpr int OROW = BN + (OUT_F32 ? 4 : 8); // staged row, elements (padding against bank conflicts)
+  constexpr int CH = 16 / OE;                  // elements per 16-byte chunk
+  static_assert(size_t(BM) * OROW * OE <= w16_lds_bytes<BM, BN, WFMT, OUT_F32>(), "staged output fits the tile's LDS");
+  uint8_t* const obase = static_cast<uint8_t*>(a.out) + (nsplit > 1 ? split * a.split_stride * OE : 0);
+  const bool staged = (reinterpret_cast<uintptr_t>(obase) & 15) == 0 && (a.ldo % CH) == 0;
   if (staged) {
-    uint16_t* sO = reinterpret_cast<uint16_t*>(lds);
     __syncthreads();  // every wave is done with the operand buffers
 #pragma unroll
     for (int j = 0; j < TN; ++j) {
       const int cl = wn * WN + 16 * j + frow;
       const int64_t col = n0 + cl;
-      const float b = HAS_BIAS && col < a.N ? load_bias(a, expert, col) : 0.f;
+      const float b = HAS_BIAS && split == 0 && col < a.N ? load_bias(a, expert, col) : 0.f;
 #pragma unroll
       for (int i = 0; i < TM; ++i)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           float v = acc[i][j][r];
           if (WFMT == W_E4M3_TENSOR) v = v * tscale;
-          sO[(wm * WM + 16 * i + 4 * (lane >> 4) + r) * OROW + cl] = f2bf(v + b);
+          const int rl = wm * WM + 16 * i + 4 * (lane >> 4) + r;
+          if (OUT_F32)
+            reinterpret_cast<float*>(lds)[rl * OROW + cl] = v + b;
+          else
+            reinterpret_cast<uint16_t*>(lds)[rl * OROW + cl] = f2bf(v + b);
         }
     }
     __syncthreads();
     const int64_t ncols = min<int64_t>(BN, a.N - n0);
-    for (int c = tid; c < m_size * (BN / 8); c += 256) {
-      const int rl = c / (BN / 8), ch = c % (BN / 8);
-      const int64_t col = n0 + ch * 8;
-      uint16_t* dst = reinterpret_cast<uint16_t*>(a.out) + sOrow[rl] * a.ldo + col;
-      const uint16_t* src = sO + rl * OROW + ch * 8;
-      if (ch * 8 + 8 <= ncols) {
+    for (int c = tid; c < m_size * (BN / CH); c += NT) {
+      const int rl = c / (BN / CH), ch = c % (BN / CH);
+      const int64_t col = n0 + ch * CH;
+      uint8_t* dst = obase + (sOrow[rl] * a.ldo + col) * OE;
+      const uint8_t* src = lds + (rl * OROW + ch * CH) * OE;
+      if (ch * CH + CH <= ncols) {
         *reinterpret_cast<uint4*>(dst) = *reinterpret_cast<const uint4*>(src);
       } else {
-        for (int e = 0; e < 8 && ch * 8 + e < ncols; ++e) dst[e] = src[e];
+        for (int e = 0; e < CH && ch * CH + e < ncols; ++e)
+          for (int k = 0; k < OE; ++k) dst[e * OE + k] = src[e * OE + k];
       }
     }
     continue;  // next row pass (its first barrier orders these LDS reads before new writes)
@@ -278,7 +328,7 @@ __device__ __forceinline__ void w16_tile(const GemmArgs& a, int64_t grid_blocks,
   for (int j = 0; j < TN; ++j) {
     const int64_t col = n0 + wn * WN + 16 * j + frow;
     if (col >= a.N) continue;
-    const float b = HAS_BIAS ? load_bias(a, expert, col) : 0.f;
+    const float b = HAS_BIAS && split == 0 ? load_bias(a, expert, col) : 0.f;
 #pragma unroll
     for (int i = 0; i < TM; ++i)
 #pragma unroll
@@ -288,11 +338,11 @@ __device__ __forceinline__ void w16_tile(const GemmArgs& a, int64_t grid_blocks,
         float v = acc[i][j][r];
         if (WFMT == W_E4M3_TENSOR) v = v * tscale;
         v = v + b;
-        const int64_t orow = sOrow[rl];
+        const int64_t o = sOrow[rl] * a.ldo + col;
         if (OUT_F32)
-          reinterpret_cast<float*>(a.out)[orow * a.ldo + col] = v;
+          reinterpret_cast<float*>(obase)[o] = v;
         else
-          reinterpret_cast<uint16_t*>(a.out)[orow * a.ldo + col] = f2bf(v);
+          reinterpret_cast<uint16_t*>(obase)[o] = f2bf(v);
       }
   }
   }  // m sub-tiles
@@ -311,38 +361,44 @@ __global__ __launch_bounds__(256) void gemm_w16_kernel(GemmArgs a, int64_t grid_
       a.bias = static_cast<const uint8_t*>(a.bias) + z * a.bias_estride * (a.bias_bf16 ? 2 : 4);
     a.out = static_cast<uint8_t*>(a.out) + z * a.o_bstride * (OUT_F32 ? 4 : 2);
   }
-  w16_tile<BM, BN, WAVES_M, MODE, WFMT, OUT_F32, HAS_BIAS, TILED>(a, grid_blocks, blockIdx.x, w16_lds);
+  w16_tile<256, BM, BN, WAVES_M, MODE, WFMT, OUT_F32, HAS_BIAS, TILED>(a, grid_blocks, blockIdx.x, w16_lds);
 }
 
-// Routed tile classes 16 / 32 / 64 / 128 rows in one launch: workgroups [off[c], off[c + 1])
-// run tiles of class c over its own work list, so the classes of a stage run side by side
-// instead of one launch after another (small batches leave most of the GPU idle in each).
+// Routed tile classes 16 / 32 / 64 / 128 rows in one launch of 512-thread workgroups (two
+// waves per SIMD, so one wave's LDS reads overlap the other's products): workgroups
+// [off[c], off[c + 1]) run tiles of class c over its own work list, so the classes of a stage
+// run side by side instead of one launch after another (small batches leave most of the GPU
+// idle in each).  The 128-row class comes first in the grid, then 64, 32, 16: the longest
+// tiles start first instead of queueing behind the other classes' workgroups.
+constexpr int kW16GroupThreads = 512;
 struct W16Group {
-  GemmArgs a[4];    // per class: the stage's arguments with that class's work list
+  GemmArgs a[4];    // per class (16, 32, 64, 128 rows): the stage's arguments with its work list
   int64_t gb[4];    // per class: work-list capacity
-  int64_t off[5];   // first workgroup of each class; off[4] = grid size
+  int64_t off[5];   // launch order 128, 64, 32, 16 rows: off[0] = 0, off[4] = grid size
 };
 
 template <int MODE, int WFMT, bool OUT_F32, bool HAS_BIAS, bool TILED>
-__global__ __launch_bounds__(256) void gemm_w16_grouped_kernel(W16Group g) {
+__global__ __launch_bounds__(kW16GroupThreads) void gemm_w16_grouped_kernel(W16Group g) {
   extern __shared__ __align__(16) uint8_t w16_lds[];
+  constexpr int NT = kW16GroupThreads;
   const int64_t b = blockIdx.x;
   if (b < g.off[1])
-    w16_tile<16, 128, 1, MODE, WFMT, OUT_F32, HAS_BIAS, TILED>(g.a[0], g.gb[0], b - g.off[0], w16_lds);
+    w16_tile<NT, 128, 128, 4, MODE, WFMT, OUT_F32, HAS_BIAS, TILED>(g.a[3], g.gb[3], b - g.off[0], w16_lds);
   else if (b < g.off[2])
-    w16_tile<32, 128, 1, MODE, WFMT, OUT_F32, HAS_BIAS, TILED>(g.a[1], g.gb[1], b - g.off[1], w16_lds);
+    w16_tile<NT, 64, 128, 2, MODE, WFMT, OUT_F32, HAS_BIAS, TILED>(g.a[2], g.gb[2], b - g.off[1], w16_lds);
   else if (b < g.off[3])
-    w16_tile<64, 128, 2, MODE, WFMT, OUT_F32, HAS_BIAS, TILED>(g.a[2], g.gb[2], b - g.off[2], w16_lds);
+    w16_tile<NT, 32, 128, 2, MODE, WFMT, OUT_F32, HAS_BIAS, TILED>(g.a[1], g.gb[1], b - g.off[2], w16_lds);
   else
-    w16_tile<128, 128, 2, MODE, WFMT, OUT_F32, HAS_BIAS, TILED>(g.a[3], g.gb[3], b - g.off[3], w16_lds);
+    w16_tile<NT, 16, 128, 1, MODE, WFMT, OUT_F32, HAS_BIAS, TILED>(g.a[0], g.gb[0], b - g.off[3], w16_lds);
 }
 
 template <int BM, int BN, int WAVES_M, int MODE, int WFMT, bool TL>
 static void launch_w16_tl(const GemmArgs& a, bool out_f32, int64_t grid_blocks, hipStream_t st, unsigned batch = 1) {
   const int64_t n_tiles = cdiv(a.N, BN);
-  const dim3 grid(unsigned(grid_blocks * n_tiles), batch), block(256);
+  const int64_t nsplit = a.k_split > 1 ? a.k_split : 1;
+  const dim3 grid(unsigned(grid_blocks * n_tiles * nsplit), batch), block(256);
   const bool bias = a.bias != nullptr;
-  const size_t lds = w16_lds_bytes<BM, BN, WFMT>();
+  const size_t lds = out_f32 ? w16_lds_bytes<BM, BN, WFMT, true>() : w16_lds_bytes<BM, BN, WFMT, false>();
 #define MXQ_W16_GO(OF, HB) \
   hipLaunchKernelGGL((gemm_w16_kernel<BM, BN, WAVES_M, MODE, WFMT, OF, HB, TL>), grid, block, lds, st, a, grid_blocks)
   if (out_f32) { if (bias) MXQ_W16_GO(true, true); else MXQ_W16_GO(true, false); }
@@ -383,7 +439,7 @@ static void launch_w16_fmt(const GemmArgs& a, int wfmt, int tile, bool out_f32, 
 
 template <int MODE, int WFMT, bool TL>
 static void launch_w16_grouped_t(const W16Group& g, bool out_f32, size_t lds, hipStream_t st) {
-  const dim3 grid(unsigned(g.off[4])), block(256);
+  const dim3 grid(unsigned(g.off[4])), block(kW16GroupThreads);
   const bool bias = g.a[0].bias != nullptr;
 #define MXQ_W16G_GO(OF, HB) \
   hipLaunchKernelGGL((gemm_w16_grouped_kernel<MODE, WFMT, OF, HB, TL>), grid, block, lds, st, g)
@@ -394,12 +450,14 @@ static void launch_w16_grouped_t(const W16Group& g, bool out_f32, size_t lds, hi
 
 template <int MODE, int WFMT>
 static void launch_w16_grouped_m(const W16Group& g, bool out_f32, hipStream_t st) {
-  // LDS of the largest class that holds workgroups
+  // LDS of the largest class that holds workgroups (launch order 128, 64, 32, 16 rows)
   size_t lds = 0;
-  const size_t per[4] = {w16_lds_bytes<16, 128, WFMT>(), w16_lds_bytes<32, 128, WFMT>(),
-                         w16_lds_bytes<64, 128, WFMT>(), w16_lds_bytes<128, 128, WFMT>()};
-  for (int c = 0; c < 4; ++c)
-    if (g.off[c + 1] > g.off[c]) lds = std::max(lds, per[c]);
+  const size_t per_f32[4] = {w16_lds_bytes<128, 128, WFMT, true>(), w16_lds_bytes<64, 128, WFMT, true>(),
+                             w16_lds_bytes<32, 128, WFMT, true>(), w16_lds_bytes<16, 128, WFMT, true>()};
+  const size_t per_bf16[4] = {w16_lds_bytes<128, 128, WFMT, false>(), w16_lds_bytes<64, 128, WFMT, false>(),
+                              w16_lds_bytes<32, 128, WFMT, false>(), w16_lds_bytes<16, 128, WFMT, false>()};
+  for (int i = 0; i < 4; ++i)
+    if (g.off[i + 1] > g.off[i]) lds = std::max(lds, out_f32 ? per_f32[i] : per_bf16[i]);
   if (g.a[0].w_tiled)
     launch_w16_grouped_t<MODE, WFMT, true>(g, out_f32, lds, st);
   else
@@ -419,7 +477,10 @@ void launch_gemm_w16_grouped(const GemmArgs cls[4], const int64_t grid_blocks[4]
   for (int c = 0; c < 4; ++c) {
     g.a[c] = cls[c];
     g.gb[c] = std::max<int64_t>(grid_blocks[c], 0);
-    g.off[c + 1] = g.off[c] + g.gb[c] * cdiv(cls[c].N, 128);
+  }
+  for (int i = 0; i < 4; ++i) {  // launch order: 128-, 64-, 32-, 16-row class
+    const int c = 3 - i;
+    g.off[i + 1] = g.off[i] + g.gb[c] * cdiv(cls[c].N, 128) * std::max<int64_t>(cls[c].k_split, 1);
   }
   if (g.off[4] <= 0) return;
   const bool mx = wfmt == W_E2M1_MX;

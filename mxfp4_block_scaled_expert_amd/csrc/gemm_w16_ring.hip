@@ -1,0 +1,434 @@
+// Routed bf16-activation expert tiles (W8A16 block-FP8 and W4A16 MXFP4 weights) fed by a ring of
+// LDS stages that direct global-to-LDS copies fill.
+//
+// What is computed is the block walk of "vLLM PR 50949 review" (moe_fp8.cpp listing): each
+// expert block's rows times its expert's weights, the e4m3 partial sum of every 128-wide K block
+// scaled by that block's weight scale before it joins the accumulator; MXFP4 weights carry an
+// e8m0 scale per 32 elements, folded into the exact e2m1 -> bf16 decode.  The products run on
+// V_MFMA_F32_16X16X32_BF16 after in-register decode of the weights (every e4m3 value and every
+// scaled e2m1 value is a bf16 value).
+//
+// How it is fed: a 128-wide K step of a tile is one LDS stage (activation rows, 128 weight rows,
+// MXFP4 scales).  GLOBAL_LOAD_LDS copies move the step straight from memory into its stage, so no
+// register staging or second barrier sits between a step's arrival and its products; NS stages
+// (three for 128-row tiles, four for smaller ones) keep NS - 1 steps in flight while one is being
+// multiplied.  Every wave issues the same number of copies per step, so one vmcnt wait per step
+// followed by one barrier publishes the step.  Eight waves (two per SIMD) let one wave's LDS
+// reads overlap the other's products.  (Measured and dropped: issuing the first steps' weight
+// copies before the row table is read, and skipping the copies of activation rows past the
+// block's row count with per-wave vmcnt targets -- both 2-5 % slower.)
+//
+// LDS layouts (per stage):
+//  * activations: row-major 256-byte rows; the 16-byte chunk c of row r sits in slot c ^ (r % 16)
+//    (the copying lane picks its source chunk by that rule), so the 16 rows an MFMA fragment read
+//    touches fall in 16 different bank groups;
+//  * e4m3 weights: per 16-row group a 2 KB block in fragment order -- half h, lane (q, r) holds
+//    bytes [32 q + 16 h, +16) of row r's 128-byte step -- the layout the tiled prepack format
+//    already has in memory, gathered the same way from the plain layout;
+//  * e2m1 weights: per 16-row group 1 KB, half h = (K step offset / 16) % 2 of the 64-byte step;
+//  * e8m0 scales: tiled, the 64 bytes of each group's scale tile for the step; plain, 4 bytes
+//    per row.
+// A ragged K tail (K a multiple of 32, not of 128) needs no zero fill: the sub-steps of 32 past K
+// are not computed, and copies past a row's end read that row's first chunk instead.
+#include <algorithm>
+#include <type_traits>
+
+#include "lds_dma.hpp"
+#include "tile_rows.hpp"
+
+namespace mxq {
+
+namespace {
+
+constexpr int kRingThreads = 512;
+constexpr int kRingMaxSteps = 128;  // K <= 16384: weight-block scales of the K range in LDS
+
+template <int WFMT>
+struct RingFmt {
+  static constexpr bool MX = WFMT == W_E2M1_MX;
+  static constexpr int w_bytes = MX ? 128 * 64 : 128 * 128;  // 128 weight rows of one K step
+  static constexpr int s_bytes = MX ? 512 : 0;                // their e8m0 scales
+};
+
+template <int BM>
+constexpr int ring_stages() { return BM == 128 ? 3 : 4; }
+
+template <int BM, int WFMT>
+constexpr int ring_stage_bytes() { return BM * 256 + RingFmt<WFMT>::w_bytes + RingFmt<WFMT>::s_bytes; }
+
+template <int BM, int WFMT, bool OUT_F32>
+constexpr size_t ring_lds_bytes() {
+  const size_t ops = size_t(ring_stages<BM>()) * ring_stage_bytes<BM, WFMT>() + kRingMaxSteps * 4;
+  const size_t out = OUT_F32 ? size_t(BM) * (128 + 4) * 4 : size_t(BM) * (128 + 8) * 2;
+  return ops > out ? ops : out;
+}
+
+}  // namespace
+
+template <int BM, int MODE, int WFMT, bool OUT_F32, bool HAS_BIAS, bool TILED>
+__device__ __forceinline__ void ring_tile(const GemmArgs& a, int64_t grid_blocks, int64_t bid, uint8_t* lds) {
+  constexpr int NT = kRingThreads, BN = 128, NS = ring_stages<BM>();
+  constexpr int WAVES_M = BM == 128 ? 4 : (BM == 16 ? 1 : 2);
+  constexpr int WAVES_N = (NT / 64) / WAVES_M;
+  constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
+  constexpr int TM = WM / 16, TN = WN / 16;
+  static_assert(TM >= 1 && TN >= 1 && TM <= 2, "wave tile");
+  constexpr bool MX = WFMT == W_E2M1_MX;
+  constexpr int STAGE = ring_stage_bytes<BM, WFMT>();
+  constexpr int W_OFF = BM * 256, S_OFF = W_OFF + RingFmt<WFMT>::w_bytes;
+  constexpr int A_INS = BM == 16 ? 1 : BM / 32;  // activation copies per wave per step
+  constexpr int P = A_INS + 2;                    // copies per wave per step (+ weights, scales)
+  static_assert(NS - 2 <= 2, "vmcnt targets below cover at most two steps in flight");
+
+  float* const sSw = reinterpret_cast<float*>(lds + NS * STAGE);  // weight-block scale per K step
+  const uint32_t lbase = lds_addr(lds);  // LDS byte address of the stages, as copies take it
+  __shared__ int64_t sArow[BM];
+  __shared__ int64_t sOrow[BM];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave / WAVES_N, wn = wave % WAVES_N;
+  const int frow = lane & 15, fq = lane >> 4;
+  // K split: chunk `split` of the tile's K range (fastest-varying), then row tile, then column tile
+  const int nsplit = a.k_split > 1 ? a.k_split : 1;
+  const int split = int(bid % nsplit);
+  const int64_t rest = bid / nsplit;
+  const int64_t tile = rest % grid_blocks;
+  const int64_t nt = rest / grid_blocks;
+  const int64_t n0 = nt * BN;
+  if (n0 >= a.N) return;
+  TileInfo t;
+  if (!tile_info<BM, MODE>(a, tile, t)) return;
+  const int64_t expert = t.expert;
+  const int KS = int(cdiv(a.K, 128));
+  int ks_b = 0, ks_e = KS;
+  if (nsplit > 1) {
+    const int cs = int(a.k_chunk >> 7);
+    ks_b = min(KS, split * cs);
+    ks_e = min(KS, ks_b + cs);
+  }
+  const int nsteps = ks_e - ks_b;
+
+  // weight-block scales of the K range (read before any copy is in flight)
+  if (WFMT == W_E4M3_BLOCK) {
+    const float* swb = reinterpret_cast<const float*>(a.ws) + expert * a.ws_estride + (n0 / 128) * a.ws_s0;
+    for (int i = tid; i < nsteps; i += NT) sSw[i] = swb[int64_t(ks_b + i) * a.ws_s1];
+  }
+
+  // ---- weight copy sources (row-independent): wave w copies the 16-row group w of the tile
+  const uint8_t* Wb = a.W + expert * a.w_estride;
+  const int64_t row_bytes = MX ? a.K / 2 : a.K;
+  const int64_t tsteps = (row_bytes + 127) / 128;  // tiled layout: 128-byte row steps per group
+  const int64_t grp16 = min<int64_t>(n0 / 16 + wave, a.N / 16 - 1);
+  const int64_t wrow = min<int64_t>(n0 + 16 * wave + frow, a.N - 1);
+  const uint8_t* gw[2];
+  int wbyte[2];  // plain layout: first byte of the lane's piece inside the row's K step
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    if (MX) {
+      // one copy per step: lane (h, qq, r) = (lane / 32, lane / 16 % 2, lane % 16)
+      const int hh = lane >> 5, qq = (lane >> 4) & 1;
+      wbyte[h] = qq * 32 + hh * 16;
+      gw[h] = TILED ? Wb + grp16 * tsteps * 2048 + hh * 1024 + (qq * 16 + frow) * 16 : Wb + wrow * a.ldw + wbyte[h];
+    } else {
+      // two copies per step (halves h): lane (qq, r) = (lane / 16, lane % 16)
+      wbyte[h] = fq * 32 + h * 16;
+      gw[h] = TILED ? Wb + grp16 * tsteps * 2048 + h * 1024 + lane * 16 : Wb + wrow * a.ldw + wbyte[h];
+    }
+  }
+  const uint8_t* gs = nullptr;  // MXFP4 scale source (lanes 0..15)
+  if (MX) {
+    const uint8_t* se = reinterpret_cast<const uint8_t*>(a.ws) + expert * a.ws_estride;
+    if (TILED)
+      gs = se + grp16 * tsteps * 128 + (lane & 15) * 4;
+    else
+      gs = se + min<int64_t>(n0 + 16 * wave + (lane & 15), a.N - 1) * a.ws_s0;
+  }
+
+  for (int m_base = 0; m_base < t.m_total; m_base += BM) {
+    const int m_size = min(BM, t.m_total - m_base);
+    __syncthreads();  // the previous pass is done with the row tables and LDS
+
+    auto issue_w = [&](int ks, int stage) __attribute__((always_inline)) {
+      const uint32_t sb = lbase + uint32_t(stage * STAGE);
+      const int64_t kbase = int64_t(ks) * 128;
+      if (MX) {
+        const int64_t step = TILED ? int64_t(ks >> 1) * 2048 + (ks & 1) * 512 : int64_t(ks) * 64;
+        const uint8_t* src = gw[0] + step;
+        if (!TILED && step + wbyte[0] >= row_bytes) src = gw[0] - wbyte[0];
+        lds_dma16(src, sb + W_OFF + wave * 1024);
+        const int64_t sstep = TILED ? int64_t(ks >> 1) * 128 + (ks & 1) * 64 : int64_t(ks) * 4;
+        if (lane < 16) lds_dma4(gs + sstep, sb + S_OFF + wave * 64);
+      } else {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int64_t step = TILED ? int64_t(ks) * 2048 : kbase;
+          const uint8_t* src = gw[h] + step;
+          if (!TILED && step + wbyte[h] >= row_bytes) src = gw[h] - wbyte[h];
+          lds_dma16(src, sb + W_OFF + wave * 2048 + h * 1024);
+        }
+      }
+    };
+
+    fill_rows<BM, MODE>(a, t, m_base, sArow, sOrow);
+    __syncthreads();
+
+    // ---- activation copy sources: copy k of wave w holds rows 4 (w + 8 k) .. +3 (BM = 16:
+    // rows 2 w, 2 w + 1 on lanes 0..31); the lane's source chunk is its slot XOR the row's swizzle
+    const uint8_t* ga[A_INS];
+    int gac[A_INS];
+#pragma unroll
+    for (int k = 0; k < A_INS; ++k) {
+      const int row = BM == 16 ? min(2 * wave + (lane >> 4), BM - 1) : 4 * (wave + 8 * k) + (lane >> 4);
+      const int c = (lane & 15) ^ (row & 15);
+      gac[k] = c;
+      ga[k] = reinterpret_cast<const uint8_t*>(a.A) + sArow[row] * a.lda * 2 + c * 16;
+    }
+
+    auto issue_a = [&](int ks, int stage) __attribute__((always_inline)) {
+      const uint32_t sb = lbase + uint32_t(stage * STAGE);
+      const int64_t kbase = int64_t(ks) * 128;
+#pragma unroll
+      for (int k = 0; k < A_INS; ++k) {
+        // a chunk past K re-reads the row's first chunk (its sub-step is never computed)
+        const uint8_t* src = kbase + gac[k] * 8 < a.K ? ga[k] + kbase * 2 : ga[k] - gac[k] * 16;
+        const uint32_t dst = sb + (BM == 16 ? wave * 512 : (wave + 8 * k) * 1024);
+        if (BM != 16 || lane < 32) lds_dma16(src, dst);
+      }
+    };
+
+    f32x4 acc[TM][TN];
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    // products of one K step for the wave's first TL row tiles (those holding block rows);
+    // FULL: all four 32-wide sub-steps lie inside K
+    auto compute = [&](int ks, int stage, auto tl_c, auto full_c) __attribute__((always_inline)) {
+      constexpr int TL = decltype(tl_c)::value;
+      constexpr bool FULL = decltype(full_c)::value;
+      const uint8_t* const sa = lds + stage * STAGE;
+      const uint8_t* const sw = sa + W_OFF;
+      const uint8_t* const ss = sa + S_OFF;
+      const int nsub = FULL ? 4 : int(min<int64_t>(4, (a.K - int64_t(ks) * 128) >> 5));
+      f32x4 part[TL][TN];
+#pragma unroll
+      for (int i = 0; i < TL; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j) part[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        if (!FULL && s >= nsub) break;
+        i32x4 af[TL], bfr[TN];
+#pragma unroll
+        for (int i = 0; i < TL; ++i) {
+          const int r = wm * WM + 16 * i + frow;
+          af[i] = *reinterpret_cast<const i32x4*>(sa + r * 256 + (((s * 4 + fq) ^ frow) << 4));
+        }
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+          const int g = (wn * WN >> 4) + j;  // 16-row weight group
+          if (MX) {
+            const uint32_t v =
+                *reinterpret_cast<const uint32_t*>(sw + g * 1024 + (s & 1) * 512 + ((s >> 1) * 16 + frow) * 16 + fq * 4);
+            const uint32_t e = TILED ? ss[g * 64 + (s >> 1) * 32 + frow * 2 + (s & 1)] : ss[(g * 16 + frow) * 4 + s];
+            uint32_t o[4];
+            e2m1x8_to_bf16(v, e8m0_to_f32(e), o);
+            bfr[j] = i32x4{int(o[0]), int(o[1]), int(o[2]), int(o[3])};
+          } else {
+            const uint2 v =
+                *reinterpret_cast<const uint2*>(sw + g * 2048 + (fq >> 1) * 1024 + (s * 16 + frow) * 16 + (fq & 1) * 8);
+            uint32_t o0, o1, o2, o3;
+            e4m3x4_to_bf16(v.x, o0, o1);
+            e4m3x4_to_bf16(v.y, o2, o3);
+            bfr[j] = i32x4{int(o0), int(o1), int(o2), int(o3)};
+          }
+        }
+#pragma unroll
+        for (int i = 0; i < TL; ++i)
+#pragma unroll
+          for (int j = 0; j < TN; ++j) {
+            if (MX)
+              acc[i][j] = mfma_16x16x32_bf16(af[i], bfr[j], acc[i][j]);
+            else
+              part[i][j] = mfma_16x16x32_bf16(af[i], bfr[j], part[i][j]);
+          }
+      }
+      if (!MX) {
+        const float swv = sSw[ks - ks_b];
+#pragma unroll
+        for (int i = 0; i < TL; ++i)
+#pragma unroll
+          for (int j = 0; j < TN; ++j)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) acc[i][j][r] = fmaf(part[i][j][r], swv, acc[i][j][r]);
+      }
+    };
+
+    // row tiles of this wave that hold rows of the block
+    const int tl = min(TM, max(0, (m_size - wm * WM + 15) >> 4));
+
+    for (int j = 0; j < NS - 1; ++j)
+      if (j < nsteps) {
+        issue_w(ks_b + j, j);
+        issue_a(ks_b + j, j);
+      }
+    for (int j = 0; j < nsteps; ++j) {
+      // this wave's copies of step j have landed once at most the copies of the steps issued
+      // after it are outstanding (copies complete in issue order); the barrier then publishes
+      // every wave's copies, and retires every wave's reads of the stage the next copies overwrite
+      const int after = min(NS - 2, nsteps - 1 - j);
+      if (after >= 2)
+        wait_vmcnt<2 * P>();
+      else if (after == 1)
+        wait_vmcnt<P>();
+      else
+        wait_vmcnt<0>();
+      __syncthreads();
+      if (j + NS - 1 < nsteps) {
+        issue_w(ks_b + j + NS - 1, (j + NS - 1) % NS);
+        issue_a(ks_b + j + NS - 1, (j + NS - 1) % NS);
+      }
+      const int ks = ks_b + j;
+      const bool full = int64_t(ks) * 128 + 128 <= a.K;
+      if (tl == TM) {
+        if (full) compute(ks, j % NS, std::integral_constant<int, TM>{}, std::true_type{});
+        else compute(ks, j % NS, std::integral_constant<int, TM>{}, std::false_type{});
+      } else if (TM == 2 && tl == 1) {
+        if (full) compute(ks, j % NS, std::integral_constant<int, 1>{}, std::true_type{});
+        else compute(ks, j % NS, std::integral_constant<int, 1>{}, std::false_type{});
+      }
+    }
+
+    // ---- epilogue: the tile goes through LDS (free once every wave is past its last products)
+    // and leaves as 16-byte row chunks; K-split chunks write fp32 partial sums to their own
+    // slice, the bias rides on chunk 0
+    constexpr int OE = OUT_F32 ? 4 : 2;
+    constexpr int OROW = BN + (OUT_F32 ? 4 : 8);
+    constexpr int CH = 16 / OE;
+    static_assert(size_t(BM) * OROW * OE <= size_t(NS) * STAGE, "staged output fits the operand stages");
+    uint8_t* const obase = static_cast<uint8_t*>(a.out) + (nsplit > 1 ? split * a.split_stride * OE : 0);
+    wait_vmcnt<0>();
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+      const int cl = wn * WN + 16 * j + frow;
+      const int64_t col = n0 + cl;
+      const float b = HAS_BIAS && split == 0 && col < a.N ? load_bias(a, expert, col) : 0.f;
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int rl = wm * WM + 16 * i + 4 * fq + r;
+          const float v = acc[i][j][r] + b;
+          if (OUT_F32)
+            reinterpret_cast<float*>(lds)[rl * OROW + cl] = v;
+          else
+            reinterpret_cast<uint16_t*>(lds)[rl * OROW + cl] = f2bf(v);
+        }
+    }
+    __syncthreads();
+    const int64_t ncols = min<int64_t>(BN, a.N - n0);
+    for (int c = tid; c < m_size * (BN / CH); c += NT) {
+      const int rl = c / (BN / CH), ch = c % (BN / CH);
+      const int64_t col = n0 + ch * CH;
+      uint8_t* dst = obase + (sOrow[rl] * a.ldo + col) * OE;
+      const uint8_t* src = lds + (rl * OROW + ch * CH) * OE;
+      if (ch * CH + CH <= ncols) {
+        *reinterpret_cast<uint4*>(dst) = *reinterpret_cast<const uint4*>(src);
+      } else {
+        for (int e = 0; e < CH * OE && ch * CH + e / OE < ncols; ++e) dst[e] = src[e];
+      }
+    }
+  }  // row passes
+}
+
+// Routed tile classes 16 / 32 / 64 / 128 rows in one launch; launch order 128, 64, 32, 16 rows
+// (the longest tiles start first).
+struct RingGroup {
+  GemmArgs a[4];   // per class (16, 32, 64, 128 rows): the stage's arguments with its work list
+  int64_t gb[4];   // per class: work-list capacity
+  int64_t off[5];  // launch order 128, 64, 32, 16 rows: off[0] = 0, off[4] = grid size
+};
+
+template <int MODE, int WFMT, bool OUT_F32, bool HAS_BIAS, bool TILED>
+__global__ __launch_bounds__(kRingThreads) void gemm_w16_ring_kernel(RingGroup g) {
+  extern __shared__ __align__(1024) uint8_t ring_lds[];
+  const int64_t b = blockIdx.x;
+  if (b < g.off[1])
+    ring_tile<128, MODE, WFMT, OUT_F32, HAS_BIAS, TILED>(g.a[3], g.gb[3], b - g.off[0], ring_lds);
+  else if (b < g.off[2])
+    ring_tile<64, MODE, WFMT, OUT_F32, HAS_BIAS, TILED>(g.a[2], g.gb[2], b - g.off[1], ring_lds);
+  else if (b < g.off[3])
+    ring_tile<32, MODE, WFMT, OUT_F32, HAS_BIAS, TILED>(g.a[1], g.gb[1], b - g.off[2], ring_lds);
+  else
+    ring_tile<16, MODE, WFMT, OUT_F32, HAS_BIAS, TILED>(g.a[0], g.gb[0], b - g.off[3], ring_lds);
+}
+
+template <int MODE, int WFMT, bool TL>
+static void launch_ring_t(const RingGroup& g, bool out_f32, hipStream_t st) {
+  size_t lds = 0;
+  const size_t f32[4] = {ring_lds_bytes<128, WFMT, true>(), ring_lds_bytes<64, WFMT, true>(),
+                         ring_lds_bytes<32, WFMT, true>(), ring_lds_bytes<16, WFMT, true>()};
+  const size_t b16[4] = {ring_lds_bytes<128, WFMT, false>(), ring_lds_bytes<64, WFMT, false>(),
+                         ring_lds_bytes<32, WFMT, false>(), ring_lds_bytes<16, WFMT, false>()};
+  for (int i = 0; i < 4; ++i)
+    if (g.off[i + 1] > g.off[i]) lds = std::max(lds, out_f32 ? f32[i] : b16[i]);
+  const dim3 grid(unsigned(g.off[4])), block(kRingThreads);
+  const bool bias = g.a[0].bias != nullptr;
+#define MXQ_RING_GO(OF, HB) \
+  hipLaunchKernelGGL((gemm_w16_ring_kernel<MODE, WFMT, OF, HB, TL>), grid, block, lds, st, g)
+  if (out_f32) { if (bias) MXQ_RING_GO(true, true); else MXQ_RING_GO(true, false); }
+  else { if (bias) MXQ_RING_GO(false, true); else MXQ_RING_GO(false, false); }
+#undef MXQ_RING_GO
+}
+
+template <int MODE, int WFMT>
+static void launch_ring_m(const RingGroup& g, bool out_f32, hipStream_t st) {
+  if (g.a[0].w_tiled)
+    launch_ring_t<MODE, WFMT, true>(g, out_f32, st);
+  else
+    launch_ring_t<MODE, WFMT, false>(g, out_f32, st);
+}
+
+bool w16_ring_shape_ok(const GemmArgs& a, int wfmt) {
+  if (wfmt != W_E4M3_BLOCK && wfmt != W_E2M1_MX) return false;
+  if (a.K <= 0 || a.K % 32 != 0 || a.K > int64_t(kRingMaxSteps) * 128) return false;
+  if ((reinterpret_cast<uintptr_t>(a.A) & 15) != 0 || a.lda % 8 != 0) return false;
+  return wfmt != W_E4M3_BLOCK || a.block_n == 128;
+}
+
+bool w16_ring_supported(const GemmArgs& a, int wfmt) {
+  if (!w16_ring_shape_ok(a, wfmt)) return false;
+  if (a.w_tiled) return a.N % 16 == 0;
+  if ((reinterpret_cast<uintptr_t>(a.W) & 15) != 0 || a.ldw % 16 != 0 || a.w_estride % 16 != 0) return false;
+  // plain e8m0 scales: one aligned dword per row per K step
+  if (wfmt == W_E2M1_MX && (a.K % 128 != 0 || a.ws_s0 % 4 != 0 || a.ws_estride % 4 != 0 ||
+                            (reinterpret_cast<uintptr_t>(a.ws) & 3) != 0))
+    return false;
+  return true;
+}
+
+void launch_gemm_w16_ring(const GemmArgs cls[4], const int64_t grid_blocks[4], int wfmt, int row_mode,
+                          bool out_f32, hipStream_t stream) {
+  RingGroup g{};
+  for (int c = 0; c < 4; ++c) {
+    g.a[c] = cls[c];
+    g.gb[c] = std::max<int64_t>(grid_blocks[c], 0);
+  }
+  for (int i = 0; i < 4; ++i) {  // launch order: 128-, 64-, 32-, 16-row class
+    const int c = 3 - i;
+    g.off[i + 1] = g.off[i] + g.gb[c] * cdiv(cls[c].N, int64_t(128)) * std::max<int64_t>(cls[c].k_split, 1);
+  }
+  if (g.off[4] <= 0) return;
+  const bool mx = wfmt == W_E2M1_MX;
+  if (row_mode == ROWS_GATHER_TOK) {
+    if (mx) launch_ring_m<ROWS_GATHER_TOK, W_E2M1_MX>(g, out_f32, stream);
+    else launch_ring_m<ROWS_GATHER_TOK, W_E4M3_BLOCK>(g, out_f32, stream);
+  } else {
+    if (mx) launch_ring_m<ROWS_COMPACT_IN, W_E2M1_MX>(g, out_f32, stream);
+    else launch_ring_m<ROWS_COMPACT_IN, W_E4M3_BLOCK>(g, out_f32, stream);
+  }
+}
+
+}  // namespace mxq

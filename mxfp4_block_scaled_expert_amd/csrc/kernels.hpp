@@ -61,6 +61,12 @@ struct GemmArgs {
   // (elements), W + z * w_estride, ws + z * ws_estride, bias + z * bias_estride and writes
   // out + z * o_bstride (elements)
   int64_t a_bstride, o_bstride;
+  // K split (routed bf16-activation stages): k_split > 1 runs every tile over K chunks of
+  // k_chunk elements (a multiple of 256), chunk c writing its fp32 partial sums to
+  // out + c * split_stride (the bias rides on chunk 0); 0 or 1: whole K, one output
+  int32_t k_split;
+  int64_t k_chunk;
+  int64_t split_stride;
 };
 
 // MX-scaled dense GEMM (gemm_mx.hip): MXFP8 activations x MXFP8 / MXFP4 weights.
@@ -116,6 +122,15 @@ void launch_gemm_w16_batched(const GemmArgs& a, int tile, int64_t batch, hipStre
 
 void launch_gemm_w16_grouped(const GemmArgs cls[4], const int64_t grid_blocks[4], int wfmt, int row_mode,
                              bool out_f32, hipStream_t stream);
+// The same classes on tiles fed by a ring of LDS stages (direct global-to-LDS copies); usable
+// when w16_ring_supported(stage arguments, wfmt): block-FP8 (128 x 128 blocks) or MXFP4 weights,
+// K % 32 == 0, K <= 16384, 16-byte aligned operand rows (plain MXFP4: K % 128 == 0).
+bool w16_ring_supported(const GemmArgs& a, int wfmt);
+// The part of that test that does not depend on the weight layout (the class policy uses it, so
+// that both layouts run the same classes and give the same bits).
+bool w16_ring_shape_ok(const GemmArgs& a, int wfmt);
+void launch_gemm_w16_ring(const GemmArgs cls[4], const int64_t grid_blocks[4], int wfmt, int row_mode,
+                          bool out_f32, hipStream_t stream);
 
 // Wavefront-reduction GEMV for routed blocks of at most 4 rows.
 // a_e4m3: activations are e4m3 + 1x128 scales (W8A8), else bf16.
@@ -169,9 +184,15 @@ void launch_moe_align(const int32_t* topk_ids, int64_t M, int32_t topk, int32_t 
 void launch_silu_mul(const uint16_t* ic0, int64_t rows, int64_t inter, int64_t ld_in, uint16_t* ic1_bf16,
                      uint8_t* ic1_q, float* ic1_s, hipStream_t stream);
 
-// out[t] = bf16(sum_k w[t,k] * y[t*topk+k]).
-// Rows whose expert id lies outside [0, E) are skipped.
-void launch_combine(const float* y, const float* topk_weights, const int32_t* topk_ids, int32_t E, int64_t M,
-                    int32_t topk, int64_t H, uint16_t* out, hipStream_t stream);
+// Split stage 1: ic0 = bf16(sum over the n_split fp32 partial slices [rows, 2I], slice c at
+// part + c * slice), then ic1 = bf16(silu(gate) * up) as launch_silu_mul.
+void launch_split_silu_mul(const float* part, int32_t n_split, int64_t slice, int64_t rows, int64_t inter,
+                           uint16_t* ic1_bf16, hipStream_t stream);
+
+// out[t] = bf16(sum_k w[t,k] * y[t*topk+k]), y[r] = sum over the n_split slices y + c * slice
+// (n_split 1: y itself).  Rows whose expert id lies outside [0, E) are skipped.
+void launch_combine(const float* y, int32_t n_split, int64_t slice, const float* topk_weights,
+                    const int32_t* topk_ids, int32_t E, int64_t M, int32_t topk, int64_t H, uint16_t* out,
+                    hipStream_t stream);
 
 }  // namespace mxq

@@ -25,6 +25,8 @@
 // token count, which caps an expert's rows when a token's experts are distinct)
 // receive nothing: a block past every launched bound goes to the largest
 // launched class.
+#include <algorithm>
+
 #include "kernels.hpp"
 #include "quant_common.hpp"
 
@@ -312,6 +314,46 @@ __global__ __launch_bounds__(256) void silu_mul_kernel(const uint16_t* __restric
   }
 }
 
+// Split stage 1: the n_split fp32 partial slices of ic0 are summed (slice order), rounded to
+// bf16 (the ic0 value) and passed through the same SiLU-and-mul as silu_mul_kernel.
+__global__ __launch_bounds__(256) void split_silu_mul_kernel(const float* __restrict__ part, int32_t n_split,
+                                                             int64_t slice, int64_t rows, int64_t inter,
+                                                             uint16_t* __restrict__ ic1) {
+  const int64_t per_row = inter / 8;
+  const int64_t idx = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (idx >= rows * per_row) return;
+  const int64_t row = idx / per_row;
+  const int64_t col = (idx - row * per_row) * 8;
+  const float* pg = part + row * 2 * inter + col;
+  float g[8], u[8];
+  {
+    const float4 g0 = *reinterpret_cast<const float4*>(pg), g1 = *reinterpret_cast<const float4*>(pg + 4);
+    const float4 u0 = *reinterpret_cast<const float4*>(pg + inter), u1 = *reinterpret_cast<const float4*>(pg + inter + 4);
+    g[0] = g0.x; g[1] = g0.y; g[2] = g0.z; g[3] = g0.w; g[4] = g1.x; g[5] = g1.y; g[6] = g1.z; g[7] = g1.w;
+    u[0] = u0.x; u[1] = u0.y; u[2] = u0.z; u[3] = u0.w; u[4] = u1.x; u[5] = u1.y; u[6] = u1.z; u[7] = u1.w;
+  }
+  for (int c = 1; c < n_split; ++c) {
+    const float* p = pg + c * slice;
+    const float4 g0 = *reinterpret_cast<const float4*>(p), g1 = *reinterpret_cast<const float4*>(p + 4);
+    const float4 u0 = *reinterpret_cast<const float4*>(p + inter), u1 = *reinterpret_cast<const float4*>(p + inter + 4);
+    g[0] += g0.x; g[1] += g0.y; g[2] += g0.z; g[3] += g0.w; g[4] += g1.x; g[5] += g1.y; g[6] += g1.z; g[7] += g1.w;
+    u[0] += u0.x; u[1] += u0.y; u[2] += u0.z; u[3] += u0.w; u[4] += u1.x; u[5] += u1.y; u[6] += u1.z; u[7] += u1.w;
+  }
+  const uint4 gb = make_uint4(pack_bf16x2(g[0], g[1]), pack_bf16x2(g[2], g[3]), pack_bf16x2(g[4], g[5]),
+                              pack_bf16x2(g[6], g[7]));
+  const uint4 ub = make_uint4(pack_bf16x2(u[0], u[1]), pack_bf16x2(u[2], u[3]), pack_bf16x2(u[4], u[5]),
+                              pack_bf16x2(u[6], u[7]));
+  *reinterpret_cast<uint4*>(ic1 + row * inter + col) = silu_mul8(gb, ub);
+}
+
+void launch_split_silu_mul(const float* part, int32_t n_split, int64_t slice, int64_t rows, int64_t inter,
+                           uint16_t* ic1_bf16, hipStream_t stream) {
+  const int64_t threads = rows * (inter / 8);
+  if (threads == 0) return;
+  hipLaunchKernelGGL(split_silu_mul_kernel, dim3(unsigned(cdiv(threads, 256))), dim3(256), 0, stream, part, n_split,
+                     slice, rows, inter, ic1_bf16);
+}
+
 void launch_silu_mul(const uint16_t* ic0, int64_t rows, int64_t inter, int64_t ld_in, uint16_t* ic1_bf16,
                      uint8_t* ic1_q, float* ic1_s, hipStream_t stream) {
   const int64_t threads = rows * (inter / 8);
@@ -327,9 +369,10 @@ void launch_silu_mul(const uint16_t* ic0, int64_t rows, int64_t inter, int64_t l
 
 // ---------------------------------------------------------------- combine
 
-__global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ y, const float* __restrict__ w,
-                                                      const int32_t* __restrict__ ids, int32_t E, int64_t M,
-                                                      int32_t topk, int64_t H, uint16_t* __restrict__ out) {
+__global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ y, int32_t n_split, int64_t slice,
+                                                      const float* __restrict__ w, const int32_t* __restrict__ ids,
+                                                      int32_t E, int64_t M, int32_t topk, int64_t H,
+                                                      uint16_t* __restrict__ out) {
   constexpr int kBatch = 8;  // routed rows whose loads go out together
   const int64_t per_row = H / 4;
   const int64_t idx = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
@@ -355,6 +398,17 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
     float4 v[kBatch];
 #pragma unroll
     for (int j = 0; j < kBatch; ++j) v[j] = *reinterpret_cast<const float4*>(y + rk[j] * H + col);
+    // K-split partial slices of y, summed in slice order
+    for (int c = 1; c < n_split; ++c) {
+#pragma unroll
+      for (int j = 0; j < kBatch; ++j) {
+        const float4 p = *reinterpret_cast<const float4*>(y + c * slice + rk[j] * H + col);
+        v[j].x += p.x;
+        v[j].y += p.y;
+        v[j].z += p.z;
+        v[j].w += p.w;
+      }
+    }
 #pragma unroll
     for (int j = 0; j < kBatch; ++j) {
       if (!ok[j]) continue;  // past top-k, or an id outside [0, E) (its y row is never written)
@@ -370,12 +424,13 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
   *reinterpret_cast<uint2*>(out + t * H + col) = o;
 }
 
-void launch_combine(const float* y, const float* topk_weights, const int32_t* topk_ids, int32_t E, int64_t M,
-                    int32_t topk, int64_t H, uint16_t* out, hipStream_t stream) {
+void launch_combine(const float* y, int32_t n_split, int64_t slice, const float* topk_weights,
+                    const int32_t* topk_ids, int32_t E, int64_t M, int32_t topk, int64_t H, uint16_t* out,
+                    hipStream_t stream) {
   const int64_t threads = M * (H / 4);
   if (threads == 0) return;
-  hipLaunchKernelGGL(combine_kernel, dim3(unsigned(cdiv(threads, 256))), dim3(256), 0, stream, y, topk_weights,
-                     topk_ids, E, M, topk, H, out);
+  hipLaunchKernelGGL(combine_kernel, dim3(unsigned(cdiv(threads, 256))), dim3(256), 0, stream, y,
+                     std::max<int32_t>(n_split, 1), slice, topk_weights, topk_ids, E, M, topk, H, out);
 }
 
 }  // namespace mxq

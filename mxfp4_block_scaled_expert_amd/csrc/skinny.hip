@@ -91,15 +91,27 @@ __global__ __launch_bounds__(256, (SkinnyShape<WFMT, A_E4M3>::W)) void skinny_ke
   const int l16 = lane & 15, q = lane >> 4;
   const int64_t N = a.N, K = a.K;
   const int64_t ntiles = (N + 64 * G - 1) / (64 * G);
-  // n-tile fastest: concurrently running workgroups stream adjacent rows of one expert
-  const int64_t tile = blockIdx.x / ntiles;
-  const int64_t nt = blockIdx.x - tile * ntiles;
+  // K split fastest (a tile's chunks run side by side), then n-tile: concurrently running
+  // workgroups stream adjacent parts of one expert
+  const int nsplit = a.k_split > 1 ? a.k_split : 1;
+  const int split = int(blockIdx.x % unsigned(nsplit));
+  const int64_t rest = blockIdx.x / unsigned(nsplit);
+  const int64_t tile = rest / ntiles;
+  const int64_t nt = rest - tile * ntiles;
   if (tile >= grid_blocks) return;
   TileInfo t;
   if (!tile_info<1, MODE>(a, tile, t)) return;
 
   const SkinnyLds L = skinny_lds_layout(MX, A_E4M3, K, G, AR);
   const int nsteps = L.kpad / KSTEP;
+  // this workgroup's K steps [st_b, st_e); an empty range (a chunk past K) stores zeros
+  int st_b = 0, st_e = nsteps;
+  if (nsplit > 1) {
+    const int cs = int(a.k_chunk / KSTEP);
+    st_b = min(nsteps, split * cs);
+    st_e = min(nsteps, st_b + cs);
+  }
+  const int st_last = max(st_e, 1) - 1;  // loads past the range re-read its last step
   const int64_t n0 = nt * 64 * G;
   const int64_t row_bytes = MX ? K / 2 : K;
   const bool ragged = !TILED && MX && (row_bytes & 127) != 0;
@@ -140,7 +152,7 @@ __global__ __launch_bounds__(256, (SkinnyShape<WFMT, A_E4M3>::W)) void skinny_ke
 
   // all weight / scale addresses are a wave-uniform base plus a 32-bit lane offset
   auto load = [&](int st, int slot) __attribute__((always_inline)) {
-    const uint32_t sc = uint32_t(min(st, nsteps - 1));
+    const uint32_t sc = uint32_t(min(st, st_last));
     if (TILED) {
       const bool last = MX && int(sc) == nsteps - 1;
       const uint32_t h0 = last ? last_h0 : 0u, h1 = last ? last_h1 : 1024u;
@@ -182,7 +194,7 @@ __global__ __launch_bounds__(256, (SkinnyShape<WFMT, A_E4M3>::W)) void skinny_ke
 
     // request the first steps of the weight stream before staging the activations
 #pragma unroll
-    for (int u = 0; u < D - 1; ++u) load(u, u);
+    for (int u = 0; u < D - 1; ++u) load(st_b + u, u);
 
     if (tid < AR) {
       int64_t ar, orw;
@@ -192,11 +204,12 @@ __global__ __launch_bounds__(256, (SkinnyShape<WFMT, A_E4M3>::W)) void skinny_ke
     }
     __syncthreads();
     {
-      // activation rows (rows >= m_size are never read), zero-padded to whole steps
-      const int chunks = L.kpad * AE / 16;
+      // activation rows (rows >= m_size are never read) over the K steps of this workgroup,
+      // zero-padded to whole steps
+      const int cb = st_b * KSTEP * AE / 16, nc = (st_e - st_b) * KSTEP * AE / 16;
       const int kchunks = int(K * AE / 16);
-      for (int c = tid; c < m_size * chunks; c += 256) {
-        const int m = c / chunks, cc = c - m * chunks;
+      for (int c = tid; c < m_size * nc; c += 256) {
+        const int m = c / nc, cc = cb + (c - m * nc);
         i32x4 v = {0, 0, 0, 0};
         if (cc < kchunks) {
           const uint8_t* src = reinterpret_cast<const uint8_t*>(a.A) + s_arow[m] * a.lda * AE + int64_t(cc) * 16;
@@ -294,21 +307,22 @@ __global__ __launch_bounds__(256, (SkinnyShape<WFMT, A_E4M3>::W)) void skinny_ke
       }
     };
 
-    for (int st0 = 0; st0 < nsteps; st0 += D) {
+    for (int st0 = st_b; st0 < st_e; st0 += D) {
 #pragma unroll
       for (int u = 0; u < D; ++u) {
         load(st0 + u + D - 1, (u + D - 1) % D);
-        if (st0 + u < nsteps) compute(st0 + u, u);
+        if (st0 + u < st_e) compute(st0 + u, u);
       }
     }
 
     // epilogue: lane (l16, q) holds D[4q + r][l16] of each group
     if (4 * q < m_size) {
+      float* const outf = reinterpret_cast<float*>(a.out) + (nsplit > 1 ? split * a.split_stride : 0);
 #pragma unroll
       for (int g = 0; g < G; ++g) {
         const int64_t col = n0 + (g * kSkWaves + wave) * 16 + l16;
         if (col >= N) continue;
-        const float b = HAS_BIAS ? load_bias(a, t.expert, col) : 0.f;
+        const float b = HAS_BIAS && split == 0 ? load_bias(a, t.expert, col) : 0.f;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int m = 4 * q + r;
@@ -316,7 +330,7 @@ __global__ __launch_bounds__(256, (SkinnyShape<WFMT, A_E4M3>::W)) void skinny_ke
           const int64_t o = s_orow[m] * a.ldo + col;
           const float v = acc[g][r] + b;
           if (OUT_F32)
-            reinterpret_cast<float*>(a.out)[o] = v;
+            outf[o] = v;
           else
             reinterpret_cast<uint16_t*>(a.out)[o] = f2bf(v);
         }
@@ -355,7 +369,8 @@ size_t skinny_lds_bytes(int wfmt, bool a_e4m3, int64_t K) {
 template <int WFMT, bool AE, int MODE, bool TL, int AR, int G, int D>
 static void launch_skinny_ar(const GemmArgs& a, bool out_f32, int64_t gb, hipStream_t st) {
   const int64_t n_tiles = cdiv(a.N, int64_t(64 * G));
-  const dim3 grid(static_cast<unsigned>(gb * n_tiles)), block(256);
+  const int64_t nsplit = a.k_split > 1 ? a.k_split : 1;
+  const dim3 grid(static_cast<unsigned>(gb * n_tiles * nsplit)), block(256);
   const size_t lds = skinny_lds_t<WFMT, AE>(a.K, AR, G);
   const bool bias = a.bias != nullptr;
 #define MXQ_SK_GO(OF, HB) \

@@ -43,7 +43,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_status_strings_and_version():
     L, lib = _lib()
-    assert lib.mxq_abi_version() == 7
+    assert lib.mxq_abi_version() == 8
     for code in range(0, 10):
         assert lib.mxq_status_string(code)
     assert b"unknown" in lib.mxq_status_string(99)
@@ -116,13 +116,14 @@ def test_argument_errors_before_any_launch():
     assert mx4(null, 4, 256, 128, 8, 2, null, null, null, null, null, null, null, 5, null, null, null, 0,
                null) == L.MXQ_ERR_ARG
     # per-call dispatch: every field validated before any pointer is looked at
-    for bad in ((7, 0, 4, 0), (0, 0, 17, 0), (0, 0, -2, 0), (0, 0, 4, 5), (1, 5, 16, 0), (1, -1, 16, 0)):
+    for bad in ((7, 0, 4, 0, 0), (0, 0, 17, 0, 0), (0, 0, -2, 0, 0), (0, 0, 4, 5, 0), (1, 5, 16, 0, 0),
+                (1, -1, 16, 0, 0), (0, 0, 4, 0, 3), (0, 0, 4, 0, -1), (0, 0, 4, 0, 16)):
         d = C.byref(L.MoeDispatch(*bad))
         assert fp8(null, 4, 256, 128, 8, 2, null, null, null, null, null, null, null, 0, 0, d, null, null, 0,
                    null) == L.MXQ_ERR_ARG, bad
         assert mx4(null, 4, 256, 128, 8, 2, null, null, null, null, null, null, null, 0, d, null, null, 0,
                    null) == L.MXQ_ERR_ARG, bad
-    for good in ((0, 0, 16, 0), (1, 4, 4, 1), (2, 0, 0, 0), (0, 0, -1, 0)):
+    for good in ((0, 0, 16, 0, 0), (1, 4, 4, 1, 1), (2, 0, 0, 0, 2), (0, 0, -1, 0, 4), (0, 0, 8, 0, 8)):
         d = C.byref(L.MoeDispatch(*good))
         assert fp8(null, 4, 256, 128, 8, 2, null, null, null, null, null, null, null, 0, 0, d, null, null, 0,
                    null) == L.MXQ_ERR_NULL, good
@@ -159,18 +160,20 @@ def test_moe_workspace_layout_query():
         mb = lib.mxq_moe_max_blocks(M, topk, E, bm)
         size = {"sorted_ids": 4 * mb * bm, "expert_ids": 4 * mb, "offsets": 4 * (mb + 1), "num_blocks": 4,
                 "qx": M * H, "sx": 4 * M * (H // 128), "ic0": 2 * R * 2 * I, "ic1": 2 * R * I,
-                "ic1_q": R * I, "ic1_s": 4 * R * (I // 128), "y": 4 * R * H}
+                "ic1_q": R * I, "ic1_s": 4 * R * (I // 128), "y": 4 * R * H,
+                "partial": 4 * 8 * R * max(2 * I, H)}  # K-split slices: 8 for R = 128
         used = {k: v for k, v in lay.items() if k != "block_m" and v >= 0}
         if aq:
             assert lay["ic1"] == -1 and min(lay["qx"], lay["sx"], lay["ic1_q"], lay["ic1_s"]) >= 0
         else:
             assert lay["qx"] == lay["sx"] == lay["ic1_q"] == lay["ic1_s"] == -1 and lay["ic1"] >= 0
+        assert (lay["partial"] >= 0) == (not aq and R <= 1024)
         spans = sorted((v, v + size[k], k) for k, v in used.items())
         for (a0, a1, ka), (b0, b1, kb) in zip(spans, spans[1:]):
             assert a1 <= b0, (ka, kb)
         assert spans[-1][1] <= total
         assert all(v % 256 == 0 for v in used.values())
-    arr = (C.c_int64 * 12)()
+    arr = (C.c_int64 * 13)()
     assert lib.mxq_fused_moe_workspace_layout(0, 7168, 2048, 256, 8, 0, 1, arr) == L.MXQ_ERR_SHAPE
     assert lib.mxq_fused_moe_workspace_layout(4, 256, 128, 8, 2, 0, 1, None) == L.MXQ_ERR_NULL
 

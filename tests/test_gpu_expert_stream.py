@@ -44,10 +44,11 @@ def _run(inp, layout, dispatch=None):
 
 
 def _stream_vs_tiny_class(inp, layout, what):
-    """Default dispatch (streaming path) and forced tiny class: bit-identical outputs."""
+    """Default dispatch (streaming path) and forced tiny class without a K split: bit-identical
+    outputs."""
     src = _tiled(inp) if layout == "tiled" else inp
     got = _run(src, layout)
-    ref = _run(src, layout, ops.Dispatch(mx.MXQ_DISPATCH_FORCED, 0))
+    ref = _run(src, layout, ops.Dispatch(mx.MXQ_DISPATCH_FORCED, 0, k_split=1))
     torch.cuda.synchronize()
     assert torch.equal(got.view(torch.int16), ref.view(torch.int16)), what
     return got

@@ -201,15 +201,64 @@ def test_zero_tokens():
 @pytest.mark.parametrize("kind", ["w8a16", "mxfp4"])
 def test_small_batch_fused_silu_matches_unfused_and_oracle(kind):
     """M <= 32: every block takes the tiny-block kernel and stage 2 computes the SiLU-and-mul while
-    staging its rows.  Forcing the tiny class keeps the same kernels with the standalone
-    SiLU-and-mul pass, so the two must agree bit for bit; both must match the oracle."""
+    staging its rows.  Forcing the tiny class (without a K split) keeps the same kernels with the
+    standalone SiLU-and-mul pass, so the two must agree bit for bit; both must match the oracle."""
     if kind == "w8a16":
         spec = _small_spec("fused_moe_fp8", 24, 8, 2, 512, 256)
     else:
         spec = _small_spec("fused_moe_mxfp4", 16, 8, 4, 2880, 2880)
     inp = synth.moe_inputs(spec, seed=41, device=gpu())
     fused = _run_gpu(inp)
-    plain = _run_gpu(inp, ops.Dispatch(mx.MXQ_DISPATCH_FORCED, 0))
+    plain = _run_gpu(inp, ops.Dispatch(mx.MXQ_DISPATCH_FORCED, 0, k_split=1))
     torch.cuda.synchronize()
     assert torch.equal(fused.view(torch.int16), plain.view(torch.int16))
     assert_bf16_close(bf16_bits(fused), _run_oracle(inp), what=f"{kind} fused SiLU")
+
+
+# ------------------------------------------------------------------ K split (bf16 activations)
+
+@pytest.mark.parametrize("k_split", [1, 2, 8])
+@pytest.mark.parametrize("forced", [None, 0, 1, 2, 3, 4])
+def test_k_split_small_blocks_every_class(forced, k_split):
+    """The small-block W8A16 routing with each tile's K cut into 2 or 8 chunks (fp32 partial
+    slices summed after each stage), per block and with every class forced."""
+    inp = synth.moe_inputs(SMALL_BLOCKS, seed=1003, device=gpu())
+    want = _run_oracle(inp)
+    mode = mx.MXQ_DISPATCH_PER_BLOCK if forced is None else mx.MXQ_DISPATCH_FORCED
+    out = _run_gpu(inp, ops.Dispatch(mode, forced or 0, k_split=k_split))
+    torch.cuda.synchronize()
+    assert_bf16_close(bf16_bits(out), want, what=f"forced={forced} k_split={k_split}")
+
+
+@pytest.mark.parametrize("k_split", [2, 4, 8])
+@pytest.mark.parametrize("forced", [0, 1, 4])
+def test_k_split_mxfp4_ragged_chunks(forced, k_split):
+    """MXFP4, K = 2880 in both stages: chunks of 1536 / 768 / 512 columns, the last one ragged
+    (a partial 128-wide tile step, a partial 256-wide tiny-kernel step)."""
+    spec = _small_spec("fused_moe_mxfp4", 40, 8, 4, 2880, 2880)
+    inp = synth.moe_inputs(spec, seed=13, device=gpu())
+    want = _run_oracle(inp)
+    out = _run_gpu(inp, ops.Dispatch(mx.MXQ_DISPATCH_FORCED, forced, 4, k_split=k_split))
+    torch.cuda.synchronize()
+    assert_bf16_close(bf16_bits(out), want, what=f"mxfp4 forced={forced} k_split={k_split}")
+
+
+@pytest.mark.parametrize("k_split", [2, 8])
+def test_k_split_bias_topk_and_dropped_ids(k_split):
+    """The stage-1 bias is added once (by the first chunk); rows with expert ids outside [0, E)
+    are dropped as without a split."""
+    spec = _small_spec("fused_moe_fp8", 77, 12, 3, 384, 256, zipf=0.8)
+    inp = synth.moe_inputs(spec, seed=12, device=gpu())
+    g = torch.Generator(device="cuda").manual_seed(3)
+    inp["w1_bias"] = torch.randn(12, 512, generator=g, device=gpu())
+    inp["topk_ids"][5, 1] = -1
+    inp["topk_ids"][9, 0] = 12
+    out = _run_gpu(inp, ops.Dispatch(k_split=k_split))
+    torch.cuda.synchronize()
+    ids = inp["topk_ids"].cpu().numpy()
+    keep = ids.copy()
+    keep[(ids < 0) | (ids >= 12)] = 0
+    w = inp["topk_weights"].clone()
+    w[torch.from_numpy((ids < 0) | (ids >= 12)).to(gpu())] = 0.0
+    ref_inp = dict(inp, topk_ids=torch.from_numpy(keep).to(gpu()), topk_weights=w)
+    assert_bf16_close(bf16_bits(out), _run_oracle(ref_inp), what=f"bias/dropped k_split={k_split}")
