@@ -520,7 +520,19 @@ mxq_status run_moe(const void* x, int64_t M, int64_t H, int64_t I, int32_t E, in
 }
 
 int dense_tile_for(int64_t M) { return M <= 16 ? 3 : M <= 32 ? 2 : M <= 64 ? 1 : 0; }
+
 int64_t tile_rows(int tile) { return tile == 0 ? 128 : tile == 1 ? 64 : tile == 2 ? 32 : 16; }
+
+// Dense bf16-activation tiles: the smallest tile that holds M rows, then smaller row tiles
+// while the grid (row tiles x 128-column tiles x batch) stays under one workgroup per compute
+// unit -- a small product is bound by the latency of its K steps, which shorter row tiles
+// take in less time, and more workgroups overlap (per-tensor 97 x 576 x 224: 15.0 -> 8.7 us;
+// 128 heads of [64, 512] x [128, 512]^T: 11.4 -> 9.8 us).
+int dense_w16_tile(int64_t M, int64_t N, int64_t batch) {
+  int tile = dense_tile_for(M);
+  while (tile < 3 && cdiv(M, tile_rows(tile)) * cdiv(N, int64_t(128)) * batch < 256) ++tile;
+  return tile;
+}
 
 }  // namespace
 
@@ -588,7 +600,7 @@ mxq_status mxq_fp8_scaled_mm(const void* A, int64_t M, int64_t K, int64_t lda, c
   g.M = M;
   g.N = N;
   g.K = K;
-  const int tile = dense_tile_for(M);
+  const int tile = dense_w16_tile(M, N, 1);
   launch_gemm_w16(g, W_E4M3_TENSOR, ROWS_DENSE, tile, false, cdiv(M, tile_rows(tile)),
                   static_cast<hipStream_t>(stream));
   return launch_status();
@@ -628,7 +640,7 @@ mxq_status mxq_fp8_scaled_bmm(const void* A, int64_t batch, int64_t M, int64_t K
   g.M = M;
   g.N = N;
   g.K = K;
-  launch_gemm_w16_batched(g, dense_tile_for(M), batch, static_cast<hipStream_t>(stream));
+  launch_gemm_w16_batched(g, dense_w16_tile(M, N, batch), batch, static_cast<hipStream_t>(stream));
   return launch_status();
 }
 

@@ -15,8 +15,9 @@
 // multiplied.  Every wave issues the same number of copies per step, so one vmcnt wait per step
 // followed by one barrier publishes the step.  Eight waves (two per SIMD) let one wave's LDS
 // reads overlap the other's products.  (Measured and dropped: issuing the first steps' weight
-// copies before the row table is read, and skipping the copies of activation rows past the
-// block's row count with per-wave vmcnt targets -- both 2-5 % slower.)
+// copies before the row table is read; skipping the copies of activation rows past the block's
+// row count, with per-wave vmcnt targets or as one-lane copies -- 1-5 % slower, the copies of
+// the repeated last row hit in cache.)
 //
 // LDS layouts (per stage):
 //  * activations: row-major 256-byte rows; the 16-byte chunk c of row r sits in slot c ^ (r % 16)
@@ -35,6 +36,7 @@
 
 #include "lds_dma.hpp"
 #include "tile_rows.hpp"
+
 
 namespace mxq {
 
@@ -114,7 +116,10 @@ __device__ __forceinline__ void ring_tile(const GemmArgs& a, int64_t grid_blocks
     for (int i = tid; i < nsteps; i += NT) sSw[i] = swb[int64_t(ks_b + i) * a.ws_s1];
   }
 
-  // ---- weight copy sources (row-independent): wave w copies the 16-row group w of the tile
+  // ---- copies: wave w copies weight group w of the tile (16 rows) and the activation copies k
+  // holding rows 4 (w + 8 k) .. +3 (BM = 16: rows 2 w, 2 w + 1 on lanes 0..31).  (Measured and
+  // dropped: the upper wave of each SIMD issuing the lower wave's share too, so that the lower
+  // one starts its products at once -- no gain.)
   const uint8_t* Wb = a.W + expert * a.w_estride;
   const int64_t row_bytes = MX ? a.K / 2 : a.K;
   const int64_t tsteps = (row_bytes + 127) / 128;  // tiled layout: 128-byte row steps per group
@@ -172,8 +177,7 @@ __device__ __forceinline__ void ring_tile(const GemmArgs& a, int64_t grid_blocks
     fill_rows<BM, MODE>(a, t, m_base, sArow, sOrow);
     __syncthreads();
 
-    // ---- activation copy sources: copy k of wave w holds rows 4 (w + 8 k) .. +3 (BM = 16:
-    // rows 2 w, 2 w + 1 on lanes 0..31); the lane's source chunk is its slot XOR the row's swizzle
+    // activation copy sources; the lane's source chunk is its slot XOR the row's swizzle
     const uint8_t* ga[A_INS];
     int gac[A_INS];
 #pragma unroll
@@ -183,7 +187,6 @@ __device__ __forceinline__ void ring_tile(const GemmArgs& a, int64_t grid_blocks
       gac[k] = c;
       ga[k] = reinterpret_cast<const uint8_t*>(a.A) + sArow[row] * a.lda * 2 + c * 16;
     }
-
     auto issue_a = [&](int ks, int stage) __attribute__((always_inline)) {
       const uint32_t sb = lbase + uint32_t(stage * STAGE);
       const int64_t kbase = int64_t(ks) * 128;
