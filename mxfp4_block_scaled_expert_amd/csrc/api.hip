@@ -174,6 +174,7 @@ KSplit pick_split(int64_t R, int32_t E, int64_t N, int64_t K, int requested) {
 struct MoeWorkspace {
   int32_t *sorted_ids, *expert_ids, *offsets, *num_blocks, *class_lists, *class_counts;
   float* partial;  // K-split partial slices (bf16 activations, R <= kSplitMaxRows)
+  int32_t* align_scratch;  // per-chunk counts of the multi-workgroup sort (many routed rows)
   uint8_t* qx;
   float* sx;
   uint16_t* ic0;
@@ -214,6 +215,8 @@ MoeWorkspace carve_moe(void* base, int64_t M, int64_t H, int64_t I, int32_t E, i
   w.y = reinterpret_cast<float*>(take(sizeof(float) * R * H));
   if (!act_quant && split_cap(R) > 1)
     w.partial = reinterpret_cast<float*>(take(sizeof(float) * split_cap(R) * R * std::max(2 * I, H)));
+  if (align_multi_scratch_ints(R, E) > 0)
+    w.align_scratch = reinterpret_cast<int32_t*>(take(sizeof(int32_t) * align_multi_scratch_ints(R, E)));
   w.bytes = off;
   return w;
 }
@@ -428,7 +431,7 @@ mxq_status run_moe(const void* x, int64_t M, int64_t H, int64_t I, int32_t E, in
   }
 
   launch_moe_align(ids, M, topk, E, kMoeBlockM, w.sorted_ids, w.expert_ids, w.offsets, w.num_blocks, mbk, pol,
-                   w.class_lists, mbk, w.class_counts, false, st);
+                   w.class_lists, mbk, w.class_counts, false, w.align_scratch, st);
   if (act_quant) launch_quant_1x128(static_cast<const uint16_t*>(x), M, H, H, w.qx, H, w.sx, st);
 
 
@@ -823,7 +826,7 @@ mxq_status mxq_moe_align(const int32_t* topk_ids, int64_t M, int32_t topk, int32
   pol.n_classes = 0;
   pol.forced = -1;
   launch_moe_align(topk_ids, M, topk, E, block_m, sorted_ids, expert_ids, offsets, num_blocks,
-                   mxq_moe_max_blocks(M, topk, E, block_m), pol, nullptr, 0, nullptr, true,
+                   mxq_moe_max_blocks(M, topk, E, block_m), pol, nullptr, 0, nullptr, true, nullptr,
                    static_cast<hipStream_t>(stream));
   return launch_status();
 }

@@ -174,10 +174,15 @@ struct ClassPolicy {
   int32_t forced;         // >= 0: every non-empty block goes to this class
   int32_t n_live;         // classes >= n_live are not launched; their blocks go to class n_live - 1
 };
+// `scratch` (NULL, or align_multi_scratch_ints(R, E) ints): with more than kAlignMultiMinRows
+// routed rows and no pad slots to write, the sort runs over many workgroups (a histogram pass,
+// the tables in one workgroup, a scatter pass) and keeps its per-chunk counts there.
+constexpr int64_t kAlignMultiMinRows = 4096;
+int64_t align_multi_scratch_ints(int64_t R, int32_t E);
 void launch_moe_align(const int32_t* topk_ids, int64_t M, int32_t topk, int32_t E, int32_t block_m,
                       int32_t* sorted_ids, int32_t* expert_ids, int32_t* offsets, int32_t* num_blocks,
                       int64_t max_blocks, const ClassPolicy& pol, int32_t* class_lists, int64_t list_stride,
-                      int32_t* class_counts, bool write_pads, hipStream_t stream);
+                      int32_t* class_counts, bool write_pads, int32_t* scratch, hipStream_t stream);
 
 // ic1 = bf16(silu(gate) * up) over compact rows; optionally re-quantised 1x128 to e4m3.
 // ic0 rows are `ld_in` elements apart; ic1 / q / s are contiguous.

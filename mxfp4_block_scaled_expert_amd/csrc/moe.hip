@@ -35,19 +35,44 @@ namespace mxq {
 
 __device__ __forceinline__ int pick_class(const ClassPolicy& pol, int m_size) {
   if (pol.forced >= 0) return pol.forced;
-  for (int c = 0; c < pol.n_live - 1; ++c)
-    if (m_size <= pol.bound[c]) return c;
-  return pol.n_live - 1;  // the tile kernels loop over row sub-tiles, so any block fits
+  // the smallest launched class whose bound holds the block; the largest launched class takes
+  // every block past the bounds (the tile kernels loop over row sub-tiles, so any block fits).
+  // Unrolled over the eight slots so that every bound is read at a constant offset (a loop
+  // indexing the argument struct at run time reads it from memory on every step).
+  int c = pol.n_live - 1;
+#pragma unroll
+  for (int k = 7; k >= 0; --k)
+    if (k < pol.n_live - 1 && m_size <= pol.bound[k]) c = k;
+  return c;
 }
 
+// Lanes of the wave holding the same valid expert id as this lane (ballots over the id's bits).
+__device__ __forceinline__ uint64_t same_expert(int e, bool valid, int nbits) {
+  uint64_t mask = __ballot(valid);
+  for (int bit = 0; bit < nbits; ++bit) {
+    const bool set = valid && ((e >> bit) & 1);
+    const uint64_t bm = __ballot(set);
+    mask &= set ? bm : ~bm;
+  }
+  return mask;
+}
+
+// Routed rows per workgroup of the multi-workgroup sort (the histogram and scatter kernels).
+constexpr int kAlignChunk = 256;
+
 // One workgroup of T threads (1024 for large routings; 256 when the routing is small, where
-// the kernel is a chain of barriers and fewer waves make each one cheaper).
-template <int T>
+// the kernel is a chain of barriers and fewer waves make each one cheaper).  MULTI: the middle
+// of the multi-workgroup sort -- the per-expert counts come from the per-chunk histograms
+// `hist` [G][E] (each chunk's first position within every expert goes to `base` [G][E]), the
+// block tables and class lists are built as in the one-workgroup sort, the block starts go to
+// `blk_out` [E + 1], and the scatter is left to align_scatter_kernel.
+template <int T, bool MULTI>
 __global__ __launch_bounds__(T) void moe_align_kernel(
     const int32_t* __restrict__ ids, int64_t R, int32_t E, int32_t block_m, int32_t* __restrict__ sorted_ids,
     int32_t* __restrict__ expert_ids, int32_t* __restrict__ offsets, int32_t* __restrict__ num_blocks,
     int64_t max_blocks, ClassPolicy pol, int32_t* __restrict__ class_lists, int64_t list_stride,
-    int32_t* __restrict__ class_counts, int write_pads, int cache_ids) {
+    int32_t* __restrict__ class_counts, int write_pads, int cache_ids, const int32_t* __restrict__ hist,
+    int32_t G, int32_t* __restrict__ base, int32_t* __restrict__ blk_out) {
   constexpr int kAlignThreads = T;
   constexpr int kAlignWaves = T / 64;
   extern __shared__ int32_t smem[];
@@ -69,17 +94,27 @@ __global__ __launch_bounds__(T) void moe_align_kernel(
   int nbits = 1;
   while ((1 << nbits) < E) ++nbits;
   const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  // lanes holding the same valid expert id as this lane (ballots over the id's bits)
-  auto same_expert = [&](int e, bool valid) __attribute__((always_inline)) {
-    uint64_t mask = __ballot(valid);
-    for (int bit = 0; bit < nbits; ++bit) {
-      const bool set = valid && ((e >> bit) & 1);
-      const uint64_t bm = __ballot(set);
-      mask &= set ? bm : ~bm;
-    }
-    return mask;
-  };
 
+  if (MULTI) {
+    // 1'. per expert: total rows, and each chunk's first position among them
+    for (int e = tid; e < E; e += kAlignThreads) {
+      // the chunk counts are read 32 at a time (one memory round trip per batch)
+      constexpr int kBatch = 32;
+      int acc = 0;
+      for (int g0 = 0; g0 < G; g0 += kBatch) {
+        int h[kBatch];
+#pragma unroll
+        for (int j = 0; j < kBatch; ++j) h[j] = g0 + j < G ? hist[int64_t(g0 + j) * E + e] : 0;
+#pragma unroll
+        for (int j = 0; j < kBatch; ++j) {
+          if (g0 + j < G) base[int64_t(g0 + j) * E + e] = acc;
+          acc += h[j];
+        }
+      }
+      cnt[e] = acc;
+    }
+    __syncthreads();
+  } else {
   // 1. per-wave histogram of the chunk (expert ids outside [0, E) are ignored); the ids are read
   // 8 steps at a time and, when they fit, kept in LDS for the second walk
   constexpr int kIdBatch = 8;
@@ -94,7 +129,7 @@ __global__ __launch_bounds__(T) void moe_align_kernel(
       const int e = r < r_hi ? eb[j] : -1;
       if (cache_ids && r < r_hi) s_ids[r] = e;
       const bool valid = e >= 0 && e < E;
-      const uint64_t mask = same_expert(e, valid);
+      const uint64_t mask = same_expert(e, valid, nbits);
       if (valid && __popcll(mask & lt) == 0) my_cnt[e] += __popcll(mask);
     }
   }
@@ -110,6 +145,7 @@ __global__ __launch_bounds__(T) void moe_align_kernel(
     cnt[e] = acc;
   }
   __syncthreads();
+  }  // MULTI
 
   // 2. exclusive scans of blocks and rows per expert (each thread owns a run of experts)
   const int per = int(cdiv(E, kAlignThreads));
@@ -239,6 +275,10 @@ __global__ __launch_bounds__(T) void moe_align_kernel(
   }
   __syncthreads();
   if (pol.n_classes > 0 && tid < pol.n_classes) class_counts[tid] = cls_cnt[tid];
+  if (MULTI) {
+    for (int e = tid; e <= E; e += kAlignThreads) blk_out[e] = blk_start[e];
+    return;
+  }
 
   // 4. stable scatter: each wave walks its chunk again; a row's position within its expert is
   // the wave's base for that expert plus its rank among the wave's earlier rows of the expert
@@ -246,7 +286,7 @@ __global__ __launch_bounds__(T) void moe_align_kernel(
     const int64_t r = r0 + lane;
     const int e = r < r_hi ? (cache_ids ? s_ids[r] : ids[r]) : -1;
     const bool valid = e >= 0 && e < E;
-    const uint64_t mask = same_expert(e, valid);
+    const uint64_t mask = same_expert(e, valid, nbits);
     const int rank = __popcll(mask & lt);
     int pos = 0;
     if (valid) pos = my_cnt[e] + rank;
@@ -258,10 +298,62 @@ __global__ __launch_bounds__(T) void moe_align_kernel(
   }
 }
 
+// Multi-workgroup sort, first pass: workgroup g counts the rows of chunk g per expert.
+__global__ __launch_bounds__(256) void align_hist_kernel(const int32_t* __restrict__ ids, int64_t R, int32_t E,
+                                                         int32_t* __restrict__ hist) {
+  extern __shared__ int32_t cnt[];  // [E]
+  const int64_t g = blockIdx.x;
+  for (int e = threadIdx.x; e < E; e += 256) cnt[e] = 0;
+  __syncthreads();
+  const int64_t r = g * kAlignChunk + threadIdx.x;
+  if (r < R) {
+    const int e = ids[r];
+    if (e >= 0 && e < E) atomicAdd(&cnt[e], 1);
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < E; e += 256) hist[g * E + e] = cnt[e];
+}
+
+// Multi-workgroup sort, last pass: workgroup g places the rows of chunk g.  A row's position
+// within its expert is the chunk's base, plus the rows of that expert in the chunk's earlier
+// waves, plus its rank among the wave's earlier rows of the expert (ballots): the same stable
+// order as the one-workgroup sort.
+__global__ __launch_bounds__(256) void align_scatter_kernel(const int32_t* __restrict__ ids, int64_t R, int32_t E,
+                                                            int32_t block_m, const int32_t* __restrict__ base,
+                                                            const int32_t* __restrict__ blk_start,
+                                                            int32_t* __restrict__ sorted_ids) {
+  extern __shared__ int32_t wcnt[];  // [4][E]: rows per expert of each wave, then their prefix
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t g = blockIdx.x;
+  for (int i = tid; i < 4 * E; i += 256) wcnt[i] = 0;
+  int nbits = 1;
+  while ((1 << nbits) < E) ++nbits;
+  const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  const int64_t r = g * kAlignChunk + tid;
+  const int e = r < R ? ids[r] : -1;
+  const bool valid = e >= 0 && e < E;
+  const uint64_t mask = same_expert(e, valid, nbits);
+  const int rank = __popcll(mask & lt);
+  __syncthreads();
+  if (valid && rank == 0) wcnt[wave * E + e] = __popcll(mask);
+  __syncthreads();
+  if (valid) {
+    int pos = base[g * E + e] + rank;
+    for (int w = 0; w < wave; ++w) pos += wcnt[w * E + e];
+    const int b = pos / block_m, slot = pos - b * block_m;
+    sorted_ids[int64_t(blk_start[e] + b) * block_m + slot] = int32_t(r);
+  }
+}
+
+int64_t align_multi_scratch_ints(int64_t R, int32_t E) {
+  if (R <= kAlignMultiMinRows) return 0;
+  return 2 * cdiv(R, int64_t(kAlignChunk)) * E + E + 1;
+}
+
 void launch_moe_align(const int32_t* topk_ids, int64_t M, int32_t topk, int32_t E, int32_t block_m,
                       int32_t* sorted_ids, int32_t* expert_ids, int32_t* offsets, int32_t* num_blocks,
                       int64_t max_blocks, const ClassPolicy& pol, int32_t* class_lists, int64_t list_stride,
-                      int32_t* class_counts, bool write_pads, hipStream_t stream) {
+                      int32_t* class_counts, bool write_pads, int32_t* scratch, hipStream_t stream) {
   // cnt[E] + blk_start[E+1] + row_start[E+1] + wave_cnt[waves][E] (+ ids[R])
   const int64_t R = M * topk;
   const bool small = R <= 2048;  // one 64-row step per wave or a few
@@ -270,14 +362,32 @@ void launch_moe_align(const int32_t* topk_ids, int64_t M, int32_t topk, int32_t 
   // keep the ids in LDS for the scatter when they fit beside the tables (gfx950: 160 KB)
   const bool cache = smem + sizeof(int32_t) * size_t(R) <= size_t(152) * 1024;
   if (cache) smem += sizeof(int32_t) * size_t(R);
+  if (scratch && !write_pads && R > kAlignMultiMinRows) {
+    // many rows: count and place them over many workgroups (one workgroup walking every row
+    // is bound by its own instruction issue); the tables in between stay in one workgroup
+    const int32_t G = int32_t(cdiv(R, int64_t(kAlignChunk)));
+    int32_t* hist = scratch;
+    int32_t* base = hist + int64_t(G) * E;
+    int32_t* blk = base + int64_t(G) * E;
+    hipLaunchKernelGGL(align_hist_kernel, dim3(G), dim3(256), sizeof(int32_t) * E, stream, topk_ids, R, E, hist);
+    // 256 threads: the tables are a chain of scans and barriers over E experts, which more
+    // waves only make longer
+    const size_t tsmem = sizeof(int32_t) * (size_t(E) * 3 + 2 + size_t(4) * E);
+    hipLaunchKernelGGL((moe_align_kernel<256, true>), dim3(1), dim3(256), tsmem, stream, topk_ids, R, E, block_m,
+                       sorted_ids, expert_ids, offsets, num_blocks, max_blocks, pol, class_lists, list_stride,
+                       class_counts, 0, 0, hist, G, base, blk);
+    hipLaunchKernelGGL(align_scatter_kernel, dim3(G), dim3(256), sizeof(int32_t) * 4 * E, stream, topk_ids, R, E,
+                       block_m, base, blk, sorted_ids);
+    return;
+  }
   if (small)
-    hipLaunchKernelGGL(moe_align_kernel<256>, dim3(1), dim3(256), smem, stream, topk_ids, R, E, block_m,
+    hipLaunchKernelGGL((moe_align_kernel<256, false>), dim3(1), dim3(256), smem, stream, topk_ids, R, E, block_m,
                        sorted_ids, expert_ids, offsets, num_blocks, max_blocks, pol, class_lists, list_stride,
-                       class_counts, write_pads ? 1 : 0, cache ? 1 : 0);
+                       class_counts, write_pads ? 1 : 0, cache ? 1 : 0, nullptr, 0, nullptr, nullptr);
   else
-    hipLaunchKernelGGL(moe_align_kernel<1024>, dim3(1), dim3(1024), smem, stream, topk_ids, R, E, block_m,
+    hipLaunchKernelGGL((moe_align_kernel<1024, false>), dim3(1), dim3(1024), smem, stream, topk_ids, R, E, block_m,
                        sorted_ids, expert_ids, offsets, num_blocks, max_blocks, pol, class_lists, list_stride,
-                       class_counts, write_pads ? 1 : 0, cache ? 1 : 0);
+                       class_counts, write_pads ? 1 : 0, cache ? 1 : 0, nullptr, 0, nullptr, nullptr);
 }
 
 // ---------------------------------------------------------------- SiLU-and-mul

@@ -247,6 +247,44 @@ def test_deepseek_prefill_stage_by_stage_sampled():
     assert torch.equal(out.view(torch.int16), out2.view(torch.int16))
 
 
+@pytest.mark.parametrize("M,E,topk", [(1100, 40, 4), (1025, 9, 8), (4096, 512, 2)])
+def test_many_rows_multi_workgroup_sort(M, E, topk):
+    """More than 4096 routed rows: the sort runs as a histogram pass, the tables in one workgroup
+    and a scatter pass.  Its tables (a ragged last chunk, few and many experts) equal the
+    oracle's bit for bit."""
+    H, I = 256, 128
+    inp = synth.moe_inputs(_spec(M, E, topk, H, I), seed=M + E, device=gpu())
+    ws = ops.fused_moe_workspace(M, H, I, E, topk, L.MXQ_WEIGHTS_FP8_BLOCK, True, gpu())
+    _run_fp8(inp, ws, "plain")
+    st = Stages(ws, M, H, I, E, topk)
+    _check_tables(st, inp["topk_ids"].cpu().numpy(), E)
+
+
+def test_many_rows_sort_drops_ids_outside_the_expert_range():
+    """Ids -1 and E drop their rows in the multi-workgroup sort as in the one-workgroup sort of
+    mxq_moe_align (the oracle rejects such ids; the one-workgroup sort is pinned to it on valid
+    routings): same block tables, same real slots."""
+    M, E, topk, H, I = 1100, 40, 4, 256, 128
+    inp = synth.moe_inputs(_spec(M, E, topk, H, I), seed=77, device=gpu())
+    ids = inp["topk_ids"].clone()
+    ids[3, 0] = -1
+    ids[M - 1, topk - 1] = E
+    ids[600, 2] = 1 << 20
+    inp["topk_ids"] = ids
+    ws = ops.fused_moe_workspace(M, H, I, E, topk, L.MXQ_WEIGHTS_FP8_BLOCK, True, gpu())
+    _run_fp8(inp, ws, "plain")
+    st = Stages(ws, M, H, I, E, topk)
+    s, e, o, nb = ops.moe_align(ids, E, st.bm)
+    torch.cuda.synchronize()
+    nb = int(nb.item())
+    s, e, o = s.cpu().numpy(), e.cpu().numpy(), o.cpu().numpy()
+    assert st.nb == nb and o[nb] == M * topk - 3
+    assert np.array_equal(st.expert_ids[:nb], e[:nb]) and np.array_equal(st.offsets[:nb + 1], o[:nb + 1])
+    for b in range(nb):
+        n = int(o[b + 1] - o[b])
+        assert np.array_equal(st.sorted_ids[b * st.bm: b * st.bm + n], s[b * st.bm: b * st.bm + n]), f"block {b}"
+
+
 # ------------------------------------------------------------------ GPT-OSS decode, every token
 
 def test_gptoss_decode_every_token_both_layouts():
