@@ -118,8 +118,9 @@ __device__ __forceinline__ void ring_tile(const GemmArgs& a, int64_t grid_blocks
 
   // ---- copies: wave w copies weight group w of the tile (16 rows) and the activation copies k
   // holding rows 4 (w + 8 k) .. +3 (BM = 16: rows 2 w, 2 w + 1 on lanes 0..31).  (Measured and
-  // dropped: the upper wave of each SIMD issuing the lower wave's share too, so that the lower
-  // one starts its products at once -- no gain.)
+  // dropped, no gain: the upper wave of each SIMD issuing the lower wave's share too, so that
+  // the lower one starts its products at once; the upper wave issuing its share after its
+  // products instead of before them.)
   const uint8_t* Wb = a.W + expert * a.w_estride;
   const int64_t row_bytes = MX ? a.K / 2 : a.K;
   const int64_t tsteps = (row_bytes + 127) / 128;  // tiled layout: 128-byte row steps per group
