@@ -262,3 +262,31 @@ def test_k_split_bias_topk_and_dropped_ids(k_split):
     w[torch.from_numpy((ids < 0) | (ids >= 12)).to(gpu())] = 0.0
     ref_inp = dict(inp, topk_ids=torch.from_numpy(keep).to(gpu()), topk_weights=w)
     assert_bf16_close(bf16_bits(out), _run_oracle(ref_inp), what=f"bias/dropped k_split={k_split}")
+
+
+@pytest.mark.parametrize("forced", [None, 1, 2, 3, 4])
+def test_mxfp4_plain_k_multiple_of_128(forced):
+    """MXFP4 with K % 128 == 0 in both stages on the plain layout: the ring-fed tiles copy one
+    aligned e8m0 dword per weight row per K step (the tiled layout and K = 2880 take other
+    copy paths); bias, top-3, every tile class."""
+    spec = _small_spec("fused_moe_mxfp4", 70, 6, 3, 1024, 384)
+    inp = synth.moe_inputs(spec, seed=71, device=gpu())
+    want = _run_oracle(inp)
+    d = None if forced is None else ops.Dispatch(mx.MXQ_DISPATCH_FORCED, forced, 4)
+    out = _run_gpu(inp, d)
+    torch.cuda.synchronize()
+    assert_bf16_close(bf16_bits(out), want, what=f"mxfp4 plain K%128 forced={forced}")
+
+
+@pytest.mark.parametrize("kind,H,I", [("fused_moe_fp8", 128, 128), ("fused_moe_fp8", 640, 384),
+                                      ("fused_moe_mxfp4", 96, 160)])
+def test_ring_tiles_narrow_and_ragged_shapes(kind, H, I):
+    """Single-step and ragged K ranges, weight-row counts that end inside a 16-row group of the
+    last 128-column tile, a single expert holding every row, every class forced."""
+    for forced in (1, 2, 3, 4):
+        spec = _small_spec(kind, 50, 1, 1, H, I)
+        inp = synth.moe_inputs(spec, seed=H + I + forced, device=gpu())
+        want = _run_oracle(inp)
+        out = _run_gpu(inp, ops.Dispatch(mx.MXQ_DISPATCH_FORCED, forced, 4))
+        torch.cuda.synchronize()
+        assert_bf16_close(bf16_bits(out), want, what=f"{kind} H={H} I={I} forced={forced}")
