@@ -261,7 +261,7 @@ mxq_status mxq_moe_align(const int32_t* topk_ids, int64_t M, int32_t topk, int32
  * The two layouts give bit-identical outputs.
  *
  * Per-call dispatch (`dispatch`, read during the call only; NULL = the defaults
- * {MXQ_DISPATCH_PER_BLOCK, 0, MXQ_TINY_ROWS_AUTO, MXQ_TINY_MFMA, MXQ_K_SPLIT_AUTO};
+ * {MXQ_DISPATCH_PER_BLOCK, 0, MXQ_TINY_ROWS_AUTO, MXQ_TINY_MFMA, MXQ_K_SPLIT_AUTO, MXQ_SORT_AUTO};
  * invalid fields -> MXQ_ERR_ARG):
  *   mode MXQ_DISPATCH_PER_BLOCK: each block's class from its own row count;
  *   mode MXQ_DISPATCH_FORCED: every block runs class `forced_class` (0 = tiny-block kernel,
@@ -297,7 +297,14 @@ mxq_status mxq_moe_align(const int32_t* topk_ids, int64_t M, int32_t topk, int32
  *        128-column tiles within 256 tiles (one per compute unit);
  *        1: never; 2 / 4 / 8: at most that many.  The workspace bounds the chunks to
  *        M * topk * chunks <= 2048.  Outputs agree with the unsplit call within rounding
- *        (the sums over K are grouped differently). */
+ *        (the sums over K are grouped differently).
+ *   sort MXQ_SORT_AUTO: small routings may skip the expert sort -- the expert-streaming case
+ *        above, and, with bf16 activations, no tiny class, at most 1024 routed rows and
+ *        E <= 512, when both stages run the direct-to-LDS 16/32/64/128-row tiles (K a
+ *        multiple of 32 up to 16384, 16-byte aligned rows; plain MXFP4: K a multiple of 128),
+ *        tiles that find their own block from topk_ids (the blocks and classes the sort
+ *        would give); MXQ_SORT_ALWAYS: the sort kernel and its block tables always run.
+ *        Both give bit-identical outputs. */
 #define MXQ_WEIGHTS_FP8_BLOCK 0
 #define MXQ_WEIGHTS_MXFP4 1
 #define MXQ_LAYOUT_PLAIN 0
@@ -309,12 +316,15 @@ mxq_status mxq_moe_align(const int32_t* topk_ids, int64_t M, int32_t topk, int32
 #define MXQ_TINY_GEMV 1
 #define MXQ_TINY_ROWS_AUTO (-1)
 #define MXQ_K_SPLIT_AUTO 0
+#define MXQ_SORT_AUTO 0
+#define MXQ_SORT_ALWAYS 1
 typedef struct mxq_moe_dispatch {
   int32_t mode;
   int32_t forced_class;
   int32_t tiny_max_rows;
   int32_t tiny_kernel;
   int32_t k_split;
+  int32_t sort;
 } mxq_moe_dispatch;
 size_t mxq_fused_moe_workspace_size(int64_t M, int64_t H, int64_t I, int32_t E, int32_t topk, int32_t weights,
                                     int32_t act_quant);

@@ -33,4 +33,7 @@ from ._lib import (  # noqa: F401
     MXQ_TINY_GEMV,
     MXQ_LAYOUT_PLAIN,
     MXQ_LAYOUT_TILED,
+    MXQ_K_SPLIT_AUTO,
+    MXQ_SORT_AUTO,
+    MXQ_SORT_ALWAYS,
 )

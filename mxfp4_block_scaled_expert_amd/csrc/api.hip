@@ -73,13 +73,19 @@ constexpr size_t kStreamMaxLds = 80 * 1024;
 constexpr int kDenseBigShape = MXQ_DENSE_BIG_SHAPE;  // tile shape of the large dense W8A8 GEMM
 
 constexpr int kMoeBlockM = 128;
+#ifndef MXQ_SELF_ROUTE
+#define MXQ_SELF_ROUTE 1
+#endif
+constexpr bool kSelfRoute = MXQ_SELF_ROUTE != 0;
+constexpr int64_t kSelfRouteMaxRows = 1024;   // routing ids held in each tile's LDS
+constexpr int32_t kSelfRouteMaxExperts = 512;  // one expert per thread of the ring-fed tile
 constexpr int kNumClasses = 5;  // tiny-block kernel, 16-, 32-, 64-, 128-row MFMA tiles
 constexpr int kClassTile[kNumClasses] = {-1, 3, 2, 1, 0};  // launcher tile index per class
 constexpr int kClassRows[kNumClasses] = {16, 16, 32, 64, 128};  // [0] is set at run time
 
 // The dispatch a call runs with: the caller's mxq_moe_dispatch, or the defaults for NULL.
 mxq_status read_dispatch(const mxq_moe_dispatch* d, mxq_moe_dispatch& out) {
-  out = mxq_moe_dispatch{MXQ_DISPATCH_PER_BLOCK, 0, MXQ_TINY_ROWS_AUTO, MXQ_TINY_MFMA, MXQ_K_SPLIT_AUTO};
+  out = mxq_moe_dispatch{MXQ_DISPATCH_PER_BLOCK, 0, MXQ_TINY_ROWS_AUTO, MXQ_TINY_MFMA, MXQ_K_SPLIT_AUTO, MXQ_SORT_AUTO};
   if (!d) return MXQ_OK;
   if (d->mode < MXQ_DISPATCH_PER_BLOCK || d->mode > MXQ_DISPATCH_LAYER_AVERAGE) return MXQ_ERR_ARG;
   if (d->tiny_kernel != MXQ_TINY_MFMA && d->tiny_kernel != MXQ_TINY_GEMV) return MXQ_ERR_ARG;
@@ -87,6 +93,7 @@ mxq_status read_dispatch(const mxq_moe_dispatch* d, mxq_moe_dispatch& out) {
   if (d->tiny_max_rows < MXQ_TINY_ROWS_AUTO || d->tiny_max_rows > 16) return MXQ_ERR_ARG;
   if (d->k_split != MXQ_K_SPLIT_AUTO && d->k_split != 1 && d->k_split != 2 && d->k_split != 4 && d->k_split != 8)
     return MXQ_ERR_ARG;
+  if (d->sort != MXQ_SORT_AUTO && d->sort != MXQ_SORT_ALWAYS) return MXQ_ERR_ARG;
   out = *d;
   return MXQ_OK;
 }
@@ -385,7 +392,8 @@ mxq_status run_moe(const void* x, int64_t M, int64_t H, int64_t I, int32_t E, in
   // Every block of the routing is tiny and the activations stay bf16: the expert-streaming
   // kernels group the routed rows by expert themselves (no sort, no block tables), stage 1 ends
   // in the SiLU-and-mul, and rows are indexed by flat routed id up to the combine.
-  if (!act_quant && pol.forced < 0 && pol.n_live == 1 && tiny == MXQ_TINY_MFMA && R <= kStreamMaxRows &&
+  if (!act_quant && dc.sort == MXQ_SORT_AUTO && pol.forced < 0 && pol.n_live == 1 && tiny == MXQ_TINY_MFMA &&
+      R <= kStreamMaxRows &&
       E <= kStreamMaxExperts && I % 16 == 0 &&
       expert_stream_lds_bytes(wfmt_w16, 1, 2 * I, H, E, R) <= kStreamMaxLds &&
       expert_stream_lds_bytes(wfmt_w16, 2, H, I, E, R) <= kStreamMaxLds) {
@@ -430,8 +438,23 @@ mxq_status run_moe(const void* x, int64_t M, int64_t H, int64_t I, int32_t E, in
     return launch_status();
   }
 
-  launch_moe_align(ids, M, topk, E, kMoeBlockM, w.sorted_ids, w.expert_ids, w.offsets, w.num_blocks, mbk, pol,
-                   w.class_lists, mbk, w.class_counts, false, w.align_scratch, st);
+  // Small bf16 routings on the ring-fed tiles with no tiny-class launch: every workgroup finds
+  // its block from the routing ids itself (the blocks the sort would lay out, with the classes
+  // it would pick) and no sort kernel runs.
+  const bool self_route = kSelfRoute && dc.sort == MXQ_SORT_AUTO && ring && R <= kSelfRouteMaxRows &&
+                          E <= kSelfRouteMaxExperts &&
+                          class_bound(0, R, E, mbk, pol) == 0;
+  if (self_route) {
+    for (GemmArgs* g : {&g1, &g2}) {
+      g->rt.route_ids = ids;
+      g->rt.route_R = int32_t(R);
+      g->rt.route_E = E;
+      g->rt.route_pol = pol;
+    }
+  } else {
+    launch_moe_align(ids, M, topk, E, kMoeBlockM, w.sorted_ids, w.expert_ids, w.offsets, w.num_blocks, mbk, pol,
+                     w.class_lists, mbk, w.class_counts, false, w.align_scratch, st);
+  }
   if (act_quant) launch_quant_1x128(static_cast<const uint16_t*>(x), M, H, H, w.qx, H, w.sx, st);
 
 
@@ -508,7 +531,10 @@ mxq_status run_moe(const void* x, int64_t M, int64_t H, int64_t I, int32_t E, in
         grp_ub[3 - tile] = ub;
       }
     }
-    if (!act_quant) {
+    if (self_route) {
+      const bool live[4] = {grp_ub[0] > 0, grp_ub[1] > 0, grp_ub[2] > 0, grp_ub[3] > 0};
+      launch_gemm_w16_ring_routed(g, mbk, live, wfmt_w16, mode, out_f32, st);
+    } else if (!act_quant) {
       if (ring)
         launch_gemm_w16_ring(grp, grp_ub, wfmt_w16, mode, out_f32, st);
       else
@@ -559,7 +585,7 @@ const char* mxq_status_string(mxq_status s) {
   }
 }
 
-int32_t mxq_abi_version(void) { return 8; }
+int32_t mxq_abi_version(void) { return 9; }
 
 mxq_status mxq_init(int32_t device) {
   if (hipSetDevice(device) != hipSuccess) return MXQ_ERR_ARCH;

@@ -67,8 +67,101 @@ constexpr size_t ring_lds_bytes() {
 
 }  // namespace
 
+// Self-routed block (small routings; every thread of the workgroup calls it): block `blk` of
+// the routing as the sort kernel would lay the blocks out -- experts ascending, each expert's
+// rows (flat ids ascending) cut into blocks of block_m -- found from the routing ids in LDS
+// (`scratch`, R + E + 24 ints).  Fills t and the block's flat routed ids s_rows (ascending) and
+// returns the block's class from its own row count, or -1 (uniformly) when the block does not
+// exist.
+__device__ __forceinline__ int self_route_block(const BlockRouting& rt, int64_t blk, TileInfo& t, int32_t* scratch,
+                                                int32_t* s_rows, int32_t* s_pick) {
+  constexpr int NT = kRingThreads, NW = kRingThreads / 64;
+  const int R = rt.route_R, E = rt.route_E, bm = rt.block_m;
+  int32_t* s_ids = scratch;      // [R]: expert of each routed row, -1 when dropped
+  int32_t* cnt = s_ids + R;      // [E]: rows per expert
+  int32_t* wsum = cnt + E;       // [2 NW]: wave sums of the scans, then [NW] wave counts
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  for (int e = tid; e < E; e += NT) cnt[e] = 0;
+  if (tid == 0) s_pick[0] = -1;
+  __syncthreads();
+  for (int r = tid; r < R; r += NT) {
+    int e = rt.route_ids[r];
+    if (e < 0 || e >= E) e = -1;
+    s_ids[r] = e;
+    if (e >= 0) atomicAdd(&cnt[e], 1);
+  }
+  __syncthreads();
+  // thread e (E <= NT): its expert's rows and blocks; exclusive scans of both over the experts
+  // (thread order is expert order)
+  const int my_rows = tid < E ? cnt[tid] : 0;
+  const int my_blks = (my_rows + bm - 1) / bm;
+  int sr = my_rows, sb = my_blks;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int tr = __shfl_up(sr, o, 64), tb = __shfl_up(sb, o, 64);
+    if (lane >= o) {
+      sr += tr;
+      sb += tb;
+    }
+  }
+  if (lane == 63) {
+    wsum[2 * wave] = sr;
+    wsum[2 * wave + 1] = sb;
+  }
+  __syncthreads();
+  int pr = 0, pb = 0;
+  for (int w = 0; w < wave; ++w) {
+    pr += wsum[2 * w];
+    pb += wsum[2 * w + 1];
+  }
+  const int row0 = pr + sr - my_rows, blk0 = pb + sb - my_blks;
+  if (tid < E && blk >= blk0 && blk < blk0 + my_blks) {
+    const int b = int(blk - blk0);
+    const int m = min(bm, my_rows - b * bm);
+    s_pick[0] = tid;
+    s_pick[1] = b;
+    s_pick[2] = m;
+    s_pick[3] = row0 + b * bm;
+    s_pick[4] = pick_class(rt.route_pol, m);
+  }
+  __syncthreads();
+  const int pe = s_pick[0];
+  if (pe < 0) return -1;
+  const int r_lo = s_pick[1] * bm, m_size = s_pick[2];
+  // the block's rows: the routed rows of expert pe whose rank among them lies in
+  // [r_lo, r_lo + m_size) (ranks from ballots and wave counts, in flat-id order)
+  int base = 0;
+  int32_t* wcnt = wsum + 2 * NW;  // [NW]
+  for (int r0 = 0; r0 < R; r0 += NT) {
+    const int r = r0 + tid;
+    const bool hit = r < R && s_ids[r] == pe;
+    const uint64_t bal = __ballot(hit);
+    if (lane == 0) wcnt[wave] = __popcll(bal);
+    __syncthreads();
+    int pre = base, tot = 0;
+    for (int w = 0; w < NW; ++w) {
+      pre += w < wave ? wcnt[w] : 0;
+      tot += wcnt[w];
+    }
+    const int i = pre + __popcll(bal & lt) - r_lo;
+    if (hit && i >= 0 && i < m_size) s_rows[i] = r;
+    base += tot;
+    __syncthreads();
+  }
+  t.expert = pe;
+  t.m0 = 0;
+  t.mb = 0;
+  t.off = s_pick[3];
+  t.m_total = m_size;
+  return s_pick[4];
+}
+
+// The tile body: block t, column tile nt, K chunk `split`.  s_rows: the block's flat routed ids
+// when the tile was self-routed, else NULL (rows from the sort's tables).
 template <int BM, int MODE, int WFMT, bool OUT_F32, bool HAS_BIAS, bool TILED>
-__device__ __forceinline__ void ring_tile(const GemmArgs& a, int64_t grid_blocks, int64_t bid, uint8_t* lds) {
+__device__ __forceinline__ void ring_body(const GemmArgs& a, const TileInfo& t, int64_t nt, int split, uint8_t* lds,
+                                          const int32_t* s_rows) {
   constexpr int NT = kRingThreads, BN = 128, NS = ring_stages<BM>();
   constexpr int WAVES_M = BM == 128 ? 4 : (BM == 16 ? 1 : 2);
   constexpr int WAVES_N = (NT / 64) / WAVES_M;
@@ -90,16 +183,9 @@ __device__ __forceinline__ void ring_tile(const GemmArgs& a, int64_t grid_blocks
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / WAVES_N, wn = wave % WAVES_N;
   const int frow = lane & 15, fq = lane >> 4;
-  // K split: chunk `split` of the tile's K range (fastest-varying), then row tile, then column tile
   const int nsplit = a.k_split > 1 ? a.k_split : 1;
-  const int split = int(bid % nsplit);
-  const int64_t rest = bid / nsplit;
-  const int64_t tile = rest % grid_blocks;
-  const int64_t nt = rest / grid_blocks;
   const int64_t n0 = nt * BN;
-  if (n0 >= a.N) return;
-  TileInfo t;
-  if (!tile_info<BM, MODE>(a, tile, t)) return;
+  const bool self_routed = s_rows != nullptr;
   const int64_t expert = t.expert;
   const int KS = int(cdiv(a.K, 128));
   int ks_b = 0, ks_e = KS;
@@ -175,7 +261,17 @@ __device__ __forceinline__ void ring_tile(const GemmArgs& a, int64_t grid_blocks
       }
     };
 
-    fill_rows<BM, MODE>(a, t, m_base, sArow, sOrow);
+    if (self_routed) {
+      // rows past the block repeat its last row and are never stored
+      for (int i = tid; i < BM; i += NT) {
+        const int ii = min(m_base + i, t.m_total - 1);
+        const int32_t r = s_rows[ii];
+        sArow[i] = MODE == ROWS_GATHER_TOK ? r / a.rt.topk : t.off + ii;
+        sOrow[i] = MODE == ROWS_GATHER_TOK ? int64_t(t.off + ii) : int64_t(r);
+      }
+    } else {
+      fill_rows<BM, MODE>(a, t, m_base, sArow, sOrow);
+    }
     __syncthreads();
 
     // activation copy sources; the lane's source chunk is its slot XOR the row's swizzle
@@ -347,6 +443,21 @@ __device__ __forceinline__ void ring_tile(const GemmArgs& a, int64_t grid_blocks
   }  // row passes
 }
 
+// One tile of a class's work list: entry `tile`, column tile nt, K chunk split (K chunk
+// fastest-varying, then the entry, then the column tile).
+template <int BM, int MODE, int WFMT, bool OUT_F32, bool HAS_BIAS, bool TILED>
+__device__ __forceinline__ void ring_tile(const GemmArgs& a, int64_t grid_blocks, int64_t bid, uint8_t* lds) {
+  const int nsplit = a.k_split > 1 ? a.k_split : 1;
+  const int split = int(bid % nsplit);
+  const int64_t rest = bid / nsplit;
+  const int64_t tile = rest % grid_blocks;
+  const int64_t nt = rest / grid_blocks;
+  if (nt * 128 >= a.N) return;
+  TileInfo t;
+  if (!tile_info<BM, MODE>(a, tile, t)) return;
+  ring_body<BM, MODE, WFMT, OUT_F32, HAS_BIAS, TILED>(a, t, nt, split, lds, nullptr);
+}
+
 // Routed tile classes 16 / 32 / 64 / 128 rows in one launch; launch order 128, 64, 32, 16 rows
 // (the longest tiles start first).
 struct RingGroup {
@@ -369,6 +480,34 @@ __global__ __launch_bounds__(kRingThreads) void gemm_w16_ring_kernel(RingGroup g
     ring_tile<16, MODE, WFMT, OUT_F32, HAS_BIAS, TILED>(g.a[0], g.gb[0], b - g.off[3], ring_lds);
 }
 
+// Self-routed small routings: workgroup (block, column tile, K chunk) -- K chunk fastest, then
+// the block in the sort's order, then the column tile -- finds its block from the routing ids,
+// then runs the tile class the block's row count picks.  Workgroups past the routing's blocks
+// exit after the lookup.
+template <int MODE, int WFMT, bool OUT_F32, bool HAS_BIAS, bool TILED>
+__global__ __launch_bounds__(kRingThreads) void gemm_w16_ring_routed_kernel(GemmArgs a, int64_t max_blocks) {
+  extern __shared__ __align__(1024) uint8_t ring_lds[];
+  __shared__ int32_t s_rows[128];
+  __shared__ int32_t s_pick[5];
+  const int nsplit = a.k_split > 1 ? a.k_split : 1;
+  const int64_t b = blockIdx.x;
+  const int split = int(b % nsplit);
+  const int64_t rest = b / nsplit;
+  const int64_t blk = rest % max_blocks;
+  const int64_t nt = rest / max_blocks;
+  TileInfo t;
+  const int c = self_route_block(a.rt, blk, t, reinterpret_cast<int32_t*>(ring_lds), s_rows, s_pick);
+  if (c < 0) return;
+  if (c >= 4)
+    ring_body<128, MODE, WFMT, OUT_F32, HAS_BIAS, TILED>(a, t, nt, split, ring_lds, s_rows);
+  else if (c == 3)
+    ring_body<64, MODE, WFMT, OUT_F32, HAS_BIAS, TILED>(a, t, nt, split, ring_lds, s_rows);
+  else if (c == 2)
+    ring_body<32, MODE, WFMT, OUT_F32, HAS_BIAS, TILED>(a, t, nt, split, ring_lds, s_rows);
+  else
+    ring_body<16, MODE, WFMT, OUT_F32, HAS_BIAS, TILED>(a, t, nt, split, ring_lds, s_rows);
+}
+
 template <int MODE, int WFMT, bool TL>
 static void launch_ring_t(const RingGroup& g, bool out_f32, hipStream_t st) {
   size_t lds = 0;
@@ -382,6 +521,28 @@ static void launch_ring_t(const RingGroup& g, bool out_f32, hipStream_t st) {
   const bool bias = g.a[0].bias != nullptr;
 #define MXQ_RING_GO(OF, HB) \
   hipLaunchKernelGGL((gemm_w16_ring_kernel<MODE, WFMT, OF, HB, TL>), grid, block, lds, st, g)
+  if (out_f32) { if (bias) MXQ_RING_GO(true, true); else MXQ_RING_GO(true, false); }
+  else { if (bias) MXQ_RING_GO(false, true); else MXQ_RING_GO(false, false); }
+#undef MXQ_RING_GO
+}
+
+// live[i]: tile class i (16, 32, 64, 128 rows) can occur
+template <int MODE, int WFMT, bool TL>
+static void launch_ring_routed_t(const GemmArgs& g, int64_t max_blocks, const bool live[4], bool out_f32,
+                                 hipStream_t st) {
+  const size_t f32[4] = {ring_lds_bytes<16, WFMT, true>(), ring_lds_bytes<32, WFMT, true>(),
+                         ring_lds_bytes<64, WFMT, true>(), ring_lds_bytes<128, WFMT, true>()};
+  const size_t b16[4] = {ring_lds_bytes<16, WFMT, false>(), ring_lds_bytes<32, WFMT, false>(),
+                         ring_lds_bytes<64, WFMT, false>(), ring_lds_bytes<128, WFMT, false>()};
+  // the lookup keeps R + E + 24 routing ints in the same LDS
+  size_t lds = sizeof(int32_t) * (size_t(g.rt.route_R) + size_t(g.rt.route_E) + 3 * (kRingThreads / 64));
+  for (int i = 0; i < 4; ++i)
+    if (live[i]) lds = std::max(lds, out_f32 ? f32[i] : b16[i]);
+  const int64_t nblocks = max_blocks * cdiv(g.N, int64_t(128)) * std::max<int64_t>(g.k_split, 1);
+  const dim3 grid{unsigned(nblocks)}, block{unsigned(kRingThreads)};
+  const bool bias = g.bias != nullptr;
+#define MXQ_RING_GO(OF, HB) \
+  hipLaunchKernelGGL((gemm_w16_ring_routed_kernel<MODE, WFMT, OF, HB, TL>), grid, block, lds, st, g, max_blocks)
   if (out_f32) { if (bias) MXQ_RING_GO(true, true); else MXQ_RING_GO(true, false); }
   else { if (bias) MXQ_RING_GO(false, true); else MXQ_RING_GO(false, false); }
 #undef MXQ_RING_GO
@@ -433,6 +594,25 @@ void launch_gemm_w16_ring(const GemmArgs cls[4], const int64_t grid_blocks[4], i
     if (mx) launch_ring_m<ROWS_COMPACT_IN, W_E2M1_MX>(g, out_f32, stream);
     else launch_ring_m<ROWS_COMPACT_IN, W_E4M3_BLOCK>(g, out_f32, stream);
   }
+}
+
+void launch_gemm_w16_ring_routed(const GemmArgs& g, int64_t max_blocks, const bool live[4], int wfmt, int row_mode,
+                                 bool out_f32, hipStream_t stream) {
+  if (max_blocks <= 0 || g.N <= 0) return;
+  const bool mx = wfmt == W_E2M1_MX;
+#define MXQ_ROUTED(MODE, WF)                                                  \
+  do {                                                                        \
+    if (g.w_tiled) launch_ring_routed_t<MODE, WF, true>(g, max_blocks, live, out_f32, stream);   \
+    else launch_ring_routed_t<MODE, WF, false>(g, max_blocks, live, out_f32, stream);            \
+  } while (0)
+  if (row_mode == ROWS_GATHER_TOK) {
+    if (mx) MXQ_ROUTED(ROWS_GATHER_TOK, W_E2M1_MX);
+    else MXQ_ROUTED(ROWS_GATHER_TOK, W_E4M3_BLOCK);
+  } else {
+    if (mx) MXQ_ROUTED(ROWS_COMPACT_IN, W_E2M1_MX);
+    else MXQ_ROUTED(ROWS_COMPACT_IN, W_E4M3_BLOCK);
+  }
+#undef MXQ_ROUTED
 }
 
 }  // namespace mxq

@@ -19,6 +19,27 @@ enum WFmt : int {
   W_E2M1_MX = 2,      // packed e2m1 + e8m0 scale per row per 32 columns
 };
 
+// Per-block tile-class policy: the class of a block of m_size rows.
+struct ClassPolicy {
+  int32_t n_classes;      // 0: no class lists
+  int32_t bound[8];       // class c takes blocks with bound[c-1] < m_size <= bound[c]
+  int32_t forced;         // >= 0: every non-empty block goes to this class
+  int32_t n_live;         // classes >= n_live are not launched; their blocks go to class n_live - 1
+};
+
+// The smallest launched class whose bound holds the block; the largest launched class takes
+// every block past the bounds (the tile kernels loop over row sub-tiles, so any block fits).
+// Unrolled over the eight slots so that every bound is read at a constant offset (a loop
+// indexing the argument struct at run time reads it from memory on every step).
+__device__ __forceinline__ int pick_class(const ClassPolicy& pol, int m_size) {
+  if (pol.forced >= 0) return pol.forced;
+  int c = pol.n_live - 1;
+#pragma unroll
+  for (int k = 7; k >= 0; --k)
+    if (k < pol.n_live - 1 && m_size <= pol.bound[k]) c = k;
+  return c;
+}
+
 // Routed-block description shared by every MoE stage kernel.
 struct BlockRouting {
   const int32_t* sorted_ids;  // [max_blocks * block_m]
@@ -29,6 +50,12 @@ struct BlockRouting {
   const int32_t* work_count;  // device scalar: number of valid entries
   int32_t block_m;
   int32_t topk;
+  // Self-routed small routings (ring-fed tiles only): with route_ids set, each workgroup finds
+  // its block from the routing itself -- blocks in the sort's order, each block's class from
+  // route_pol -- and no sort kernel runs.
+  const int32_t* route_ids;   // [route_R] expert of each flat routed row (ids outside [0, E) drop)
+  int32_t route_R, route_E;
+  ClassPolicy route_pol;
 };
 
 struct GemmArgs {
@@ -131,6 +158,10 @@ bool w16_ring_supported(const GemmArgs& a, int wfmt);
 bool w16_ring_shape_ok(const GemmArgs& a, int wfmt);
 void launch_gemm_w16_ring(const GemmArgs cls[4], const int64_t grid_blocks[4], int wfmt, int row_mode,
                           bool out_f32, hipStream_t stream);
+// The same tiles self-routed (g.rt.route_ids set): one workgroup per (block, column tile, K
+// chunk) over max_blocks blocks; live[i]: tile class i (16, 32, 64, 128 rows) can occur.
+void launch_gemm_w16_ring_routed(const GemmArgs& g, int64_t max_blocks, const bool live[4], int wfmt, int row_mode,
+                                 bool out_f32, hipStream_t stream);
 
 // Wavefront-reduction GEMV for routed blocks of at most 4 rows.
 // a_e4m3: activations are e4m3 + 1x128 scales (W8A8), else bf16.
@@ -168,12 +199,6 @@ void launch_prepack_s(const uint8_t* s, int64_t E, int64_t N, int64_t groups, ui
 // per-block selector: class c's i-th block descriptor is the int4 at
 // class_lists + (c * list_stride + i) * 4 (block id, expert, first compact row, row
 // count), and class_counts[c] holds the number of entries.
-struct ClassPolicy {
-  int32_t n_classes;      // 0: no class lists
-  int32_t bound[8];       // class c takes blocks with bound[c-1] < m_size <= bound[c]
-  int32_t forced;         // >= 0: every non-empty block goes to this class
-  int32_t n_live;         // classes >= n_live are not launched; their blocks go to class n_live - 1
-};
 // `scratch` (NULL, or align_multi_scratch_ints(R, E) ints): with more than kAlignMultiMinRows
 // routed rows and no pad slots to write, the sort runs over many workgroups (a histogram pass,
 // the tables in one workgroup, a scatter pass) and keeps its per-chunk counts there.

@@ -32,20 +32,6 @@
 
 namespace mxq {
 
-
-__device__ __forceinline__ int pick_class(const ClassPolicy& pol, int m_size) {
-  if (pol.forced >= 0) return pol.forced;
-  // the smallest launched class whose bound holds the block; the largest launched class takes
-  // every block past the bounds (the tile kernels loop over row sub-tiles, so any block fits).
-  // Unrolled over the eight slots so that every bound is read at a constant offset (a loop
-  // indexing the argument struct at run time reads it from memory on every step).
-  int c = pol.n_live - 1;
-#pragma unroll
-  for (int k = 7; k >= 0; --k)
-    if (k < pol.n_live - 1 && m_size <= pol.bound[k]) c = k;
-  return c;
-}
-
 // Lanes of the wave holding the same valid expert id as this lane (ballots over the id's bits).
 __device__ __forceinline__ uint64_t same_expert(int e, bool valid, int nbits) {
   uint64_t mask = __ballot(valid);

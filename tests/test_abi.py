@@ -41,9 +41,16 @@ def test_library_exports_every_declared_symbol():
         assert n in L.SIGNATURES, f"{n} has no ctypes signature in the binding"
 
 
+def test_dispatch_struct_matches_header():
+    from mxfp4_block_scaled_expert_amd import _lib as L
+    src = open(HEADER).read()
+    body = re.search(r"typedef struct mxq_moe_dispatch \{(.*?)\} mxq_moe_dispatch;", src, re.S).group(1)
+    assert [f for f, _ in L.MoeDispatch._fields_] == re.findall(r"int32_t (\w+);", body)
+
+
 def test_status_strings_and_version():
     L, lib = _lib()
-    assert lib.mxq_abi_version() == 8
+    assert lib.mxq_abi_version() == 9
     for code in range(0, 10):
         assert lib.mxq_status_string(code)
     assert b"unknown" in lib.mxq_status_string(99)
@@ -116,14 +123,16 @@ def test_argument_errors_before_any_launch():
     assert mx4(null, 4, 256, 128, 8, 2, null, null, null, null, null, null, null, 5, null, null, null, 0,
                null) == L.MXQ_ERR_ARG
     # per-call dispatch: every field validated before any pointer is looked at
-    for bad in ((7, 0, 4, 0, 0), (0, 0, 17, 0, 0), (0, 0, -2, 0, 0), (0, 0, 4, 5, 0), (1, 5, 16, 0, 0),
-                (1, -1, 16, 0, 0), (0, 0, 4, 0, 3), (0, 0, 4, 0, -1), (0, 0, 4, 0, 16)):
+    for bad in ((7, 0, 4, 0, 0, 0), (0, 0, 17, 0, 0, 0), (0, 0, -2, 0, 0, 0), (0, 0, 4, 5, 0, 0),
+                (1, 5, 16, 0, 0, 0), (1, -1, 16, 0, 0, 0), (0, 0, 4, 0, 3, 0), (0, 0, 4, 0, -1, 0),
+                (0, 0, 4, 0, 16, 0), (0, 0, 4, 0, 0, 2), (0, 0, 4, 0, 0, -1)):
         d = C.byref(L.MoeDispatch(*bad))
         assert fp8(null, 4, 256, 128, 8, 2, null, null, null, null, null, null, null, 0, 0, d, null, null, 0,
                    null) == L.MXQ_ERR_ARG, bad
         assert mx4(null, 4, 256, 128, 8, 2, null, null, null, null, null, null, null, 0, d, null, null, 0,
                    null) == L.MXQ_ERR_ARG, bad
-    for good in ((0, 0, 16, 0, 0), (1, 4, 4, 1, 1), (2, 0, 0, 0, 2), (0, 0, -1, 0, 4), (0, 0, 8, 0, 8)):
+    for good in ((0, 0, 16, 0, 0, 0), (1, 4, 4, 1, 1, 1), (2, 0, 0, 0, 2, 0), (0, 0, -1, 0, 4, 1),
+                 (0, 0, 8, 0, 8, 0)):
         d = C.byref(L.MoeDispatch(*good))
         assert fp8(null, 4, 256, 128, 8, 2, null, null, null, null, null, null, null, 0, 0, d, null, null, 0,
                    null) == L.MXQ_ERR_NULL, good

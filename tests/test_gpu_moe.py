@@ -290,3 +290,54 @@ def test_ring_tiles_narrow_and_ragged_shapes(kind, H, I):
         out = _run_gpu(inp, ops.Dispatch(mx.MXQ_DISPATCH_FORCED, forced, 4))
         torch.cuda.synchronize()
         assert_bf16_close(bf16_bits(out), want, what=f"{kind} H={H} I={I} forced={forced}")
+
+
+# ------------------------------------------------------------------ self-routed tiles
+
+def _auto_and_sorted(inp, layout="plain", **d):
+    outs = []
+    for srt in (mx.MXQ_SORT_AUTO, mx.MXQ_SORT_ALWAYS):
+        dd = ops.Dispatch(sort=srt, **d)
+        if inp["kind"] == "fused_moe_mxfp4":
+            outs.append(ops.fused_moe_mxfp4(inp["x"], inp["topk_ids"], inp["topk_weights"], inp["w1"],
+                                            inp["w1_scale"], inp["w2"], inp["w2_scale"], inp["w1_bias"],
+                                            weight_layout=layout, dispatch=dd))
+        else:
+            outs.append(_run_gpu(inp, dd))
+    torch.cuda.synchronize()
+    return outs
+
+
+@pytest.mark.parametrize("case", ["small_blocks", "multi_block_expert", "r1024", "e512_forced", "mxfp4"])
+def test_self_routed_tiles_match_sorted(case):
+    """Small bf16 routings without a tiny class skip the sort: each tile finds its block from the
+    routing ids.  The blocks, their rows, order and classes equal the sort's, so the outputs equal
+    the sorted path's bit for bit (and the oracle's within tolerance): the small-block routing
+    (empty experts, blocks in several classes), an expert holding several 128-row blocks, 1024
+    routed rows, E = 512 with forced classes, and MXFP4 on both weight layouts."""
+    runs = [{}]
+    if case == "small_blocks":
+        inp = synth.moe_inputs(SMALL_BLOCKS, seed=1003, device=gpu())
+        runs = [{}, dict(k_split=1), dict(k_split=8)]
+    elif case == "multi_block_expert":
+        inp = synth.moe_inputs(_small_spec("fused_moe_fp8", 300, 4, 2, 256, 128, zipf=1.5), seed=61, device=gpu())
+        assert np.bincount(inp["topk_ids"].cpu().numpy().ravel(), minlength=4).max() > 256
+    elif case == "r1024":
+        inp = synth.moe_inputs(_small_spec("fused_moe_fp8", 256, 64, 4, 256, 256, zipf=0.9), seed=62, device=gpu())
+    elif case == "e512_forced":
+        inp = synth.moe_inputs(_small_spec("fused_moe_fp8", 300, 512, 2, 128, 128), seed=63, device=gpu())
+        runs = [dict(tiny_max_rows=0)] + [dict(mode=mx.MXQ_DISPATCH_FORCED, forced_class=c) for c in (1, 2, 3, 4)]
+    else:
+        inp = synth.moe_inputs(_small_spec("fused_moe_mxfp4", 40, 8, 4, 2880, 2880), seed=13, device=gpu())
+        runs = [{}, dict(mode=mx.MXQ_DISPATCH_FORCED, forced_class=1), dict(k_split=1)]
+    want = _run_oracle(inp)
+    for d in runs:
+        auto, srt = _auto_and_sorted(inp, **d)
+        assert torch.equal(auto.view(torch.int16), srt.view(torch.int16)), (case, d)
+        assert_bf16_close(bf16_bits(auto), want, what=f"self-routed {case} {d}")
+        if case == "mxfp4":
+            tin = dict(inp, w1=ops.moe_prepack(inp["w1"]), w2=ops.moe_prepack(inp["w2"]),
+                       w1_scale=ops.moe_prepack_scales(inp["w1_scale"]),
+                       w2_scale=ops.moe_prepack_scales(inp["w2_scale"]))
+            for t in _auto_and_sorted(tin, "tiled", **d):
+                assert torch.equal(t.view(torch.int16), auto.view(torch.int16)), (case, "tiled", d)
