@@ -72,6 +72,11 @@ constexpr size_t kStreamMaxLds = 80 * 1024;
 #endif
 constexpr int kDenseBigShape = MXQ_DENSE_BIG_SHAPE;  // tile shape of the large dense W8A8 GEMM
 
+#ifndef MXQ_DENSE_RING
+#define MXQ_DENSE_RING 1
+#endif
+constexpr bool kDenseRing = MXQ_DENSE_RING != 0;
+
 constexpr int kMoeBlockM = 128;
 #ifndef MXQ_SELF_ROUTE
 #define MXQ_SELF_ROUTE 1
@@ -563,6 +568,18 @@ int dense_w16_tile(int64_t M, int64_t N, int64_t batch) {
   return tile;
 }
 
+// Dense per-tensor products take the ring-fed tiles when the grid holds at most one workgroup
+// per compute unit and K spans two or more 128-wide steps: such a product is bound by the
+// latency of its K steps, and the ring keeps three of them in flight (per-tensor 97 x 576 x
+// 224: 8.7 -> 6.8 us; 128 heads of [64, 512] x [128, 512]^T: 9.8 -> 8.8 us).  Larger grids keep
+// the register-staged tiles, two or more workgroups per compute unit (128 heads of [1024, 128]
+// x [512, 128]^T: 64 against 84 us on the ring).  Both give the same bits (same products in
+// the same order, the scale and bias applied after the last one).
+bool dense_ring(const GemmArgs& g, int tile, int64_t batch) {
+  return kDenseRing && g.K > 128 && cdiv(g.M, tile_rows(tile)) * cdiv(g.N, int64_t(128)) * batch <= 256 &&
+         w16_ring_dense_supported(g, batch);
+}
+
 }  // namespace
 
 extern "C" {
@@ -630,8 +647,11 @@ mxq_status mxq_fp8_scaled_mm(const void* A, int64_t M, int64_t K, int64_t lda, c
   g.N = N;
   g.K = K;
   const int tile = dense_w16_tile(M, N, 1);
-  launch_gemm_w16(g, W_E4M3_TENSOR, ROWS_DENSE, tile, false, cdiv(M, tile_rows(tile)),
-                  static_cast<hipStream_t>(stream));
+  if (dense_ring(g, tile, 1))
+    launch_gemm_w16_ring_dense(g, tile, 1, static_cast<hipStream_t>(stream));
+  else
+    launch_gemm_w16(g, W_E4M3_TENSOR, ROWS_DENSE, tile, false, cdiv(M, tile_rows(tile)),
+                    static_cast<hipStream_t>(stream));
   return launch_status();
 }
 
@@ -669,7 +689,11 @@ mxq_status mxq_fp8_scaled_bmm(const void* A, int64_t batch, int64_t M, int64_t K
   g.M = M;
   g.N = N;
   g.K = K;
-  launch_gemm_w16_batched(g, dense_w16_tile(M, N, batch), batch, static_cast<hipStream_t>(stream));
+  const int tile = dense_w16_tile(M, N, batch);
+  if (dense_ring(g, tile, batch))
+    launch_gemm_w16_ring_dense(g, tile, batch, static_cast<hipStream_t>(stream));
+  else
+    launch_gemm_w16_batched(g, tile, batch, static_cast<hipStream_t>(stream));
   return launch_status();
 }
 

@@ -169,6 +169,9 @@ __device__ __forceinline__ void ring_body(const GemmArgs& a, const TileInfo& t, 
   constexpr int TM = WM / 16, TN = WN / 16;
   static_assert(TM >= 1 && TN >= 1 && TM <= 2, "wave tile");
   constexpr bool MX = WFMT == W_E2M1_MX;
+  // MXFP4 (scales folded into the decode) and per-tensor e4m3 (one scale, applied in the
+  // epilogue) accumulate straight into acc; block e4m3 scales each K step's partial sum
+  constexpr bool DIRECT = MX || WFMT == W_E4M3_TENSOR;
   constexpr int STAGE = ring_stage_bytes<BM, WFMT>();
   constexpr int W_OFF = BM * 256, S_OFF = W_OFF + RingFmt<WFMT>::w_bytes;
   constexpr int A_INS = BM == 16 ? 1 : BM / 32;  // activation copies per wave per step
@@ -348,13 +351,13 @@ __device__ __forceinline__ void ring_body(const GemmArgs& a, const TileInfo& t, 
         for (int i = 0; i < TL; ++i)
 #pragma unroll
           for (int j = 0; j < TN; ++j) {
-            if (MX)
+            if (DIRECT)
               acc[i][j] = mfma_16x16x32_bf16(af[i], bfr[j], acc[i][j]);
             else
               part[i][j] = mfma_16x16x32_bf16(af[i], bfr[j], part[i][j]);
           }
       }
-      if (!MX) {
+      if (!DIRECT) {
         const float swv = sSw[ks - ks_b];
 #pragma unroll
         for (int i = 0; i < TL; ++i)
@@ -408,6 +411,7 @@ __device__ __forceinline__ void ring_body(const GemmArgs& a, const TileInfo& t, 
     constexpr int CH = 16 / OE;
     static_assert(size_t(BM) * OROW * OE <= size_t(NS) * STAGE, "staged output fits the operand stages");
     uint8_t* const obase = static_cast<uint8_t*>(a.out) + (nsplit > 1 ? split * a.split_stride * OE : 0);
+    const float tscale = WFMT == W_E4M3_TENSOR ? reinterpret_cast<const float*>(a.ws)[0] : 1.f;
     wait_vmcnt<0>();
     __syncthreads();
 #pragma unroll
@@ -420,7 +424,7 @@ __device__ __forceinline__ void ring_body(const GemmArgs& a, const TileInfo& t, 
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int rl = wm * WM + 16 * i + 4 * fq + r;
-          const float v = acc[i][j][r] + b;
+          const float v = (WFMT == W_E4M3_TENSOR ? acc[i][j][r] * tscale : acc[i][j][r]) + b;
           if (OUT_F32)
             reinterpret_cast<float*>(lds)[rl * OROW + cl] = v;
           else
@@ -506,6 +510,24 @@ __global__ __launch_bounds__(kRingThreads) void gemm_w16_ring_routed_kernel(Gemm
     ring_body<32, MODE, WFMT, OUT_F32, HAS_BIAS, TILED>(a, t, nt, split, ring_lds, s_rows);
   else
     ring_body<16, MODE, WFMT, OUT_F32, HAS_BIAS, TILED>(a, t, nt, split, ring_lds, s_rows);
+}
+
+// Dense per-tensor W8A16 products (bf16 out): row tile fastest, then the column tile; batch
+// entry z = blockIdx.y reads A + z a_bstride, W + z w_estride, ws + z ws_estride, bias +
+// z bias_estride and writes out + z o_bstride.
+template <int BM, bool HAS_BIAS>
+__global__ __launch_bounds__(kRingThreads) void gemm_w16_ring_dense_kernel(GemmArgs a, int64_t grid_blocks) {
+  extern __shared__ __align__(1024) uint8_t ring_lds[];
+  const int64_t z = blockIdx.y;
+  a.A = static_cast<const uint16_t*>(a.A) + z * a.a_bstride;
+  a.W += z * a.w_estride;
+  a.ws = static_cast<const float*>(a.ws) + z * a.ws_estride;
+  if (HAS_BIAS) a.bias = static_cast<const uint8_t*>(a.bias) + z * a.bias_estride * (a.bias_bf16 ? 2 : 4);
+  a.out = static_cast<uint16_t*>(a.out) + z * a.o_bstride;
+  const int64_t tile = blockIdx.x % grid_blocks, nt = blockIdx.x / grid_blocks;
+  TileInfo t;
+  if (!tile_info<BM, ROWS_DENSE>(a, tile, t)) return;
+  ring_body<BM, ROWS_DENSE, W_E4M3_TENSOR, false, HAS_BIAS, false>(a, t, nt, 0, ring_lds, nullptr);
 }
 
 template <int MODE, int WFMT, bool TL>
@@ -613,6 +635,34 @@ void launch_gemm_w16_ring_routed(const GemmArgs& g, int64_t max_blocks, const bo
     else MXQ_ROUTED(ROWS_COMPACT_IN, W_E4M3_BLOCK);
   }
 #undef MXQ_ROUTED
+}
+
+bool w16_ring_dense_supported(const GemmArgs& a, int64_t batch) {
+  const auto al16 = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; };
+  if (a.K <= 0 || a.K % 32 != 0 || a.N <= 0 || a.M <= 0) return false;
+  if (!al16(a.A) || a.lda % 8 != 0 || !al16(a.W) || a.ldw % 16 != 0 || !al16(a.out) || a.ldo % 8 != 0) return false;
+  return batch <= 1 || (a.a_bstride % 8 == 0 && a.w_estride % 16 == 0 && a.o_bstride % 8 == 0);
+}
+
+template <int BM>
+static void launch_ring_dense_t(const GemmArgs& a, int64_t batch, hipStream_t st) {
+  const int64_t gb = cdiv(a.M, int64_t(BM));
+  const dim3 grid{unsigned(gb * cdiv(a.N, int64_t(128))), unsigned(batch)}, block{unsigned(kRingThreads)};
+  const size_t lds = ring_lds_bytes<BM, W_E4M3_TENSOR, false>();
+  if (a.bias)
+    hipLaunchKernelGGL((gemm_w16_ring_dense_kernel<BM, true>), grid, block, lds, st, a, gb);
+  else
+    hipLaunchKernelGGL((gemm_w16_ring_dense_kernel<BM, false>), grid, block, lds, st, a, gb);
+}
+
+void launch_gemm_w16_ring_dense(const GemmArgs& a, int tile, int64_t batch, hipStream_t stream) {
+  if (batch <= 0 || a.M <= 0 || a.N <= 0) return;
+  switch (tile) {
+    case 0: launch_ring_dense_t<128>(a, batch, stream); break;
+    case 1: launch_ring_dense_t<64>(a, batch, stream); break;
+    case 2: launch_ring_dense_t<32>(a, batch, stream); break;
+    default: launch_ring_dense_t<16>(a, batch, stream); break;
+  }
 }
 
 }  // namespace mxq

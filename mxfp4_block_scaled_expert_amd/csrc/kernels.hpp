@@ -158,6 +158,11 @@ bool w16_ring_supported(const GemmArgs& a, int wfmt);
 bool w16_ring_shape_ok(const GemmArgs& a, int wfmt);
 void launch_gemm_w16_ring(const GemmArgs cls[4], const int64_t grid_blocks[4], int wfmt, int row_mode,
                           bool out_f32, hipStream_t stream);
+// The same tiles on dense per-tensor W8A16 products (bf16 out, batch entries on grid.y as in
+// launch_gemm_w16_batched; tile 0..3 = 128, 64, 32, 16 rows).  Supported: K % 32 == 0,
+// 16-byte aligned A / W / out rows (and batch strides), plain weights.
+bool w16_ring_dense_supported(const GemmArgs& a, int64_t batch);
+void launch_gemm_w16_ring_dense(const GemmArgs& a, int tile, int64_t batch, hipStream_t stream);
 // The same tiles self-routed (g.rt.route_ids set): one workgroup per (block, column tile, K
 // chunk) over max_blocks blocks; live[i]: tile class i (16, 32, 64, 128 rows) can occur.
 void launch_gemm_w16_ring_routed(const GemmArgs& g, int64_t max_blocks, const bool live[4], int wfmt, int row_mode,

@@ -64,7 +64,11 @@ def _oracle_bmm(d, bias=None):
     return OD.fp8_scaled_bmm(bf16_bits(d["a"]), u8(d["w"]), scales, None if bias is None else bias)
 
 
-@pytest.mark.parametrize("B,M,N,K", [(4, 97, 224, 576), (16, 1, 128, 512), (3, 130, 200, 512), (2, 33, 128, 96)])
+# (24, 97, 224, 576): the batch's grid exceeds one workgroup per compute unit, so the batched
+# call runs the register-staged tiles while each 2-D reference call runs the ring-fed tiles --
+# the two kernels must agree bit for bit
+@pytest.mark.parametrize("B,M,N,K", [(4, 97, 224, 576), (16, 1, 128, 512), (3, 130, 200, 512), (2, 33, 128, 96),
+                                     (24, 97, 224, 576)])
 @pytest.mark.parametrize("per_entry_scale", [True, False])
 def test_fp8_scaled_bmm_matches_per_entry_products_and_oracle(B, M, N, K, per_entry_scale):
     d = synth.batched_w8a16(B, M, N, K, seed=B * 7 + M + N + K, device=gpu(), per_entry_scale=per_entry_scale)
