@@ -302,9 +302,10 @@ mxq_status mxq_moe_align(const int32_t* topk_ids, int64_t M, int32_t topk, int32
  *        above, and, with bf16 activations, no tiny class, at most 1024 routed rows and
  *        E <= 512, when both stages run the direct-to-LDS 16/32/64/128-row tiles (K a
  *        multiple of 32 up to 16384, 16-byte aligned rows; plain MXFP4: K a multiple of 128),
- *        tiles that find their own block from topk_ids (the blocks and classes the sort
- *        would give); MXQ_SORT_ALWAYS: the sort kernel and its block tables always run.
- *        Both give bit-identical outputs. */
+ *        tiles that find their own rows from topk_ids (each expert's rows in the sort's
+ *        order, cut into blocks of 64); MXQ_SORT_ALWAYS: the sort kernel and its block
+ *        tables always run.  Both give bit-identical outputs (every row's products are the
+ *        same, whichever block holds it). */
 #define MXQ_WEIGHTS_FP8_BLOCK 0
 #define MXQ_WEIGHTS_MXFP4 1
 #define MXQ_LAYOUT_PLAIN 0

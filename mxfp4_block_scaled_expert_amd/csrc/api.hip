@@ -84,6 +84,13 @@ constexpr int kMoeBlockM = 128;
 constexpr bool kSelfRoute = MXQ_SELF_ROUTE != 0;
 constexpr int64_t kSelfRouteMaxRows = 1024;   // routing ids held in each tile's LDS
 constexpr int32_t kSelfRouteMaxExperts = 512;  // one expert per thread of the ring-fed tile
+// Self-routed tiles cut each expert's rows into blocks of 64 (interleaved A/B against 128 and
+// 32: W8A16 E = 8 with blocks of 4, 5, 33, 12, 1, 73 rows 30.6 against 34.6 / 36.7 us; 256
+// tokens top-2 over 8 experts 40.7 against 48.4 / 56.1 us; 256 tokens top-4 over 64 experts
+// 124 against 131 / 133 us; MXFP4 256 tokens top-4 over 32 experts 223 against 224 / 281 us):
+// an expert's rows run on twice the workgroups of 128-row blocks, each with shorter K steps.
+constexpr int32_t kSelfRouteBlockM = 64;
+static_assert(kSelfRouteBlockM <= 128, "the self-routed tile keeps a block's row ids in 128 LDS slots");
 constexpr int kNumClasses = 5;  // tiny-block kernel, 16-, 32-, 64-, 128-row MFMA tiles
 constexpr int kClassTile[kNumClasses] = {-1, 3, 2, 1, 0};  // launcher tile index per class
 constexpr int kClassRows[kNumClasses] = {16, 16, 32, 64, 128};  // [0] is set at run time
@@ -444,13 +451,16 @@ mxq_status run_moe(const void* x, int64_t M, int64_t H, int64_t I, int32_t E, in
   }
 
   // Small bf16 routings on the ring-fed tiles with no tiny-class launch: every workgroup finds
-  // its block from the routing ids itself (the blocks the sort would lay out, with the classes
-  // it would pick) and no sort kernel runs.
+  // its block from the routing ids itself (the expert-ordered blocks the sort would lay out,
+  // cut at 64 rows, each with the class the policy picks for its row count) and no sort kernel
+  // runs; every row's products are those of the sorted path, so the outputs are the same bits.
   const bool self_route = kSelfRoute && dc.sort == MXQ_SORT_AUTO && ring && R <= kSelfRouteMaxRows &&
                           E <= kSelfRouteMaxExperts &&
                           class_bound(0, R, E, mbk, pol) == 0;
+  const int64_t self_mbk = mxq_moe_max_blocks(M, topk, E, kSelfRouteBlockM);
   if (self_route) {
     for (GemmArgs* g : {&g1, &g2}) {
+      g->rt.block_m = kSelfRouteBlockM;
       g->rt.route_ids = ids;
       g->rt.route_R = int32_t(R);
       g->rt.route_E = E;
@@ -538,7 +548,7 @@ mxq_status run_moe(const void* x, int64_t M, int64_t H, int64_t I, int32_t E, in
     }
     if (self_route) {
       const bool live[4] = {grp_ub[0] > 0, grp_ub[1] > 0, grp_ub[2] > 0, grp_ub[3] > 0};
-      launch_gemm_w16_ring_routed(g, mbk, live, wfmt_w16, mode, out_f32, st);
+      launch_gemm_w16_ring_routed(g, self_mbk, live, wfmt_w16, mode, out_f32, st);
     } else if (!act_quant) {
       if (ring)
         launch_gemm_w16_ring(grp, grp_ub, wfmt_w16, mode, out_f32, st);

@@ -485,11 +485,12 @@ __global__ __launch_bounds__(kRingThreads) void gemm_w16_ring_kernel(RingGroup g
 }
 
 // Self-routed small routings: workgroup (block, column tile, K chunk) -- K chunk fastest, then
-// the block in the sort's order, then the column tile -- finds its block from the routing ids,
+// the column tile, then the block in the sort's order -- finds its block from the routing ids,
 // then runs the tile class the block's row count picks.  Workgroups past the routing's blocks
-// exit after the lookup.
+// exit after the lookup; they come last in the grid, so a grid larger than the GPU holds never
+// keeps a live workgroup waiting behind them.
 template <int MODE, int WFMT, bool OUT_F32, bool HAS_BIAS, bool TILED>
-__global__ __launch_bounds__(kRingThreads) void gemm_w16_ring_routed_kernel(GemmArgs a, int64_t max_blocks) {
+__global__ __launch_bounds__(kRingThreads) void gemm_w16_ring_routed_kernel(GemmArgs a) {
   extern __shared__ __align__(1024) uint8_t ring_lds[];
   __shared__ int32_t s_rows[128];
   __shared__ int32_t s_pick[5];
@@ -497,8 +498,9 @@ __global__ __launch_bounds__(kRingThreads) void gemm_w16_ring_routed_kernel(Gemm
   const int64_t b = blockIdx.x;
   const int split = int(b % nsplit);
   const int64_t rest = b / nsplit;
-  const int64_t blk = rest % max_blocks;
-  const int64_t nt = rest / max_blocks;
+  const int64_t n_tiles = cdiv(a.N, int64_t(128));
+  const int64_t nt = rest % n_tiles;
+  const int64_t blk = rest / n_tiles;
   TileInfo t;
   const int c = self_route_block(a.rt, blk, t, reinterpret_cast<int32_t*>(ring_lds), s_rows, s_pick);
   if (c < 0) return;
@@ -564,7 +566,7 @@ static void launch_ring_routed_t(const GemmArgs& g, int64_t max_blocks, const bo
   const dim3 grid{unsigned(nblocks)}, block{unsigned(kRingThreads)};
   const bool bias = g.bias != nullptr;
 #define MXQ_RING_GO(OF, HB) \
-  hipLaunchKernelGGL((gemm_w16_ring_routed_kernel<MODE, WFMT, OF, HB, TL>), grid, block, lds, st, g, max_blocks)
+  hipLaunchKernelGGL((gemm_w16_ring_routed_kernel<MODE, WFMT, OF, HB, TL>), grid, block, lds, st, g)
   if (out_f32) { if (bias) MXQ_RING_GO(true, true); else MXQ_RING_GO(true, false); }
   else { if (bias) MXQ_RING_GO(false, true); else MXQ_RING_GO(false, false); }
 #undef MXQ_RING_GO

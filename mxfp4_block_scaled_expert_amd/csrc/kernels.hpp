@@ -51,8 +51,8 @@ struct BlockRouting {
   int32_t block_m;
   int32_t topk;
   // Self-routed small routings (ring-fed tiles only): with route_ids set, each workgroup finds
-  // its block from the routing itself -- blocks in the sort's order, each block's class from
-  // route_pol -- and no sort kernel runs.
+  // its block from the routing itself -- the sort's expert order, each expert's rows cut into
+  // blocks of block_m, each block's class from route_pol -- and no sort kernel runs.
   const int32_t* route_ids;   // [route_R] expert of each flat routed row (ids outside [0, E) drop)
   int32_t route_R, route_E;
   ClassPolicy route_pol;

@@ -310,11 +310,12 @@ def _auto_and_sorted(inp, layout="plain", **d):
 
 @pytest.mark.parametrize("case", ["small_blocks", "multi_block_expert", "r1024", "e512_forced", "mxfp4"])
 def test_self_routed_tiles_match_sorted(case):
-    """Small bf16 routings without a tiny class skip the sort: each tile finds its block from the
-    routing ids.  The blocks, their rows, order and classes equal the sort's, so the outputs equal
-    the sorted path's bit for bit (and the oracle's within tolerance): the small-block routing
-    (empty experts, blocks in several classes), an expert holding several 128-row blocks, 1024
-    routed rows, E = 512 with forced classes, and MXFP4 on both weight layouts."""
+    """Small bf16 routings without a tiny class skip the sort: each tile finds its rows from the
+    routing ids (the sort's expert order, cut into 64-row blocks).  Every row's products are the
+    sorted path's, so the outputs equal it bit for bit (and the oracle's within tolerance): the
+    small-block routing (empty experts, blocks in several classes), an expert holding several
+    128-row blocks, 1024 routed rows, E = 512 with forced classes, and MXFP4 on both weight
+    layouts."""
     runs = [{}]
     if case == "small_blocks":
         inp = synth.moe_inputs(SMALL_BLOCKS, seed=1003, device=gpu())
