@@ -261,7 +261,8 @@ mxq_status mxq_moe_align(const int32_t* topk_ids, int64_t M, int32_t topk, int32
  * The two layouts give bit-identical outputs.
  *
  * Per-call dispatch (`dispatch`, read during the call only; NULL = the defaults
- * {MXQ_DISPATCH_PER_BLOCK, 0, MXQ_TINY_ROWS_AUTO, MXQ_TINY_MFMA, MXQ_K_SPLIT_AUTO, MXQ_SORT_AUTO};
+ * {MXQ_DISPATCH_PER_BLOCK, 0, MXQ_TINY_ROWS_AUTO, MXQ_TINY_MFMA, MXQ_K_SPLIT_AUTO, MXQ_SORT_AUTO,
+ * MXQ_FUSE_AUTO};
  * invalid fields -> MXQ_ERR_ARG):
  *   mode MXQ_DISPATCH_PER_BLOCK: each block's class from its own row count;
  *   mode MXQ_DISPATCH_FORCED: every block runs class `forced_class` (0 = tiny-block kernel,
@@ -305,7 +306,15 @@ mxq_status mxq_moe_align(const int32_t* topk_ids, int64_t M, int32_t topk, int32
  *        tiles that find their own rows from topk_ids (each expert's rows in the sort's
  *        order, cut into blocks of 64); MXQ_SORT_ALWAYS: the sort kernel and its block
  *        tables always run.  Both give bit-identical outputs (every row's products are the
- *        same, whichever block holds it). */
+ *        same, whichever block holds it).
+ *   fuse MXQ_FUSE_AUTO: with bf16 activations the SiLU-and-mul joins a neighbouring kernel
+ *        where one fits -- the expert-streaming case above; the tiny-block kernel's stage-2
+ *        row staging when the tiny class takes every block; and, when stage 1 runs wholly on
+ *        the direct-to-LDS tiles (no tiny class) with whole K ranges and I a multiple of 64,
+ *        the stage-1 epilogue: each tile pairs 64 gate rows of w1 with the matching 64 up rows
+ *        and writes bf16(silu(g) * u) of its bf16-rounded outputs.  MXQ_FUSE_NONE: stage 1
+ *        always writes ic0 and the standalone SiLU-and-mul forms ic1.  Both give
+ *        bit-identical outputs (the same rounding points and the same SiLU expression). */
 #define MXQ_WEIGHTS_FP8_BLOCK 0
 #define MXQ_WEIGHTS_MXFP4 1
 #define MXQ_LAYOUT_PLAIN 0
@@ -319,6 +328,8 @@ mxq_status mxq_moe_align(const int32_t* topk_ids, int64_t M, int32_t topk, int32
 #define MXQ_K_SPLIT_AUTO 0
 #define MXQ_SORT_AUTO 0
 #define MXQ_SORT_ALWAYS 1
+#define MXQ_FUSE_AUTO 0
+#define MXQ_FUSE_NONE 1
 typedef struct mxq_moe_dispatch {
   int32_t mode;
   int32_t forced_class;
@@ -326,6 +337,7 @@ typedef struct mxq_moe_dispatch {
   int32_t tiny_kernel;
   int32_t k_split;
   int32_t sort;
+  int32_t fuse;
 } mxq_moe_dispatch;
 size_t mxq_fused_moe_workspace_size(int64_t M, int64_t H, int64_t I, int32_t E, int32_t topk, int32_t weights,
                                     int32_t act_quant);

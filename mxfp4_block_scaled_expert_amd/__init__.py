@@ -36,4 +36,6 @@ from ._lib import (  # noqa: F401
     MXQ_K_SPLIT_AUTO,
     MXQ_SORT_AUTO,
     MXQ_SORT_ALWAYS,
+    MXQ_FUSE_AUTO,
+    MXQ_FUSE_NONE,
 )

@@ -42,6 +42,8 @@ MXQ_TINY_ROWS_AUTO = -1
 MXQ_K_SPLIT_AUTO = 0
 MXQ_SORT_AUTO = 0
 MXQ_SORT_ALWAYS = 1
+MXQ_FUSE_AUTO = 0
+MXQ_FUSE_NONE = 1
 
 MXQ_LAYOUT_PLAIN = 0
 MXQ_LAYOUT_TILED = 1
@@ -54,7 +56,8 @@ MOE_WS_FIELDS = ("sorted_ids", "expert_ids", "offsets", "num_blocks", "qx", "sx"
 class MoeDispatch(C.Structure):
     """struct mxq_moe_dispatch (per-call dispatch of the fused MoE)."""
     _fields_ = [("mode", C.c_int32), ("forced_class", C.c_int32), ("tiny_max_rows", C.c_int32),
-                ("tiny_kernel", C.c_int32), ("k_split", C.c_int32), ("sort", C.c_int32)]
+                ("tiny_kernel", C.c_int32), ("k_split", C.c_int32), ("sort", C.c_int32),
+                ("fuse", C.c_int32)]
 
 _p = C.c_void_p
 _i32 = C.c_int32

@@ -97,7 +97,8 @@ constexpr int kClassRows[kNumClasses] = {16, 16, 32, 64, 128};  // [0] is set at
 
 // The dispatch a call runs with: the caller's mxq_moe_dispatch, or the defaults for NULL.
 mxq_status read_dispatch(const mxq_moe_dispatch* d, mxq_moe_dispatch& out) {
-  out = mxq_moe_dispatch{MXQ_DISPATCH_PER_BLOCK, 0, MXQ_TINY_ROWS_AUTO, MXQ_TINY_MFMA, MXQ_K_SPLIT_AUTO, MXQ_SORT_AUTO};
+  out = mxq_moe_dispatch{MXQ_DISPATCH_PER_BLOCK, 0, MXQ_TINY_ROWS_AUTO, MXQ_TINY_MFMA, MXQ_K_SPLIT_AUTO, MXQ_SORT_AUTO,
+                         MXQ_FUSE_AUTO};
   if (!d) return MXQ_OK;
   if (d->mode < MXQ_DISPATCH_PER_BLOCK || d->mode > MXQ_DISPATCH_LAYER_AVERAGE) return MXQ_ERR_ARG;
   if (d->tiny_kernel != MXQ_TINY_MFMA && d->tiny_kernel != MXQ_TINY_GEMV) return MXQ_ERR_ARG;
@@ -106,6 +107,7 @@ mxq_status read_dispatch(const mxq_moe_dispatch* d, mxq_moe_dispatch& out) {
   if (d->k_split != MXQ_K_SPLIT_AUTO && d->k_split != 1 && d->k_split != 2 && d->k_split != 4 && d->k_split != 8)
     return MXQ_ERR_ARG;
   if (d->sort != MXQ_SORT_AUTO && d->sort != MXQ_SORT_ALWAYS) return MXQ_ERR_ARG;
+  if (d->fuse != MXQ_FUSE_AUTO && d->fuse != MXQ_FUSE_NONE) return MXQ_ERR_ARG;
   out = *d;
   return MXQ_OK;
 }
@@ -404,7 +406,8 @@ mxq_status run_moe(const void* x, int64_t M, int64_t H, int64_t I, int32_t E, in
   // Every block of the routing is tiny and the activations stay bf16: the expert-streaming
   // kernels group the routed rows by expert themselves (no sort, no block tables), stage 1 ends
   // in the SiLU-and-mul, and rows are indexed by flat routed id up to the combine.
-  if (!act_quant && dc.sort == MXQ_SORT_AUTO && pol.forced < 0 && pol.n_live == 1 && tiny == MXQ_TINY_MFMA &&
+  if (!act_quant && dc.sort == MXQ_SORT_AUTO && dc.fuse == MXQ_FUSE_AUTO && pol.forced < 0 && pol.n_live == 1 &&
+      tiny == MXQ_TINY_MFMA &&
       R <= kStreamMaxRows &&
       E <= kStreamMaxExperts && I % 16 == 0 &&
       expert_stream_lds_bytes(wfmt_w16, 1, 2 * I, H, E, R) <= kStreamMaxLds &&
@@ -493,17 +496,27 @@ mxq_status run_moe(const void* x, int64_t M, int64_t H, int64_t I, int32_t E, in
 
   // With bf16 activations and only the tiny-block class launched, stage 2 computes the
   // SiLU-and-mul while staging its rows (no ic1 round trip, one launch fewer).
-  const bool fuse_silu = !act_quant && pol.forced < 0 && pol.n_live == 1 && tiny == MXQ_TINY_MFMA && sp1.n == 1 &&
-                         skinny_lds_bytes(wfmt_w16, false, I) <= kSkinnyMaxLds;
+  const bool fuse_silu = !act_quant && dc.fuse == MXQ_FUSE_AUTO && pol.forced < 0 && pol.n_live == 1 &&
+                         tiny == MXQ_TINY_MFMA && sp1.n == 1 && skinny_lds_bytes(wfmt_w16, false, I) <= kSkinnyMaxLds;
   if (fuse_silu) {
     g2.A = w.ic0;
     g2.lda = 2 * I;
     g2.a_silu = 1;
   }
+  // With bf16 activations, stage 1 wholly on the ring-fed tiles (no tiny-class launch) and
+  // whole K ranges, each stage-1 tile pairs 64 gate with the matching 64 up columns and ends in
+  // the SiLU-and-mul: ic1 comes straight out of stage 1, one launch fewer.
+  const bool pair_silu = !act_quant && dc.fuse == MXQ_FUSE_AUTO && ring && sp1.n == 1 && I % 64 == 0 &&
+                         class_bound(0, R, E, mbk, pol) == 0;
+  if (pair_silu) {
+    g1.silu_pair = 1;
+    g1.out = w.ic1;
+    g1.ldo = I;
+  }
   for (int stage = 0; stage < 2; ++stage) {
     if (stage == 1 && sp1.n > 1)
       launch_split_silu_mul(w.partial, sp1.n, R * 2 * I, R, I, w.ic1, st);
-    else if (stage == 1 && !fuse_silu)
+    else if (stage == 1 && !fuse_silu && !pair_silu)
       launch_silu_mul(w.ic0, R, I, 2 * I, w.ic1, w.ic1_q, w.ic1_s, st);
     GemmArgs& g = stage == 0 ? g1 : g2;
     const int mode = stage == 0 ? ROWS_GATHER_TOK : ROWS_COMPACT_IN;
@@ -612,7 +625,7 @@ const char* mxq_status_string(mxq_status s) {
   }
 }
 
-int32_t mxq_abi_version(void) { return 9; }
+int32_t mxq_abi_version(void) { return 10; }
 
 mxq_status mxq_init(int32_t device) {
   if (hipSetDevice(device) != hipSuccess) return MXQ_ERR_ARCH;

@@ -35,6 +35,7 @@
 #include <type_traits>
 
 #include "lds_dma.hpp"
+#include "quant_common.hpp"
 #include "tile_rows.hpp"
 
 
@@ -60,7 +61,7 @@ constexpr int ring_stage_bytes() { return BM * 256 + RingFmt<WFMT>::w_bytes + Ri
 
 template <int BM, int WFMT, bool OUT_F32>
 constexpr size_t ring_lds_bytes() {
-  const size_t ops = size_t(ring_stages<BM>()) * ring_stage_bytes<BM, WFMT>() + kRingMaxSteps * 4;
+  const size_t ops = size_t(ring_stages<BM>()) * ring_stage_bytes<BM, WFMT>() + 2 * kRingMaxSteps * 4;
   const size_t out = OUT_F32 ? size_t(BM) * (128 + 4) * 4 : size_t(BM) * (128 + 8) * 2;
   return ops > out ? ops : out;
 }
@@ -189,6 +190,14 @@ __device__ __forceinline__ void ring_body(const GemmArgs& a, const TileInfo& t, 
   const int nsplit = a.k_split > 1 ? a.k_split : 1;
   const int64_t n0 = nt * BN;
   const bool self_routed = s_rows != nullptr;
+  // Paired tile (stage 1 with the SiLU-and-mul in its epilogue; no K split): tile nt holds ic1
+  // columns [64 nt, +64), its weight-row groups 0..3 are the gate rows 64 nt + 16 g and groups
+  // 4..7 the matching up rows I + 64 nt + 16 (g - 4) (N = 2 I, I a multiple of 64).
+  const bool pair = a.silu_pair != 0;
+  const int64_t half = a.N / 2;
+  auto group_row0 = [&](int g) -> int64_t {
+    return pair ? (g < 4 ? 64 * nt + 16 * g : half + 64 * nt + 16 * (g - 4)) : n0 + 16 * g;
+  };
   const int64_t expert = t.expert;
   const int KS = int(cdiv(a.K, 128));
   int ks_b = 0, ks_e = KS;
@@ -201,8 +210,14 @@ __device__ __forceinline__ void ring_body(const GemmArgs& a, const TileInfo& t, 
 
   // weight-block scales of the K range (read before any copy is in flight)
   if (WFMT == W_E4M3_BLOCK) {
-    const float* swb = reinterpret_cast<const float*>(a.ws) + expert * a.ws_estride + (n0 / 128) * a.ws_s0;
-    for (int i = tid; i < nsteps; i += NT) sSw[i] = swb[int64_t(ks_b + i) * a.ws_s1];
+    // paired: the gate half's 128-row scale block in sSw[0, steps), the up half's in
+    // sSw[kRingMaxSteps, +steps)
+    const float* sw0 = reinterpret_cast<const float*>(a.ws) + expert * a.ws_estride;
+    const int64_t nb0 = group_row0(0) / 128, nb1 = group_row0(4) / 128;
+    for (int i = tid; i < nsteps; i += NT) {
+      sSw[i] = sw0[nb0 * a.ws_s0 + int64_t(ks_b + i) * a.ws_s1];
+      if (pair) sSw[kRingMaxSteps + i] = sw0[nb1 * a.ws_s0 + int64_t(ks_b + i) * a.ws_s1];
+    }
   }
 
   // ---- copies: wave w copies weight group w of the tile (16 rows) and the activation copies k
@@ -213,8 +228,9 @@ __device__ __forceinline__ void ring_body(const GemmArgs& a, const TileInfo& t, 
   const uint8_t* Wb = a.W + expert * a.w_estride;
   const int64_t row_bytes = MX ? a.K / 2 : a.K;
   const int64_t tsteps = (row_bytes + 127) / 128;  // tiled layout: 128-byte row steps per group
-  const int64_t grp16 = min<int64_t>(n0 / 16 + wave, a.N / 16 - 1);
-  const int64_t wrow = min<int64_t>(n0 + 16 * wave + frow, a.N - 1);
+  const int64_t grow0 = group_row0(wave);  // first weight row of this wave's 16-row group
+  const int64_t grp16 = min<int64_t>(grow0 / 16, a.N / 16 - 1);
+  const int64_t wrow = min<int64_t>(grow0 + frow, a.N - 1);
   const uint8_t* gw[2];
   int wbyte[2];  // plain layout: first byte of the lane's piece inside the row's K step
 #pragma unroll
@@ -236,7 +252,7 @@ __device__ __forceinline__ void ring_body(const GemmArgs& a, const TileInfo& t, 
     if (TILED)
       gs = se + grp16 * tsteps * 128 + (lane & 15) * 4;
     else
-      gs = se + min<int64_t>(n0 + 16 * wave + (lane & 15), a.N - 1) * a.ws_s0;
+      gs = se + min<int64_t>(grow0 + (lane & 15), a.N - 1) * a.ws_s0;
   }
 
   for (int m_base = 0; m_base < t.m_total; m_base += BM) {
@@ -358,7 +374,7 @@ __device__ __forceinline__ void ring_body(const GemmArgs& a, const TileInfo& t, 
           }
       }
       if (!DIRECT) {
-        const float swv = sSw[ks - ks_b];
+        const float swv = sSw[(pair && wn * WN >= 64 ? kRingMaxSteps : 0) + ks - ks_b];
 #pragma unroll
         for (int i = 0; i < TL; ++i)
 #pragma unroll
@@ -417,7 +433,7 @@ __device__ __forceinline__ void ring_body(const GemmArgs& a, const TileInfo& t, 
 #pragma unroll
     for (int j = 0; j < TN; ++j) {
       const int cl = wn * WN + 16 * j + frow;
-      const int64_t col = n0 + cl;
+      const int64_t col = pair ? group_row0(cl >> 4) + (cl & 15) : n0 + cl;  // the weight row
       const float b = HAS_BIAS && split == 0 && col < a.N ? load_bias(a, expert, col) : 0.f;
 #pragma unroll
       for (int i = 0; i < TM; ++i)
@@ -432,6 +448,17 @@ __device__ __forceinline__ void ring_body(const GemmArgs& a, const TileInfo& t, 
         }
     }
     __syncthreads();
+    if (!OUT_F32 && pair) {
+      // staged row: the bf16 ic0 values of gate columns [0, 64) and up columns [64, 128); out =
+      // ic1 [rows, I], 8 outputs per 16-byte chunk
+      for (int c = tid; c < m_size * 8; c += NT) {
+        const int rl = c >> 3, ch = c & 7;
+        const uint8_t* src = lds + (rl * OROW + ch * 8) * 2;
+        const uint4 h = silu_mul8(*reinterpret_cast<const uint4*>(src), *reinterpret_cast<const uint4*>(src + 128));
+        *reinterpret_cast<uint4*>(obase + (sOrow[rl] * a.ldo + 64 * nt + ch * 8) * 2) = h;
+      }
+      continue;  // next row pass (its first barrier orders these LDS reads before new writes)
+    }
     const int64_t ncols = min<int64_t>(BN, a.N - n0);
     for (int c = tid; c < m_size * (BN / CH); c += NT) {
       const int rl = c / (BN / CH), ch = c % (BN / CH);

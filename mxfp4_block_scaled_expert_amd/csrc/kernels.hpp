@@ -94,6 +94,10 @@ struct GemmArgs {
   int32_t k_split;
   int64_t k_chunk;
   int64_t split_stride;
+  // Stage 1 on the ring-fed tiles with the SiLU-and-mul in the epilogue (N = 2 I, I % 64 == 0,
+  // whole K): column tile nt pairs gate rows [64 nt, +64) with up rows [I + 64 nt, +64) and
+  // writes bf16(silu(gate) * up) of the bf16-rounded stage-1 values to out [rows, ldo = I]
+  int32_t silu_pair;
 };
 
 // MX-scaled dense GEMM (gemm_mx.hip): MXFP8 activations x MXFP8 / MXFP4 weights.

@@ -344,13 +344,15 @@ class Dispatch(NamedTuple):
     tiny_kernel: int = L.MXQ_TINY_MFMA
     k_split: int = L.MXQ_K_SPLIT_AUTO
     sort: int = L.MXQ_SORT_AUTO
+    fuse: int = L.MXQ_FUSE_AUTO
 
 
 def _dispatch(d: Optional[Dispatch]):
     if d is None:
         return None
     return ctypes.byref(L.MoeDispatch(int(d.mode), int(d.forced_class), int(d.tiny_max_rows), int(d.tiny_kernel),
-                                      int(d.k_split), int(d.sort)))
+                                      int(d.k_split), int(d.sort),
+                                      int(d.fuse)))
 
 
 def silu_and_mul(ic0: torch.Tensor, quant: bool = False):

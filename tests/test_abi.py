@@ -50,7 +50,7 @@ def test_dispatch_struct_matches_header():
 
 def test_status_strings_and_version():
     L, lib = _lib()
-    assert lib.mxq_abi_version() == 9
+    assert lib.mxq_abi_version() == 10
     for code in range(0, 10):
         assert lib.mxq_status_string(code)
     assert b"unknown" in lib.mxq_status_string(99)
@@ -123,16 +123,17 @@ def test_argument_errors_before_any_launch():
     assert mx4(null, 4, 256, 128, 8, 2, null, null, null, null, null, null, null, 5, null, null, null, 0,
                null) == L.MXQ_ERR_ARG
     # per-call dispatch: every field validated before any pointer is looked at
-    for bad in ((7, 0, 4, 0, 0, 0), (0, 0, 17, 0, 0, 0), (0, 0, -2, 0, 0, 0), (0, 0, 4, 5, 0, 0),
-                (1, 5, 16, 0, 0, 0), (1, -1, 16, 0, 0, 0), (0, 0, 4, 0, 3, 0), (0, 0, 4, 0, -1, 0),
-                (0, 0, 4, 0, 16, 0), (0, 0, 4, 0, 0, 2), (0, 0, 4, 0, 0, -1)):
+    for bad in ((7, 0, 4, 0, 0, 0, 0), (0, 0, 17, 0, 0, 0, 0), (0, 0, -2, 0, 0, 0, 0), (0, 0, 4, 5, 0, 0, 0),
+                (1, 5, 16, 0, 0, 0, 0), (1, -1, 16, 0, 0, 0, 0), (0, 0, 4, 0, 3, 0, 0), (0, 0, 4, 0, -1, 0, 0),
+                (0, 0, 4, 0, 16, 0, 0), (0, 0, 4, 0, 0, 2, 0), (0, 0, 4, 0, 0, -1, 0), (0, 0, 4, 0, 0, 0, 2),
+                (0, 0, 4, 0, 0, 0, -1)):
         d = C.byref(L.MoeDispatch(*bad))
         assert fp8(null, 4, 256, 128, 8, 2, null, null, null, null, null, null, null, 0, 0, d, null, null, 0,
                    null) == L.MXQ_ERR_ARG, bad
         assert mx4(null, 4, 256, 128, 8, 2, null, null, null, null, null, null, null, 0, d, null, null, 0,
                    null) == L.MXQ_ERR_ARG, bad
-    for good in ((0, 0, 16, 0, 0, 0), (1, 4, 4, 1, 1, 1), (2, 0, 0, 0, 2, 0), (0, 0, -1, 0, 4, 1),
-                 (0, 0, 8, 0, 8, 0)):
+    for good in ((0, 0, 16, 0, 0, 0, 0), (1, 4, 4, 1, 1, 1, 1), (2, 0, 0, 0, 2, 0, 1), (0, 0, -1, 0, 4, 1, 0),
+                 (0, 0, 8, 0, 8, 0, 1)):
         d = C.byref(L.MoeDispatch(*good))
         assert fp8(null, 4, 256, 128, 8, 2, null, null, null, null, null, null, null, 0, 0, d, null, null, 0,
                    null) == L.MXQ_ERR_NULL, good

@@ -342,3 +342,66 @@ def test_self_routed_tiles_match_sorted(case):
                        w2_scale=ops.moe_prepack_scales(inp["w2_scale"]))
             for t in _auto_and_sorted(tin, "tiled", **d):
                 assert torch.equal(t.view(torch.int16), auto.view(torch.int16)), (case, "tiled", d)
+
+
+# ------------------------------------------------------------------ SiLU-and-mul in the stage-1 epilogue
+
+@pytest.mark.parametrize("case", ["small_blocks", "bias_top3_dropped", "m256", "mxfp4", "forced"])
+def test_fused_silu_stage1_matches_unfused(case):
+    """With bf16 activations, stage 1 wholly on the direct-to-LDS tiles and whole K ranges, each
+    stage-1 tile pairs 64 gate with the matching 64 up weight rows and writes ic1 itself.  The
+    same call with MXQ_FUSE_NONE (ic0 written, then the standalone SiLU-and-mul) gives the same
+    bits; both match the oracle.  Self-routed and sorted tiles, plain and tiled weights, a bias
+    on both halves, dropped ids, and every tile class forced."""
+    extra = [{}]
+    if case == "small_blocks":
+        inp = synth.moe_inputs(SMALL_BLOCKS, seed=1003, device=gpu())
+        runs = [dict(k_split=1), dict(k_split=1, sort=mx.MXQ_SORT_ALWAYS)]
+    elif case == "bias_top3_dropped":
+        inp = synth.moe_inputs(_small_spec("fused_moe_fp8", 77, 12, 3, 384, 256, zipf=0.8), seed=12, device=gpu())
+        g = torch.Generator(device="cuda").manual_seed(3)
+        inp["w1_bias"] = torch.randn(12, 512, generator=g, device=gpu())
+        inp["topk_ids"][5, 1] = -1
+        inp["topk_ids"][9, 0] = 12
+        runs = [dict(k_split=1), dict(k_split=1, sort=mx.MXQ_SORT_ALWAYS)]
+    elif case == "m256":
+        inp = synth.moe_inputs(_small_spec("fused_moe_fp8", 256, 8, 2, 512, 256, zipf=1.2), seed=81, device=gpu())
+        runs = [{}, dict(sort=mx.MXQ_SORT_ALWAYS)]
+    elif case == "mxfp4":
+        inp = synth.moe_inputs(_small_spec("fused_moe_mxfp4", 40, 8, 4, 2880, 2880), seed=13, device=gpu())
+        runs = [dict(k_split=1)]
+        extra = [{}, {"tiled": True}]
+    else:
+        inp = synth.moe_inputs(_small_spec("fused_moe_fp8", 70, 6, 3, 1024, 384), seed=71, device=gpu())
+        runs = [dict(mode=mx.MXQ_DISPATCH_FORCED, forced_class=c, k_split=1) for c in (1, 2, 3, 4)]
+    ids = inp["topk_ids"].cpu().numpy()
+    E = inp["E"]
+    ref = inp
+    if case == "bias_top3_dropped":
+        keep = ids.copy()
+        keep[(ids < 0) | (ids >= E)] = 0
+        w = inp["topk_weights"].clone()
+        w[torch.from_numpy((ids < 0) | (ids >= E)).to(gpu())] = 0.0
+        ref = dict(inp, topk_ids=torch.from_numpy(keep).to(gpu()), topk_weights=w)
+    want = _run_oracle(ref)
+    for ex in extra:
+        src = inp
+        layout = "plain"
+        if ex.get("tiled"):
+            src = dict(inp, w1=ops.moe_prepack(inp["w1"]), w2=ops.moe_prepack(inp["w2"]),
+                       w1_scale=ops.moe_prepack_scales(inp["w1_scale"]),
+                       w2_scale=ops.moe_prepack_scales(inp["w2_scale"]))
+            layout = "tiled"
+        for d in runs:
+            outs = []
+            for fuse in (mx.MXQ_FUSE_AUTO, mx.MXQ_FUSE_NONE):
+                dd = ops.Dispatch(fuse=fuse, **d)
+                if src["kind"] == "fused_moe_mxfp4":
+                    outs.append(ops.fused_moe_mxfp4(src["x"], src["topk_ids"], src["topk_weights"], src["w1"],
+                                                    src["w1_scale"], src["w2"], src["w2_scale"], src["w1_bias"],
+                                                    weight_layout=layout, dispatch=dd))
+                else:
+                    outs.append(_run_gpu(src, dd))
+            torch.cuda.synchronize()
+            assert torch.equal(outs[0].view(torch.int16), outs[1].view(torch.int16)), (case, layout, d)
+            assert_bf16_close(bf16_bits(outs[0]), want, what=f"fused SiLU {case} {layout} {d}")
