@@ -367,7 +367,7 @@ def _moe_setup(name_or_spec, seed: int, layout: str = "tiled", M=None, dispatch=
                               weight_layout=layout, dispatch=dispatch[0] if dispatch else None)
 
     flops = 2.0 * Mt * topk * (2 * I * H + H * I)
-    return {"inp": inp, "run": run, "bytes": byts, "flops": flops, "M": Mt}
+    return {"inp": inp, "run": run, "out": out, "bytes": byts, "flops": flops, "M": Mt}
 
 
 def bench_moe(name: str, steps: int, warmup: int, seed: int, layout: str = "tiled"):
