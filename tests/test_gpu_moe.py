@@ -308,7 +308,7 @@ def _auto_and_sorted(inp, layout="plain", **d):
     return outs
 
 
-@pytest.mark.parametrize("case", ["small_blocks", "multi_block_expert", "r1024", "e512_forced", "mxfp4"])
+@pytest.mark.parametrize("case", ["small_blocks", "multi_block_expert", "r1024", "e512_forced", "r1024_e512", "mxfp4"])
 def test_self_routed_tiles_match_sorted(case):
     """Small bf16 routings without a tiny class skip the sort: each tile finds its rows from the
     routing ids (the sort's expert order, cut into 64-row blocks).  Every row's products are the
@@ -328,6 +328,11 @@ def test_self_routed_tiles_match_sorted(case):
     elif case == "e512_forced":
         inp = synth.moe_inputs(_small_spec("fused_moe_fp8", 300, 512, 2, 128, 128), seed=63, device=gpu())
         runs = [dict(tiny_max_rows=0)] + [dict(mode=mx.MXQ_DISPATCH_FORCED, forced_class=c) for c in (1, 2, 3, 4)]
+    elif case == "r1024_e512":
+        # the largest self-routed routing: 1024 routed rows over 512 experts (its routing ids and
+        # counts fill the most LDS)
+        inp = synth.moe_inputs(_small_spec("fused_moe_fp8", 512, 512, 2, 128, 128, zipf=1.0), seed=64, device=gpu())
+        runs = [dict(tiny_max_rows=0), dict(mode=mx.MXQ_DISPATCH_FORCED, forced_class=4)]
     else:
         inp = synth.moe_inputs(_small_spec("fused_moe_mxfp4", 40, 8, 4, 2880, 2880), seed=13, device=gpu())
         runs = [{}, dict(mode=mx.MXQ_DISPATCH_FORCED, forced_class=1), dict(k_split=1)]
