@@ -513,12 +513,18 @@ def cpu_baseline(budget_s: float = 12.0):
     cref.block_fp8_linear_bf16(xb[:probe], w, sw, 128)
     per_row = (time.perf_counter() - t0) / probe
     rows = int(max(probe, min(M, budget_s / max(per_row, 1e-9))))
-    t0 = time.perf_counter()
-    cref.block_fp8_linear_bf16(xb[:rows], w, sw, 128)
-    dt = time.perf_counter() - t0
-    return {"value": 2.0 * rows * N * K / dt / 1e12, "unit": "TFLOP/s", "cores": cref.threads(), "kind": "oracle",
+    # one call on the sampled rows; when the whole workload takes less than the budget, whole
+    # calls are repeated until it is spent
+    calls, dt = 0, 0.0
+    while calls == 0 or (rows == M and dt < budget_s):
+        t0 = time.perf_counter()
+        cref.block_fp8_linear_bf16(xb[:rows], w, sw, 128)
+        dt += time.perf_counter() - t0
+        calls += 1
+    return {"value": 2.0 * rows * N * K * calls / dt / 1e12, "unit": "TFLOP/s", "cores": cref.threads(),
+            "kind": "oracle",
             "sample": f"C++ oracle (oracle/cpp/oracle.cpp), first {rows} of 2048 rows of the 2048x2048x7168 "
-                      f"block-FP8 linear with bf16 input (quantise + linear), one call, {dt:.1f} s"}
+                      f"block-FP8 linear with bf16 input (quantise + linear), {calls} call(s), {dt:.1f} s"}
 
 
 def calibrate_copy(steps: int = 10, mib: int = 256):
