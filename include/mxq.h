@@ -295,7 +295,9 @@ mxq_status mxq_moe_align(const int32_t* topk_ids, int64_t M, int32_t topk, int32
  *        columns) that run as workgroups of their own and write fp32 partial sums to the
  *        workspace; the kernel after the stage sums them in chunk order.  AUTO: with at
  *        most 256 routed rows, the most chunks that keep min(E, M * topk) blocks of
- *        128-column tiles within 256 tiles (one per compute unit);
+ *        128-column tiles within 256 tiles (one per compute unit) -- except a stage of a
+ *        routing the tiles can route themselves (see `sort`) whose largest grid of 16-, 32-
+ *        or 64-row blocks fits 256 workgroups: it runs unsplit on those blocks;
  *        1: never; 2 / 4 / 8: at most that many.  The workspace bounds the chunks to
  *        M * topk * chunks <= 2048.  Outputs agree with the unsplit call within rounding
  *        (the sums over K are grouped differently).
@@ -304,7 +306,7 @@ mxq_status mxq_moe_align(const int32_t* topk_ids, int64_t M, int32_t topk, int32
  *        E <= 512, when both stages run the direct-to-LDS 16/32/64/128-row tiles (K a
  *        multiple of 32 up to 16384, 16-byte aligned rows; plain MXFP4: K a multiple of 128),
  *        tiles that find their own rows from topk_ids (each expert's rows in the sort's
- *        order, cut into blocks of 64); MXQ_SORT_ALWAYS: the sort kernel and its block
+ *        order, cut into blocks of 16, 32 or 64); MXQ_SORT_ALWAYS: the sort kernel and its block
  *        tables always run.  Both give bit-identical outputs (every row's products are the
  *        same, whichever block holds it).
  *   fuse MXQ_FUSE_AUTO: with bf16 activations the SiLU-and-mul joins a neighbouring kernel

@@ -89,6 +89,8 @@ constexpr int32_t kSelfRouteMaxExperts = 512;  // one expert per thread of the r
 // tokens top-2 over 8 experts 40.7 against 48.4 / 56.1 us; 256 tokens top-4 over 64 experts
 // 124 against 131 / 133 us; MXFP4 256 tokens top-4 over 32 experts 223 against 224 / 281 us):
 // an expert's rows run on twice the workgroups of 128-row blocks, each with shorter K steps.
+// A stage whose grid still fits the GPU with smaller blocks takes them instead of a K split
+// (self_fill_block_m).
 constexpr int32_t kSelfRouteBlockM = 64;
 static_assert(kSelfRouteBlockM <= 128, "the self-routed tile keeps a block's row ids in 128 LDS slots");
 constexpr int kNumClasses = 5;  // tiny-block kernel, 16-, 32-, 64-, 128-row MFMA tiles
@@ -253,6 +255,18 @@ int64_t class_bound(int c, int64_t R, int32_t E, int64_t max_blocks, const Class
   int64_t ub = std::min<int64_t>(max_blocks, R / (lo + 1));
   if (hi < kMoeBlockM) ub = std::min<int64_t>(ub, E);  // only an expert's last block is partial
   return std::max<int64_t>(ub, 0);
+}
+
+// Self-routed stages: the smallest block size (16, 32 or 64 rows) whose largest possible grid
+// (blocks x column tiles) fits the GPU's compute units -- the stage's rows alone then fill the
+// GPU and it runs without a K split; 0 when no size fits (64-row blocks and the K-split rule).
+// Interleaved A/B: W8A16 E = 8 with blocks of 4, 5, 33, 12, 1, 73 rows 30.6 -> 26.2 us (16-row
+// blocks, no split, the SiLU-and-mul in the stage-1 epilogue), 64 tokens top-2 over 8 experts
+// 29.2 -> 26.3 us; larger routings keep 64-row blocks (no change).
+int32_t self_fill_block_m(int64_t M, int32_t topk, int32_t E, int64_t n_tiles) {
+  for (int32_t bm : {16, 32, 64})
+    if (mxq_moe_max_blocks(M, topk, E, bm) * n_tiles <= kSplitTargetTiles) return bm;
+  return 0;
 }
 
 // Per-block tile-class policy (page [A], implementation items 1-2: each block's kernel from its
@@ -457,13 +471,20 @@ mxq_status run_moe(const void* x, int64_t M, int64_t H, int64_t I, int32_t E, in
   // its block from the routing ids itself (the expert-ordered blocks the sort would lay out,
   // cut at 64 rows, each with the class the policy picks for its row count) and no sort kernel
   // runs; every row's products are those of the sorted path, so the outputs are the same bits.
-  const bool self_route = kSelfRoute && dc.sort == MXQ_SORT_AUTO && ring && R <= kSelfRouteMaxRows &&
-                          E <= kSelfRouteMaxExperts &&
-                          class_bound(0, R, E, mbk, pol) == 0;
-  const int64_t self_mbk = mxq_moe_max_blocks(M, topk, E, kSelfRouteBlockM);
+  // A stage whose self-routed rows alone fill the GPU runs without a K split.  The split follows
+  // from the routing's size whether or not the sort runs (MXQ_SORT_ALWAYS), so the two paths
+  // compute the same sums.
+  const bool self_routable = kSelfRoute && ring && R <= kSelfRouteMaxRows && E <= kSelfRouteMaxExperts &&
+                             class_bound(0, R, E, mbk, pol) == 0;
+  const bool self_route = self_routable && dc.sort == MXQ_SORT_AUTO;
+  const int32_t fill1 = self_routable ? self_fill_block_m(M, topk, E, cdiv(2 * I, int64_t(128))) : 0;
+  const int32_t fill2 = self_routable ? self_fill_block_m(M, topk, E, cdiv(H, int64_t(128))) : 0;
+  const int32_t self_bm1 = fill1 > 0 ? fill1 : kSelfRouteBlockM, self_bm2 = fill2 > 0 ? fill2 : kSelfRouteBlockM;
+  const int64_t self_mbk1 = mxq_moe_max_blocks(M, topk, E, self_bm1);
+  const int64_t self_mbk2 = mxq_moe_max_blocks(M, topk, E, self_bm2);
   if (self_route) {
     for (GemmArgs* g : {&g1, &g2}) {
-      g->rt.block_m = kSelfRouteBlockM;
+      g->rt.block_m = g == &g1 ? self_bm1 : self_bm2;
       g->rt.route_ids = ids;
       g->rt.route_R = int32_t(R);
       g->rt.route_E = E;
@@ -479,8 +500,9 @@ mxq_status run_moe(const void* x, int64_t M, int64_t H, int64_t I, int32_t E, in
   // K split (bf16 activations; not with the GEMV tiny kernel): partial slices in the workspace
   const bool gemv_runs = tiny == MXQ_TINY_GEMV && !tiled;  // the GEMV kernel writes whole sums only
   const bool can_split = !act_quant && !gemv_runs && w.partial;
-  const KSplit sp1 = can_split ? pick_split(R, E, 2 * I, H, dc.k_split) : KSplit{1, 0};
-  const KSplit sp2 = can_split ? pick_split(R, E, H, I, dc.k_split) : KSplit{1, 0};
+  const bool auto_split = dc.k_split == MXQ_K_SPLIT_AUTO;
+  const KSplit sp1 = can_split && !(auto_split && fill1 > 0) ? pick_split(R, E, 2 * I, H, dc.k_split) : KSplit{1, 0};
+  const KSplit sp2 = can_split && !(auto_split && fill2 > 0) ? pick_split(R, E, H, I, dc.k_split) : KSplit{1, 0};
   if (sp1.n > 1) {
     g1.k_split = sp1.n;
     g1.k_chunk = sp1.chunk;
@@ -561,7 +583,7 @@ mxq_status run_moe(const void* x, int64_t M, int64_t H, int64_t I, int32_t E, in
     }
     if (self_route) {
       const bool live[4] = {grp_ub[0] > 0, grp_ub[1] > 0, grp_ub[2] > 0, grp_ub[3] > 0};
-      launch_gemm_w16_ring_routed(g, self_mbk, live, wfmt_w16, mode, out_f32, st);
+      launch_gemm_w16_ring_routed(g, stage == 0 ? self_mbk1 : self_mbk2, live, wfmt_w16, mode, out_f32, st);
     } else if (!act_quant) {
       if (ring)
         launch_gemm_w16_ring(grp, grp_ub, wfmt_w16, mode, out_f32, st);
