@@ -314,9 +314,12 @@ mxq_status mxq_moe_align(const int32_t* topk_ids, int64_t M, int32_t topk, int32
  *        row staging when the tiny class takes every block; and, when stage 1 runs wholly on
  *        the direct-to-LDS tiles (no tiny class) with whole K ranges and I a multiple of 64,
  *        the stage-1 epilogue: each tile pairs 64 gate rows of w1 with the matching 64 up rows
- *        and writes bf16(silu(g) * u) of its bf16-rounded outputs.  MXQ_FUSE_NONE: stage 1
- *        always writes ic0 and the standalone SiLU-and-mul forms ic1.  Both give
- *        bit-identical outputs (the same rounding points and the same SiLU expression). */
+ *        and writes bf16(silu(g) * u) of its bf16-rounded outputs.  With top-1 routing, a
+ *        self-routed stage 2 and whole K ranges, the top-k combine also joins the stage-2
+ *        epilogue (out = bf16(weight * y), rows of dropped ids zeroed).  MXQ_FUSE_NONE:
+ *        stage 1 always writes ic0, the standalone SiLU-and-mul forms ic1 and the combine
+ *        kernel forms out.  Both give bit-identical outputs (the same rounding points, the
+ *        same SiLU expression and the same combine arithmetic). */
 #define MXQ_WEIGHTS_FP8_BLOCK 0
 #define MXQ_WEIGHTS_MXFP4 1
 #define MXQ_LAYOUT_PLAIN 0

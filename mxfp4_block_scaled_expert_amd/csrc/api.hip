@@ -535,6 +535,14 @@ mxq_status run_moe(const void* x, int64_t M, int64_t H, int64_t I, int32_t E, in
     g1.out = w.ic1;
     g1.ldo = I;
   }
+  // Self-routed stage 2 with top-1 routing and whole K ranges: the combine (one weighted row per
+  // token) folds into the stage-2 epilogue, which writes out directly.
+  const bool fold_top1 = self_route && topk == 1 && sp2.n == 1 && dc.fuse == MXQ_FUSE_AUTO;
+  if (fold_top1) {
+    g2.out = out;
+    g2.ldo = H;
+    g2.top1_w = wts;
+  }
   for (int stage = 0; stage < 2; ++stage) {
     if (stage == 1 && sp1.n > 1)
       launch_split_silu_mul(w.partial, sp1.n, R * 2 * I, R, I, w.ic1, st);
@@ -542,7 +550,7 @@ mxq_status run_moe(const void* x, int64_t M, int64_t H, int64_t I, int32_t E, in
       launch_silu_mul(w.ic0, R, I, 2 * I, w.ic1, w.ic1_q, w.ic1_s, st);
     GemmArgs& g = stage == 0 ? g1 : g2;
     const int mode = stage == 0 ? ROWS_GATHER_TOK : ROWS_COMPACT_IN;
-    const bool out_f32 = stage == 1 || sp1.n > 1;
+    const bool out_f32 = (stage == 1 && !fold_top1) || (stage == 0 && sp1.n > 1);
     // bf16 activations: the 16/32/64/128-row tile classes go out together in one grouped launch
     GemmArgs grp[4] = {g, g, g, g};
     int64_t grp_ub[4] = {0, 0, 0, 0};
@@ -593,7 +601,7 @@ mxq_status run_moe(const void* x, int64_t M, int64_t H, int64_t I, int32_t E, in
   }
   if (sp2.n > 1)
     launch_combine(w.partial, sp2.n, R * H, wts, ids, E, M, topk, H, static_cast<uint16_t*>(out), st);
-  else
+  else if (!fold_top1)
     launch_combine(w.y, 1, 0, wts, ids, E, M, topk, H, static_cast<uint16_t*>(out), st);
   return launch_status();
 }

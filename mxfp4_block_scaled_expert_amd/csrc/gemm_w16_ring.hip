@@ -71,7 +71,8 @@ constexpr size_t ring_lds_bytes() {
 // Self-routed block (small routings; every thread of the workgroup calls it): block `blk` of
 // the routing as the sort kernel would lay the blocks out -- experts ascending, each expert's
 // rows (flat ids ascending) cut into blocks of block_m -- found from the routing ids in LDS
-// (`scratch`, R + E + 24 ints).  Fills t and the block's flat routed ids s_rows (ascending) and
+// (`scratch`, R + E + 24 ints; on return its first R ints hold each routed row's expert, -1 when
+// dropped).  Fills t and the block's flat routed ids s_rows (ascending) and
 // returns the block's class from its own row count, or -1 (uniformly) when the block does not
 // exist.
 __device__ __forceinline__ int self_route_block(const BlockRouting& rt, int64_t blk, TileInfo& t, int32_t* scratch,
@@ -183,6 +184,7 @@ __device__ __forceinline__ void ring_body(const GemmArgs& a, const TileInfo& t, 
   const uint32_t lbase = lds_addr(lds);  // LDS byte address of the stages, as copies take it
   __shared__ int64_t sArow[BM];
   __shared__ int64_t sOrow[BM];
+  __shared__ float sWt[BM];  // top-1 fold: the routing weight of each output row
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / WAVES_N, wn = wave % WAVES_N;
@@ -287,6 +289,7 @@ __device__ __forceinline__ void ring_body(const GemmArgs& a, const TileInfo& t, 
         const int32_t r = s_rows[ii];
         sArow[i] = MODE == ROWS_GATHER_TOK ? r / a.rt.topk : t.off + ii;
         sOrow[i] = MODE == ROWS_GATHER_TOK ? int64_t(t.off + ii) : int64_t(r);
+        if (MODE == ROWS_COMPACT_IN && a.top1_w) sWt[i] = a.top1_w[r];
       }
     } else {
       fill_rows<BM, MODE>(a, t, m_base, sArow, sOrow);
@@ -440,7 +443,9 @@ __device__ __forceinline__ void ring_body(const GemmArgs& a, const TileInfo& t, 
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int rl = wm * WM + 16 * i + 4 * fq + r;
-          const float v = (WFMT == W_E4M3_TENSOR ? acc[i][j][r] * tscale : acc[i][j][r]) + b;
+          float v = (WFMT == W_E4M3_TENSOR ? acc[i][j][r] * tscale : acc[i][j][r]) + b;
+          // the top-1 combine, as the combine kernel evaluates it (an fma onto +0)
+          if (MODE == ROWS_COMPACT_IN && !OUT_F32 && a.top1_w) v = fmaf(sWt[rl], v, 0.f);
           if (OUT_F32)
             reinterpret_cast<float*>(lds)[rl * OROW + cl] = v;
           else
@@ -530,6 +535,23 @@ __global__ __launch_bounds__(kRingThreads) void gemm_w16_ring_routed_kernel(Gemm
   const int64_t blk = rest / n_tiles;
   TileInfo t;
   const int c = self_route_block(a.rt, blk, t, reinterpret_cast<int32_t*>(ring_lds), s_rows, s_pick);
+  if (MODE == ROWS_COMPACT_IN && !OUT_F32 && a.top1_w && blk == 0 && split == 0) {
+    // top-1 fold: the first block's workgroup of each column tile zeroes that tile's columns of
+    // the tokens whose id was dropped (the lookup left each row's expert, -1 when dropped, in
+    // the first R ints of the scratch); the barrier keeps those reads ahead of the tile's copies
+    const int32_t* s_ids = reinterpret_cast<const int32_t*>(ring_lds);
+    const int64_t n0 = nt * 128, ncols = min<int64_t>(128, a.N - n0);
+    for (int e = threadIdx.x; e < a.rt.route_R * 16; e += kRingThreads) {
+      const int r = e >> 4, ch = e & 15;
+      if (s_ids[r] >= 0 || ch * 8 >= ncols) continue;
+      uint16_t* o = static_cast<uint16_t*>(a.out) + int64_t(r) * a.ldo + n0 + ch * 8;
+      if (ch * 8 + 8 <= ncols)
+        *reinterpret_cast<uint4*>(o) = make_uint4(0, 0, 0, 0);
+      else
+        for (int k = 0; ch * 8 + k < ncols; ++k) o[k] = 0;
+    }
+    __syncthreads();
+  }
   if (c < 0) return;
   if (c >= 4)
     ring_body<128, MODE, WFMT, OUT_F32, HAS_BIAS, TILED>(a, t, nt, split, ring_lds, s_rows);

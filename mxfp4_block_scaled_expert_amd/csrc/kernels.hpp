@@ -98,6 +98,10 @@ struct GemmArgs {
   // whole K): column tile nt pairs gate rows [64 nt, +64) with up rows [I + 64 nt, +64) and
   // writes bf16(silu(gate) * up) of the bf16-rounded stage-1 values to out [rows, ldo = I]
   int32_t silu_pair;
+  // Self-routed stage 2 with top-1 routing and whole K ranges: the top-k combine folds into the
+  // epilogue -- out (bf16 [M, ldo]) row t = bf16(top1_w[t] * y[t]), and the rows of tokens
+  // whose id lies outside [0, E) are written as zeros
+  const float* top1_w;
 };
 
 // MX-scaled dense GEMM (gemm_mx.hip): MXFP8 activations x MXFP8 / MXFP4 weights.

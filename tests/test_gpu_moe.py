@@ -351,17 +351,24 @@ def test_self_routed_tiles_match_sorted(case):
 
 # ------------------------------------------------------------------ SiLU-and-mul in the stage-1 epilogue
 
-@pytest.mark.parametrize("case", ["small_blocks", "bias_top3_dropped", "m256", "mxfp4", "forced"])
+@pytest.mark.parametrize("case", ["small_blocks", "top1_dropped", "bias_top3_dropped", "m256", "mxfp4", "forced"])
 def test_fused_silu_stage1_matches_unfused(case):
     """With bf16 activations, stage 1 wholly on the direct-to-LDS tiles and whole K ranges, each
     stage-1 tile pairs 64 gate with the matching 64 up weight rows and writes ic1 itself.  The
     same call with MXQ_FUSE_NONE (ic0 written, then the standalone SiLU-and-mul) gives the same
     bits; both match the oracle.  Self-routed and sorted tiles, plain and tiled weights, a bias
-    on both halves, dropped ids, and every tile class forced."""
+    on both halves, dropped ids, and every tile class forced.  With top-1 routing the self-routed
+    stage 2 also folds the combine into its epilogue (zeroing the rows of dropped tokens)."""
     extra = [{}]
     if case == "small_blocks":
         inp = synth.moe_inputs(SMALL_BLOCKS, seed=1003, device=gpu())
-        runs = [dict(k_split=1), dict(k_split=1, sort=mx.MXQ_SORT_ALWAYS)]
+        runs = [{}, dict(k_split=1), dict(k_split=1, sort=mx.MXQ_SORT_ALWAYS)]
+    elif case == "top1_dropped":
+        inp = synth.moe_inputs(SMALL_BLOCKS, seed=1003, device=gpu())
+        inp["topk_ids"][3, 0] = -1
+        inp["topk_ids"][40, 0] = 8
+        inp["topk_ids"][127, 0] = -7
+        runs = [{}, dict(k_split=1), dict(sort=mx.MXQ_SORT_ALWAYS)]
     elif case == "bias_top3_dropped":
         inp = synth.moe_inputs(_small_spec("fused_moe_fp8", 77, 12, 3, 384, 256, zipf=0.8), seed=12, device=gpu())
         g = torch.Generator(device="cuda").manual_seed(3)
@@ -382,7 +389,7 @@ def test_fused_silu_stage1_matches_unfused(case):
     ids = inp["topk_ids"].cpu().numpy()
     E = inp["E"]
     ref = inp
-    if case == "bias_top3_dropped":
+    if case in ("bias_top3_dropped", "top1_dropped"):
         keep = ids.copy()
         keep[(ids < 0) | (ids >= E)] = 0
         w = inp["topk_weights"].clone()
@@ -410,3 +417,22 @@ def test_fused_silu_stage1_matches_unfused(case):
             torch.cuda.synchronize()
             assert torch.equal(outs[0].view(torch.int16), outs[1].view(torch.int16)), (case, layout, d)
             assert_bf16_close(bf16_bits(outs[0]), want, what=f"fused SiLU {case} {layout} {d}")
+
+
+def test_output_buffer_in_a_larger_allocation():
+    """The top-1 combine folded into stage 2 writes exactly the output rows: an output window
+    inside a zeroed larger buffer (16-byte aligned, as every pointer must be) gets the same bits
+    as a fresh output and the bytes around it stay zero; an output 8 bytes off that alignment
+    is refused before anything runs."""
+    inp = synth.moe_inputs(SMALL_BLOCKS, seed=1003, device=gpu())
+    M, H = inp["x"].shape
+    ref = _run_gpu(inp)
+    buf = torch.zeros(M * H + 16, dtype=torch.bfloat16, device=gpu())
+    out = buf[8:8 + M * H].view(M, H)
+    got = _run_gpu(inp, out=out)
+    torch.cuda.synchronize()
+    assert got.data_ptr() == out.data_ptr()
+    assert torch.equal(got.view(torch.int16), ref.view(torch.int16))
+    assert torch.all(buf[:8] == 0) and torch.all(buf[8 + M * H:] == 0)
+    with pytest.raises(ValueError):
+        _run_gpu(inp, out=buf[4:4 + M * H].view(M, H))
