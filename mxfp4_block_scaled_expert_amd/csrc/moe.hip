@@ -491,9 +491,13 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
       wk[j] = w[r];
       rk[j] = r;
     }
+    // non-temporal: y is read once (c5: 3.41 -> 3.39 ms)
     float4 v[kBatch];
 #pragma unroll
-    for (int j = 0; j < kBatch; ++j) v[j] = *reinterpret_cast<const float4*>(y + rk[j] * H + col);
+    for (int j = 0; j < kBatch; ++j) {
+      const f32x4 t = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(y + rk[j] * H + col));
+      v[j] = make_float4(t[0], t[1], t[2], t[3]);
+    }
     // K-split partial slices of y, summed in slice order
     for (int c = 1; c < n_split; ++c) {
 #pragma unroll
