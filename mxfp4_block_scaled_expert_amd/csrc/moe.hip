@@ -491,7 +491,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
       wk[j] = w[r];
       rk[j] = r;
     }
-    // non-temporal: y is read once (c5: 3.41 -> 3.39 ms)
+    // non-temporal: y is read once (4096 tokens top-8 over 256 experts, H = 7168: 3.41 -> 3.39 ms)
     float4 v[kBatch];
 #pragma unroll
     for (int j = 0; j < kBatch; ++j) {
