@@ -351,7 +351,8 @@ def test_self_routed_tiles_match_sorted(case):
 
 # ------------------------------------------------------------------ SiLU-and-mul in the stage-1 epilogue
 
-@pytest.mark.parametrize("case", ["small_blocks", "top1_dropped", "bias_top3_dropped", "m256", "mxfp4", "forced"])
+@pytest.mark.parametrize("case", ["small_blocks", "top1_dropped", "bias_top3_dropped", "m256", "mxfp4", "mxfp4_top1",
+                                  "forced"])
 def test_fused_silu_stage1_matches_unfused(case):
     """With bf16 activations, stage 1 wholly on the direct-to-LDS tiles and whole K ranges, each
     stage-1 tile pairs 64 gate with the matching 64 up weight rows and writes ic1 itself.  The
@@ -382,6 +383,11 @@ def test_fused_silu_stage1_matches_unfused(case):
     elif case == "mxfp4":
         inp = synth.moe_inputs(_small_spec("fused_moe_mxfp4", 40, 8, 4, 2880, 2880), seed=13, device=gpu())
         runs = [dict(k_split=1)]
+        extra = [{}, {"tiled": True}]
+    elif case == "mxfp4_top1":
+        # top-1 MXFP4 with a w1 bias and a ragged K (I = H = 2880): both epilogue folds
+        inp = synth.moe_inputs(_small_spec("fused_moe_mxfp4", 96, 8, 1, 2880, 2880), seed=14, device=gpu())
+        runs = [{}, dict(sort=mx.MXQ_SORT_ALWAYS)]
         extra = [{}, {"tiled": True}]
     else:
         inp = synth.moe_inputs(_small_spec("fused_moe_fp8", 70, 6, 3, 1024, 384), seed=71, device=gpu())
