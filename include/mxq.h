@@ -391,6 +391,54 @@ mxq_status mxq_fused_moe_mxfp4(const void* x, int64_t M, int64_t H, int64_t I, i
 mxq_status mxq_fused_moe_workspace_layout(int64_t M, int64_t H, int64_t I, int32_t E, int32_t topk, int32_t weights,
                                           int32_t act_quant, int64_t* offsets);
 
+/* The kernel plan a fused-MoE call of these sizes and this dispatch would run (host only: no
+ * device is touched; the call's pointers are taken to be 16-byte aligned, as they must be).
+ * Fills plan[MXQ_MOE_PLAN_FIELDS] and returns MXQ_OK; MXQ_ERR_SHAPE / MXQ_ERR_ARG for what the
+ * call would refuse (M >= 1 here), MXQ_ERR_NULL for a NULL plan.  weights MXQ_WEIGHTS_*,
+ * act_quant 0 / 1 (FP8 weights only), weight_layout MXQ_LAYOUT_*.  Fields:
+ *   PATH      MXQ_MOE_PATH_SORTED (the sort kernel and its block tables, then the tile classes),
+ *             MXQ_MOE_PATH_EXPERT_STREAM (every block tiny: two expert-streaming kernels, the
+ *             other fields but SILU / COMBINE / K_SPLIT* zero or one), MXQ_MOE_PATH_SELF_ROUTED
+ *             (the tiles find their own rows from topk_ids, no sort kernel);
+ *   TILES     MXQ_MOE_TILES_RING (bf16 activations, direct-to-LDS tiles), _REGISTER (bf16
+ *             activations, register-staged tiles), _W8A8, _W8A8_WIDE (W8A8 with the 128 x 256
+ *             tile for its largest class);
+ *   CLASSES   bit c set when block class c can occur (0 = tiny-block kernel, 1..4 = 16-, 32-,
+ *             64-, 128-row tiles);
+ *   BLOCK_M1 / BLOCK_M2  rows per routed block in stage 1 / 2 (128 on the sorted path);
+ *   K_SPLIT1 / K_SPLIT2  K chunks per tile in stage 1 / 2;
+ *   SILU      where the SiLU-and-mul runs: MXQ_MOE_SILU_KERNEL (its own kernel), _SPLIT_SUM (the
+ *             kernel that also sums stage 1's K chunks), _STAGE1_EPILOGUE, _STAGE2_STAGING (the
+ *             tiny-block kernel of stage 2), _EXPERT_STREAM;
+ *   COMBINE   MXQ_MOE_COMBINE_KERNEL or _STAGE2_EPILOGUE (top-1, self-routed). */
+#define MXQ_MOE_PLAN_PATH 0
+#define MXQ_MOE_PLAN_TILES 1
+#define MXQ_MOE_PLAN_CLASSES 2
+#define MXQ_MOE_PLAN_BLOCK_M1 3
+#define MXQ_MOE_PLAN_BLOCK_M2 4
+#define MXQ_MOE_PLAN_K_SPLIT1 5
+#define MXQ_MOE_PLAN_K_SPLIT2 6
+#define MXQ_MOE_PLAN_SILU 7
+#define MXQ_MOE_PLAN_COMBINE 8
+#define MXQ_MOE_PLAN_FIELDS 9
+#define MXQ_MOE_PATH_SORTED 0
+#define MXQ_MOE_PATH_EXPERT_STREAM 1
+#define MXQ_MOE_PATH_SELF_ROUTED 2
+#define MXQ_MOE_TILES_RING 0
+#define MXQ_MOE_TILES_REGISTER 1
+#define MXQ_MOE_TILES_W8A8 2
+#define MXQ_MOE_TILES_W8A8_WIDE 3
+#define MXQ_MOE_SILU_KERNEL 0
+#define MXQ_MOE_SILU_SPLIT_SUM 1
+#define MXQ_MOE_SILU_STAGE1_EPILOGUE 2
+#define MXQ_MOE_SILU_STAGE2_STAGING 3
+#define MXQ_MOE_SILU_EXPERT_STREAM 4
+#define MXQ_MOE_COMBINE_KERNEL 0
+#define MXQ_MOE_COMBINE_STAGE2_EPILOGUE 1
+mxq_status mxq_fused_moe_plan(int64_t M, int64_t H, int64_t I, int32_t E, int32_t topk, int32_t weights,
+                              int32_t act_quant, int32_t weight_layout, const mxq_moe_dispatch* dispatch,
+                              int32_t* plan);
+
 /* ------------------------------------------------------------------ SiLU-and-mul
  * The activation between the two expert stages (page [A], implementation item 2 and the
  * moe_fp8.cpp listing: stage 1 writes a 2N-wide gate/up intermediate that the activation

@@ -48,6 +48,15 @@ MXQ_FUSE_NONE = 1
 MXQ_LAYOUT_PLAIN = 0
 MXQ_LAYOUT_TILED = 1
 
+# fields of mxq_fused_moe_plan, and the values of its enumerated fields
+MOE_PLAN_FIELDS = ("path", "tiles", "classes", "block_m1", "block_m2", "k_split1", "k_split2", "silu", "combine")
+MOE_PLAN_NAMES = {
+    "path": ("sorted", "expert_stream", "self_routed"),
+    "tiles": ("ring", "register", "w8a8", "w8a8_wide"),
+    "silu": ("kernel", "split_sum", "stage1_epilogue", "stage2_staging", "expert_stream"),
+    "combine": ("kernel", "stage2_epilogue"),
+}
+
 # byte offsets reported by mxq_fused_moe_workspace_layout
 MOE_WS_FIELDS = ("sorted_ids", "expert_ids", "offsets", "num_blocks", "qx", "sx", "ic0", "ic1", "ic1_q", "ic1_s",
                  "y", "block_m", "partial")
@@ -89,6 +98,8 @@ SIGNATURES = {
     "mxq_fused_moe_mxfp4": (_i32, [_p, _i64, _i64, _i64, _i32, _i32, _p, _p, _p, _p, _p, _p, _p, _i32,
                                     C.POINTER(MoeDispatch), _p, _p, _sz, _p]),
     "mxq_fused_moe_workspace_layout": (_i32, [_i64, _i64, _i64, _i32, _i32, _i32, _i32, C.POINTER(_i64)]),
+    "mxq_fused_moe_plan": (_i32, [_i64, _i64, _i64, _i32, _i32, _i32, _i32, _i32, C.POINTER(MoeDispatch),
+                                  C.POINTER(_i32)]),
     "mxq_silu_and_mul": (_i32, [_p, _i64, _i64, _i64, _p, _p, _p, _p]),
     "mxq_moe_prepack_size": (_sz, [_i64, _i64, _i64]),
     "mxq_moe_prepack_scales_size": (_sz, [_i64, _i64, _i64]),

@@ -337,24 +337,17 @@ ClassPolicy make_policy(int64_t M, int64_t R, int32_t E, bool big_tile, bool rin
   return pol;
 }
 
-mxq_status run_moe(const void* x, int64_t M, int64_t H, int64_t I, int32_t E, int32_t topk, const int32_t* ids,
-                   const float* wts, const void* w1, const void* w1s, const void* w2, const void* w2s,
-                   const float* b1, int wfmt, bool act_quant, bool tiled, const mxq_moe_dispatch& dc, void* out,
-                   void* ws, size_t ws_bytes, hipStream_t st) {
+// The two stage GEMMs of a fused-MoE call over the carved workspace w (stage 1: ic0 = x @ w1^T
+// + b1 by compact row; stage 2: y = ic1 @ w2^T, rows scattered back to flat ids).
+void moe_stage_args(GemmArgs& g1, GemmArgs& g2, const MoeWorkspace& w, const void* x, const void* w1,
+                    const void* w1s, const void* w2, const void* w2s, const float* b1, int64_t M, int64_t H,
+                    int64_t I, int32_t topk, int wfmt, bool act_quant, bool tiled) {
   const int64_t R = M * topk;
-  if (R == 0) return MXQ_OK;
-  const int64_t mbk = mxq_moe_max_blocks(M, topk, E, kMoeBlockM);
-  MoeWorkspace w = carve_moe(ws, M, H, I, E, topk, act_quant);
-  if (!ws || ws_bytes < w.bytes) return MXQ_ERR_WORKSPACE;
-  // the 128 x 256 W8A8 tile: K <= 16384 on both stages and operand offsets below 4 GiB
-  const bool big_tile = act_quant && H <= 16384 && I <= 16384 && big_tile_offsets_fit(M, R, H, I);
   const bool mx = wfmt == W_E2M1_MX;
-  const int wfmt_w16 = mx ? W_E2M1_MX : W_E4M3_BLOCK;
-
   BlockRouting rt{w.sorted_ids, w.expert_ids, w.offsets, nullptr, nullptr, kMoeBlockM, topk};
 
   // stage 1: ic0 = x @ w1^T (+ b1), compact rows
-  GemmArgs g1{};
+  g1 = GemmArgs{};
   g1.A = act_quant ? static_cast<const void*>(w.qx) : x;
   g1.lda = H;
   g1.sa = w.sx;
@@ -384,7 +377,7 @@ mxq_status run_moe(const void* x, int64_t M, int64_t H, int64_t I, int32_t E, in
   g1.rt = rt;
 
   // stage 2: y = ic1 @ w2^T, rows scattered back to flat ids
-  GemmArgs g2{};
+  g2 = GemmArgs{};
   g2.A = act_quant ? static_cast<const void*>(w.ic1_q) : static_cast<const void*>(w.ic1);
   g2.lda = I;
   g2.sa = w.ic1_s;
@@ -410,22 +403,105 @@ mxq_status run_moe(const void* x, int64_t M, int64_t H, int64_t I, int32_t E, in
   g2.K = I;
   g2.rt = rt;
 
+}
+
+// Every host-side decision of a fused-MoE call, from sizes, the dispatch and the stage
+// arguments' layout and alignment (no device state is read).
+struct MoePlan {
+  bool big_tile;            // W8A8: the 128 x 256 direct-to-LDS tile takes the 65..128-row blocks
+  bool ring_shape, ring;    // bf16 activations: the ring-fed tiles (shape only / and alignment)
+  ClassPolicy pol;
+  bool expert_stream;       // every block tiny: the two expert-streaming kernels, no sort
+  bool self_routable, self_route;  // small routing the tiles can route themselves (and do)
+  int32_t bm1, bm2;         // self-routed block rows per stage
+  int64_t mbk1, mbk2;       // their largest block counts
+  bool fill1, fill2;        // a stage whose self-routed grid fits the GPU (no K split)
+  KSplit sp1, sp2;
+  bool fuse_silu;           // SiLU-and-mul in the tiny kernel's stage-2 row staging
+  bool pair_silu;           // SiLU-and-mul in the stage-1 epilogue of the ring-fed tiles
+  bool fold_top1;           // top-1 combine in the self-routed stage-2 epilogue
+};
+
+MoePlan plan_moe(const GemmArgs& g1, const GemmArgs& g2, int64_t M, int64_t H, int64_t I, int32_t E, int32_t topk,
+                 int wfmt, bool act_quant, bool tiled, const mxq_moe_dispatch& dc) {
+  MoePlan p{};
+  const int64_t R = M * topk;
+  const int64_t mbk = mxq_moe_max_blocks(M, topk, E, kMoeBlockM);
+  const int wfmt_w16 = wfmt == W_E2M1_MX ? W_E2M1_MX : W_E4M3_BLOCK;
+  // the 128 x 256 W8A8 tile: K <= 16384 on both stages and operand offsets below 4 GiB
+  p.big_tile = act_quant && H <= 16384 && I <= 16384 && big_tile_offsets_fit(M, R, H, I);
   // bf16 activations: both stages take the ring-fed tiles (the class policy looks only at the
   // layout-independent part, so that plain and tiled weights run the same classes)
-  const bool ring_shape = !act_quant && w16_ring_shape_ok(g1, wfmt_w16) && w16_ring_shape_ok(g2, wfmt_w16);
-  const bool ring = ring_shape && w16_ring_supported(g1, wfmt_w16) && w16_ring_supported(g2, wfmt_w16);
-  const ClassPolicy pol = make_policy(M, R, E, big_tile, ring_shape, wfmt, act_quant, dc);
+  p.ring_shape = !act_quant && w16_ring_shape_ok(g1, wfmt_w16) && w16_ring_shape_ok(g2, wfmt_w16);
+  p.ring = p.ring_shape && w16_ring_supported(g1, wfmt_w16) && w16_ring_supported(g2, wfmt_w16);
+  p.pol = make_policy(M, R, E, p.big_tile, p.ring_shape, wfmt, act_quant, dc);
   const int tiny = dc.tiny_kernel;
-
   // Every block of the routing is tiny and the activations stay bf16: the expert-streaming
   // kernels group the routed rows by expert themselves (no sort, no block tables), stage 1 ends
   // in the SiLU-and-mul, and rows are indexed by flat routed id up to the combine.
-  if (!act_quant && dc.sort == MXQ_SORT_AUTO && dc.fuse == MXQ_FUSE_AUTO && pol.forced < 0 && pol.n_live == 1 &&
-      tiny == MXQ_TINY_MFMA &&
-      R <= kStreamMaxRows &&
-      E <= kStreamMaxExperts && I % 16 == 0 &&
-      expert_stream_lds_bytes(wfmt_w16, 1, 2 * I, H, E, R) <= kStreamMaxLds &&
-      expert_stream_lds_bytes(wfmt_w16, 2, H, I, E, R) <= kStreamMaxLds) {
+  p.expert_stream = !act_quant && dc.sort == MXQ_SORT_AUTO && dc.fuse == MXQ_FUSE_AUTO && p.pol.forced < 0 &&
+                    p.pol.n_live == 1 && tiny == MXQ_TINY_MFMA && R <= kStreamMaxRows && E <= kStreamMaxExperts &&
+                    I % 16 == 0 && expert_stream_lds_bytes(wfmt_w16, 1, 2 * I, H, E, R) <= kStreamMaxLds &&
+                    expert_stream_lds_bytes(wfmt_w16, 2, H, I, E, R) <= kStreamMaxLds;
+  if (p.expert_stream) return p;
+  // Small bf16 routings on the ring-fed tiles with no tiny-class launch: every workgroup finds
+  // its block from the routing ids itself (the expert-ordered blocks the sort would lay out,
+  // cut at 16, 32 or 64 rows, each with the class the policy picks for its row count) and no
+  // sort kernel runs; every row's products are those of the sorted path, so the outputs are the
+  // same bits.  A stage whose self-routed rows alone fill the GPU runs without a K split.  The
+  // split follows from the routing's size whether or not the sort runs (MXQ_SORT_ALWAYS), so the
+  // two paths compute the same sums.
+  p.self_routable = kSelfRoute && p.ring && R <= kSelfRouteMaxRows && E <= kSelfRouteMaxExperts &&
+                    class_bound(0, R, E, mbk, p.pol) == 0;
+  p.self_route = p.self_routable && dc.sort == MXQ_SORT_AUTO;
+  const int32_t f1 = p.self_routable ? self_fill_block_m(M, topk, E, cdiv(2 * I, int64_t(128))) : 0;
+  const int32_t f2 = p.self_routable ? self_fill_block_m(M, topk, E, cdiv(H, int64_t(128))) : 0;
+  p.fill1 = f1 > 0;
+  p.fill2 = f2 > 0;
+  p.bm1 = p.fill1 ? f1 : kSelfRouteBlockM;
+  p.bm2 = p.fill2 ? f2 : kSelfRouteBlockM;
+  p.mbk1 = mxq_moe_max_blocks(M, topk, E, p.bm1);
+  p.mbk2 = mxq_moe_max_blocks(M, topk, E, p.bm2);
+  // K split (bf16 activations; not with the GEMV tiny kernel): partial slices in the workspace
+  const bool gemv_runs = tiny == MXQ_TINY_GEMV && !tiled;  // the GEMV kernel writes whole sums only
+  const bool can_split = !act_quant && !gemv_runs && split_cap(R) > 1;
+  const bool auto_split = dc.k_split == MXQ_K_SPLIT_AUTO;
+  p.sp1 = can_split && !(auto_split && p.fill1) ? pick_split(R, E, 2 * I, H, dc.k_split) : KSplit{1, 0};
+  p.sp2 = can_split && !(auto_split && p.fill2) ? pick_split(R, E, H, I, dc.k_split) : KSplit{1, 0};
+  // With bf16 activations and only the tiny-block class launched, stage 2 computes the
+  // SiLU-and-mul while staging its rows (no ic1 round trip, one launch fewer).
+  p.fuse_silu = !act_quant && dc.fuse == MXQ_FUSE_AUTO && p.pol.forced < 0 && p.pol.n_live == 1 &&
+                tiny == MXQ_TINY_MFMA && p.sp1.n == 1 && skinny_lds_bytes(wfmt_w16, false, I) <= kSkinnyMaxLds;
+  // With bf16 activations, stage 1 wholly on the ring-fed tiles (no tiny-class launch) and
+  // whole K ranges, each stage-1 tile pairs 64 gate with the matching 64 up columns and ends in
+  // the SiLU-and-mul: ic1 comes straight out of stage 1, one launch fewer.
+  p.pair_silu = !act_quant && dc.fuse == MXQ_FUSE_AUTO && p.ring && p.sp1.n == 1 && I % 64 == 0 &&
+                class_bound(0, R, E, mbk, p.pol) == 0;
+  // Self-routed stage 2 with top-1 routing and whole K ranges: the combine (one weighted row per
+  // token) folds into the stage-2 epilogue, which writes out directly.
+  p.fold_top1 = p.self_route && topk == 1 && p.sp2.n == 1 && dc.fuse == MXQ_FUSE_AUTO;
+  return p;
+}
+
+mxq_status run_moe(const void* x, int64_t M, int64_t H, int64_t I, int32_t E, int32_t topk, const int32_t* ids,
+                   const float* wts, const void* w1, const void* w1s, const void* w2, const void* w2s,
+                   const float* b1, int wfmt, bool act_quant, bool tiled, const mxq_moe_dispatch& dc, void* out,
+                   void* ws, size_t ws_bytes, hipStream_t st) {
+  const int64_t R = M * topk;
+  if (R == 0) return MXQ_OK;
+  const int64_t mbk = mxq_moe_max_blocks(M, topk, E, kMoeBlockM);
+  MoeWorkspace w = carve_moe(ws, M, H, I, E, topk, act_quant);
+  if (!ws || ws_bytes < w.bytes) return MXQ_ERR_WORKSPACE;
+  const bool mx = wfmt == W_E2M1_MX;
+  const int wfmt_w16 = mx ? W_E2M1_MX : W_E4M3_BLOCK;
+  GemmArgs g1, g2;
+  moe_stage_args(g1, g2, w, x, w1, w1s, w2, w2s, b1, M, H, I, topk, wfmt, act_quant, tiled);
+  const MoePlan plan = plan_moe(g1, g2, M, H, I, E, topk, wfmt, act_quant, tiled, dc);
+  const bool big_tile = plan.big_tile, ring = plan.ring;
+  const ClassPolicy pol = plan.pol;
+  const int tiny = dc.tiny_kernel;
+
+  if (plan.expert_stream) {
     const EsRoute er{ids, int32_t(R), E, topk};
     GemmArgs s1{};
     s1.A = x;
@@ -467,24 +543,11 @@ mxq_status run_moe(const void* x, int64_t M, int64_t H, int64_t I, int32_t E, in
     return launch_status();
   }
 
-  // Small bf16 routings on the ring-fed tiles with no tiny-class launch: every workgroup finds
-  // its block from the routing ids itself (the expert-ordered blocks the sort would lay out,
-  // cut at 64 rows, each with the class the policy picks for its row count) and no sort kernel
-  // runs; every row's products are those of the sorted path, so the outputs are the same bits.
-  // A stage whose self-routed rows alone fill the GPU runs without a K split.  The split follows
-  // from the routing's size whether or not the sort runs (MXQ_SORT_ALWAYS), so the two paths
-  // compute the same sums.
-  const bool self_routable = kSelfRoute && ring && R <= kSelfRouteMaxRows && E <= kSelfRouteMaxExperts &&
-                             class_bound(0, R, E, mbk, pol) == 0;
-  const bool self_route = self_routable && dc.sort == MXQ_SORT_AUTO;
-  const int32_t fill1 = self_routable ? self_fill_block_m(M, topk, E, cdiv(2 * I, int64_t(128))) : 0;
-  const int32_t fill2 = self_routable ? self_fill_block_m(M, topk, E, cdiv(H, int64_t(128))) : 0;
-  const int32_t self_bm1 = fill1 > 0 ? fill1 : kSelfRouteBlockM, self_bm2 = fill2 > 0 ? fill2 : kSelfRouteBlockM;
-  const int64_t self_mbk1 = mxq_moe_max_blocks(M, topk, E, self_bm1);
-  const int64_t self_mbk2 = mxq_moe_max_blocks(M, topk, E, self_bm2);
+  const bool self_route = plan.self_route;
+  const int64_t self_mbk1 = plan.mbk1, self_mbk2 = plan.mbk2;
   if (self_route) {
     for (GemmArgs* g : {&g1, &g2}) {
-      g->rt.block_m = g == &g1 ? self_bm1 : self_bm2;
+      g->rt.block_m = g == &g1 ? plan.bm1 : plan.bm2;
       g->rt.route_ids = ids;
       g->rt.route_R = int32_t(R);
       g->rt.route_E = E;
@@ -496,13 +559,8 @@ mxq_status run_moe(const void* x, int64_t M, int64_t H, int64_t I, int32_t E, in
   }
   if (act_quant) launch_quant_1x128(static_cast<const uint16_t*>(x), M, H, H, w.qx, H, w.sx, st);
 
-
-  // K split (bf16 activations; not with the GEMV tiny kernel): partial slices in the workspace
-  const bool gemv_runs = tiny == MXQ_TINY_GEMV && !tiled;  // the GEMV kernel writes whole sums only
-  const bool can_split = !act_quant && !gemv_runs && w.partial;
-  const bool auto_split = dc.k_split == MXQ_K_SPLIT_AUTO;
-  const KSplit sp1 = can_split && !(auto_split && fill1 > 0) ? pick_split(R, E, 2 * I, H, dc.k_split) : KSplit{1, 0};
-  const KSplit sp2 = can_split && !(auto_split && fill2 > 0) ? pick_split(R, E, H, I, dc.k_split) : KSplit{1, 0};
+  // K split: partial slices in the workspace
+  const KSplit sp1 = plan.sp1, sp2 = plan.sp2;
   if (sp1.n > 1) {
     g1.k_split = sp1.n;
     g1.k_chunk = sp1.chunk;
@@ -516,28 +574,17 @@ mxq_status run_moe(const void* x, int64_t M, int64_t H, int64_t I, int32_t E, in
     g2.out = w.partial;
   }
 
-  // With bf16 activations and only the tiny-block class launched, stage 2 computes the
-  // SiLU-and-mul while staging its rows (no ic1 round trip, one launch fewer).
-  const bool fuse_silu = !act_quant && dc.fuse == MXQ_FUSE_AUTO && pol.forced < 0 && pol.n_live == 1 &&
-                         tiny == MXQ_TINY_MFMA && sp1.n == 1 && skinny_lds_bytes(wfmt_w16, false, I) <= kSkinnyMaxLds;
+  const bool fuse_silu = plan.fuse_silu, pair_silu = plan.pair_silu, fold_top1 = plan.fold_top1;
   if (fuse_silu) {
     g2.A = w.ic0;
     g2.lda = 2 * I;
     g2.a_silu = 1;
   }
-  // With bf16 activations, stage 1 wholly on the ring-fed tiles (no tiny-class launch) and
-  // whole K ranges, each stage-1 tile pairs 64 gate with the matching 64 up columns and ends in
-  // the SiLU-and-mul: ic1 comes straight out of stage 1, one launch fewer.
-  const bool pair_silu = !act_quant && dc.fuse == MXQ_FUSE_AUTO && ring && sp1.n == 1 && I % 64 == 0 &&
-                         class_bound(0, R, E, mbk, pol) == 0;
   if (pair_silu) {
     g1.silu_pair = 1;
     g1.out = w.ic1;
     g1.ldo = I;
   }
-  // Self-routed stage 2 with top-1 routing and whole K ranges: the combine (one weighted row per
-  // token) folds into the stage-2 epilogue, which writes out directly.
-  const bool fold_top1 = self_route && topk == 1 && sp2.n == 1 && dc.fuse == MXQ_FUSE_AUTO;
   if (fold_top1) {
     g2.out = out;
     g2.ldo = H;
@@ -655,7 +702,7 @@ const char* mxq_status_string(mxq_status s) {
   }
 }
 
-int32_t mxq_abi_version(void) { return 10; }
+int32_t mxq_abi_version(void) { return 11; }
 
 mxq_status mxq_init(int32_t device) {
   if (hipSetDevice(device) != hipSuccess) return MXQ_ERR_ARCH;
@@ -963,6 +1010,56 @@ mxq_status mxq_fused_moe_workspace_layout(int64_t M, int64_t H, int64_t I, int32
   offsets[MXQ_MOE_WS_Y] = off(w.y);
   offsets[MXQ_MOE_WS_BLOCK_M] = kMoeBlockM;
   offsets[MXQ_MOE_WS_PARTIAL] = off(w.partial);
+  return MXQ_OK;
+}
+
+mxq_status mxq_fused_moe_plan(int64_t M, int64_t H, int64_t I, int32_t E, int32_t topk, int32_t weights,
+                              int32_t act_quant, int32_t weight_layout, const mxq_moe_dispatch* dispatch,
+                              int32_t* plan) {
+  if (weights != MXQ_WEIGHTS_FP8_BLOCK && weights != MXQ_WEIGHTS_MXFP4) return MXQ_ERR_ARG;
+  if (act_quant != 0 && act_quant != 1) return MXQ_ERR_ARG;
+  if (weights == MXQ_WEIGHTS_MXFP4 && act_quant) return MXQ_ERR_ARG;
+  if (weight_layout != MXQ_LAYOUT_PLAIN && weight_layout != MXQ_LAYOUT_TILED) return MXQ_ERR_ARG;
+  mxq_moe_dispatch dc;
+  MXQ_TRY(read_dispatch(dispatch, dc));
+  if (M <= 0 || H <= 0 || I <= 0 || E <= 0 || E > 512 || topk <= 0 || topk > E) return MXQ_ERR_SHAPE;
+  const int64_t q = weights == MXQ_WEIGHTS_MXFP4 ? 32 : 128;
+  if (H % q != 0 || I % q != 0) return MXQ_ERR_SHAPE;
+  if (!plan) return MXQ_ERR_NULL;
+  const bool mx = weights == MXQ_WEIGHTS_MXFP4, aq = act_quant != 0, tiled = weight_layout == MXQ_LAYOUT_TILED;
+  // stage arguments over stand-in pointers (16-byte aligned, as every call's pointers are)
+  auto fake = [](int i) { return reinterpret_cast<void*>(uintptr_t(i) << 24); };
+  const MoeWorkspace w = carve_moe(fake(1), M, H, I, E, topk, aq);
+  GemmArgs g1, g2;
+  moe_stage_args(g1, g2, w, fake(2), fake(3), fake(4), fake(5), fake(6), nullptr, M, H, I, topk,
+                 mx ? W_E2M1_MX : W_E4M3_BLOCK, aq, tiled);
+  const MoePlan p = plan_moe(g1, g2, M, H, I, E, topk, mx ? W_E2M1_MX : W_E4M3_BLOCK, aq, tiled, dc);
+  const int64_t R = M * topk, mbk = mxq_moe_max_blocks(M, topk, E, kMoeBlockM);
+  for (int i = 0; i < MXQ_MOE_PLAN_FIELDS; ++i) plan[i] = 0;
+  if (p.expert_stream) {
+    plan[MXQ_MOE_PLAN_PATH] = MXQ_MOE_PATH_EXPERT_STREAM;
+    plan[MXQ_MOE_PLAN_CLASSES] = 1;
+    plan[MXQ_MOE_PLAN_K_SPLIT1] = plan[MXQ_MOE_PLAN_K_SPLIT2] = 1;
+    plan[MXQ_MOE_PLAN_SILU] = MXQ_MOE_SILU_EXPERT_STREAM;
+    plan[MXQ_MOE_PLAN_COMBINE] = MXQ_MOE_COMBINE_KERNEL;
+    return MXQ_OK;
+  }
+  plan[MXQ_MOE_PLAN_PATH] = p.self_route ? MXQ_MOE_PATH_SELF_ROUTED : MXQ_MOE_PATH_SORTED;
+  plan[MXQ_MOE_PLAN_TILES] = aq ? (p.big_tile ? MXQ_MOE_TILES_W8A8_WIDE : MXQ_MOE_TILES_W8A8)
+                                : (p.ring ? MXQ_MOE_TILES_RING : MXQ_MOE_TILES_REGISTER);
+  int32_t classes = 0;
+  for (int c = 0; c < kNumClasses; ++c)
+    if (class_bound(c, R, E, mbk, p.pol) > 0) classes |= 1 << c;
+  plan[MXQ_MOE_PLAN_CLASSES] = classes;
+  plan[MXQ_MOE_PLAN_BLOCK_M1] = p.self_route ? p.bm1 : kMoeBlockM;
+  plan[MXQ_MOE_PLAN_BLOCK_M2] = p.self_route ? p.bm2 : kMoeBlockM;
+  plan[MXQ_MOE_PLAN_K_SPLIT1] = p.sp1.n;
+  plan[MXQ_MOE_PLAN_K_SPLIT2] = p.sp2.n;
+  plan[MXQ_MOE_PLAN_SILU] = p.sp1.n > 1    ? MXQ_MOE_SILU_SPLIT_SUM
+                            : p.pair_silu ? MXQ_MOE_SILU_STAGE1_EPILOGUE
+                            : p.fuse_silu ? MXQ_MOE_SILU_STAGE2_STAGING
+                                          : MXQ_MOE_SILU_KERNEL;
+  plan[MXQ_MOE_PLAN_COMBINE] = p.fold_top1 ? MXQ_MOE_COMBINE_STAGE2_EPILOGUE : MXQ_MOE_COMBINE_KERNEL;
   return MXQ_OK;
 }
 

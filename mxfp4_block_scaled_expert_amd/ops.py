@@ -336,6 +336,27 @@ def fused_moe_workspace_layout(M: int, H: int, I: int, E: int, topk: int, weight
     return {k: int(arr[i]) for i, k in enumerate(L.MOE_WS_FIELDS)}
 
 
+def fused_moe_plan(M: int, H: int, I: int, E: int, topk: int, weights: int, act_quant: bool = False,
+                   weight_layout: str = "plain", dispatch: Optional["Dispatch"] = None) -> Dict[str, object]:
+    """The kernel plan a fused-MoE call of these sizes would run (``mxq_fused_moe_plan``; host
+    only): path, tile family, the block classes that can occur (set of class ids), rows per
+    block and K chunks per stage, and where the SiLU-and-mul and the combine run."""
+    arr = (ctypes.c_int32 * len(L.MOE_PLAN_FIELDS))()
+    L.check("mxq_fused_moe_plan",
+            L.load().mxq_fused_moe_plan(M, H, I, E, topk, weights, int(act_quant), _layout(weight_layout),
+                                        _dispatch(dispatch), arr))
+    out: Dict[str, object] = {}
+    for i, k in enumerate(L.MOE_PLAN_FIELDS):
+        v = int(arr[i])
+        if k == "classes":
+            out[k] = {c for c in range(5) if v >> c & 1}
+        elif k in L.MOE_PLAN_NAMES:
+            out[k] = L.MOE_PLAN_NAMES[k][v]
+        else:
+            out[k] = v
+    return out
+
+
 class Dispatch(NamedTuple):
     """Per-call dispatch of the fused MoE (``struct mxq_moe_dispatch``); None = the defaults."""
     mode: int = L.MXQ_DISPATCH_PER_BLOCK

@@ -50,7 +50,7 @@ def test_dispatch_struct_matches_header():
 
 def test_status_strings_and_version():
     L, lib = _lib()
-    assert lib.mxq_abi_version() == 10
+    assert lib.mxq_abi_version() == 11
     for code in range(0, 10):
         assert lib.mxq_status_string(code)
     assert b"unknown" in lib.mxq_status_string(99)
@@ -226,3 +226,52 @@ def test_batched_binding_rejects_mismatched_shapes_without_gpu():
         ops.fp8_scaled_bmm(x, w, torch.ones(1), torch.zeros(3, 128))
     with pytest.raises(ValueError):
         ops.fp8_scaled_bmm(x.float(), w, torch.ones(1))
+
+
+def test_fused_moe_plan_host_logic():
+    """The host-side plan of a fused-MoE call (mxq_fused_moe_plan: no device touched) for the
+    workloads' shapes and the dispatch knobs: which path, tiles, block sizes, K splits and
+    fusions the call runs."""
+    L, _ = _lib()
+    from mxfp4_block_scaled_expert_amd.ops import Dispatch, fused_moe_plan
+    FP8, MX = L.MXQ_WEIGHTS_FP8_BLOCK, L.MXQ_WEIGHTS_MXFP4
+    # small-block W8A16 (128 tokens top-1 over 8 experts): self-routed 16-row blocks fill the
+    # GPU, no K split, the SiLU-and-mul and the combine in the stage epilogues
+    c3 = fused_moe_plan(128, 2048, 1024, 8, 1, FP8, weight_layout="tiled")
+    assert c3["path"] == "self_routed" and c3["tiles"] == "ring" and 0 not in c3["classes"]
+    assert (c3["block_m1"], c3["block_m2"], c3["k_split1"], c3["k_split2"]) == (16, 16, 1, 1)
+    assert (c3["silu"], c3["combine"]) == ("stage1_epilogue", "stage2_epilogue")
+    # the knobs: no fusion; the sort kept (same splits, so the same sums); a forced K split
+    nf = fused_moe_plan(128, 2048, 1024, 8, 1, FP8, dispatch=Dispatch(fuse=L.MXQ_FUSE_NONE))
+    assert (nf["path"], nf["silu"], nf["combine"]) == ("self_routed", "kernel", "kernel")
+    so = fused_moe_plan(128, 2048, 1024, 8, 1, FP8, dispatch=Dispatch(sort=L.MXQ_SORT_ALWAYS))
+    assert (so["path"], so["block_m1"], so["k_split1"], so["k_split2"]) == ("sorted", 128, 1, 1)
+    assert (so["silu"], so["combine"]) == ("stage1_epilogue", "kernel")
+    ks = fused_moe_plan(128, 2048, 1024, 8, 1, FP8, dispatch=Dispatch(k_split=2))
+    assert (ks["k_split1"], ks["k_split2"], ks["silu"], ks["combine"]) == (2, 2, "split_sum", "kernel")
+    # 256 tokens top-2 over 8 experts: 64-row self-routed blocks, SiLU fused, top-2 combine kernel
+    m256 = fused_moe_plan(256, 2048, 1024, 8, 2, FP8)
+    assert (m256["path"], m256["block_m1"], m256["k_split1"]) == ("self_routed", 64, 1)
+    assert (m256["silu"], m256["combine"]) == ("stage1_epilogue", "kernel")
+    # GPT-OSS decode (32 tokens top-4 over 128 MXFP4 experts): every block tiny, expert streaming
+    c4 = fused_moe_plan(32, 2880, 2880, 128, 4, MX, weight_layout="tiled")
+    assert (c4["path"], c4["silu"]) == ("expert_stream", "expert_stream")
+    # MXFP4 on the plain layout with K % 128 != 0: the register-staged tiles, sorted
+    mxp = fused_moe_plan(40, 2880, 2880, 8, 4, MX)
+    assert (mxp["path"], mxp["tiles"]) == ("sorted", "register")
+    assert fused_moe_plan(40, 2880, 2880, 8, 4, MX, weight_layout="tiled")["tiles"] == "ring"
+    # DeepSeek prefill (4096 tokens top-8 over 256 experts, W8A8): sorted, every class folded into
+    # the 128-row class on the 128 x 256 tile, the SiLU-and-mul with its re-quantisation and the
+    # combine as kernels
+    c5 = fused_moe_plan(4096, 7168, 2048, 256, 8, FP8, act_quant=True, weight_layout="tiled")
+    assert (c5["path"], c5["tiles"], c5["classes"]) == ("sorted", "w8a8_wide", {4})
+    assert (c5["block_m1"], c5["k_split1"], c5["silu"], c5["combine"]) == (128, 1, "kernel", "kernel")
+    # refusals, as the call's
+    lib = L.load()
+    arr = (C.c_int32 * len(L.MOE_PLAN_FIELDS))()
+    assert lib.mxq_fused_moe_plan(4, 256, 256, 8, 2, 7, 0, 0, None, arr) == L.MXQ_ERR_ARG
+    assert lib.mxq_fused_moe_plan(4, 256, 256, 8, 2, MX, 1, 0, None, arr) == L.MXQ_ERR_ARG
+    assert lib.mxq_fused_moe_plan(4, 200, 256, 8, 2, FP8, 0, 0, None, arr) == L.MXQ_ERR_SHAPE
+    assert lib.mxq_fused_moe_plan(0, 256, 256, 8, 2, FP8, 0, 0, None, arr) == L.MXQ_ERR_SHAPE
+    assert lib.mxq_fused_moe_plan(4, 256, 256, 8, 9, FP8, 0, 0, None, arr) == L.MXQ_ERR_SHAPE
+    assert lib.mxq_fused_moe_plan(4, 256, 256, 8, 2, FP8, 0, 0, None, None) == L.MXQ_ERR_NULL
