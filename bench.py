@@ -383,7 +383,20 @@ def bench_moe(name: str, steps: int, warmup: int, seed: int, layout: str = "tile
         "hbm_frac": byts / (us * 1e-6) / 1e9 / HBM_PEAK_GBS,
         "fp8_mfma_frac": flops / (us * 1e-6) / 1e12 / FP8_PEAK_TFLOPS,
         "distinct_experts": int(np.unique(w["inp"]["topk_ids"].cpu().numpy()).size),
+        "plan": _moe_plan(w["inp"], layout),
     }
+
+
+def _moe_plan(inp, layout: str):
+    """The kernel plan the timed call runs (mxq_fused_moe_plan), classes as a sorted list."""
+    from mxfp4_block_scaled_expert_amd import ops
+    from mxfp4_block_scaled_expert_amd import _lib as L
+    M, H = inp["x"].shape
+    mx = inp["kind"] == "fused_moe_mxfp4"
+    p = ops.fused_moe_plan(M, H, inp["I"], inp["E"], inp["topk"], L.MXQ_WEIGHTS_MXFP4 if mx else L.MXQ_WEIGHTS_FP8_BLOCK,
+                           act_quant=bool(inp["act_quant"]), weight_layout=layout)
+    p["classes"] = sorted(p["classes"])
+    return p
 
 
 def bench_mla_bmm(steps: int, warmup: int, tokens: int = 64):
