@@ -297,7 +297,8 @@ mxq_status mxq_moe_align(const int32_t* topk_ids, int64_t M, int32_t topk, int32
  *        most 256 routed rows, the most chunks that keep min(E, M * topk) blocks of
  *        128-column tiles within 256 tiles (one per compute unit) -- except a stage of a
  *        routing the tiles can route themselves (see `sort`) whose largest grid of 16-, 32-
- *        or 64-row blocks fits 256 workgroups: it runs unsplit on those blocks;
+ *        or 64-row blocks fits 256 workgroups: it runs unsplit on those blocks; and a routing
+ *        the expert-streaming kernels can take runs unsplit whatever `sort` and `fuse` say;
  *        1: never; 2 / 4 / 8: at most that many.  The workspace bounds the chunks to
  *        M * topk * chunks <= 2048.  Outputs agree with the unsplit call within rounding
  *        (the sums over K are grouped differently).

@@ -439,10 +439,13 @@ MoePlan plan_moe(const GemmArgs& g1, const GemmArgs& g2, int64_t M, int64_t H, i
   // Every block of the routing is tiny and the activations stay bf16: the expert-streaming
   // kernels group the routed rows by expert themselves (no sort, no block tables), stage 1 ends
   // in the SiLU-and-mul, and rows are indexed by flat routed id up to the combine.
-  p.expert_stream = !act_quant && dc.sort == MXQ_SORT_AUTO && dc.fuse == MXQ_FUSE_AUTO && p.pol.forced < 0 &&
-                    p.pol.n_live == 1 && tiny == MXQ_TINY_MFMA && R <= kStreamMaxRows && E <= kStreamMaxExperts &&
-                    I % 16 == 0 && expert_stream_lds_bytes(wfmt_w16, 1, 2 * I, H, E, R) <= kStreamMaxLds &&
-                    expert_stream_lds_bytes(wfmt_w16, 2, H, I, E, R) <= kStreamMaxLds;
+  // (Such a routing runs without a K split whatever the sort and fuse knobs say, so that the
+  // sorted path they select computes the same sums.)
+  const bool streamable = !act_quant && p.pol.forced < 0 && p.pol.n_live == 1 && tiny == MXQ_TINY_MFMA &&
+                          R <= kStreamMaxRows && E <= kStreamMaxExperts && I % 16 == 0 &&
+                          expert_stream_lds_bytes(wfmt_w16, 1, 2 * I, H, E, R) <= kStreamMaxLds &&
+                          expert_stream_lds_bytes(wfmt_w16, 2, H, I, E, R) <= kStreamMaxLds;
+  p.expert_stream = streamable && dc.sort == MXQ_SORT_AUTO && dc.fuse == MXQ_FUSE_AUTO;
   if (p.expert_stream) return p;
   // Small bf16 routings on the ring-fed tiles with no tiny-class launch: every workgroup finds
   // its block from the routing ids itself (the expert-ordered blocks the sort would lay out,
@@ -466,8 +469,10 @@ MoePlan plan_moe(const GemmArgs& g1, const GemmArgs& g2, int64_t M, int64_t H, i
   const bool gemv_runs = tiny == MXQ_TINY_GEMV && !tiled;  // the GEMV kernel writes whole sums only
   const bool can_split = !act_quant && !gemv_runs && split_cap(R) > 1;
   const bool auto_split = dc.k_split == MXQ_K_SPLIT_AUTO;
-  p.sp1 = can_split && !(auto_split && p.fill1) ? pick_split(R, E, 2 * I, H, dc.k_split) : KSplit{1, 0};
-  p.sp2 = can_split && !(auto_split && p.fill2) ? pick_split(R, E, H, I, dc.k_split) : KSplit{1, 0};
+  p.sp1 = can_split && !(auto_split && (p.fill1 || streamable)) ? pick_split(R, E, 2 * I, H, dc.k_split)
+                                                                 : KSplit{1, 0};
+  p.sp2 = can_split && !(auto_split && (p.fill2 || streamable)) ? pick_split(R, E, H, I, dc.k_split)
+                                                                 : KSplit{1, 0};
   // With bf16 activations and only the tiny-block class launched, stage 2 computes the
   // SiLU-and-mul while staging its rows (no ic1 round trip, one launch fewer).
   p.fuse_silu = !act_quant && dc.fuse == MXQ_FUSE_AUTO && p.pol.forced < 0 && p.pol.n_live == 1 &&

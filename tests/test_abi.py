@@ -253,9 +253,13 @@ def test_fused_moe_plan_host_logic():
     m256 = fused_moe_plan(256, 2048, 1024, 8, 2, FP8)
     assert (m256["path"], m256["block_m1"], m256["k_split1"]) == ("self_routed", 64, 1)
     assert (m256["silu"], m256["combine"]) == ("stage1_epilogue", "kernel")
-    # GPT-OSS decode (32 tokens top-4 over 128 MXFP4 experts): every block tiny, expert streaming
+    # GPT-OSS decode (32 tokens top-4 over 128 MXFP4 experts): every block tiny, expert streaming;
+    # with the sort kept the sorted path runs unsplit too (the same sums)
     c4 = fused_moe_plan(32, 2880, 2880, 128, 4, MX, weight_layout="tiled")
     assert (c4["path"], c4["silu"]) == ("expert_stream", "expert_stream")
+    for d in (Dispatch(sort=L.MXQ_SORT_ALWAYS), Dispatch(fuse=L.MXQ_FUSE_NONE)):
+        p = fused_moe_plan(15, 384, 512, 1, 1, FP8, dispatch=d)
+        assert (p["path"], p["classes"], p["k_split1"], p["k_split2"]) == ("sorted", {0}, 1, 1)
     # MXFP4 on the plain layout with K % 128 != 0: the register-staged tiles, sorted
     mxp = fused_moe_plan(40, 2880, 2880, 8, 4, MX)
     assert (mxp["path"], mxp["tiles"]) == ("sorted", "register")

@@ -442,3 +442,38 @@ def test_output_buffer_in_a_larger_allocation():
     assert torch.all(buf[:8] == 0) and torch.all(buf[8 + M * H:] == 0)
     with pytest.raises(ValueError):
         _run_gpu(inp, out=buf[4:4 + M * H].view(M, H))
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_random_small_routings_all_paths_agree(seed):
+    """Seeded random small bf16 routings (tokens, experts, top-k, sizes, Zipf skew, a few dropped
+    ids, FP8 or MXFP4 weights): the default call (self-routed where it applies, with its epilogue
+    folds), the call with the sort kept and the call with no fusion give the same bits, and all
+    match the oracle."""
+    rng = np.random.default_rng(1000 + seed)
+    kind = "fused_moe_mxfp4" if seed % 3 == 2 else "fused_moe_fp8"
+    E = int(rng.choice([1, 2, 5, 8, 16, 40]))
+    topk = int(rng.integers(1, min(E, 4) + 1))
+    M = int(rng.integers(1, 200))
+    H = int(rng.choice([128, 256, 384]))
+    I = int(rng.choice([128, 256, 512]))
+    spec = _small_spec(kind, M, E, topk, H, I, zipf=float(rng.choice([0.0, 0.8, 1.3])) or None)
+    inp = synth.moe_inputs(spec, seed=seed + 7, device=gpu())
+    ids = inp["topk_ids"].cpu().numpy()
+    drop = rng.random(ids.shape) < 0.03
+    if drop.any():
+        bad = np.where(rng.random(ids.shape) < 0.5, -1, E)
+        ids = np.where(drop, bad, ids).astype(np.int32)
+        inp["topk_ids"] = torch.from_numpy(ids).to(gpu())
+    keep = np.where((ids < 0) | (ids >= E), 0, ids).astype(np.int32)
+    w = inp["topk_weights"].clone()
+    w[torch.from_numpy((ids < 0) | (ids >= E)).to(gpu())] = 0.0
+    want = _run_oracle(dict(inp, topk_ids=torch.from_numpy(keep).to(gpu()), topk_weights=w))
+    outs = [_run_gpu(inp, ops.Dispatch(sort=so, fuse=fu))
+            for so, fu in ((mx.MXQ_SORT_AUTO, mx.MXQ_FUSE_AUTO), (mx.MXQ_SORT_ALWAYS, mx.MXQ_FUSE_AUTO),
+                           (mx.MXQ_SORT_AUTO, mx.MXQ_FUSE_NONE))]
+    torch.cuda.synchronize()
+    what = f"seed {seed}: {kind} M={M} E={E} topk={topk} H={H} I={I}"
+    for o in outs[1:]:
+        assert torch.equal(o.view(torch.int16), outs[0].view(torch.int16)), what
+    assert_bf16_close(bf16_bits(outs[0]), want, what=what)
