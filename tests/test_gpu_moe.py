@@ -444,12 +444,12 @@ def test_output_buffer_in_a_larger_allocation():
         _run_gpu(inp, out=buf[4:4 + M * H].view(M, H))
 
 
-@pytest.mark.parametrize("seed", range(12))
+@pytest.mark.parametrize("seed", range(24))
 def test_random_small_routings_all_paths_agree(seed):
     """Seeded random small bf16 routings (tokens, experts, top-k, sizes, Zipf skew, a few dropped
-    ids, FP8 or MXFP4 weights): the default call (self-routed where it applies, with its epilogue
-    folds), the call with the sort kept and the call with no fusion give the same bits, and all
-    match the oracle."""
+    ids, FP8 or MXFP4 weights, per-block / forced-class / layer-average dispatch): the default
+    call (self-routed where it applies, with its epilogue folds), the call with the sort kept and
+    the call with no fusion give the same bits, and all match the oracle."""
     rng = np.random.default_rng(1000 + seed)
     kind = "fused_moe_mxfp4" if seed % 3 == 2 else "fused_moe_fp8"
     E = int(rng.choice([1, 2, 5, 8, 16, 40]))
@@ -469,11 +469,13 @@ def test_random_small_routings_all_paths_agree(seed):
     w = inp["topk_weights"].clone()
     w[torch.from_numpy((ids < 0) | (ids >= E)).to(gpu())] = 0.0
     want = _run_oracle(dict(inp, topk_ids=torch.from_numpy(keep).to(gpu()), topk_weights=w))
-    outs = [_run_gpu(inp, ops.Dispatch(sort=so, fuse=fu))
+    mode = [{}, {}, dict(mode=mx.MXQ_DISPATCH_FORCED, forced_class=int(rng.integers(0, 5))),
+            dict(mode=mx.MXQ_DISPATCH_LAYER_AVERAGE)][seed % 4]
+    outs = [_run_gpu(inp, ops.Dispatch(sort=so, fuse=fu, **mode))
             for so, fu in ((mx.MXQ_SORT_AUTO, mx.MXQ_FUSE_AUTO), (mx.MXQ_SORT_ALWAYS, mx.MXQ_FUSE_AUTO),
                            (mx.MXQ_SORT_AUTO, mx.MXQ_FUSE_NONE))]
     torch.cuda.synchronize()
-    what = f"seed {seed}: {kind} M={M} E={E} topk={topk} H={H} I={I}"
+    what = f"seed {seed}: {kind} M={M} E={E} topk={topk} H={H} I={I} {mode}"
     for o in outs[1:]:
         assert torch.equal(o.view(torch.int16), outs[0].view(torch.int16)), what
     assert_bf16_close(bf16_bits(outs[0]), want, what=what)
