@@ -252,3 +252,27 @@ def test_block_linear_zero_rows():
     d = _block_case(1, 256, 256, 128, seed=4)
     out = ops.block_fp8_linear(d["x"][:0], d["w"], [128, 128], d["sw"])
     assert out.shape == (0, 256)
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_random_per_tensor_shapes_both_kernels_and_oracle(seed):
+    """Seeded random per-tensor W8A16 shapes (M 1..300, N 16..700, K a multiple of 32 up to
+    1024, with and without bias): a batched call large enough to run the register-staged
+    kernel equals, entry by entry, the 2-D calls (the ring-fed kernel where the grid fits the
+    GPU and K > 128), and both match the oracle."""
+    rng = np.random.default_rng(500 + seed)
+    M = int(rng.integers(1, 301))
+    N = int(rng.integers(1, 44)) * 16
+    K = int(rng.integers(1, 33)) * 32
+    B = 40
+    d = synth.batched_w8a16(B, M, N, K, seed=seed + 3, device=gpu(), has_bias=bool(seed % 2))
+    out = ops.fp8_scaled_bmm(d["a"], d["w"], d["scale"], d["bias"])
+    torch.cuda.synchronize()
+    for z in (0, B // 2, B - 1):
+        ref = ops.fp8_scaled_mm(d["a"][z], d["w"][z], d["scale"][z].reshape(1),
+                                None if d["bias"] is None else d["bias"][z])
+        torch.cuda.synchronize()
+        assert torch.equal(out[z].view(torch.int16), ref.view(torch.int16)), f"M={M} N={N} K={K} entry {z}"
+    want = _oracle_bmm(dict(d, a=d["a"][:2], w=d["w"][:2], scale=d["scale"][:2]),
+                       None if d["bias"] is None else f32(d["bias"][:2]))
+    assert_bf16_close(bf16_bits(out[:2]), want, what=f"random bmm M={M} N={N} K={K}")
