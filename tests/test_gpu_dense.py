@@ -276,3 +276,20 @@ def test_random_per_tensor_shapes_both_kernels_and_oracle(seed):
     want = _oracle_bmm(dict(d, a=d["a"][:2], w=d["w"][:2], scale=d["scale"][:2]),
                        None if d["bias"] is None else f32(d["bias"][:2]))
     assert_bf16_close(bf16_bits(out[:2]), want, what=f"random bmm M={M} N={N} K={K}")
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_random_block_linear_shapes(seed):
+    """Seeded random block-FP8 W8A8 shapes (M 1..600 across the 128-row switch to the large
+    tile, N 16..1024 including partial 256- and 128-wide column tiles, K a multiple of 128 up
+    to 1024, 128x128 or 1x128 weight blocks, with and without bias) against the oracle."""
+    rng = np.random.default_rng(900 + seed)
+    M = int(rng.integers(1, 601))
+    N = int(rng.integers(1, 65)) * 16
+    K = int(rng.integers(1, 9)) * 128
+    block_n = [128, 1][seed % 2]
+    bias = torch.float32 if seed % 3 else None
+    d = _block_case(M, N, K, block_n, seed=seed + 11, bias_dtype=bias)
+    out = ops.block_fp8_linear(d["x"], d["w"], [block_n, 128], d["sw"], bias=d["bias"])
+    torch.cuda.synchronize()
+    assert_bf16_close(bf16_bits(out), _oracle_block(d), what=f"random block linear {M}x{N}x{K} bn={block_n}")
