@@ -455,8 +455,12 @@ def test_random_small_routings_all_paths_agree(seed):
     E = int(rng.choice([1, 2, 5, 8, 16, 40]))
     topk = int(rng.integers(1, min(E, 4) + 1))
     M = int(rng.integers(1, 200))
-    H = int(rng.choice([128, 256, 384]))
-    I = int(rng.choice([128, 256, 512]))
+    if kind == "fused_moe_mxfp4":  # ragged K steps (multiples of 32)
+        H = int(rng.choice([96, 160, 256, 352]))
+        I = int(rng.choice([96, 160, 256, 352]))
+    else:
+        H = int(rng.choice([128, 256, 384]))
+        I = int(rng.choice([128, 256, 512]))
     spec = _small_spec(kind, M, E, topk, H, I, zipf=float(rng.choice([0.0, 0.8, 1.3])) or None)
     inp = synth.moe_inputs(spec, seed=seed + 7, device=gpu())
     ids = inp["topk_ids"].cpu().numpy()
@@ -479,3 +483,21 @@ def test_random_small_routings_all_paths_agree(seed):
     for o in outs[1:]:
         assert torch.equal(o.view(torch.int16), outs[0].view(torch.int16)), what
     assert_bf16_close(bf16_bits(outs[0]), want, what=what)
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_random_w8a8_routings(seed):
+    """Seeded random W8A8 routings (tokens 1..600 so that blocks fill every class and the
+    128-row tile, 2..64 experts, top-1..top-8, Zipf skew) against the oracle (the requantised
+    end-to-end bar; the stages are held to the strict bar in the stage-by-stage tests)."""
+    rng = np.random.default_rng(3000 + seed)
+    E = int(rng.choice([2, 6, 16, 64]))
+    topk = int(rng.integers(1, min(E, 8) + 1))
+    M = int(rng.integers(1, 601))
+    H = int(rng.choice([128, 256, 512]))
+    I = int(rng.choice([128, 256, 384]))
+    spec = _small_spec("fused_moe_fp8", M, E, topk, H, I, zipf=float(rng.choice([0.0, 1.1])) or None, act_quant=True)
+    inp = synth.moe_inputs(spec, seed=seed + 17, device=gpu())
+    out = _run_gpu(inp)
+    torch.cuda.synchronize()
+    assert_bf16_close_requant(bf16_bits(out), _run_oracle(inp), what=f"w8a8 seed {seed}: M={M} E={E} topk={topk} H={H} I={I}")
