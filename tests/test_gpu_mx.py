@@ -82,6 +82,23 @@ def test_mx_linear_ragged_shapes(M, N, K, w_format):
     assert_bf16_close(bf16_bits(out), _oracle_linear(d), what=f"mx {w_format} {M}x{N}x{K}")
 
 
+@pytest.mark.parametrize("seed", range(8))
+def test_mx_linear_random_shapes(seed):
+    """Seeded random MX linear shapes (M 1..600 across the 128-row tile switch, N 8..1024, K a
+    multiple of 128 up to 1536, MXFP4 or MXFP8 weights, with and without bias) against the
+    oracle."""
+    rng = np.random.default_rng(700 + seed)
+    M = int(rng.integers(1, 601))
+    N = int(rng.integers(1, 129)) * 8
+    K = int(rng.integers(1, 13)) * 128
+    w_format = ["e2m1", "e4m3"][seed % 2]
+    d = synth.mx_linear(M, N, K, seed=seed + 21, device=gpu(), w_format=w_format,
+                        bias_dtype=torch.float32 if seed % 3 else None)
+    out = ops.mx_linear(d["x"], d["w"], d["sw"], w_format, bias=d["bias"])
+    torch.cuda.synchronize()
+    assert_bf16_close(bf16_bits(out), _oracle_linear(d), what=f"random mx {w_format} {M}x{N}x{K}")
+
+
 @pytest.mark.parametrize("w_format", ["e2m1", "e4m3"])
 def test_mx_linear_prequantised_bf16_bias_and_3d(w_format):
     d = synth.mx_linear(34, 384, 640, seed=9, device=gpu(), w_format=w_format, bias_dtype=torch.bfloat16)
