@@ -303,7 +303,7 @@ mxq_status mxq_moe_align(const int32_t* topk_ids, int64_t M, int32_t topk, int32
  *        M * topk * chunks <= 2048.  Outputs agree with the unsplit call within rounding
  *        (the sums over K are grouped differently).
  *   sort MXQ_SORT_AUTO: small routings may skip the expert sort -- the expert-streaming case
- *        above, and, with bf16 activations, no tiny class, at most 1024 routed rows and
+ *        above, and, with bf16 activations, no tiny class, at most 2048 routed rows and
  *        E <= 512, when both stages run the direct-to-LDS 16/32/64/128-row tiles (K a
  *        multiple of 32 up to 16384, 16-byte aligned rows; plain MXFP4: K a multiple of 128),
  *        tiles that find their own rows from topk_ids (each expert's rows in the sort's

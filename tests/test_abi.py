@@ -253,6 +253,10 @@ def test_fused_moe_plan_host_logic():
     m256 = fused_moe_plan(256, 2048, 1024, 8, 2, FP8)
     assert (m256["path"], m256["block_m1"], m256["k_split1"]) == ("self_routed", 64, 1)
     assert (m256["silu"], m256["combine"]) == ("stage1_epilogue", "kernel")
+    # the largest self-routed routing is 2048 routed rows (512 tokens top-4); one token more sorts
+    r2k = fused_moe_plan(512, 2048, 1024, 64, 4, FP8)
+    assert (r2k["path"], r2k["block_m1"], r2k["k_split1"]) == ("self_routed", 64, 1)
+    assert fused_moe_plan(513, 2048, 1024, 64, 4, FP8)["path"] == "sorted"
     # GPT-OSS decode (32 tokens top-4 over 128 MXFP4 experts): every block tiny, expert streaming;
     # with the sort kept the sorted path runs unsplit too (the same sums)
     c4 = fused_moe_plan(32, 2880, 2880, 128, 4, MX, weight_layout="tiled")

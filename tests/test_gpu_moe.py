@@ -15,6 +15,7 @@ import pytest
 import torch
 
 import mxfp4_block_scaled_expert_amd as mx
+from mxfp4_block_scaled_expert_amd import _lib as L
 from mxfp4_block_scaled_expert_amd import ops, synth
 from oracle import moe as OM
 from oracle.align import moe_align as oracle_align
@@ -308,14 +309,16 @@ def _auto_and_sorted(inp, layout="plain", **d):
     return outs
 
 
-@pytest.mark.parametrize("case", ["small_blocks", "multi_block_expert", "r1024", "e512_forced", "r1024_e512", "mxfp4"])
+@pytest.mark.parametrize("case", ["small_blocks", "multi_block_expert", "r1024", "e512_forced", "r2048_e512",
+                                  "r2048_mxfp4", "mxfp4"])
 def test_self_routed_tiles_match_sorted(case):
     """Small bf16 routings without a tiny class skip the sort: each tile finds its rows from the
     routing ids (the sort's expert order, cut into 64-row blocks).  Every row's products are the
     sorted path's, so the outputs equal it bit for bit (and the oracle's within tolerance): the
     small-block routing (empty experts, blocks in several classes), an expert holding several
-    128-row blocks, 1024 routed rows, E = 512 with forced classes, and MXFP4 on both weight
-    layouts."""
+    128-row blocks, 1024 routed rows, E = 512 with forced classes, the largest self-routed
+    routing (2048 routed rows over 512 experts), 2048 MXFP4 routed rows, and MXFP4 on both
+    weight layouts."""
     runs = [{}]
     if case == "small_blocks":
         inp = synth.moe_inputs(SMALL_BLOCKS, seed=1003, device=gpu())
@@ -328,16 +331,24 @@ def test_self_routed_tiles_match_sorted(case):
     elif case == "e512_forced":
         inp = synth.moe_inputs(_small_spec("fused_moe_fp8", 300, 512, 2, 128, 128), seed=63, device=gpu())
         runs = [dict(tiny_max_rows=0)] + [dict(mode=mx.MXQ_DISPATCH_FORCED, forced_class=c) for c in (1, 2, 3, 4)]
-    elif case == "r1024_e512":
-        # the largest self-routed routing: 1024 routed rows over 512 experts (its routing ids and
+    elif case == "r2048_e512":
+        # the largest self-routed routing: 2048 routed rows over 512 experts (its routing ids and
         # counts fill the most LDS)
-        inp = synth.moe_inputs(_small_spec("fused_moe_fp8", 512, 512, 2, 128, 128, zipf=1.0), seed=64, device=gpu())
+        inp = synth.moe_inputs(_small_spec("fused_moe_fp8", 1024, 512, 2, 128, 128, zipf=1.0), seed=64, device=gpu())
         runs = [dict(tiny_max_rows=0), dict(mode=mx.MXQ_DISPATCH_FORCED, forced_class=4)]
+    elif case == "r2048_mxfp4":
+        inp = synth.moe_inputs(_small_spec("fused_moe_mxfp4", 512, 32, 4, 256, 256), seed=65, device=gpu())
     else:
         inp = synth.moe_inputs(_small_spec("fused_moe_mxfp4", 40, 8, 4, 2880, 2880), seed=13, device=gpu())
         runs = [{}, dict(mode=mx.MXQ_DISPATCH_FORCED, forced_class=1), dict(k_split=1)]
     want = _run_oracle(inp)
+    M, H = inp["x"].shape
+    wts = L.MXQ_WEIGHTS_MXFP4 if inp["kind"] == "fused_moe_mxfp4" else L.MXQ_WEIGHTS_FP8_BLOCK
     for d in runs:
+        # (MXFP4 with K = 2880 self-routes on the tiled layout only)
+        plan = ops.fused_moe_plan(M, H, inp["I"], inp["E"], inp["topk"], wts, dispatch=ops.Dispatch(**d),
+                                  weight_layout="tiled" if case == "mxfp4" else "plain")
+        assert plan["path"] == "self_routed", (case, d, plan)
         auto, srt = _auto_and_sorted(inp, **d)
         assert torch.equal(auto.view(torch.int16), srt.view(torch.int16)), (case, d)
         assert_bf16_close(bf16_bits(auto), want, what=f"self-routed {case} {d}")
