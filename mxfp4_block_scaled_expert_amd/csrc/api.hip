@@ -68,9 +68,10 @@ constexpr int64_t kStreamMaxRows = 4096;
 constexpr int32_t kStreamMaxExperts = 512;
 constexpr size_t kStreamMaxLds = 80 * 1024;
 #ifndef MXQ_DENSE_BIG_SHAPE
-#define MXQ_DENSE_BIG_SHAPE 0
+#define MXQ_DENSE_BIG_SHAPE (-1)
 #endif
-constexpr int kDenseBigShape = MXQ_DENSE_BIG_SHAPE;  // tile shape of the large dense W8A8 GEMM
+// tile shape of the large dense W8A8 GEMM: -1 picks it from the grid (dense_big_shape)
+constexpr int kDenseBigShape = MXQ_DENSE_BIG_SHAPE;
 
 #ifndef MXQ_DENSE_RING
 #define MXQ_DENSE_RING 1
@@ -134,6 +135,20 @@ constexpr int64_t kWideTileN = 256;
 int64_t wide_tile_columns(int64_t N) {
   const int64_t tail = N % kWideTileN;
   return (tail != 0 && tail <= kWideTileN / 2) ? N - tail : N;
+}
+
+// Tile shape of the dense direct-to-LDS W8A8 GEMM from the grid it gives: each tile runs its K
+// range as one serial chain, so until the 256 compute units are full, more and smaller tiles
+// finish sooner -- the 128 x 128 three-stage tile when its tiles fit one round, else the
+// 128 x 256 three-stage tile when its tiles do, else the 256 x 256 two-stage tile (interleaved
+// on the box, K = 7168: M = 2048, N = 2048 92 -> 48 us; M = 4096, N = 2048 93 -> 68 us; M = 512,
+// N = 7168, K = 2048 31 -> 19 us; 2048 x 7168 x 2048 stays on the 256 x 256 tile, 34 us against
+// 41 on 128 x 256).  Shapes as launch_gemm_w8a8_big numbers them.
+int dense_big_shape(int64_t M, int64_t N) {
+  if (kDenseBigShape >= 0) return kDenseBigShape;
+  if (cdiv(M, int64_t(128)) * cdiv(N, int64_t(128)) <= 256) return 3;
+  if (cdiv(M, int64_t(128)) * cdiv(N, int64_t(256)) <= 256) return 1;
+  return 0;
 }
 
 // Columns [n0, N) of a GEMM as a problem of their own: weights, weight-scale grid rows, bias
@@ -861,13 +876,14 @@ mxq_status mxq_block_fp8_linear(const void* A, int32_t a_dtype, const float* a_s
   g.K = K;
   if ((block_n == 128 || block_n == 1) && M > 128 && K <= 16384 && int64_t(M) * lqa < (int64_t(1) << 32) &&
       N * K < (int64_t(1) << 32)) {
-    // the wide tile for the column tiles of width 256, the 128-wide tile for a narrow last one
-    const int64_t nw = wide_tile_columns(N);
+    // a 256-wide tile for the column tiles of width 256 and the register-staged 128-wide tile
+    // for a narrow last one; the 128 x 128 tile for all of N
+    const int shape = dense_big_shape(M, N);
+    const int64_t nw = shape >= 2 ? N : wide_tile_columns(N);
     if (nw > 0) {
       GemmArgs gw = g;
       gw.N = nw;
-      launch_gemm_w8a8_big(gw, ROWS_DENSE, kDenseBigShape, false, cdiv(M, int64_t(big_tile_rows(kDenseBigShape))),
-                           st);
+      launch_gemm_w8a8_big(gw, ROWS_DENSE, shape, false, cdiv(M, int64_t(big_tile_rows(shape))), st);
     }
     if (nw < N) launch_gemm_w8a8(column_slice(g, nw, false), ROWS_DENSE, 0, false, cdiv(M, int64_t(128)), st);
   } else {
