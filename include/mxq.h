@@ -141,10 +141,18 @@ mxq_status mxq_fp8_scaled_bmm(const void* A, int64_t batch, int64_t M, int64_t K
  *             MXQ_DTYPE_BF16 (page [C], fp8_utils.py listing: the output takes bf16 for
  *             pre-quantised input and the input's dtype otherwise, bf16 for every input
  *             this entry point accepts); anything else -> MXQ_ERR_DTYPE.
- *   workspace bf16 input needs mxq_block_fp8_linear_workspace_size(M, K, a_dtype) bytes
- *             (the quantised activations); e4m3 input needs none (may be NULL).
- *   K must be a multiple of 128.  FP8 matrix cores (16x16x128 per K block), fp32 accumulation. */
-size_t mxq_block_fp8_linear_workspace_size(int64_t M, int64_t K, int32_t a_dtype);
+ *   workspace mxq_block_fp8_linear_workspace_size(M, N, K, a_dtype) bytes, or MXQ_ERR_WORKSPACE:
+ *             bf16 input's quantised activations, and for the few-row cases below the fp32
+ *             partial sums of a K split (at most 8 MiB); NULL allowed where the size is 0.
+ *   K must be a multiple of 128.  FP8 matrix cores (16x16x128 per K block), fp32 accumulation.
+ *   Few rows -- M <= 64 where the row tiles would run at most 32 workgroups, 96 for M <= 8
+ *   (ceil(M / t) * ceil(N / 128), t = 16, 32 or 64 rows for M <= 16, 32, 64) -- with
+ *   N * K < 2^32 and K <= 15744 run on the weight-streaming kernel (tiles of 4 or 8 rows); that
+ *   path may cut K into chunks of whole 128-wide blocks whose partial sums are added in chunk
+ *   order, so its sums are grouped differently from the tiles' (the result agrees within
+ *   rounding; path and split depend on M, N and K only, and with 1 x 128 weight blocks the
+ *   tiles run and the partial-sum space goes unused). */
+size_t mxq_block_fp8_linear_workspace_size(int64_t M, int64_t N, int64_t K, int32_t a_dtype);
 mxq_status mxq_block_fp8_linear(const void* A, int32_t a_dtype, const float* a_scale, int64_t M, int64_t K,
                                 int64_t lda, const void* W, int64_t N, const float* w_scale, int64_t ws_stride0,
                                 int64_t ws_stride1, int32_t block_n, int32_t block_k, const void* bias,
@@ -157,12 +165,15 @@ mxq_status mxq_block_fp8_linear(const void* A, int32_t a_dtype, const float* a_s
  * the same arguments minus the workspace, same kernels and bit-identical results.  A bf16
  * input's quantised codes and scales go to a static device array of
  * MXQ_NOALLOC_SCRATCH_BYTES (32 MiB) that the library holds on every GPU it runs on until the
- * process ends; inputs needing more (M * K + 4 * M * K / 128 bytes, 256-byte aligned parts,
- * i.e. about M * K <= 32.5 M) return MXQ_ERR_SCRATCH before anything is enqueued.  The call
+ * process ends, and so do the K-split partial sums of the few-row path; inputs needing more than
+ * the array (mxq_block_fp8_linear_workspace_size bytes: M * K + 4 * M * K / 128 for bf16
+ * input, i.e. about M * K <= 32.5 M, plus at most 8 MiB of partial sums) return
+ * MXQ_ERR_SCRATCH before anything is enqueued.  The call
  * allocates nothing.  Every call on one GPU shares that GPU's array: calls that may overlap
  * on one GPU (different streams, no ordering between them) race and must not be issued; calls
  * on one stream are ordered and safe.  Nothing in the array needs to start at zero (the
- * quantiser writes all of it that the GEMM reads).  e4m3 input uses no scratch. */
+ * quantiser and the split GEMM write all of it that is read).  e4m3 input uses the array only
+ * for those partial sums. */
 #define MXQ_NOALLOC_SCRATCH_BYTES (32u << 20)
 mxq_status mxq_block_fp8_linear_noalloc(const void* A, int32_t a_dtype, const float* a_scale, int64_t M, int64_t K,
                                         int64_t lda, const void* W, int64_t N, const float* w_scale,

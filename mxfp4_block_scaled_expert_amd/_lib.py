@@ -82,7 +82,7 @@ SIGNATURES = {
     "mxq_fp8_scaled_mm": (_i32, [_p, _i64, _i64, _i64, _p, _i64, _p, _p, _i32, _p, _i64, _p]),
     "mxq_fp8_scaled_bmm": (_i32, [_p, _i64, _i64, _i64, _i64, _i64, _p, _i64, _i64, _p, _i64, _p, _i32, _i64,
                                    _p, _i64, _i64, _p]),
-    "mxq_block_fp8_linear_workspace_size": (_sz, [_i64, _i64, _i32]),
+    "mxq_block_fp8_linear_workspace_size": (_sz, [_i64, _i64, _i64, _i32]),
     "mxq_block_fp8_linear": (_i32, [_p, _i32, _p, _i64, _i64, _i64, _p, _i64, _p, _i64, _i64, _i32, _i32,
                                      _p, _i32, _p, _i32, _i64, _p, _sz, _p]),
     "mxq_block_fp8_linear_noalloc": (_i32, [_p, _i32, _p, _i64, _i64, _i64, _p, _i64, _p, _i64, _i64, _i32,

@@ -725,7 +725,7 @@ const char* mxq_status_string(mxq_status s) {
   }
 }
 
-int32_t mxq_abi_version(void) { return 11; }
+int32_t mxq_abi_version(void) { return 12; }
 
 mxq_status mxq_init(int32_t device) {
   if (hipSetDevice(device) != hipSuccess) return MXQ_ERR_ARCH;
@@ -820,9 +820,61 @@ mxq_status mxq_fp8_scaled_bmm(const void* A, int64_t batch, int64_t M, int64_t K
   return launch_status();
 }
 
-size_t mxq_block_fp8_linear_workspace_size(int64_t M, int64_t K, int32_t a_dtype) {
+// Dense W8A8 GEMMs of few rows stream their weights through the tiny-block kernel (tiles of 4
+// or 8 rows and 64 or 128 columns) rather than the 16..128-row tiles: they are bound by reading
+// W once, which the tiles do on far fewer workgroups -- while the tiles' grid would hold at
+// most kSkDenseTileGrid workgroups (kSkDenseTileGrid8 for up to 8 rows, one row tile here)
+// and M <= kSkDenseMaxRows (interleaved on the box: 1 x 2048 x 7168 52.2 -> 12.4 us,
+// 13 x 2048 x 4096 24.0 -> 14.2, 32 x 1024 x 7168 39.7 -> 18.9, 64 x 2048 x 7168 62.0 -> 39.5,
+// 8 x 7168 x 2048 19.2 -> 14.9; the tiles stay where their grid is wider: 16 x 24576 x 1536
+// 16.9 against 26.1, 8 x 24576 x 1536 16.8 against 19.8, 64 x 7168 x 2048 22.3 against 27.3;
+// the bound 96 sits between the measured 56-workgroup win and 192-workgroup loss).  K is cut into S chunks (whole 128-column steps, at least four per
+// chunk) until the grid reaches kSkDenseWorkgroups; the chunks' fp32 partial sums sit in the
+// workspace and one more kernel adds them in chunk order.
+#ifndef MXQ_SK_DENSE_MAX
+#define MXQ_SK_DENSE_MAX 64
+#endif
+constexpr int64_t kSkDenseTileGrid = 32, kSkDenseTileGrid8 = 96;
+#ifndef MXQ_SK_DENSE_WG
+#define MXQ_SK_DENSE_WG 512
+#endif
+constexpr int64_t kSkDenseMaxRows = MXQ_SK_DENSE_MAX;
+constexpr int64_t kSkDenseWorkgroups = MXQ_SK_DENSE_WG;
+constexpr size_t kSkDenseMaxPartial = size_t(8) << 20;  // partial-sum bytes at most
+
+struct DenseSkinny {
+  bool on;
+  int32_t split;       // S
+  int64_t chunk;       // K elements per chunk
+  size_t partial_bytes;
+};
+
+DenseSkinny dense_skinny_plan(int64_t M, int64_t N, int64_t K) {
+  DenseSkinny p{false, 1, K, 0};
+  if (kSkDenseMaxRows <= 0 || M < 1 || M > kSkDenseMaxRows || N < 1 || K < 128 || K % 128 != 0 ||
+      N * K >= (int64_t(1) << 32) || skinny_lds_bytes(W_E4M3_BLOCK, true, K) > kSkinnyMaxLds)
+    return p;
+  if (cdiv(M, tile_rows(dense_tile_for(M))) * cdiv(N, int64_t(128)) > (M <= 8 ? kSkDenseTileGrid8 : kSkDenseTileGrid))
+    return p;
+  p.on = true;
+  const int64_t steps = K / 128;
+  const int64_t wgs = cdiv(M, int64_t(skinny_dense_rows(N, K))) * skinny_dense_col_tiles(N);
+  while (p.split < 8 && wgs * p.split * 2 <= kSkDenseWorkgroups && steps >= 8 * p.split &&
+         size_t(4) * 2 * p.split * M * N <= kSkDenseMaxPartial)
+    p.split *= 2;
+  p.chunk = cdiv(steps, int64_t(p.split)) * 128;
+  p.partial_bytes = p.split > 1 ? align256(sizeof(float) * p.split * M * N) : 0;
+  return p;
+}
+
+size_t block_linear_quant_bytes(int64_t M, int64_t K, int32_t a_dtype) {
   if (a_dtype != MXQ_DTYPE_BF16 || M <= 0 || K <= 0) return 0;
   return align256(size_t(M) * K) + align256(sizeof(float) * M * (K / 128));
+}
+
+size_t mxq_block_fp8_linear_workspace_size(int64_t M, int64_t N, int64_t K, int32_t a_dtype) {
+  if (M <= 0 || N <= 0 || K <= 0 || (a_dtype != MXQ_DTYPE_BF16 && a_dtype != MXQ_DTYPE_E4M3)) return 0;
+  return block_linear_quant_bytes(M, K, a_dtype) + dense_skinny_plan(M, N, K).partial_bytes;
 }
 
 mxq_status mxq_block_fp8_linear(const void* A, int32_t a_dtype, const float* a_scale, int64_t M, int64_t K,
@@ -846,9 +898,9 @@ mxq_status mxq_block_fp8_linear(const void* A, int32_t a_dtype, const float* a_s
   const uint8_t* qa = static_cast<const uint8_t*>(A);
   const float* sa = a_scale;
   int64_t lqa = lda;
+  const size_t need = mxq_block_fp8_linear_workspace_size(M, N, K, a_dtype);
+  if (need > 0 && (!workspace || workspace_bytes < need)) return MXQ_ERR_WORKSPACE;
   if (a_dtype == MXQ_DTYPE_BF16) {
-    const size_t need = mxq_block_fp8_linear_workspace_size(M, K, a_dtype);
-    if (!workspace || workspace_bytes < need) return MXQ_ERR_WORKSPACE;
     uint8_t* q = static_cast<uint8_t*>(workspace);
     float* s = reinterpret_cast<float*>(q + align256(size_t(M) * K));
     launch_quant_1x128(static_cast<const uint16_t*>(A), M, K, lda, q, K, s, st);
@@ -874,7 +926,22 @@ mxq_status mxq_block_fp8_linear(const void* A, int32_t a_dtype, const float* a_s
   g.M = M;
   g.N = N;
   g.K = K;
-  if ((block_n == 128 || block_n == 1) && M > 128 && K <= 16384 && int64_t(M) * lqa < (int64_t(1) << 32) &&
+  const DenseSkinny sk = dense_skinny_plan(M, N, K);
+  if (block_n == 128 && sk.on && int64_t(M) * lqa < (int64_t(1) << 32)) {
+    if (sk.split > 1) {
+      float* part = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + block_linear_quant_bytes(M, K, a_dtype));
+      GemmArgs gs = g;
+      gs.out = part;
+      gs.ldo = N;
+      gs.k_split = sk.split;
+      gs.k_chunk = sk.chunk;
+      gs.split_stride = M * N;
+      launch_skinny_dense(gs, true, st);
+      launch_dense_split_sum(part, sk.split, M, N, static_cast<uint16_t*>(out), ldo, st);
+    } else {
+      launch_skinny_dense(g, false, st);
+    }
+  } else if ((block_n == 128 || block_n == 1) && M > 128 && K <= 16384 && int64_t(M) * lqa < (int64_t(1) << 32) &&
       N * K < (int64_t(1) << 32)) {
     // a 256-wide tile for the column tiles of width 256 and the register-staged 128-wide tile
     // for a narrow last one; the 128 x 128 tile for all of N
@@ -902,7 +969,7 @@ mxq_status mxq_block_fp8_linear_noalloc(const void* A, int32_t a_dtype, const fl
   if (block_k != 128 || (block_n != 1 && block_n != 128)) return MXQ_ERR_BLOCK;
   if (a_dtype != MXQ_DTYPE_BF16 && a_dtype != MXQ_DTYPE_E4M3) return MXQ_ERR_DTYPE;
   if (M < 0 || N < 0 || K < 0 || K % 128 != 0) return MXQ_ERR_SHAPE;
-  const size_t need = mxq_block_fp8_linear_workspace_size(M, K, a_dtype);
+  const size_t need = mxq_block_fp8_linear_workspace_size(M, N, K, a_dtype);
   if (need > size_t(MXQ_NOALLOC_SCRATCH_BYTES)) return MXQ_ERR_SCRATCH;
   void* ws = nullptr;
   if (need > 0 && M > 0 && N > 0) {

@@ -100,7 +100,8 @@ __global__ __launch_bounds__(256, (SkinnyShape<WFMT, A_E4M3>::W)) void skinny_ke
   const int64_t nt = rest - tile * ntiles;
   if (tile >= grid_blocks) return;
   TileInfo t;
-  if (!tile_info<1, MODE>(a, tile, t)) return;
+  // dense: a tile is AR consecutive rows (one pass); routed: a tile is one expert block
+  if (!tile_info<(MODE == ROWS_DENSE ? AR : 1), MODE>(a, tile, t)) return;
 
   const SkinnyLds L = skinny_lds_layout(MX, A_E4M3, K, G, AR);
   const int nsteps = L.kpad / KSTEP;
@@ -408,6 +409,59 @@ static void launch_skinny_mode(const GemmArgs& a, int wfmt, bool a_e4m3, bool ou
     launch_skinny_t<W_E4M3_BLOCK, true, MODE>(a, out_f32, gb, st);
   else
     launch_skinny_t<W_E4M3_BLOCK, false, MODE>(a, out_f32, gb, st);
+}
+
+// Dense W8A8 rows (e4m3 activations and weights in the plain layout, 128 x 128 weight blocks):
+// tiles of AR rows (8, or 4 when eight rows of K would pass the LDS cap), all launched at once.
+int skinny_dense_rows(int64_t N, int64_t K) { return skinny_rows_t<W_E4M3_BLOCK, true>(K, skinny_groups(N)); }
+
+int64_t skinny_dense_col_tiles(int64_t N) { return cdiv(N, int64_t(64 * skinny_groups(N))); }
+
+void launch_skinny_dense(const GemmArgs& a, bool out_f32, hipStream_t st) {
+  if (a.M <= 0 || a.N <= 0) return;
+  const int ar = skinny_dense_rows(a.N, a.K);
+  const int64_t tiles = cdiv(a.M, int64_t(ar));
+  if (skinny_groups(a.N) == 2) {
+    if (ar == 8) launch_skinny_ar<W_E4M3_BLOCK, true, ROWS_DENSE, false, 8, 2, 3>(a, out_f32, tiles, st);
+    else launch_skinny_ar<W_E4M3_BLOCK, true, ROWS_DENSE, false, 4, 2, 3>(a, out_f32, tiles, st);
+  } else {
+    if (ar == 8) launch_skinny_ar<W_E4M3_BLOCK, true, ROWS_DENSE, false, 8, 1, 4>(a, out_f32, tiles, st);
+    else launch_skinny_ar<W_E4M3_BLOCK, true, ROWS_DENSE, false, 4, 1, 4>(a, out_f32, tiles, st);
+  }
+}
+
+// out[m, n] = bf16(sum over chunks c = 0 .. S-1, in that order, of part[c][m][n]); the bias rode
+// on chunk 0.  Four columns per thread when N is a multiple of four.
+__global__ __launch_bounds__(256) void dense_split_sum_kernel(const float* __restrict__ part, int32_t S, int64_t M,
+                                                              int64_t N, uint16_t* __restrict__ out, int64_t ldo) {
+  const int64_t slice = M * N;
+  const bool vec = (N & 3) == 0;
+  const int64_t per = vec ? 4 : 1;
+  const int64_t i = (int64_t(blockIdx.x) * 256 + threadIdx.x) * per;
+  if (i >= slice) return;
+  const int64_t m = i / N, n = i - m * N;
+  if (vec) {
+    f32x4 acc = *reinterpret_cast<const f32x4*>(part + i);
+    for (int c = 1; c < S; ++c) {
+      const f32x4 v = *reinterpret_cast<const f32x4*>(part + c * slice + i);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) acc[r] += v[r];
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) out[m * ldo + n + r] = f2bf(acc[r]);
+  } else {
+    float acc = part[i];
+    for (int c = 1; c < S; ++c) acc += part[c * slice + i];
+    out[m * ldo + n] = f2bf(acc);
+  }
+}
+
+void launch_dense_split_sum(const float* part, int32_t S, int64_t M, int64_t N, uint16_t* out, int64_t ldo,
+                            hipStream_t st) {
+  if (M <= 0 || N <= 0) return;
+  const int64_t per = (N & 3) == 0 ? 4 : 1;
+  const dim3 grid{unsigned(cdiv(cdiv(M * N, per), int64_t(256)))}, block{256u};
+  hipLaunchKernelGGL(dense_split_sum_kernel, grid, block, 0, st, part, S, M, N, out, ldo);
 }
 
 void launch_skinny(const GemmArgs& a, int wfmt, bool a_e4m3, int row_mode, bool out_f32, int64_t grid_blocks,

@@ -208,7 +208,7 @@ def block_fp8_linear(x: torch.Tensor, weight: torch.Tensor, block_size: Sequence
         raise ValueError("bias must have N elements")
     out = torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
     lib = L.load()
-    ws_bytes = lib.mxq_block_fp8_linear_workspace_size(M, K, a_dtype)
+    ws_bytes = lib.mxq_block_fp8_linear_workspace_size(M, N, K, a_dtype)
     ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=x.device)
     st = lib.mxq_block_fp8_linear(a.data_ptr(), a_dtype, _ptr(a_scale), M, K, a.stride(0), w.data_ptr(), N,
                                   weight_scale.data_ptr(), weight_scale.stride(0), weight_scale.stride(1), block_n,

@@ -50,7 +50,7 @@ def test_dispatch_struct_matches_header():
 
 def test_status_strings_and_version():
     L, lib = _lib()
-    assert lib.mxq_abi_version() == 11
+    assert lib.mxq_abi_version() == 12
     for code in range(0, 10):
         assert lib.mxq_status_string(code)
     assert b"unknown" in lib.mxq_status_string(99)
@@ -65,9 +65,22 @@ def test_max_blocks_matches_formula():
 
 def test_workspace_queries():
     L, lib = _lib()
-    assert lib.mxq_block_fp8_linear_workspace_size(2048, 2048, L.MXQ_DTYPE_E4M3) == 0
-    n = lib.mxq_block_fp8_linear_workspace_size(2048, 2048, L.MXQ_DTYPE_BF16)
-    assert n >= 2048 * 2048 + 2048 * 16 * 4
+    assert lib.mxq_block_fp8_linear_workspace_size(2048, 7168, 2048, L.MXQ_DTYPE_E4M3) == 0
+    n = lib.mxq_block_fp8_linear_workspace_size(2048, 7168, 2048, L.MXQ_DTYPE_BF16)
+    assert n == 2048 * 2048 + 2048 * 16 * 4
+    # up to 16 rows: the K split's fp32 partial sums too (S slices of M x N, S a power of two
+    # up to 8, at most 8 MiB)
+    for M, N, K in [(1, 7168, 2048), (16, 2048, 7168), (16, 65536, 16384), (1, 64, 1024)]:
+        q = lib.mxq_block_fp8_linear_workspace_size(M, N, K, L.MXQ_DTYPE_BF16)
+        e = lib.mxq_block_fp8_linear_workspace_size(M, N, K, L.MXQ_DTYPE_E4M3)
+        assert q - e == ((M * K + 255) // 256 * 256) + ((4 * M * K // 128 + 255) // 256 * 256)
+        assert e == 0 or (e % (4 * M * N) == 0 and e // (4 * M * N) in (2, 4, 8) and e <= 8 << 20), (M, N, K, e)
+    assert lib.mxq_block_fp8_linear_workspace_size(1, 7168, 2048, L.MXQ_DTYPE_E4M3) > 0
+    # past 8 rows only where the row tiles' grid is small (32 workgroups at most)
+    assert lib.mxq_block_fp8_linear_workspace_size(17, 7168, 2048, L.MXQ_DTYPE_E4M3) == 0
+    # 8 row tiles of 4 x 16 column tiles of 64 = 128 workgroups: 4 chunks fill 512
+    assert lib.mxq_block_fp8_linear_workspace_size(32, 1024, 7168, L.MXQ_DTYPE_E4M3) == 4 * 32 * 1024 * 4
+    assert lib.mxq_block_fp8_linear_workspace_size(65, 1024, 7168, L.MXQ_DTYPE_E4M3) == 0
     a = lib.mxq_fused_moe_workspace_size(4096, 7168, 2048, 256, 8, L.MXQ_WEIGHTS_FP8_BLOCK, 1)
     b = lib.mxq_fused_moe_workspace_size(4096, 7168, 2048, 256, 8, L.MXQ_WEIGHTS_FP8_BLOCK, 0)
     R = 4096 * 8

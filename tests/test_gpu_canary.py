@@ -56,14 +56,15 @@ def _stream():
 
 
 @pytest.mark.parametrize("M,N,K,block_n", [(300, 200, 384, 128), (17, 1000, 256, 128), (257, 640, 384, 1),
-                                           (1, 130, 128, 128), (129, 264, 256, 1), (64, 136, 1152, 128)])
+                                           (1, 130, 128, 128), (129, 264, 256, 1), (64, 136, 1152, 128),
+                                           (5, 998, 4096, 128)])
 def test_block_linear_writes_only_its_output(M, N, K, block_n):
     lib = L.load()
     d = synth.block_linear(M, N, K, seed=M + N + K, device=gpu(), block_n=block_n, bias_dtype=torch.float32)
     ref = ops.block_fp8_linear(d["x"], d["w"], [block_n, 128], d["sw"], bias=d["bias"])
     ldo = N + 40
     full, out = _guarded(M, N, ldo, torch.bfloat16, CANARY16)
-    ws_n = lib.mxq_block_fp8_linear_workspace_size(M, K, L.MXQ_DTYPE_BF16)
+    ws_n = lib.mxq_block_fp8_linear_workspace_size(M, N, K, L.MXQ_DTYPE_BF16)
     ws = torch.empty(ws_n, dtype=torch.uint8, device=gpu())
     st = lib.mxq_block_fp8_linear(d["x"].data_ptr(), L.MXQ_DTYPE_BF16, None, M, K, K, d["w"].data_ptr(), N,
                                   d["sw"].data_ptr(), d["sw"].stride(0), d["sw"].stride(1), block_n, 128,

@@ -17,6 +17,7 @@ import numpy as np
 import pytest
 import torch
 
+from mxfp4_block_scaled_expert_amd import _lib as L
 from mxfp4_block_scaled_expert_amd import ops, synth
 from oracle import dense as OD
 from oracle.quant import per_token_group_quant_fp8 as oracle_quant
@@ -307,3 +308,28 @@ def test_block_linear_grid_picked_tiles(shape, block_n):
     out = ops.block_fp8_linear(d["x"], d["w"], [block_n, 128], d["sw"], bias=d["bias"])
     torch.cuda.synchronize()
     assert_bf16_close(bf16_bits(out), _oracle_block(d), what=f"block linear {M}x{N}x{K} bn={block_n}")
+
+
+@pytest.mark.parametrize("M,N,K,prequant,split", [(1, 2048, 7168, False, 8), (5, 998, 7168, False, 8),
+                                                  (13, 2048, 4096, True, 4), (40, 1024, 7168, False, 2),
+                                                  (8, 12288, 1536, True, 2), (3, 300, 256, False, 1),
+                                                  (64, 256, 4096, True, 8)])
+def test_block_linear_few_rows(M, N, K, prequant, split):
+    """Few-row block linears (128 x 128 weight blocks) run on the weight-streaming kernel in
+    tiles of 4 or 8 rows, K cut into `split` chunks whose fp32 partial sums a second kernel adds
+    in chunk order: ragged row tiles, a column count that is not a multiple of 4 (the scalar
+    sum), 64- and 128-column tiles, bf16 input quantised in the call (the partial sums after
+    the codes in the workspace) and pre-quantised input (bit-equal to it), a bias, and one
+    unsplit case writing bf16 directly; each against the oracle."""
+    lib = L.load()
+    part = lib.mxq_block_fp8_linear_workspace_size(M, N, K, L.MXQ_DTYPE_E4M3)
+    assert part == (0 if split == 1 else (4 * split * M * N + 255) // 256 * 256)
+    d = _block_case(M, N, K, 128, seed=M * 7 + N, bias_dtype=torch.float32)
+    out = ops.block_fp8_linear(d["x"], d["w"], [128, 128], d["sw"], bias=d["bias"])
+    if prequant:
+        q, s = ops.per_token_group_quant_fp8(d["x"])
+        out_q = ops.block_fp8_linear(q, d["w"], [128, 128], d["sw"], input_scale=s, bias=d["bias"])
+        torch.cuda.synchronize()
+        assert torch.equal(out_q.view(torch.int16), out.view(torch.int16))
+    torch.cuda.synchronize()
+    assert_bf16_close(bf16_bits(out), _oracle_block(d), what=f"few-row block linear {M}x{N}x{K}")

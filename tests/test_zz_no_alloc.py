@@ -24,7 +24,7 @@ def _call(lib, d, M, N, K, out, noalloc, bias=None, x=None, a_dtype=None, a_scal
               sw.stride(1), d["block_n"], 128, b, L.MXQ_DTYPE_F32, out.data_ptr(), L.MXQ_DTYPE_BF16, N)
     if noalloc:
         return lib.mxq_block_fp8_linear_noalloc(*common, _stream())
-    n = lib.mxq_block_fp8_linear_workspace_size(M, K, a_dtype)
+    n = lib.mxq_block_fp8_linear_workspace_size(M, N, K, a_dtype)
     ws = torch.empty(max(n, 1), dtype=torch.uint8, device="cuda")
     st = lib.mxq_block_fp8_linear(*common, ws.data_ptr(), n, _stream())
     torch.cuda.synchronize()
@@ -81,3 +81,31 @@ def test_noalloc_prequantised_input_needs_no_scratch():
     want = torch.empty(M, N, dtype=torch.bfloat16, device=dev)
     assert _call(lib, d, M, N, K, want, False, x=q, a_dtype=L.MXQ_DTYPE_E4M3, a_scale=s) == L.MXQ_OK
     assert torch.equal(got.view(torch.int16), want.view(torch.int16))
+
+
+@pytest.mark.gpu
+def test_noalloc_few_rows_split_matches_on_two_calls():
+    """Few rows: the K split's fp32 partial sums go to the static array as well.  Two calls in a
+    row on one stream (the second smaller, with a ragged column count and pre-quantised input),
+    each bit-identical to the allocating entry point on the same inputs."""
+    lib = L.load()
+    dev = torch.device("cuda", 0)
+    outs = []
+    for M, N, K, preq in [(8, 2048, 7168, False), (3, 998, 4096, True)]:
+        assert lib.mxq_block_fp8_linear_workspace_size(M, N, K, L.MXQ_DTYPE_E4M3) > 0  # the split runs
+        d = synth.block_linear(M, N, K, seed=M + N + K, device=dev, bias_dtype=torch.float32)
+        kw = {}
+        if preq:
+            q = torch.empty(M, K, dtype=torch.uint8, device=dev)
+            s = torch.empty(M, K // 128, dtype=torch.float32, device=dev)
+            assert lib.mxq_per_token_group_quant_fp8(d["x"].data_ptr(), M, K, K, 128, q.data_ptr(), s.data_ptr(),
+                                                     _stream()) == 0
+            kw = dict(x=q, a_dtype=L.MXQ_DTYPE_E4M3, a_scale=s)
+        got = torch.empty(M, N, dtype=torch.bfloat16, device=dev)
+        assert _call(lib, d, M, N, K, got, True, d["bias"], **kw) == L.MXQ_OK
+        outs.append((d, got, M, N, K, kw))
+    torch.cuda.synchronize()
+    for d, got, M, N, K, kw in outs:
+        want = torch.empty(M, N, dtype=torch.bfloat16, device=dev)
+        assert _call(lib, d, M, N, K, want, False, d["bias"], **kw) == L.MXQ_OK
+        assert torch.equal(got.view(torch.int16), want.view(torch.int16)), f"{M}x{N}x{K}"
