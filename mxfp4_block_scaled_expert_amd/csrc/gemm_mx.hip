@@ -266,9 +266,15 @@ static void launch_mx_t(const MxArgs& a, hipStream_t st) {
     hipLaunchKernelGGL((gemm_mx_kernel<BM, WFMT, false>), grid, block, 0, st, a, row_tiles, n_tiles);
 }
 
+// 128-row tiles up to 128 rows, and wherever they fit the 256 compute units in one round: each
+// tile runs its K range as one serial chain, so below a full GPU more, smaller tiles finish
+// sooner; 256-row tiles otherwise.
+#ifndef MXQ_MX_FILL
+#define MXQ_MX_FILL 1
+#endif
 void launch_gemm_mx(const MxArgs& a, hipStream_t st) {
   if (a.M <= 0 || a.N <= 0) return;
-  const bool small = a.M <= 128;
+  const bool small = a.M <= 128 || (MXQ_MX_FILL && cdiv(a.M, int64_t(128)) * cdiv(a.N, int64_t(256)) <= 256);
   if (a.w_fmt == MX_W_E2M1) {
     if (small) launch_mx_t<128, MX_W_E2M1>(a, st); else launch_mx_t<256, MX_W_E2M1>(a, st);
   } else {

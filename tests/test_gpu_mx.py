@@ -84,7 +84,7 @@ def test_mx_linear_ragged_shapes(M, N, K, w_format):
 
 @pytest.mark.parametrize("seed", range(8))
 def test_mx_linear_random_shapes(seed):
-    """Seeded random MX linear shapes (M 1..600 across the 128-row tile switch, N 8..1024, K a
+    """Seeded random MX linear shapes (M 1..600 on the 128-row tiles, N 8..1024, K a
     multiple of 128 up to 1536, MXFP4 or MXFP8 weights, with and without bias) against the
     oracle."""
     rng = np.random.default_rng(700 + seed)
@@ -97,6 +97,19 @@ def test_mx_linear_random_shapes(seed):
     out = ops.mx_linear(d["x"], d["w"], d["sw"], w_format, bias=d["bias"])
     torch.cuda.synchronize()
     assert_bf16_close(bf16_bits(out), _oracle_linear(d), what=f"random mx {w_format} {M}x{N}x{K}")
+
+
+@pytest.mark.parametrize("w_format", ["e2m1", "e4m3"])
+@pytest.mark.parametrize("shape", [(300, 520, 384), (2100, 4000, 256)])
+def test_mx_linear_tile_rows_from_the_grid(shape, w_format):
+    """128-row tiles wherever their grid fits the GPU in one round (300 x 520: three row tiles,
+    the last ragged, and an 8-column last tile), 256-row tiles otherwise (2100 x 4000: a 52-row
+    last row tile and a 160-column last tile); each against the oracle."""
+    M, N, K = shape
+    d = synth.mx_linear(M, N, K, seed=M + N, device=gpu(), w_format=w_format, bias_dtype=torch.float32)
+    out = ops.mx_linear(d["x"], d["w"], d["sw"], w_format, bias=d["bias"])
+    torch.cuda.synchronize()
+    assert_bf16_close(bf16_bits(out), _oracle_linear(d), what=f"mx {w_format} {M}x{N}x{K}")
 
 
 @pytest.mark.parametrize("w_format", ["e2m1", "e4m3"])
