@@ -145,9 +145,11 @@ mxq_status mxq_fp8_scaled_bmm(const void* A, int64_t batch, int64_t M, int64_t K
  *             bf16 input's quantised activations, and for the few-row cases below the fp32
  *             partial sums of a K split (at most 8 MiB); NULL allowed where the size is 0.
  *   K must be a multiple of 128.  FP8 matrix cores (16x16x128 per K block), fp32 accumulation.
- *   Few rows -- M <= 64 where the row tiles would run at most 32 workgroups, 96 for M <= 8
- *   (ceil(M / t) * ceil(N / 128), t = 16, 32 or 64 rows for M <= 16, 32, 64) -- with
- *   N * K < 2^32 and K <= 15744 run on the weight-streaming kernel (tiles of 4 or 8 rows); that
+ *   Few rows -- M <= 32 with K >= 4096, or M <= 64 where the row tiles would run at most 32
+ *   workgroups, 96 for M <= 8 (ceil(M / t) * ceil(N / 128), t = 16, 32 or 64 rows for
+ *   M <= 16, 32, 64) -- with
+ *   N * K < 2^32 (and a tile's rows of its K chunk within the kernel's LDS) run on the
+ *   weight-streaming kernel (tiles of 4 or 8 rows, each workgroup staging only its K chunk); that
  *   path may cut K into chunks of whole 128-wide blocks whose partial sums are added in chunk
  *   order, so its sums are grouped differently from the tiles' (the result agrees within
  *   rounding; path and split depend on M, N and K only, and with 1 x 128 weight blocks the

@@ -822,19 +822,24 @@ mxq_status mxq_fp8_scaled_bmm(const void* A, int64_t batch, int64_t M, int64_t K
 
 // Dense W8A8 GEMMs of few rows stream their weights through the tiny-block kernel (tiles of 4
 // or 8 rows and 64 or 128 columns) rather than the 16..128-row tiles: they are bound by reading
-// W once, which the tiles do on far fewer workgroups -- while the tiles' grid would hold at
-// most kSkDenseTileGrid workgroups (kSkDenseTileGrid8 for up to 8 rows, one row tile here)
-// and M <= kSkDenseMaxRows (interleaved on the box: 1 x 2048 x 7168 52.2 -> 12.4 us,
-// 13 x 2048 x 4096 24.0 -> 14.2, 32 x 1024 x 7168 39.7 -> 18.9, 64 x 2048 x 7168 62.0 -> 39.5,
-// 8 x 7168 x 2048 19.2 -> 14.9; the tiles stay where their grid is wider: 16 x 24576 x 1536
-// 16.9 against 26.1, 8 x 24576 x 1536 16.8 against 19.8, 64 x 7168 x 2048 22.3 against 27.3;
-// the bound 96 sits between the measured 56-workgroup win and 192-workgroup loss).  K is cut into S chunks (whole 128-column steps, at least four per
+// W once, which the tiles do on far fewer workgroups, each over a long serial K chain.  Used
+// for M <= kSkDenseMaxRows while the tiles' grid would hold at most kSkDenseTileGrid workgroups
+// (kSkDenseTileGrid8 for up to 8 rows), and for up to kSkDenseLongKRows rows whenever
+// K >= kSkDenseLongK (interleaved on the box: 1 x 2048 x 7168 52.2 -> 12.4 us, 13 x 2048 x 4096
+// 24.0 -> 13.6, 16 x 2048 x 7168 53.6 -> 16.9, 64 x 2048 x 7168 62.0 -> 27.9, 8 x 7168 x 2048
+// 19.2 -> 14.9, 1 x 7168 x 16384 110.6 -> 38.4; with long K on wide grids 1 x 16384 x 7168
+// 54.6 -> 33.2, 4 x 16384 x 4096 34.3 -> 23.6, 16 x 8192 x 7168 54.5 -> 34.9, 32 x 7168 x 7168
+// 56.4 -> 52.9; the tiles stay with short K on wide grids: 8 x 24576 x 1536 16.7 against
+// 19.9, 1 x 32768 x 2048 20.3 against 21.8, 16 x 7168 x 2048 19.3 against 20.4, 64 x 7168 x
+// 2048 22.3 against 27.4; the bound 96 sits between a measured 56-workgroup win and
+// 128-workgroup loss at K = 2048).  K is cut into S chunks (whole 128-column steps, at least four per
 // chunk) until the grid reaches kSkDenseWorkgroups; the chunks' fp32 partial sums sit in the
 // workspace and one more kernel adds them in chunk order.
 #ifndef MXQ_SK_DENSE_MAX
 #define MXQ_SK_DENSE_MAX 64
 #endif
 constexpr int64_t kSkDenseTileGrid = 32, kSkDenseTileGrid8 = 96;
+constexpr int64_t kSkDenseLongK = 4096, kSkDenseLongKRows = 32;
 #ifndef MXQ_SK_DENSE_WG
 #define MXQ_SK_DENSE_WG 512
 #endif
@@ -844,26 +849,38 @@ constexpr size_t kSkDenseMaxPartial = size_t(8) << 20;  // partial-sum bytes at 
 
 struct DenseSkinny {
   bool on;
+  int32_t rows;        // rows per tile (8, or 4 when eight rows of the K chunk pass the LDS cap)
   int32_t split;       // S
   int64_t chunk;       // K elements per chunk
   size_t partial_bytes;
 };
 
 DenseSkinny dense_skinny_plan(int64_t M, int64_t N, int64_t K) {
-  DenseSkinny p{false, 1, K, 0};
+  DenseSkinny p{false, 8, 1, K, 0};
   if (kSkDenseMaxRows <= 0 || M < 1 || M > kSkDenseMaxRows || N < 1 || K < 128 || K % 128 != 0 ||
-      N * K >= (int64_t(1) << 32) || skinny_lds_bytes(W_E4M3_BLOCK, true, K) > kSkinnyMaxLds)
+      N * K >= (int64_t(1) << 32))
     return p;
-  if (cdiv(M, tile_rows(dense_tile_for(M))) * cdiv(N, int64_t(128)) > (M <= 8 ? kSkDenseTileGrid8 : kSkDenseTileGrid))
+  const bool long_k = K >= kSkDenseLongK && M <= kSkDenseLongKRows;
+  if (!long_k &&
+      cdiv(M, tile_rows(dense_tile_for(M))) * cdiv(N, int64_t(128)) > (M <= 8 ? kSkDenseTileGrid8 : kSkDenseTileGrid))
     return p;
-  p.on = true;
   const int64_t steps = K / 128;
-  const int64_t wgs = cdiv(M, int64_t(skinny_dense_rows(N, K))) * skinny_dense_col_tiles(N);
-  while (p.split < 8 && wgs * p.split * 2 <= kSkDenseWorkgroups && steps >= 8 * p.split &&
-         size_t(4) * 2 * p.split * M * N <= kSkDenseMaxPartial)
-    p.split *= 2;
-  p.chunk = cdiv(steps, int64_t(p.split)) * 128;
-  p.partial_bytes = p.split > 1 ? align256(sizeof(float) * p.split * M * N) : 0;
+  // eight rows per tile while their K chunk stays within 32 KB of LDS (several workgroups per
+  // compute unit), else four within 64 KB
+  for (const int ar : {8, 4}) {
+    int32_t S = 1;
+    const int64_t wgs = cdiv(M, int64_t(ar)) * skinny_dense_col_tiles(N);
+    while (S < 8 && wgs * S * 2 <= kSkDenseWorkgroups && steps >= 8 * S && size_t(4) * 2 * S * M * N <= kSkDenseMaxPartial)
+      S *= 2;
+    const int64_t chunk = cdiv(steps, int64_t(S)) * 128;
+    if (skinny_dense_lds(N, K, ar, S > 1 ? chunk : 0) > (ar == 8 ? size_t(32) << 10 : kSkinnyMaxLds)) continue;
+    p.on = true;
+    p.rows = ar;
+    p.split = S;
+    p.chunk = chunk;
+    p.partial_bytes = S > 1 ? align256(sizeof(float) * S * M * N) : 0;
+    break;
+  }
   return p;
 }
 
@@ -936,10 +953,10 @@ mxq_status mxq_block_fp8_linear(const void* A, int32_t a_dtype, const float* a_s
       gs.k_split = sk.split;
       gs.k_chunk = sk.chunk;
       gs.split_stride = M * N;
-      launch_skinny_dense(gs, true, st);
+      launch_skinny_dense(gs, sk.rows, true, st);
       launch_dense_split_sum(part, sk.split, M, N, static_cast<uint16_t*>(out), ldo, st);
     } else {
-      launch_skinny_dense(g, false, st);
+      launch_skinny_dense(g, sk.rows, false, st);
     }
   } else if ((block_n == 128 || block_n == 1) && M > 128 && K <= 16384 && int64_t(M) * lqa < (int64_t(1) << 32) &&
       N * K < (int64_t(1) << 32)) {

@@ -53,18 +53,21 @@ struct SkinnyShape {
 };
 }  // namespace
 
-// LDS layout (bytes): activation rows [AR][row_stride] | weight scales [K/128][nb] | act scales [K/128][AR]
+// LDS layout (bytes): activation rows [AR][row_stride] | weight scales [K/128][nb] | act scales [K/128][AR].
+// A row holds the workgroup's own K range: kstage elements (a K chunk when K is split; 0: all of K).
 struct SkinnyLds {
   int row_stride, kpad, kb, nb;
   uint32_t sw_off, sa_off, total;
 };
 
-__host__ __device__ inline SkinnyLds skinny_lds_layout(bool mx, bool a_e4m3, int64_t K, int G, int AR) {
+__host__ __device__ inline SkinnyLds skinny_lds_layout(bool mx, bool a_e4m3, int64_t K, int G, int AR,
+                                                      int64_t kstage = 0) {
   SkinnyLds L;
   const int kstep = mx ? 256 : 128;
   const int ae = a_e4m3 ? 1 : 2;
   L.kpad = int((K + kstep - 1) / kstep) * kstep;
-  L.row_stride = L.kpad * ae + 16;  // +16 B: rows read together fall in different LDS banks
+  const int64_t ks = kstage > 0 && kstage < L.kpad ? kstage : L.kpad;
+  L.row_stride = int((ks + kstep - 1) / kstep) * kstep * ae + 16;  // +16 B: rows read together fall in different banks
   L.kb = int(K >> 7);
   L.nb = G >= 2 ? G / 2 : 1;
   L.sw_off = uint32_t(AR * L.row_stride);
@@ -103,7 +106,7 @@ __global__ __launch_bounds__(256, (SkinnyShape<WFMT, A_E4M3>::W)) void skinny_ke
   // dense: a tile is AR consecutive rows (one pass); routed: a tile is one expert block
   if (!tile_info<(MODE == ROWS_DENSE ? AR : 1), MODE>(a, tile, t)) return;
 
-  const SkinnyLds L = skinny_lds_layout(MX, A_E4M3, K, G, AR);
+  const SkinnyLds L = skinny_lds_layout(MX, A_E4M3, K, G, AR, nsplit > 1 ? a.k_chunk : 0);
   const int nsteps = L.kpad / KSTEP;
   // this workgroup's K steps [st_b, st_e); an empty range (a chunk past K) stores zeros
   int st_b = 0, st_e = nsteps;
@@ -224,7 +227,7 @@ __global__ __launch_bounds__(256, (SkinnyShape<WFMT, A_E4M3>::W)) void skinny_ke
             v = *reinterpret_cast<const i32x4*>(src);
           }
         }
-        *reinterpret_cast<i32x4*>(smem + m * L.row_stride + cc * 16) = v;
+        *reinterpret_cast<i32x4*>(smem + m * L.row_stride + (cc - cb) * 16) = v;
       }
       if (!MX) {
         // weight block scales of the workgroup's n-blocks, [kb][nb]
@@ -260,7 +263,7 @@ __global__ __launch_bounds__(256, (SkinnyShape<WFMT, A_E4M3>::W)) void skinny_ke
       if constexpr (MX) {
 #pragma unroll
         for (int s = 0; s < 8; ++s) {
-          const i32x4 af = *reinterpret_cast<const i32x4*>(arow + (st * KSTEP + q * 64 + 8 * s) * 2);
+          const i32x4 af = *reinterpret_cast<const i32x4*>(arow + ((st - st_b) * KSTEP + q * 64 + 8 * s) * 2);
 #pragma unroll
           for (int g = 0; g < G; ++g) {
             uint32_t o[4];
@@ -270,8 +273,8 @@ __global__ __launch_bounds__(256, (SkinnyShape<WFMT, A_E4M3>::W)) void skinny_ke
           }
         }
       } else if constexpr (A_E4M3) {
-        const i32x4 a0 = *reinterpret_cast<const i32x4*>(arow + st * KSTEP + q * 32);
-        const i32x4 a1 = *reinterpret_cast<const i32x4*>(arow + st * KSTEP + q * 32 + 16);
+        const i32x4 a0 = *reinterpret_cast<const i32x4*>(arow + (st - st_b) * KSTEP + q * 32);
+        const i32x4 a1 = *reinterpret_cast<const i32x4*>(arow + (st - st_b) * KSTEP + q * 32 + 16);
         const i32x8 af = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
         const f32x4 sa = *reinterpret_cast<const f32x4*>(s_sa + st * AR + 4 * sa_q);
 #pragma unroll
@@ -290,7 +293,7 @@ __global__ __launch_bounds__(256, (SkinnyShape<WFMT, A_E4M3>::W)) void skinny_ke
         for (int g = 0; g < G; ++g) part[g] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
-          const i32x4 af = *reinterpret_cast<const i32x4*>(arow + (st * KSTEP + q * 32 + 8 * s) * 2);
+          const i32x4 af = *reinterpret_cast<const i32x4*>(arow + ((st - st_b) * KSTEP + q * 32 + 8 * s) * 2);
 #pragma unroll
           for (int g = 0; g < G; ++g) {
             uint32_t o0, o1, o2, o3;
@@ -368,11 +371,12 @@ size_t skinny_lds_bytes(int wfmt, bool a_e4m3, int64_t K) {
 }
 
 template <int WFMT, bool AE, int MODE, bool TL, int AR, int G, int D>
-static void launch_skinny_ar(const GemmArgs& a, bool out_f32, int64_t gb, hipStream_t st) {
+static void launch_skinny_ar(const GemmArgs& a, bool out_f32, int64_t gb, hipStream_t st, size_t lds_bytes = 0) {
   const int64_t n_tiles = cdiv(a.N, int64_t(64 * G));
   const int64_t nsplit = a.k_split > 1 ? a.k_split : 1;
   const dim3 grid(static_cast<unsigned>(gb * n_tiles * nsplit)), block(256);
-  const size_t lds = skinny_lds_t<WFMT, AE>(a.K, AR, G);
+  // (routed blocks: LDS for all of K, at least the chunk-sized layout the kernel uses)
+  const size_t lds = lds_bytes > 0 ? lds_bytes : skinny_lds_t<WFMT, AE>(a.K, AR, G);
   const bool bias = a.bias != nullptr;
 #define MXQ_SK_GO(OF, HB) \
   hipLaunchKernelGGL((skinny_kernel<WFMT, AE, MODE, OF, HB, TL, AR, G, D>), grid, block, lds, st, a, gb)
@@ -413,20 +417,22 @@ static void launch_skinny_mode(const GemmArgs& a, int wfmt, bool a_e4m3, bool ou
 
 // Dense W8A8 rows (e4m3 activations and weights in the plain layout, 128 x 128 weight blocks):
 // tiles of AR rows (8, or 4 when eight rows of K would pass the LDS cap), all launched at once.
-int skinny_dense_rows(int64_t N, int64_t K) { return skinny_rows_t<W_E4M3_BLOCK, true>(K, skinny_groups(N)); }
+size_t skinny_dense_lds(int64_t N, int64_t K, int ar, int64_t kstage) {
+  return skinny_lds_layout(false, true, K, skinny_groups(N), ar, kstage).total;
+}
 
 int64_t skinny_dense_col_tiles(int64_t N) { return cdiv(N, int64_t(64 * skinny_groups(N))); }
 
-void launch_skinny_dense(const GemmArgs& a, bool out_f32, hipStream_t st) {
+void launch_skinny_dense(const GemmArgs& a, int ar, bool out_f32, hipStream_t st) {
   if (a.M <= 0 || a.N <= 0) return;
-  const int ar = skinny_dense_rows(a.N, a.K);
   const int64_t tiles = cdiv(a.M, int64_t(ar));
+  const size_t lds = skinny_dense_lds(a.N, a.K, ar, a.k_split > 1 ? a.k_chunk : 0);
   if (skinny_groups(a.N) == 2) {
-    if (ar == 8) launch_skinny_ar<W_E4M3_BLOCK, true, ROWS_DENSE, false, 8, 2, 3>(a, out_f32, tiles, st);
-    else launch_skinny_ar<W_E4M3_BLOCK, true, ROWS_DENSE, false, 4, 2, 3>(a, out_f32, tiles, st);
+    if (ar == 8) launch_skinny_ar<W_E4M3_BLOCK, true, ROWS_DENSE, false, 8, 2, 3>(a, out_f32, tiles, st, lds);
+    else launch_skinny_ar<W_E4M3_BLOCK, true, ROWS_DENSE, false, 4, 2, 3>(a, out_f32, tiles, st, lds);
   } else {
-    if (ar == 8) launch_skinny_ar<W_E4M3_BLOCK, true, ROWS_DENSE, false, 8, 1, 4>(a, out_f32, tiles, st);
-    else launch_skinny_ar<W_E4M3_BLOCK, true, ROWS_DENSE, false, 4, 1, 4>(a, out_f32, tiles, st);
+    if (ar == 8) launch_skinny_ar<W_E4M3_BLOCK, true, ROWS_DENSE, false, 8, 1, 4>(a, out_f32, tiles, st, lds);
+    else launch_skinny_ar<W_E4M3_BLOCK, true, ROWS_DENSE, false, 4, 1, 4>(a, out_f32, tiles, st, lds);
   }
 }
 

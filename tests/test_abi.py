@@ -78,8 +78,8 @@ def test_workspace_queries():
     assert lib.mxq_block_fp8_linear_workspace_size(1, 7168, 2048, L.MXQ_DTYPE_E4M3) > 0
     # past 8 rows only where the row tiles' grid is small (32 workgroups at most)
     assert lib.mxq_block_fp8_linear_workspace_size(17, 7168, 2048, L.MXQ_DTYPE_E4M3) == 0
-    # 8 row tiles of 4 x 16 column tiles of 64 = 128 workgroups: 4 chunks fill 512
-    assert lib.mxq_block_fp8_linear_workspace_size(32, 1024, 7168, L.MXQ_DTYPE_E4M3) == 4 * 32 * 1024 * 4
+    # 4 row tiles of 8 x 16 column tiles of 64 = 64 workgroups: 8 chunks fill 512
+    assert lib.mxq_block_fp8_linear_workspace_size(32, 1024, 7168, L.MXQ_DTYPE_E4M3) == 8 * 32 * 1024 * 4
     assert lib.mxq_block_fp8_linear_workspace_size(65, 1024, 7168, L.MXQ_DTYPE_E4M3) == 0
     a = lib.mxq_fused_moe_workspace_size(4096, 7168, 2048, 256, 8, L.MXQ_WEIGHTS_FP8_BLOCK, 1)
     b = lib.mxq_fused_moe_workspace_size(4096, 7168, 2048, 256, 8, L.MXQ_WEIGHTS_FP8_BLOCK, 0)

@@ -311,16 +311,19 @@ def test_block_linear_grid_picked_tiles(shape, block_n):
 
 
 @pytest.mark.parametrize("M,N,K,prequant,split", [(1, 2048, 7168, False, 8), (5, 998, 7168, False, 8),
-                                                  (13, 2048, 4096, True, 4), (40, 1024, 7168, False, 2),
+                                                  (13, 2048, 4096, True, 8), (40, 1024, 7168, False, 4),
                                                   (8, 12288, 1536, True, 2), (3, 300, 256, False, 1),
-                                                  (64, 256, 4096, True, 8)])
+                                                  (64, 256, 4096, True, 8), (1, 7168, 16384, False, 8),
+                                                  (4, 16384, 4096, True, 4)])
 def test_block_linear_few_rows(M, N, K, prequant, split):
     """Few-row block linears (128 x 128 weight blocks) run on the weight-streaming kernel in
     tiles of 4 or 8 rows, K cut into `split` chunks whose fp32 partial sums a second kernel adds
     in chunk order: ragged row tiles, a column count that is not a multiple of 4 (the scalar
     sum), 64- and 128-column tiles, bf16 input quantised in the call (the partial sums after
     the codes in the workspace) and pre-quantised input (bit-equal to it), a bias, and one
-    unsplit case writing bf16 directly; each against the oracle."""
+    unsplit case writing bf16 directly, K = 16384, where only a K chunk of each row fits the
+    workgroup's LDS, and a long-K call whose row tiles would fill the GPU (4 x 16384 x 4096);
+    each against the oracle."""
     lib = L.load()
     part = lib.mxq_block_fp8_linear_workspace_size(M, N, K, L.MXQ_DTYPE_E4M3)
     assert part == (0 if split == 1 else (4 * split * M * N + 255) // 256 * 256)
