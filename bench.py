@@ -267,10 +267,13 @@ def bench_per_tensor(steps: int, warmup: int):
     d = synth.dense_w8a16(M, N, K, seed=1001, device=dev)
     out = torch.empty(M, N, dtype=torch.bfloat16, device=dev)
     sh = torch.cuda.current_stream().cuda_stream
+    ws_n = lib.mxq_fp8_scaled_mm_workspace_size(M, N, K)
+    ws = torch.empty(max(ws_n, 1), dtype=torch.uint8, device=dev)
 
     def run():
         _check(lib.mxq_fp8_scaled_mm(d["a"].data_ptr(), M, K, K, d["w"].data_ptr(), N, d["scale"].data_ptr(),
-                                     d["bias"].data_ptr(), L.MXQ_DTYPE_F32, out.data_ptr(), N, sh), "fp8_scaled_mm")
+                                     d["bias"].data_ptr(), L.MXQ_DTYPE_F32, out.data_ptr(), N, ws.data_ptr(), ws_n,
+                                     sh), "fp8_scaled_mm")
     st, _ = _time_calls(run, steps, warmup)
     byts = M * K * 2 + N * K + N * 4 + M * N * 2
     return {"workload": "per_tensor_w8a16_97x576x224", "us": st, "tflops": 2.0 * M * N * K / (st["median"] * 1e-6) / 1e12,

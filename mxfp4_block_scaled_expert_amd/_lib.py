@@ -79,7 +79,8 @@ SIGNATURES = {
     "mxq_abi_version": (_i32, []),
     "mxq_init": (_i32, [_i32]),
     "mxq_per_token_group_quant_fp8": (_i32, [_p, _i64, _i64, _i64, _i32, _p, _p, _p]),
-    "mxq_fp8_scaled_mm": (_i32, [_p, _i64, _i64, _i64, _p, _i64, _p, _p, _i32, _p, _i64, _p]),
+    "mxq_fp8_scaled_mm_workspace_size": (_sz, [_i64, _i64, _i64]),
+    "mxq_fp8_scaled_mm": (_i32, [_p, _i64, _i64, _i64, _p, _i64, _p, _p, _i32, _p, _i64, _p, _sz, _p]),
     "mxq_fp8_scaled_bmm": (_i32, [_p, _i64, _i64, _i64, _i64, _i64, _p, _i64, _i64, _p, _i64, _p, _i32, _i64,
                                    _p, _i64, _i64, _p]),
     "mxq_block_fp8_linear_workspace_size": (_sz, [_i64, _i64, _i64, _i32]),

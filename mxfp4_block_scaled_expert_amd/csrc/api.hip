@@ -703,6 +703,92 @@ bool dense_ring(const GemmArgs& g, int tile, int64_t batch) {
          w16_ring_dense_supported(g, batch);
 }
 
+// Dense W8A8 GEMMs of few rows stream their weights through the tiny-block kernel (tiles of 4
+// or 8 rows and 64 or 128 columns) rather than the 16..128-row tiles: they are bound by reading
+// W once, which the tiles do on far fewer workgroups, each over a long serial K chain.  Used
+// for M <= kSkDenseMaxRows while the tiles' grid would hold at most kSkDenseTileGrid workgroups
+// (kSkDenseTileGrid8 for up to 8 rows), and for up to kSkDenseLongKRows rows whenever
+// K >= kSkDenseLongK (interleaved on the box: 1 x 2048 x 7168 52.2 -> 12.4 us, 13 x 2048 x 4096
+// 24.0 -> 13.6, 16 x 2048 x 7168 53.6 -> 16.9, 64 x 2048 x 7168 62.0 -> 27.9, 8 x 7168 x 2048
+// 19.2 -> 14.9, 1 x 7168 x 16384 110.6 -> 38.4; with long K on wide grids 1 x 16384 x 7168
+// 54.6 -> 33.2, 4 x 16384 x 4096 34.3 -> 23.6, 16 x 8192 x 7168 54.5 -> 34.9, 32 x 7168 x 7168
+// 56.4 -> 52.9; the tiles stay with short K on wide grids: 8 x 24576 x 1536 16.7 against
+// 19.9, 1 x 32768 x 2048 20.3 against 21.8, 16 x 7168 x 2048 19.3 against 20.4, 64 x 7168 x
+// 2048 22.3 against 27.4; the bound 96 sits between a measured 56-workgroup win and
+// 128-workgroup loss at K = 2048).  K is cut into S chunks (whole 128-column steps, at least four per
+// chunk) until the grid reaches kSkDenseWorkgroups; the chunks' fp32 partial sums sit in the
+// workspace and one more kernel adds them in chunk order.
+#ifndef MXQ_SK_DENSE_MAX
+#define MXQ_SK_DENSE_MAX 64
+#endif
+constexpr int64_t kSkDenseTileGrid = 32, kSkDenseTileGrid8 = 96;
+constexpr int64_t kSkDenseLongK = 4096, kSkDenseLongKRows = 32;
+#ifndef MXQ_SK_DENSE_WG
+#define MXQ_SK_DENSE_WG 512
+#endif
+constexpr int64_t kSkDenseMaxRows = MXQ_SK_DENSE_MAX;
+constexpr int64_t kSkDenseWorkgroups = MXQ_SK_DENSE_WG;
+constexpr size_t kSkDenseMaxPartial = size_t(8) << 20;  // partial-sum bytes at most
+
+struct DenseSkinny {
+  bool on;
+  int32_t rows;        // rows per tile (8, or 4 when eight rows of the K chunk pass the LDS cap)
+  int32_t split;       // S
+  int64_t chunk;       // K elements per chunk
+  size_t partial_bytes;
+};
+
+DenseSkinny dense_skinny_plan(int64_t M, int64_t N, int64_t K, bool a_e4m3) {
+  DenseSkinny p{false, 8, 1, K, 0};
+  if (kSkDenseMaxRows <= 0 || M < 1 || M > kSkDenseMaxRows || N < 1 || K < 128 || K % 128 != 0 ||
+      N * K >= (int64_t(1) << 32))
+    return p;
+  const bool long_k = K >= kSkDenseLongK && M <= kSkDenseLongKRows;
+  if (!long_k &&
+      cdiv(M, tile_rows(dense_tile_for(M))) * cdiv(N, int64_t(128)) > (M <= 8 ? kSkDenseTileGrid8 : kSkDenseTileGrid))
+    return p;
+  const int64_t steps = K / 128;
+  // eight rows per tile while their K chunk stays within 32 KB of LDS (several workgroups per
+  // compute unit), else four within 64 KB
+  for (const int ar : {8, 4}) {
+    int32_t S = 1;
+    const int64_t wgs = cdiv(M, int64_t(ar)) * skinny_dense_col_tiles(N);
+    while (S < 8 && wgs * S * 2 <= kSkDenseWorkgroups && steps >= 8 * S && size_t(4) * 2 * S * M * N <= kSkDenseMaxPartial)
+      S *= 2;
+    const int64_t chunk = cdiv(steps, int64_t(S)) * 128;
+    if (skinny_dense_lds(N, K, ar, S > 1 ? chunk : 0, a_e4m3) > (ar == 8 ? size_t(32) << 10 : kSkinnyMaxLds)) continue;
+    p.on = true;
+    p.rows = ar;
+    p.split = S;
+    p.chunk = chunk;
+    p.partial_bytes = S > 1 ? align256(sizeof(float) * S * M * N) : 0;
+    break;
+  }
+  return p;
+}
+
+size_t block_linear_quant_bytes(int64_t M, int64_t K, int32_t a_dtype) {
+  if (a_dtype != MXQ_DTYPE_BF16 || M <= 0 || K <= 0) return 0;
+  return align256(size_t(M) * K) + align256(sizeof(float) * M * (K / 128));
+}
+
+// Per-tensor W8A16 GEMMs of few rows stream their weights the same way (the per-tensor scale
+// read as a 128 x 128 block grid with strides 0), in a narrower range than W8A8: with bf16
+// activations each weight byte costs a decode and two bf16 MFMAs, and the ring-fed tiles are
+// stronger -- up to 16 rows, K >= 4096 (a multiple of 128), the tiles' grid at most 32
+// workgroups (interleaved on the box: 1 x 2048 x 7168 35.2 -> 22.4 us, 16 x 2048 x 7168 35.3 ->
+// 21.2; the tiles stay at 1 x 7168 x 2048 19.6 against 22.3, 8 x 7168 x 2048 19.6 against 22.1,
+// 32 x 7168 x 7168 35.6 against 79.0, 64 x 2048 x 7168 35.2 against 41.6, and tie at
+// 4 x 16384 x 4096).
+#ifndef MXQ_SK_W16
+#define MXQ_SK_W16 1
+#endif
+DenseSkinny per_tensor_skinny_plan(int64_t M, int64_t N, int64_t K) {
+  if (!MXQ_SK_W16 || M > 16 || K < 4096 || cdiv(M, int64_t(16)) * cdiv(N, int64_t(128)) > 32)
+    return DenseSkinny{false, 8, 1, K, 0};
+  return dense_skinny_plan(M, N, K, false);
+}
+
 }  // namespace
 
 extern "C" {
@@ -725,7 +811,7 @@ const char* mxq_status_string(mxq_status s) {
   }
 }
 
-int32_t mxq_abi_version(void) { return 12; }
+int32_t mxq_abi_version(void) { return 13; }
 
 mxq_status mxq_init(int32_t device) {
   if (hipSetDevice(device) != hipSuccess) return MXQ_ERR_ARCH;
@@ -747,15 +833,54 @@ mxq_status mxq_per_token_group_quant_fp8(const void* x, int64_t M, int64_t K, in
   return launch_status();
 }
 
+size_t mxq_fp8_scaled_mm_workspace_size(int64_t M, int64_t N, int64_t K) {
+  if (M <= 0 || N <= 0 || K <= 0) return 0;
+  return per_tensor_skinny_plan(M, N, K).partial_bytes;
+}
+
 mxq_status mxq_fp8_scaled_mm(const void* A, int64_t M, int64_t K, int64_t lda, const void* W, int64_t N,
                              const float* scale, const void* bias, int32_t bias_dtype, void* out, int64_t ldo,
-                             void* stream) {
+                             void* workspace, size_t workspace_bytes, void* stream) {
   if (M < 0 || N < 0 || K < 0 || K % 32 != 0 || lda < K || lda % 8 != 0 || ldo < N) return MXQ_ERR_SHAPE;
   if (bias && bias_dtype != MXQ_DTYPE_F32 && bias_dtype != MXQ_DTYPE_BF16) return MXQ_ERR_DTYPE;
   if (M == 0 || N == 0) return MXQ_OK;
   if (!A || !W || !scale || !out) return MXQ_ERR_NULL;
   if (!aligned16(A) || !aligned16(W)) return MXQ_ERR_SHAPE;
+  const size_t need = mxq_fp8_scaled_mm_workspace_size(M, N, K);
+  if (need > 0 && (!workspace || workspace_bytes < need)) return MXQ_ERR_WORKSPACE;
   MXQ_TRY(check_arch());
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const DenseSkinny sk = per_tensor_skinny_plan(M, N, K);
+  if (sk.on) {
+    GemmArgs gs{};
+    gs.A = A;
+    gs.lda = lda;
+    gs.W = static_cast<const uint8_t*>(W);
+    gs.ldw = K;
+    gs.ws = scale;  // every (column block, K block) reads the one scale
+    gs.ws_s0 = 0;
+    gs.ws_s1 = 0;
+    gs.bias = bias;
+    gs.bias_bf16 = bias_dtype == MXQ_DTYPE_BF16;
+    gs.M = M;
+    gs.N = N;
+    gs.K = K;
+    if (sk.split > 1) {
+      float* part = static_cast<float*>(workspace);
+      gs.out = part;
+      gs.ldo = N;
+      gs.k_split = sk.split;
+      gs.k_chunk = sk.chunk;
+      gs.split_stride = M * N;
+      launch_skinny_dense(gs, sk.rows, false, true, st);
+      launch_dense_split_sum(part, sk.split, M, N, static_cast<uint16_t*>(out), ldo, st);
+    } else {
+      gs.out = out;
+      gs.ldo = ldo;
+      launch_skinny_dense(gs, sk.rows, false, false, st);
+    }
+    return launch_status();
+  }
   GemmArgs g{};
   g.A = A;
   g.lda = lda;
@@ -820,78 +945,10 @@ mxq_status mxq_fp8_scaled_bmm(const void* A, int64_t batch, int64_t M, int64_t K
   return launch_status();
 }
 
-// Dense W8A8 GEMMs of few rows stream their weights through the tiny-block kernel (tiles of 4
-// or 8 rows and 64 or 128 columns) rather than the 16..128-row tiles: they are bound by reading
-// W once, which the tiles do on far fewer workgroups, each over a long serial K chain.  Used
-// for M <= kSkDenseMaxRows while the tiles' grid would hold at most kSkDenseTileGrid workgroups
-// (kSkDenseTileGrid8 for up to 8 rows), and for up to kSkDenseLongKRows rows whenever
-// K >= kSkDenseLongK (interleaved on the box: 1 x 2048 x 7168 52.2 -> 12.4 us, 13 x 2048 x 4096
-// 24.0 -> 13.6, 16 x 2048 x 7168 53.6 -> 16.9, 64 x 2048 x 7168 62.0 -> 27.9, 8 x 7168 x 2048
-// 19.2 -> 14.9, 1 x 7168 x 16384 110.6 -> 38.4; with long K on wide grids 1 x 16384 x 7168
-// 54.6 -> 33.2, 4 x 16384 x 4096 34.3 -> 23.6, 16 x 8192 x 7168 54.5 -> 34.9, 32 x 7168 x 7168
-// 56.4 -> 52.9; the tiles stay with short K on wide grids: 8 x 24576 x 1536 16.7 against
-// 19.9, 1 x 32768 x 2048 20.3 against 21.8, 16 x 7168 x 2048 19.3 against 20.4, 64 x 7168 x
-// 2048 22.3 against 27.4; the bound 96 sits between a measured 56-workgroup win and
-// 128-workgroup loss at K = 2048).  K is cut into S chunks (whole 128-column steps, at least four per
-// chunk) until the grid reaches kSkDenseWorkgroups; the chunks' fp32 partial sums sit in the
-// workspace and one more kernel adds them in chunk order.
-#ifndef MXQ_SK_DENSE_MAX
-#define MXQ_SK_DENSE_MAX 64
-#endif
-constexpr int64_t kSkDenseTileGrid = 32, kSkDenseTileGrid8 = 96;
-constexpr int64_t kSkDenseLongK = 4096, kSkDenseLongKRows = 32;
-#ifndef MXQ_SK_DENSE_WG
-#define MXQ_SK_DENSE_WG 512
-#endif
-constexpr int64_t kSkDenseMaxRows = MXQ_SK_DENSE_MAX;
-constexpr int64_t kSkDenseWorkgroups = MXQ_SK_DENSE_WG;
-constexpr size_t kSkDenseMaxPartial = size_t(8) << 20;  // partial-sum bytes at most
-
-struct DenseSkinny {
-  bool on;
-  int32_t rows;        // rows per tile (8, or 4 when eight rows of the K chunk pass the LDS cap)
-  int32_t split;       // S
-  int64_t chunk;       // K elements per chunk
-  size_t partial_bytes;
-};
-
-DenseSkinny dense_skinny_plan(int64_t M, int64_t N, int64_t K) {
-  DenseSkinny p{false, 8, 1, K, 0};
-  if (kSkDenseMaxRows <= 0 || M < 1 || M > kSkDenseMaxRows || N < 1 || K < 128 || K % 128 != 0 ||
-      N * K >= (int64_t(1) << 32))
-    return p;
-  const bool long_k = K >= kSkDenseLongK && M <= kSkDenseLongKRows;
-  if (!long_k &&
-      cdiv(M, tile_rows(dense_tile_for(M))) * cdiv(N, int64_t(128)) > (M <= 8 ? kSkDenseTileGrid8 : kSkDenseTileGrid))
-    return p;
-  const int64_t steps = K / 128;
-  // eight rows per tile while their K chunk stays within 32 KB of LDS (several workgroups per
-  // compute unit), else four within 64 KB
-  for (const int ar : {8, 4}) {
-    int32_t S = 1;
-    const int64_t wgs = cdiv(M, int64_t(ar)) * skinny_dense_col_tiles(N);
-    while (S < 8 && wgs * S * 2 <= kSkDenseWorkgroups && steps >= 8 * S && size_t(4) * 2 * S * M * N <= kSkDenseMaxPartial)
-      S *= 2;
-    const int64_t chunk = cdiv(steps, int64_t(S)) * 128;
-    if (skinny_dense_lds(N, K, ar, S > 1 ? chunk : 0) > (ar == 8 ? size_t(32) << 10 : kSkinnyMaxLds)) continue;
-    p.on = true;
-    p.rows = ar;
-    p.split = S;
-    p.chunk = chunk;
-    p.partial_bytes = S > 1 ? align256(sizeof(float) * S * M * N) : 0;
-    break;
-  }
-  return p;
-}
-
-size_t block_linear_quant_bytes(int64_t M, int64_t K, int32_t a_dtype) {
-  if (a_dtype != MXQ_DTYPE_BF16 || M <= 0 || K <= 0) return 0;
-  return align256(size_t(M) * K) + align256(sizeof(float) * M * (K / 128));
-}
 
 size_t mxq_block_fp8_linear_workspace_size(int64_t M, int64_t N, int64_t K, int32_t a_dtype) {
   if (M <= 0 || N <= 0 || K <= 0 || (a_dtype != MXQ_DTYPE_BF16 && a_dtype != MXQ_DTYPE_E4M3)) return 0;
-  return block_linear_quant_bytes(M, K, a_dtype) + dense_skinny_plan(M, N, K).partial_bytes;
+  return block_linear_quant_bytes(M, K, a_dtype) + dense_skinny_plan(M, N, K, true).partial_bytes;
 }
 
 mxq_status mxq_block_fp8_linear(const void* A, int32_t a_dtype, const float* a_scale, int64_t M, int64_t K,
@@ -943,7 +1000,7 @@ mxq_status mxq_block_fp8_linear(const void* A, int32_t a_dtype, const float* a_s
   g.M = M;
   g.N = N;
   g.K = K;
-  const DenseSkinny sk = dense_skinny_plan(M, N, K);
+  const DenseSkinny sk = dense_skinny_plan(M, N, K, true);
   if (block_n == 128 && sk.on && int64_t(M) * lqa < (int64_t(1) << 32)) {
     if (sk.split > 1) {
       float* part = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + block_linear_quant_bytes(M, K, a_dtype));
@@ -953,10 +1010,10 @@ mxq_status mxq_block_fp8_linear(const void* A, int32_t a_dtype, const float* a_s
       gs.k_split = sk.split;
       gs.k_chunk = sk.chunk;
       gs.split_stride = M * N;
-      launch_skinny_dense(gs, sk.rows, true, st);
+      launch_skinny_dense(gs, sk.rows, true, true, st);
       launch_dense_split_sum(part, sk.split, M, N, static_cast<uint16_t*>(out), ldo, st);
     } else {
-      launch_skinny_dense(g, sk.rows, false, st);
+      launch_skinny_dense(g, sk.rows, true, false, st);
     }
   } else if ((block_n == 128 || block_n == 1) && M > 128 && K <= 16384 && int64_t(M) * lqa < (int64_t(1) << 32) &&
       N * K < (int64_t(1) << 32)) {

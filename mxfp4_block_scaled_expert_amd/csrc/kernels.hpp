@@ -183,15 +183,16 @@ void launch_gemv(const GemmArgs& a, int wfmt, bool a_e4m3, int row_mode, bool ou
 
 // Weight-streaming MFMA kernel for routed blocks of at most 4 rows (more rows are processed
 // 4 at a time); routed row modes only.
-// Dense W8A8 rows on the weight-streaming kernel (e4m3 activations and plain e4m3 weights with
-// 128 x 128 blocks, N * K < 2^32): tiles of `ar` (4 or 8) rows, 64 or 128 columns
-// (skinny_dense_col_tiles per row tile), K split by a.k_split / a.k_chunk (fp32 partial slices
-// when split, out_f32 then true), each workgroup staging only its K range in LDS
+// Dense rows on the weight-streaming kernel (e4m3 activations with 1x128 scales, or bf16
+// activations; plain e4m3 weights with 128 x 128 block scales -- a per-tensor scale is the grid
+// with strides 0 -- K a multiple of 128, N * K < 2^32): tiles of `ar` (4 or 8) rows, 64 or 128
+// columns (skinny_dense_col_tiles per row tile), K split by a.k_split / a.k_chunk (fp32 partial
+// slices when split, out_f32 then true), each workgroup staging only its K range in LDS
 // (skinny_dense_lds bytes for kstage staged elements, 0 = all of K); launch_dense_split_sum adds
 // the slices in chunk order into bf16.
-size_t skinny_dense_lds(int64_t N, int64_t K, int ar, int64_t kstage);
+size_t skinny_dense_lds(int64_t N, int64_t K, int ar, int64_t kstage, bool a_e4m3);
 int64_t skinny_dense_col_tiles(int64_t N);
-void launch_skinny_dense(const GemmArgs& a, int ar, bool out_f32, hipStream_t stream);
+void launch_skinny_dense(const GemmArgs& a, int ar, bool a_e4m3, bool out_f32, hipStream_t stream);
 void launch_dense_split_sum(const float* part, int32_t S, int64_t M, int64_t N, uint16_t* out, int64_t ldo,
                             hipStream_t stream);
 void launch_skinny(const GemmArgs& a, int wfmt, bool a_e4m3, int row_mode, bool out_f32, int64_t grid_blocks,

@@ -417,23 +417,31 @@ static void launch_skinny_mode(const GemmArgs& a, int wfmt, bool a_e4m3, bool ou
 
 // Dense W8A8 rows (e4m3 activations and weights in the plain layout, 128 x 128 weight blocks):
 // tiles of AR rows (8, or 4 when eight rows of K would pass the LDS cap), all launched at once.
-size_t skinny_dense_lds(int64_t N, int64_t K, int ar, int64_t kstage) {
-  return skinny_lds_layout(false, true, K, skinny_groups(N), ar, kstage).total;
+size_t skinny_dense_lds(int64_t N, int64_t K, int ar, int64_t kstage, bool a_e4m3) {
+  return skinny_lds_layout(false, a_e4m3, K, skinny_groups(N), ar, kstage).total;
 }
 
 int64_t skinny_dense_col_tiles(int64_t N) { return cdiv(N, int64_t(64 * skinny_groups(N))); }
 
-void launch_skinny_dense(const GemmArgs& a, int ar, bool out_f32, hipStream_t st) {
-  if (a.M <= 0 || a.N <= 0) return;
+template <bool AE>
+static void launch_skinny_dense_t(const GemmArgs& a, int ar, bool out_f32, hipStream_t st) {
   const int64_t tiles = cdiv(a.M, int64_t(ar));
-  const size_t lds = skinny_dense_lds(a.N, a.K, ar, a.k_split > 1 ? a.k_chunk : 0);
+  const size_t lds = skinny_dense_lds(a.N, a.K, ar, a.k_split > 1 ? a.k_chunk : 0, AE);
   if (skinny_groups(a.N) == 2) {
-    if (ar == 8) launch_skinny_ar<W_E4M3_BLOCK, true, ROWS_DENSE, false, 8, 2, 3>(a, out_f32, tiles, st, lds);
-    else launch_skinny_ar<W_E4M3_BLOCK, true, ROWS_DENSE, false, 4, 2, 3>(a, out_f32, tiles, st, lds);
+    if (ar == 8) launch_skinny_ar<W_E4M3_BLOCK, AE, ROWS_DENSE, false, 8, 2, 3>(a, out_f32, tiles, st, lds);
+    else launch_skinny_ar<W_E4M3_BLOCK, AE, ROWS_DENSE, false, 4, 2, 3>(a, out_f32, tiles, st, lds);
   } else {
-    if (ar == 8) launch_skinny_ar<W_E4M3_BLOCK, true, ROWS_DENSE, false, 8, 1, 4>(a, out_f32, tiles, st, lds);
-    else launch_skinny_ar<W_E4M3_BLOCK, true, ROWS_DENSE, false, 4, 1, 4>(a, out_f32, tiles, st, lds);
+    if (ar == 8) launch_skinny_ar<W_E4M3_BLOCK, AE, ROWS_DENSE, false, 8, 1, 4>(a, out_f32, tiles, st, lds);
+    else launch_skinny_ar<W_E4M3_BLOCK, AE, ROWS_DENSE, false, 4, 1, 4>(a, out_f32, tiles, st, lds);
   }
+}
+
+void launch_skinny_dense(const GemmArgs& a, int ar, bool a_e4m3, bool out_f32, hipStream_t st) {
+  if (a.M <= 0 || a.N <= 0) return;
+  if (a_e4m3)
+    launch_skinny_dense_t<true>(a, ar, out_f32, st);
+  else
+    launch_skinny_dense_t<false>(a, ar, out_f32, st);
 }
 
 // out[m, n] = bf16(sum over chunks c = 0 .. S-1, in that order, of part[c][m][n]); the bias rode

@@ -117,8 +117,11 @@ def fp8_scaled_mm(x: torch.Tensor, weight: torch.Tensor, scale: torch.Tensor,
     out = torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
     sc = scale.reshape(1).contiguous()
     b = None if bias is None else bias.contiguous()
-    st = L.load().mxq_fp8_scaled_mm(x2.data_ptr(), M, K, x2.stride(0), w.data_ptr(), N, sc.data_ptr(), _ptr(b),
-                                    _bias_dtype(b), out.data_ptr(), N, _stream())
+    lib = L.load()
+    ws_bytes = lib.mxq_fp8_scaled_mm_workspace_size(M, N, K)
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=x.device)
+    st = lib.mxq_fp8_scaled_mm(x2.data_ptr(), M, K, x2.stride(0), w.data_ptr(), N, sc.data_ptr(), _ptr(b),
+                               _bias_dtype(b), out.data_ptr(), N, ws.data_ptr(), ws_bytes, _stream())
     L.check("mxq_fp8_scaled_mm", st)
     return out.view(*x.shape[:-1], N)
 

@@ -50,7 +50,7 @@ def test_dispatch_struct_matches_header():
 
 def test_status_strings_and_version():
     L, lib = _lib()
-    assert lib.mxq_abi_version() == 12
+    assert lib.mxq_abi_version() == 13
     for code in range(0, 10):
         assert lib.mxq_status_string(code)
     assert b"unknown" in lib.mxq_status_string(99)
@@ -109,8 +109,16 @@ def test_argument_errors_before_any_launch():
     assert lib.mxq_per_token_group_quant_fp8(null, 4, 200, 200, 128, null, null, null) == L.MXQ_ERR_SHAPE
     assert lib.mxq_per_token_group_quant_fp8(null, 4, 256, 256, 128, null, null, null) == L.MXQ_ERR_NULL
     assert lib.mxq_per_token_group_quant_fp8(null, 0, 256, 256, 128, null, null, null) == L.MXQ_OK
-    assert lib.mxq_fp8_scaled_mm(null, 4, 100, 100, null, 8, null, null, 0, null, 8, null) == L.MXQ_ERR_SHAPE
-    assert lib.mxq_fp8_scaled_mm(null, 4, 128, 128, null, 8, null, null, 7, null, 8, null) == L.MXQ_ERR_NULL
+    assert lib.mxq_fp8_scaled_mm(null, 4, 100, 100, null, 8, null, null, 0, null, 8, null, 0, null) == L.MXQ_ERR_SHAPE
+    assert lib.mxq_fp8_scaled_mm(null, 4, 128, 128, null, 8, null, null, 7, null, 8, null, 0, null) == L.MXQ_ERR_NULL
+    # few rows with K a multiple of 128: a K split needs its partial sums in the workspace
+    assert lib.mxq_fp8_scaled_mm_workspace_size(97, 224, 576) == 0
+    n = lib.mxq_fp8_scaled_mm_workspace_size(1, 2048, 7168)
+    assert n > 0 and n % (4 * 2048) == 0 and n // (4 * 2048) in (2, 4, 8)
+    assert lib.mxq_fp8_scaled_mm_workspace_size(1, 2048, 7136) == 0  # K not a multiple of 128: the tiles
+    fake = C.c_void_p(1 << 20)
+    assert lib.mxq_fp8_scaled_mm(fake, 1, 7168, 7168, fake, 2048, fake, null, 0, fake, 2048, null, 0,
+                                 null) == L.MXQ_ERR_WORKSPACE
     # batched per-tensor: K % 32, lda, batch limit, overlapping outputs, strides, null pointers
     bmm = lib.mxq_fp8_scaled_bmm
     assert bmm(null, 2, 4, 100, 100, 400, null, 8, 800, null, 0, null, 0, 0, null, 8, 32, null) == L.MXQ_ERR_SHAPE

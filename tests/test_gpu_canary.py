@@ -76,15 +76,18 @@ def test_block_linear_writes_only_its_output(M, N, K, block_n):
     assert torch.equal(out.contiguous().view(torch.int16), ref.view(torch.int16))
 
 
-@pytest.mark.parametrize("M,N,K", [(97, 224, 576), (130, 200, 512), (1, 128, 32), (33, 136, 96)])
+@pytest.mark.parametrize("M,N,K", [(97, 224, 576), (130, 200, 512), (1, 128, 32), (33, 136, 96), (5, 998, 4096)])
 def test_per_tensor_mm_writes_only_its_output(M, N, K):
     lib = L.load()
     d = synth.dense_w8a16(M, N, K, seed=M * 3 + N + K, device=gpu())
     ref = ops.fp8_scaled_mm(d["a"], d["w"], d["scale"], d["bias"])
     ldo = N + 24
     full, out = _guarded(M, N, ldo, torch.bfloat16, CANARY16)
+    ws_n = lib.mxq_fp8_scaled_mm_workspace_size(M, N, K)
+    ws = torch.empty(max(ws_n, 1), dtype=torch.uint8, device=gpu())
     st = lib.mxq_fp8_scaled_mm(d["a"].data_ptr(), M, K, K, d["w"].data_ptr(), N, d["scale"].data_ptr(),
-                               d["bias"].data_ptr(), L.MXQ_DTYPE_F32, out.data_ptr(), ldo, _stream())
+                               d["bias"].data_ptr(), L.MXQ_DTYPE_F32, out.data_ptr(), ldo, ws.data_ptr(), ws_n,
+                               _stream())
     assert st == 0
     torch.cuda.synchronize()
     _assert_canaries(full, M, N, CANARY16)

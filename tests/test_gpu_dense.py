@@ -45,6 +45,23 @@ def test_fp8_scaled_mm_page_grid(M, N, K, scale_as_vector, has_bias):
     assert_bf16_close(bf16_bits(out), want, what=f"fp8_scaled_mm {M}x{N}x{K}")
 
 
+@pytest.mark.parametrize("M,N,K,stream", [(1, 2048, 7168, True), (5, 998, 4096, True), (16, 2048, 7168, True),
+                                          (3, 1024, 16384, True), (9, 4096, 4096, True), (16, 2048, 2048, False),
+                                          (32, 1024, 7168, False)])
+def test_fp8_scaled_mm_few_rows(M, N, K, stream):
+    """Few-row per-tensor W8A16 products with long K run on the weight-streaming kernel (the
+    scale applied to each 128-wide K block's partial sum, K split into chunks summed in chunk
+    order): one row, ragged rows and a column count that is not a multiple of 4, two row
+    tiles, K = 16384 staged a chunk at a time, 128-column tiles; and two neighbours that stay
+    on the tiles; each with a bias against the oracle."""
+    assert (L.load().mxq_fp8_scaled_mm_workspace_size(M, N, K) > 0) == stream
+    d = synth.dense_w8a16(M, N, K, seed=M + N + K, device=gpu())
+    out = ops.fp8_scaled_mm(d["a"], d["w"], d["scale"], d["bias"])
+    torch.cuda.synchronize()
+    want = OD.fp8_scaled_mm(bf16_bits(d["a"]), u8(d["w"]), float(f32(d["scale"])[0]), f32(d["bias"]))
+    assert_bf16_close(bf16_bits(out), want, what=f"fp8_scaled_mm few rows {M}x{N}x{K}")
+
+
 def test_fp8_scaled_mm_workload_and_bf16_bias_and_3d():
     d = synth.dense_w8a16(97, 224, 576, seed=1, device=gpu())
     x3 = d["a"].view(1, 97, 576)
@@ -57,6 +74,26 @@ def test_fp8_scaled_mm_workload_and_bf16_bias_and_3d():
 
 
 # ---- batched per-tensor W8A16 (MLA-style per-head products)
+
+def _mm_runs_tiles(M, K):
+    """A 2-D per-tensor call of few rows with K a multiple of 128 may run the weight-streaming
+    kernel, which groups the K sums differently; otherwise it runs the tiles the batched call
+    uses, bit for bit."""
+    return K % 128 != 0 or M > 64
+
+
+def _assert_entry(out_z, ref, d, z, scale_z, bias_z, what):
+    """Entry z of a batched call against the 2-D call: bit for bit where both run the tiles,
+    else both against the oracle."""
+    M, K = ref.shape[0], d["a"].shape[-1]
+    if _mm_runs_tiles(M, K):
+        assert torch.equal(out_z.view(torch.int16), ref.view(torch.int16)), what
+        return
+    want = OD.fp8_scaled_mm(bf16_bits(d["a"][z] if d["a"].dim() == 3 else d["a"]), u8(d["w"][z] if d["w"].dim() == 3 else d["w"]),
+                            float(f32(scale_z)[0]), None if bias_z is None else f32(bias_z))
+    assert_bf16_close(bf16_bits(ref), want, what=what + " (2-D)")
+    assert_bf16_close(bf16_bits(out_z), want, what=what + " (batched)")
+
 
 def _oracle_bmm(d, bias=None):
     B = d["a"].shape[0]
@@ -76,10 +113,10 @@ def test_fp8_scaled_bmm_matches_per_entry_products_and_oracle(B, M, N, K, per_en
     out = ops.fp8_scaled_bmm(d["a"], d["w"], d["scale"], d["bias"])
     torch.cuda.synchronize()
     assert out.shape == (B, M, N)
-    for z in range(B):  # every entry is the 2-D product, bit for bit
+    for z in range(B):  # every entry is the 2-D product (bit for bit where both run the tiles)
         sz = d["scale"][z if per_entry_scale else 0].reshape(1)
         ref = ops.fp8_scaled_mm(d["a"][z], d["w"][z], sz, d["bias"][z])
-        assert torch.equal(out[z].view(torch.int16), ref.view(torch.int16)), f"entry {z}"
+        _assert_entry(out[z], ref, d, z, sz, d["bias"][z], f"entry {z}")
     assert_bf16_close(bf16_bits(out), _oracle_bmm(d, f32(d["bias"])), what=f"bmm {B}x{M}x{N}x{K}")
 
 
@@ -121,14 +158,16 @@ def test_fp8_scaled_bmm_shared_inputs_through_the_c_abi():
     torch.cuda.synchronize()
     for z in range(B):
         ref = ops.fp8_scaled_mm(d["a"][0], d["w"][z], d["scale"][z].reshape(1))
-        assert torch.equal(out[z].view(torch.int16), ref.view(torch.int16))
+        _assert_entry(out[z], ref, {"a": d["a"][0], "w": d["w"][z]}, z, d["scale"][z].reshape(1), None,
+                      f"shared A, entry {z}")
     # per-entry A, shared W (entry 0) and shared scale
     assert lib.mxq_fp8_scaled_bmm(d["a"].data_ptr(), B, M, K, K, M * K, d["w"].data_ptr(), N, 0, d["scale"].data_ptr(),
                                   0, None, 0, 0, out.data_ptr(), N, M * N, st) == 0
     torch.cuda.synchronize()
     for z in range(B):
         ref = ops.fp8_scaled_mm(d["a"][z], d["w"][0], d["scale"][0].reshape(1))
-        assert torch.equal(out[z].view(torch.int16), ref.view(torch.int16))
+        _assert_entry(out[z], ref, {"a": d["a"][z], "w": d["w"][0]}, z, d["scale"][0].reshape(1), None,
+                      f"shared W, entry {z}")
     # overlapping outputs are refused before any launch
     assert lib.mxq_fp8_scaled_bmm(d["a"].data_ptr(), B, M, K, K, M * K, d["w"].data_ptr(), N, N * K,
                                   d["scale"].data_ptr(), 1, None, 0, 0, out.data_ptr(), N, N, st) == L.MXQ_ERR_SHAPE
@@ -260,7 +299,8 @@ def test_random_per_tensor_shapes_both_kernels_and_oracle(seed):
     """Seeded random per-tensor W8A16 shapes (M 1..300, N 16..700, K a multiple of 32 up to
     1024, with and without bias): a batched call large enough to run the register-staged
     kernel equals, entry by entry, the 2-D calls (the ring-fed kernel where the grid fits the
-    GPU and K > 128), and both match the oracle."""
+    GPU and K > 128; few rows with K a multiple of 128 may stream instead, checked against the
+    oracle), and both match the oracle."""
     rng = np.random.default_rng(500 + seed)
     M = int(rng.integers(1, 301))
     N = int(rng.integers(1, 44)) * 16
@@ -273,7 +313,8 @@ def test_random_per_tensor_shapes_both_kernels_and_oracle(seed):
         ref = ops.fp8_scaled_mm(d["a"][z], d["w"][z], d["scale"][z].reshape(1),
                                 None if d["bias"] is None else d["bias"][z])
         torch.cuda.synchronize()
-        assert torch.equal(out[z].view(torch.int16), ref.view(torch.int16)), f"M={M} N={N} K={K} entry {z}"
+        _assert_entry(out[z], ref, d, z, d["scale"][z].reshape(1), None if d["bias"] is None else d["bias"][z],
+                      f"M={M} N={N} K={K} entry {z}")
     want = _oracle_bmm(dict(d, a=d["a"][:2], w=d["w"][:2], scale=d["scale"][:2]),
                        None if d["bias"] is None else f32(d["bias"][:2]))
     assert_bf16_close(bf16_bits(out[:2]), want, what=f"random bmm M={M} N={N} K={K}")
