@@ -41,6 +41,19 @@ def test_library_exports_every_declared_symbol():
         assert n in L.SIGNATURES, f"{n} has no ctypes signature in the binding"
 
 
+def test_library_exports_no_undeclared_c_symbol():
+    """Every unmangled (C-linkage) function the library defines is declared in mxq.h: internal
+    helpers stay in C++ namespaces, out of the C ABI."""
+    import shutil
+    import subprocess
+    L, _ = _lib()
+    if shutil.which("nm") is None:
+        pytest.skip("nm not available")
+    out = subprocess.run(["nm", "-D", "--defined-only", L.LIB_PATH], capture_output=True, text=True, check=True).stdout
+    c_syms = {ln.split()[-1] for ln in out.splitlines() if ln.split()[-2:-1] == ["T"] and not ln.split()[-1].startswith("_Z")}
+    assert c_syms == set(_declared()), sorted(c_syms ^ set(_declared()))
+
+
 def test_dispatch_struct_matches_header():
     from mxfp4_block_scaled_expert_amd import _lib as L
     src = open(HEADER).read()
