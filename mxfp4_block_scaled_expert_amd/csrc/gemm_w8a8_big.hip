@@ -158,6 +158,12 @@ __global__ __launch_bounds__((BigCfg<BM, BN, NW, NS>::THREADS)) void gemm_w8a8_b
   const uint8_t* Wb = a.W + expert * a.w_estride;
   const float* swb = reinterpret_cast<const float*>(a.ws) + expert * a.ws_estride;
   const int KB = int(a.K >> 7);
+  // dense K split (blockIdx.y = chunk): K blocks [kb0, kb0 + nkb), fp32 partial sums to the
+  // chunk's slice of `out`; an empty chunk writes zeros
+  const int nsplit = MODE == ROWS_DENSE && a.k_split > 1 ? a.k_split : 1;
+  const int split = nsplit > 1 ? int(blockIdx.y) : 0;
+  const int kb0 = nsplit > 1 ? min(KB, split * int(a.k_chunk >> 7)) : 0;
+  const int nkb = nsplit > 1 ? min(KB - kb0, int(a.k_chunk >> 7)) : KB;
   constexpr int NSB = BN > 128 ? 2 : 1;  // 128-wide weight-scale blocks the tile spans
   // staged once, after the first operand DMA is in flight so the two latencies overlap
   auto stage_weight_scales = [&]() __attribute__((always_inline)) {
@@ -330,30 +336,31 @@ __global__ __launch_bounds__((BigCfg<BM, BN, NW, NS>::THREADS)) void gemm_w8a8_b
     // ---- K loop.  Loads retire in issue order.  Each iteration waits for its own stage,
     // publishes it with a barrier (which also retires every wave's reads of the stage the
     // next DMA overwrites), issues the DMA S - 1 blocks ahead, and computes.
+    // (j counts the workgroup's K blocks, kb0 + j is the block; without a split kb0 = 0, nkb = KB)
     if (S == 2) {
-      issue(0, 0);
+      if (nkb > 0) issue(kb0, 0);
       if (!SWCOL && m_base == 0) stage_weight_scales();
-      for (int kb = 0; kb < KB; ++kb) {
+      for (int j = 0; j < nkb; ++j) {
         wait_vmcnt<0>();
         __syncthreads();
-        if (kb + 1 < KB) issue(kb + 1, (kb + 1) & 1);
-        compute_rows(kb, kb & 1);
+        if (j + 1 < nkb) issue(kb0 + j + 1, (j + 1) & 1);
+        compute_rows(kb0 + j, j & 1);
       }
     } else {
-      // ops a copying wave has issued after DMA(kb) at the top of iteration kb: DMA(kb+1) when
+      // ops a copying wave has issued after DMA(j) at the top of iteration j: DMA(j+1) when
       // it exists (the other waves have none outstanding)
-      issue(0, 0);
-      if (KB > 1) issue(1, 1);
+      if (nkb > 0) issue(kb0, 0);
+      if (nkb > 1) issue(kb0 + 1, 1);
       if (!SWCOL && m_base == 0) stage_weight_scales();
       int s = 0;
-      for (int kb = 0; kb < KB; ++kb) {
-        if (kb + 1 < KB)
+      for (int j = 0; j < nkb; ++j) {
+        if (j + 1 < nkb)
           wait_vmcnt<kIssueOps>();
         else
           wait_vmcnt<0>();
         __syncthreads();
-        if (kb + 2 < KB) issue(kb + 2, s == 0 ? 2 : s - 1);
-        compute_rows(kb, s);
+        if (j + 2 < nkb) issue(kb0 + j + 2, s == 0 ? 2 : s - 1);
+        compute_rows(kb0 + j, s);
         s = s == S - 1 ? 0 : s + 1;
       }
     }
@@ -370,7 +377,7 @@ __global__ __launch_bounds__((BigCfg<BM, BN, NW, NS>::THREADS)) void gemm_w8a8_b
       for (int j = 0; j < 4; ++j) {
         const int64_t n = n0 + wn * 64 + 16 * j + 4 * q;
         float b[4] = {0.f, 0.f, 0.f, 0.f};
-        if (HAS_BIAS) {
+        if (HAS_BIAS && split == 0) {  // (a K split adds the bias on its first chunk only)
 #pragma unroll
           for (int r = 0; r < 4; ++r) b[r] = (n + r < a.N) ? load_bias(a, expert, n + r) : 0.f;
         }
@@ -413,11 +420,12 @@ __global__ __launch_bounds__((BigCfg<BM, BN, NW, NS>::THREADS)) void gemm_w8a8_b
         }
       }
     } else {
+      float* const outf = reinterpret_cast<float*>(a.out) + (nsplit > 1 ? split * a.split_stride : 0);
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int64_t n = n0 + wn * 64 + 16 * j + 4 * q;
         float b[4] = {0.f, 0.f, 0.f, 0.f};
-        if (HAS_BIAS) {
+        if (HAS_BIAS && split == 0) {  // (a K split adds the bias on its first chunk only)
 #pragma unroll
           for (int r = 0; r < 4; ++r) b[r] = (n + r < a.N) ? load_bias(a, expert, n + r) : 0.f;
         }
@@ -428,11 +436,11 @@ __global__ __launch_bounds__((BigCfg<BM, BN, NW, NS>::THREADS)) void gemm_w8a8_b
           const int64_t o = sOrow[ml] * a.ldo + n;
           const float v[4] = {acc[i][j][0] + b[0], acc[i][j][1] + b[1], acc[i][j][2] + b[2], acc[i][j][3] + b[3]};
           if (vec_store && n + 3 < a.N) {
-            *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(a.out) + o) = f32x4{v[0], v[1], v[2], v[3]};
+            *reinterpret_cast<f32x4*>(outf + o) = f32x4{v[0], v[1], v[2], v[3]};
           } else {
 #pragma unroll
             for (int r = 0; r < 4; ++r)
-              if (n + r < a.N) reinterpret_cast<float*>(a.out)[o + r] = v[r];
+              if (n + r < a.N) outf[o + r] = v[r];
           }
         }
       }
@@ -446,7 +454,8 @@ static void launch_big_t(const GemmArgs& a, bool out_f32, int64_t grid_blocks, h
   // whole rounds over the 8 XCDs; routed: every XCD's share of bands at full width
   const int64_t nwg = MODE == ROWS_DENSE ? cdiv(grid_blocks * n_tiles, 8) * 8
                                          : 8 * cdiv(cdiv(grid_blocks, kRoutedBand), 8) * kRoutedBand * n_tiles;
-  const dim3 grid(static_cast<unsigned>(nwg)), block(BigCfg<BM, BN, NW, NS>::THREADS);
+  const unsigned chunks = MODE == ROWS_DENSE && a.k_split > 1 ? unsigned(a.k_split) : 1u;
+  const dim3 grid(static_cast<unsigned>(nwg), chunks), block(BigCfg<BM, BN, NW, NS>::THREADS);
   const bool bias = a.bias != nullptr;
 #define MXQ_BIG_GO(OF, HB)                                                                                     \
   hipLaunchKernelGGL((gemm_w8a8_big_kernel<BM, BN, NW, NS, MODE, OF, HB, TL, SWC>), grid, block, 0, st, a, grid_blocks, \

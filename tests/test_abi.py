@@ -93,7 +93,13 @@ def test_workspace_queries():
     assert lib.mxq_block_fp8_linear_workspace_size(17, 7168, 2048, L.MXQ_DTYPE_E4M3) == 0
     # 4 row tiles of 8 x 16 column tiles of 64 = 64 workgroups: 8 chunks fill 512
     assert lib.mxq_block_fp8_linear_workspace_size(32, 1024, 7168, L.MXQ_DTYPE_E4M3) == 8 * 32 * 1024 * 4
-    assert lib.mxq_block_fp8_linear_workspace_size(65, 1024, 7168, L.MXQ_DTYPE_E4M3) == 0
+    # past 64 rows the weight-streaming path stops and the few-tile K split below takes over
+    assert lib.mxq_block_fp8_linear_workspace_size(65, 1024, 7168, L.MXQ_DTYPE_E4M3) == 8 * 65 * 1024 * 4
+    # 65..1024 rows on few 128 x 128 tiles with long K: the K split's partial sums (at most
+    # 16 MiB, M * K at most 8 M), 16 tiles of 128 x 128 here: 8 chunks
+    assert lib.mxq_block_fp8_linear_workspace_size(128, 2048, 7168, L.MXQ_DTYPE_E4M3) == 8 * 128 * 2048 * 4
+    assert lib.mxq_block_fp8_linear_workspace_size(2048, 2048, 7168, L.MXQ_DTYPE_E4M3) == 0  # 256 tiles
+    assert lib.mxq_block_fp8_linear_workspace_size(1025, 1024, 2048, L.MXQ_DTYPE_E4M3) == 0
     a = lib.mxq_fused_moe_workspace_size(4096, 7168, 2048, 256, 8, L.MXQ_WEIGHTS_FP8_BLOCK, 1)
     b = lib.mxq_fused_moe_workspace_size(4096, 7168, 2048, 256, 8, L.MXQ_WEIGHTS_FP8_BLOCK, 0)
     R = 4096 * 8

@@ -377,3 +377,20 @@ def test_block_linear_few_rows(M, N, K, prequant, split):
         assert torch.equal(out_q.view(torch.int16), out.view(torch.int16))
     torch.cuda.synchronize()
     assert_bf16_close(bf16_bits(out), _oracle_block(d), what=f"few-row block linear {M}x{N}x{K}")
+
+
+@pytest.mark.parametrize("M,N,K,block_n", [(128, 2048, 7168, 128), (300, 520, 4096, 128), (1000, 1024, 4096, 128),
+                                           (96, 998, 7168, 1), (65, 256, 8192, 128)])
+def test_block_linear_few_tiles_k_split(M, N, K, block_n):
+    """65 to 1024 rows whose 128 x 128 tiles leave the GPU mostly idle: each tile's K range runs
+    as 2, 4 or 8 chunks (workgroups of their own) writing fp32 partial sums, added in chunk
+    order by the split-sum kernel: ragged rows and columns, a column count that is not a
+    multiple of 4, per-column (1 x 128) weight scales, a bias added once, and one row past
+    the 64-row tiles; each against the oracle."""
+    lib = L.load()
+    part = lib.mxq_block_fp8_linear_workspace_size(M, N, K, L.MXQ_DTYPE_E4M3)
+    assert part > 0 and part % (4 * M * N) in (0, 256 - (4 * M * N) % 256) and part // (4 * M * N) in (2, 4, 8)
+    d = _block_case(M, N, K, block_n, seed=M + N + K, bias_dtype=torch.float32)
+    out = ops.block_fp8_linear(d["x"], d["w"], [block_n, 128], d["sw"], bias=d["bias"])
+    torch.cuda.synchronize()
+    assert_bf16_close(bf16_bits(out), _oracle_block(d), what=f"few-tile split {M}x{N}x{K} bn={block_n}")

@@ -109,3 +109,24 @@ def test_noalloc_few_rows_split_matches_on_two_calls():
         want = torch.empty(M, N, dtype=torch.bfloat16, device=dev)
         assert _call(lib, d, M, N, K, want, False, d["bias"], **kw) == L.MXQ_OK
         assert torch.equal(got.view(torch.int16), want.view(torch.int16)), f"{M}x{N}x{K}"
+
+
+@pytest.mark.gpu
+def test_noalloc_few_tiles_split_matches_on_two_calls():
+    """65..1024 rows on few tiles with long K: the K split's partial sums go to the static array.
+    Two calls in a row on one stream (the second smaller and ragged), each bit-identical to the
+    allocating entry point on the same inputs."""
+    lib = L.load()
+    dev = torch.device("cuda", 0)
+    outs = []
+    for M, N, K in [(128, 2048, 7168), (300, 520, 4096)]:
+        assert lib.mxq_block_fp8_linear_workspace_size(M, N, K, L.MXQ_DTYPE_E4M3) > 0  # the split runs
+        d = synth.block_linear(M, N, K, seed=M + N + K, device=dev, bias_dtype=torch.float32)
+        got = torch.empty(M, N, dtype=torch.bfloat16, device=dev)
+        assert _call(lib, d, M, N, K, got, True, d["bias"]) == L.MXQ_OK
+        outs.append((d, got, M, N, K))
+    torch.cuda.synchronize()
+    for d, got, M, N, K in outs:
+        want = torch.empty(M, N, dtype=torch.bfloat16, device=dev)
+        assert _call(lib, d, M, N, K, want, False, d["bias"]) == L.MXQ_OK
+        assert torch.equal(got.view(torch.int16), want.view(torch.int16)), f"{M}x{N}x{K}"
