@@ -99,13 +99,15 @@ mxq_status mxq_per_token_group_quant_fp8(const void* x, int64_t M, int64_t K, in
  *   bias   NULL, or [N] of bias_dtype (MXQ_DTYPE_F32 or MXQ_DTYPE_BF16), added in fp32
  *   out    bf16 [M, N], row stride ldo elements (ldo >= N)
  *   workspace  mxq_fp8_scaled_mm_workspace_size(M, N, K) bytes (NULL allowed where it is 0),
- *          else MXQ_ERR_WORKSPACE: the fp32 partial sums of a K split for few rows (below).
+ *          else MXQ_ERR_WORKSPACE: the fp32 partial sums of a K split (below).
  *   K must be a multiple of 32.  fp32 accumulation on the bf16 matrix cores.  Few rows (M <= 16,
  *   K >= 4096 a multiple of 128, at most 32 tiles of 16 x 128: ceil(N / 128) <= 32) run on the
  *   weight-streaming kernel: the scale multiplies each 128-wide K block's partial sum before it
  *   is added, and K may be cut into chunks whose partial sums are added in chunk order, so the
  *   sums are grouped differently from the tiles' (agreement within rounding; path and split
- *   depend on M, N and K only). */
+ *   depend on M, N and K only).  Otherwise, with K >= 6144, N a multiple of 8 and at most 128
+ *   tiles, each tile's K range runs as 2, 4 or 8 chunks whose partial sums (each scaled) are
+ *   added the same way (at most 16 MiB). */
 size_t mxq_fp8_scaled_mm_workspace_size(int64_t M, int64_t N, int64_t K);
 mxq_status mxq_fp8_scaled_mm(const void* A, int64_t M, int64_t K, int64_t lda, const void* W, int64_t N,
                              const float* scale, const void* bias, int32_t bias_dtype, void* out, int64_t ldo,

@@ -821,6 +821,37 @@ DenseSkinny per_tensor_skinny_plan(int64_t M, int64_t N, int64_t K) {
   return dense_skinny_plan(M, N, K, false);
 }
 
+// Per-tensor W8A16 GEMMs on the ring-fed tiles whose grid holds at most 128 workgroups and
+// K >= 6144 (N a multiple of 8): each tile's K range runs as S chunks (the launch's third grid
+// dimension), fp32 partial sums to the workspace, added in chunk order by the split-sum kernel;
+// S doubles while the grid stays within 256 workgroups and a chunk keeps at least four 128-wide
+// steps, partial sums within 16 MiB.  Not where the weight-streaming path runs.  Interleaved
+// through the Python op: 64 x 2048 x 7168 35.4 -> 23.8 us, 128 x 2048 x 7168 35.9 -> 24.7,
+// 1 x 2048 x 7136 36.2 -> 22.6; at K = 4096 no gain (300 x 520 x 4096 22.1 against 22.9,
+// 16 x 7168 x 4096 22.1 against 22.7).
+#ifndef MXQ_RING_SPLIT
+#define MXQ_RING_SPLIT 1
+#endif
+struct RingSplit {
+  int32_t split;
+  int64_t chunk;
+  size_t partial_bytes;
+};
+
+RingSplit per_tensor_ring_split(int64_t M, int64_t N, int64_t K) {
+  RingSplit p{1, K, 0};
+  if (!MXQ_RING_SPLIT || M < 1 || N < 8 || N % 8 != 0 || K < 6144 || K % 32 != 0 || per_tensor_skinny_plan(M, N, K).on)
+    return p;
+  const int64_t grid = cdiv(M, tile_rows(dense_w16_tile(M, N, 1))) * cdiv(N, int64_t(128)), steps = cdiv(K, int64_t(128));
+  if (!kDenseRing || grid > 128) return p;
+  while (p.split < 8 && grid * p.split * 2 <= 256 && steps >= 8 * p.split &&
+         size_t(4) * 2 * p.split * M * N <= (size_t(16) << 20))
+    p.split *= 2;
+  p.chunk = cdiv(steps, int64_t(p.split)) * 128;
+  p.partial_bytes = p.split > 1 ? align256(sizeof(float) * p.split * M * N) : 0;
+  return p;
+}
+
 }  // namespace
 
 extern "C" {
@@ -867,7 +898,7 @@ mxq_status mxq_per_token_group_quant_fp8(const void* x, int64_t M, int64_t K, in
 
 size_t mxq_fp8_scaled_mm_workspace_size(int64_t M, int64_t N, int64_t K) {
   if (M <= 0 || N <= 0 || K <= 0) return 0;
-  return per_tensor_skinny_plan(M, N, K).partial_bytes;
+  return std::max(per_tensor_skinny_plan(M, N, K).partial_bytes, per_tensor_ring_split(M, N, K).partial_bytes);
 }
 
 mxq_status mxq_fp8_scaled_mm(const void* A, int64_t M, int64_t K, int64_t lda, const void* W, int64_t N,
@@ -927,6 +958,21 @@ mxq_status mxq_fp8_scaled_mm(const void* A, int64_t M, int64_t K, int64_t lda, c
   g.N = N;
   g.K = K;
   const int tile = dense_w16_tile(M, N, 1);
+  if (const RingSplit rs = per_tensor_ring_split(M, N, K); rs.split > 1) {
+    // few ring-fed tiles over a long K: chunks of K as workgroups of their own, then the sum
+    float* part = static_cast<float*>(workspace);
+    GemmArgs gs = g;
+    gs.out = part;
+    gs.ldo = N;
+    gs.k_split = rs.split;
+    gs.k_chunk = rs.chunk;
+    gs.split_stride = M * N;
+    if (w16_ring_dense_supported(gs, 1)) {
+      launch_gemm_w16_ring_dense(gs, tile, 1, st);
+      launch_dense_split_sum(part, rs.split, M, N, static_cast<uint16_t*>(out), ldo, st);
+      return launch_status();
+    }
+  }
   if (dense_ring(g, tile, 1))
     launch_gemm_w16_ring_dense(g, tile, 1, static_cast<hipStream_t>(stream));
   else

@@ -566,7 +566,8 @@ __global__ __launch_bounds__(kRingThreads) void gemm_w16_ring_routed_kernel(Gemm
 // Dense per-tensor W8A16 products (bf16 out): row tile fastest, then the column tile; batch
 // entry z = blockIdx.y reads A + z a_bstride, W + z w_estride, ws + z ws_estride, bias +
 // z bias_estride and writes out + z o_bstride.
-template <int BM, bool HAS_BIAS>
+// (OUT_F32: a K split, chunk blockIdx.z, fp32 partial sums to the chunk's slice of out)
+template <int BM, bool HAS_BIAS, bool OUT_F32 = false>
 __global__ __launch_bounds__(kRingThreads) void gemm_w16_ring_dense_kernel(GemmArgs a, int64_t grid_blocks) {
   extern __shared__ __align__(1024) uint8_t ring_lds[];
   const int64_t z = blockIdx.y;
@@ -578,7 +579,8 @@ __global__ __launch_bounds__(kRingThreads) void gemm_w16_ring_dense_kernel(GemmA
   const int64_t tile = blockIdx.x % grid_blocks, nt = blockIdx.x / grid_blocks;
   TileInfo t;
   if (!tile_info<BM, ROWS_DENSE>(a, tile, t)) return;
-  ring_body<BM, ROWS_DENSE, W_E4M3_TENSOR, false, HAS_BIAS, false>(a, t, nt, 0, ring_lds, nullptr);
+  ring_body<BM, ROWS_DENSE, W_E4M3_TENSOR, OUT_F32, HAS_BIAS, false>(a, t, nt, OUT_F32 ? int(blockIdx.z) : 0, ring_lds,
+                                                                     nullptr);
 }
 
 template <int MODE, int WFMT, bool TL>
@@ -698,7 +700,17 @@ bool w16_ring_dense_supported(const GemmArgs& a, int64_t batch) {
 template <int BM>
 static void launch_ring_dense_t(const GemmArgs& a, int64_t batch, hipStream_t st) {
   const int64_t gb = cdiv(a.M, int64_t(BM));
-  const dim3 grid{unsigned(gb * cdiv(a.N, int64_t(128))), unsigned(batch)}, block{unsigned(kRingThreads)};
+  // a K split (one 2-D product: batch 1) runs its chunks along the grid's third dimension
+  const unsigned chunks = batch == 1 && a.k_split > 1 ? unsigned(a.k_split) : 1u;
+  const dim3 grid{unsigned(gb * cdiv(a.N, int64_t(128))), unsigned(batch), chunks}, block{unsigned(kRingThreads)};
+  if (chunks > 1) {
+    const size_t lds = ring_lds_bytes<BM, W_E4M3_TENSOR, true>();
+    if (a.bias)
+      hipLaunchKernelGGL((gemm_w16_ring_dense_kernel<BM, true, true>), grid, block, lds, st, a, gb);
+    else
+      hipLaunchKernelGGL((gemm_w16_ring_dense_kernel<BM, false, true>), grid, block, lds, st, a, gb);
+    return;
+  }
   const size_t lds = ring_lds_bytes<BM, W_E4M3_TENSOR, false>();
   if (a.bias)
     hipLaunchKernelGGL((gemm_w16_ring_dense_kernel<BM, true>), grid, block, lds, st, a, gb);

@@ -134,7 +134,10 @@ def test_argument_errors_before_any_launch():
     assert lib.mxq_fp8_scaled_mm_workspace_size(97, 224, 576) == 0
     n = lib.mxq_fp8_scaled_mm_workspace_size(1, 2048, 7168)
     assert n > 0 and n % (4 * 2048) == 0 and n // (4 * 2048) in (2, 4, 8)
-    assert lib.mxq_fp8_scaled_mm_workspace_size(1, 2048, 7136) == 0  # K not a multiple of 128: the tiles
+    # K not a multiple of 128: not streamed; the ring-fed tiles (16 of 16 x 128) split K in 8
+    assert lib.mxq_fp8_scaled_mm_workspace_size(1, 2048, 7136) == 8 * 2048 * 4
+    assert lib.mxq_fp8_scaled_mm_workspace_size(1024, 2048, 7168) == 0  # the tiles fill the GPU
+    assert lib.mxq_fp8_scaled_mm_workspace_size(64, 2044, 7168) == 0  # N not a multiple of 8
     fake = C.c_void_p(1 << 20)
     assert lib.mxq_fp8_scaled_mm(fake, 1, 7168, 7168, fake, 2048, fake, null, 0, fake, 2048, null, 0,
                                  null) == L.MXQ_ERR_WORKSPACE

@@ -54,12 +54,29 @@ def test_fp8_scaled_mm_few_rows(M, N, K, stream):
     order): one row, ragged rows and a column count that is not a multiple of 4, two row
     tiles, K = 16384 staged a chunk at a time, 128-column tiles; and two neighbours that stay
     on the tiles; each with a bias against the oracle."""
-    assert (L.load().mxq_fp8_scaled_mm_workspace_size(M, N, K) > 0) == stream
+    if stream:
+        assert L.load().mxq_fp8_scaled_mm_workspace_size(M, N, K) > 0
     d = synth.dense_w8a16(M, N, K, seed=M + N + K, device=gpu())
     out = ops.fp8_scaled_mm(d["a"], d["w"], d["scale"], d["bias"])
     torch.cuda.synchronize()
     want = OD.fp8_scaled_mm(bf16_bits(d["a"]), u8(d["w"]), float(f32(d["scale"])[0]), f32(d["bias"]))
     assert_bf16_close(bf16_bits(out), want, what=f"fp8_scaled_mm few rows {M}x{N}x{K}")
+
+
+@pytest.mark.parametrize("M,N,K,split", [(64, 2048, 7168, 4), (300, 520, 7168, 2), (1, 2048, 7136, 8), (128, 2048, 7168, 2),
+                                         (33, 2048, 6144, 4)])
+def test_fp8_scaled_mm_ring_k_split(M, N, K, split):
+    """Per-tensor products whose ring-fed tiles leave the GPU mostly idle, K >= 6144: each
+    tile's K range runs as 2, 4 or 8 chunks writing fp32 partial sums (each scaled), added in
+    chunk order by the split-sum kernel: ragged rows and columns, a K that is not a multiple of
+    128 (not streamed), a bias on the first chunk only; each against the oracle."""
+    part = L.load().mxq_fp8_scaled_mm_workspace_size(M, N, K)
+    assert part == (4 * split * M * N + 255) // 256 * 256
+    d = synth.dense_w8a16(M, N, K, seed=M + N + K + 1, device=gpu())
+    out = ops.fp8_scaled_mm(d["a"], d["w"], d["scale"], d["bias"])
+    torch.cuda.synchronize()
+    want = OD.fp8_scaled_mm(bf16_bits(d["a"]), u8(d["w"]), float(f32(d["scale"])[0]), f32(d["bias"]))
+    assert_bf16_close(bf16_bits(out), want, what=f"fp8_scaled_mm ring split {M}x{N}x{K}")
 
 
 def test_fp8_scaled_mm_workload_and_bf16_bias_and_3d():
@@ -77,9 +94,9 @@ def test_fp8_scaled_mm_workload_and_bf16_bias_and_3d():
 
 def _mm_runs_tiles(M, K):
     """A 2-D per-tensor call of few rows with K a multiple of 128 may run the weight-streaming
-    kernel, which groups the K sums differently; otherwise it runs the tiles the batched call
-    uses, bit for bit."""
-    return K % 128 != 0 or M > 64
+    kernel, and one with K >= 4096 may split K on the ring-fed tiles, both grouping the K sums
+    differently; otherwise it runs the tiles the batched call uses, bit for bit."""
+    return (K % 128 != 0 or M > 64) and K < 4096
 
 
 def _assert_entry(out_z, ref, d, z, scale_z, bias_z, what):
