@@ -213,16 +213,20 @@ mxq_status mxq_block_fp8_linear_noalloc(const void* A, int32_t a_dtype, const fl
  * mxq_mx_linear: out[m, n] = bf16( sum_k a[m, k] w[n, k] + bias[n] ),
  *   a = dec(qa) * 2^(sa - 127), w = dec(qw) * 2^(sw - 127), fp32 accumulation.
  *   A        a_dtype MXQ_DTYPE_BF16: bf16 [M, K] (row stride lda elements), quantised inside
- *            the call exactly as mxq_mxfp8_quant does (workspace of
- *            mxq_mx_linear_workspace_size bytes); a_dtype MXQ_DTYPE_E4M3: codes [M, K] (row
- *            stride lda bytes, a multiple of 16) with a_scale e8m0 [M, K/32] contiguous.
+ *            the call exactly as mxq_mxfp8_quant does; a_dtype MXQ_DTYPE_E4M3: codes [M, K]
+ *            (row stride lda bytes, a multiple of 16) with a_scale e8m0 [M, K/32] contiguous.
+ *   workspace  mxq_mx_linear_workspace_size(M, N, K, a_dtype) bytes (NULL allowed where it is
+ *            0), else MXQ_ERR_WORKSPACE: bf16 input's codes and scales, and -- with K >= 4096
+ *            on at most 128 tiles (128 or 256 rows x 256 columns) -- the fp32 partial sums of
+ *            a K split (2, 4 or 8 chunks added in chunk order: sums grouped differently,
+ *            agreement within rounding; at most 16 MiB).
  *   W        w_dtype MXQ_DTYPE_E4M3: e4m3 [N, K];  MXQ_DTYPE_E2M1: packed e2m1 [N, K/2];
  *            contiguous, with w_scale e8m0 [N, K/32] contiguous (4-byte aligned).
  *   bias     NULL or [N] of bias_dtype (fp32 or bf16), added in fp32
  *   out      bf16 [M, N], row stride ldo elements
  *   K must be a multiple of 128; every operand below 4 GiB (else MXQ_ERR_SHAPE). */
 mxq_status mxq_mxfp8_quant(const void* x, int64_t M, int64_t K, int64_t ldx, void* q, void* s, void* stream);
-size_t mxq_mx_linear_workspace_size(int64_t M, int64_t K, int32_t a_dtype);
+size_t mxq_mx_linear_workspace_size(int64_t M, int64_t N, int64_t K, int32_t a_dtype);
 mxq_status mxq_mx_linear(const void* A, int32_t a_dtype, const void* a_scale, int64_t M, int64_t K, int64_t lda,
                          const void* W, int32_t w_dtype, int64_t N, const void* w_scale, const void* bias,
                          int32_t bias_dtype, void* out, int64_t ldo, void* workspace, size_t workspace_bytes,

@@ -89,7 +89,7 @@ SIGNATURES = {
     "mxq_block_fp8_linear_noalloc": (_i32, [_p, _i32, _p, _i64, _i64, _i64, _p, _i64, _p, _i64, _i64, _i32,
                                              _i32, _p, _i32, _p, _i32, _i64, _p]),
     "mxq_mxfp8_quant": (_i32, [_p, _i64, _i64, _i64, _p, _p, _p]),
-    "mxq_mx_linear_workspace_size": (_sz, [_i64, _i64, _i32]),
+    "mxq_mx_linear_workspace_size": (_sz, [_i64, _i64, _i64, _i32]),
     "mxq_mx_linear": (_i32, [_p, _i32, _p, _i64, _i64, _i64, _p, _i32, _i64, _p, _p, _i32, _p, _i64, _p, _sz, _p]),
     "mxq_moe_max_blocks": (_i64, [_i64, _i32, _i32, _i32]),
     "mxq_moe_align": (_i32, [_p, _i64, _i32, _i32, _i32, _p, _p, _p, _p, _p]),

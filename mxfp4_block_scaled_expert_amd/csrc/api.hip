@@ -852,6 +852,33 @@ RingSplit per_tensor_ring_split(int64_t M, int64_t N, int64_t K) {
   return p;
 }
 
+// MX linears whose tiles (128 or 256 rows as launch_gemm_mx picks them, 256 columns) number at
+// most 128 and K >= 4096: each tile's K range runs as S chunks (the launch's second grid
+// dimension), fp32 partial sums to the workspace after the quantised activations, added in
+// chunk order by the split-sum kernel; S doubles while the grid stays within 256 workgroups and a
+// chunk keeps at least four 128-wide steps, partial sums within 16 MiB.
+#ifndef MXQ_MX_SPLIT
+#define MXQ_MX_SPLIT 1
+#endif
+RingSplit mx_split(int64_t M, int64_t N, int64_t K) {
+  RingSplit p{1, K, 0};
+  if (!MXQ_MX_SPLIT || M < 1 || N < 1 || K < 4096 || K % 128 != 0) return p;
+  const int64_t nt = cdiv(N, int64_t(256)), t128 = cdiv(M, int64_t(128)) * nt;
+  const int64_t tiles = (M <= 128 || t128 <= 256) ? t128 : cdiv(M, int64_t(256)) * nt, kb = K / 128;
+  if (tiles > 128) return p;
+  while (p.split < 8 && tiles * p.split * 2 <= 256 && kb >= 8 * p.split &&
+         size_t(4) * 2 * p.split * M * N <= (size_t(16) << 20))
+    p.split *= 2;
+  p.chunk = cdiv(kb, int64_t(p.split)) * 128;
+  p.partial_bytes = p.split > 1 ? align256(sizeof(float) * p.split * M * N) : 0;
+  return p;
+}
+
+size_t mx_quant_bytes(int64_t M, int64_t K, int32_t a_dtype) {
+  if (a_dtype != MXQ_DTYPE_BF16 || M <= 0 || K <= 0) return 0;
+  return align256(size_t(M) * K) + align256(size_t(M) * (K / 32));
+}
+
 }  // namespace
 
 extern "C" {
@@ -874,7 +901,7 @@ const char* mxq_status_string(mxq_status s) {
   }
 }
 
-int32_t mxq_abi_version(void) { return 13; }
+int32_t mxq_abi_version(void) { return 14; }
 
 mxq_status mxq_init(int32_t device) {
   if (hipSetDevice(device) != hipSuccess) return MXQ_ERR_ARCH;
@@ -1157,9 +1184,9 @@ mxq_status mxq_mxfp8_quant(const void* x, int64_t M, int64_t K, int64_t ldx, voi
   return launch_status();
 }
 
-size_t mxq_mx_linear_workspace_size(int64_t M, int64_t K, int32_t a_dtype) {
-  if (a_dtype != MXQ_DTYPE_BF16 || M <= 0 || K <= 0) return 0;
-  return align256(size_t(M) * K) + align256(size_t(M) * (K / 32));
+size_t mxq_mx_linear_workspace_size(int64_t M, int64_t N, int64_t K, int32_t a_dtype) {
+  if (M <= 0 || N <= 0 || K <= 0 || (a_dtype != MXQ_DTYPE_BF16 && a_dtype != MXQ_DTYPE_E4M3)) return 0;
+  return mx_quant_bytes(M, K, a_dtype) + mx_split(M, N, K).partial_bytes;
 }
 
 mxq_status mxq_mx_linear(const void* A, int32_t a_dtype, const void* a_scale, int64_t M, int64_t K, int64_t lda,
@@ -1190,9 +1217,9 @@ mxq_status mxq_mx_linear(const void* A, int32_t a_dtype, const void* a_scale, in
   g.lda = lda;
   g.sa = a_scale;
   g.lds_bytes = K / 32;
+  const size_t need = mxq_mx_linear_workspace_size(M, N, K, a_dtype);
+  if (need > 0 && (!workspace || workspace_bytes < need)) return MXQ_ERR_WORKSPACE;
   if (a_dtype == MXQ_DTYPE_BF16) {
-    const size_t need = mxq_mx_linear_workspace_size(M, K, a_dtype);
-    if (!workspace || workspace_bytes < need) return MXQ_ERR_WORKSPACE;
     uint8_t* q = static_cast<uint8_t*>(workspace);
     uint8_t* s = q + align256(size_t(M) * K);
     launch_quant_mx(static_cast<const uint16_t*>(A), M, K, lda, q, s, st);
@@ -1212,6 +1239,19 @@ mxq_status mxq_mx_linear(const void* A, int32_t a_dtype, const void* a_scale, in
   g.M = M;
   g.N = N;
   g.K = K;
+  if (const RingSplit sp = mx_split(M, N, K); sp.split > 1) {
+    // few tiles over a long K: chunks of K as workgroups of their own, then the sum
+    float* part = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + mx_quant_bytes(M, K, a_dtype));
+    MxArgs gs = g;
+    gs.out = part;
+    gs.ldo = N;
+    gs.k_split = sp.split;
+    gs.k_chunk = sp.chunk;
+    gs.split_stride = M * N;
+    launch_gemm_mx(gs, st);
+    launch_dense_split_sum(part, sp.split, M, N, static_cast<uint16_t*>(out), ldo, st);
+    return launch_status();
+  }
   launch_gemm_mx(g, st);
   return launch_status();
 }

@@ -78,7 +78,8 @@ __device__ __forceinline__ f32x4 mfma_mx(const i32x8& w, const i32x8& a, const f
 
 }  // namespace
 
-template <int BM, int WFMT, bool HAS_BIAS>
+// OUT_F32: a K split -- chunk blockIdx.y runs its K steps and writes fp32 partial sums
+template <int BM, int WFMT, bool HAS_BIAS, bool OUT_F32 = false>
 __global__ __launch_bounds__(512) void gemm_mx_kernel(MxArgs a, int64_t row_tiles, int64_t n_tiles) {
   using C = MxCfg<BM, WFMT>;
   constexpr int TI = C::TI, WROWS = C::WROWS;
@@ -197,14 +198,55 @@ __global__ __launch_bounds__(512) void gemm_mx_kernel(MxArgs a, int64_t row_tile
   // K loop: wait for this stage, publish it with a barrier (which also retires every wave's
   // reads of the stage the next copy overwrites), copy the next K step, compute
   const int KB = int(a.K / kMxK);
-  issue(0, 0);
-  for (int kb = 0; kb < KB; ++kb) {
+  // the workgroup's K steps [kb0, kb0 + nkb) (all of them without a split; an empty chunk
+  // writes zeros)
+  const int split = OUT_F32 ? int(blockIdx.y) : 0;
+  const int kb0 = OUT_F32 ? min(KB, split * int(a.k_chunk / kMxK)) : 0;
+  const int nkb = OUT_F32 ? min(KB - kb0, int(a.k_chunk / kMxK)) : KB;
+  if (nkb > 0) issue(kb0, 0);
+  for (int j = 0; j < nkb; ++j) {
     wait_vmcnt<0>();
     __syncthreads();
-    if (kb + 1 < KB) issue(kb + 1, (kb + 1) & 1);
-    compute(kb & 1);
+    if (j + 1 < nkb) issue(kb0 + j + 1, (j + 1) & 1);
+    compute(j & 1);
   }
   wait_vmcnt<0>();
+
+  if constexpr (OUT_F32) {
+    // fp32 partial sums straight from the accumulators: lane owns rows mrow + 16 i + l16,
+    // columns n0 + wn*64 + 16 j + 4 q .. + 3; the bias on chunk 0
+    float* const outf = reinterpret_cast<float*>(a.out) + split * a.split_stride;
+    const bool vec4 = (reinterpret_cast<uintptr_t>(outf) & 15) == 0 && (a.ldo & 3) == 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int64_t n = n0 + wn * 64 + 16 * j + 4 * q;
+      float bias[4] = {0.f, 0.f, 0.f, 0.f};
+      if (HAS_BIAS && split == 0) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int64_t c = min<int64_t>(n + r, a.N - 1);
+          bias[r] = a.bias_bf16 ? bf16f(reinterpret_cast<const uint16_t*>(a.bias)[c])
+                                : reinterpret_cast<const float*>(a.bias)[c];
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < TI; ++i) {
+        const int ml = mrow + 16 * i + l16;
+        if (ml >= m_size) continue;
+        float* o = outf + (m0 + ml) * a.ldo + n;
+        const float v[4] = {acc[i][j][0] + bias[0], acc[i][j][1] + bias[1], acc[i][j][2] + bias[2],
+                            acc[i][j][3] + bias[3]};
+        if (vec4 && n + 4 <= a.N) {
+          *reinterpret_cast<f32x4*>(o) = f32x4{v[0], v[1], v[2], v[3]};
+        } else {
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            if (n + r < a.N) o[r] = v[r];
+        }
+      }
+    }
+    return;
+  }
 
   // epilogue: lane owns rows mrow + 16 i + l16, columns n0 + wn*64 + 16 j + 4 q .. + 3.  Each
   // wave's WROWS x 64 bf16 block goes through LDS (the operand stages are free) and leaves as
@@ -259,7 +301,15 @@ __global__ __launch_bounds__(512) void gemm_mx_kernel(MxArgs a, int64_t row_tile
 template <int BM, int WFMT>
 static void launch_mx_t(const MxArgs& a, hipStream_t st) {
   const int64_t row_tiles = cdiv(a.M, int64_t(BM)), n_tiles = cdiv(a.N, int64_t(256));
-  const dim3 grid(static_cast<unsigned>(cdiv(row_tiles * n_tiles, 8) * 8)), block(512);
+  const unsigned chunks = a.k_split > 1 ? unsigned(a.k_split) : 1u;
+  const dim3 grid(static_cast<unsigned>(cdiv(row_tiles * n_tiles, 8) * 8), chunks), block(512);
+  if (chunks > 1) {
+    if (a.bias)
+      hipLaunchKernelGGL((gemm_mx_kernel<BM, WFMT, true, true>), grid, block, 0, st, a, row_tiles, n_tiles);
+    else
+      hipLaunchKernelGGL((gemm_mx_kernel<BM, WFMT, false, true>), grid, block, 0, st, a, row_tiles, n_tiles);
+    return;
+  }
   if (a.bias)
     hipLaunchKernelGGL((gemm_mx_kernel<BM, WFMT, true>), grid, block, 0, st, a, row_tiles, n_tiles);
   else

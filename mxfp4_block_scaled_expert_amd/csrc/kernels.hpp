@@ -121,6 +121,11 @@ struct MxArgs {
   void* out;           // bf16 [M, N], row stride ldo elements
   int64_t ldo;
   int64_t M, N, K;     // K % 128 == 0
+  // K split: k_split > 1 chunks of k_chunk elements (a multiple of 128), chunk c (blockIdx.y)
+  // writing fp32 partial sums to out + c * split_stride floats (row stride ldo); the bias rides
+  // on chunk 0
+  int32_t k_split;
+  int64_t k_chunk, split_stride;
 };
 void launch_gemm_mx(const MxArgs& a, hipStream_t stream);
 // bf16 [M, K] (row stride ldx) -> e4m3 [M, K] (contiguous) + e8m0 [M, K/32] (contiguous)

@@ -281,7 +281,7 @@ def mx_linear(x: torch.Tensor, weight: torch.Tensor, weight_scale: torch.Tensor,
     if out is None:
         out = torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
     lib = L.load()
-    ws_bytes = lib.mxq_mx_linear_workspace_size(M, K, a_dtype)
+    ws_bytes = lib.mxq_mx_linear_workspace_size(M, N, K, a_dtype)
     ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=x.device)
     st = lib.mxq_mx_linear(a.data_ptr(), a_dtype, _ptr(a_scale), M, K, a.stride(0), w.data_ptr(), _MX_W[w_format], N,
                            sw.data_ptr(), _ptr(b), _bias_dtype(b), out.data_ptr(), N, ws.data_ptr(), ws_bytes,

@@ -63,7 +63,7 @@ def test_dispatch_struct_matches_header():
 
 def test_status_strings_and_version():
     L, lib = _lib()
-    assert lib.mxq_abi_version() == 13
+    assert lib.mxq_abi_version() == 14
     for code in range(0, 10):
         assert lib.mxq_status_string(code)
     assert b"unknown" in lib.mxq_status_string(99)

@@ -113,6 +113,22 @@ def test_mx_linear_tile_rows_from_the_grid(shape, w_format):
 
 
 @pytest.mark.parametrize("w_format", ["e2m1", "e4m3"])
+@pytest.mark.parametrize("shape,split", [((300, 520, 4096), 8), ((100, 1000, 7168), 8)])
+def test_mx_linear_few_tiles_k_split(shape, split, w_format):
+    """MX linears on few tiles with K >= 4096: each tile's K range runs as chunks writing fp32
+    partial sums (the bias on the first only), added in chunk order: ragged rows and columns;
+    against the oracle."""
+    M, N, K = shape
+    lib = L.load()
+    part = lib.mxq_mx_linear_workspace_size(M, N, K, L.MXQ_DTYPE_E4M3)
+    assert part == (4 * split * M * N + 255) // 256 * 256
+    d = synth.mx_linear(M, N, K, seed=M + N + K, device=gpu(), w_format=w_format, bias_dtype=torch.float32)
+    out = ops.mx_linear(d["x"], d["w"], d["sw"], w_format, bias=d["bias"])
+    torch.cuda.synchronize()
+    assert_bf16_close(bf16_bits(out), _oracle_linear(d), what=f"mx split {w_format} {M}x{N}x{K}")
+
+
+@pytest.mark.parametrize("w_format", ["e2m1", "e4m3"])
 def test_mx_linear_prequantised_bf16_bias_and_3d(w_format):
     d = synth.mx_linear(34, 384, 640, seed=9, device=gpu(), w_format=w_format, bias_dtype=torch.bfloat16)
     q, s = ops.mxfp8_quant(d["x"])
@@ -165,7 +181,7 @@ def test_mx_linear_writes_only_its_output_and_refuses_bad_arguments():
     canary = 0x7FBF
     buf = torch.full(((M + 6) * ldo,), np.int16(np.uint16(canary).view(np.int16)), dtype=torch.int16, device=gpu())
     out = buf.view(M + 6, ldo)[3:3 + M, :N].view(torch.bfloat16)
-    n = lib.mxq_mx_linear_workspace_size(M, K, L.MXQ_DTYPE_BF16)
+    n = lib.mxq_mx_linear_workspace_size(M, N, K, L.MXQ_DTYPE_BF16)
     ws = torch.empty(n, dtype=torch.uint8, device=gpu())
     sh = torch.cuda.current_stream().cuda_stream
     assert lib.mxq_mx_linear(d["x"].data_ptr(), L.MXQ_DTYPE_BF16, None, M, K, K, d["w"].data_ptr(), L.MXQ_DTYPE_E2M1,
