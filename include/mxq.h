@@ -162,8 +162,8 @@ mxq_status mxq_fp8_scaled_bmm(const void* A, int64_t batch, int64_t M, int64_t K
  *   weight-streaming kernel (tiles of 4 or 8 rows, each workgroup staging only its K chunk); that
  *   path may cut K into chunks of whole 128-wide blocks whose partial sums are added in chunk
  *   order, so its sums are grouped differently from the tiles' (the result agrees within
- *   rounding; path and split depend on M, N and K only, and with 1 x 128 weight blocks the
- *   tiles run and the partial-sum space goes unused).  65..1024 rows on few 128 x 128 tiles
+ *   rounding; path and split depend on M, N, K and the weight recipe only; the workspace size
+ *   covers either recipe).  65..1024 rows on few 128 x 128 tiles
  *   with K >= 4096 (and M * K <= 8 M) split each tile's K range the same way (partial sums at
  *   most 16 MiB). */
 size_t mxq_block_fp8_linear_workspace_size(int64_t M, int64_t N, int64_t K, int32_t a_dtype);

@@ -738,7 +738,8 @@ struct DenseSkinny {
   size_t partial_bytes;
 };
 
-DenseSkinny dense_skinny_plan(int64_t M, int64_t N, int64_t K, bool a_e4m3) {
+// (swcol: 1 x 128 weight blocks, whose per-column scales of a K chunk also sit in LDS)
+DenseSkinny dense_skinny_plan(int64_t M, int64_t N, int64_t K, bool a_e4m3, bool swcol = false) {
   DenseSkinny p{false, 8, 1, K, 0};
   if (kSkDenseMaxRows <= 0 || M < 1 || M > kSkDenseMaxRows || N < 1 || K < 128 || K % 128 != 0 ||
       N * K >= (int64_t(1) << 32))
@@ -756,7 +757,8 @@ DenseSkinny dense_skinny_plan(int64_t M, int64_t N, int64_t K, bool a_e4m3) {
     while (S < 8 && wgs * S * 2 <= kSkDenseWorkgroups && steps >= 8 * S && size_t(4) * 2 * S * M * N <= kSkDenseMaxPartial)
       S *= 2;
     const int64_t chunk = cdiv(steps, int64_t(S)) * 128;
-    if (skinny_dense_lds(N, K, ar, S > 1 ? chunk : 0, a_e4m3) > (ar == 8 ? size_t(32) << 10 : kSkinnyMaxLds)) continue;
+    if (skinny_dense_lds(N, K, ar, S > 1 ? chunk : 0, a_e4m3, swcol) > (ar == 8 ? size_t(32) << 10 : kSkinnyMaxLds))
+      continue;
     p.on = true;
     p.rows = ar;
     p.split = S;
@@ -1053,8 +1055,10 @@ mxq_status mxq_fp8_scaled_bmm(const void* A, int64_t batch, int64_t M, int64_t K
 
 size_t mxq_block_fp8_linear_workspace_size(int64_t M, int64_t N, int64_t K, int32_t a_dtype) {
   if (M <= 0 || N <= 0 || K <= 0 || (a_dtype != MXQ_DTYPE_BF16 && a_dtype != MXQ_DTYPE_E4M3)) return 0;
+  // (the weight recipe is not an argument: room for whichever plan either recipe takes)
   return block_linear_quant_bytes(M, K, a_dtype) +
-         std::max(dense_skinny_plan(M, N, K, true).partial_bytes, dense_big_split(M, N, K).partial_bytes);
+         std::max({dense_skinny_plan(M, N, K, true).partial_bytes, dense_skinny_plan(M, N, K, true, true).partial_bytes,
+                   dense_big_split(M, N, K).partial_bytes});
 }
 
 mxq_status mxq_block_fp8_linear(const void* A, int32_t a_dtype, const float* a_scale, int64_t M, int64_t K,
@@ -1106,8 +1110,8 @@ mxq_status mxq_block_fp8_linear(const void* A, int32_t a_dtype, const float* a_s
   g.M = M;
   g.N = N;
   g.K = K;
-  const DenseSkinny sk = dense_skinny_plan(M, N, K, true);
-  if (block_n == 128 && sk.on && int64_t(M) * lqa < (int64_t(1) << 32)) {
+  const DenseSkinny sk = dense_skinny_plan(M, N, K, true, block_n == 1);
+  if ((block_n == 128 || block_n == 1) && sk.on && int64_t(M) * lqa < (int64_t(1) << 32)) {
     if (sk.split > 1) {
       float* part = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + block_linear_quant_bytes(M, K, a_dtype));
       GemmArgs gs = g;
@@ -1116,10 +1120,10 @@ mxq_status mxq_block_fp8_linear(const void* A, int32_t a_dtype, const float* a_s
       gs.k_split = sk.split;
       gs.k_chunk = sk.chunk;
       gs.split_stride = M * N;
-      launch_skinny_dense(gs, sk.rows, true, true, st);
+      launch_skinny_dense(gs, sk.rows, true, true, st, block_n == 1);
       launch_dense_split_sum(part, sk.split, M, N, static_cast<uint16_t*>(out), ldo, st);
     } else {
-      launch_skinny_dense(g, sk.rows, true, false, st);
+      launch_skinny_dense(g, sk.rows, true, false, st, block_n == 1);
     }
   } else if (const BigSplit bs = dense_big_split(M, N, K);
              bs.split > 1 && (block_n == 128 || block_n == 1) && int64_t(M) * lqa < (int64_t(1) << 32)) {

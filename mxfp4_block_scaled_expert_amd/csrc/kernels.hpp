@@ -195,9 +195,11 @@ void launch_gemv(const GemmArgs& a, int wfmt, bool a_e4m3, int row_mode, bool ou
 // slices when split, out_f32 then true), each workgroup staging only its K range in LDS
 // (skinny_dense_lds bytes for kstage staged elements, 0 = all of K); launch_dense_split_sum adds
 // the slices in chunk order into bf16.
-size_t skinny_dense_lds(int64_t N, int64_t K, int ar, int64_t kstage, bool a_e4m3);
+// swcol: per-column (1 x 128) weight scales, e4m3 activations only.
+size_t skinny_dense_lds(int64_t N, int64_t K, int ar, int64_t kstage, bool a_e4m3, bool swcol = false);
 int64_t skinny_dense_col_tiles(int64_t N);
-void launch_skinny_dense(const GemmArgs& a, int ar, bool a_e4m3, bool out_f32, hipStream_t stream);
+void launch_skinny_dense(const GemmArgs& a, int ar, bool a_e4m3, bool out_f32, hipStream_t stream,
+                         bool swcol = false);
 void launch_dense_split_sum(const float* part, int32_t S, int64_t M, int64_t N, uint16_t* out, int64_t ldo,
                             hipStream_t stream);
 void launch_skinny(const GemmArgs& a, int wfmt, bool a_e4m3, int row_mode, bool out_f32, int64_t grid_blocks,

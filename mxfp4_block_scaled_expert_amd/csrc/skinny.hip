@@ -60,8 +60,9 @@ struct SkinnyLds {
   uint32_t sw_off, sa_off, total;
 };
 
+// swcol: per-column weight scales (1 x 128 blocks) of the staged K steps, [steps][64 G]
 __host__ __device__ inline SkinnyLds skinny_lds_layout(bool mx, bool a_e4m3, int64_t K, int G, int AR,
-                                                      int64_t kstage = 0) {
+                                                      int64_t kstage = 0, bool swcol = false) {
   SkinnyLds L;
   const int kstep = mx ? 256 : 128;
   const int ae = a_e4m3 ? 1 : 2;
@@ -71,13 +72,15 @@ __host__ __device__ inline SkinnyLds skinny_lds_layout(bool mx, bool a_e4m3, int
   L.kb = int(K >> 7);
   L.nb = G >= 2 ? G / 2 : 1;
   L.sw_off = uint32_t(AR * L.row_stride);
-  const uint32_t sw_bytes = mx ? 0u : uint32_t(L.kb * L.nb * 4);
+  const uint32_t sw_bytes = mx ? 0u : swcol ? uint32_t((L.row_stride - 16) / (kstep * ae) * 64 * G * 4)
+                                              : uint32_t(L.kb * L.nb * 4);
   L.sa_off = (L.sw_off + sw_bytes + 15u) & ~15u;
   L.total = L.sa_off + (a_e4m3 ? uint32_t(L.kb * AR * 4) : 0u);
   return L;
 }
 
-template <int WFMT, bool A_E4M3, int MODE, bool OUT_F32, bool HAS_BIAS, bool TILED, int AR, int G, int D>
+template <int WFMT, bool A_E4M3, int MODE, bool OUT_F32, bool HAS_BIAS, bool TILED, int AR, int G, int D,
+          bool SWCOL = false>
 __global__ __launch_bounds__(256, (SkinnyShape<WFMT, A_E4M3>::W)) void skinny_kernel(GemmArgs a,
                                                                                      int64_t grid_blocks) {
   constexpr bool MX = WFMT == W_E2M1_MX;
@@ -106,7 +109,8 @@ __global__ __launch_bounds__(256, (SkinnyShape<WFMT, A_E4M3>::W)) void skinny_ke
   // dense: a tile is AR consecutive rows (one pass); routed: a tile is one expert block
   if (!tile_info<(MODE == ROWS_DENSE ? AR : 1), MODE>(a, tile, t)) return;
 
-  const SkinnyLds L = skinny_lds_layout(MX, A_E4M3, K, G, AR, nsplit > 1 ? a.k_chunk : 0);
+  static_assert(!SWCOL || (A_E4M3 && !MX && MODE == ROWS_DENSE), "per-column weight scales: dense W8A8 rows");
+  const SkinnyLds L = skinny_lds_layout(MX, A_E4M3, K, G, AR, nsplit > 1 ? a.k_chunk : 0, SWCOL);
   const int nsteps = L.kpad / KSTEP;
   // this workgroup's K steps [st_b, st_e); an empty range (a chunk past K) stores zeros
   int st_b = 0, st_e = nsteps;
@@ -234,6 +238,15 @@ __global__ __launch_bounds__(256, (SkinnyShape<WFMT, A_E4M3>::W)) void skinny_ke
         float* s_sw = reinterpret_cast<float*>(smem + L.sw_off);
         const float* swe = reinterpret_cast<const float*>(a.ws) + t.expert * a.ws_estride;
         const int64_t nb_total = (N + 127) / 128;
+        if constexpr (SWCOL) {
+          // the scales of the workgroup's 64 G columns over its K steps, [step - st_b][column]
+          constexpr int NCOL = 64 * G;
+          for (int c = tid; c < (st_e - st_b) * NCOL; c += 256) {
+            const int j = c / NCOL, cl = c - j * NCOL;
+            const int64_t col = min<int64_t>(n0 + cl, N - 1);
+            s_sw[c] = swe[col * a.ws_s0 + int64_t(st_b + j) * a.ws_s1];
+          }
+        } else
         for (int c = tid; c < L.kb * L.nb; c += 256) {
           const int kb = c / L.nb, nb = c - kb * L.nb;
           const int64_t gnb = min<int64_t>((n0 >> 7) + nb, nb_total - 1);
@@ -283,7 +296,9 @@ __global__ __launch_bounds__(256, (SkinnyShape<WFMT, A_E4M3>::W)) void skinny_ke
           const i32x4 w1 = wb[slot][g][1];
           const i32x8 bf = {w0[0], w0[1], w0[2], w0[3], w1[0], w1[1], w1[2], w1[3]};
           const f32x4 part = mfma_16x16x128_e4m3(af, bf, f32x4{0.f, 0.f, 0.f, 0.f});
-          const float sw = s_sw[st * L.nb + ((g * kSkWaves + wave) >> 3)];
+          // (per-column scales: this lane's output column, (g * kSkWaves + wave) * 16 + l16)
+          const float sw = SWCOL ? s_sw[(st - st_b) * (64 * G) + (g * kSkWaves + wave) * 16 + l16]
+                                 : s_sw[st * L.nb + ((g * kSkWaves + wave) >> 3)];
 #pragma unroll
           for (int r = 0; r < 4; ++r) acc[g][r] = fmaf(part[r], sw * sa[r], acc[g][r]);
         }
@@ -370,7 +385,7 @@ size_t skinny_lds_bytes(int wfmt, bool a_e4m3, int64_t K) {
   return skinny_lds_t<W_E4M3_BLOCK, false>(K, skinny_rows_t<W_E4M3_BLOCK, false>(K, 2), 2);
 }
 
-template <int WFMT, bool AE, int MODE, bool TL, int AR, int G, int D>
+template <int WFMT, bool AE, int MODE, bool TL, int AR, int G, int D, bool SWC = false>
 static void launch_skinny_ar(const GemmArgs& a, bool out_f32, int64_t gb, hipStream_t st, size_t lds_bytes = 0) {
   const int64_t n_tiles = cdiv(a.N, int64_t(64 * G));
   const int64_t nsplit = a.k_split > 1 ? a.k_split : 1;
@@ -379,7 +394,7 @@ static void launch_skinny_ar(const GemmArgs& a, bool out_f32, int64_t gb, hipStr
   const size_t lds = lds_bytes > 0 ? lds_bytes : skinny_lds_t<WFMT, AE>(a.K, AR, G);
   const bool bias = a.bias != nullptr;
 #define MXQ_SK_GO(OF, HB) \
-  hipLaunchKernelGGL((skinny_kernel<WFMT, AE, MODE, OF, HB, TL, AR, G, D>), grid, block, lds, st, a, gb)
+  hipLaunchKernelGGL((skinny_kernel<WFMT, AE, MODE, OF, HB, TL, AR, G, D, SWC>), grid, block, lds, st, a, gb)
   if (out_f32) { if (bias) MXQ_SK_GO(true, true); else MXQ_SK_GO(true, false); }
   else { if (bias) MXQ_SK_GO(false, true); else MXQ_SK_GO(false, false); }
 #undef MXQ_SK_GO
@@ -417,31 +432,33 @@ static void launch_skinny_mode(const GemmArgs& a, int wfmt, bool a_e4m3, bool ou
 
 // Dense W8A8 rows (e4m3 activations and weights in the plain layout, 128 x 128 weight blocks):
 // tiles of AR rows (8, or 4 when eight rows of K would pass the LDS cap), all launched at once.
-size_t skinny_dense_lds(int64_t N, int64_t K, int ar, int64_t kstage, bool a_e4m3) {
-  return skinny_lds_layout(false, a_e4m3, K, skinny_groups(N), ar, kstage).total;
+size_t skinny_dense_lds(int64_t N, int64_t K, int ar, int64_t kstage, bool a_e4m3, bool swcol) {
+  return skinny_lds_layout(false, a_e4m3, K, skinny_groups(N), ar, kstage, swcol).total;
 }
 
 int64_t skinny_dense_col_tiles(int64_t N) { return cdiv(N, int64_t(64 * skinny_groups(N))); }
 
-template <bool AE>
+template <bool AE, bool SWC>
 static void launch_skinny_dense_t(const GemmArgs& a, int ar, bool out_f32, hipStream_t st) {
   const int64_t tiles = cdiv(a.M, int64_t(ar));
-  const size_t lds = skinny_dense_lds(a.N, a.K, ar, a.k_split > 1 ? a.k_chunk : 0, AE);
+  const size_t lds = skinny_dense_lds(a.N, a.K, ar, a.k_split > 1 ? a.k_chunk : 0, AE, SWC);
   if (skinny_groups(a.N) == 2) {
-    if (ar == 8) launch_skinny_ar<W_E4M3_BLOCK, AE, ROWS_DENSE, false, 8, 2, 3>(a, out_f32, tiles, st, lds);
-    else launch_skinny_ar<W_E4M3_BLOCK, AE, ROWS_DENSE, false, 4, 2, 3>(a, out_f32, tiles, st, lds);
+    if (ar == 8) launch_skinny_ar<W_E4M3_BLOCK, AE, ROWS_DENSE, false, 8, 2, 3, SWC>(a, out_f32, tiles, st, lds);
+    else launch_skinny_ar<W_E4M3_BLOCK, AE, ROWS_DENSE, false, 4, 2, 3, SWC>(a, out_f32, tiles, st, lds);
   } else {
-    if (ar == 8) launch_skinny_ar<W_E4M3_BLOCK, AE, ROWS_DENSE, false, 8, 1, 4>(a, out_f32, tiles, st, lds);
-    else launch_skinny_ar<W_E4M3_BLOCK, AE, ROWS_DENSE, false, 4, 1, 4>(a, out_f32, tiles, st, lds);
+    if (ar == 8) launch_skinny_ar<W_E4M3_BLOCK, AE, ROWS_DENSE, false, 8, 1, 4, SWC>(a, out_f32, tiles, st, lds);
+    else launch_skinny_ar<W_E4M3_BLOCK, AE, ROWS_DENSE, false, 4, 1, 4, SWC>(a, out_f32, tiles, st, lds);
   }
 }
 
-void launch_skinny_dense(const GemmArgs& a, int ar, bool a_e4m3, bool out_f32, hipStream_t st) {
+void launch_skinny_dense(const GemmArgs& a, int ar, bool a_e4m3, bool out_f32, hipStream_t st, bool swcol) {
   if (a.M <= 0 || a.N <= 0) return;
-  if (a_e4m3)
-    launch_skinny_dense_t<true>(a, ar, out_f32, st);
+  if (swcol && a_e4m3)
+    launch_skinny_dense_t<true, true>(a, ar, out_f32, st);
+  else if (a_e4m3)
+    launch_skinny_dense_t<true, false>(a, ar, out_f32, st);
   else
-    launch_skinny_dense_t<false>(a, ar, out_f32, st);
+    launch_skinny_dense_t<false, false>(a, ar, out_f32, st);
 }
 
 // out[m, n] = bf16(sum over chunks c = 0 .. S-1, in that order, of part[c][m][n]); the bias rode

@@ -373,8 +373,10 @@ def test_block_linear_grid_picked_tiles(shape, block_n):
                                                   (8, 12288, 1536, True, 2), (3, 300, 256, False, 1),
                                                   (64, 256, 4096, True, 8), (1, 7168, 16384, False, 8),
                                                   (4, 16384, 4096, True, 4)])
-def test_block_linear_few_rows(M, N, K, prequant, split):
-    """Few-row block linears (128 x 128 weight blocks) run on the weight-streaming kernel in
+@pytest.mark.parametrize("block_n", [128, 1])
+def test_block_linear_few_rows(M, N, K, prequant, split, block_n):
+    """Few-row block linears (128 x 128 or 1 x 128 weight blocks; the latter with each K chunk's
+    column scales in LDS) run on the weight-streaming kernel in
     tiles of 4 or 8 rows, K cut into `split` chunks whose fp32 partial sums a second kernel adds
     in chunk order: ragged row tiles, a column count that is not a multiple of 4 (the scalar
     sum), 64- and 128-column tiles, bf16 input quantised in the call (the partial sums after
@@ -385,15 +387,15 @@ def test_block_linear_few_rows(M, N, K, prequant, split):
     lib = L.load()
     part = lib.mxq_block_fp8_linear_workspace_size(M, N, K, L.MXQ_DTYPE_E4M3)
     assert part == (0 if split == 1 else (4 * split * M * N + 255) // 256 * 256)
-    d = _block_case(M, N, K, 128, seed=M * 7 + N, bias_dtype=torch.float32)
-    out = ops.block_fp8_linear(d["x"], d["w"], [128, 128], d["sw"], bias=d["bias"])
+    d = _block_case(M, N, K, block_n, seed=M * 7 + N, bias_dtype=torch.float32)
+    out = ops.block_fp8_linear(d["x"], d["w"], [block_n, 128], d["sw"], bias=d["bias"])
     if prequant:
         q, s = ops.per_token_group_quant_fp8(d["x"])
-        out_q = ops.block_fp8_linear(q, d["w"], [128, 128], d["sw"], input_scale=s, bias=d["bias"])
+        out_q = ops.block_fp8_linear(q, d["w"], [block_n, 128], d["sw"], input_scale=s, bias=d["bias"])
         torch.cuda.synchronize()
         assert torch.equal(out_q.view(torch.int16), out.view(torch.int16))
     torch.cuda.synchronize()
-    assert_bf16_close(bf16_bits(out), _oracle_block(d), what=f"few-row block linear {M}x{N}x{K}")
+    assert_bf16_close(bf16_bits(out), _oracle_block(d), what=f"few-row block linear {M}x{N}x{K} bn={block_n}")
 
 
 @pytest.mark.parametrize("M,N,K,block_n", [(128, 2048, 7168, 128), (300, 520, 4096, 128), (1000, 1024, 4096, 128),
