@@ -1137,9 +1137,13 @@ mxq_status mxq_block_fp8_linear(const void* A, int32_t a_dtype, const float* a_s
     gs.split_stride = M * N;
     launch_gemm_w8a8_big(gs, ROWS_DENSE, 3, true, cdiv(M, int64_t(128)), st);
     launch_dense_split_sum(part, bs.split, M, N, static_cast<uint16_t*>(out), ldo, st);
-  } else if ((block_n == 128 || block_n == 1) && M > 128 && K <= 16384 && int64_t(M) * lqa < (int64_t(1) << 32) &&
+  } else if ((block_n == 128 || block_n == 1) && K <= 16384 && int64_t(M) * lqa < (int64_t(1) << 32) &&
       N * K < (int64_t(1) << 32)) {
-    // a 256-wide tile for the column tiles of width 256 and the register-staged 128-wide tile
+    // The direct-to-LDS tiles at any row count: they beat the register-staged tiles at every
+    // measured M with the same bits (interleaved: 128 x 7168 x 2048 27.2 -> 18.2 us, 64 x 7168 x
+    // 2048 22.2 -> 18.0, 100 x 24576 x 1536 24.0 -> 16.5, 16 x 7168 x 2048 19.1 -> 17.3,
+    // 1 x 24576 x 1536 16.2 -> 15.6); the register-staged tiles keep K > 16384 and operands past
+    // 4 GiB.  A 256-wide tile for the column tiles of width 256 and the register-staged 128-wide tile
     // for a narrow last one; the 128 x 128 tile for all of N
     const int shape = dense_big_shape(M, N);
     const int64_t nw = shape >= 2 ? N : wide_tile_columns(N);

@@ -355,12 +355,13 @@ def test_random_block_linear_shapes(seed):
 
 
 @pytest.mark.parametrize("block_n", [128, 1])
-@pytest.mark.parametrize("shape", [(300, 520, 384), (1100, 3900, 256), (2100, 4000, 128)])
+@pytest.mark.parametrize("shape", [(300, 520, 384), (1100, 3900, 256), (2100, 4000, 128), (130, 256, 16512)])
 def test_block_linear_grid_picked_tiles(shape, block_n):
     """The dense W8A8 GEMM picks its tile from the grid: 300 x 520 fits one round of 128 x 128
     tiles (ragged rows and an 8-column last tile); 1100 x 3900 one round of 128 x 256 tiles
     (ragged rows, the 60-column tail on the 128-wide register-staged tile); 2100 x 4000 takes
-    the 256 x 256 tile (ragged rows and a 160-column last tile).  Each against the oracle."""
+    the 256 x 256 tile (ragged rows and a 160-column last tile); K = 16512, past the
+    direct-to-LDS tiles' range, runs on the register-staged tiles.  Each against the oracle."""
     M, N, K = shape
     d = _block_case(M, N, K, block_n, seed=M + block_n, bias_dtype=torch.float32)
     out = ops.block_fp8_linear(d["x"], d["w"], [block_n, 128], d["sw"], bias=d["bias"])
