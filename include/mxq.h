@@ -216,7 +216,7 @@ mxq_status mxq_block_fp8_linear_noalloc(const void* A, int32_t a_dtype, const fl
  *            the call exactly as mxq_mxfp8_quant does; a_dtype MXQ_DTYPE_E4M3: codes [M, K]
  *            (row stride lda bytes, a multiple of 16) with a_scale e8m0 [M, K/32] contiguous.
  *   workspace  mxq_mx_linear_workspace_size(M, N, K, a_dtype) bytes (NULL allowed where it is
- *            0), else MXQ_ERR_WORKSPACE: bf16 input's codes and scales, and -- with K >= 4096
+ *            0), else MXQ_ERR_WORKSPACE: bf16 input's codes and scales, and -- with K >= 3072
  *            on at most 128 tiles (128 or 256 rows x 256 columns) -- the fp32 partial sums of
  *            a K split (2, 4 or 8 chunks added in chunk order: sums grouped differently,
  *            agreement within rounding; at most 16 MiB).

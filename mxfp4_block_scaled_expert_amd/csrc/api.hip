@@ -855,7 +855,9 @@ RingSplit per_tensor_ring_split(int64_t M, int64_t N, int64_t K) {
 }
 
 // MX linears whose tiles (128 or 256 rows as launch_gemm_mx picks them, 256 columns) number at
-// most 128 and K >= 4096: each tile's K range runs as S chunks (the launch's second grid
+// most 128 and K >= 3072 (at K = 2048 mixed through the Python op: MXFP4 1 x 7168 x 2048 22.0
+// against 24.5 us split, MXFP8 256 x 2048 x 2048 25.8 -> 22.9; at 3072 32 x 4096 x 3072 27.6 ->
+// 23.6 / 33.0 -> 23.5 with MXFP4 / MXFP8 weights): each tile's K range runs as S chunks (the launch's second grid
 // dimension), fp32 partial sums to the workspace after the quantised activations, added in
 // chunk order by the split-sum kernel; S doubles while the grid stays within 256 workgroups and a
 // chunk keeps at least four 128-wide steps, partial sums within 16 MiB.
@@ -864,7 +866,7 @@ RingSplit per_tensor_ring_split(int64_t M, int64_t N, int64_t K) {
 #endif
 RingSplit mx_split(int64_t M, int64_t N, int64_t K) {
   RingSplit p{1, K, 0};
-  if (!MXQ_MX_SPLIT || M < 1 || N < 1 || K < 4096 || K % 128 != 0) return p;
+  if (!MXQ_MX_SPLIT || M < 1 || N < 1 || K < 3072 || K % 128 != 0) return p;
   const int64_t nt = cdiv(N, int64_t(256)), t128 = cdiv(M, int64_t(128)) * nt;
   const int64_t tiles = (M <= 128 || t128 <= 256) ? t128 : cdiv(M, int64_t(256)) * nt, kb = K / 128;
   if (tiles > 128) return p;
