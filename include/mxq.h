@@ -179,9 +179,10 @@ mxq_status mxq_block_fp8_linear(const void* A, int32_t a_dtype, const float* a_s
  * the same arguments minus the workspace, same kernels and bit-identical results.  A bf16
  * input's quantised codes and scales go to a static device array of
  * MXQ_NOALLOC_SCRATCH_BYTES (32 MiB) that the library holds on every GPU it runs on until the
- * process ends, and so do the K-split partial sums of the few-row path; inputs needing more than
- * the array (mxq_block_fp8_linear_workspace_size bytes: M * K + 4 * M * K / 128 for bf16
- * input, i.e. about M * K <= 32.5 M, plus at most 8 MiB of partial sums) return
+ * process ends, and so do the K-split partial sums of the few-row and few-tile paths; inputs
+ * needing more than the array (mxq_block_fp8_linear_workspace_size bytes: M * K + 4 * M * K / 128
+ * for bf16 input, i.e. about M * K <= 32.5 M, plus the partial sums -- at most 8 MiB for few
+ * rows, 16 MiB for few tiles, whose M * K <= 8 M keeps the total within the array) return
  * MXQ_ERR_SCRATCH before anything is enqueued.  The call
  * allocates nothing.  Every call on one GPU shares that GPU's array: calls that may overlap
  * on one GPU (different streams, no ordering between them) race and must not be issued; calls
