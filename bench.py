@@ -257,6 +257,42 @@ def bench_linear(steps: int, warmup: int):
     }
 
 
+def bench_linear_small(steps: int, warmup: int, M: int, N: int, K: int):
+    """A block-FP8 W8A8 linear of few rows or few tiles (pre-quantised e4m3 input, 128x128 weight
+    blocks) on rotating weight sets beyond the last-level cache, per-call events: the
+    weight-streaming path (few rows) or the K-split 128x128 tiles (few tiles); reported with the
+    weight bytes' rate against HBM."""
+    from mxfp4_block_scaled_expert_amd import synth
+    L, lib = _lib()
+    dev = torch.device("cuda", 0)
+    n_rot = max(2, -(-(600 << 20) // (N * K)))
+    base = synth.block_linear(M, N, K, seed=4242, device=dev)
+    q = torch.empty(M, K, dtype=torch.uint8, device=dev)
+    sq = torch.empty(M, K // 128, dtype=torch.float32, device=dev)
+    sh = torch.cuda.current_stream().cuda_stream
+    _check(lib.mxq_per_token_group_quant_fp8(base["x"].data_ptr(), M, K, K, 128, q.data_ptr(), sq.data_ptr(), sh),
+           "quant")
+    ws_n = lib.mxq_block_fp8_linear_workspace_size(M, N, K, L.MXQ_DTYPE_E4M3)
+    ws = torch.empty(max(ws_n, 1), dtype=torch.uint8, device=dev)
+    out = torch.empty(M, N, dtype=torch.bfloat16, device=dev)
+    ws_list = [base["w"]] + [torch.randint(0, 256, (N, K), dtype=torch.uint8, device=dev) & 0x77
+                             for _ in range(n_rot - 1)]
+    it = [0]
+
+    def run():
+        w = ws_list[it[0] % n_rot]
+        it[0] += 1
+        _check(lib.mxq_block_fp8_linear(q.data_ptr(), L.MXQ_DTYPE_E4M3, sq.data_ptr(), M, K, K, w.data_ptr(), N,
+                                        base["sw"].data_ptr(), K // 128, 1, 128, 128, None, 0, out.data_ptr(),
+                                        L.MXQ_DTYPE_BF16, N, ws.data_ptr(), ws_n, sh), "block_fp8_linear")
+    st, _ = _time_calls(run, steps, warmup)
+    wbytes = N * K
+    return {"workload": f"block_w8a8_linear_{M}x{K}x{N}", "us": st,
+            "tflops": 2.0 * M * N * K / (st["median"] * 1e-6) / 1e12,
+            "weight_tbs": wbytes / (st["median"] * 1e-6) / 1e12,
+            "hbm_frac": wbytes / (st["median"] * 1e-6) / 8e12, "k_split_workspace_bytes": ws_n}
+
+
 def bench_per_tensor(steps: int, warmup: int):
     """The per-tensor W8A16 GEMM of the SGLang CPU page's test, bf16 [97, 576] x e4m3 [224, 576]^T
     with an fp32 bias: launch-latency bound (0.29 MB, 25 MFLOP), reported in µs."""
@@ -615,6 +651,9 @@ def main():
     secondary = {}
     if not a.no_secondary:
         secondary["per_tensor_w8a16_97x576x224"] = bench_per_tensor(a.steps, a.warmup)
+        secondary["block_linear_decode_m16_k7168_n2048"] = bench_linear_small(max(10, a.steps), a.warmup, 16, 2048, 7168)
+        secondary["block_linear_few_tiles_m128_k7168_n2048"] = bench_linear_small(max(10, a.steps), a.warmup, 128, 2048,
+                                                                                    7168)
         secondary["w8a16_small_blocks_e8"] = bench_moe("moe_block_fp8_w8a16_e8_h2048_i1024", a.steps, a.warmup,
                                                        1003)
         torch.cuda.empty_cache()
